@@ -1,0 +1,226 @@
+"""
+TEST INFRASTRUCTURE ONLY: the CPU oracle for the routed MoE FFN layer.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP library and its Python binding
+never do; the two share no code.
+
+``moe_oracle.c`` (double precision, OpenMP) is the oracle proper; it is built
+into ``liboracle.so`` next to it. ``brute.py`` holds independent numpy
+restatements for tiny inputs that pin it. Parity status of every function is
+listed below; all are pinned by tests in ``tests/test_oracle_*.py``:
+
+  route / limit / plan / expert / layer / decode   pinned (brute force,
+  closed forms, invariants, numpy library routines).
+  The pages' own drop shares and speedups come from trained routers and
+  other systems: parity unpinned (no input here reproduces them).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "moe_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+DT = {"f32": 0, "bf16": 1, "f16": 2, "q4b32": 3}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, OpenMP, baseline x86-64)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC",
+                               "-std=c11", "-Wall", SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or (os.path.getmtime(LIB)
+                                       < os.path.getmtime(SRC)):
+            build()
+        L = ctypes.CDLL(LIB)
+        i64, i32, dbl, vp = (ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                             ctypes.c_void_p)
+        L.orc_route.argtypes = [i64, i32, i32, vp, vp, vp]
+        L.orc_limit.argtypes = [i64, i32, i32, dbl]
+        L.orc_limit.restype = i64
+        L.orc_plan.argtypes = [i64, i32, i32, i32, dbl, vp, vp, vp, vp, vp,
+                               vp, vp, vp, vp, vp]
+        L.orc_expert.argtypes = [i64, i64, i64, vp, i32, vp, vp, vp, vp, vp,
+                                 vp, i32, dbl, vp, vp, vp, vp]
+        L.orc_layer.argtypes = [i64, i64, i64, i32, i32, i32, vp, i32, vp, vp,
+                                vp, vp, vp, vp, i32, dbl, vp, vp, vp, i64, vp,
+                                vp]
+        L.orc_decode.argtypes = [vp, vp, i32, i64, i64, i64, vp]
+        L.orc_decode_f16.argtypes = [vp, i64, vp]
+        L.orc_num_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _np(t):
+    """A CPU tensor as a numpy array of its raw storage (16-bit as uint16)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return np.ascontiguousarray(t)
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _weight(w):
+    """(data, scales) raw numpy arrays of one weight tensor or q4 pair."""
+    if isinstance(w, (tuple, list)):
+        return _np(w[0]), _np(w[1])
+    return _np(w), None
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+def route(logits, k: int):
+    """ids [T, k] int32 (rank order) and weights [T, k] float64."""
+    lg = np.ascontiguousarray(_np(logits), dtype=np.float32)
+    T, E = lg.shape
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float64)
+    rc = lib().orc_route(T, E, k, _p(lg), _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError(f"orc_route failed ({rc})")
+    return ids, w
+
+
+def limit(T: int, E: int, k: int, cf: float) -> int:
+    """Capacity per expert; -1 means uncapped."""
+    return int(lib().orc_limit(T, E, k, float(cf)))
+
+
+def plan(ids: np.ndarray, E: int, cf: float, n_shared: int = 0) -> dict:
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    P = T * k + n_shared * T
+    out = dict(
+        slot=np.zeros((T, k), np.int32), keep=np.zeros((T, k), np.uint8),
+        counts=np.zeros(E + n_shared, np.int64),
+        offsets=np.zeros(E + n_shared + 1, np.int64),
+        pair_token=np.full(P, -1, np.int32), pair_src=np.full(P, -2, np.int32),
+        tok2pair=np.zeros((T, k), np.int32))
+    lim = np.zeros(1, np.int64)
+    dropped = np.zeros(1, np.int64)
+    rc = lib().orc_plan(T, E, k, n_shared, float(cf), _p(ids), _p(lim),
+                        _p(out["slot"]), _p(out["keep"]), _p(out["counts"]),
+                        _p(out["offsets"]), _p(out["pair_token"]),
+                        _p(out["pair_src"]), _p(out["tok2pair"]), _p(dropped))
+    if rc != 0:
+        raise ValueError(f"orc_plan failed ({rc})")
+    n = int(out["offsets"][-1])
+    out["pair_token"] = out["pair_token"][:n]
+    out["pair_src"] = out["pair_src"][:n]
+    out["limit"] = int(lim[0])
+    out["dropped"] = int(dropped[0])
+    out["kept"] = T * k - int(dropped[0])
+    out["drop_fraction"] = (int(dropped[0]) / (T * k)) if T * k else 0.0
+    return out
+
+
+def expert(x_row, e: int, w_gate, w_up, w_down, x_dtype: str, w_dtype: str,
+           c: float):
+    """g, u, h [F] and yp [D] of expert e on one token, in float64."""
+    xr = _np(x_row).reshape(-1)
+    D = xr.shape[0]
+    wg, wgs = _weight(w_gate)
+    wu, wus = _weight(w_up)
+    wd, wds = _weight(w_down)
+    F = wg.shape[1]
+    g, u, h = (np.zeros(F) for _ in range(3))
+    yp = np.zeros(D)
+    rc = lib().orc_expert(D, F, e, _p(xr), DT[x_dtype], _p(wg), _p(wgs),
+                          _p(wu), _p(wus), _p(wd), _p(wds), DT[w_dtype],
+                          float(c), _p(g), _p(u), _p(h), _p(yp))
+    if rc != 0:
+        raise ValueError(f"orc_expert failed ({rc})")
+    return g, u, h, yp
+
+
+def layer(x, w_gate, w_up, w_down, ids, w, keep, *, E: int, n_shared: int,
+          x_dtype: str, w_dtype: str, c: float, tokens=None):
+    """y [len(tokens) or T, D] float64 for the given routing and keep mask."""
+    xa = _np(x)
+    T, D = xa.shape
+    wg, wgs = _weight(w_gate)
+    wu, wus = _weight(w_up)
+    wd, wds = _weight(w_down)
+    F = wg.shape[1]
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = np.ascontiguousarray(w, np.float64)
+    keep = np.ascontiguousarray(keep, np.uint8)
+    k = ids.shape[1]
+    tl = None if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    n = T if tl is None else tl.shape[0]
+    y = np.zeros((n, D))
+    rc = lib().orc_layer(T, D, F, E, k, n_shared, _p(xa), DT[x_dtype], _p(wg),
+                         _p(wgs), _p(wu), _p(wus), _p(wd), _p(wds),
+                         DT[w_dtype], float(c), _p(ids), _p(w), _p(keep), n,
+                         _p(tl), _p(y))
+    if rc != 0:
+        raise ValueError(f"orc_layer failed ({rc})")
+    return y
+
+
+def decode(w, e: int, w_dtype: str) -> np.ndarray:
+    """Expert e's [N, K] weight matrix decoded exactly to float64."""
+    data, scales = _weight(w)
+    N = data.shape[1]
+    K = data.shape[2] * (2 if w_dtype == "q4b32" else 1)
+    out = np.zeros((N, K))
+    rc = lib().orc_decode(_p(data), _p(scales), DT[w_dtype], e, N, K, _p(out))
+    if rc != 0:
+        raise ValueError(f"orc_decode failed ({rc})")
+    return out
+
+
+def decode_f16_bits(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, np.uint16)
+    out = np.zeros(b.shape)
+    lib().orc_decode_f16(_p(b), b.size, _p(out))
+    return out
+
+
+def dequant_q4_to_f16_bits(w, e: int) -> np.ndarray:
+    """fp16(q * s) of expert e, rounded to nearest-even: uint16 bits [N, K].
+
+    The product q*s is exact in float64 (a 4-bit integer times an fp16), and
+    numpy's float64 -> float16 cast rounds to nearest, ties to even.
+    """
+    exact = decode(w, e, "q4b32")
+    return exact.astype(np.float16).view(np.uint16)
+
+
+def run_workload(wl: dict, tokens=None) -> dict:
+    """Route, plan and (for the given tokens) the layer output of a workload."""
+    ids, w = route(wl["logits"], wl["k"])
+    pl = plan(ids, wl["E"], wl["capacity_factor"], wl["n_shared"])
+    y = layer(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids, w,
+              pl["keep"], E=wl["E"], n_shared=wl["n_shared"],
+              x_dtype=wl["x_dtype"], w_dtype=wl["w_dtype"],
+              c=wl["swiglu_limit"], tokens=tokens)
+    return dict(ids=ids, w=w, plan=pl, y=y)

@@ -1,0 +1,356 @@
+/*
+ * moe_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, double-precision CPU oracle for the forward pass of a routed
+ * mixture-of-experts FFN layer on a prompt. Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg load it; the HIP library never
+ * does, and the two share no code, header, table or helper.
+ *
+ * What it computes, and where the pages say so:
+ *   route    top-k of the router over each token, the chosen weights
+ *            renormalised to sum to one (mini-AGI PR #3, minagi/pool.py,
+ *            `requested(scores)`, the comment on the kept mass).
+ *   plan     capacity drop in token order: a pair is kept while its expert
+ *            holds fewer than `limit` earlier pairs; pairs sorted by expert
+ *            (mini-AGI PR #3 and #4, minagi/pool.py, the `keep` filter and the
+ *            argsort/bincount over the flattened expert ids; the capacity
+ *            factor caps an expert at a multiple of its even share of the
+ *            batch, configs/strix_halo_large.yaml, `capacity_factor`).
+ *   expert   h = silu(x Wg^T) * (x Wu^T), y = h Wd^T (mini-AGI PR #4,
+ *            minagi/pool.py, `experts()`), with the clamp of the FP16 fat
+ *            expert route (Strata PR #4366, "Problem and result" and
+ *            "Approach").
+ *   combine  y[t] = sum over kept pairs of weight * expert output; a dropped
+ *            pair adds nothing (the weights are filtered by `keep` after they
+ *            were normalised, mini-AGI PR #4, minagi/pool.py).
+ *
+ * Readings where the pages leave a step open (all listed in the design notes):
+ *   - top-k by logits (softmax is monotone), ties to the lower expert index,
+ *     +0 and -0 equal; NaN logits are refused;
+ *   - limit = max(1, floor(cf * T * k / E)); cf == 0 means no cap;
+ *   - the clamp: gate clamped above at c, up clamped to [-c, c], c <= 0 off;
+ *   - a shared expert (index E) sees every token with weight 1, never drops;
+ *   - 4-bit weights: two's-complement nibbles, low nibble = even K index,
+ *     one fp16 scale per 32 consecutive K values of an output row, value q*s.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC moe_oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2, ORC_Q4B32 = 3 };
+
+/* ---- exact decoding of stored values ---------------------------------- */
+
+/* IEEE 754 binary16 -> double, exact (sign, 5-bit exponent, 10-bit fraction). */
+static double f16_bits_to_double(uint16_t h)
+{
+    int sign = h >> 15;
+    int ex = (h >> 10) & 31;
+    int fr = h & 1023;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -24);               /* subnormal: fr * 2^-24 */
+    else if (ex == 31)
+        v = fr ? NAN : INFINITY;
+    else
+        v = ldexp((double)(fr + 1024), ex - 25);  /* (1 + fr/1024) * 2^(ex-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double dense_value(const void *base, int dtype, size_t idx)
+{
+    switch (dtype) {
+    case ORC_F32: return (double)((const float *)base)[idx];
+    case ORC_BF16: return bf16_bits_to_double(((const uint16_t *)base)[idx]);
+    case ORC_F16: return f16_bits_to_double(((const uint16_t *)base)[idx]);
+    default: return NAN;
+    }
+}
+
+/* Element (n, kk) of expert e's [N, K] weight matrix, decoded exactly. */
+static double weight_value(const void *data, const void *scales, int dtype,
+                           int64_t e, int64_t N, int64_t K, int64_t n, int64_t kk)
+{
+    if (dtype != ORC_Q4B32)
+        return dense_value(data, dtype, (size_t)((e * N + n) * K + kk));
+    const uint8_t *bytes = (const uint8_t *)data;
+    uint8_t byte = bytes[(e * N + n) * (K / 2) + kk / 2];
+    int nib = (kk & 1) ? (byte >> 4) : (byte & 15);
+    int q = nib >= 8 ? nib - 16 : nib;           /* two's complement, -8..7 */
+    const uint16_t *s = (const uint16_t *)scales;
+    double scale = f16_bits_to_double(s[(e * N + n) * (K / 32) + kk / 32]);
+    return (double)q * scale;
+}
+
+/* Decode one expert's [N, K] matrix into out (row-major), for the tests. */
+int orc_decode(const void *data, const void *scales, int dtype, int64_t e,
+               int64_t N, int64_t K, double *out)
+{
+    if (dtype < ORC_F32 || dtype > ORC_Q4B32 || (dtype == ORC_Q4B32 && K % 32))
+        return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t kk = 0; kk < K; ++kk)
+            out[n * K + kk] = weight_value(data, scales, dtype, e, N, K, n, kk);
+    return 0;
+}
+
+int orc_decode_f16(const uint16_t *bits, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f16_bits_to_double(bits[i]);
+    return 0;
+}
+
+/* ---- route ------------------------------------------------------------- */
+
+/*
+ * For every token: the k experts of largest logit, ordered by rank, where the
+ * rank of expert e is the number of experts that beat it (a larger logit, or
+ * an equal logit and a lower index). Weights w_j = exp(l_j - l_0) / sum_i
+ * exp(l_i - l_0) over the k chosen: full softmax renormalised over the top-k.
+ */
+int orc_route(int64_t T, int E, int k, const float *logits, int32_t *ids,
+              double *w)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E)
+        return -1;
+    for (int64_t i = 0; i < T * E; ++i)
+        if (isnan(logits[i]))
+            return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        int found = 0;
+        for (int e = 0; e < E; ++e) {
+            int rank = 0;
+            for (int f = 0; f < E; ++f)
+                if (l[f] > l[e] || (l[f] == l[e] && f < e))
+                    ++rank;
+            if (rank < k) {
+                ids[t * k + rank] = e;
+                ++found;
+            }
+        }
+        if (found != k) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        double l0 = (double)l[ids[t * k]];
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j)
+            sum += exp((double)l[ids[t * k + j]] - l0);
+        for (int j = 0; j < k; ++j)
+            w[t * k + j] = exp((double)l[ids[t * k + j]] - l0) / sum;
+    }
+    return bad ? -3 : 0;
+}
+
+/* ---- capacity and dispatch plan --------------------------------------- */
+
+/* Most pairs one expert may keep: cf times its fair share T*k/E, floored,
+ * at least 1; -1 means uncapped (cf == 0). */
+int64_t orc_limit(int64_t T, int E, int k, double cf)
+{
+    if (cf == 0.0)
+        return -1;
+    double fair = cf * (double)T * (double)k / (double)E;
+    int64_t lim = (int64_t)floor(fair);
+    return lim < 1 ? 1 : lim;
+}
+
+/*
+ * Walk the pairs in token order. slot = how many earlier tokens chose the
+ * same expert; keep iff slot < limit. Kept pairs are placed in an
+ * expert-sorted list at offsets[e] + slot. The shared expert, when present, is
+ * index E and holds every token in order, weight 1, never dropped.
+ * Outputs (caller-allocated): slot[T*k], keep[T*k], counts[E+ns],
+ * offsets[E+ns+1], pair_token[P], pair_src[P] (t*k+j, or -1 for a shared
+ * pair), tok2pair[T*k] (-1 when dropped), *dropped, *limit_out.
+ */
+int orc_plan(int64_t T, int E, int k, int n_shared, double cf,
+             const int32_t *ids, int64_t *limit_out, int32_t *slot,
+             uint8_t *keep, int64_t *counts, int64_t *offsets,
+             int32_t *pair_token, int32_t *pair_src, int32_t *tok2pair,
+             int64_t *dropped)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || n_shared < 0 || n_shared > 1 ||
+        !(cf >= 0.0) || isinf(cf))
+        return -1;
+    int64_t limit = orc_limit(T, E, k, cf);
+    int64_t *seen = calloc((size_t)E, sizeof *seen);
+    if (!seen)
+        return -4;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int e = ids[t * k + j];
+            if (e < 0 || e >= E) {
+                free(seen);
+                return -1;
+            }
+            int64_t s = seen[e]++;
+            slot[t * k + j] = (int32_t)s;
+            keep[t * k + j] = (limit < 0 || s < limit) ? 1 : 0;
+        }
+    int64_t kept = 0;
+    for (int e = 0; e < E; ++e) {
+        counts[e] = (limit < 0 || seen[e] < limit) ? seen[e] : limit;
+        kept += counts[e];
+    }
+    if (n_shared)
+        counts[E] = T;
+    offsets[0] = 0;
+    for (int e = 0; e < E + n_shared; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int64_t p = t * k + j;
+            if (keep[p]) {
+                int64_t pos = offsets[ids[p]] + slot[p];
+                pair_token[pos] = (int32_t)t;
+                pair_src[pos] = (int32_t)p;
+                tok2pair[p] = (int32_t)pos;
+            } else {
+                tok2pair[p] = -1;
+            }
+        }
+    if (n_shared)
+        for (int64_t t = 0; t < T; ++t) {
+            pair_token[offsets[E] + t] = (int32_t)t;
+            pair_src[offsets[E] + t] = -1;
+        }
+    *dropped = T * k - kept;
+    *limit_out = limit;
+    free(seen);
+    return 0;
+}
+
+/* ---- one expert on one token ------------------------------------------ */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * g = Wg[e] x, u = Wu[e] x, h = silu(min(g, c)) * clamp(u, -c, c) (no clamp
+ * when c <= 0), yp = Wd[e] h. Any of g, u, h may be NULL.
+ */
+static void expert_ffn(int64_t D, int64_t F, int64_t e, const double *x,
+                       const void *wg, const void *wg_s, const void *wu,
+                       const void *wu_s, const void *wd, const void *wd_s,
+                       int w_dtype, double c, double *g, double *u, double *h,
+                       double *yp)
+{
+    double *hh = malloc((size_t)F * sizeof *hh);
+    for (int64_t f = 0; f < F; ++f) {
+        double gs = 0.0, us = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            gs += weight_value(wg, wg_s, w_dtype, e, F, D, f, d) * x[d];
+            us += weight_value(wu, wu_s, w_dtype, e, F, D, f, d) * x[d];
+        }
+        double gc = gs, uc = us;
+        if (c > 0.0) {
+            gc = gs < c ? gs : c;
+            uc = us < -c ? -c : (us > c ? c : us);
+        }
+        hh[f] = silu(gc) * uc;
+        if (g) g[f] = gs;
+        if (u) u[f] = us;
+        if (h) h[f] = hh[f];
+    }
+    for (int64_t d = 0; d < D; ++d) {
+        double s = 0.0;
+        for (int64_t f = 0; f < F; ++f)
+            s += weight_value(wd, wd_s, w_dtype, e, D, F, d, f) * hh[f];
+        yp[d] = s;
+    }
+    free(hh);
+}
+
+int orc_expert(int64_t D, int64_t F, int64_t e, const void *xrow, int x_dtype,
+               const void *wg, const void *wg_s, const void *wu,
+               const void *wu_s, const void *wd, const void *wd_s,
+               int w_dtype, double c, double *g, double *u, double *h,
+               double *yp)
+{
+    if (x_dtype < ORC_F32 || x_dtype > ORC_F16 || w_dtype < ORC_F32 ||
+        w_dtype > ORC_Q4B32)
+        return -1;
+    double *x = malloc((size_t)D * sizeof *x);
+    for (int64_t d = 0; d < D; ++d)
+        x[d] = dense_value(xrow, x_dtype, (size_t)d);
+    expert_ffn(D, F, e, x, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype, c, g, u, h,
+               yp);
+    free(x);
+    return 0;
+}
+
+/* ---- the layer --------------------------------------------------------- */
+
+/*
+ * y[t] = sum_j keep[t,j] * w[t,j] * expert(ids[t,j], x[t]) (+ shared expert),
+ * for the tokens in tok_list (all T tokens when tok_list is NULL). No
+ * renormalisation after drops.
+ */
+int orc_layer(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
+              const void *x, int x_dtype, const void *wg, const void *wg_s,
+              const void *wu, const void *wu_s, const void *wd,
+              const void *wd_s, int w_dtype, double c, const int32_t *ids,
+              const double *w, const uint8_t *keep, int64_t n_tok,
+              const int64_t *tok_list, double *y)
+{
+    if (x_dtype < ORC_F32 || x_dtype > ORC_F16 || w_dtype < ORC_F32 ||
+        w_dtype > ORC_Q4B32 || (w_dtype == ORC_Q4B32 && (D % 32 || F % 32)))
+        return -1;
+    if (!tok_list)
+        n_tok = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_tok; ++i) {
+        int64_t t = tok_list ? tok_list[i] : i;
+        double *xt = malloc((size_t)D * sizeof *xt);
+        double *yp = malloc((size_t)D * sizeof *yp);
+        double *yt = y + i * D;
+        for (int64_t d = 0; d < D; ++d) {
+            xt[d] = dense_value(x, x_dtype, (size_t)(t * D + d));
+            yt[d] = 0.0;
+        }
+        for (int j = 0; j < k; ++j) {
+            if (!keep[t * k + j])
+                continue;
+            expert_ffn(D, F, ids[t * k + j], xt, wg, wg_s, wu, wu_s, wd, wd_s,
+                       w_dtype, c, NULL, NULL, NULL, yp);
+            for (int64_t d = 0; d < D; ++d)
+                yt[d] += w[t * k + j] * yp[d];
+        }
+        if (n_shared) {
+            expert_ffn(D, F, E, xt, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype, c,
+                       NULL, NULL, NULL, yp);
+            for (int64_t d = 0; d < D; ++d)
+                yt[d] += yp[d];
+        }
+        free(xt);
+        free(yp);
+    }
+    return 0;
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
