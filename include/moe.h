@@ -1,0 +1,217 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts FFN layer.
+ *
+ * The layer, forward pass on a prompt of T tokens:
+ *   1. route     each token keeps its k largest router logits; their weights
+ *                are the softmax renormalised over those k (mini-AGI PR #3,
+ *                minagi/pool.py, `requested(scores)`);
+ *   2. capacity  an expert keeps at most `limit` pairs, first come by token
+ *                index; the rest drop and add nothing (mini-AGI PR #3/#4,
+ *                configs/strix_halo_large.yaml `capacity_factor`, and the
+ *                `keep` filter in minagi/pool.py);
+ *   3. dispatch  kept token-expert pairs grouped by expert (the argsort and
+ *                bincount over expert ids in minagi/pool.py);
+ *   4. experts   per expert: gathered rows times W_gate and W_up, clamped
+ *                SwiGLU, times W_down (minagi/pool.py `experts()`; the clamp
+ *                and the dequantise-once FP16 route for experts holding many
+ *                rows from Strata PR #4366, "Problem and result" and
+ *                "Approach"; a K-parallel tile for experts holding few pairs
+ *                from TensorFold PR #1607, "What this changes");
+ *   5. combine   y[t] = sum of the token's kept pairs' weighted outputs.
+ *
+ * Conventions for every call:
+ *   - The caller owns all device memory: logits, x, weights, y and both
+ *     workspaces (sizes from the *_workspace_bytes queries). The library only
+ *     allocates a small host-side plan handle. Workspaces are caller-provided
+ *     because buffer sizes that change every call fragmented the allocator on
+ *     the mini-AGI PR #4 README's `expandable_segments` row.
+ *   - Every device call is asynchronous on `stream` (a hipStream_t; NULL =
+ *     the default stream). Nothing synchronises the host except
+ *     moe_plan_stats_get and moe_phase_times.
+ *   - Arguments are validated on the host before any launch. On a non-OK
+ *     status nothing was launched (so y is untouched) unless the status is
+ *     MOE_EHIP from a launch; moe_last_error() then names the cause.
+ *   - Device pointers must be 16-byte aligned. Matrices are row-major and
+ *     K-contiguous: W_gate, W_up are [E + n_shared, F, D], W_down is
+ *     [E + n_shared, D, F], as the pages use them through W.transpose(1, 2).
+ *   - Supported dtype pairs (x, W): (F32, F32), (BF16, BF16), (F16, F16),
+ *     (F16, Q4B32). Anything else is MOE_EUNSUPPORTED, never a fallback.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* bad argument (sizes, pointers, alignment)    */
+    MOE_EUNSUPPORTED = -2,  /* dtype combination or size the library lacks */
+    MOE_EWORKSPACE = -3,    /* workspace smaller than the size query       */
+    MOE_EHIP = -4           /* the HIP runtime reported an error           */
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_F16 = 2,
+    /* 4-bit block weights: `data` is uint8 [.., N, K/2] holding two's-
+     * complement nibbles (low nibble = even K index), `scales` is fp16
+     * [.., N, K/32], one scale per 32 consecutive K values of a row; the
+     * value is q * s. Weights only; x must be F16. */
+    MOE_Q4B32 = 3
+} moe_dtype;
+
+/* Plan shape. 1 <= k <= E <= 1024; T >= 0; T*(k+1) < 2^31; n_shared in
+ * {0, 1}: a shared expert (index E in the weights) sees every token with
+ * weight 1 and never drops (TensorFold PR #1607 plans of 256 experts plus a
+ * shared slot). capacity_factor >= 0 and finite; 0 means uncapped (the
+ * pages' default), otherwise limit = max(1, floor(cf * T * k / E)). */
+typedef struct {
+    int32_t T, E, k, n_shared;
+    float capacity_factor;
+} moe_plan_desc;
+
+/* Forward options; moe_options_default() fills the defaults.
+ *   swiglu_limit      c of h = silu(min(g, c)) * clamp(u, -c, c); <= 0 turns
+ *                     the clamp off. Default 7.0.
+ *   splitk_max_pairs  S: bf16/f16 experts holding n <= S pairs run the
+ *                     split-K tile, the rest the full MFMA tile. An f32
+ *                     bound compared exactly in f64 (TensorFold PR #1607,
+ *                     "Why 3.5, and why a fraction"); 0 sends every expert
+ *                     to the full tile, a huge value every expert to
+ *                     split-K. Default: the switch point measured on MI355X.
+ *   fat_rows          4-bit weights only: experts holding >= fat_rows pairs
+ *                     are dequantised once to fp16 and run the full tile;
+ *                     the rest run the fused-dequant split-K tile. <= 0 turns
+ *                     the fat route off; 1..16 is raised to 17, the light
+ *                     tiles owning experts of 16 rows or fewer (Strata PR
+ *                     #4366, maintainer's review). Default 64.
+ *   flags             MOE_OPT_PHASE_EVENTS records HIP events around each
+ *                     forward phase on `stream` (see moe_phase_times). */
+typedef struct {
+    float swiglu_limit;
+    float splitk_max_pairs;
+    int32_t fat_rows;
+    int32_t flags;
+} moe_options;
+
+#define MOE_OPT_PHASE_EVENTS 1
+
+/* One weight tensor. `scales` is NULL unless dtype is MOE_Q4B32. */
+typedef struct {
+    int32_t dtype;
+    const void *data;
+    const void *scales;
+} moe_weight;
+
+typedef struct moe_plan moe_plan;   /* opaque host handle */
+
+typedef struct {
+    int64_t T, E, k, n_shared;
+    int64_t limit;          /* -1 when uncapped                            */
+    int64_t pairs;          /* T*k routed pairs before the drop            */
+    int64_t kept;           /* routed pairs kept                           */
+    int64_t dropped;        /* pairs - kept                                */
+    int64_t touched;        /* routed experts holding >= 1 kept pair       */
+    int64_t max_rows;       /* most kept pairs one routed expert holds     */
+    int64_t nonfinite;      /* NaN logits seen (ordered below -inf)        */
+    int64_t thin, full, fat;/* routed experts per forward route, for the
+                               options passed to moe_plan_stats_get        */
+    double drop_fraction;   /* dropped / pairs (mini-AGI PR #3,
+                               tools/bench_hw.py `dropped_share`)          */
+} moe_plan_stats;
+
+/* Device arrays of a plan, inside its workspace, for inspection. All int32
+ * unless noted; P = offsets[E + n_shared]. */
+typedef struct {
+    const int32_t *topk_id;    /* [T, k] expert ids in rank order           */
+    const float *topk_w;       /* [T, k] f32 weights, renormalised          */
+    const int32_t *slot;       /* [T, k] earlier tokens choosing that expert*/
+    const int32_t *tok2pair;   /* [T, k] position in the pair list, or -1   */
+    const int32_t *counts;     /* [E + n_shared] kept pairs per expert      */
+    const int32_t *offsets;    /* [E + n_shared + 1] exclusive scan         */
+    const int32_t *pair_token; /* [P] token of each expert-sorted pair      */
+    const float *pair_w;       /* [P] its weight (1 for the shared expert)  */
+    const int64_t *stats;      /* [8] dropped, kept, nonfinite, touched,
+                                  max_rows, 0, 0, 0                         */
+} moe_plan_views;
+
+/* --- plan: route + capacity + dispatch -------------------------------- */
+
+/* Bytes of device workspace moe_plan_create needs; 0 on invalid desc. */
+size_t moe_plan_workspace_bytes(const moe_plan_desc *desc);
+
+/* Route `logits` (f32 [T, E], device) and build the dispatch plan into `ws`
+ * (device, >= moe_plan_workspace_bytes, 256-byte aligned). Launches only;
+ * no host sync. The plan handle refers into `ws`: keep both alive while the
+ * plan is used, free the handle with moe_plan_destroy. Ties in the logits go
+ * to the lower expert index; +0 and -0 are equal; NaN ranks below -inf. */
+moe_status moe_plan_create(const moe_plan_desc *desc, const float *logits,
+                           void *ws, size_t ws_bytes, void *stream,
+                           moe_plan **out);
+
+/* Copies the plan's counters to the host (synchronises `stream`). */
+moe_status moe_plan_stats_get(const moe_plan *plan, const moe_options *opt,
+                              moe_plan_stats *out, void *stream);
+
+moe_status moe_plan_get_views(const moe_plan *plan, moe_plan_views *out);
+
+void moe_plan_destroy(moe_plan *plan);
+
+/* --- forward: experts + combine --------------------------------------- */
+
+void moe_options_default(moe_options *opt);
+
+/* Bytes of device workspace moe_forward needs for this plan, sizes, dtypes
+ * and options (the dequantised fp16 copies of 4-bit fat experts included,
+ * sized for the most fat experts the plan could hold); 0 if unsupported. */
+size_t moe_forward_workspace_bytes(const moe_plan *plan, int32_t D, int32_t F,
+                                   int32_t x_dtype, int32_t w_dtype,
+                                   const moe_options *opt);
+
+/* y[T, D] = the layer on x[T, D]. D and F must be multiples of 128. `opt`
+ * may be NULL for the defaults. The plan must come from logits over the same
+ * T tokens. y_dtype is MOE_F32 (the residual stream's precision: the pages
+ * compute the dispatch buffer in the compute dtype and return the layer
+ * output in the residual's fp32, mini-AGI PR #4, minagi/pool.py, the
+ * compute-dtype comment) or x's dtype (one rounding of that f32 result).
+ * Each kept pair's weighted output is held in f32 before the combine. */
+moe_status moe_forward(const moe_plan *plan, const void *x, int32_t x_dtype,
+                       moe_weight w_gate, moe_weight w_up, moe_weight w_down,
+                       int32_t D, int32_t F, void *y, int32_t y_dtype,
+                       void *ws, size_t ws_bytes, const moe_options *opt,
+                       void *stream);
+
+/* --- standalone pieces ------------------------------------------------- */
+
+/* Dequantise rows of 4-bit block weights to fp16, once: out[r, c] =
+ * fp16_rne(q * s) for a [rows, K] matrix (Strata PR #4366, "Approach": one
+ * expert's weights decoded to FP16 once). K multiple of 32. Async. */
+moe_status moe_dequant_q4(const void *data, const void *scales, int64_t rows,
+                          int64_t K, void *out_f16, void *stream);
+
+/* Milliseconds spent in each forward phase, summed over the moe_forward
+ * calls since the last reset that ran with MOE_OPT_PHASE_EVENTS; `calls`
+ * receives the count. Phases: 0 classify, 1 dequant-once, 2 gate/up full
+ * tile, 3 gate/up split-K, 4 down full tile, 5 down split-K, 6 combine.
+ * Synchronises on the recorded events. reset != 0 clears afterwards. */
+#define MOE_N_PHASES 7
+moe_status moe_phase_times(double *ms, int32_t n, int64_t *calls,
+                           int32_t reset);
+
+/* Thread-local message for the last non-OK status of this thread. */
+const char *moe_last_error(void);
+
+/* Library version string. */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,346 @@
+"""
+Python binding of the MI355X routed mixture-of-experts FFN layer.
+
+A thin ctypes layer over ``libmoe_mi355x.so`` (C ABI in ``include/moe.h``):
+it marshals torch tensors into pointers and sizes, takes the current HIP
+stream, and allocates the caller-owned workspaces with ``torch.empty``.
+Every step of the layer runs in the library's HIP kernels; there is no
+fallback. If the library is not built, every call raises.
+
+    plan = moe_plan_create(logits, k=8, capacity_factor=0.0)
+    y = moe_forward(plan, x, w_gate, w_up, w_down)
+
+Weights are torch tensors [E (+1 shared), F, D] / [E (+1), D, F] in x's dtype,
+or, for 4-bit block weights, ``(packed uint8 [.., N, K/2], scales fp16
+[.., N, K/32])`` pairs.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_F16, MOE_Q4B32 = 0, 1, 2, 3
+MOE_OPT_PHASE_EVENTS = 1
+MOE_N_PHASES = 7
+PHASES = ("classify", "dequant_once", "gateup_full", "gateup_splitk",
+          "down_full", "down_splitk", "combine")
+
+STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED",
+                -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
+
+_TORCH_TO_MOE = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16,
+                 torch.float16: MOE_F16}
+
+EXPORTED = (
+    "moe_plan_workspace_bytes", "moe_plan_create", "moe_plan_stats_get",
+    "moe_plan_get_views", "moe_plan_destroy", "moe_options_default",
+    "moe_forward_workspace_bytes", "moe_forward", "moe_dequant_q4",
+    "moe_phase_times", "moe_last_error", "moe_version",
+)
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("swiglu_limit", ctypes.c_float),
+                ("splitk_max_pairs", ctypes.c_float),
+                ("fat_rows", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class Weight(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+class PlanStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "T", "E", "k", "n_shared", "limit", "pairs", "kept", "dropped",
+        "touched", "max_rows", "nonfinite", "thin", "full", "fat")] + [
+        ("drop_fraction", ctypes.c_double)]
+
+
+class PlanViews(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "topk_id", "topk_w", "slot", "tok2pair", "counts", "offsets",
+        "pair_token", "pair_w", "stats")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library(path: str = LIB_PATH):
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with __graft_entry__.build() or "
+            "python mixture_experts_routed_route_amd/build.py")
+    L = ctypes.CDLL(path)
+    vp, sz, i32, i64 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                        ctypes.c_int64)
+    L.moe_plan_workspace_bytes.argtypes = [ctypes.POINTER(PlanDesc)]
+    L.moe_plan_workspace_bytes.restype = sz
+    L.moe_plan_create.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, sz, vp,
+                                  ctypes.POINTER(vp)]
+    L.moe_plan_create.restype = i32
+    L.moe_plan_stats_get.argtypes = [vp, ctypes.POINTER(Options),
+                                     ctypes.POINTER(PlanStats), vp]
+    L.moe_plan_stats_get.restype = i32
+    L.moe_plan_get_views.argtypes = [vp, ctypes.POINTER(PlanViews)]
+    L.moe_plan_get_views.restype = i32
+    L.moe_plan_destroy.argtypes = [vp]
+    L.moe_plan_destroy.restype = None
+    L.moe_options_default.argtypes = [ctypes.POINTER(Options)]
+    L.moe_options_default.restype = None
+    L.moe_forward_workspace_bytes.argtypes = [vp, i32, i32, i32, i32,
+                                              ctypes.POINTER(Options)]
+    L.moe_forward_workspace_bytes.restype = sz
+    L.moe_forward.argtypes = [vp, vp, i32, Weight, Weight, Weight, i32, i32,
+                              vp, i32, vp, sz, ctypes.POINTER(Options), vp]
+    L.moe_forward.restype = i32
+    L.moe_dequant_q4.argtypes = [vp, vp, i64, i64, vp, vp]
+    L.moe_dequant_q4.restype = i32
+    L.moe_phase_times.argtypes = [ctypes.POINTER(ctypes.c_double), i32,
+                                  ctypes.POINTER(i64), i32]
+    L.moe_phase_times.restype = i32
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_version.argtypes = []
+    L.moe_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def moe_last_error() -> str:
+    return library().moe_last_error().decode()
+
+
+def moe_version() -> str:
+    return library().moe_version().decode()
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoeError(status, moe_last_error())
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def moe_options_default() -> Options:
+    o = Options()
+    library().moe_options_default(ctypes.byref(o))
+    return o
+
+
+def make_options(swiglu_limit=None, splitk_max_pairs=None, fat_rows=None,
+                 flags=None) -> Options:
+    o = moe_options_default()
+    if swiglu_limit is not None:
+        o.swiglu_limit = float(swiglu_limit)
+    if splitk_max_pairs is not None:
+        o.splitk_max_pairs = float(splitk_max_pairs)
+    if fat_rows is not None:
+        o.fat_rows = int(fat_rows)
+    if flags is not None:
+        o.flags = int(flags)
+    return o
+
+
+class Plan:
+    """A dispatch plan: host handle + its device workspace (kept alive)."""
+
+    def __init__(self, handle, ws, logits, desc: PlanDesc):
+        self.handle = handle
+        self.ws = ws
+        self.logits = logits
+        self.desc = desc
+        self.T, self.E, self.k = desc.T, desc.E, desc.k
+        self.n_shared = desc.n_shared
+        self.capacity_factor = desc.capacity_factor
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h and _lib is not None:
+            _lib.moe_plan_destroy(h)
+
+
+def moe_plan_workspace_bytes(T, E, k, capacity_factor=0.0, n_shared=0) -> int:
+    d = PlanDesc(T, E, k, n_shared, capacity_factor)
+    return int(library().moe_plan_workspace_bytes(ctypes.byref(d)))
+
+
+def moe_plan_create(logits: torch.Tensor, k: int, capacity_factor: float = 0.0,
+                    n_shared: int = 0) -> Plan:
+    """Route f32 logits [T, E] (device) and build the dispatch plan."""
+    L = library()
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be a 2-D float32 tensor")
+    logits = logits.contiguous()
+    T, E = logits.shape
+    d = PlanDesc(T, E, int(k), int(n_shared), float(capacity_factor))
+    nbytes = L.moe_plan_workspace_bytes(ctypes.byref(d))
+    if nbytes == 0:
+        raise MoeError(MOE_EINVAL, moe_last_error())
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=logits.device)
+    h = ctypes.c_void_p()
+    _check(L.moe_plan_create(ctypes.byref(d), logits.data_ptr(), ws.data_ptr(),
+                             nbytes, _stream(logits.device), ctypes.byref(h)))
+    return Plan(h, ws, logits, d)
+
+
+def moe_plan_stats_get(plan: Plan, options: Options | None = None) -> dict:
+    st = PlanStats()
+    o = options or moe_options_default()
+    _check(library().moe_plan_stats_get(plan.handle, ctypes.byref(o),
+                                        ctypes.byref(st),
+                                        _stream(plan.ws.device)))
+    return {n: getattr(st, n) for n, _ in PlanStats._fields_}
+
+
+def moe_plan_get_views(plan: Plan) -> dict:
+    """torch views of the plan's device arrays (inside its workspace)."""
+    v = PlanViews()
+    _check(library().moe_plan_get_views(plan.handle, ctypes.byref(v)))
+    base = plan.ws.data_ptr()
+    T, k = plan.T, plan.k
+    n_exp = plan.E + plan.n_shared
+
+    def view(ptr, n, dtype):
+        off = ptr - base
+        size = torch.tensor([], dtype=dtype).element_size()
+        return plan.ws[off:off + n * size].view(dtype)
+
+    out = {
+        "topk_id": view(v.topk_id, T * k, torch.int32).view(T, k),
+        "topk_w": view(v.topk_w, T * k, torch.float32).view(T, k),
+        "slot": view(v.slot, T * k, torch.int32).view(T, k),
+        "tok2pair": view(v.tok2pair, T * k, torch.int32).view(T, k),
+        "counts": view(v.counts, n_exp, torch.int32),
+        "offsets": view(v.offsets, n_exp + 1, torch.int32),
+        "stats": view(v.stats, 8, torch.int64),
+    }
+    P = int(out["offsets"][-1].item())
+    out["pair_token"] = view(v.pair_token, P, torch.int32)
+    out["pair_w"] = view(v.pair_w, P, torch.float32)
+    return out
+
+
+def _weight(w, device) -> tuple:
+    if isinstance(w, (tuple, list)):
+        data, scales = w
+        if data.dtype != torch.uint8 or scales.dtype != torch.float16:
+            raise ValueError("4-bit weights are (uint8 data, float16 scales)")
+        if data.device != device or scales.device != device:
+            raise ValueError("weights must be on the input's device")
+        data, scales = data.contiguous(), scales.contiguous()
+        return Weight(MOE_Q4B32, data.data_ptr(), scales.data_ptr()), (data, scales)
+    if w.dtype not in _TORCH_TO_MOE:
+        raise ValueError(f"unsupported weight dtype {w.dtype}")
+    if w.device != device:
+        raise ValueError("weights must be on the input's device")
+    w = w.contiguous()
+    return Weight(_TORCH_TO_MOE[w.dtype], w.data_ptr(), None), (w,)
+
+
+def _dims(w_gate):
+    if isinstance(w_gate, (tuple, list)):
+        data = w_gate[0]
+        return data.shape[1], data.shape[2] * 2      # F, D
+    return w_gate.shape[1], w_gate.shape[2]
+
+
+def moe_forward_workspace_bytes(plan: Plan, D: int, F: int, x_dtype: int,
+                                w_dtype: int, options: Options | None = None) -> int:
+    o = options or moe_options_default()
+    return int(library().moe_forward_workspace_bytes(
+        plan.handle, D, F, x_dtype, w_dtype, ctypes.byref(o)))
+
+
+def moe_forward(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
+                options: Options | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None,
+                y_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """y [T, D] in f32 (the residual stream's dtype) or in x's dtype.
+
+    Pass ``workspace`` (and ``out``) to reuse buffers across calls."""
+    L = library()
+    if x.dtype not in _TORCH_TO_MOE or x.dim() != 2:
+        raise ValueError("x must be a 2-D float32/bfloat16/float16 tensor")
+    x = x.contiguous()
+    T, D = x.shape
+    if T != plan.T:
+        raise ValueError(f"x has {T} tokens, the plan {plan.T}")
+    F, Dw = _dims(w_gate)
+    if Dw != D:
+        raise ValueError(f"weights have d_model {Dw}, x has {D}")
+    o = options or moe_options_default()
+    wg, keep_g = _weight(w_gate, x.device)
+    wu, keep_u = _weight(w_up, x.device)
+    wd, keep_d = _weight(w_down, x.device)
+    xdt = _TORCH_TO_MOE[x.dtype]
+    nbytes = L.moe_forward_workspace_bytes(plan.handle, D, F, xdt, wg.dtype,
+                                           ctypes.byref(o))
+    if nbytes == 0:
+        raise MoeError(MOE_EUNSUPPORTED, moe_last_error())
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty(T, D, dtype=y_dtype, device=x.device)
+    if out.dtype not in (torch.float32, x.dtype) or out.shape != (T, D) \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, D] f32 or x-dtype tensor")
+    _check(L.moe_forward(plan.handle, x.data_ptr(), xdt, wg, wu, wd, D, F,
+                         out.data_ptr(), _TORCH_TO_MOE[out.dtype],
+                         workspace.data_ptr(),
+                         workspace.numel(), ctypes.byref(o),
+                         _stream(x.device)))
+    return out
+
+
+def moe_dequant_q4(data: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """fp16_rne(q * s) of [.., N, K/2] 4-bit rows; returns [.., N, K] fp16."""
+    if data.dtype != torch.uint8 or scales.dtype != torch.float16:
+        raise ValueError("expects uint8 data and float16 scales")
+    data, scales = data.contiguous(), scales.contiguous()
+    K = data.shape[-1] * 2
+    rows = data.numel() // data.shape[-1]
+    out = torch.empty(*data.shape[:-1], K, dtype=torch.float16,
+                      device=data.device)
+    _check(library().moe_dequant_q4(data.data_ptr(), scales.data_ptr(), rows,
+                                    K, out.data_ptr(), _stream(data.device)))
+    return out
+
+
+def moe_phase_times(reset: bool = True) -> tuple:
+    """(ms per phase summed over recorded calls, number of calls)."""
+    ms = (ctypes.c_double * MOE_N_PHASES)()
+    calls = ctypes.c_int64()
+    _check(library().moe_phase_times(ms, MOE_N_PHASES, ctypes.byref(calls),
+                                     1 if reset else 0))
+    return dict(zip(PHASES, list(ms))), int(calls.value)
+
+
+# short aliases
+plan = moe_plan_create
+forward = moe_forward

@@ -1,0 +1,866 @@
+// Forward kernels of the routed MoE layer on gfx950.
+//
+// Per expert: gathered rows of x times W_gate and W_up, clamped SwiGLU, times
+// W_down, each pair's output scaled by its routing weight (mini-AGI PR #4,
+// minagi/pool.py, `experts()`; the clamp from Strata PR #4366, "Approach").
+// Three routes, chosen per expert from its row count on the device:
+//   full    LDS-staged MFMA tile (v_mfma_f32_32x32x16) for experts with many
+//           rows; the fused SwiGLU runs in the gate/up tile's epilogue;
+//   fat     4-bit experts with many rows: weights dequantised once to fp16
+//           (Strata PR #4366: decode once instead of once per 64-row chunk),
+//           then the full tile;
+//   split-K a K-parallel tile for experts holding few pairs (TensorFold PR
+//           #1607): weights stream once from HBM straight into
+//           v_mfma_f32_16x16x32 operands, four waves split K and reduce in LDS
+//           in a fixed order; 4-bit weights are dequantised in registers.
+// The combine gathers each token's weighted pair rows in fixed order, with no
+// atomics.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---- element types ----------------------------------------------------------
+
+struct F16T {
+  using S = _Float16;
+  using V8 = half8;
+  static constexpr int kBytes = 2;
+};
+struct BF16T {
+  using S = __bf16;
+  using V8 = bf16x8;
+  static constexpr int kBytes = 2;
+};
+struct F32T {
+  using S = float;
+  static constexpr int kBytes = 4;
+};
+
+__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <class V>
+__device__ __forceinline__ V as_v8(uint4 u) { return __builtin_bit_cast(V, u); }
+
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// h = silu(min(g, c)) * clamp(u, -c, c); c <= 0: plain silu(g) * u.
+__device__ __forceinline__ float swiglu(float g, float u, float c) {
+  if (c > 0.f) {
+    g = fminf(g, c);
+    u = fminf(fmaxf(u, -c), c);
+  }
+  return g / (1.f + expf(-g)) * u;
+}
+
+// 32 consecutive 4-bit values (16 bytes, low nibble first) times their block
+// scale, as 4 x 8 fp16: fp16 bits 0x6400 | v encode 1024 + v exactly, v =
+// nibble ^ 8; subtracting 1032 leaves the signed value q exactly, and one
+// fp16 multiply gives fp16_rne(q * s).
+__device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
+  const half2v s2 = {s, s};
+  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    const uint32_t x = words[wi] ^ 0x88888888u;
+    const uint32_t lo = x & 0x0F0F0F0Fu;
+    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      // bytes of the result: [lo_b, 0, hi_b, 0] (selector 12 gives zero)
+      const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
+      const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+      half2v h = __builtin_bit_cast(half2v, pr);
+      h = (h + off) * s2;
+      out[wi][2 * b] = h[0];
+      out[wi][2 * b + 1] = h[1];
+    }
+  }
+}
+
+// ---- classify -------------------------------------------------------------
+
+__device__ __forceinline__ int warp_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan over the block (thread order) with the block total.
+__device__ __forceinline__ int block_excl(int v, int* total, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = warp_incl_scan(v);
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  int pre = 0, tot = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+    if (i < wave) pre += sh[i];
+    tot += sh[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return pre + incl - v;
+}
+
+// One block of 1024 threads. Route per expert from its kept rows n:
+//   mode 0 (f32): split-K; mode 1 (bf16/f16): split-K iff n <= S, else full;
+//   mode 2 (q4): fat iff fat_rows > 0 and n >= fat_rows, else split-K.
+// Full/fat experts are ordered largest first (ties: lower index) and cut into
+// kFullBM-row tiles; split-K experts into groups of <= 64 rows, groups of at
+// most 16 rows going to the one-block list.
+__global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
+  __shared__ int cnt[kMaxExperts + 1];
+  __shared__ int rte[kMaxExperts + 1];
+  __shared__ int order[kMaxExperts + 1];
+  __shared__ int sh[16];
+  __shared__ int nfull_sh;
+  const int n = a.n_exp;
+  if (threadIdx.x == 0) nfull_sh = 0;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int c = a.counts[e];
+    int r = kRouteNone;
+    if (c > 0) {
+      if (a.mode == 0) r = kRouteSplitK;
+      else if (a.mode == 1) r = ((double)c <= a.S) ? kRouteSplitK : kRouteFull;
+      else r = (a.fat_rows > 0 && c >= a.fat_rows) ? kRouteFat : kRouteSplitK;
+    }
+    cnt[e] = c;
+    rte[e] = r;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    if (rte[e] < kRouteFull) continue;
+    int rank = 0;
+    const int c = cnt[e];
+    for (int f = 0; f < n; ++f)
+      if (rte[f] >= kRouteFull && (cnt[f] > c || (cnt[f] == c && f < e)))
+        ++rank;
+    order[rank] = e;
+    atomicAdd(&nfull_sh, 1);
+  }
+  __syncthreads();
+  const int nfull = nfull_sh;
+  // full tiles in largest-first order
+  int carry = 0;
+  for (int b = 0; b < nfull; b += blockDim.x) {
+    const int r = b + threadIdx.x;
+    const int e = r < nfull ? order[r] : 0;
+    const int nt = r < nfull ? (cnt[e] + kFullBM - 1) / kFullBM : 0;
+    int tot = 0;
+    const int pre = carry + block_excl(nt, &tot, sh);
+    for (int i = 0; i < nt; ++i) {
+      a.full_tiles[2 * (pre + i)] = e;
+      a.full_tiles[2 * (pre + i) + 1] = i * kFullBM;
+    }
+    carry += tot;
+  }
+  const int n_tiles = carry;
+  // split-K groups and fat slots in expert order
+  int c1 = 0, c4 = 0, cf = 0;
+  for (int b = 0; b < n; b += blockDim.x) {
+    const int e = b + threadIdx.x;
+    int g1 = 0, g4 = 0, fat = 0, c = 0;
+    if (e < n) {
+      c = cnt[e];
+      if (rte[e] == kRouteSplitK) {
+        const int ng = (c + kSkRows - 1) / kSkRows;
+        const int last = c - (ng - 1) * kSkRows;
+        g4 = (ng - 1) + (last > 16 ? 1 : 0);
+        g1 = last <= 16 ? 1 : 0;
+      }
+      fat = rte[e] == kRouteFat ? 1 : 0;
+    }
+    int t1 = 0, t4 = 0, tf = 0;
+    const int p1 = c1 + block_excl(g1, &t1, sh);
+    const int p4 = c4 + block_excl(g4, &t4, sh);
+    const int pf = cf + block_excl(fat, &tf, sh);
+    if (e < n) {
+      if (rte[e] == kRouteSplitK) {
+        const int ng = (c + kSkRows - 1) / kSkRows;
+        for (int g = 0; g < ng; ++g) {
+          const int row0 = g * kSkRows;
+          const int rows = min(kSkRows, c - row0);
+          int32_t* dst = (rows <= 16) ? a.sk1 + 4 * p1
+                                      : a.sk4 + 4 * (p4 + g);
+          dst[0] = e;
+          dst[1] = row0;
+          dst[2] = rows;
+          dst[3] = 0;
+        }
+      }
+      a.fat_slot[e] = fat ? pf : -1;
+      if (fat) a.fat_list[pf] = e;
+    }
+    c1 += t1;
+    c4 += t4;
+    cf += tf;
+  }
+  if (threadIdx.x == 0) {
+    a.meta[kMetaFullTiles] = n_tiles;
+    a.meta[kMetaSk1] = c1;
+    a.meta[kMetaSk4] = c4;
+    a.meta[kMetaFat] = cf;
+  }
+}
+
+hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(classify_kernel, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---- dequantise once --------------------------------------------------------
+
+__device__ __forceinline__ void dequant_unit(const uint8_t* q, const uint16_t* sc,
+                                             _Float16* out, size_t row, int kb,
+                                             int K) {
+  const uint4 raw = ldg16(q + row * (size_t)(K / 2) + (size_t)kb * 16);
+  const uint16_t sb = sc[row * (size_t)(K / 32) + kb];
+  half8 h[4];
+  dequant32(raw, __builtin_bit_cast(_Float16, sb), h);
+  uint4* dst = reinterpret_cast<uint4*>(out + row * (size_t)K + (size_t)kb * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = __builtin_bit_cast(uint4, h[i]);
+}
+
+// Fat experts: slot s of the staging buffer holds expert fat_list[s]'s
+// [rows, K] matrix as fp16. Grid-stride over (slot, row, 32-value block).
+__global__ __launch_bounds__(256) void dequant_fat_kernel(
+    const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
+    _Float16* __restrict__ out, int rows, int K,
+    const int32_t* __restrict__ fat_list, const int32_t* __restrict__ meta) {
+  const int nfat = meta[kMetaFat];
+  const int kbs = K / 32;
+  const size_t per = (size_t)rows * kbs;
+  const size_t total = per * (size_t)nfat;
+  for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < total;
+       u += (size_t)gridDim.x * blockDim.x) {
+    const int slot = (int)(u / per);
+    const size_t rem = u - (size_t)slot * per;
+    const int row = (int)(rem / kbs);
+    const int kb = (int)(rem - (size_t)row * kbs);
+    const size_t e = (size_t)fat_list[slot];
+    const uint4 raw = ldg16(q + (e * rows + row) * (size_t)(K / 2) + (size_t)kb * 16);
+    const uint16_t sb = sc[(e * rows + row) * (size_t)kbs + kb];
+    half8 h[4];
+    dequant32(raw, __builtin_bit_cast(_Float16, sb), h);
+    uint4* dst = reinterpret_cast<uint4*>(
+        out + ((size_t)slot * rows + row) * (size_t)K + (size_t)kb * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = __builtin_bit_cast(uint4, h[i]);
+  }
+}
+
+__global__ __launch_bounds__(256) void dequant_rows_kernel(
+    const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
+    _Float16* __restrict__ out, int64_t rows, int K) {
+  const int kbs = K / 32;
+  const size_t total = (size_t)rows * kbs;
+  for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < total;
+       u += (size_t)gridDim.x * blockDim.x) {
+    const size_t row = u / kbs;
+    dequant_unit(q, sc, out, row, (int)(u - row * kbs), K);
+  }
+}
+
+hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
+                              int rows, int K, const int32_t* fat_list,
+                              const int32_t* meta, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(dequant_fat_kernel, dim3(grid), dim3(256), 0, s,
+                     (const uint8_t*)q, (const uint16_t*)sc, (_Float16*)out,
+                     rows, K, fat_list, meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
+                               int64_t rows, int K, hipStream_t s) {
+  const size_t units = (size_t)rows * (K / 32);
+  const int grid = (int)std::min<size_t>((units + 255) / 256, 65536);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_rows_kernel, dim3(grid), dim3(256), 0, s,
+                     (const uint8_t*)q, (const uint16_t*)sc, (_Float16*)out,
+                     rows, K);
+  return hipGetLastError();
+}
+
+// ---- full MFMA tile -------------------------------------------------------------
+//
+// Block = 4 waves (2 x 2), tile kFullBM x kFullBN, K staged kFullBK at a time
+// through two LDS buffers. Gate/up: the 128 B-rows of a tile are, per wave
+// column wn, 32 rows of W_gate then 32 rows of W_up for the same 32 output
+// features, so each lane holds g and u of one (row, feature) in matching
+// accumulators. LDS rows are 128 bytes; 16-byte chunk c of row r sits at
+// chunk c ^ ((r >> 1) & 7), which keeps both the staging writes and the
+// MFMA operand reads free of bank conflicts.
+
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+template <class TT, int MODE>
+__global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
+  using S = typename TT::S;
+  using V8 = typename TT::V8;
+  constexpr int BM = kFullBM, BN = kFullBN, BK = kFullBK;
+  constexpr int STAGE = (BM + BN) * BK * 2;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = a.K;
+  const int N = a.N;
+  const int nk = K / BK;
+  const int NNB = MODE == 0 ? N / 64 : N / 128;
+  const int n_items = a.meta[a.meta_index] * NNB;
+  const int c16 = tid & 7;        // this thread's 16-byte chunk of a row
+  const int rbase = tid >> 3;     // rows rbase + 32 i
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int ti = item / NNB;
+    const int nb = item - ti * NNB;
+    const int e = a.list[2 * ti];
+    const int row0 = a.list[2 * ti + 1];
+    const int off = a.offsets[e];
+    const int ne = a.offsets[e + 1] - off;
+    const int slot = a.fat_slot ? a.fat_slot[e] : -1;
+    const char* arow[4];
+    const char* brow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rbase + 32 * i;
+      const int rr = min(row0 + r, ne - 1);
+      if (MODE == 0) {
+        const int tok = a.pair_token[off + rr];
+        arow[i] = (const char*)a.A + (size_t)tok * K * 2;
+      } else {
+        arow[i] = (const char*)a.A + (size_t)(off + rr) * K * 2;
+      }
+      int brow_idx;
+      const void* bbase;
+      if (MODE == 0) {
+        const int half = r >> 6, rr2 = r & 63;
+        const int mat = rr2 >> 5;
+        brow_idx = nb * 64 + half * 32 + (rr2 & 31);
+        bbase = slot >= 0 ? (mat ? a.S1 : a.S0) : (mat ? a.B1 : a.B0);
+      } else {
+        brow_idx = nb * 128 + r;
+        bbase = slot >= 0 ? a.S0 : a.B0;
+      }
+      const size_t eix = slot >= 0 ? (size_t)slot : (size_t)e;
+      brow[i] = (const char*)bbase + ((eix * N + brow_idx) * (size_t)K) * 2;
+    }
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+    uint4 ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = ldg16(arow[i] + c16 * 16);
+      rb[i] = ldg16(brow[i] + c16 * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rbase + 32 * i;
+      *reinterpret_cast<uint4*>(smem + swz(r, c16)) = ra[i];
+      *reinterpret_cast<uint4*>(smem + BM * 128 + swz(r, c16)) = rb[i];
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) {
+        const int kb = (kt + 1) * BK * 2 + c16 * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ra[i] = ldg16(arow[i] + kb);
+          rb[i] = ldg16(brow[i] + kb);
+        }
+      }
+      const char* As = smem + cur * STAGE;
+      const char* Bs = As + BM * 128;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int ch = ks * 2 + (lane >> 5);
+        V8 av[2], bv[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const int r = wm * 64 + mi * 32 + (lane & 31);
+          av[mi] = as_v8<V8>(*reinterpret_cast<const uint4*>(As + swz(r, ch)));
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int r = wn * 64 + ni * 32 + (lane & 31);
+          bv[ni] = as_v8<V8>(*reinterpret_cast<const uint4*>(Bs + swz(r, ch)));
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = mfma32(av[mi], bv[ni], acc[mi][ni]);
+      }
+      if (kt + 1 < nk) {
+        char* Ad = smem + (cur ^ 1) * STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rbase + 32 * i;
+          *reinterpret_cast<uint4*>(Ad + swz(r, c16)) = ra[i];
+          *reinterpret_cast<uint4*>(Ad + BM * 128 + swz(r, c16)) = rb[i];
+        }
+      }
+      __syncthreads();
+    }
+
+    // epilogue: 32x32 accumulator element r of lane l is row
+    // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+    const int j = lane & 31;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int grow = row0 + row;
+        if (grow >= ne) continue;
+        const size_t prow = (size_t)(off + grow);
+        if (MODE == 0) {
+          const int f = nb * 64 + wn * 32 + j;
+          const float h = swiglu(acc[mi][0][r], acc[mi][1][r], a.clamp);
+          reinterpret_cast<S*>(a.out)[prow * N + f] = (S)h;
+        } else {
+          const float pw = a.pair_w[prow];
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) {
+            const int d = nb * 128 + wn * 64 + ni * 32 + j;
+            reinterpret_cast<float*>(a.out)[prow * N + d] = acc[mi][ni][r] * pw;
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
+                            hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (xdt == MOE_F16) {
+    if (a.mode == 0)
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 0>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 1>), dim3(grid), dim3(256), 0, s, a);
+  } else if (xdt == MOE_BF16) {
+    if (a.mode == 0)
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 0>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---- split-K tile -----------------------------------------------------------------
+//
+// Block = 4 waves on one item (split-K group of <= 16 RB rows, 64 output
+// columns); wave w takes a contiguous quarter of K. Lane (n = l % 16,
+// q = l / 16) streams, per super-step of KSS values of K, a contiguous
+// 32 (16-bit) or 16 (f32) values of its weight row and of its A row, and
+// MFMA i uses slice i of them, so every MFMA's K values are matched between
+// A and B. Gate/up columns: blocks cb = 0..3 are W_gate f0..f0+15, W_up
+// f0..f0+15, W_gate f0+16.., W_up f0+16.. for f0 = 32 nb, so g and u of one
+// feature land in matching accumulators of one lane.
+
+// 16-bit activations (bf16/f16), dense or 4-bit weights.
+template <class TT, int WQ, int RB, int MODE>
+__device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
+                                              int NNB, float* red) {
+  using S = typename TT::S;
+  using V8 = typename TT::V8;
+  constexpr int KSS = 128;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int K = a.K, N = a.N;
+  const int g = item / NNB;
+  const int nb = item - g * NNB;
+  const int e = a.list[4 * g];
+  const int row0 = a.list[4 * g + 1];
+  const int nrows = a.list[4 * g + 2];
+  const int off = a.offsets[e];
+  const char* ap[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = row0 + min(rb * 16 + n, nrows - 1);
+    if (MODE == 0)
+      ap[rb] = (const char*)a.A + (size_t)a.pair_token[off + rr] * K * 2;
+    else
+      ap[rb] = (const char*)a.A + (size_t)(off + rr) * K * 2;
+  }
+  const char* bp[4];
+  const uint16_t* bsp[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    int row;
+    const void* base;
+    const void* sbase;
+    if (MODE == 0) {
+      row = nb * 32 + (cb >> 1) * 16 + n;
+      base = (cb & 1) ? a.B1 : a.B0;
+      sbase = (cb & 1) ? a.B1s : a.B0s;
+    } else {
+      row = nb * 64 + cb * 16 + n;
+      base = a.B0;
+      sbase = a.B0s;
+    }
+    const size_t wrow = (size_t)e * N + row;
+    if (WQ) {
+      bp[cb] = (const char*)base + wrow * (size_t)(K / 2);
+      bsp[cb] = (const uint16_t*)sbase + wrow * (size_t)(K / 32);
+    } else {
+      bp[cb] = (const char*)base + wrow * (size_t)K * 2;
+      bsp[cb] = nullptr;
+    }
+  }
+  floatx4 acc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int nss = K / KSS;
+  const int s0 = wave * nss / 4, s1 = (wave + 1) * nss / 4;
+  for (int s = s0; s < s1; ++s) {
+    const int k0 = s * KSS + q * 32;
+    V8 av[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[rb][i] = as_v8<V8>(ldg16(ap[rb] + (size_t)k0 * 2 + i * 16));
+    V8 bv[4][4];
+    if (WQ) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint4 raw = ldg16(bp[cb] + k0 / 2);
+        const uint16_t sb = bsp[cb][k0 / 32];
+        half8 h[4];
+        dequant32(raw, __builtin_bit_cast(_Float16, sb), h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[cb][i] = __builtin_bit_cast(V8, h[i]);
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[cb][i] = as_v8<V8>(ldg16(bp[cb] + (size_t)k0 * 2 + i * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(av[rb][i], bv[cb][i], acc[rb][cb]);
+  }
+
+  // fixed-order reduction over the four K quarters: ((w0 + w1) + w2) + w3
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* p = red + ((rb * 4 + cb) * 4 + r) * 64 + lane;
+            *p = (w == 0) ? acc[rb][cb][r] : *p + acc[rb][cb][r];
+          }
+    }
+    __syncthreads();
+  }
+  if (wave == 3) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[rb][cb][r] = red[((rb * 4 + cb) * 4 + r) * 64 + lane] + acc[rb][cb][r];
+    // 16x16 accumulator element r of lane l is row 4 (l / 16) + r, column l % 16
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rb * 16 + q * 4 + r;
+        if (row >= nrows) continue;
+        const size_t prow = (size_t)(off + row0 + row);
+        if (MODE == 0) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int f = nb * 32 + pr * 16 + n;
+            const float h = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
+            reinterpret_cast<S*>(a.out)[prow * N + f] = (S)h;
+          }
+        } else {
+          const float pw = a.pair_w[prow];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const int d = nb * 64 + cb * 16 + n;
+            reinterpret_cast<float*>(a.out)[prow * N + d] = acc[rb][cb][r] * pw;
+          }
+        }
+      }
+  }
+  __syncthreads();
+}
+
+// f32 activations and weights: v_mfma_f32_16x16x4f32, super-step of 64.
+template <int RB, int MODE>
+__device__ __forceinline__ void splitk_body32(const GemmArgs& a, int item,
+                                              int NNB, float* red) {
+  constexpr int KSS = 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int K = a.K, N = a.N;
+  const int g = item / NNB;
+  const int nb = item - g * NNB;
+  const int e = a.list[4 * g];
+  const int row0 = a.list[4 * g + 1];
+  const int nrows = a.list[4 * g + 2];
+  const int off = a.offsets[e];
+  const float* ap[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = row0 + min(rb * 16 + n, nrows - 1);
+    if (MODE == 0)
+      ap[rb] = (const float*)a.A + (size_t)a.pair_token[off + rr] * K;
+    else
+      ap[rb] = (const float*)a.A + (size_t)(off + rr) * K;
+  }
+  const float* bp[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    int row;
+    const void* base;
+    if (MODE == 0) {
+      row = nb * 32 + (cb >> 1) * 16 + n;
+      base = (cb & 1) ? a.B1 : a.B0;
+    } else {
+      row = nb * 64 + cb * 16 + n;
+      base = a.B0;
+    }
+    bp[cb] = (const float*)base + ((size_t)e * N + row) * K;
+  }
+  floatx4 acc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int nss = K / KSS;
+  const int s0 = wave * nss / 4, s1 = (wave + 1) * nss / 4;
+  for (int s = s0; s < s1; ++s) {
+    const int k0 = s * KSS + q * 16;
+    float av[RB][16], bv[4][16];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(ap[rb] + k0 + 4 * i);
+        av[rb][4 * i] = v.x; av[rb][4 * i + 1] = v.y;
+        av[rb][4 * i + 2] = v.z; av[rb][4 * i + 3] = v.w;
+      }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(bp[cb] + k0 + 4 * i);
+        bv[cb][4 * i] = v.x; bv[cb][4 * i + 1] = v.y;
+        bv[cb][4 * i + 2] = v.z; bv[cb][4 * i + 3] = v.w;
+      }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16f32(av[rb][i], bv[cb][i], acc[rb][cb]);
+  }
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* p = red + ((rb * 4 + cb) * 4 + r) * 64 + lane;
+            *p = (w == 0) ? acc[rb][cb][r] : *p + acc[rb][cb][r];
+          }
+    }
+    __syncthreads();
+  }
+  if (wave == 3) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[rb][cb][r] = red[((rb * 4 + cb) * 4 + r) * 64 + lane] + acc[rb][cb][r];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rb * 16 + q * 4 + r;
+        if (row >= nrows) continue;
+        const size_t prow = (size_t)(off + row0 + row);
+        float* out = reinterpret_cast<float*>(a.out);
+        if (MODE == 0) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int f = nb * 32 + pr * 16 + n;
+            out[prow * N + f] = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
+          }
+        } else {
+          const float pw = a.pair_w[prow];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const int d = nb * 64 + cb * 16 + n;
+            out[prow * N + d] = acc[rb][cb][r] * pw;
+          }
+        }
+      }
+  }
+  __syncthreads();
+}
+
+template <class TT, int WQ, int RB, int MODE>
+__global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
+  __shared__ float red[RB * 4 * 4 * 64];
+  const int NNB = MODE == 0 ? a.N / 32 : a.N / 64;
+  const int n_items = a.meta[a.meta_index] * NNB;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    if constexpr (TT::kBytes == 4)
+      splitk_body32<RB, MODE>(a, item, NNB, red);
+    else
+      splitk_body16<TT, WQ, RB, MODE>(a, item, NNB, red);
+  }
+}
+
+template <class TT, int WQ, int RB>
+static hipError_t splitk_mode(const GemmArgs& a, int grid, hipStream_t s) {
+  if (a.mode == 0)
+    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 0>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 1>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class TT, int WQ>
+static hipError_t splitk_rb(const GemmArgs& a, int rb, int grid, hipStream_t s) {
+  return rb == 1 ? splitk_mode<TT, WQ, 1>(a, grid, s) : splitk_mode<TT, WQ, 4>(a, grid, s);
+}
+
+hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
+                              int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (xdt == MOE_F32 && wdt == MOE_F32) return splitk_rb<F32T, 0>(a, rb, grid, s);
+  if (xdt == MOE_BF16 && wdt == MOE_BF16) return splitk_rb<BF16T, 0>(a, rb, grid, s);
+  if (xdt == MOE_F16 && wdt == MOE_F16) return splitk_rb<F16T, 0>(a, rb, grid, s);
+  if (xdt == MOE_F16 && wdt == MOE_Q4B32) {
+    // the down stage reads H (fp16) as A in every case
+    return splitk_rb<F16T, 1>(a, rb, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---- combine ------------------------------------------------------------------------
+//
+// y[t, d..d+7] = sum over j of Ypair[tok2pair[t, j], d..d+7] (j ascending,
+// dropped pairs skipped) + the shared expert's row. Ypair holds each kept
+// pair's weighted output in f32; the sum is f32 and rounded once to y's
+// dtype. Each output is written by one thread: no atomics.
+
+template <class S>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ ypair, const int32_t* __restrict__ tok2pair,
+    const int32_t* __restrict__ offsets, int T, int D, int k, int n_shared,
+    int E, S* __restrict__ y) {
+  const int per_row = D / 8;
+  const size_t total = (size_t)T * per_row;
+  const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int t = (int)(idx / per_row);
+  const int d = (int)(idx - (size_t)t * per_row) * 8;
+  float4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+  auto add_row = [&](size_t p) {
+    const float4* src = reinterpret_cast<const float4*>(ypair + p * D + d);
+    const float4 a = src[0], b = src[1];
+    lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+    hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+  };
+  for (int j = 0; j < k; ++j) {
+    const int p = tok2pair[(size_t)t * k + j];
+    if (p >= 0) add_row((size_t)p);
+  }
+  if (n_shared) add_row((size_t)(offsets[E] + t));
+  S* out = y + (size_t)t * D + d;
+  if constexpr (sizeof(S) == 4) {
+    reinterpret_cast<float4*>(out)[0] = lo;
+    reinterpret_cast<float4*>(out)[1] = hi;
+  } else {
+    typedef S s8 __attribute__((ext_vector_type(8)));
+    s8 o;
+    o[0] = (S)lo.x; o[1] = (S)lo.y; o[2] = (S)lo.z; o[3] = (S)lo.w;
+    o[4] = (S)hi.x; o[5] = (S)hi.y; o[6] = (S)hi.z; o[7] = (S)hi.w;
+    *reinterpret_cast<s8*>(out) = o;
+  }
+}
+
+hipError_t launch_combine(const void* ypair, const int32_t* tok2pair,
+                          const int32_t* offsets, int T, int D, int k,
+                          int n_shared, int E, int ydt, void* y,
+                          hipStream_t s) {
+  const size_t total = (size_t)T * (D / 8);
+  if (total == 0) return hipSuccess;
+  const int grid = (int)((total + 255) / 256);
+  const float* yp = (const float*)ypair;
+  if (ydt == MOE_F32)
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, s,
+                       yp, tok2pair, offsets, T, D, k, n_shared, E, (float*)y);
+  else if (ydt == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<__bf16>, dim3(grid), dim3(256), 0, s,
+                       yp, tok2pair, offsets, T, D, k, n_shared, E, (__bf16*)y);
+  else
+    hipLaunchKernelGGL(combine_kernel<_Float16>, dim3(grid), dim3(256), 0, s,
+                       yp, tok2pair, offsets, T, D, k, n_shared, E, (_Float16*)y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

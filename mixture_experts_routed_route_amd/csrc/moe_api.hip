@@ -1,0 +1,578 @@
+// C ABI of the routed MoE layer: host-side validation, workspace layouts
+// and launch sequencing. Every argument is checked before the first launch;
+// every launch goes to the caller's stream; nothing here synchronises except
+// moe_plan_stats_get and moe_phase_times.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_EHIP, "%s: %s (%s)", where, hipGetErrorName(e),
+              hipGetErrorString(e));
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline int xbytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+struct PlanLayout {
+  size_t ids, w, slot, tok2pair, hist, total, counts, offsets, pair_token,
+      pair_w, stats, bytes;
+  int NC;
+};
+
+bool desc_ok(const moe_plan_desc* d, std::string* why) {
+  char buf[256];
+  if (!d) { *why = "desc is NULL"; return false; }
+  if (d->E < 1 || d->E > kMaxExperts) {
+    snprintf(buf, sizeof buf, "E=%d outside 1..%d", d->E, kMaxExperts);
+    *why = buf; return false;
+  }
+  if (d->k < 1 || d->k > d->E) {
+    snprintf(buf, sizeof buf, "k=%d outside 1..E=%d", d->k, d->E);
+    *why = buf; return false;
+  }
+  if (d->T < 0) { *why = "T < 0"; return false; }
+  if (d->n_shared != 0 && d->n_shared != 1) { *why = "n_shared not 0 or 1"; return false; }
+  if (!std::isfinite(d->capacity_factor) || d->capacity_factor < 0.f) {
+    snprintf(buf, sizeof buf, "capacity_factor=%g must be finite and >= 0",
+             (double)d->capacity_factor);
+    *why = buf; return false;
+  }
+  if ((int64_t)d->T * (d->k + 1) >= ((int64_t)1 << 31)) {
+    *why = "T*(k+1) must be below 2^31"; return false;
+  }
+  return true;
+}
+
+PlanLayout plan_layout(const moe_plan_desc& d) {
+  PlanLayout L{};
+  const size_t Tk = (size_t)d.T * d.k;
+  const size_t P = Tk + (size_t)d.n_shared * d.T;
+  L.NC = (d.T + kChunk - 1) / kChunk;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  L.ids = take(Tk * 4);
+  L.w = take(Tk * 4);
+  L.slot = take(Tk * 4);
+  L.tok2pair = take(Tk * 4);
+  L.hist = take((size_t)L.NC * (d.E + 1) * 4);
+  L.total = take((size_t)(d.E + 1) * 4);
+  L.counts = take((size_t)(d.E + 1) * 4);
+  L.offsets = take((size_t)(d.E + 2) * 4);
+  L.pair_token = take(P * 4 + 4);
+  L.pair_w = take(P * 4 + 4);
+  L.stats = take(8 * 8);
+  L.bytes = o;
+  return L;
+}
+
+int64_t capacity_limit(const moe_plan_desc& d) {
+  if (d.capacity_factor == 0.f) return -1;
+  const double fair = (double)d.capacity_factor * (double)d.T * d.k / d.E;
+  const double f = std::floor(fair);
+  if (f < 1.0) return 1;
+  if (f > 2e9) return -1;   // beyond any count: same as no cap
+  return (int64_t)f;
+}
+
+struct DevInfo { int ncu = 0; };
+
+moe_status device_info(int* dev, DevInfo* info) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static std::mutex mu;
+  static std::vector<int> ncu_cache;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)ncu_cache.size() <= *dev) ncu_cache.resize(*dev + 1, 0);
+  if (ncu_cache[*dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, *dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    ncu_cache[*dev] = n > 0 ? n : 1;
+  }
+  info->ncu = ncu_cache[*dev];
+  return MOE_OK;
+}
+
+// ---- phase events ---------------------------------------------------------
+
+struct PhaseRecord {
+  hipEvent_t ev[2 * MOE_N_PHASES];
+  bool used[MOE_N_PHASES];
+};
+std::mutex g_ev_mu;
+std::vector<PhaseRecord> g_records;
+size_t g_records_used = 0;
+
+PhaseRecord* acquire_record(moe_status* st) {
+  std::lock_guard<std::mutex> lock(g_ev_mu);
+  if (g_records_used == g_records.size()) {
+    PhaseRecord r{};
+    for (int i = 0; i < 2 * MOE_N_PHASES; ++i) {
+      hipError_t e = hipEventCreate(&r.ev[i]);
+      if (e != hipSuccess) {
+        *st = hip_fail(e, "hipEventCreate");
+        return nullptr;
+      }
+    }
+    g_records.push_back(r);
+  }
+  PhaseRecord* r = &g_records[g_records_used++];
+  for (int i = 0; i < MOE_N_PHASES; ++i) r->used[i] = false;
+  return r;
+}
+
+struct PhaseScope {
+  PhaseRecord* rec;
+  int phase;
+  hipStream_t s;
+  PhaseScope(PhaseRecord* r, int p, hipStream_t st) : rec(r), phase(p), s(st) {
+    if (rec) hipEventRecord(rec->ev[2 * phase], s);
+  }
+  ~PhaseScope() {
+    if (rec) {
+      hipEventRecord(rec->ev[2 * phase + 1], s);
+      rec->used[phase] = true;
+    }
+  }
+};
+
+struct FwdLayout {
+  size_t H, Y, full_tiles, sk1, sk4, fat_slot, fat_list, meta, stg_g, stg_u,
+      stg_d, bytes;
+  int cap_tiles, cap_sk1, cap_sk4, max_fat, fat_rows;
+  bool can_full, can_sk1, can_sk4, can_fat;
+};
+
+bool dtypes_ok(int xdt, int wdt) {
+  return (xdt == MOE_F32 && wdt == MOE_F32) ||
+         (xdt == MOE_BF16 && wdt == MOE_BF16) ||
+         (xdt == MOE_F16 && wdt == MOE_F16) ||
+         (xdt == MOE_F16 && wdt == MOE_Q4B32);
+}
+
+int effective_fat_rows(const moe_options& o) {
+  if (o.fat_rows <= 0) return 0;
+  return std::max(o.fat_rows, 17);
+}
+
+FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
+                     const moe_options& o) {
+  FwdLayout L{};
+  const int64_t Pmax = (int64_t)d.T * d.k + (int64_t)d.n_shared * d.T;
+  const int n_exp = d.E + d.n_shared;
+  L.cap_tiles = n_exp + (int)(Pmax / kFullBM) + 1;
+  L.cap_sk1 = n_exp;
+  L.cap_sk4 = n_exp + (int)(Pmax / kSkRows) + 1;
+  L.fat_rows = wdt == MOE_Q4B32 ? effective_fat_rows(o) : 0;
+  L.max_fat = 0;
+  if (L.fat_rows > 0)
+    L.max_fat = (int)std::min<int64_t>(n_exp, Pmax / L.fat_rows);
+  if (wdt == MOE_F32) {
+    L.can_full = false; L.can_sk1 = true; L.can_sk4 = true; L.can_fat = false;
+  } else if (wdt == MOE_Q4B32) {
+    L.can_fat = L.max_fat > 0;
+    L.can_full = L.can_fat;
+    L.can_sk1 = true;
+    L.can_sk4 = L.fat_rows == 0 || L.fat_rows > 17;
+  } else {
+    const double S = (double)o.splitk_max_pairs;
+    L.can_fat = false;
+    L.can_full = S < (double)Pmax;
+    L.can_sk1 = S >= 1.0;
+    L.can_sk4 = S > 16.0;
+  }
+  const int xb = xbytes(xdt);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  L.H = take((size_t)Pmax * F * xb + 16);
+  L.Y = take((size_t)Pmax * D * 4 + 16);   // Ypair in f32
+  L.full_tiles = take((size_t)L.cap_tiles * 8);
+  L.sk1 = take((size_t)L.cap_sk1 * 16);
+  L.sk4 = take((size_t)L.cap_sk4 * 16);
+  L.fat_slot = take((size_t)n_exp * 4);
+  L.fat_list = take((size_t)n_exp * 4);
+  L.meta = take(kMetaCount * 4);
+  L.stg_g = take((size_t)L.max_fat * F * D * 2);
+  L.stg_u = take((size_t)L.max_fat * F * D * 2);
+  L.stg_d = take((size_t)L.max_fat * D * F * 2);
+  L.bytes = off;
+  return L;
+}
+
+moe_options defaults() {
+  moe_options o;
+  o.swiglu_limit = 7.0f;
+  o.splitk_max_pairs = 4.0f;
+  o.fat_rows = 64;
+  o.flags = 0;
+  return o;
+}
+
+bool weight_ok(const moe_weight& w, int wdt, std::string* why, const char* name) {
+  char buf[200];
+  if (w.dtype != wdt) {
+    snprintf(buf, sizeof buf, "%s dtype %d differs from w_gate's %d", name, w.dtype, wdt);
+    *why = buf; return false;
+  }
+  if (!w.data) { snprintf(buf, sizeof buf, "%s data is NULL", name); *why = buf; return false; }
+  if (!aligned16(w.data)) { snprintf(buf, sizeof buf, "%s data not 16-byte aligned", name); *why = buf; return false; }
+  if (wdt == MOE_Q4B32) {
+    if (!w.scales) { snprintf(buf, sizeof buf, "%s scales NULL for Q4B32", name); *why = buf; return false; }
+    if ((reinterpret_cast<uintptr_t>(w.scales) & 1u) != 0) {
+      snprintf(buf, sizeof buf, "%s scales not 2-byte aligned", name); *why = buf; return false;
+    }
+  }
+  return true;
+}
+
+}  // namespace
+
+struct moe_plan {
+  moe_plan_desc desc;
+  int64_t limit;
+  char* ws;
+  PlanLayout L;
+};
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+void moe_options_default(moe_options* opt) {
+  if (opt) *opt = defaults();
+}
+
+size_t moe_plan_workspace_bytes(const moe_plan_desc* desc) {
+  std::string why;
+  if (!desc_ok(desc, &why)) { fail(MOE_EINVAL, "%s", why.c_str()); return 0; }
+  return plan_layout(*desc).bytes;
+}
+
+moe_status moe_plan_create(const moe_plan_desc* desc, const float* logits,
+                           void* ws, size_t ws_bytes, void* stream,
+                           moe_plan** out) {
+  std::string why;
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!desc_ok(desc, &why)) return fail(MOE_EINVAL, "%s", why.c_str());
+  if (desc->T > 0 && !logits) return fail(MOE_EINVAL, "logits is NULL");
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (!aligned16(logits) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(MOE_EINVAL, "logits must be 16-byte and ws 256-byte aligned");
+  const PlanLayout L = plan_layout(*desc);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_EWORKSPACE, "plan workspace %zu bytes < %zu needed",
+                ws_bytes, L.bytes);
+  int dev;
+  DevInfo info;
+  moe_status st = device_info(&dev, &info);
+  if (st != MOE_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* b = static_cast<char*>(ws);
+  const moe_plan_desc& d = *desc;
+  const int64_t limit = capacity_limit(d);
+  hipError_t e;
+  if (L.NC > 0) {
+    e = launch_route_hist(logits, d.T, d.E, d.k, (int32_t*)(b + L.ids),
+                          (float*)(b + L.w), (int32_t*)(b + L.hist), s);
+    if (e != hipSuccess) return hip_fail(e, "route kernel");
+  }
+  e = launch_scan((int32_t*)(b + L.hist), L.NC, d.T, d.E, d.k, d.n_shared,
+                  limit, (int32_t*)(b + L.total), (int32_t*)(b + L.counts),
+                  (int32_t*)(b + L.offsets), (int64_t*)(b + L.stats), s);
+  if (e != hipSuccess) return hip_fail(e, "scan kernel");
+  if (L.NC > 0) {
+    e = launch_permute((const int32_t*)(b + L.ids), (const float*)(b + L.w),
+                       (const int32_t*)(b + L.hist),
+                       (const int32_t*)(b + L.offsets), d.T, d.E, d.k,
+                       d.n_shared, limit, (int32_t*)(b + L.slot),
+                       (int32_t*)(b + L.tok2pair), (int32_t*)(b + L.pair_token),
+                       (float*)(b + L.pair_w), s);
+    if (e != hipSuccess) return hip_fail(e, "permute kernel");
+  }
+  moe_plan* p = new (std::nothrow) moe_plan;
+  if (!p) return fail(MOE_EINVAL, "out of host memory");
+  p->desc = d;
+  p->limit = limit;
+  p->ws = b;
+  p->L = L;
+  *out = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan* plan) { delete plan; }
+
+moe_status moe_plan_get_views(const moe_plan* p, moe_plan_views* v) {
+  if (!p || !v) return fail(MOE_EINVAL, "NULL plan or views");
+  char* b = p->ws;
+  v->topk_id = (const int32_t*)(b + p->L.ids);
+  v->topk_w = (const float*)(b + p->L.w);
+  v->slot = (const int32_t*)(b + p->L.slot);
+  v->tok2pair = (const int32_t*)(b + p->L.tok2pair);
+  v->counts = (const int32_t*)(b + p->L.counts);
+  v->offsets = (const int32_t*)(b + p->L.offsets);
+  v->pair_token = (const int32_t*)(b + p->L.pair_token);
+  v->pair_w = (const float*)(b + p->L.pair_w);
+  v->stats = (const int64_t*)(b + p->L.stats);
+  return MOE_OK;
+}
+
+moe_status moe_plan_stats_get(const moe_plan* p, const moe_options* opt,
+                              moe_plan_stats* out, void* stream) {
+  if (!p || !out) return fail(MOE_EINVAL, "NULL plan or stats");
+  const moe_options o = opt ? *opt : defaults();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const moe_plan_desc& d = p->desc;
+  int64_t st[8];
+  std::vector<int32_t> counts((size_t)d.E + d.n_shared);
+  hipError_t e = hipMemcpyAsync(st, p->ws + p->L.stats, sizeof st,
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(counts.data(), p->ws + p->L.counts,
+                       counts.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "moe_plan_stats_get");
+  moe_plan_stats r{};
+  r.T = d.T; r.E = d.E; r.k = d.k; r.n_shared = d.n_shared;
+  r.limit = p->limit;
+  r.pairs = (int64_t)d.T * d.k;
+  r.dropped = st[0];
+  r.kept = st[1];
+  r.nonfinite = st[2];
+  r.touched = st[3];
+  r.max_rows = st[4];
+  r.drop_fraction = r.pairs ? (double)r.dropped / (double)r.pairs : 0.0;
+  const int fr = effective_fat_rows(o);
+  for (int e2 = 0; e2 < d.E; ++e2) {
+    const int c = counts[e2];
+    if (c <= 0) continue;
+    // route counts for 4-bit weights (fat_rows) and for dense bf16/f16 (S)
+    if (fr > 0 && c >= fr) r.fat++;
+    if ((double)c <= (double)o.splitk_max_pairs) r.thin++;
+    else r.full++;
+  }
+  *out = r;
+  return MOE_OK;
+}
+
+size_t moe_forward_workspace_bytes(const moe_plan* p, int32_t D, int32_t F,
+                                   int32_t x_dtype, int32_t w_dtype,
+                                   const moe_options* opt) {
+  if (!p || D <= 0 || F <= 0 || D % 128 || F % 128 || !dtypes_ok(x_dtype, w_dtype)) {
+    fail(MOE_EINVAL, "bad plan, sizes or dtypes for the workspace query");
+    return 0;
+  }
+  const moe_options o = opt ? *opt : defaults();
+  return fwd_layout(p->desc, D, F, x_dtype, w_dtype, o).bytes;
+}
+
+moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
+                       moe_weight w_gate, moe_weight w_up, moe_weight w_down,
+                       int32_t D, int32_t F, void* y, int32_t y_dtype,
+                       void* ws, size_t ws_bytes, const moe_options* opt,
+                       void* stream) {
+  std::string why;
+  if (!p) return fail(MOE_EINVAL, "plan is NULL");
+  const moe_plan_desc& d = p->desc;
+  const moe_options o = opt ? *opt : defaults();
+  if (D <= 0 || F <= 0 || D % 128 || F % 128)
+    return fail(MOE_EUNSUPPORTED, "D=%d and F=%d must be positive multiples of 128", D, F);
+  const int wdt = w_gate.dtype;
+  if (!dtypes_ok(x_dtype, wdt))
+    return fail(MOE_EUNSUPPORTED, "dtype pair (x=%d, W=%d) not supported", x_dtype, wdt);
+  if (!weight_ok(w_gate, wdt, &why, "w_gate") || !weight_ok(w_up, wdt, &why, "w_up") ||
+      !weight_ok(w_down, wdt, &why, "w_down"))
+    return fail(MOE_EINVAL, "%s", why.c_str());
+  if (y_dtype != MOE_F32 && y_dtype != x_dtype)
+    return fail(MOE_EUNSUPPORTED, "y dtype %d must be F32 or x's dtype", y_dtype);
+  if (std::isnan(o.swiglu_limit) || std::isnan(o.splitk_max_pairs))
+    return fail(MOE_EINVAL, "NaN option");
+  if (d.T > 0 && (!x || !y)) return fail(MOE_EINVAL, "x or y is NULL");
+  if (!aligned16(x) || !aligned16(y))
+    return fail(MOE_EINVAL, "x and y must be 16-byte aligned");
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(MOE_EINVAL, "workspace NULL or not 256-byte aligned");
+  const FwdLayout L = fwd_layout(d, D, F, x_dtype, wdt, o);
+  if (ws_bytes < L.bytes)
+    return fail(MOE_EWORKSPACE, "forward workspace %zu bytes < %zu needed",
+                ws_bytes, L.bytes);
+  if (d.T == 0) return MOE_OK;
+  int dev;
+  DevInfo info;
+  moe_status st = device_info(&dev, &info);
+  if (st != MOE_OK) return st;
+  PhaseRecord* rec = nullptr;
+  if (o.flags & MOE_OPT_PHASE_EVENTS) {
+    rec = acquire_record(&st);
+    if (!rec) return st;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* b = static_cast<char*>(ws);
+  char* pb = p->ws;
+  const int n_exp = d.E + d.n_shared;
+  int32_t* meta = (int32_t*)(b + L.meta);
+  hipError_t e;
+
+  {
+    PhaseScope ps(rec, 0, s);
+    ClassifyArgs ca{};
+    ca.counts = (const int32_t*)(pb + p->L.counts);
+    ca.n_exp = n_exp;
+    ca.mode = wdt == MOE_F32 ? 0 : (wdt == MOE_Q4B32 ? 2 : 1);
+    ca.S = (double)o.splitk_max_pairs;
+    ca.fat_rows = L.fat_rows;
+    ca.full_tiles = (int32_t*)(b + L.full_tiles);
+    ca.sk1 = (int32_t*)(b + L.sk1);
+    ca.sk4 = (int32_t*)(b + L.sk4);
+    ca.fat_slot = (int32_t*)(b + L.fat_slot);
+    ca.fat_list = (int32_t*)(b + L.fat_list);
+    ca.meta = meta;
+    e = launch_classify(ca, s);
+    if (e != hipSuccess) return hip_fail(e, "classify kernel");
+  }
+  if (L.can_fat) {
+    PhaseScope ps(rec, 1, s);
+    const int grid = info.ncu * 8;
+    e = launch_dequant_fat(w_gate.data, w_gate.scales, b + L.stg_g, F, D,
+                           (const int32_t*)(b + L.fat_list), meta, grid, s);
+    if (e == hipSuccess)
+      e = launch_dequant_fat(w_up.data, w_up.scales, b + L.stg_u, F, D,
+                             (const int32_t*)(b + L.fat_list), meta, grid, s);
+    if (e == hipSuccess)
+      e = launch_dequant_fat(w_down.data, w_down.scales, b + L.stg_d, D, F,
+                             (const int32_t*)(b + L.fat_list), meta, grid, s);
+    if (e != hipSuccess) return hip_fail(e, "dequant kernel");
+  }
+
+  GemmArgs g{};
+  g.offsets = (const int32_t*)(pb + p->L.offsets);
+  g.pair_token = (const int32_t*)(pb + p->L.pair_token);
+  g.pair_w = (const float*)(pb + p->L.pair_w);
+  g.meta = meta;
+  g.clamp = o.swiglu_limit;
+  g.fat_slot = L.can_fat ? (const int32_t*)(b + L.fat_slot) : nullptr;
+  void* H = b + L.H;
+  void* Y = b + L.Y;
+  const int sk_rb1_grid_cap = info.ncu * 8;
+  const int sk_rb4_grid_cap = info.ncu * 4;
+  const int full_grid_cap = info.ncu * 2;
+
+  for (int stage = 0; stage < 2; ++stage) {
+    g.mode = stage;
+    if (stage == 0) {
+      g.K = D; g.N = F; g.A = x; g.out = H;
+      g.B0 = w_gate.data; g.B0s = w_gate.scales;
+      g.B1 = w_up.data; g.B1s = w_up.scales;
+      g.S0 = b + L.stg_g; g.S1 = b + L.stg_u;
+    } else {
+      g.K = F; g.N = D; g.A = H; g.out = Y;
+      g.B0 = w_down.data; g.B0s = w_down.scales;
+      g.B1 = nullptr; g.B1s = nullptr;
+      g.S0 = b + L.stg_d; g.S1 = nullptr;
+    }
+    if (L.can_full) {
+      PhaseScope ps(rec, stage == 0 ? 2 : 4, s);
+      const int nnb = stage == 0 ? F / 64 : D / 128;
+      g.list = (const int32_t*)(b + L.full_tiles);
+      g.meta_index = kMetaFullTiles;
+      const int grid = (int)std::min<int64_t>((int64_t)L.cap_tiles * nnb, full_grid_cap);
+      e = launch_gemm_full(g, x_dtype, grid, s);
+      if (e != hipSuccess) return hip_fail(e, "full tile kernel");
+    }
+    {
+      PhaseScope ps(rec, stage == 0 ? 3 : 5, s);
+      const int nnb = stage == 0 ? F / 32 : D / 64;
+      if (L.can_sk1) {
+        g.list = (const int32_t*)(b + L.sk1);
+        g.meta_index = kMetaSk1;
+        const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk1 * nnb, sk_rb1_grid_cap);
+        e = launch_gemm_splitk(g, x_dtype, wdt, 1, grid, s);
+        if (e != hipSuccess) return hip_fail(e, "split-K kernel");
+      }
+      if (L.can_sk4) {
+        g.list = (const int32_t*)(b + L.sk4);
+        g.meta_index = kMetaSk4;
+        const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * nnb, sk_rb4_grid_cap);
+        e = launch_gemm_splitk(g, x_dtype, wdt, 4, grid, s);
+        if (e != hipSuccess) return hip_fail(e, "split-K kernel");
+      }
+    }
+  }
+  {
+    PhaseScope ps(rec, 6, s);
+    e = launch_combine(Y, (const int32_t*)(pb + p->L.tok2pair),
+                       (const int32_t*)(pb + p->L.offsets), d.T, D, d.k,
+                       d.n_shared, d.E, y_dtype, y, s);
+    if (e != hipSuccess) return hip_fail(e, "combine kernel");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_dequant_q4(const void* data, const void* scales, int64_t rows,
+                          int64_t K, void* out_f16, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return fail(MOE_EINVAL, "rows >= 0 and K a positive multiple of 32");
+  if (K > (1 << 30)) return fail(MOE_EUNSUPPORTED, "K too large");
+  if (rows == 0) return MOE_OK;
+  if (!data || !scales || !out_f16) return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned16(data) || !aligned16(out_f16) || (reinterpret_cast<uintptr_t>(scales) & 1u))
+    return fail(MOE_EINVAL, "data/out must be 16-byte aligned, scales 2-byte");
+  hipError_t e = launch_dequant_rows(data, scales, out_f16, rows, (int)K,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequant kernel");
+  return MOE_OK;
+}
+
+moe_status moe_phase_times(double* ms, int32_t n, int64_t* calls, int32_t reset) {
+  std::lock_guard<std::mutex> lock(g_ev_mu);
+  std::vector<double> acc(MOE_N_PHASES, 0.0);
+  for (size_t i = 0; i < g_records_used; ++i) {
+    PhaseRecord& r = g_records[i];
+    for (int ph = 0; ph < MOE_N_PHASES; ++ph) {
+      if (!r.used[ph]) continue;
+      hipError_t e = hipEventSynchronize(r.ev[2 * ph + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, r.ev[2 * ph], r.ev[2 * ph + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      acc[ph] += t;
+    }
+  }
+  if (ms)
+    for (int i = 0; i < n && i < MOE_N_PHASES; ++i) ms[i] = acc[i];
+  if (calls) *calls = (int64_t)g_records_used;
+  if (reset) g_records_used = 0;
+  return MOE_OK;
+}
+
+}  // extern "C"

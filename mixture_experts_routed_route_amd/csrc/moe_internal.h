@@ -1,0 +1,104 @@
+// Internal declarations shared by the HIP sources of the MI355X MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---- vector types for gfx950 MFMA operands ------------------------------
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Plan chunking: tokens per chunk of the capacity scan (one 64-bit mask per
+// expert and chunk gives the in-chunk stable rank by popcount).
+constexpr int kChunk = 64;
+constexpr int kMaxExperts = 1024;
+
+// Full MFMA tile geometry (rows of A, output columns, K per stage).
+constexpr int kFullBM = 128;
+constexpr int kFullBN = 128;
+constexpr int kFullBK = 64;
+// Split-K tile: output columns per item and rows per row block.
+constexpr int kSkNB = 64;
+constexpr int kSkRows = 64;   // rows per split-K group (4 blocks of 16)
+
+// Forward route tags per expert.
+enum Route : int32_t { kRouteNone = 0, kRouteSplitK = 1, kRouteFull = 2,
+                       kRouteFat = 3 };
+
+// Forward meta counters written by the classify kernel.
+enum Meta : int32_t { kMetaFullTiles = 0, kMetaSk1 = 1, kMetaSk4 = 2,
+                      kMetaFat = 3, kMetaCount = 8 };
+
+// ---- launchers (plan_kernels.hip) ---------------------------------------
+hipError_t launch_route_hist(const float* logits, int T, int E, int k,
+                             int32_t* ids, float* w, int32_t* hist,
+                             hipStream_t s);
+hipError_t launch_scan(int32_t* hist, int NC, int T, int E, int k,
+                       int n_shared, int64_t limit, int32_t* total,
+                       int32_t* counts, int32_t* offsets, int64_t* stats,
+                       hipStream_t s);
+hipError_t launch_permute(const int32_t* ids, const float* w,
+                          const int32_t* base, const int32_t* offsets, int T,
+                          int E, int k, int n_shared, int64_t limit,
+                          int32_t* slot, int32_t* tok2pair,
+                          int32_t* pair_token, float* pair_w, hipStream_t s);
+
+// ---- forward (forward_kernels.hip) --------------------------------------
+struct ClassifyArgs {
+  const int32_t* counts;   // [n_exp]
+  int n_exp;               // E + n_shared
+  int mode;                // 0: all split-K (f32), 1: by S (bf16/f16), 2: q4
+  double S;                // split-K bound in pairs per expert (f32 value)
+  int fat_rows;            // q4: >= fat_rows -> fat; <= 0 off
+  int32_t* full_tiles;     // [cap] (expert, row0) pairs as int2
+  int32_t* sk1;            // [cap] (expert, row0, nrows, 0) as int4
+  int32_t* sk4;            // [cap] same, 17..64 rows
+  int32_t* fat_slot;       // [n_exp]
+  int32_t* fat_list;       // [n_exp]
+  int32_t* meta;           // [kMetaCount]
+};
+hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s);
+
+// Operand set of one GEMM stage (gate/up or down).
+struct GemmArgs {
+  int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down (x w)
+  int K, N;                 // K: reduction; N: output width (F or D)
+  const void* A;            // gate/up: x [T, D]; down: H [P, F]
+  const int32_t* pair_token;// gather map for gate/up
+  const int32_t* offsets;   // [n_exp + 1]
+  const float* pair_w;      // [P]
+  // B operands, [n_exp, rows, K]: gate/up use B0 = W_gate, B1 = W_up; down
+  // uses B0 = W_down. q4: data + scales.
+  const void* B0; const void* B0s;
+  const void* B1; const void* B1s;
+  // Dequantised fp16 copies of fat experts: [slot, rows, K]; nullptr if none.
+  const void* S0; const void* S1;
+  const int32_t* fat_slot;
+  void* out;                // H [P, F] (x's dtype) or Ypair [P, D] (f32)
+  float clamp;              // SwiGLU limit, <= 0 off
+  const int32_t* list;      // work list (full tiles or split-K groups)
+  const int32_t* meta;      // counts of the work lists
+  int meta_index;           // which meta counter holds this list's length
+};
+hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
+                            hipStream_t s);
+hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
+                              int grid, hipStream_t s);
+hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
+                              int rows, int K, const int32_t* fat_list,
+                              const int32_t* meta, int grid, hipStream_t s);
+hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
+                               int64_t rows, int K, hipStream_t s);
+hipError_t launch_combine(const void* ypair, const int32_t* tok2pair,
+                          const int32_t* offsets, int T, int D, int k,
+                          int n_shared, int E, int ydt, void* y,
+                          hipStream_t s);
+
+}  // namespace moe

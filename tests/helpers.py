@@ -1,0 +1,111 @@
+"""Shared pieces of the GPU parity tests: run the HIP path through the C ABI,
+run the oracle on the same seeded inputs, and compare."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mixture_experts_routed_route_amd as moe
+import oracle
+
+# Layer-output bars: max|y - ref| <= TOL * RMS(ref) (normwise, per token set).
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}
+# Gate weights: f32 on the GPU against f64 in the oracle.
+W_RTOL = 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(w, dev="cuda"):
+    if isinstance(w, (tuple, list)):
+        return tuple(t.to(dev) for t in w)
+    return w.to(dev)
+
+
+def gpu_plan(wl, dev="cuda"):
+    logits = wl["logits"].to(dev)
+    p = moe.moe_plan_create(logits, wl["k"], wl["capacity_factor"],
+                            wl["n_shared"])
+    return p
+
+
+def plan_arrays(p) -> dict:
+    v = moe.moe_plan_get_views(p)
+    torch.cuda.synchronize()
+    return {k: t.cpu().numpy() for k, t in v.items()}
+
+
+def check_plan(wl, p, ids_ref=None, w_ref=None):
+    """Bit-exact routing/drop/permutation; weights within W_RTOL."""
+    g = plan_arrays(p)
+    if ids_ref is None:
+        ids_ref, w_ref = oracle.route(wl["logits"], wl["k"])
+    ref = oracle.plan(ids_ref, wl["E"], wl["capacity_factor"], wl["n_shared"])
+    assert np.array_equal(g["topk_id"], ids_ref), "top-k ids differ"
+    err = np.abs(g["topk_w"].astype(np.float64) - w_ref)
+    assert np.all(err <= W_RTOL * np.abs(w_ref) + 1e-30), float(err.max())
+    assert np.array_equal(g["slot"], ref["slot"]), "slots differ"
+    assert np.array_equal(g["tok2pair"], ref["tok2pair"]), "tok2pair differs"
+    assert np.array_equal(g["counts"], ref["counts"]), "counts differ"
+    assert np.array_equal(g["offsets"], ref["offsets"]), "offsets differ"
+    assert np.array_equal(g["pair_token"], ref["pair_token"]), "permutation"
+    src = ref["pair_src"]
+    pw_ref = np.where(src >= 0, w_ref.reshape(-1)[np.maximum(src, 0)], 1.0)
+    assert np.all(np.abs(g["pair_w"] - pw_ref) <= W_RTOL * pw_ref + 1e-30)
+    st = moe.moe_plan_stats_get(p)
+    assert st["dropped"] == ref["dropped"]
+    assert st["kept"] == ref["kept"]
+    assert st["limit"] == ref["limit"]
+    assert st["drop_fraction"] == ref["drop_fraction"]
+    # the reported drop fraction is the count recomputed from the plan
+    T, k = ids_ref.shape
+    if T * k:
+        assert st["drop_fraction"] == (T * k - g["offsets"][wl["E"]]) / (T * k)
+    return g, ref, st
+
+
+def gpu_layer(wl, options=None, dev="cuda", plan=None):
+    p = plan if plan is not None else gpu_plan(wl, dev)
+    x = wl["x"].to(dev)
+    y = moe.moe_forward(p, x, to_dev(wl["w_gate"], dev), to_dev(wl["w_up"], dev),
+                        to_dev(wl["w_down"], dev), options=options)
+    torch.cuda.synchronize()
+    return p, y
+
+
+def oracle_layer(wl, tokens=None, ids=None, w=None, keep=None):
+    if ids is None:
+        ids, w = oracle.route(wl["logits"], wl["k"])
+        pl = oracle.plan(ids, wl["E"], wl["capacity_factor"], wl["n_shared"])
+        keep = pl["keep"]
+    return oracle.layer(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids,
+                        w, keep, E=wl["E"], n_shared=wl["n_shared"],
+                        x_dtype=wl["x_dtype"], w_dtype=wl["w_dtype"],
+                        c=wl["swiglu_limit"], tokens=tokens)
+
+
+def sample_tokens(T, n, seed=0):
+    if n >= T:
+        return None
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(T, size=n, replace=False))
+    # always include the first and last tokens (chunk edges, ragged tail)
+    return np.unique(np.concatenate([[0, T - 1], idx]))
+
+
+def check_layer(wl, y, tokens=None, ref=None):
+    """max|y - ref| <= TOL * RMS(ref) over the checked tokens."""
+    if ref is None:
+        ref = oracle_layer(wl, tokens)
+    yy = y.float().cpu().numpy().astype(np.float64)
+    if tokens is not None:
+        yy = yy[tokens]
+    assert np.all(np.isfinite(yy)), "non-finite output"
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    err = float(np.max(np.abs(yy - ref))) if ref.size else 0.0
+    tol = TOL[wl["x_dtype"]]
+    assert err <= tol * rms + 1e-30, f"max err {err:.3e} > {tol} x RMS {rms:.3e}"
+    return err, rms

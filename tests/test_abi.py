@@ -1,0 +1,132 @@
+"""
+The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, and rejects bad arguments on the host before any
+launch. Without a device, a valid call reports MOE_EHIP with a message.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mixture_experts_routed_route_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert "moe_forward" in names and "moe_plan_create" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moe.EXPORTED)
+    assert "gfx950" in moe.moe_version()
+
+
+def test_options_default(lib):
+    o = moe.moe_options_default()
+    assert o.swiglu_limit == 7.0
+    assert o.fat_rows == 64
+    assert o.splitk_max_pairs > 0
+    assert o.flags == 0
+
+
+def _desc(T=64, E=8, k=2, n_shared=0, cf=0.0):
+    return moe.PlanDesc(T, E, k, n_shared, cf)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k=0), dict(k=9), dict(E=0), dict(E=1025, k=1), dict(T=-1),
+    dict(n_shared=2), dict(cf=-1.0), dict(cf=float("nan")),
+    dict(cf=float("inf")), dict(T=1 << 30, k=2),
+])
+def test_plan_desc_validation(lib, kw):
+    d = _desc(**kw)
+    assert lib.moe_plan_workspace_bytes(ctypes.byref(d)) == 0
+    h = ctypes.c_void_p()
+    st = lib.moe_plan_create(ctypes.byref(d), 0x1000, 0x10000, 1 << 20, None,
+                             ctypes.byref(h))
+    assert st == moe.MOE_EINVAL
+    assert moe.moe_last_error()
+    assert not h.value
+
+
+def test_plan_pointer_and_workspace_validation(lib):
+    d = _desc()
+    need = lib.moe_plan_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    h = ctypes.c_void_p()
+    assert lib.moe_plan_create(ctypes.byref(d), None, 0x10000, need, None,
+                               ctypes.byref(h)) == moe.MOE_EINVAL
+    assert lib.moe_plan_create(ctypes.byref(d), 0x1000, None, need, None,
+                               ctypes.byref(h)) == moe.MOE_EINVAL
+    assert lib.moe_plan_create(ctypes.byref(d), 0x1004, 0x10000, need, None,
+                               ctypes.byref(h)) == moe.MOE_EINVAL   # misaligned
+    assert lib.moe_plan_create(ctypes.byref(d), 0x1000, 0x10010, need, None,
+                               ctypes.byref(h)) == moe.MOE_EINVAL   # ws align
+    assert lib.moe_plan_create(ctypes.byref(d), 0x1000, 0x10000, need - 1,
+                               None, ctypes.byref(h)) == moe.MOE_EWORKSPACE
+    assert "workspace" in moe.moe_last_error()
+    assert lib.moe_plan_create(ctypes.byref(d), 0x1000, 0x10000, need, None,
+                               None) == moe.MOE_EINVAL
+
+
+def test_workspace_grows_with_tokens(lib):
+    a = lib.moe_plan_workspace_bytes(ctypes.byref(_desc(T=64)))
+    b = lib.moe_plan_workspace_bytes(ctypes.byref(_desc(T=640)))
+    c = lib.moe_plan_workspace_bytes(ctypes.byref(_desc(T=640, n_shared=1)))
+    assert 0 < a < b < c
+    assert a % 256 == 0
+
+
+def test_forward_needs_a_plan(lib):
+    w = moe.Weight(moe.MOE_BF16, 0x1000, None)
+    st = lib.moe_forward(None, 0x1000, moe.MOE_BF16, w, w, w, 128, 128,
+                         0x2000, moe.MOE_F32, 0x10000, 1 << 20, None, None)
+    assert st == moe.MOE_EINVAL
+    assert lib.moe_forward_workspace_bytes(None, 128, 128, moe.MOE_BF16,
+                                           moe.MOE_BF16, None) == 0
+
+
+def test_dequant_validation(lib):
+    assert lib.moe_dequant_q4(0x1000, 0x2000, 4, 48, 0x3000, None) == moe.MOE_EINVAL
+    assert lib.moe_dequant_q4(0x1000, 0x2000, -1, 64, 0x3000, None) == moe.MOE_EINVAL
+    assert lib.moe_dequant_q4(None, None, 0, 64, None, None) == moe.MOE_OK
+    assert lib.moe_dequant_q4(0x1008, 0x2000, 4, 64, 0x3000, None) == moe.MOE_EINVAL
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0,
+                    reason="checks the no-device error path")
+def test_no_device_reports_ehip(lib):
+    d = _desc()
+    need = lib.moe_plan_workspace_bytes(ctypes.byref(d))
+    h = ctypes.c_void_p()
+    st = lib.moe_plan_create(ctypes.byref(d), 0x1000, 0x10000, need, None,
+                             ctypes.byref(h))
+    assert st == moe.MOE_EHIP
+    assert "hip" in moe.moe_last_error().lower()
+    assert not h.value
+    ms, calls = moe.moe_phase_times()
+    assert calls == 0 and all(v == 0 for v in ms.values())
+
+
+def test_python_binding_rejects_bad_tensors():
+    with pytest.raises(ValueError):
+        moe.moe_plan_create(torch.zeros(4, 4, dtype=torch.float64), 2)
+    with pytest.raises(ValueError):
+        moe.moe_dequant_q4(torch.zeros(4, 16, dtype=torch.int8),
+                           torch.zeros(4, 1, dtype=torch.float16))

@@ -112,8 +112,13 @@ def make_layer(T: int, D: int, F: int, E: int, k: int, dtype: str, *,
                logits: torch.Tensor | None = None, logit_bias=None,
                bf16_logits: bool = False, x_std: float = 1.0,
                w_std: float = 0.02, seed: int = 0, capacity_factor=0.0,
-               swiglu_limit: float = 7.0, name: str = "custom") -> dict:
-    """A seeded layer instance. The draw order is fixed: logits, x, weights."""
+               swiglu_limit: float = 7.0, name: str = "custom",
+               with_weights: bool = True) -> dict:
+    """A seeded layer instance. The draw order is fixed: logits, x, weights.
+
+    ``with_weights=False`` draws the logits alone (identical to the full
+    draw's logits), for plan-only uses of the large workloads.
+    """
     g = _gen(seed)
     w_dtype = w_dtype or dtype
     if logits is None:
@@ -123,6 +128,12 @@ def make_layer(T: int, D: int, F: int, E: int, k: int, dtype: str, *,
     if bf16_logits:
         logits = logits.to(torch.bfloat16).to(torch.float32)
     logits = logits.to(torch.float32).contiguous()
+    base = dict(name=name, T=T, D=D, F=F, E=E, k=k, n_shared=n_shared,
+                x_dtype=dtype, w_dtype=w_dtype or dtype, logits=logits,
+                capacity_factor=float(capacity_factor),
+                swiglu_limit=float(swiglu_limit), seed=seed)
+    if not with_weights:
+        return base
     x = as_dtype(_normal((T, D), x_std, g), dtype)
     Et = E + n_shared
     if w_dtype == Q4B32:
@@ -131,15 +142,11 @@ def make_layer(T: int, D: int, F: int, E: int, k: int, dtype: str, *,
         wd = q4_weights(Et, D, F, g)
     else:
         wg, wu, wd = dense_weights(Et, D, F, w_std, w_dtype, g)
-    return dict(name=name, T=T, D=D, F=F, E=E, k=k, n_shared=n_shared,
-                x_dtype=dtype, w_dtype=w_dtype, logits=logits, x=x,
-                w_gate=wg, w_up=wu, w_down=wd,
-                capacity_factor=float(capacity_factor),
-                swiglu_limit=float(swiglu_limit), seed=seed)
+    return dict(base, x=x, w_gate=wg, w_up=wu, w_down=wd)
 
 
 def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
-           pairs_per_expert=None) -> dict:
+           pairs_per_expert=None, with_weights: bool = True) -> dict:
     """The five named workloads (sizes from the routed-MoE pages).
 
     1 tiny fp32: T=64, D=128, F=256, E=8, top-2, cf 0.
@@ -156,28 +163,28 @@ def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
     if n == 1:
         return make_layer(64, 128, 256, 8, 2, F32, seed=seed,
                           capacity_factor=capacity_factor or 0.0,
-                          name=CONFIG_NAMES[1])
+                          name=CONFIG_NAMES[1], with_weights=with_weights)
     if n == 2:
         g = _gen(seed + 1000)
         bias = torch.randn(128, generator=g) * 2.0
         cf = 1.5 if capacity_factor is None else capacity_factor
         return make_layer(2048, 512, 1024, 128, 2, BF16, logit_bias=bias,
                           bf16_logits=True, seed=seed, capacity_factor=cf,
-                          name=CONFIG_NAMES[2])
+                          name=CONFIG_NAMES[2], with_weights=with_weights)
     if n == 3:
         g = _gen(seed + 1000)
         bias = zipf_bias(128, 1.1, g)
         return make_layer(4096, 2048, 768, 128, 8, BF16, logit_bias=bias,
                           bf16_logits=True, seed=seed,
                           capacity_factor=capacity_factor or 0.0,
-                          name=CONFIG_NAMES[3])
+                          name=CONFIG_NAMES[3], with_weights=with_weights)
     if n == 4:
         g = _gen(seed + 1000)
         bias = zipf_bias(256, 1.1, g)
         return make_layer(13312, 4096, 2048, 256, 8, F16, w_dtype=Q4B32,
                           logit_bias=bias, seed=seed,
                           capacity_factor=capacity_factor or 0.0,
-                          name=CONFIG_NAMES[4])
+                          name=CONFIG_NAMES[4], with_weights=with_weights)
     if n == 5:
         if pairs_per_expert is not None:
             p = int(pairs_per_expert)
@@ -186,11 +193,13 @@ def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
             logits = logits.to(torch.bfloat16).to(torch.float32)
             return make_layer(T5, 2048, 768, 128, 8, BF16, n_shared=1,
                               logits=logits, seed=seed,
-                              name=f"{CONFIG_NAMES[5]}_p{p}")
+                              name=f"{CONFIG_NAMES[5]}_p{p}",
+                              with_weights=with_weights)
         T5 = 128 if T is None else int(T)
         return make_layer(T5, 2048, 768, 128, 8, BF16, n_shared=1,
                           bf16_logits=True, seed=seed,
-                          name=f"{CONFIG_NAMES[5]}_T{T5}")
+                          name=f"{CONFIG_NAMES[5]}_T{T5}",
+                          with_weights=with_weights)
     raise ValueError(f"no workload {n}")
 
 
