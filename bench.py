@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""
+Benchmark of the routed MoE FFN layer on one MI355X.
+
+A step is one pass of the whole hot path on one batch of seeded synthetic
+input already resident in HBM: moe_plan_create (route, capacity, dispatch)
+then moe_forward (classify, dequantise-once, gate/up tiles with clamped
+SwiGLU, down tiles, combine). W untimed warm-up steps, then exactly K timed
+steps between two device synchronisations.
+
+Default workload: the 13,312-token prompt over 256 4-bit experts
+(d_model 4096, expert d_ff 2048, top-8, Zipf(1.1) popularity), the size at
+which the dequant-once FP16 route of Strata PR #4366 was measured.
+``--config N`` selects another named workload (1..5).
+
+Prints one JSON line: the metric (routed-expert TFLOP/s, 6 D F flops per
+kept pair), pairs/s, the dominant kernel's roofline (HIP events around its
+launches on the library's stream, over the timed region), and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "mixture_experts_routed_route_amd", "csrc",
+                          "forward_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--capacity-factor", type=float, default=None)
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--pairs-per-expert", type=int, default=None)
+    ap.add_argument("--splitk-max-pairs", type=float, default=None)
+    ap.add_argument("--fat-rows", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--no-phase-events", action="store_true")
+    return ap.parse_args()
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("source_sha") != source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build "
+              "runs the layer on one GPU (expert parallelism over several "
+              "GPUs is a design note only); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_routed_route_amd as moe
+    import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = W.config(args.config, capacity_factor=args.capacity_factor, T=args.T,
+                  pairs_per_expert=args.pairs_per_expert)
+    T, D, F, E, k, ns = (wl[n] for n in ("T", "D", "F", "E", "k", "n_shared"))
+    logits = wl["logits"].to(dev)
+    x = wl["x"].to(dev)
+
+    def dv(w):
+        return tuple(t.to(dev) for t in w) if isinstance(w, tuple) else w.to(dev)
+
+    wg, wu, wd = dv(wl["w_gate"]), dv(wl["w_up"]), dv(wl["w_down"])
+    opts = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
+                            fat_rows=args.fat_rows)
+    if not args.no_phase_events:
+        opts.flags |= moe.MOE_OPT_PHASE_EVENTS
+
+    plan_ws = torch.empty(moe.moe_plan_workspace_bytes(T, E, k,
+                                                       wl["capacity_factor"], ns),
+                          dtype=torch.uint8, device=dev)
+    p = moe.moe_plan_create(logits, k, wl["capacity_factor"], ns,
+                            workspace=plan_ws)
+    wdt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "f16": moe.MOE_F16,
+           "q4b32": moe.MOE_Q4B32}[wl["w_dtype"]]
+    xdt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "f16": moe.MOE_F16}[wl["x_dtype"]]
+    fwd_ws = torch.empty(moe.moe_forward_workspace_bytes(p, D, F, xdt, wdt, opts),
+                         dtype=torch.uint8, device=dev)
+    y = torch.empty(T, D, dtype=torch.float32, device=dev)
+
+    def step():
+        pl = moe.moe_plan_create(logits, k, wl["capacity_factor"], ns,
+                                 workspace=plan_ws)
+        moe.moe_forward(pl, x, wg, wu, wd, options=opts, out=y,
+                        workspace=fwd_ws)
+        return pl
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.moe_phase_times(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pl = step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    phase_ms, calls = ((None, 0) if args.no_phase_events
+                       else moe.moe_phase_times(reset=True))
+
+    # routing facts of this workload (one host read, outside the timing)
+    st = moe.moe_plan_stats_get(pl, opts)
+    counts = moe.moe_plan_get_views(pl)["counts"].cpu().numpy().astype(np.int64)
+    kept_pairs = int(counts.sum())                       # shared included
+    flops = W.flops_per_pair(D, F) * kept_pairs
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    pairs_s = kept_pairs / (ms_per_step * 1e-3)
+
+    # routes per expert (the library's rule, restated for accounting)
+    fat_rows = opts.fat_rows if wl["w_dtype"] == "q4b32" else 0
+    if 0 < fat_rows < 17:
+        fat_rows = 17
+    S = float(opts.splitk_max_pairs)
+    if wl["w_dtype"] == "q4b32":
+        full_mask = (counts >= fat_rows) if fat_rows > 0 else counts < 0
+    elif wl["w_dtype"] == "f32":
+        full_mask = counts < 0
+    else:
+        full_mask = counts.astype(np.float64) > S
+    sk_mask = (counts > 0) & ~full_mask
+    rows_full = int(counts[full_mask].sum())
+    wbytes = W.weight_bytes_per_expert(D, F, wl["w_dtype"]) / 3.0   # per matrix
+    xb = W.dtype_bytes(wl["x_dtype"])
+
+    roofline = None
+    if phase_ms:
+        per = {name: v / max(calls, 1) for name, v in phase_ms.items()}
+        unit = {
+            "gateup_full": ("mfma", 4.0 * D * F * rows_full),
+            "down_full": ("mfma", 2.0 * D * F * rows_full),
+            "gateup_splitk": ("hbm", 2 * wbytes * int(sk_mask.sum())
+                              + int(counts[sk_mask].sum()) * D * xb),
+            "down_splitk": ("hbm", wbytes * int(sk_mask.sum())
+                            + int(counts[sk_mask].sum()) * (F * xb + D * 4)),
+            "dequant_once": ("hbm", int(full_mask.sum()) * 3 * D * F
+                             * (0.5625 + 2.0) if wl["w_dtype"] == "q4b32" else 0),
+            "combine": ("hbm", kept_pairs * D * 4 + T * D * 4),
+            "classify": ("hbm", 0),
+        }
+        dom = max((n for n in per if per[n] > 0), key=lambda n: per[n])
+        bound, amount = unit[dom]
+        sec = per[dom] * 1e-3
+        if bound == "mfma":
+            achieved = amount / sec / 1e12
+            peak = PEAK_TFLOPS[wl["x_dtype"]]
+            u = "TFLOP/s"
+        else:
+            achieved = amount / sec / 1e9
+            peak = PEAK_HBM_GBS
+            u = "GB/s"
+        traffic = load_traffic(wl["name"], dom)
+        roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2),
+                    "peak": peak, "unit": u, "frac": round(achieved / peak, 4),
+                    "traffic": traffic,
+                    "algorithmic_per_launch": amount,
+                    "avg_launch_ms": round(per[dom], 4),
+                    "phase_ms_per_step": {n: round(v, 4) for n, v in per.items()}}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    out = {
+        "metric": "routed-expert TFLOP/s per MoE layer (6*D*F per kept pair)",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl["x_dtype"],
+        "data": "synthetic (seeded; workloads.py)",
+        "config": {"workload": wl["name"], "T": T, "d_model": D, "d_ff": F,
+                   "experts": E, "top_k": k, "shared": ns,
+                   "weights": wl["w_dtype"],
+                   "capacity_factor": wl["capacity_factor"],
+                   "parallelism": "single GPU"},
+        "pairs_per_s": round(pairs_s, 1),
+        "kept_pairs": kept_pairs,
+        "drop_fraction": st["drop_fraction"],
+        "routes": {"full_or_fat_experts": int(full_mask.sum()),
+                   "splitk_experts": int(sk_mask.sum()),
+                   "rows_full": rows_full,
+                   "splitk_max_pairs": S, "fat_rows": fat_rows},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "hardware": hardware(torch),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    route + plan over all T tokens, then the layer on the first tokens
+    until about target_s seconds of work; reported in TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    t0 = time.perf_counter()
+    ids, w = oracle.route(wl["logits"], wl["k"])
+    pl = oracle.plan(ids, wl["E"], wl["capacity_factor"], wl["n_shared"])
+    t_plan = time.perf_counter() - t0
+    T = wl["T"]
+    n = 8
+    total_t, total_pairs, done = 0.0, 0, 0
+    while done < T and total_t < target_s:
+        toks = np.arange(done, min(T, done + n))
+        t0 = time.perf_counter()
+        oracle.layer(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids, w,
+                     pl["keep"], E=wl["E"], n_shared=wl["n_shared"],
+                     x_dtype=wl["x_dtype"], w_dtype=wl["w_dtype"],
+                     c=wl["swiglu_limit"], tokens=toks)
+        total_t += time.perf_counter() - t0
+        total_pairs += int(pl["keep"][toks].sum()) + wl["n_shared"] * len(toks)
+        done += len(toks)
+        n *= 2
+    flops = W.flops_per_pair(wl["D"], wl["F"]) * total_pairs
+    return {"value": round(flops / total_t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"route+plan of all {T} tokens ({t_plan:.2f} s), then "
+                      f"the layer on the first {done} tokens ({total_pairs} "
+                      f"kept pairs) in {total_t:.1f} s",
+            "pairs_per_s": round(total_pairs / total_t, 2)}
+
+
+def hardware(torch):
+    props = torch.cuda.get_device_properties(0)
+    return {"device": props.name,
+            "arch": getattr(props, "gcnArchName", ""),
+            "cus": props.multi_processor_count,
+            "hbm_gib": round(props.total_memory / 2 ** 30, 1),
+            "torch": torch.__version__, "hip": torch.version.hip,
+            "host_cpu": platform.processor() or platform.machine(),
+            "host_threads": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -92,7 +92,14 @@ typedef struct {
  *                     tiles owning experts of 16 rows or fewer (Strata PR
  *                     #4366, maintainer's review). Default 64.
  *   flags             MOE_OPT_PHASE_EVENTS records HIP events around each
- *                     forward phase on `stream` (see moe_phase_times). */
+ *                     forward phase on `stream` (see moe_phase_times).
+ *                     MOE_OPT_BF16_PLAIN_H keeps the SwiGLU output of bf16
+ *                     layers as one bf16 value (the pages' compute-dtype
+ *                     buffer). By default a bf16 layer carries it as a
+ *                     bf16 pair hi + lo (hi = bf16(h), lo = bf16(h - hi),
+ *                     about 16 significant bits) and the down projection
+ *                     multiplies both, so a layer whose output is mostly
+ *                     dropped rows still meets 2e-2 x RMS(ref). */
 typedef struct {
     float swiglu_limit;
     float splitk_max_pairs;
@@ -101,6 +108,7 @@ typedef struct {
 } moe_options;
 
 #define MOE_OPT_PHASE_EVENTS 1
+#define MOE_OPT_BF16_PLAIN_H 2
 
 /* One weight tensor. `scales` is NULL unless dtype is MOE_Q4B32. */
 typedef struct {

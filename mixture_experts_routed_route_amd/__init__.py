@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_F16, MOE_Q4B32 = 0, 1, 2, 3
 MOE_OPT_PHASE_EVENTS = 1
+MOE_OPT_BF16_PLAIN_H = 2
 MOE_N_PHASES = 7
 PHASES = ("classify", "dequant_once", "gateup_full", "gateup_splitk",
           "down_full", "down_splitk", "combine")
@@ -191,8 +192,11 @@ def moe_plan_workspace_bytes(T, E, k, capacity_factor=0.0, n_shared=0) -> int:
 
 
 def moe_plan_create(logits: torch.Tensor, k: int, capacity_factor: float = 0.0,
-                    n_shared: int = 0) -> Plan:
-    """Route f32 logits [T, E] (device) and build the dispatch plan."""
+                    n_shared: int = 0,
+                    workspace: torch.Tensor | None = None) -> Plan:
+    """Route f32 logits [T, E] (device) and build the dispatch plan.
+
+    Pass ``workspace`` (uint8, device) to reuse one buffer across plans."""
     L = library()
     if logits.dtype != torch.float32 or logits.dim() != 2:
         raise ValueError("logits must be a 2-D float32 tensor")
@@ -202,7 +206,10 @@ def moe_plan_create(logits: torch.Tensor, k: int, capacity_factor: float = 0.0,
     nbytes = L.moe_plan_workspace_bytes(ctypes.byref(d))
     if nbytes == 0:
         raise MoeError(MOE_EINVAL, moe_last_error())
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=logits.device)
+    if workspace is not None and workspace.numel() >= nbytes:
+        ws = workspace
+    else:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=logits.device)
     h = ctypes.c_void_p()
     _check(L.moe_plan_create(ctypes.byref(d), logits.data_ptr(), ws.data_ptr(),
                              nbytes, _stream(logits.device), ctypes.byref(h)))

@@ -318,12 +318,14 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
 }
 
-template <class TT, int MODE>
+template <class TT, int MODE, int LO>
 __global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
   using S = typename TT::S;
   using V8 = typename TT::V8;
   constexpr int BM = kFullBM, BN = kFullBN, BK = kFullBK;
-  constexpr int STAGE = (BM + BN) * BK * 2;
+  constexpr int NA = 1 + LO;             // A planes: H, or H hi and lo
+  constexpr int BOFF = NA * BM * 128;    // B's offset inside a stage
+  constexpr int STAGE = (NA * BM + BN) * BK * 2;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -346,6 +348,7 @@ __global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
     const int ne = a.offsets[e + 1] - off;
     const int slot = a.fat_slot ? a.fat_slot[e] : -1;
     const char* arow[4];
+    const char* arow2[4];
     const char* brow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -357,6 +360,7 @@ __global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
       } else {
         arow[i] = (const char*)a.A + (size_t)(off + rr) * K * 2;
       }
+      arow2[i] = LO ? (const char*)a.A2 + (size_t)(off + rr) * K * 2 : nullptr;
       int brow_idx;
       const void* bbase;
       if (MODE == 0) {
@@ -380,17 +384,19 @@ __global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-    uint4 ra[4], rb[4];
+    uint4 ra[4], ra2[LO ? 4 : 1], rb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ra[i] = ldg16(arow[i] + c16 * 16);
+      if (LO) ra2[i] = ldg16(arow2[i] + c16 * 16);
       rb[i] = ldg16(brow[i] + c16 * 16);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rbase + 32 * i;
       *reinterpret_cast<uint4*>(smem + swz(r, c16)) = ra[i];
-      *reinterpret_cast<uint4*>(smem + BM * 128 + swz(r, c16)) = rb[i];
+      if (LO) *reinterpret_cast<uint4*>(smem + BM * 128 + swz(r, c16)) = ra2[i];
+      *reinterpret_cast<uint4*>(smem + BOFF + swz(r, c16)) = rb[i];
     }
     __syncthreads();
 
@@ -401,11 +407,12 @@ __global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ra[i] = ldg16(arow[i] + kb);
+          if (LO) ra2[i] = ldg16(arow2[i] + kb);
           rb[i] = ldg16(brow[i] + kb);
         }
       }
       const char* As = smem + cur * STAGE;
-      const char* Bs = As + BM * 128;
+      const char* Bs = As + BOFF;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const int ch = ks * 2 + (lane >> 5);
@@ -425,6 +432,19 @@ __global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni)
             acc[mi][ni] = mfma32(av[mi], bv[ni], acc[mi][ni]);
+        if (LO) {
+          // low plane of H: (hi + lo) W accumulated in f32
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi) {
+            const int r = wm * 64 + mi * 32 + (lane & 31);
+            av[mi] = as_v8<V8>(*reinterpret_cast<const uint4*>(As + BM * 128 + swz(r, ch)));
+          }
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+              acc[mi][ni] = mfma32(av[mi], bv[ni], acc[mi][ni]);
+        }
       }
       if (kt + 1 < nk) {
         char* Ad = smem + (cur ^ 1) * STAGE;
@@ -432,7 +452,8 @@ __global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int r = rbase + 32 * i;
           *reinterpret_cast<uint4*>(Ad + swz(r, c16)) = ra[i];
-          *reinterpret_cast<uint4*>(Ad + BM * 128 + swz(r, c16)) = rb[i];
+          if (LO) *reinterpret_cast<uint4*>(Ad + BM * 128 + swz(r, c16)) = ra2[i];
+          *reinterpret_cast<uint4*>(Ad + BOFF + swz(r, c16)) = rb[i];
         }
       }
       __syncthreads();
@@ -452,7 +473,9 @@ __global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
         if (MODE == 0) {
           const int f = nb * 64 + wn * 32 + j;
           const float h = swiglu(acc[mi][0][r], acc[mi][1][r], a.clamp);
-          reinterpret_cast<S*>(a.out)[prow * N + f] = (S)h;
+          const S hv = (S)h;
+          reinterpret_cast<S*>(a.out)[prow * N + f] = hv;
+          if (a.out2) reinterpret_cast<S*>(a.out2)[prow * N + f] = (S)(h - (float)hv);
         } else {
           const float pw = a.pair_w[prow];
 #pragma unroll
@@ -471,14 +494,16 @@ hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
   if (grid <= 0) return hipSuccess;
   if (xdt == MOE_F16) {
     if (a.mode == 0)
-      hipLaunchKernelGGL((gemm_full_kernel<F16T, 0>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 0, 0>), dim3(grid), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_full_kernel<F16T, 1>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 1, 0>), dim3(grid), dim3(256), 0, s, a);
   } else if (xdt == MOE_BF16) {
     if (a.mode == 0)
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 0>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 0, 0>), dim3(grid), dim3(256), 0, s, a);
+    else if (a.A2)
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 1>), dim3(grid), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 0>), dim3(grid), dim3(256), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -497,7 +522,7 @@ hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
 // feature land in matching accumulators of one lane.
 
 // 16-bit activations (bf16/f16), dense or 4-bit weights.
-template <class TT, int WQ, int RB, int MODE>
+template <class TT, int WQ, int RB, int MODE, int LO>
 __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
                                               int NNB, float* red) {
   using S = typename TT::S;
@@ -514,6 +539,7 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
   const int nrows = a.list[4 * g + 2];
   const int off = a.offsets[e];
   const char* ap[RB];
+  const char* ap2[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int rr = row0 + min(rb * 16 + n, nrows - 1);
@@ -521,6 +547,7 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
       ap[rb] = (const char*)a.A + (size_t)a.pair_token[off + rr] * K * 2;
     else
       ap[rb] = (const char*)a.A + (size_t)(off + rr) * K * 2;
+    ap2[rb] = LO ? (const char*)a.A2 + (size_t)(off + rr) * K * 2 : nullptr;
   }
   const char* bp[4];
   const uint16_t* bsp[4];
@@ -585,6 +612,19 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(av[rb][i], bv[cb][i], acc[rb][cb]);
+    if (LO) {
+      // low plane of H: (hi + lo) W accumulated in f32
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[rb][i] = as_v8<V8>(ldg16(ap2[rb] + (size_t)k0 * 2 + i * 16));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(av[rb][i], bv[cb][i], acc[rb][cb]);
+    }
   }
 
   // fixed-order reduction over the four K quarters: ((w0 + w1) + w2) + w3
@@ -624,7 +664,9 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
           for (int pr = 0; pr < 2; ++pr) {
             const int f = nb * 32 + pr * 16 + n;
             const float h = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
-            reinterpret_cast<S*>(a.out)[prow * N + f] = (S)h;
+            const S hv = (S)h;
+            reinterpret_cast<S*>(a.out)[prow * N + f] = hv;
+            if (a.out2) reinterpret_cast<S*>(a.out2)[prow * N + f] = (S)(h - (float)hv);
           }
         } else {
           const float pw = a.pair_w[prow];
@@ -760,7 +802,7 @@ __device__ __forceinline__ void splitk_body32(const GemmArgs& a, int item,
   __syncthreads();
 }
 
-template <class TT, int WQ, int RB, int MODE>
+template <class TT, int WQ, int RB, int MODE, int LO>
 __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
   __shared__ float red[RB * 4 * 4 * 64];
   const int NNB = MODE == 0 ? a.N / 32 : a.N / 64;
@@ -769,16 +811,18 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
     if constexpr (TT::kBytes == 4)
       splitk_body32<RB, MODE>(a, item, NNB, red);
     else
-      splitk_body16<TT, WQ, RB, MODE>(a, item, NNB, red);
+      splitk_body16<TT, WQ, RB, MODE, LO>(a, item, NNB, red);
   }
 }
 
 template <class TT, int WQ, int RB>
 static hipError_t splitk_mode(const GemmArgs& a, int grid, hipStream_t s) {
   if (a.mode == 0)
-    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 0>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 0, 0>), dim3(grid), dim3(256), 0, s, a);
+  else if (TT::kBytes == 2 && !WQ && a.A2)
+    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 1, 1>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 1>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 1, 0>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -166,10 +166,11 @@ struct PhaseScope {
 };
 
 struct FwdLayout {
-  size_t H, Y, full_tiles, sk1, sk4, fat_slot, fat_list, meta, stg_g, stg_u,
+  size_t H, H2, Y, full_tiles, sk1, sk4, fat_slot, fat_list, meta, stg_g, stg_u,
       stg_d, bytes;
   int cap_tiles, cap_sk1, cap_sk4, max_fat, fat_rows;
   bool can_full, can_sk1, can_sk4, can_fat;
+  bool split_h;   // bf16: SwiGLU output as a hi + lo bf16 pair
 };
 
 bool dtypes_ok(int xdt, int wdt) {
@@ -214,6 +215,8 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
   L.H = take((size_t)Pmax * F * xb + 16);
+  L.split_h = xdt == MOE_BF16 && !(o.flags & MOE_OPT_BF16_PLAIN_H);
+  L.H2 = take(L.split_h ? (size_t)Pmax * F * 2 + 16 : 0);
   L.Y = take((size_t)Pmax * D * 4 + 16);   // Ypair in f32
   L.full_tiles = take((size_t)L.cap_tiles * 8);
   L.sk1 = take((size_t)L.cap_sk1 * 16);
@@ -483,6 +486,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   g.clamp = o.swiglu_limit;
   g.fat_slot = L.can_fat ? (const int32_t*)(b + L.fat_slot) : nullptr;
   void* H = b + L.H;
+  void* H2 = L.split_h ? b + L.H2 : nullptr;
   void* Y = b + L.Y;
   const int sk_rb1_grid_cap = info.ncu * 8;
   const int sk_rb4_grid_cap = info.ncu * 4;
@@ -491,12 +495,12 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   for (int stage = 0; stage < 2; ++stage) {
     g.mode = stage;
     if (stage == 0) {
-      g.K = D; g.N = F; g.A = x; g.out = H;
+      g.K = D; g.N = F; g.A = x; g.A2 = nullptr; g.out = H; g.out2 = H2;
       g.B0 = w_gate.data; g.B0s = w_gate.scales;
       g.B1 = w_up.data; g.B1s = w_up.scales;
       g.S0 = b + L.stg_g; g.S1 = b + L.stg_u;
     } else {
-      g.K = F; g.N = D; g.A = H; g.out = Y;
+      g.K = F; g.N = D; g.A = H; g.A2 = H2; g.out = Y; g.out2 = nullptr;
       g.B0 = w_down.data; g.B0s = w_down.scales;
       g.B1 = nullptr; g.B1s = nullptr;
       g.S0 = b + L.stg_d; g.S1 = nullptr;

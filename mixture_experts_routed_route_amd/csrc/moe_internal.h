@@ -71,6 +71,7 @@ struct GemmArgs {
   int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down (x w)
   int K, N;                 // K: reduction; N: output width (F or D)
   const void* A;            // gate/up: x [T, D]; down: H [P, F]
+  const void* A2;           // down, bf16 split H: the low plane; else null
   const int32_t* pair_token;// gather map for gate/up
   const int32_t* offsets;   // [n_exp + 1]
   const float* pair_w;      // [P]
@@ -82,6 +83,7 @@ struct GemmArgs {
   const void* S0; const void* S1;
   const int32_t* fat_slot;
   void* out;                // H [P, F] (x's dtype) or Ypair [P, D] (f32)
+  void* out2;               // gate/up, bf16 split H: low plane; else null
   float clamp;              // SwiGLU limit, <= 0 off
   const int32_t* list;      // work list (full tiles or split-K groups)
   const int32_t* meta;      // counts of the work lists
