@@ -248,7 +248,7 @@ __device__ __forceinline__ void dequant_unit(const uint8_t* q, const uint16_t* s
 // [rows, K] matrix as fp16. Grid-stride over (slot, row, 32-value block).
 __global__ __launch_bounds__(256) void dequant_fat_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
-    _Float16* __restrict__ out, int rows, int K,
+    _Float16* __restrict__ out, int rows, int K, int out_ld,
     const int32_t* __restrict__ fat_list, const int32_t* __restrict__ meta) {
   const int nfat = meta[kMetaFat];
   const int kbs = K / 32;
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void dequant_fat_kernel(
     half8 h[4];
     dequant32(raw, __builtin_bit_cast(_Float16, sb), h);
     uint4* dst = reinterpret_cast<uint4*>(
-        out + ((size_t)slot * rows + row) * (size_t)K + (size_t)kb * 32);
+        out + ((size_t)slot * rows + row) * (size_t)out_ld + (size_t)kb * 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = __builtin_bit_cast(uint4, h[i]);
   }
@@ -285,11 +285,12 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(
 }
 
 hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
-                              int rows, int K, const int32_t* fat_list,
-                              const int32_t* meta, int grid, hipStream_t s) {
+                              int rows, int K, int out_ld,
+                              const int32_t* fat_list, const int32_t* meta,
+                              int grid, hipStream_t s) {
   hipLaunchKernelGGL(dequant_fat_kernel, dim3(grid), dim3(256), 0, s,
                      (const uint8_t*)q, (const uint16_t*)sc, (_Float16*)out,
-                     rows, K, fat_list, meta);
+                     rows, K, out_ld, fat_list, meta);
   return hipGetLastError();
 }
 
@@ -301,212 +302,6 @@ hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
   hipLaunchKernelGGL(dequant_rows_kernel, dim3(grid), dim3(256), 0, s,
                      (const uint8_t*)q, (const uint16_t*)sc, (_Float16*)out,
                      rows, K);
-  return hipGetLastError();
-}
-
-// ---- full MFMA tile -------------------------------------------------------------
-//
-// Block = 4 waves (2 x 2), tile kFullBM x kFullBN, K staged kFullBK at a time
-// through two LDS buffers. Gate/up: the 128 B-rows of a tile are, per wave
-// column wn, 32 rows of W_gate then 32 rows of W_up for the same 32 output
-// features, so each lane holds g and u of one (row, feature) in matching
-// accumulators. LDS rows are 128 bytes; 16-byte chunk c of row r sits at
-// chunk c ^ ((r >> 1) & 7), which keeps both the staging writes and the
-// MFMA operand reads free of bank conflicts.
-
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
-}
-
-template <class TT, int MODE, int LO>
-__global__ __launch_bounds__(256, 2) void gemm_full_kernel(GemmArgs a) {
-  using S = typename TT::S;
-  using V8 = typename TT::V8;
-  constexpr int BM = kFullBM, BN = kFullBN, BK = kFullBK;
-  constexpr int NA = 1 + LO;             // A planes: H, or H hi and lo
-  constexpr int BOFF = NA * BM * 128;    // B's offset inside a stage
-  constexpr int STAGE = (NA * BM + BN) * BK * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int K = a.K;
-  const int N = a.N;
-  const int nk = K / BK;
-  const int NNB = MODE == 0 ? N / 64 : N / 128;
-  const int n_items = a.meta[a.meta_index] * NNB;
-  const int c16 = tid & 7;        // this thread's 16-byte chunk of a row
-  const int rbase = tid >> 3;     // rows rbase + 32 i
-
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int ti = item / NNB;
-    const int nb = item - ti * NNB;
-    const int e = a.list[2 * ti];
-    const int row0 = a.list[2 * ti + 1];
-    const int off = a.offsets[e];
-    const int ne = a.offsets[e + 1] - off;
-    const int slot = a.fat_slot ? a.fat_slot[e] : -1;
-    const char* arow[4];
-    const char* arow2[4];
-    const char* brow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rbase + 32 * i;
-      const int rr = min(row0 + r, ne - 1);
-      if (MODE == 0) {
-        const int tok = a.pair_token[off + rr];
-        arow[i] = (const char*)a.A + (size_t)tok * K * 2;
-      } else {
-        arow[i] = (const char*)a.A + (size_t)(off + rr) * K * 2;
-      }
-      arow2[i] = LO ? (const char*)a.A2 + (size_t)(off + rr) * K * 2 : nullptr;
-      int brow_idx;
-      const void* bbase;
-      if (MODE == 0) {
-        const int half = r >> 6, rr2 = r & 63;
-        const int mat = rr2 >> 5;
-        brow_idx = nb * 64 + half * 32 + (rr2 & 31);
-        bbase = slot >= 0 ? (mat ? a.S1 : a.S0) : (mat ? a.B1 : a.B0);
-      } else {
-        brow_idx = nb * 128 + r;
-        bbase = slot >= 0 ? a.S0 : a.B0;
-      }
-      const size_t eix = slot >= 0 ? (size_t)slot : (size_t)e;
-      brow[i] = (const char*)bbase + ((eix * N + brow_idx) * (size_t)K) * 2;
-    }
-
-    floatx16 acc[2][2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-    uint4 ra[4], ra2[LO ? 4 : 1], rb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ldg16(arow[i] + c16 * 16);
-      if (LO) ra2[i] = ldg16(arow2[i] + c16 * 16);
-      rb[i] = ldg16(brow[i] + c16 * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rbase + 32 * i;
-      *reinterpret_cast<uint4*>(smem + swz(r, c16)) = ra[i];
-      if (LO) *reinterpret_cast<uint4*>(smem + BM * 128 + swz(r, c16)) = ra2[i];
-      *reinterpret_cast<uint4*>(smem + BOFF + swz(r, c16)) = rb[i];
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) {
-        const int kb = (kt + 1) * BK * 2 + c16 * 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ra[i] = ldg16(arow[i] + kb);
-          if (LO) ra2[i] = ldg16(arow2[i] + kb);
-          rb[i] = ldg16(brow[i] + kb);
-        }
-      }
-      const char* As = smem + cur * STAGE;
-      const char* Bs = As + BOFF;
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int ch = ks * 2 + (lane >> 5);
-        V8 av[2], bv[2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const int r = wm * 64 + mi * 32 + (lane & 31);
-          av[mi] = as_v8<V8>(*reinterpret_cast<const uint4*>(As + swz(r, ch)));
-        }
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int r = wn * 64 + ni * 32 + (lane & 31);
-          bv[ni] = as_v8<V8>(*reinterpret_cast<const uint4*>(Bs + swz(r, ch)));
-        }
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = mfma32(av[mi], bv[ni], acc[mi][ni]);
-        if (LO) {
-          // low plane of H: (hi + lo) W accumulated in f32
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi) {
-            const int r = wm * 64 + mi * 32 + (lane & 31);
-            av[mi] = as_v8<V8>(*reinterpret_cast<const uint4*>(As + BM * 128 + swz(r, ch)));
-          }
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-              acc[mi][ni] = mfma32(av[mi], bv[ni], acc[mi][ni]);
-        }
-      }
-      if (kt + 1 < nk) {
-        char* Ad = smem + (cur ^ 1) * STAGE;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rbase + 32 * i;
-          *reinterpret_cast<uint4*>(Ad + swz(r, c16)) = ra[i];
-          if (LO) *reinterpret_cast<uint4*>(Ad + BM * 128 + swz(r, c16)) = ra2[i];
-          *reinterpret_cast<uint4*>(Ad + BOFF + swz(r, c16)) = rb[i];
-        }
-      }
-      __syncthreads();
-    }
-
-    // epilogue: 32x32 accumulator element r of lane l is row
-    // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
-    const int j = lane & 31;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int grow = row0 + row;
-        if (grow >= ne) continue;
-        const size_t prow = (size_t)(off + grow);
-        if (MODE == 0) {
-          const int f = nb * 64 + wn * 32 + j;
-          const float h = swiglu(acc[mi][0][r], acc[mi][1][r], a.clamp);
-          const S hv = (S)h;
-          reinterpret_cast<S*>(a.out)[prow * N + f] = hv;
-          if (a.out2) reinterpret_cast<S*>(a.out2)[prow * N + f] = (S)(h - (float)hv);
-        } else {
-          const float pw = a.pair_w[prow];
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni) {
-            const int d = nb * 128 + wn * 64 + ni * 32 + j;
-            reinterpret_cast<float*>(a.out)[prow * N + d] = acc[mi][ni][r] * pw;
-          }
-        }
-      }
-    }
-  }
-}
-
-hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
-                            hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
-  if (xdt == MOE_F16) {
-    if (a.mode == 0)
-      hipLaunchKernelGGL((gemm_full_kernel<F16T, 0, 0>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_full_kernel<F16T, 1, 0>), dim3(grid), dim3(256), 0, s, a);
-  } else if (xdt == MOE_BF16) {
-    if (a.mode == 0)
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 0, 0>), dim3(grid), dim3(256), 0, s, a);
-    else if (a.A2)
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 1>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 0>), dim3(grid), dim3(256), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 
@@ -544,10 +339,10 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
   for (int rb = 0; rb < RB; ++rb) {
     const int rr = row0 + min(rb * 16 + n, nrows - 1);
     if (MODE == 0)
-      ap[rb] = (const char*)a.A + (size_t)a.pair_token[off + rr] * K * 2;
+      ap[rb] = (const char*)a.A + (size_t)a.pair_token[off + rr] * a.a_ld * 2;
     else
-      ap[rb] = (const char*)a.A + (size_t)(off + rr) * K * 2;
-    ap2[rb] = LO ? (const char*)a.A2 + (size_t)(off + rr) * K * 2 : nullptr;
+      ap[rb] = (const char*)a.A + (size_t)(off + rr) * a.a_ld * 2;
+    ap2[rb] = LO ? (const char*)a.A2 + (size_t)(off + rr) * a.a_ld * 2 : nullptr;
   }
   const char* bp[4];
   const uint16_t* bsp[4];
@@ -665,15 +460,15 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
             const int f = nb * 32 + pr * 16 + n;
             const float h = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
             const S hv = (S)h;
-            reinterpret_cast<S*>(a.out)[prow * N + f] = hv;
-            if (a.out2) reinterpret_cast<S*>(a.out2)[prow * N + f] = (S)(h - (float)hv);
+            reinterpret_cast<S*>(a.out)[prow * a.out_ld + f] = hv;
+            if (a.out2) reinterpret_cast<S*>(a.out2)[prow * a.out_ld + f] = (S)(h - (float)hv);
           }
         } else {
           const float pw = a.pair_w[prow];
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const int d = nb * 64 + cb * 16 + n;
-            reinterpret_cast<float*>(a.out)[prow * N + d] = acc[rb][cb][r] * pw;
+            reinterpret_cast<float*>(a.out)[prow * a.out_ld + d] = acc[rb][cb][r] * pw;
           }
         }
       }
@@ -701,9 +496,9 @@ __device__ __forceinline__ void splitk_body32(const GemmArgs& a, int item,
   for (int rb = 0; rb < RB; ++rb) {
     const int rr = row0 + min(rb * 16 + n, nrows - 1);
     if (MODE == 0)
-      ap[rb] = (const float*)a.A + (size_t)a.pair_token[off + rr] * K;
+      ap[rb] = (const float*)a.A + (size_t)a.pair_token[off + rr] * a.a_ld;
     else
-      ap[rb] = (const float*)a.A + (size_t)(off + rr) * K;
+      ap[rb] = (const float*)a.A + (size_t)(off + rr) * a.a_ld;
   }
   const float* bp[4];
 #pragma unroll
@@ -787,14 +582,14 @@ __device__ __forceinline__ void splitk_body32(const GemmArgs& a, int item,
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
             const int f = nb * 32 + pr * 16 + n;
-            out[prow * N + f] = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
+            out[prow * a.out_ld + f] = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
           }
         } else {
           const float pw = a.pair_w[prow];
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const int d = nb * 64 + cb * 16 + n;
-            out[prow * N + d] = acc[rb][cb][r] * pw;
+            out[prow * a.out_ld + d] = acc[rb][cb][r] * pw;
           }
         }
       }

@@ -1,0 +1,393 @@
+// Full MFMA tile of the routed MoE layer on gfx950 (experts holding many
+// rows, and the dequantised-once fp16 copies of 4-bit fat experts).
+//
+// One block = 4 waves computes a 256 (weight rows) x 256 (token rows) tile.
+// K streams through a ring of four 32 KB LDS stages (32 K values each) that
+// buffer_load ... lds fills directly (no register staging): every wave issues
+// eight 1 KB loads per stage, three stages run ahead of the MFMAs, and each
+// lane picks the global 16-byte chunk that lands in the XOR-swizzled LDS slot
+// the MFMA operand reads expect. Waits are explicit counted vmcnt waits plus
+// s_barrier, and LDS loads and fragment reads are interleaved with the MFMA
+// stream (sched_group_barrier) so the matrix pipe is not left idle.
+//
+// The weight rows are the MFMA's A operand and the gathered token rows its B
+// operand, so a lane's 32x32 accumulator holds 4 consecutive output features
+// of one token per group of four registers: the epilogue writes 8-byte (H)
+// and 16-byte (per-pair output) vectors. Gate/up tiles interleave 32-row
+// blocks of W_gate and W_up over the same features, so g and u of one
+// (feature, token) sit in matching accumulators of one lane and the clamped
+// SwiGLU runs in the epilogue (mini-AGI PR #4, minagi/pool.py, `experts()`;
+// clamp from Strata PR #4366, "Approach"). Tokens are gathered on load
+// through the plan's pair list; no gathered copy of x is materialised.
+//
+// Work is persistent: block b takes items b, b + G, ... Items are tiles of
+// the classify kernel's largest-first list crossed with output-column
+// blocks; within a round the items of one XCD (blocks b = x mod 8) are a
+// contiguous run of a 4 x 8 (row tiles x column tiles) grouping, so the 32
+// blocks resident on an XCD share their A and B slices in its L2.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+struct F16T { using S = _Float16; using V8 = half8; using V4 = half4v; };
+struct BF16T { using S = __bf16; using V8 = bf16x8; using V4 = bf16x4; };
+
+__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes): scalar registers hold the
+// descriptor, lanes pass 32-bit byte offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+
+
+// 64-byte LDS rows (32 K values); 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 2) & 3): the 16 rows one MFMA operand read touches per phase
+// cover all 64 banks, and a wave's 1 KB direct-to-LDS write is contiguous.
+__device__ __forceinline__ int swz64(int r, int c) {
+  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
+
+__device__ __forceinline__ float swiglu(float g, float u, float c) {
+  if (c > 0.f) {
+    g = fminf(g, c);
+    u = fminf(fmaxf(u, -c), c);
+  }
+  return g / (1.f + expf(-g)) * u;
+}
+
+// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// vmcnt(N) and lgkmcnt(0) together.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kBW = 256;   // weight rows per tile
+constexpr int kBK = 32;    // K per LDS stage
+constexpr int kNS = 4;     // LDS stages (kNS - 1 in flight)
+constexpr int kRowB = kBK * 2;
+constexpr int kStage = 512 * kRowB;   // 256 weight + 256 token rows
+constexpr int kGM = 4;     // row tiles per schedule group
+constexpr int kDmaPerWave = 8;        // 1 KB blocks per wave per stage
+
+}  // namespace
+
+template <class TT, int MODE, int LO>
+__global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
+  using S = typename TT::S;
+  using V8 = typename TT::V8;
+  using V4 = typename TT::V4;
+  constexpr int BT = LO ? 128 : 256;       // token rows per pass
+  constexpr int TB = BT / 64;              // 32-row token blocks per wave
+  constexpr int NPASS = 256 / BT;          // passes over a 256-row tile
+  __shared__ __attribute__((aligned(1024))) char smem[kNS * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave index in a scalar register: descriptors and LDS bases stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ww = wave >> 1, wt = wave & 1;
+  const int K = a.K, N = a.N;
+  const int nk = K / kBK;
+  const int NNB = MODE == 0 ? N / 128 : (N + kBW - 1) / kBW;
+  const int n_tiles = a.meta[a.meta_index];
+  const int n_items = n_tiles * NNB;
+  const int G = gridDim.x;
+  // this lane's rows in its wave's DMA blocks: block b = 8 wave + jj covers
+  // stage rows 16 b .. 16 b + 15; lane writes row 16 b + lane / 4, physical
+  // chunk lane % 4, so it loads logical chunk (lane % 4) ^ ((row >> 2) & 3)
+  const int dma_r = lane >> 2;
+
+  for (int i = blockIdx.x; i < n_items; i += G) {
+    // XCD-aware permutation inside a full round, then 4 x 8 grouping
+    int L = i;
+    const int rb0 = (i / G) * G;
+    if ((G & 7) == 0 && rb0 + G <= n_items) {
+      const int w = i - rb0;
+      L = rb0 + (w & 7) * (G >> 3) + (w >> 3);
+    }
+    const int group = L / (kGM * NNB);
+    const int first = group * kGM;
+    const int gm = min(kGM, n_tiles - first);
+    const int within = L - first * NNB;
+    const int ti_ = first + within % gm;
+    const int nb = within / gm;
+
+    const int e = a.list[2 * ti_];
+    const int tile_row0 = a.list[2 * ti_ + 1];
+    const int off = a.offsets[e];
+    const int ne = a.offsets[e + 1] - off;
+    const int slot = a.fat_slot ? a.fat_slot[e] : -1;
+    const size_t eix = slot >= 0 ? (size_t)slot : (size_t)e;
+    // caller weights are [N, K] rows of K; fp16 fat copies have padded rows
+    const uint32_t w_ld = slot >= 0 ? (uint32_t)a.s_ld : (uint32_t)K;
+    const uint32_t mat_bytes = (uint32_t)N * w_ld * 2u;
+
+    __amdgpu_buffer_rsrc_t r_even, r_odd;   // descriptors of this wave's blocks
+    if (wave < 2) {
+      const char* b0 = (const char*)(slot >= 0 ? a.S0 : a.B0);
+      r_even = make_rsrc(b0 + eix * mat_bytes, mat_bytes);
+      if (MODE == 0) {
+        const char* b1 = (const char*)(slot >= 0 ? a.S1 : a.B1);
+        r_odd = make_rsrc(b1 + eix * mat_bytes, mat_bytes);
+      } else {
+        r_odd = r_even;
+      }
+    } else {
+      r_even = make_rsrc((LO && wave == 3) ? a.A2 : a.A, a.a_bytes);
+      r_odd = r_even;
+    }
+
+    for (int pass = 0; pass < NPASS; ++pass) {
+      const int row0 = tile_row0 + pass * BT;
+      if (row0 >= ne) break;   // block-uniform
+      uint32_t voff[kDmaPerWave];
+#pragma unroll
+      for (int jj = 0; jj < kDmaPerWave; ++jj) {
+        const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;   // stage row
+        const int c = (lane & 3) ^ ((R >> 2) & 3);
+        uint32_t rowoff;
+        if (wave < 2) {
+          int row;
+          if (MODE == 0)   // 32-row blocks alternate W_gate / W_up
+            row = nb * 128 + (R >> 7) * 64 + ((R >> 6) & 1) * 32 + (R & 31);
+          else
+            row = min(nb * kBW + R, N - 1);
+          rowoff = (uint32_t)row * w_ld * 2u;
+        } else {
+          const int Rt = R - 256;
+          const int rr = min(row0 + (Rt % BT), ne - 1);
+          const uint32_t prow = MODE == 0 ? (uint32_t)a.pair_token[off + rr]
+                                          : (uint32_t)(off + rr);
+          rowoff = prow * (uint32_t)a.a_ld * 2u;
+        }
+        voff[jj] = rowoff + (uint32_t)c * 16u;
+      }
+      // Refill of ring stage kt. Past the last stage the slice nk-1 is read
+      // again (an L2 hit) into a buffer no one reads any more, so every
+      // stage issues the same number of loads and every wait below is a
+      // constant count.
+      auto issue_one = [&](int kt, int jj) {
+        char* base = smem + (kt % kNS) * kStage + wave * kDmaPerWave * 1024;
+        const int soff = min(kt, nk - 1) * kRowB;
+        const __amdgpu_buffer_rsrc_t rs =
+            (MODE == 0 && ((jj >> 1) & 1)) ? r_odd : r_even;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_ptr_t)(base + jj * 1024), 16, (int)voff[jj], soff, 0, 0);
+      };
+      auto issue = [&](int kt) {
+#pragma unroll
+        for (int jj = 0; jj < kDmaPerWave; ++jj) issue_one(kt, jj);
+      };
+
+      floatx16 acc[4][TB];
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[wi][t][r] = 0.f;
+
+      // operand fragments of one 16-deep K step (hi and, for LO, lo planes)
+      struct Frag { V8 w[4]; V8 t[TB]; V8 tl[LO ? TB : 1]; };
+      auto read_frag = [&](int kt, int ks, Frag& f) {
+        const char* Ws = smem + (kt % kNS) * kStage;
+        const char* Ts = Ws + kBW * kRowB;
+        const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi) {
+          const int r = ww * 128 + wi * 32 + (lane & 31);
+          f.w[wi] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ws + swz64(r, ch)));
+        }
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const int r = wt * (BT / 2) + t * 32 + (lane & 31);
+          f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
+          if (LO)
+            f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
+        }
+      };
+      // one fragment read of a step: pieces 0..3 weights, then tokens (hi,
+      // lo interleaved for LO)
+      auto read_piece = [&](int kt, int ks, int idx, Frag& f) {
+        const char* Ws = smem + (kt % kNS) * kStage;
+        const char* Ts = Ws + kBW * kRowB;
+        const int ch = ks * 2 + (lane >> 5);
+        if (idx < 4) {
+          const int r = ww * 128 + idx * 32 + (lane & 31);
+          f.w[idx] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ws + swz64(r, ch)));
+        } else {
+          const int j = idx - 4;
+          const int t = LO ? j >> 1 : j;
+          const int r = wt * (BT / 2) + t * 32 + (lane & 31);
+          if (LO && (j & 1))
+            f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
+          else
+            f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
+        }
+      };
+      auto mma = [&](const Frag& f) {
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+          for (int t = 0; t < TB; ++t) acc[wi][t] = mfma32(f.w[wi], f.t[t], acc[wi][t]);
+        if (LO) {
+          // low plane of H: (hi + lo) W accumulated in f32
+#pragma unroll
+          for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+            for (int t = 0; t < TB; ++t) acc[wi][t] = mfma32(f.w[wi], f.tl[t], acc[wi][t]);
+        }
+      };
+
+      // all earlier reads of the ring and stores are done before refilling
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int s = 0; s < kNS - 1; ++s) issue(s);
+      wait_vmcnt<(kNS - 2) * kDmaPerWave>();   // stage 0 landed
+      __builtin_amdgcn_s_barrier();
+      Frag f0, f1;
+      read_frag(0, 0, f0);
+
+      // Per stage kt (two 16-deep steps): refill the ring three stages
+      // ahead, read step 1 while step 0 multiplies, then (once stage kt+1
+      // has landed for every wave) read its step 0 while step 1 multiplies.
+      // Every read of stage kt completes before the mid-stage barrier, so
+      // the refill of its buffer at the next stage's top never races it.
+      // MFMAs issue in order behind each other; loads placed between them
+      // issue while the matrix pipe is busy instead of in a burst that
+      // leaves it idle: MFMA, LDS read, MFMA, ring refill, ...
+      constexpr int kMf = 4 * TB * (LO ? 2 : 1);   // MFMAs per 16-deep step
+      constexpr int kRd = 4 + TB * (LO ? 2 : 1);   // fragment reads per step
+      static_assert(kRd == kDmaPerWave, "one refill per fragment read");
+      for (int kt = 0; kt < nk; ++kt) {
+        // LDS writes of the refill and LDS reads keep source order (the
+        // compiler cannot tell them apart), so alternate them here
+#pragma unroll
+        for (int q = 0; q < kRd; ++q) {
+          issue_one(kt + kNS - 1, q);
+          read_piece(kt, 1, q, f1);
+        }
+        mma(f0);
+#pragma unroll
+        for (int q = 0; q < kMf / 2; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          if (q < kRd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          if (q < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // step-1 reads done, stage kt+1 landed for this wave; after the
+        // barrier, for every wave (past the end: unread refill data)
+        wait_vm_lgkm0<(kNS - 2) * kDmaPerWave>();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int q = 0; q < kRd; ++q) read_piece(kt + 1, 0, q, f0);
+        mma(f1);
+#pragma unroll
+        for (int q = 0; q < kMf; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          if (q < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // epilogue: accumulator r of a 32x32 block is weight row
+      // 8 (r / 4) + 4 (lane / 32) + r % 4, token column lane % 32
+      // lane-derived epilogue values are defined here, after the K loop, so
+      // their addresses are not hoisted above it (they would hold registers
+      // the loop needs for operand fragments)
+      int lane_e = lane;
+      asm volatile("" : "+v"(lane_e));
+      const int jt = lane_e & 31;
+      const int hi4 = (lane_e >> 5) * 4;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const int trow_ = row0 + wt * (BT / 2) + t * 32 + jt;
+        if (trow_ >= ne) continue;
+        const size_t prow = (size_t)(off + trow_);
+        if (MODE == 0) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int f = nb * 128 + ww * 64 + p * 32 + rq * 8 + hi4;
+              V4 hv, lv;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float h = swiglu(acc[2 * p][t][rq * 4 + q],
+                                       acc[2 * p + 1][t][rq * 4 + q], a.clamp);
+                hv[q] = (S)h;
+                lv[q] = (S)(h - (float)hv[q]);
+              }
+              *reinterpret_cast<V4*>(reinterpret_cast<S*>(a.out) + prow * a.out_ld + f) = hv;
+              if (a.out2)
+                *reinterpret_cast<V4*>(reinterpret_cast<S*>(a.out2) + prow * a.out_ld + f) = lv;
+            }
+        } else {
+          const float pw = a.pair_w[prow];
+#pragma unroll
+          for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int d = nb * kBW + ww * 128 + wi * 32 + rq * 8 + hi4;
+              if (d >= N) continue;
+              float4 v;
+              v.x = acc[wi][t][rq * 4 + 0] * pw;
+              v.y = acc[wi][t][rq * 4 + 1] * pw;
+              v.z = acc[wi][t][rq * 4 + 2] * pw;
+              v.w = acc[wi][t][rq * 4 + 3] * pw;
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + prow * a.out_ld + d) = v;
+            }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
+                            hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (xdt == MOE_F16) {
+    if (a.mode == 0)
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 0, 0>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 1, 0>), dim3(grid), dim3(256), 0, s, a);
+  } else if (xdt == MOE_BF16) {
+    if (a.mode == 0)
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 0, 0>), dim3(grid), dim3(256), 0, s, a);
+    else if (a.A2)
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 1>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 0>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -171,6 +171,7 @@ struct FwdLayout {
   int cap_tiles, cap_sk1, cap_sk4, max_fat, fat_rows;
   bool can_full, can_sk1, can_sk4, can_fat;
   bool split_h;   // bf16: SwiGLU output as a hi + lo bf16 pair
+  int h_ld, sg_ld, sd_ld;   // padded row strides (elements)
 };
 
 bool dtypes_ok(int xdt, int wdt) {
@@ -212,11 +213,14 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
     L.can_sk4 = S > 16.0;
   }
   const int xb = xbytes(xdt);
+  L.h_ld = F + kPadBytes / xb;
+  L.sg_ld = D + kPadBytes / 2;     // fp16 copies of gate/up rows (K = D)
+  L.sd_ld = F + kPadBytes / 2;     // fp16 copies of down rows (K = F)
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
-  L.H = take((size_t)Pmax * F * xb + 16);
+  L.H = take((size_t)Pmax * L.h_ld * xb + 16);
   L.split_h = xdt == MOE_BF16 && !(o.flags & MOE_OPT_BF16_PLAIN_H);
-  L.H2 = take(L.split_h ? (size_t)Pmax * F * 2 + 16 : 0);
+  L.H2 = take(L.split_h ? (size_t)Pmax * L.h_ld * 2 + 16 : 0);
   L.Y = take((size_t)Pmax * D * 4 + 16);   // Ypair in f32
   L.full_tiles = take((size_t)L.cap_tiles * 8);
   L.sk1 = take((size_t)L.cap_sk1 * 16);
@@ -224,9 +228,9 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.fat_slot = take((size_t)n_exp * 4);
   L.fat_list = take((size_t)n_exp * 4);
   L.meta = take(kMetaCount * 4);
-  L.stg_g = take((size_t)L.max_fat * F * D * 2);
-  L.stg_u = take((size_t)L.max_fat * F * D * 2);
-  L.stg_d = take((size_t)L.max_fat * D * F * 2);
+  L.stg_g = take((size_t)L.max_fat * F * L.sg_ld * 2);
+  L.stg_u = take((size_t)L.max_fat * F * L.sg_ld * 2);
+  L.stg_d = take((size_t)L.max_fat * D * L.sd_ld * 2);
   L.bytes = off;
   return L;
 }
@@ -427,6 +431,13 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u))
     return fail(MOE_EINVAL, "workspace NULL or not 256-byte aligned");
   const FwdLayout L = fwd_layout(d, D, F, x_dtype, wdt, o);
+  const size_t Pmax_rows = (size_t)d.T * d.k + (size_t)d.n_shared * d.T;
+  const size_t lim31 = ((size_t)1 << 31) - 1;
+  if ((size_t)d.T * D * xbytes(x_dtype) > lim31 ||
+      Pmax_rows * (F * xbytes(x_dtype) + kPadBytes) > lim31 ||
+      (size_t)D * (F + kPadBytes) * 4 > lim31)
+    return fail(MOE_EUNSUPPORTED, "x, the SwiGLU buffer and each weight "
+                "matrix must each stay below 2 GiB");
   if (ws_bytes < L.bytes)
     return fail(MOE_EWORKSPACE, "forward workspace %zu bytes < %zu needed",
                 ws_bytes, L.bytes);
@@ -468,13 +479,16 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     PhaseScope ps(rec, 1, s);
     const int grid = info.ncu * 8;
     e = launch_dequant_fat(w_gate.data, w_gate.scales, b + L.stg_g, F, D,
-                           (const int32_t*)(b + L.fat_list), meta, grid, s);
+                           L.sg_ld, (const int32_t*)(b + L.fat_list), meta,
+                           grid, s);
     if (e == hipSuccess)
       e = launch_dequant_fat(w_up.data, w_up.scales, b + L.stg_u, F, D,
-                             (const int32_t*)(b + L.fat_list), meta, grid, s);
+                             L.sg_ld, (const int32_t*)(b + L.fat_list), meta,
+                             grid, s);
     if (e == hipSuccess)
       e = launch_dequant_fat(w_down.data, w_down.scales, b + L.stg_d, D, F,
-                             (const int32_t*)(b + L.fat_list), meta, grid, s);
+                             L.sd_ld, (const int32_t*)(b + L.fat_list), meta,
+                             grid, s);
     if (e != hipSuccess) return hip_fail(e, "dequant kernel");
   }
 
@@ -490,24 +504,28 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   void* Y = b + L.Y;
   const int sk_rb1_grid_cap = info.ncu * 8;
   const int sk_rb4_grid_cap = info.ncu * 4;
-  const int full_grid_cap = info.ncu * 2;
+  const int full_grid_cap = info.ncu;      // one 128 KB-LDS block per CU
 
   for (int stage = 0; stage < 2; ++stage) {
     g.mode = stage;
     if (stage == 0) {
       g.K = D; g.N = F; g.A = x; g.A2 = nullptr; g.out = H; g.out2 = H2;
+      g.a_bytes = (uint32_t)((size_t)d.T * D * xbytes(x_dtype));
+      g.a_ld = D; g.s_ld = L.sg_ld; g.out_ld = L.h_ld;
       g.B0 = w_gate.data; g.B0s = w_gate.scales;
       g.B1 = w_up.data; g.B1s = w_up.scales;
       g.S0 = b + L.stg_g; g.S1 = b + L.stg_u;
     } else {
       g.K = F; g.N = D; g.A = H; g.A2 = H2; g.out = Y; g.out2 = nullptr;
+      g.a_bytes = (uint32_t)(Pmax_rows * L.h_ld * xbytes(x_dtype));
+      g.a_ld = L.h_ld; g.s_ld = L.sd_ld; g.out_ld = D;
       g.B0 = w_down.data; g.B0s = w_down.scales;
       g.B1 = nullptr; g.B1s = nullptr;
       g.S0 = b + L.stg_d; g.S1 = nullptr;
     }
     if (L.can_full) {
       PhaseScope ps(rec, stage == 0 ? 2 : 4, s);
-      const int nnb = stage == 0 ? F / 64 : D / 128;
+      const int nnb = stage == 0 ? F / 128 : (D + 255) / 256;
       g.list = (const int32_t*)(b + L.full_tiles);
       g.meta_index = kMetaFullTiles;
       const int grid = (int)std::min<int64_t>((int64_t)L.cap_tiles * nnb, full_grid_cap);

@@ -20,10 +20,12 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kChunk = 64;
 constexpr int kMaxExperts = 1024;
 
-// Full MFMA tile geometry (rows of A, output columns, K per stage).
-constexpr int kFullBM = 128;
-constexpr int kFullBN = 128;
-constexpr int kFullBK = 64;
+// Token rows per full-tile work item (the classify kernel's tile list).
+constexpr int kFullBM = 256;
+// Row padding of the buffers the library lays out itself (the SwiGLU output
+// and the fp16 fat-expert copies): 256 bytes, so rows whose unpadded stride
+// is a large power of two do not all start on the same L2 channel.
+constexpr int kPadBytes = 256;
 // Split-K tile: output columns per item and rows per row block.
 constexpr int kSkNB = 64;
 constexpr int kSkRows = 64;   // rows per split-K group (4 blocks of 16)
@@ -72,6 +74,10 @@ struct GemmArgs {
   int K, N;                 // K: reduction; N: output width (F or D)
   const void* A;            // gate/up: x [T, D]; down: H [P, F]
   const void* A2;           // down, bf16 split H: the low plane; else null
+  uint32_t a_bytes;         // bytes of A (and of A2): below 2^31
+  int a_ld;                 // A row stride, elements
+  int s_ld;                 // row stride of the fp16 fat-expert copies, elements
+  int out_ld;               // output row stride, elements
   const int32_t* pair_token;// gather map for gate/up
   const int32_t* offsets;   // [n_exp + 1]
   const float* pair_w;      // [P]
@@ -94,8 +100,9 @@ hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
 hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
                               int grid, hipStream_t s);
 hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
-                              int rows, int K, const int32_t* fat_list,
-                              const int32_t* meta, int grid, hipStream_t s);
+                              int rows, int K, int out_ld,
+                              const int32_t* fat_list, const int32_t* meta,
+                              int grid, hipStream_t s);
 hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
                                int64_t rows, int K, hipStream_t s);
 hipError_t launch_combine(const void* ypair, const int32_t* tok2pair,
