@@ -231,56 +231,65 @@ hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s) {
 }
 
 // ---- dequantise once --------------------------------------------------------
+//
+// One unit = 8 consecutive values of a row: 4 bytes of nibbles in, 16 bytes
+// of fp16 out, so a wave's loads cover 256 contiguous bytes and its stores
+// 1 KB. The four lanes of a 32-value block share its scale.
 
-__device__ __forceinline__ void dequant_unit(const uint8_t* q, const uint16_t* sc,
-                                             _Float16* out, size_t row, int kb,
-                                             int K) {
-  const uint4 raw = ldg16(q + row * (size_t)(K / 2) + (size_t)kb * 16);
-  const uint16_t sb = sc[row * (size_t)(K / 32) + kb];
-  half8 h[4];
-  dequant32(raw, __builtin_bit_cast(_Float16, sb), h);
-  uint4* dst = reinterpret_cast<uint4*>(out + row * (size_t)K + (size_t)kb * 32);
+__device__ __forceinline__ uint4 dequant8(uint32_t word, _Float16 s) {
+  const half2v s2 = {s, s};
+  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const uint32_t x = word ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu;
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+  uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = __builtin_bit_cast(uint4, h[i]);
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
+    half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u);
+    h = (h + off) * s2;
+    o[b] = __builtin_bit_cast(uint32_t, h);
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
 }
 
 // Fat experts: slot s of the staging buffer holds expert fat_list[s]'s
-// [rows, K] matrix as fp16. Grid-stride over (slot, row, 32-value block).
+// [rows, K] matrix as fp16, rows out_ld apart. Grid-stride over 8-value units.
 __global__ __launch_bounds__(256) void dequant_fat_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
     _Float16* __restrict__ out, int rows, int K, int out_ld,
     const int32_t* __restrict__ fat_list, const int32_t* __restrict__ meta) {
   const int nfat = meta[kMetaFat];
-  const int kbs = K / 32;
-  const size_t per = (size_t)rows * kbs;
+  const int upr = K / 8;                        // units per row
+  const size_t per = (size_t)rows * upr;
   const size_t total = per * (size_t)nfat;
   for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < total;
        u += (size_t)gridDim.x * blockDim.x) {
     const int slot = (int)(u / per);
     const size_t rem = u - (size_t)slot * per;
-    const int row = (int)(rem / kbs);
-    const int kb = (int)(rem - (size_t)row * kbs);
-    const size_t e = (size_t)fat_list[slot];
-    const uint4 raw = ldg16(q + (e * rows + row) * (size_t)(K / 2) + (size_t)kb * 16);
-    const uint16_t sb = sc[(e * rows + row) * (size_t)kbs + kb];
-    half8 h[4];
-    dequant32(raw, __builtin_bit_cast(_Float16, sb), h);
-    uint4* dst = reinterpret_cast<uint4*>(
-        out + ((size_t)slot * rows + row) * (size_t)out_ld + (size_t)kb * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = __builtin_bit_cast(uint4, h[i]);
+    const int row = (int)(rem / upr);
+    const int c8 = (int)(rem - (size_t)row * upr);
+    const size_t er = (size_t)fat_list[slot] * rows + row;
+    const uint32_t word = reinterpret_cast<const uint32_t*>(q + er * (size_t)(K / 2))[c8];
+    const uint16_t sb = sc[er * (size_t)(K / 32) + (c8 >> 2)];
+    reinterpret_cast<uint4*>(out + ((size_t)slot * rows + row) * (size_t)out_ld)[c8] =
+        dequant8(word, __builtin_bit_cast(_Float16, sb));
   }
 }
 
 __global__ __launch_bounds__(256) void dequant_rows_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
     _Float16* __restrict__ out, int64_t rows, int K) {
-  const int kbs = K / 32;
-  const size_t total = (size_t)rows * kbs;
+  const int upr = K / 8;
+  const size_t total = (size_t)rows * upr;
   for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < total;
        u += (size_t)gridDim.x * blockDim.x) {
-    const size_t row = u / kbs;
-    dequant_unit(q, sc, out, row, (int)(u - row * kbs), K);
+    const size_t row = u / upr;
+    const int c8 = (int)(u - row * upr);
+    const uint32_t word = reinterpret_cast<const uint32_t*>(q + row * (size_t)(K / 2))[c8];
+    const uint16_t sb = sc[row * (size_t)(K / 32) + (c8 >> 2)];
+    reinterpret_cast<uint4*>(out + row * (size_t)K)[c8] =
+        dequant8(word, __builtin_bit_cast(_Float16, sb));
   }
 }
 
@@ -296,7 +305,7 @@ hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
 
 hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
                                int64_t rows, int K, hipStream_t s) {
-  const size_t units = (size_t)rows * (K / 32);
+  const size_t units = (size_t)rows * (K / 8);
   const int grid = (int)std::min<size_t>((units + 255) / 256, 65536);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_rows_kernel, dim3(grid), dim3(256), 0, s,

@@ -1,0 +1,311 @@
+// Wide fused-dequant tile for experts holding 17..64 rows of a prompt.
+//
+// For such an expert every output column is multiplied by the same few
+// dozen gathered rows, so re-reading those rows per 64-column block (what the
+// split-K tile does) costs several times the weight bytes. Here one block of
+// 4 waves covers 256 output columns: the expert's rows (<= 64) are staged
+// once per 128-deep K chunk in LDS by direct-to-LDS loads and shared by the
+// four waves, while each wave streams its own 64 weight rows from HBM three
+// chunks ahead and, for 4-bit weights, dequantises them in registers (the
+// fused-dequant tiles the Strata PR #4366 route description leaves to the
+// experts under the fat-row threshold).
+//
+// Lane (n = l % 16, q = l / 16) of v_mfma_f32_16x16x32 holds, for K sub-chunk
+// i of a 128-deep chunk, A/B values at k = 32 q + 8 i .. + 8, matched between
+// operands. A row r of a chunk is 256 bytes in LDS with 16-byte chunk c at
+// c ^ (r % 16), so the 16 rows of one operand read hit 16 distinct bank
+// groups. Gate/up column blocks cb = 0..3 of a wave are W_gate f0.., W_up
+// f0.., W_gate f0+16.., W_up f0+16.., f0 = 128 nb + 32 w.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+struct WF16 { using S = _Float16; using V8 = half8; };
+struct WBF16 { using S = __bf16; using V8 = bf16x8; };
+
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ float swiglu(float g, float u, float c) {
+  if (c > 0.f) {
+    g = fminf(g, c);
+    u = fminf(fmaxf(u, -c), c);
+  }
+  return g / (1.f + expf(-g)) * u;
+}
+
+// 32 nibbles (low first) times their block scale -> 4 x 8 fp16, exactly
+// fp16_rne(q * s): 0x6400 | v is 1024 + v, v = nibble ^ 8, minus 1032 is q.
+__device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
+  const half2v s2 = {s, s};
+  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    const uint32_t x = words[wi] ^ 0x88888888u;
+    const uint32_t lo = x & 0x0F0F0F0Fu;
+    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
+      half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u);
+      h = (h + off) * s2;
+      out[wi][2 * b] = h[0];
+      out[wi][2 * b + 1] = h[1];
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+constexpr int kChunkK = 128;            // K per LDS chunk
+constexpr int kRowsW = 64;              // token rows per item (4 blocks of 16)
+constexpr int kChunkB = kRowsW * kChunkK * 2;   // 16 KB per LDS chunk
+constexpr int kPD = 3;                  // weight chunks ahead per wave
+constexpr int kNA = 3;                  // LDS chunks of A (two ahead)
+
+}  // namespace
+
+// Weight operand of one 128-deep chunk for one lane: 4 column blocks.
+template <int WQ>
+struct WChunk;
+template <>
+struct WChunk<1> { uint4 q[4]; uint32_t s[4]; };
+template <>
+struct WChunk<0> { uint4 d[4][4]; };
+
+template <class TT, int WQ, int MODE>
+__global__ __launch_bounds__(256, 2) void gemm_wide_kernel(GemmArgs a) {
+  using S = typename TT::S;
+  using V8 = typename TT::V8;
+  __shared__ __attribute__((aligned(1024))) char smem[kNA * kChunkB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, q = lane >> 4;
+  const int K = a.K, N = a.N;
+  const int nch = K / kChunkK;
+  const int cols_per_item = MODE == 0 ? 128 : 256;      // features / outputs
+  const int NNB = (N + cols_per_item - 1) / cols_per_item;
+  const int n_items = a.meta[a.meta_index] * NNB;
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.A, a.a_bytes);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int g = item / NNB;
+    const int nb = item - g * NNB;
+    const int e = a.list[4 * g];
+    const int row0 = a.list[4 * g + 1];
+    const int nrows = a.list[4 * g + 2];
+    const int off = a.offsets[e];
+
+    // A staging: block of 16 x 1 KB per chunk, 4 per wave; lane writes row
+    // 4 b + lane / 16 at physical chunk lane % 16 = logical (lane%16)^(row%16)
+    uint32_t aoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * (wave * 4 + j) + (lane >> 4);
+      const int rr = row0 + min(r, nrows - 1);
+      const uint32_t prow = MODE == 0 ? (uint32_t)a.pair_token[off + rr]
+                                      : (uint32_t)(off + rr);
+      const int c = (lane & 15) ^ (r & 15);
+      aoff[j] = prow * (uint32_t)a.a_ld * 2u + (uint32_t)c * 16u;
+    }
+    auto issue_a = [&](int ch) {
+      char* base = smem + (ch % kNA) * kChunkB + wave * 4 * 1024;
+      const int soff = min(ch, nch - 1) * kChunkK * 2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(base + j * 1024),
+                                                 16, (int)aoff[j], soff, 0, 0);
+    };
+
+    // this wave's 4 weight rows-blocks (16 rows each)
+    const int col0 = MODE == 0 ? nb * 128 + wave * 32 : nb * 256 + wave * 64;
+    const bool active = col0 < N;       // wave-uniform
+    const char* bp[4];
+    const uint16_t* bsp[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      int row;
+      const void* base;
+      const void* sbase;
+      if (MODE == 0) {
+        row = min(col0 + (cb >> 1) * 16 + n, N - 1);
+        base = (cb & 1) ? a.B1 : a.B0;
+        sbase = (cb & 1) ? a.B1s : a.B0s;
+      } else {
+        row = min(col0 + cb * 16 + n, N - 1);
+        base = a.B0;
+        sbase = a.B0s;
+      }
+      const size_t wrow = (size_t)e * N + row;
+      if (WQ) {
+        bp[cb] = (const char*)base + wrow * (size_t)(K / 2);
+        bsp[cb] = (const uint16_t*)sbase + wrow * (size_t)(K / 32);
+      } else {
+        bp[cb] = (const char*)base + wrow * (size_t)K * 2;
+        bsp[cb] = nullptr;
+      }
+    }
+    auto load_w = [&](int ch, WChunk<WQ>& w) {
+      const int cc = min(ch, nch - 1);
+      const int k0 = cc * kChunkK + q * 32;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        if constexpr (WQ) {
+          w.q[cb] = ldg16(bp[cb] + k0 / 2);
+          w.s[cb] = (uint32_t)bsp[cb][k0 / 32];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w.d[cb][i] = ldg16(bp[cb] + (size_t)k0 * 2 + i * 16);
+        }
+      }
+    };
+
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int ch, const WChunk<WQ>& w) {
+      V8 bv[4][4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        if constexpr (WQ) {
+          half8 h[4];
+          dequant32(w.q[cb], __builtin_bit_cast(_Float16, (uint16_t)w.s[cb]), h);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bv[cb][i] = __builtin_bit_cast(V8, h[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bv[cb][i] = __builtin_bit_cast(V8, w.d[cb][i]);
+        }
+      }
+      const char* As = smem + (ch % kNA) * kChunkB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int r = rb * 16 + n;
+          const int c = (q * 4 + i) ^ (r & 15);
+          const V8 av = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(As + r * 256 + c * 16));
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(av, bv[cb][i], acc[rb][cb]);
+        }
+      }
+    };
+
+    // Ring: A two chunks ahead in LDS, weights three chunks ahead in
+    // registers. Issue order is W0 A0 W1 A1 W2, then per step s: A(s+2),
+    // compute(s), W(s+3). vmcnt retires in order, so at the top of step s
+    // "A(s) landed" is "at most W(s+1), A(s+1), W(s+2) outstanding", which
+    // also retires W(s) (issued before A(s)). The barrier then publishes
+    // A(s) to all waves and frees the buffer A(s+2) refills (last read by
+    // compute(s-1), before this barrier). Past the end, loads re-read the
+    // last chunk into buffers and slots no one reads.
+    constexpr int kWvm = WQ ? 8 : 16;    // weight loads per chunk per lane
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    WChunk<WQ> w0, w1, w2;
+    load_w(0, w0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(1, w1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(2, w2);
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int ch, WChunk<WQ>& w) {
+      wait_vmcnt<2 * kWvm + 4>();
+      __builtin_amdgcn_s_barrier();
+      issue_a(ch + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (active && ch < nch) compute(ch, w);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(ch + kPD, w);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // every path issues the same loads (steps past the end only load), so
+    // the compiler's own waits agree with the counted ones
+    const int nsteps = (nch + kPD - 1) / kPD * kPD;
+    for (int ch = 0; ch < nsteps; ch += kPD) {
+      step(ch, w0);
+      step(ch + 1, w1);
+      step(ch + 2, w2);
+    }
+
+    if (active) {
+      // 16x16 accumulator r of lane l: row 4 (l / 16) + r, column l % 16
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rb * 16 + q * 4 + r;
+          if (row >= nrows) continue;
+          const size_t prow = (size_t)(off + row0 + row);
+          if (MODE == 0) {
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+              const int f = col0 + pr * 16 + n;
+              const float h = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
+              const S hv = (S)h;
+              reinterpret_cast<S*>(a.out)[prow * a.out_ld + f] = hv;
+              if (a.out2) reinterpret_cast<S*>(a.out2)[prow * a.out_ld + f] = (S)(h - (float)hv);
+            }
+          } else {
+            const float pw = a.pair_w[prow];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              const int d = col0 + cb * 16 + n;
+              if (d < N) reinterpret_cast<float*>(a.out)[prow * a.out_ld + d] = acc[rb][cb][r] * pw;
+            }
+          }
+        }
+    }
+  }
+}
+
+hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
+                            hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+#define MOE_WIDE(TT, WQ)                                                              \
+  do {                                                                                \
+    if (a.mode == 0)                                                                  \
+      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 0>), dim3(grid), dim3(256), 0, s, a); \
+    else                                                                              \
+      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 1>), dim3(grid), dim3(256), 0, s, a); \
+  } while (0)
+  if (xdt == MOE_F16 && wdt == MOE_Q4B32) MOE_WIDE(WF16, 1);
+  else if (xdt == MOE_F16 && wdt == MOE_F16) MOE_WIDE(WF16, 0);
+  else if (xdt == MOE_BF16 && wdt == MOE_BF16) MOE_WIDE(WBF16, 0);
+  else return hipErrorInvalidValue;
+#undef MOE_WIDE
+  return hipGetLastError();
+}
+
+}  // namespace moe

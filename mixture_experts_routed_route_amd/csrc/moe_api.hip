@@ -545,8 +545,15 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       if (L.can_sk4) {
         g.list = (const int32_t*)(b + L.sk4);
         g.meta_index = kMetaSk4;
-        const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * nnb, sk_rb4_grid_cap);
-        e = launch_gemm_splitk(g, x_dtype, wdt, 4, grid, s);
+        if (x_dtype == MOE_F32) {
+          const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * nnb, sk_rb4_grid_cap);
+          e = launch_gemm_splitk(g, x_dtype, wdt, 4, grid, s);
+        } else {
+          // groups of 17..64 rows: wide fused-dequant tile, 256 columns/item
+          const int wnb = stage == 0 ? (F + 127) / 128 : (D + 255) / 256;
+          const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * wnb, info.ncu * 2);
+          e = launch_gemm_wide(g, x_dtype, wdt, grid, s);
+        }
         if (e != hipSuccess) return hip_fail(e, "split-K kernel");
       }
     }

@@ -99,6 +99,8 @@ hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
                             hipStream_t s);
 hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
                               int grid, hipStream_t s);
+hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
+                            hipStream_t s);
 hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
                               int rows, int K, int out_ld,
                               const int32_t* fat_list, const int32_t* meta,
