@@ -35,8 +35,15 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "mixture_experts_routed_route_amd", "csrc",
-                          "forward_kernels.hip")
+CSRC = os.path.join(ROOT, "mixture_experts_routed_route_amd", "csrc")
+# source file of each phase's kernel: a committed counter summary applies to
+# the phase only while this file (and the shared header) is unchanged
+KERNEL_SRC = {"gateup_full": "gemm_full.hip", "down_full": "gemm_full.hip",
+              "gateup_splitk": "forward_kernels.hip",
+              "down_splitk": "forward_kernels.hip",
+              "dequant_once": "forward_kernels.hip",
+              "combine": "forward_kernels.hip",
+              "classify": "forward_kernels.hip"}
 
 
 def parse():
@@ -54,11 +61,17 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-phase-events", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also copy MIB MiB device-to-device once (a plain "
+                         "copy of known size for scaling counter readings)")
     return ap.parse_args()
 
 
-def source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_SRC[kernel], "moe_internal.h"):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, kernel: str):
@@ -71,7 +84,7 @@ def load_traffic(workload: str, kernel: str):
         rec = json.load(open(path))
     except Exception:
         return None
-    if rec.get("source_sha") != source_sha():
+    if rec.get("source_sha") != source_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -127,6 +140,13 @@ def main():
                         workspace=fwd_ws)
         return pl
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
