@@ -188,7 +188,7 @@ size_t moe_forward_workspace_bytes(const moe_plan *plan, int32_t D, int32_t F,
  * compute the dispatch buffer in the compute dtype and return the layer
  * output in the residual's fp32, mini-AGI PR #4, minagi/pool.py, the
  * compute-dtype comment) or x's dtype (one rounding of that f32 result).
- * Each kept pair's weighted output is held in f32 before the combine. */
+ * Each kept pair's output is held in f32; the combine weights and sums them. */
 moe_status moe_forward(const moe_plan *plan, const void *x, int32_t x_dtype,
                        moe_weight w_gate, moe_weight w_up, moe_weight w_down,
                        int32_t D, int32_t F, void *y, int32_t y_dtype,

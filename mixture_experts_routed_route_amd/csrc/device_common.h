@@ -1,0 +1,92 @@
+// Device helpers shared by the gfx950 kernels: MFMA wrappers, buffer
+// resources for direct-to-LDS loads, counted waits, the clamped SwiGLU and
+// the 4-bit block decode.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <class V>
+__device__ __forceinline__ V as_v8(uint4 u) { return __builtin_bit_cast(V, u); }
+
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Raw buffer resource over [base, base + bytes): scalar registers hold the
+// descriptor, lanes pass 32-bit byte offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// vmcnt(N) and lgkmcnt(0) together.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+
+// h = silu(min(g, c)) * clamp(u, -c, c); c <= 0: plain silu(g) * u.
+__device__ __forceinline__ float swiglu(float g, float u, float c) {
+  if (c > 0.f) {
+    g = fminf(g, c);
+    u = fminf(fmaxf(u, -c), c);
+  }
+  return g / (1.f + expf(-g)) * u;
+}
+
+// 32 consecutive 4-bit values (16 bytes, low nibble first) times their block
+// scale, as 4 x 8 fp16: fp16 bits 0x6400 | v encode 1024 + v exactly, v =
+// nibble ^ 8; subtracting 1032 leaves the signed value q exactly, and one
+// fp16 multiply gives fp16_rne(q * s).
+__device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
+  const half2v s2 = {s, s};
+  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    const uint32_t x = words[wi] ^ 0x88888888u;
+    const uint32_t lo = x & 0x0F0F0F0Fu;
+    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      // bytes of the result: [lo_b, 0, hi_b, 0] (selector 12 gives zero)
+      const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
+      const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+      half2v h = __builtin_bit_cast(half2v, pr);
+      h = (h + off) * s2;
+      out[wi][2 * b] = h[0];
+      out[wi][2 * b + 1] = h[1];
+    }
+  }
+}
+
+}  // namespace moe

@@ -1,8 +1,9 @@
 // Forward kernels of the routed MoE layer on gfx950.
 //
 // Per expert: gathered rows of x times W_gate and W_up, clamped SwiGLU, times
-// W_down, each pair's output scaled by its routing weight (mini-AGI PR #4,
-// minagi/pool.py, `experts()`; the clamp from Strata PR #4366, "Approach").
+// W_down; the combine scales each pair's output by its routing weight
+// (mini-AGI PR #4, minagi/pool.py, `experts()`; the clamp from Strata PR
+// #4366, "Approach").
 // Three routes, chosen per expert from its row count on the device:
 //   full    LDS-staged MFMA tile (v_mfma_f32_32x32x16) for experts with many
 //           rows; the fused SwiGLU runs in the gate/up tile's epilogue;
@@ -13,11 +14,11 @@
 //           #1607): weights stream once from HBM straight into
 //           v_mfma_f32_16x16x32 operands, four waves split K and reduce in LDS
 //           in a fixed order; 4-bit weights are dequantised in registers.
-// The combine gathers each token's weighted pair rows in fixed order, with no
-// atomics.
+// The combine gathers each token's pair rows, weighted, in fixed order, with
+// no atomics.
 #include <algorithm>
 
-#include "moe_internal.h"
+#include "device_common.h"
 
 namespace moe {
 
@@ -37,64 +38,6 @@ struct F32T {
   using S = float;
   static constexpr int kBytes = 4;
 };
-
-__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma16f32(float a, float b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-template <class V>
-__device__ __forceinline__ V as_v8(uint4 u) { return __builtin_bit_cast(V, u); }
-
-__device__ __forceinline__ uint4 ldg16(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-// h = silu(min(g, c)) * clamp(u, -c, c); c <= 0: plain silu(g) * u.
-__device__ __forceinline__ float swiglu(float g, float u, float c) {
-  if (c > 0.f) {
-    g = fminf(g, c);
-    u = fminf(fmaxf(u, -c), c);
-  }
-  return g / (1.f + expf(-g)) * u;
-}
-
-// 32 consecutive 4-bit values (16 bytes, low nibble first) times their block
-// scale, as 4 x 8 fp16: fp16 bits 0x6400 | v encode 1024 + v exactly, v =
-// nibble ^ 8; subtracting 1032 leaves the signed value q exactly, and one
-// fp16 multiply gives fp16_rne(q * s).
-__device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
-  const half2v s2 = {s, s};
-  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int wi = 0; wi < 4; ++wi) {
-    const uint32_t x = words[wi] ^ 0x88888888u;
-    const uint32_t lo = x & 0x0F0F0F0Fu;
-    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      // bytes of the result: [lo_b, 0, hi_b, 0] (selector 12 gives zero)
-      const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
-      const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
-      half2v h = __builtin_bit_cast(half2v, pr);
-      h = (h + off) * s2;
-      out[wi][2 * b] = h[0];
-      out[wi][2 * b + 1] = h[1];
-    }
-  }
-}
 
 // ---- classify -------------------------------------------------------------
 
@@ -131,15 +74,18 @@ __device__ __forceinline__ int block_excl(int v, int* total, int* sh) {
 // kFullBM-row tiles; split-K experts into groups of <= 64 rows, groups of at
 // most 16 rows going to the one-block list.
 __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
-  __shared__ int cnt[kMaxExperts + 1];
-  __shared__ int rte[kMaxExperts + 1];
-  __shared__ int order[kMaxExperts + 1];
+  constexpr int kPadE = (kMaxExperts + 1 + 3) / 4 * 4;
+  __shared__ int cnt[kPadE];
+  __shared__ int rte[kPadE];
+  __shared__ __attribute__((aligned(16))) int fkey[kPadE];   // rows if full, else -1
+  __shared__ int order[kPadE];
   __shared__ int sh[16];
   __shared__ int nfull_sh;
   const int n = a.n_exp;
+  const int n4 = (n + 3) / 4 * 4;
   if (threadIdx.x == 0) nfull_sh = 0;
-  for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    const int c = a.counts[e];
+  for (int e = threadIdx.x; e < n4; e += blockDim.x) {
+    const int c = e < n ? a.counts[e] : 0;
     int r = kRouteNone;
     if (c > 0) {
       if (a.mode == 0) r = kRouteSplitK;
@@ -148,15 +94,21 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
     }
     cnt[e] = c;
     rte[e] = r;
+    fkey[e] = r >= kRouteFull ? c : -1;
   }
   __syncthreads();
+  // rank among full/fat experts: more rows first, then the lower index
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     if (rte[e] < kRouteFull) continue;
     int rank = 0;
     const int c = cnt[e];
-    for (int f = 0; f < n; ++f)
-      if (rte[f] >= kRouteFull && (cnt[f] > c || (cnt[f] == c && f < e)))
-        ++rank;
+    for (int f = 0; f < n4; f += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(&fkey[f]);
+      rank += (v.x > c || (v.x == c && f + 0 < e)) ? 1 : 0;
+      rank += (v.y > c || (v.y == c && f + 1 < e)) ? 1 : 0;
+      rank += (v.z > c || (v.z == c && f + 2 < e)) ? 1 : 0;
+      rank += (v.w > c || (v.w == c && f + 3 < e)) ? 1 : 0;
+    }
     order[rank] = e;
     atomicAdd(&nfull_sh, 1);
   }
@@ -202,12 +154,20 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
         for (int g = 0; g < ng; ++g) {
           const int row0 = g * kSkRows;
           const int rows = min(kSkRows, c - row0);
+          const int pstart = a.offsets[e] + row0;
           int32_t* dst = (rows <= 16) ? a.sk1 + 4 * p1
                                       : a.sk4 + 4 * (p4 + g);
           dst[0] = e;
           dst[1] = row0;
           dst[2] = rows;
-          dst[3] = 0;
+          dst[3] = pstart;
+          if (rows <= 16 && a.sk1_tok) {
+            int tk[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) tk[t] = a.pair_token[pstart + min(t, rows - 1)];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) a.sk1_tok[16 * p1 + t] = tk[t];
+          }
         }
       }
       a.fat_slot[e] = fat ? pf : -1;
@@ -473,11 +433,10 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
             if (a.out2) reinterpret_cast<S*>(a.out2)[prow * a.out_ld + f] = (S)(h - (float)hv);
           }
         } else {
-          const float pw = a.pair_w[prow];
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const int d = nb * 64 + cb * 16 + n;
-            reinterpret_cast<float*>(a.out)[prow * a.out_ld + d] = acc[rb][cb][r] * pw;
+            reinterpret_cast<float*>(a.out)[prow * a.out_ld + d] = acc[rb][cb][r];
           }
         }
       }
@@ -594,11 +553,10 @@ __device__ __forceinline__ void splitk_body32(const GemmArgs& a, int item,
             out[prow * a.out_ld + f] = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
           }
         } else {
-          const float pw = a.pair_w[prow];
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const int d = nb * 64 + cb * 16 + n;
-            out[prow * a.out_ld + d] = acc[rb][cb][r] * pw;
+            out[prow * a.out_ld + d] = acc[rb][cb][r];
           }
         }
       }
@@ -650,16 +608,18 @@ hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
 
 // ---- combine ------------------------------------------------------------------------
 //
-// y[t, d..d+7] = sum over j of Ypair[tok2pair[t, j], d..d+7] (j ascending,
-// dropped pairs skipped) + the shared expert's row. Ypair holds each kept
-// pair's weighted output in f32; the sum is f32 and rounded once to y's
-// dtype. Each output is written by one thread: no atomics.
+// y[t, d..d+7] = sum over j of w[t, j] * Ypair[tok2pair[t, j], d..d+7] (j
+// ascending, dropped pairs skipped) + the shared expert's row (weight 1).
+// Ypair holds each kept pair's unweighted output in f32; each product and
+// the sum are f32 and the result is rounded once to y's dtype (mini-AGI PR
+// #4, minagi/pool.py: the weighted gather back to tokens). Each output is
+// written by one thread: no atomics.
 
 template <class S>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ ypair, const int32_t* __restrict__ tok2pair,
-    const int32_t* __restrict__ offsets, int T, int D, int k, int n_shared,
-    int E, S* __restrict__ y) {
+    const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
+    int T, int D, int k, int n_shared, int E, S* __restrict__ y) {
   const int per_row = D / 8;
   const size_t total = (size_t)T * per_row;
   const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
@@ -667,17 +627,22 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int t = (int)(idx / per_row);
   const int d = (int)(idx - (size_t)t * per_row) * 8;
   float4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-  auto add_row = [&](size_t p) {
-    const float4* src = reinterpret_cast<const float4*>(ypair + p * D + d);
+  for (int j = 0; j < k; ++j) {
+    const int p = tok2pair[(size_t)t * k + j];
+    if (p < 0) continue;
+    const float w = topk_w[(size_t)t * k + j];
+    const float4* src = reinterpret_cast<const float4*>(ypair + (size_t)p * D + d);
+    const float4 a = src[0], b = src[1];
+    lo.x += a.x * w; lo.y += a.y * w; lo.z += a.z * w; lo.w += a.w * w;
+    hi.x += b.x * w; hi.y += b.y * w; hi.z += b.z * w; hi.w += b.w * w;
+  }
+  if (n_shared) {
+    const float4* src = reinterpret_cast<const float4*>(
+        ypair + (size_t)(offsets[E] + t) * D + d);
     const float4 a = src[0], b = src[1];
     lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
     hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
-  };
-  for (int j = 0; j < k; ++j) {
-    const int p = tok2pair[(size_t)t * k + j];
-    if (p >= 0) add_row((size_t)p);
   }
-  if (n_shared) add_row((size_t)(offsets[E] + t));
   S* out = y + (size_t)t * D + d;
   if constexpr (sizeof(S) == 4) {
     reinterpret_cast<float4*>(out)[0] = lo;
@@ -692,8 +657,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }
 
 hipError_t launch_combine(const void* ypair, const int32_t* tok2pair,
-                          const int32_t* offsets, int T, int D, int k,
-                          int n_shared, int E, int ydt, void* y,
+                          const float* topk_w, const int32_t* offsets, int T,
+                          int D, int k, int n_shared, int E, int ydt, void* y,
                           hipStream_t s) {
   const size_t total = (size_t)T * (D / 8);
   if (total == 0) return hipSuccess;
@@ -701,13 +666,13 @@ hipError_t launch_combine(const void* ypair, const int32_t* tok2pair,
   const float* yp = (const float*)ypair;
   if (ydt == MOE_F32)
     hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, s,
-                       yp, tok2pair, offsets, T, D, k, n_shared, E, (float*)y);
+                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (float*)y);
   else if (ydt == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<__bf16>, dim3(grid), dim3(256), 0, s,
-                       yp, tok2pair, offsets, T, D, k, n_shared, E, (__bf16*)y);
+                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (__bf16*)y);
   else
     hipLaunchKernelGGL(combine_kernel<_Float16>, dim3(grid), dim3(256), 0, s,
-                       yp, tok2pair, offsets, T, D, k, n_shared, E, (_Float16*)y);
+                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (_Float16*)y);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@
 // blocks; within a round the items of one XCD (blocks b = x mod 8) are a
 // contiguous run of a 4 x 8 (row tiles x column tiles) grouping, so the 32
 // blocks resident on an XCD share their A and B slices in its L2.
-#include "moe_internal.h"
+#include "device_common.h"
 
 namespace moe {
 
@@ -37,23 +37,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 struct F16T { using S = _Float16; using V8 = half8; using V4 = half4v; };
 struct BF16T { using S = __bf16; using V8 = bf16x8; using V4 = bf16x4; };
 
-__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Raw buffer resource over [base, base + bytes): scalar registers hold the
-// descriptor, lanes pass 32-bit byte offsets.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
-                                                            uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)bytes, 0x00020000);
-}
-
-
-
 // 64-byte LDS rows (32 K values); 16-byte chunk c of row r sits at chunk
 // c ^ ((r >> 2) & 3): the 16 rows one MFMA operand read touches per phase
 // cover all 64 banks, and a wave's 1 KB direct-to-LDS write is contiguous.
@@ -61,29 +44,6 @@ __device__ __forceinline__ int swz64(int r, int c) {
   return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
 }
 
-__device__ __forceinline__ float swiglu(float g, float u, float c) {
-  if (c > 0.f) {
-    g = fminf(g, c);
-    u = fminf(fmaxf(u, -c), c);
-  }
-  return g / (1.f + expf(-g)) * u;
-}
-
-// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// vmcnt(N) and lgkmcnt(0) together.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kBW = 256;   // weight rows per tile
 constexpr int kBK = 32;    // K per LDS stage
@@ -349,7 +309,6 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
                 *reinterpret_cast<V4*>(reinterpret_cast<S*>(a.out2) + prow * a.out_ld + f) = lv;
             }
         } else {
-          const float pw = a.pair_w[prow];
 #pragma unroll
           for (int wi = 0; wi < 4; ++wi)
 #pragma unroll
@@ -357,10 +316,10 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
               const int d = nb * kBW + ww * 128 + wi * 32 + rq * 8 + hi4;
               if (d >= N) continue;
               float4 v;
-              v.x = acc[wi][t][rq * 4 + 0] * pw;
-              v.y = acc[wi][t][rq * 4 + 1] * pw;
-              v.z = acc[wi][t][rq * 4 + 2] * pw;
-              v.w = acc[wi][t][rq * 4 + 3] * pw;
+              v.x = acc[wi][t][rq * 4 + 0];
+              v.y = acc[wi][t][rq * 4 + 1];
+              v.z = acc[wi][t][rq * 4 + 2];
+              v.w = acc[wi][t][rq * 4 + 3];
               *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + prow * a.out_ld + d) = v;
             }
         }

@@ -16,69 +16,15 @@
 // c ^ (r % 16), so the 16 rows of one operand read hit 16 distinct bank
 // groups. Gate/up column blocks cb = 0..3 of a wave are W_gate f0.., W_up
 // f0.., W_gate f0+16.., W_up f0+16.., f0 = 128 nb + 32 w.
-#include "moe_internal.h"
+#include "device_common.h"
 
 namespace moe {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct WF16 { using S = _Float16; using V8 = half8; };
 struct WBF16 { using S = __bf16; using V8 = bf16x8; };
-
-__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
-                                                            uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 ldg16(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-__device__ __forceinline__ float swiglu(float g, float u, float c) {
-  if (c > 0.f) {
-    g = fminf(g, c);
-    u = fminf(fmaxf(u, -c), c);
-  }
-  return g / (1.f + expf(-g)) * u;
-}
-
-// 32 nibbles (low first) times their block scale -> 4 x 8 fp16, exactly
-// fp16_rne(q * s): 0x6400 | v is 1024 + v, v = nibble ^ 8, minus 1032 is q.
-__device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
-  const half2v s2 = {s, s};
-  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int wi = 0; wi < 4; ++wi) {
-    const uint32_t x = words[wi] ^ 0x88888888u;
-    const uint32_t lo = x & 0x0F0F0F0Fu;
-    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
-      half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u);
-      h = (h + off) * s2;
-      out[wi][2 * b] = h[0];
-      out[wi][2 * b + 1] = h[1];
-    }
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 constexpr int kChunkK = 128;            // K per LDS chunk
 constexpr int kRowsW = 64;              // token rows per item (4 blocks of 16)
@@ -278,11 +224,10 @@ __global__ __launch_bounds__(256, 2) void gemm_wide_kernel(GemmArgs a) {
               if (a.out2) reinterpret_cast<S*>(a.out2)[prow * a.out_ld + f] = (S)(h - (float)hv);
             }
           } else {
-            const float pw = a.pair_w[prow];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
               const int d = col0 + cb * 16 + n;
-              if (d < N) reinterpret_cast<float*>(a.out)[prow * a.out_ld + d] = acc[rb][cb][r] * pw;
+              if (d < N) reinterpret_cast<float*>(a.out)[prow * a.out_ld + d] = acc[rb][cb][r];
             }
           }
         }

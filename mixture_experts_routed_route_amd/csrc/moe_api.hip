@@ -166,8 +166,8 @@ struct PhaseScope {
 };
 
 struct FwdLayout {
-  size_t H, H2, Y, full_tiles, sk1, sk4, fat_slot, fat_list, meta, stg_g, stg_u,
-      stg_d, bytes;
+  size_t H, H2, Y, full_tiles, sk1, sk4, sk1_tok, part, fat_slot, fat_list,
+      meta, stg_g, stg_u, stg_d, bytes;
   int cap_tiles, cap_sk1, cap_sk4, max_fat, fat_rows;
   bool can_full, can_sk1, can_sk4, can_fat;
   bool split_h;   // bf16: SwiGLU output as a hi + lo bf16 pair
@@ -225,6 +225,8 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.full_tiles = take((size_t)L.cap_tiles * 8);
   L.sk1 = take((size_t)L.cap_sk1 * 16);
   L.sk4 = take((size_t)L.cap_sk4 * 16);
+  L.sk1_tok = take((size_t)L.cap_sk1 * 16 * 4);
+  L.part = take((size_t)kStreamMaxRuns * 2 * kStreamSlotFloats * 4);
   L.fat_slot = take((size_t)n_exp * 4);
   L.fat_list = take((size_t)n_exp * 4);
   L.meta = take(kMetaCount * 4);
@@ -469,6 +471,9 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     ca.full_tiles = (int32_t*)(b + L.full_tiles);
     ca.sk1 = (int32_t*)(b + L.sk1);
     ca.sk4 = (int32_t*)(b + L.sk4);
+    ca.offsets = (const int32_t*)(pb + p->L.offsets);
+    ca.pair_token = (const int32_t*)(pb + p->L.pair_token);
+    ca.sk1_tok = (int32_t*)(b + L.sk1_tok);
     ca.fat_slot = (int32_t*)(b + L.fat_slot);
     ca.fat_list = (int32_t*)(b + L.fat_list);
     ca.meta = meta;
@@ -538,8 +543,16 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       if (L.can_sk1) {
         g.list = (const int32_t*)(b + L.sk1);
         g.meta_index = kMetaSk1;
-        const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk1 * nnb, sk_rb1_grid_cap);
-        e = launch_gemm_splitk(g, x_dtype, wdt, 1, grid, s);
+        if (x_dtype != MOE_F32 && stream_supported(stage, g.K, g.N, wdt)) {
+          // groups of <= 16 rows: the stream tile, units split evenly
+          g.tok = (const int32_t*)(b + L.sk1_tok);
+          g.part = (float*)(b + L.part);
+          const int grid = std::min(info.ncu, kStreamMaxRuns);
+          e = launch_gemm_stream(g, x_dtype, wdt, grid, s);
+        } else {
+          const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk1 * nnb, sk_rb1_grid_cap);
+          e = launch_gemm_splitk(g, x_dtype, wdt, 1, grid, s);
+        }
         if (e != hipSuccess) return hip_fail(e, "split-K kernel");
       }
       if (L.can_sk4) {
@@ -561,6 +574,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   {
     PhaseScope ps(rec, 6, s);
     e = launch_combine(Y, (const int32_t*)(pb + p->L.tok2pair),
+                       (const float*)(pb + p->L.w),
                        (const int32_t*)(pb + p->L.offsets), d.T, D, d.k,
                        d.n_shared, d.E, y_dtype, y, s);
     if (e != hipSuccess) return hip_fail(e, "combine kernel");

@@ -29,6 +29,10 @@ constexpr int kPadBytes = 256;
 // Split-K tile: output columns per item and rows per row block.
 constexpr int kSkNB = 64;
 constexpr int kSkRows = 64;   // rows per split-K group (4 blocks of 16)
+// Stream tile: most runs (workgroups) per launch; each run owns two fp32
+// partial-sum slots of 256 threads x 8 values in the workspace.
+constexpr int kStreamMaxRuns = 512;
+constexpr int kStreamSlotFloats = 2048;
 
 // Forward route tags per expert.
 enum Route : int32_t { kRouteNone = 0, kRouteSplitK = 1, kRouteFull = 2,
@@ -60,8 +64,11 @@ struct ClassifyArgs {
   double S;                // split-K bound in pairs per expert (f32 value)
   int fat_rows;            // q4: >= fat_rows -> fat; <= 0 off
   int32_t* full_tiles;     // [cap] (expert, row0) pairs as int2
-  int32_t* sk1;            // [cap] (expert, row0, nrows, 0) as int4
+  int32_t* sk1;            // [cap] (expert, row0, nrows, pstart) as int4
   int32_t* sk4;            // [cap] same, 17..64 rows
+  const int32_t* offsets;  // [n_exp + 1]: pstart = offsets[e] + row0
+  const int32_t* pair_token;   // [P]
+  int32_t* sk1_tok;        // [cap, 16]: x rows of each sk1 group, clamped
   int32_t* fat_slot;       // [n_exp]
   int32_t* fat_list;       // [n_exp]
   int32_t* meta;           // [kMetaCount]
@@ -70,7 +77,7 @@ hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s);
 
 // Operand set of one GEMM stage (gate/up or down).
 struct GemmArgs {
-  int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down (x w)
+  int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down
   int K, N;                 // K: reduction; N: output width (F or D)
   const void* A;            // gate/up: x [T, D]; down: H [P, F]
   const void* A2;           // down, bf16 split H: the low plane; else null
@@ -80,7 +87,7 @@ struct GemmArgs {
   int out_ld;               // output row stride, elements
   const int32_t* pair_token;// gather map for gate/up
   const int32_t* offsets;   // [n_exp + 1]
-  const float* pair_w;      // [P]
+  const float* pair_w;      // [P] (the combine applies the weights)
   // B operands, [n_exp, rows, K]: gate/up use B0 = W_gate, B1 = W_up; down
   // uses B0 = W_down. q4: data + scales.
   const void* B0; const void* B0s;
@@ -88,17 +95,22 @@ struct GemmArgs {
   // Dequantised fp16 copies of fat experts: [slot, rows, K]; nullptr if none.
   const void* S0; const void* S1;
   const int32_t* fat_slot;
-  void* out;                // H [P, F] (x's dtype) or Ypair [P, D] (f32)
+  void* out;                // H [P, F] (x's dtype) or Ypair [P, D] (f32, unweighted)
   void* out2;               // gate/up, bf16 split H: low plane; else null
   float clamp;              // SwiGLU limit, <= 0 off
   const int32_t* list;      // work list (full tiles or split-K groups)
   const int32_t* meta;      // counts of the work lists
   int meta_index;           // which meta counter holds this list's length
+  const int32_t* tok;       // stream tile, gate/up: the sk1 groups' x rows
+  float* part;              // stream tile: [kStreamMaxRuns, 2, kStreamSlotFloats]
 };
 hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
                             hipStream_t s);
 hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
                               int grid, hipStream_t s);
+bool stream_supported(int mode, int K, int N, int wdt);
+hipError_t launch_gemm_stream(const GemmArgs& a, int xdt, int wdt, int grid,
+                              hipStream_t s);
 hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
                             hipStream_t s);
 hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
@@ -108,7 +120,8 @@ hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
 hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
                                int64_t rows, int K, hipStream_t s);
 hipError_t launch_combine(const void* ypair, const int32_t* tok2pair,
-                          const int32_t* offsets, int T, int D, int k,
+                          const float* topk_w, const int32_t* offsets, int T,
+                          int D, int k,
                           int n_shared, int E, int ydt, void* y,
                           hipStream_t s);
 

@@ -27,85 +27,139 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float(b);
 }
 
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) {
-  return a > b ? a : b;
+// Number of lanes whose predicate holds, over the wave.
+__device__ __forceinline__ int wave_count(bool pred) {
+  return __popcll(__ballot(pred));
 }
 
 // One wavefront per token; PER = ceil(E / 64) logits per lane (expert
-// lane + 64 p). Each of the k rounds takes the wave's largest packed key
-// (order key in the high word, ~expert in the low word, so equal logits
-// resolve to the lower expert index), then clears it in its owner lane.
+// lane + 64 p). The k-th largest order key tau is built bit by bit from the
+// top (a candidate stays if at least k keys reach it): 32 steps of
+// compare + ballot + popcount, no data exchange between lanes. Keys above
+// tau are chosen, then keys equal to tau in expert order until k are
+// chosen, so equal logits resolve to the lower expert index. A chosen
+// expert's position j is the number of chosen experts ranked above it.
 // Weights: exp(l_j - l_0) / sum_i exp(l_i - l_0) in double, rounded to f32.
-// Block = 4 waves x 16 tokens = one 64-token chunk; the block's histogram row
-// hist[chunk, 0..E-1] counts the chunk's choices per expert, hist[chunk, E]
-// its NaN logits.
+// Block = 16 waves x 4 tokens = one 64-token chunk; the block's histogram
+// row hist[chunk, 0..E-1] counts the chunk's choices per expert, and
+// hist[chunk, E] its NaN logits.
 template <int PER>
-__global__ __launch_bounds__(256) void route_hist_kernel(
+__global__ __launch_bounds__(1024) void route_hist_kernel(
     const float* __restrict__ logits, int T, int E, int k,
     int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ hist) {
   extern __shared__ int32_t sh_hist[];   // E + 1
+  constexpr int kTokPerWave = kChunk / 16;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x;
   for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_hist[e] = 0;
   __syncthreads();
 
-  int nan_count = 0;
-  for (int i = 0; i < kChunk / 4; ++i) {
-    const int t = chunk * kChunk + wave * (kChunk / 4) + i;
-    if (t >= T) break;   // wave-uniform
-    const float* row = logits + (size_t)t * E;
-    uint64_t key[PER];
+  const int tbase = chunk * kChunk + wave * kTokPerWave;
+  // every logit this wave needs, loaded up front
+  float lv[kTokPerWave][PER];
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i) {
+    const int t = tbase + i;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int e = lane + 64 * p;
-      if (e < E) {
-        const float v = row[e];
-        nan_count += (v != v) ? 1 : 0;
-        key[p] = ((uint64_t)order_key(v) << 32) | (uint32_t)(~(uint32_t)e);
-      } else {
-        key[p] = 0ull;
+      lv[i][p] = (t < T && e < E) ? logits[(size_t)t * E + e] : 0.f;
+    }
+  }
+  // keys of the wave's tokens (a token past T has no valid expert: it
+  // chooses nothing and writes nothing)
+  uint32_t key[kTokPerWave][PER];
+  bool valid[kTokPerWave][PER];
+  int nan_count = 0;
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      valid[i][p] = tbase + i < T && lane + 64 * p < E;
+      key[i][p] = order_key(lv[i][p]);
+      nan_count += (valid[i][p] && lv[i][p] != lv[i][p]) ? 1 : 0;
+    }
+  // tau: the k-th largest key of each token, the tokens side by side
+  uint32_t tau[kTokPerWave];
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i) tau[i] = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+    for (int i = 0; i < kTokPerWave; ++i) {
+      const uint32_t test = tau[i] | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) cnt += wave_count(valid[i][p] && key[i][p] >= test);
+      if (cnt >= k) tau[i] = test;
+    }
+  }
+  const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i) {
+    const int t = tbase + i;
+    int above = 0;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) above += wave_count(valid[i][p] && key[i][p] > tau[i]);
+    // ties at tau: the first (k - above) in expert order
+    int ties_before = 0;
+    bool sel[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const bool eqp = valid[i][p] && key[i][p] == tau[i];
+      const uint64_t eq = __ballot(eqp);
+      const int r = ties_before + __popcll(eq & lanes_below);
+      sel[p] = valid[i][p] && (key[i][p] > tau[i] || (eqp && r < k - above));
+      ties_before += __popcll(eq);
+    }
+    // positions: chosen experts ranked above each chosen one; the largest
+    // chosen key is l_0's
+    int pos[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) pos[p] = 0;
+    uint32_t top = 0u;
+#pragma unroll
+    for (int pp = 0; pp < PER; ++pp) {
+      uint64_t m = __ballot(sel[pp]);
+      while (m) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const uint32_t ko = (uint32_t)__builtin_amdgcn_readlane((int)key[i][pp], l);
+        const int eo = l + 64 * pp;
+        top = ko > top ? ko : top;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+          const int e = lane + 64 * p;
+          pos[p] += (sel[p] && (ko > key[i][p] || (ko == key[i][p] && eo < e))) ? 1 : 0;
+        }
       }
     }
-    int sel[PER];
-    float val[PER];
-#pragma unroll
-    for (int p = 0; p < PER; ++p) { sel[p] = 0; val[p] = 0.f; }
-    float l0 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int p = 1; p < PER; ++p) best = umax64(best, key[p]);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1)
-        best = umax64(best, (uint64_t)__shfl_xor((unsigned long long)best, off));
-      const int e = (int)(~(uint32_t)best);
-      const float v = key_value((uint32_t)(best >> 32));
-      if (j == 0) l0 = v;
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        if (lane + 64 * p == e) key[p] = 0ull;
-        if (p == (j >> 6) && lane == (j & 63)) { sel[p] = e; val[p] = v; }
-      }
-      if (lane == 0) atomicAdd(&sh_hist[e], 1);
-    }
+    const double l0 = (double)key_value(top);
     double ex[PER];
-    double s = 0.0;
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int j = lane + 64 * p;
-      ex[p] = (j < k) ? exp((double)val[p] - (double)l0) : 0.0;
-      s += ex[p];
+    for (int p = 0; p < PER; ++p) ex[p] = sel[p] ? exp((double)lv[i][p] - l0) : 0.0;
+    // the sum in expert order, the same in every lane
+    double sum = 0.0;
+#pragma unroll
+    for (int pp = 0; pp < PER; ++pp) {
+      uint64_t m = __ballot(sel[pp]);
+      while (m) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const uint64_t bits = (uint64_t)__double_as_longlong(ex[pp]);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, l);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), l);
+        sum += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+      }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-#pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int j = lane + 64 * p;
-      if (j < k) {
-        ids[(size_t)t * k + j] = sel[p];
-        w[(size_t)t * k + j] = (float)(ex[p] / s);
+      if (sel[p]) {
+        const int e = lane + 64 * p;
+        ids[(size_t)t * k + pos[p]] = e;
+        w[(size_t)t * k + pos[p]] = (float)(ex[p] / sum);
+        atomicAdd(&sh_hist[e], 1);
       }
     }
   }
@@ -124,7 +178,7 @@ hipError_t launch_route_hist(const float* logits, int T, int E, int k,
   const size_t sh = (size_t)(E + 1) * sizeof(int32_t);
   const int per = (E + 63) / 64;
 #define MOE_ROUTE(P)                                                        \
-  hipLaunchKernelGGL(route_hist_kernel<P>, dim3(NC), dim3(256), sh, s,     \
+  hipLaunchKernelGGL(route_hist_kernel<P>, dim3(NC), dim3(1024), sh, s,    \
                      logits, T, E, k, ids, w, hist)
   if (per <= 1) MOE_ROUTE(1);
   else if (per <= 2) MOE_ROUTE(2);
@@ -163,42 +217,49 @@ __device__ __forceinline__ int block_scan_excl(int v, int* total,
   return wave_pre + incl - v;
 }
 
-// One block of 1024 threads. Thread (expert lane el, part p of 16) scans the
-// chunk column of expert g+el over its share of chunks, twice: first the
-// part sums, then in-place exclusive bases. Afterwards: kept counts
-// min(total, limit), offsets by exclusive scan over experts (the shared
-// expert, if any, last with T rows), and the plan counters.
+// One block of 1024 threads. The chunk columns of the E + 1 histogram
+// columns are cut into P parts (P = 1024 / (E + 1), at most 16), so thread
+// (part, column) scans one part of one column, twice: first the part sums,
+// then in-place exclusive bases. Afterwards: kept counts min(total, limit),
+// offsets by exclusive scan over experts (the shared expert, if any, last
+// with T rows), and the plan counters.
 __global__ __launch_bounds__(1024) void scan_kernel(
     int32_t* __restrict__ hist, int NC, int T, int E, int k, int n_shared,
     int64_t limit, int32_t* __restrict__ total, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int64_t* __restrict__ stats) {
-  __shared__ int part_sum[16][64];
+  __shared__ int part_sum[1024];
   __shared__ int tot[kMaxExperts + 1];
   __shared__ int sh_waves[16];
   __shared__ int red[4];
-  const int el = threadIdx.x & 63;
-  const int part = threadIdx.x >> 6;
   const int EH = E + 1;
-  const int cp = (NC + 15) / 16;
+  const int P = max(1, min(16, (int)blockDim.x / EH));
+  const int W = (int)blockDim.x / P;          // columns per pass
+  const int part = threadIdx.x / W;
+  const int col = threadIdx.x - part * W;
+  const int cp = (NC + P - 1) / P;
   const int c0 = min(NC, part * cp);
   const int c1 = min(NC, c0 + cp);
-  for (int g = 0; g < EH; g += 64) {
-    const int e = g + el;
+  for (int g = 0; g < EH; g += W) {
+    const int e = g + col;
+    const bool mine = part < P && e < EH;
     int s = 0;
-    if (e < EH)
+    if (mine) {
+#pragma unroll 8
       for (int c = c0; c < c1; ++c) s += hist[(size_t)c * EH + e];
-    part_sum[part][el] = s;
+    }
+    if (part < P) part_sum[part * W + col] = s;
     __syncthreads();
-    int run = 0;
-    for (int p = 0; p < part; ++p) run += part_sum[p][el];
-    if (e < EH) {
+    if (mine) {
+      int run = 0;
+      for (int p = 0; p < part; ++p) run += part_sum[p * W + col];
+#pragma unroll 8
       for (int c = c0; c < c1; ++c) {
         const size_t ix = (size_t)c * EH + e;
         const int v = hist[ix];
         hist[ix] = run;
         run += v;
       }
-      if (part == 15) tot[e] = run;
+      if (part == P - 1) tot[e] = run;
     }
     __syncthreads();
   }

@@ -118,6 +118,21 @@ def test_edge_one_token_and_ragged():
         check_layer(wl, y)
 
 
+@pytest.mark.parametrize("dt,T", [(W.BF16, 1), (W.F16, 3), (W.Q4B32, 2)])
+def test_stream_tile_few_groups(dt, T):
+    # a few thin groups: every (group, 128-row block) item of the stream tile
+    # spans several of its equal runs, so the fix-up adds partial sums from
+    # three or more runs
+    if dt == W.Q4B32:
+        wl = W.make_layer(T, 1024, 512, 16, 4, W.F16, w_dtype=W.Q4B32,
+                          seed=40 + T)
+    else:
+        wl = W.make_layer(T, 2048, 768, 16, 4, dt, seed=40 + T, n_shared=1)
+    say(f"layer stream tile few groups {dt} T={T}")
+    p, y = gpu_layer(wl)
+    check_layer(wl, y)
+
+
 def test_edge_empty_prompt():
     wl = W.make_layer(0, 128, 128, 4, 2, W.BF16, seed=25)
     p, y = gpu_layer(wl)
