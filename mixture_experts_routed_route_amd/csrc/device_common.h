@@ -89,4 +89,27 @@ __device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
   }
 }
 
+// Per-pair outputs of the down projection: fp16 when the layer computes in
+// fp16 (no range or precision is lost against its fp16 intermediate), f32
+// otherwise (bf16's 8-bit significand would cost the output its tolerance).
+template <class S> struct YPairOf { using T = float; };
+template <> struct YPairOf<_Float16> { using T = _Float16; };
+
+template <class Y>
+__device__ __forceinline__ void store_y4(void* base, size_t idx, float a,
+                                         float b, float c, float d) {
+  if constexpr (sizeof(Y) == 2) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 v = {(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+    *reinterpret_cast<h4*>(reinterpret_cast<_Float16*>(base) + idx) = v;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = float4{a, b, c, d};
+  }
+}
+
+template <class Y>
+__device__ __forceinline__ void store_y1(void* base, size_t idx, float a) {
+  reinterpret_cast<Y*>(base)[idx] = (Y)a;
+}
+
 }  // namespace moe

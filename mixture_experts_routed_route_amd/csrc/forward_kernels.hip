@@ -71,8 +71,9 @@ __device__ __forceinline__ int block_excl(int v, int* total, int* sh) {
 //   mode 0 (f32): split-K; mode 1 (bf16/f16): split-K iff n <= S, else full;
 //   mode 2 (q4): fat iff fat_rows > 0 and n >= fat_rows, else split-K.
 // Full/fat experts are ordered largest first (ties: lower index) and cut into
-// kFullBM-row tiles; split-K experts into groups of <= 64 rows, groups of at
-// most 16 rows going to the one-block list.
+// kFullBM-row tiles. Split-K experts are cut into groups of <= 64 rows;
+// groups of at most 16 rows go to the first list, the others to the second;
+// for the stream tile each group's x rows go to a table beside its list.
 __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
   constexpr int kPadE = (kMaxExperts + 1 + 3) / 4 * 4;
   __shared__ int cnt[kPadE];
@@ -155,18 +156,24 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
           const int row0 = g * kSkRows;
           const int rows = min(kSkRows, c - row0);
           const int pstart = a.offsets[e] + row0;
-          int32_t* dst = (rows <= 16) ? a.sk1 + 4 * p1
-                                      : a.sk4 + 4 * (p4 + g);
+          const bool one = rows <= 16;
+          const int slot = one ? p1 : p4 + g;
+          int32_t* dst = (one ? a.sk1 : a.sk4) + 4 * slot;
           dst[0] = e;
           dst[1] = row0;
           dst[2] = rows;
           dst[3] = pstart;
-          if (rows <= 16 && a.sk1_tok) {
-            int tk[16];
+          int32_t* tok = one ? a.sk1_tok : a.sk4_tok;
+          if (tok) {
+            // the group's x rows for the stream tile, clamped to its last
+            tok += (size_t)kStreamTokRows * slot;
+            for (int t0 = 0; t0 < (one ? 16 : kStreamTokRows); t0 += 16) {
+              int tk[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) tk[t] = a.pair_token[pstart + min(t, rows - 1)];
+              for (int t = 0; t < 16; ++t) tk[t] = a.pair_token[pstart + min(t0 + t, rows - 1)];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) a.sk1_tok[16 * p1 + t] = tk[t];
+              for (int t = 0; t < 16; ++t) tok[t0 + t] = tk[t];
+            }
           }
         }
       }
@@ -436,7 +443,7 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const int d = nb * 64 + cb * 16 + n;
-            reinterpret_cast<float*>(a.out)[prow * a.out_ld + d] = acc[rb][cb][r];
+            store_y1<typename YPairOf<S>::T>(a.out, prow * a.out_ld + d, acc[rb][cb][r]);
           }
         }
       }
@@ -610,14 +617,28 @@ hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
 //
 // y[t, d..d+7] = sum over j of w[t, j] * Ypair[tok2pair[t, j], d..d+7] (j
 // ascending, dropped pairs skipped) + the shared expert's row (weight 1).
-// Ypair holds each kept pair's unweighted output in f32; each product and
-// the sum are f32 and the result is rounded once to y's dtype (mini-AGI PR
-// #4, minagi/pool.py: the weighted gather back to tokens). Each output is
-// written by one thread: no atomics.
+// Ypair holds each kept pair's unweighted output (f32, or fp16 in an fp16
+// layer); each product and the sum are f32 and the result is rounded once to
+// y's dtype (mini-AGI PR #4, minagi/pool.py: the weighted gather back to
+// tokens). Each output is written by one thread: no atomics.
 
-template <class S>
+template <class Y>
+__device__ __forceinline__ void load_y8(const Y* p, float v[8]) {
+  if constexpr (sizeof(Y) == 2) {
+    const half8 h = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(p));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <class Y, class S>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const float* __restrict__ ypair, const int32_t* __restrict__ tok2pair,
+    const Y* __restrict__ ypair, const int32_t* __restrict__ tok2pair,
     const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
     int T, int D, int k, int n_shared, int E, S* __restrict__ y) {
   const int per_row = D / 8;
@@ -626,54 +647,64 @@ __global__ __launch_bounds__(256) void combine_kernel(
   if (idx >= total) return;
   const int t = (int)(idx / per_row);
   const int d = (int)(idx - (size_t)t * per_row) * 8;
-  float4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const int p = tok2pair[(size_t)t * k + j];
     if (p < 0) continue;
     const float w = topk_w[(size_t)t * k + j];
-    const float4* src = reinterpret_cast<const float4*>(ypair + (size_t)p * D + d);
-    const float4 a = src[0], b = src[1];
-    lo.x += a.x * w; lo.y += a.y * w; lo.z += a.z * w; lo.w += a.w * w;
-    hi.x += b.x * w; hi.y += b.y * w; hi.z += b.z * w; hi.w += b.w * w;
+    float v[8];
+    load_y8(ypair + (size_t)p * D + d, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i] * w;
   }
   if (n_shared) {
-    const float4* src = reinterpret_cast<const float4*>(
-        ypair + (size_t)(offsets[E] + t) * D + d);
-    const float4 a = src[0], b = src[1];
-    lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
-    hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+    float v[8];
+    load_y8(ypair + (size_t)(offsets[E] + t) * D + d, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
   S* out = y + (size_t)t * D + d;
   if constexpr (sizeof(S) == 4) {
-    reinterpret_cast<float4*>(out)[0] = lo;
-    reinterpret_cast<float4*>(out)[1] = hi;
+    reinterpret_cast<float4*>(out)[0] = float4{acc[0], acc[1], acc[2], acc[3]};
+    reinterpret_cast<float4*>(out)[1] = float4{acc[4], acc[5], acc[6], acc[7]};
   } else {
     typedef S s8 __attribute__((ext_vector_type(8)));
     s8 o;
-    o[0] = (S)lo.x; o[1] = (S)lo.y; o[2] = (S)lo.z; o[3] = (S)lo.w;
-    o[4] = (S)hi.x; o[5] = (S)hi.y; o[6] = (S)hi.z; o[7] = (S)hi.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (S)acc[i];
     *reinterpret_cast<s8*>(out) = o;
   }
 }
 
-hipError_t launch_combine(const void* ypair, const int32_t* tok2pair,
-                          const float* topk_w, const int32_t* offsets, int T,
-                          int D, int k, int n_shared, int E, int ydt, void* y,
-                          hipStream_t s) {
+template <class Y>
+static hipError_t combine_y(const void* ypair, const int32_t* tok2pair,
+                            const float* topk_w, const int32_t* offsets, int T,
+                            int D, int k, int n_shared, int E, int ydt, void* y,
+                            int grid, hipStream_t s) {
+  const Y* yp = (const Y*)ypair;
+  if (ydt == MOE_F32)
+    hipLaunchKernelGGL((combine_kernel<Y, float>), dim3(grid), dim3(256), 0, s,
+                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (float*)y);
+  else if (ydt == MOE_BF16)
+    hipLaunchKernelGGL((combine_kernel<Y, __bf16>), dim3(grid), dim3(256), 0, s,
+                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (__bf16*)y);
+  else
+    hipLaunchKernelGGL((combine_kernel<Y, _Float16>), dim3(grid), dim3(256), 0, s,
+                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (_Float16*)y);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* ypair, int ypair_f16,
+                          const int32_t* tok2pair, const float* topk_w,
+                          const int32_t* offsets, int T, int D, int k,
+                          int n_shared, int E, int ydt, void* y, hipStream_t s) {
   const size_t total = (size_t)T * (D / 8);
   if (total == 0) return hipSuccess;
   const int grid = (int)((total + 255) / 256);
-  const float* yp = (const float*)ypair;
-  if (ydt == MOE_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, s,
-                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (float*)y);
-  else if (ydt == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<__bf16>, dim3(grid), dim3(256), 0, s,
-                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (__bf16*)y);
-  else
-    hipLaunchKernelGGL(combine_kernel<_Float16>, dim3(grid), dim3(256), 0, s,
-                       yp, tok2pair, topk_w, offsets, T, D, k, n_shared, E, (_Float16*)y);
-  return hipGetLastError();
+  return ypair_f16 ? combine_y<_Float16>(ypair, tok2pair, topk_w, offsets, T, D, k,
+                                         n_shared, E, ydt, y, grid, s)
+                   : combine_y<float>(ypair, tok2pair, topk_w, offsets, T, D, k,
+                                      n_shared, E, ydt, y, grid, s);
 }
 
 }  // namespace moe

@@ -96,11 +96,14 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
     const int ti_ = first + within % gm;
     const int nb = within / gm;
 
-    const int e = a.list[2 * ti_];
-    const int tile_row0 = a.list[2 * ti_ + 1];
-    const int off = a.offsets[e];
-    const int ne = a.offsets[e + 1] - off;
-    const int slot = a.fat_slot ? a.fat_slot[e] : -1;
+    // item descriptors through the scalar cache: vector loads here would
+    // make the waits for them also drain the previous item's stores
+    typedef const __attribute__((address_space(4))) int32_t* sconst_i32;
+    const int e = ((sconst_i32)a.list)[2 * ti_];
+    const int tile_row0 = ((sconst_i32)a.list)[2 * ti_ + 1];
+    const int off = ((sconst_i32)a.offsets)[e];
+    const int ne = ((sconst_i32)a.offsets)[e + 1] - off;
+    const int slot = a.fat_slot ? ((sconst_i32)a.fat_slot)[e] : -1;
     const size_t eix = slot >= 0 ? (size_t)slot : (size_t)e;
     // caller weights are [N, K] rows of K; fp16 fat copies have padded rows
     const uint32_t w_ld = slot >= 0 ? (uint32_t)a.s_ld : (uint32_t)K;
@@ -223,8 +226,10 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         }
       };
 
-      // all earlier reads of the ring and stores are done before refilling
-      wait_vmcnt<0>();
+      // every wave is past its reads of the ring before it is refilled; the
+      // previous pass's refills are done (their wait sits before its
+      // epilogue), so only its stores may still be in flight: they drain
+      // while the first stages load
       __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int s = 0; s < kNS - 1; ++s) issue(s);
@@ -276,6 +281,10 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
+      // the refills issued past the last stage land before anything else
+      // is issued, so the next pass's refills of the same ring slots are
+      // ordered after them whatever order loads complete in
+      wait_vmcnt<0>();
       // epilogue: accumulator r of a 32x32 block is weight row
       // 8 (r / 4) + 4 (lane / 32) + r % 4, token column lane % 32
       // lane-derived epilogue values are defined here, after the K loop, so
@@ -315,12 +324,10 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
             for (int rq = 0; rq < 4; ++rq) {
               const int d = nb * kBW + ww * 128 + wi * 32 + rq * 8 + hi4;
               if (d >= N) continue;
-              float4 v;
-              v.x = acc[wi][t][rq * 4 + 0];
-              v.y = acc[wi][t][rq * 4 + 1];
-              v.z = acc[wi][t][rq * 4 + 2];
-              v.w = acc[wi][t][rq * 4 + 3];
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + prow * a.out_ld + d) = v;
+              store_y4<typename YPairOf<S>::T>(
+                  a.out, prow * a.out_ld + d, acc[wi][t][rq * 4 + 0],
+                  acc[wi][t][rq * 4 + 1], acc[wi][t][rq * 4 + 2],
+                  acc[wi][t][rq * 4 + 3]);
             }
         }
       }

@@ -227,7 +227,8 @@ __global__ __launch_bounds__(256, 2) void gemm_wide_kernel(GemmArgs a) {
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
               const int d = col0 + cb * 16 + n;
-              if (d < N) reinterpret_cast<float*>(a.out)[prow * a.out_ld + d] = acc[rb][cb][r];
+              if (d < N)
+                store_y1<typename YPairOf<S>::T>(a.out, prow * a.out_ld + d, acc[rb][cb][r]);
             }
           }
         }

@@ -166,9 +166,10 @@ struct PhaseScope {
 };
 
 struct FwdLayout {
-  size_t H, H2, Y, full_tiles, sk1, sk4, sk1_tok, part, fat_slot, fat_list,
-      meta, stg_g, stg_u, stg_d, bytes;
+  size_t H, H2, Y, full_tiles, sk1, sk4, sk1_tok, sk4_tok, part, fat_slot,
+      fat_list, meta, stg_g, stg_u, stg_d, bytes;
   int cap_tiles, cap_sk1, cap_sk4, max_fat, fat_rows;
+  bool stream;       // split-K groups on the stream tile
   bool can_full, can_sk1, can_sk4, can_fat;
   bool split_h;   // bf16: SwiGLU output as a hi + lo bf16 pair
   int h_ld, sg_ld, sd_ld;   // padded row strides (elements)
@@ -198,6 +199,10 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.max_fat = 0;
   if (L.fat_rows > 0)
     L.max_fat = (int)std::min<int64_t>(n_exp, Pmax / L.fat_rows);
+  // the stream tile takes the split-K groups of a bf16/f16/q4 layer whose
+  // sizes it tiles
+  L.stream = wdt != MOE_F32 && stream_supported(0, D, F, wdt) &&
+             stream_supported(1, F, D, wdt);
   if (wdt == MOE_F32) {
     L.can_full = false; L.can_sk1 = true; L.can_sk4 = true; L.can_fat = false;
   } else if (wdt == MOE_Q4B32) {
@@ -221,12 +226,13 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.H = take((size_t)Pmax * L.h_ld * xb + 16);
   L.split_h = xdt == MOE_BF16 && !(o.flags & MOE_OPT_BF16_PLAIN_H);
   L.H2 = take(L.split_h ? (size_t)Pmax * L.h_ld * 2 + 16 : 0);
-  L.Y = take((size_t)Pmax * D * 4 + 16);   // Ypair in f32
+  L.Y = take((size_t)Pmax * D * (xdt == MOE_F16 ? 2 : 4) + 16);   // Ypair
   L.full_tiles = take((size_t)L.cap_tiles * 8);
   L.sk1 = take((size_t)L.cap_sk1 * 16);
   L.sk4 = take((size_t)L.cap_sk4 * 16);
-  L.sk1_tok = take((size_t)L.cap_sk1 * 16 * 4);
-  L.part = take((size_t)kStreamMaxRuns * 2 * kStreamSlotFloats * 4);
+  L.sk1_tok = take(L.stream ? (size_t)L.cap_sk1 * kStreamTokRows * 4 : 0);
+  L.sk4_tok = take(L.stream ? (size_t)L.cap_sk4 * kStreamTokRows * 4 : 0);
+  L.part = take(L.stream ? (size_t)kStreamMaxRuns * 2 * kStreamSlotFloats * 4 : 0);
   L.fat_slot = take((size_t)n_exp * 4);
   L.fat_list = take((size_t)n_exp * 4);
   L.meta = take(kMetaCount * 4);
@@ -240,7 +246,7 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
 moe_options defaults() {
   moe_options o;
   o.swiglu_limit = 7.0f;
-  o.splitk_max_pairs = 4.0f;
+  o.splitk_max_pairs = 16.0f;
   o.fat_rows = 64;
   o.flags = 0;
   return o;
@@ -473,7 +479,8 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     ca.sk4 = (int32_t*)(b + L.sk4);
     ca.offsets = (const int32_t*)(pb + p->L.offsets);
     ca.pair_token = (const int32_t*)(pb + p->L.pair_token);
-    ca.sk1_tok = (int32_t*)(b + L.sk1_tok);
+    ca.sk1_tok = L.stream ? (int32_t*)(b + L.sk1_tok) : nullptr;
+    ca.sk4_tok = L.stream ? (int32_t*)(b + L.sk4_tok) : nullptr;
     ca.fat_slot = (int32_t*)(b + L.fat_slot);
     ca.fat_list = (int32_t*)(b + L.fat_list);
     ca.meta = meta;
@@ -540,15 +547,17 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     {
       PhaseScope ps(rec, stage == 0 ? 3 : 5, s);
       const int nnb = stage == 0 ? F / 32 : D / 64;
+      if (L.stream) {
+        g.part = (float*)(b + L.part);
+      }
+      const int stream_grid = std::min(info.ncu, kStreamMaxRuns);
       if (L.can_sk1) {
+        // groups of <= 16 rows
         g.list = (const int32_t*)(b + L.sk1);
         g.meta_index = kMetaSk1;
-        if (x_dtype != MOE_F32 && stream_supported(stage, g.K, g.N, wdt)) {
-          // groups of <= 16 rows: the stream tile, units split evenly
+        if (L.stream) {
           g.tok = (const int32_t*)(b + L.sk1_tok);
-          g.part = (float*)(b + L.part);
-          const int grid = std::min(info.ncu, kStreamMaxRuns);
-          e = launch_gemm_stream(g, x_dtype, wdt, grid, s);
+          e = launch_gemm_stream(g, x_dtype, wdt, 16, stream_grid, s);
         } else {
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk1 * nnb, sk_rb1_grid_cap);
           e = launch_gemm_splitk(g, x_dtype, wdt, 1, grid, s);
@@ -556,13 +565,17 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
         if (e != hipSuccess) return hip_fail(e, "split-K kernel");
       }
       if (L.can_sk4) {
+        // groups of 17..64 rows
         g.list = (const int32_t*)(b + L.sk4);
         g.meta_index = kMetaSk4;
         if (x_dtype == MOE_F32) {
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * nnb, sk_rb4_grid_cap);
           e = launch_gemm_splitk(g, x_dtype, wdt, 4, grid, s);
+        } else if (L.stream) {
+          g.tok = (const int32_t*)(b + L.sk4_tok);
+          e = launch_gemm_stream(g, x_dtype, wdt, kStreamTokRows, stream_grid, s);
         } else {
-          // groups of 17..64 rows: wide fused-dequant tile, 256 columns/item
+          // wide fused-dequant tile, 256 columns per item
           const int wnb = stage == 0 ? (F + 127) / 128 : (D + 255) / 256;
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * wnb, info.ncu * 2);
           e = launch_gemm_wide(g, x_dtype, wdt, grid, s);
@@ -573,7 +586,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   }
   {
     PhaseScope ps(rec, 6, s);
-    e = launch_combine(Y, (const int32_t*)(pb + p->L.tok2pair),
+    e = launch_combine(Y, x_dtype == MOE_F16, (const int32_t*)(pb + p->L.tok2pair),
                        (const float*)(pb + p->L.w),
                        (const int32_t*)(pb + p->L.offsets), d.T, D, d.k,
                        d.n_shared, d.E, y_dtype, y, s);

@@ -30,9 +30,12 @@ constexpr int kPadBytes = 256;
 constexpr int kSkNB = 64;
 constexpr int kSkRows = 64;   // rows per split-K group (4 blocks of 16)
 // Stream tile: most runs (workgroups) per launch; each run owns two fp32
-// partial-sum slots of 256 threads x 8 values in the workspace.
+// partial-sum slots of 256 threads x 32 values in the workspace. Its groups
+// hold at most kStreamTokRows pairs (the classify kernel's token table has
+// that many entries per group).
 constexpr int kStreamMaxRuns = 512;
-constexpr int kStreamSlotFloats = 2048;
+constexpr int kStreamSlotFloats = 8192;
+constexpr int kStreamTokRows = 64;
 
 // Forward route tags per expert.
 enum Route : int32_t { kRouteNone = 0, kRouteSplitK = 1, kRouteFull = 2,
@@ -64,11 +67,14 @@ struct ClassifyArgs {
   double S;                // split-K bound in pairs per expert (f32 value)
   int fat_rows;            // q4: >= fat_rows -> fat; <= 0 off
   int32_t* full_tiles;     // [cap] (expert, row0) pairs as int2
-  int32_t* sk1;            // [cap] (expert, row0, nrows, pstart) as int4
-  int32_t* sk4;            // [cap] same, 17..64 rows
+  int32_t* sk1;            // [cap] (expert, row0, nrows, pstart) as int4,
+                           // groups of <= 16 rows
+  int32_t* sk4;            // [cap] same, groups of 17..64 rows
   const int32_t* offsets;  // [n_exp + 1]: pstart = offsets[e] + row0
   const int32_t* pair_token;   // [P]
-  int32_t* sk1_tok;        // [cap, 16]: x rows of each sk1 group, clamped
+  int32_t* sk1_tok;        // [cap, kStreamTokRows]: x rows of each sk1
+                           // group, clamped to its last row; or null
+  int32_t* sk4_tok;        // the same for sk4; or null
   int32_t* fat_slot;       // [n_exp]
   int32_t* fat_list;       // [n_exp]
   int32_t* meta;           // [kMetaCount]
@@ -95,7 +101,8 @@ struct GemmArgs {
   // Dequantised fp16 copies of fat experts: [slot, rows, K]; nullptr if none.
   const void* S0; const void* S1;
   const int32_t* fat_slot;
-  void* out;                // H [P, F] (x's dtype) or Ypair [P, D] (f32, unweighted)
+  void* out;                // H [P, F] (x's dtype) or Ypair [P, D] (unweighted;
+                            // fp16 in an fp16 layer, else f32)
   void* out2;               // gate/up, bf16 split H: low plane; else null
   float clamp;              // SwiGLU limit, <= 0 off
   const int32_t* list;      // work list (full tiles or split-K groups)
@@ -109,8 +116,8 @@ hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
 hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
                               int grid, hipStream_t s);
 bool stream_supported(int mode, int K, int N, int wdt);
-hipError_t launch_gemm_stream(const GemmArgs& a, int xdt, int wdt, int grid,
-                              hipStream_t s);
+hipError_t launch_gemm_stream(const GemmArgs& a, int xdt, int wdt, int rows,
+                              int grid, hipStream_t s);
 hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
                             hipStream_t s);
 hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
@@ -119,10 +126,9 @@ hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
                               int grid, hipStream_t s);
 hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
                                int64_t rows, int K, hipStream_t s);
-hipError_t launch_combine(const void* ypair, const int32_t* tok2pair,
-                          const float* topk_w, const int32_t* offsets, int T,
-                          int D, int k,
-                          int n_shared, int E, int ydt, void* y,
-                          hipStream_t s);
+hipError_t launch_combine(const void* ypair, int ypair_f16,
+                          const int32_t* tok2pair, const float* topk_w,
+                          const int32_t* offsets, int T, int D, int k,
+                          int n_shared, int E, int ydt, void* y, hipStream_t s);
 
 }  // namespace moe

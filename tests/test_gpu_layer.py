@@ -118,11 +118,30 @@ def test_edge_one_token_and_ragged():
         check_layer(wl, y)
 
 
+@pytest.mark.parametrize("S", [16.0, 64.0])
+def test_stream_tile_row_blocks(S):
+    # split-K experts of up to 64 rows: groups of 16 rows (S <= 16) or of
+    # 64 rows in four token blocks (S > 16), bf16 hi + lo planes included
+    wl = W.make_layer(600, 512, 256, 32, 2, W.BF16, seed=51, n_shared=1)
+    say(f"layer stream tile S={S}")
+    p, y = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=S))
+    check_layer(wl, y, sample_tokens(wl["T"], 96, seed=3))
+
+
+def test_q4_thin_groups_odd_width():
+    # 4-bit thin experts with F = 384 (three 128-wide column blocks): groups
+    # of <= 16 rows on the one-block split-K tile, 17..64 on the wide tile
+    wl = W.make_layer(300, 512, 384, 16, 4, W.F16, w_dtype=W.Q4B32, seed=52)
+    say("layer q4 F=384")
+    p, y = gpu_layer(wl, options=moe.make_options(fat_rows=1000000))
+    check_layer(wl, y, sample_tokens(wl["T"], 64, seed=4))
+
+
 @pytest.mark.parametrize("dt,T", [(W.BF16, 1), (W.F16, 3), (W.Q4B32, 2)])
-def test_stream_tile_few_groups(dt, T):
-    # a few thin groups: every (group, 128-row block) item of the stream tile
-    # spans several of its equal runs, so the fix-up adds partial sums from
-    # three or more runs
+def test_thin_tiles_few_groups(dt, T):
+    # a few thin groups: every (group, 128-row block) item of the 16-bit
+    # stream tile spans several of its equal runs, so the fix-up adds partial
+    # sums from three or more runs; 4-bit: the split-K tile on a few groups
     if dt == W.Q4B32:
         wl = W.make_layer(T, 1024, 512, 16, 4, W.F16, w_dtype=W.Q4B32,
                           seed=40 + T)
