@@ -220,27 +220,38 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, _Float16 s) {
   return uint4{o[0], o[1], o[2], o[3]};
 }
 
-// Fat experts: slot s of the staging buffer holds expert fat_list[s]'s
-// [rows, K] matrix as fp16, rows out_ld apart. Grid-stride over 8-value units.
+// Fat experts: slot s of a staging buffer holds expert fat_list[s]'s
+// [rows, K] matrix as fp16, rows out_ld apart. blockIdx.y picks one of up to
+// three matrices (W_gate, W_up, W_down); blocks stride over the matrix's rows
+// of every fat slot, the block's threads over a row's 8-value units.
+struct DequantSet {
+  const uint8_t* q[3];
+  const uint16_t* sc[3];
+  _Float16* out[3];
+  int rows[3], K[3], out_ld[3];
+};
+
 __global__ __launch_bounds__(256) void dequant_fat_kernel(
-    const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
-    _Float16* __restrict__ out, int rows, int K, int out_ld,
-    const int32_t* __restrict__ fat_list, const int32_t* __restrict__ meta) {
+    DequantSet d, const int32_t* __restrict__ fat_list,
+    const int32_t* __restrict__ meta) {
+  const int m = blockIdx.y;
+  const uint8_t* __restrict__ q = d.q[m];
+  const uint16_t* __restrict__ sc = d.sc[m];
+  _Float16* __restrict__ out = d.out[m];
+  const int rows = d.rows[m], K = d.K[m], out_ld = d.out_ld[m];
   const int nfat = meta[kMetaFat];
-  const int upr = K / 8;                        // units per row
-  const size_t per = (size_t)rows * upr;
-  const size_t total = per * (size_t)nfat;
-  for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < total;
-       u += (size_t)gridDim.x * blockDim.x) {
-    const int slot = (int)(u / per);
-    const size_t rem = u - (size_t)slot * per;
-    const int row = (int)(rem / upr);
-    const int c8 = (int)(rem - (size_t)row * upr);
+  const int upr = K / 8;                  // units per row
+  const int total_rows = nfat * rows;
+  for (int R = blockIdx.x; R < total_rows; R += gridDim.x) {
+    const int slot = R / rows;
+    const int row = R - slot * rows;
     const size_t er = (size_t)fat_list[slot] * rows + row;
-    const uint32_t word = reinterpret_cast<const uint32_t*>(q + er * (size_t)(K / 2))[c8];
-    const uint16_t sb = sc[er * (size_t)(K / 32) + (c8 >> 2)];
-    reinterpret_cast<uint4*>(out + ((size_t)slot * rows + row) * (size_t)out_ld)[c8] =
-        dequant8(word, __builtin_bit_cast(_Float16, sb));
+    const uint32_t* qr = reinterpret_cast<const uint32_t*>(q + er * (size_t)(K / 2));
+    const uint16_t* sr = sc + er * (size_t)(K / 32);
+    uint4* orow = reinterpret_cast<uint4*>(out + (size_t)R * out_ld);
+#pragma unroll 4
+    for (int c8 = threadIdx.x; c8 < upr; c8 += blockDim.x)
+      orow[c8] = dequant8(qr[c8], __builtin_bit_cast(_Float16, sr[c8 >> 2]));
   }
 }
 
@@ -260,13 +271,23 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(
   }
 }
 
-hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
-                              int rows, int K, int out_ld,
+hipError_t launch_dequant_fat(const void* const q[3], const void* const sc[3],
+                              void* const out[3], const int rows[3],
+                              const int K[3], const int out_ld[3], int n,
                               const int32_t* fat_list, const int32_t* meta,
                               int grid, hipStream_t s) {
-  hipLaunchKernelGGL(dequant_fat_kernel, dim3(grid), dim3(256), 0, s,
-                     (const uint8_t*)q, (const uint16_t*)sc, (_Float16*)out,
-                     rows, K, out_ld, fat_list, meta);
+  if (n < 1 || n > 3) return hipErrorInvalidValue;
+  DequantSet d{};
+  for (int i = 0; i < n; ++i) {
+    d.q[i] = (const uint8_t*)q[i];
+    d.sc[i] = (const uint16_t*)sc[i];
+    d.out[i] = (_Float16*)out[i];
+    d.rows[i] = rows[i];
+    d.K[i] = K[i];
+    d.out_ld[i] = out_ld[i];
+  }
+  hipLaunchKernelGGL(dequant_fat_kernel, dim3(grid, n), dim3(256), 0, s, d,
+                     fat_list, meta);
   return hipGetLastError();
 }
 

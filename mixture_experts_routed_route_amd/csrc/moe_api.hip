@@ -490,17 +490,16 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   if (L.can_fat) {
     PhaseScope ps(rec, 1, s);
     const int grid = info.ncu * 8;
-    e = launch_dequant_fat(w_gate.data, w_gate.scales, b + L.stg_g, F, D,
-                           L.sg_ld, (const int32_t*)(b + L.fat_list), meta,
-                           grid, s);
-    if (e == hipSuccess)
-      e = launch_dequant_fat(w_up.data, w_up.scales, b + L.stg_u, F, D,
-                             L.sg_ld, (const int32_t*)(b + L.fat_list), meta,
-                             grid, s);
-    if (e == hipSuccess)
-      e = launch_dequant_fat(w_down.data, w_down.scales, b + L.stg_d, D, F,
-                             L.sd_ld, (const int32_t*)(b + L.fat_list), meta,
-                             grid, s);
+    // one launch for the three matrices; rows of fat slots fit in int
+    // (max_fat * max(F, D) <= P * max(F, D) / fat_rows)
+    const void* const q[3] = {w_gate.data, w_up.data, w_down.data};
+    const void* const sc[3] = {w_gate.scales, w_up.scales, w_down.scales};
+    void* const out[3] = {b + L.stg_g, b + L.stg_u, b + L.stg_d};
+    const int rows[3] = {F, F, D};
+    const int Ks[3] = {D, D, F};
+    const int lds[3] = {L.sg_ld, L.sg_ld, L.sd_ld};
+    e = launch_dequant_fat(q, sc, out, rows, Ks, lds, 3,
+                           (const int32_t*)(b + L.fat_list), meta, grid, s);
     if (e != hipSuccess) return hip_fail(e, "dequant kernel");
   }
 

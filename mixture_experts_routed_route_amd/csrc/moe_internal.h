@@ -120,8 +120,9 @@ hipError_t launch_gemm_stream(const GemmArgs& a, int xdt, int wdt, int rows,
                               int grid, hipStream_t s);
 hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
                             hipStream_t s);
-hipError_t launch_dequant_fat(const void* q, const void* sc, void* out,
-                              int rows, int K, int out_ld,
+hipError_t launch_dequant_fat(const void* const q[3], const void* const sc[3],
+                              void* const out[3], const int rows[3],
+                              const int K[3], const int out_ld[3], int n,
                               const int32_t* fat_list, const int32_t* meta,
                               int grid, hipStream_t s);
 hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
