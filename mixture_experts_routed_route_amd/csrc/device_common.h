@@ -55,12 +55,16 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 // h = silu(min(g, c)) * clamp(u, -c, c); c <= 0: plain silu(g) * u.
+// silu(g) = g / (1 + e^-g) with the hardware's 2^x and reciprocal (about
+// one ulp each): the epilogues evaluate it for every (pair, feature), and a
+// libm-accurate exp there costs more time than the tile's last stages.
 __device__ __forceinline__ float swiglu(float g, float u, float c) {
   if (c > 0.f) {
     g = fminf(g, c);
     u = fminf(fmaxf(u, -c), c);
   }
-  return g / (1.f + expf(-g)) * u;
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896340736f);
+  return g * __builtin_amdgcn_rcpf(1.f + e) * u;
 }
 
 // 32 consecutive 4-bit values (16 bytes, low nibble first) times their block

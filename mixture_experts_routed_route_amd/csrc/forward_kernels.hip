@@ -221,37 +221,60 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, _Float16 s) {
 }
 
 // Fat experts: slot s of a staging buffer holds expert fat_list[s]'s
-// [rows, K] matrix as fp16, rows out_ld apart. blockIdx.y picks one of up to
-// three matrices (W_gate, W_up, W_down); blocks stride over the matrix's rows
-// of every fat slot, the block's threads over a row's 8-value units.
+// [rows, K] matrix as fp16, k-block-major: [K / 32][rows][32], so that the
+// full tile reads one stage's rows as a single contiguous slab. blockIdx.y
+// picks one of up to three matrices (W_gate, W_up, W_down). A block takes
+// tiles of 64 rows x 4 blocks of 32 values (rows a multiple of 64, K of
+// 128): it reads each row's 64 bytes of nibbles as one run, decodes into LDS
+// in the output order, and writes the tile's four 4 KB runs 1 KB per store
+// instruction.
 struct DequantSet {
   const uint8_t* q[3];
   const uint16_t* sc[3];
   _Float16* out[3];
-  int rows[3], K[3], out_ld[3];
+  int rows[3], K[3];
 };
 
 __global__ __launch_bounds__(256) void dequant_fat_kernel(
     DequantSet d, const int32_t* __restrict__ fat_list,
     const int32_t* __restrict__ meta) {
+  __shared__ __attribute__((aligned(16))) char tile[4 * 64 * 64];   // [kb][row][32 fp16]
   const int m = blockIdx.y;
   const uint8_t* __restrict__ q = d.q[m];
   const uint16_t* __restrict__ sc = d.sc[m];
   _Float16* __restrict__ out = d.out[m];
-  const int rows = d.rows[m], K = d.K[m], out_ld = d.out_ld[m];
+  const int rows = d.rows[m], K = d.K[m];
   const int nfat = meta[kMetaFat];
-  const int upr = K / 8;                  // units per row
-  const int total_rows = nfat * rows;
-  for (int R = blockIdx.x; R < total_rows; R += gridDim.x) {
-    const int slot = R / rows;
-    const int row = R - slot * rows;
-    const size_t er = (size_t)fat_list[slot] * rows + row;
-    const uint32_t* qr = reinterpret_cast<const uint32_t*>(q + er * (size_t)(K / 2));
-    const uint16_t* sr = sc + er * (size_t)(K / 32);
-    uint4* orow = reinterpret_cast<uint4*>(out + (size_t)R * out_ld);
-#pragma unroll 4
-    for (int c8 = threadIdx.x; c8 < upr; c8 += blockDim.x)
-      orow[c8] = dequant8(qr[c8], __builtin_bit_cast(_Float16, sr[c8 >> 2]));
+  const int kbs = K / 32;                         // 32-value blocks per row
+  const int rt = rows / 64, kt4 = kbs / 4;        // tiles per slot: rt x kt4
+  const int per_slot = rt * kt4;
+  const int total = nfat * per_slot;
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, qq = tid & 3;           // decode: row, block
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int slot = w / per_slot;
+    const int rem = w - slot * per_slot;
+    const int kq = rem / rt;
+    const int kb0 = kq * 4;
+    const int row0 = (rem - kq * rt) * 64;
+    const size_t er = (size_t)fat_list[slot] * rows + row0 + r;
+    const uint4 qa = *reinterpret_cast<const uint4*>(q + er * (size_t)(K / 2) + (kb0 + qq) * 16);
+    const _Float16 sa = __builtin_bit_cast(_Float16, sc[er * (size_t)kbs + kb0 + qq]);
+    half8 ha[4];
+    dequant32(qa, sa, ha);
+    __syncthreads();   // the previous tile's stores have read the LDS tile
+    char* ta = tile + (qq * 64 + r) * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(ta + i * 16) = __builtin_bit_cast(uint4, ha[i]);
+    __syncthreads();
+    // 1024 16-byte pieces; block kb's 64 rows are 4 KB contiguous
+    char* os = reinterpret_cast<char*>(out + (size_t)slot * rows * K);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + (it * 256 + tid) * 16);
+      *reinterpret_cast<uint4*>(os + ((size_t)(kb0 + it) * rows + row0) * 64 + tid * 16) = v;
+    }
   }
 }
 
@@ -273,9 +296,8 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(
 
 hipError_t launch_dequant_fat(const void* const q[3], const void* const sc[3],
                               void* const out[3], const int rows[3],
-                              const int K[3], const int out_ld[3], int n,
-                              const int32_t* fat_list, const int32_t* meta,
-                              int grid, hipStream_t s) {
+                              const int K[3], int n, const int32_t* fat_list,
+                              const int32_t* meta, int grid, hipStream_t s) {
   if (n < 1 || n > 3) return hipErrorInvalidValue;
   DequantSet d{};
   for (int i = 0; i < n; ++i) {
@@ -284,7 +306,6 @@ hipError_t launch_dequant_fat(const void* const q[3], const void* const sc[3],
     d.out[i] = (_Float16*)out[i];
     d.rows[i] = rows[i];
     d.K[i] = K[i];
-    d.out_ld[i] = out_ld[i];
   }
   hipLaunchKernelGGL(dequant_fat_kernel, dim3(grid, n), dim3(256), 0, s, d,
                      fat_list, meta);

@@ -105,9 +105,11 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
     const int ne = ((sconst_i32)a.offsets)[e + 1] - off;
     const int slot = a.fat_slot ? ((sconst_i32)a.fat_slot)[e] : -1;
     const size_t eix = slot >= 0 ? (size_t)slot : (size_t)e;
-    // caller weights are [N, K] rows of K; fp16 fat copies have padded rows
-    const uint32_t w_ld = slot >= 0 ? (uint32_t)a.s_ld : (uint32_t)K;
-    const uint32_t mat_bytes = (uint32_t)N * w_ld * 2u;
+    // caller weights are [N, K] rows of K; the fp16 fat copies are
+    // k-block-major, [K / 32][N][32], so one stage's 256 (or 2 x 128) weight
+    // rows are a single contiguous 16 KB (2 x 8 KB) slab
+    const bool tiled = slot >= 0;
+    const uint32_t mat_bytes = (uint32_t)N * (uint32_t)K * 2u;
 
     __amdgpu_buffer_rsrc_t r_even, r_odd;   // descriptors of this wave's blocks
     if (wave < 2) {
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
             row = nb * 128 + (R >> 7) * 64 + ((R >> 6) & 1) * 32 + (R & 31);
           else
             row = min(nb * kBW + R, N - 1);
-          rowoff = (uint32_t)row * w_ld * 2u;
+          rowoff = tiled ? (uint32_t)row * (uint32_t)kRowB : (uint32_t)row * (uint32_t)K * 2u;
         } else {
           const int Rt = R - 256;
           const int rr = min(row0 + (Rt % BT), ne - 1);
@@ -149,13 +151,15 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         }
         voff[jj] = rowoff + (uint32_t)c * 16u;
       }
+      // bytes from one stage's slice of a row to the next stage's
+      const int s_step = (wave < 2 && tiled) ? N * kRowB : kRowB;
       // Refill of ring stage kt. Past the last stage the slice nk-1 is read
       // again (an L2 hit) into a buffer no one reads any more, so every
       // stage issues the same number of loads and every wait below is a
       // constant count.
       auto issue_one = [&](int kt, int jj) {
         char* base = smem + (kt % kNS) * kStage + wave * kDmaPerWave * 1024;
-        const int soff = min(kt, nk - 1) * kRowB;
+        const int soff = min(kt, nk - 1) * s_step;
         const __amdgpu_buffer_rsrc_t rs =
             (MODE == 0 && ((jj >> 1) & 1)) ? r_odd : r_even;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -294,40 +298,90 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
       asm volatile("" : "+v"(lane_e));
       const int jt = lane_e & 31;
       const int hi4 = (lane_e >> 5) * 4;
+      using Y = typename YPairOf<S>::T;
+      if constexpr (MODE == 0 || sizeof(Y) == 2) {
+        // Through LDS: a lane holds 4 consecutive features of one token, so
+        // stores straight from the accumulators would write 16 B to each of
+        // 32 rows per instruction. Each wave stages its 128 tokens x (64
+        // features, or 128 outputs) as 2-byte values in its own 32 KB of the
+        // (now idle) ring, token-major with 8-byte chunks XOR-swizzled by
+        // token, then stores whole 128 / 256-byte row segments.
+        __builtin_amdgcn_s_barrier();   // every wave is done with the ring
+        char* stg = smem + wave * 32768;
+        constexpr int kRowB = MODE == 0 ? 128 : 256;     // staged bytes per token
+        constexpr int kSwz = MODE == 0 ? 7 : 15;
 #pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        const int trow_ = row0 + wt * (BT / 2) + t * 32 + jt;
-        if (trow_ >= ne) continue;
-        const size_t prow = (size_t)(off + trow_);
-        if (MODE == 0) {
+        for (int t = 0; t < TB; ++t) {
+          const int tok = t * 32 + jt;
+          const int sw = ((tok >> 1) & kSwz) << 1;
+          if (MODE == 0) {
 #pragma unroll
-          for (int p = 0; p < 2; ++p)
+            for (int p = 0; p < 2; ++p)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-              const int f = nb * 128 + ww * 64 + p * 32 + rq * 8 + hi4;
-              V4 hv, lv;
+              for (int rq = 0; rq < 4; ++rq) {
+                V4 hv, lv;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float h = swiglu(acc[2 * p][t][rq * 4 + q],
-                                       acc[2 * p + 1][t][rq * 4 + q], a.clamp);
-                hv[q] = (S)h;
-                lv[q] = (S)(h - (float)hv[q]);
+                for (int q = 0; q < 4; ++q) {
+                  const float h = swiglu(acc[2 * p][t][rq * 4 + q],
+                                         acc[2 * p + 1][t][rq * 4 + q], a.clamp);
+                  hv[q] = (S)h;
+                  lv[q] = (S)(h - (float)hv[q]);
+                }
+                const int pc = (p * 8 + rq * 2 + (hi4 >> 2)) ^ sw;
+                *reinterpret_cast<V4*>(stg + tok * kRowB + pc * 8) = hv;
+                if (a.out2) *reinterpret_cast<V4*>(stg + 16384 + tok * kRowB + pc * 8) = lv;
               }
-              *reinterpret_cast<V4*>(reinterpret_cast<S*>(a.out) + prow * a.out_ld + f) = hv;
-              if (a.out2)
-                *reinterpret_cast<V4*>(reinterpret_cast<S*>(a.out2) + prow * a.out_ld + f) = lv;
-            }
-        } else {
+          } else {
+#pragma unroll
+            for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+              for (int rq = 0; rq < 4; ++rq) {
+                typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                h4 v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = (_Float16)acc[wi][t][rq * 4 + q];
+                const int pc = (wi * 8 + rq * 2 + (hi4 >> 2)) ^ sw;
+                *reinterpret_cast<h4*>(stg + tok * kRowB + pc * 8) = v;
+              }
+          }
+        }
+        // read back 1 KB per instruction: kRowB / 16 lanes per token row
+        constexpr int kLpr = kRowB / 16;
+        constexpr int kRowsPer = 64 / kLpr;
+        const int rl = lane_e / kLpr, jp = lane_e % kLpr;
+        const int tok_base = row0 + wt * (BT / 2);
+        const int planes = (MODE == 0 && a.out2) ? 2 : 1;
+        for (int pl = 0; pl < planes; ++pl) {
+          S* dst = reinterpret_cast<S*>(pl ? a.out2 : a.out);
+#pragma unroll 4
+          for (int it = 0; it < 128 / kRowsPer; ++it) {
+            const int tok = it * kRowsPer + rl;
+            const int sw = ((tok >> 1) & kSwz) << 1;
+            const uint4 v = *reinterpret_cast<const uint4*>(
+                stg + pl * 16384 + tok * kRowB + (((2 * jp) ^ sw) * 8));
+            if (tok_base + tok >= ne) continue;
+            const size_t prow = (size_t)(off + tok_base + tok);
+            const int col = MODE == 0 ? nb * 128 + ww * 64 + jp * 8
+                                      : nb * kBW + ww * 128 + jp * 8;
+            if (MODE == 1 && col >= N) continue;
+            *reinterpret_cast<uint4*>(dst + prow * a.out_ld + col) = v;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const int trow_ = row0 + wt * (BT / 2) + t * 32 + jt;
+          if (trow_ >= ne) continue;
+          const size_t prow = (size_t)(off + trow_);
 #pragma unroll
           for (int wi = 0; wi < 4; ++wi)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
               const int d = nb * kBW + ww * 128 + wi * 32 + rq * 8 + hi4;
               if (d >= N) continue;
-              store_y4<typename YPairOf<S>::T>(
-                  a.out, prow * a.out_ld + d, acc[wi][t][rq * 4 + 0],
-                  acc[wi][t][rq * 4 + 1], acc[wi][t][rq * 4 + 2],
-                  acc[wi][t][rq * 4 + 3]);
+              store_y4<Y>(a.out, prow * a.out_ld + d, acc[wi][t][rq * 4 + 0],
+                          acc[wi][t][rq * 4 + 1], acc[wi][t][rq * 4 + 2],
+                          acc[wi][t][rq * 4 + 3]);
             }
         }
       }

@@ -172,7 +172,7 @@ struct FwdLayout {
   bool stream;       // split-K groups on the stream tile
   bool can_full, can_sk1, can_sk4, can_fat;
   bool split_h;   // bf16: SwiGLU output as a hi + lo bf16 pair
-  int h_ld, sg_ld, sd_ld;   // padded row strides (elements)
+  int h_ld;                 // padded row stride of H (elements)
 };
 
 bool dtypes_ok(int xdt, int wdt) {
@@ -219,8 +219,6 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   }
   const int xb = xbytes(xdt);
   L.h_ld = F + kPadBytes / xb;
-  L.sg_ld = D + kPadBytes / 2;     // fp16 copies of gate/up rows (K = D)
-  L.sd_ld = F + kPadBytes / 2;     // fp16 copies of down rows (K = F)
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
   L.H = take((size_t)Pmax * L.h_ld * xb + 16);
@@ -236,9 +234,10 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.fat_slot = take((size_t)n_exp * 4);
   L.fat_list = take((size_t)n_exp * 4);
   L.meta = take(kMetaCount * 4);
-  L.stg_g = take((size_t)L.max_fat * F * L.sg_ld * 2);
-  L.stg_u = take((size_t)L.max_fat * F * L.sg_ld * 2);
-  L.stg_d = take((size_t)L.max_fat * D * L.sd_ld * 2);
+  // fp16 copies of fat experts, k-block-major [K / 32][rows][32]
+  L.stg_g = take((size_t)L.max_fat * F * D * 2);
+  L.stg_u = take((size_t)L.max_fat * F * D * 2);
+  L.stg_d = take((size_t)L.max_fat * D * F * 2);
   L.bytes = off;
   return L;
 }
@@ -443,7 +442,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   const size_t lim31 = ((size_t)1 << 31) - 1;
   if ((size_t)d.T * D * xbytes(x_dtype) > lim31 ||
       Pmax_rows * (F * xbytes(x_dtype) + kPadBytes) > lim31 ||
-      (size_t)D * (F + kPadBytes) * 4 > lim31)
+      (size_t)D * F * 4 > lim31)
     return fail(MOE_EUNSUPPORTED, "x, the SwiGLU buffer and each weight "
                 "matrix must each stay below 2 GiB");
   if (ws_bytes < L.bytes)
@@ -490,15 +489,13 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   if (L.can_fat) {
     PhaseScope ps(rec, 1, s);
     const int grid = info.ncu * 8;
-    // one launch for the three matrices; rows of fat slots fit in int
-    // (max_fat * max(F, D) <= P * max(F, D) / fat_rows)
+    // one launch for the three matrices
     const void* const q[3] = {w_gate.data, w_up.data, w_down.data};
     const void* const sc[3] = {w_gate.scales, w_up.scales, w_down.scales};
     void* const out[3] = {b + L.stg_g, b + L.stg_u, b + L.stg_d};
     const int rows[3] = {F, F, D};
     const int Ks[3] = {D, D, F};
-    const int lds[3] = {L.sg_ld, L.sg_ld, L.sd_ld};
-    e = launch_dequant_fat(q, sc, out, rows, Ks, lds, 3,
+    e = launch_dequant_fat(q, sc, out, rows, Ks, 3,
                            (const int32_t*)(b + L.fat_list), meta, grid, s);
     if (e != hipSuccess) return hip_fail(e, "dequant kernel");
   }
@@ -522,14 +519,14 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     if (stage == 0) {
       g.K = D; g.N = F; g.A = x; g.A2 = nullptr; g.out = H; g.out2 = H2;
       g.a_bytes = (uint32_t)((size_t)d.T * D * xbytes(x_dtype));
-      g.a_ld = D; g.s_ld = L.sg_ld; g.out_ld = L.h_ld;
+      g.a_ld = D; g.out_ld = L.h_ld;
       g.B0 = w_gate.data; g.B0s = w_gate.scales;
       g.B1 = w_up.data; g.B1s = w_up.scales;
       g.S0 = b + L.stg_g; g.S1 = b + L.stg_u;
     } else {
       g.K = F; g.N = D; g.A = H; g.A2 = H2; g.out = Y; g.out2 = nullptr;
       g.a_bytes = (uint32_t)(Pmax_rows * L.h_ld * xbytes(x_dtype));
-      g.a_ld = L.h_ld; g.s_ld = L.sd_ld; g.out_ld = D;
+      g.a_ld = L.h_ld; g.out_ld = D;
       g.B0 = w_down.data; g.B0s = w_down.scales;
       g.B1 = nullptr; g.B1s = nullptr;
       g.S0 = b + L.stg_d; g.S1 = nullptr;

@@ -22,9 +22,8 @@ constexpr int kMaxExperts = 1024;
 
 // Token rows per full-tile work item (the classify kernel's tile list).
 constexpr int kFullBM = 256;
-// Row padding of the buffers the library lays out itself (the SwiGLU output
-// and the fp16 fat-expert copies): 256 bytes, so rows whose unpadded stride
-// is a large power of two do not all start on the same L2 channel.
+// Row padding of the SwiGLU output H: 256 bytes, so rows whose unpadded
+// stride is a large power of two do not all start on the same L2 channel.
 constexpr int kPadBytes = 256;
 // Split-K tile: output columns per item and rows per row block.
 constexpr int kSkNB = 64;
@@ -89,7 +88,6 @@ struct GemmArgs {
   const void* A2;           // down, bf16 split H: the low plane; else null
   uint32_t a_bytes;         // bytes of A (and of A2): below 2^31
   int a_ld;                 // A row stride, elements
-  int s_ld;                 // row stride of the fp16 fat-expert copies, elements
   int out_ld;               // output row stride, elements
   const int32_t* pair_token;// gather map for gate/up
   const int32_t* offsets;   // [n_exp + 1]
@@ -98,7 +96,8 @@ struct GemmArgs {
   // uses B0 = W_down. q4: data + scales.
   const void* B0; const void* B0s;
   const void* B1; const void* B1s;
-  // Dequantised fp16 copies of fat experts: [slot, rows, K]; nullptr if none.
+  // Dequantised fp16 copies of fat experts, k-block-major: [slot][K / 32]
+  // [rows][32]; nullptr if none.
   const void* S0; const void* S1;
   const int32_t* fat_slot;
   void* out;                // H [P, F] (x's dtype) or Ypair [P, D] (unweighted;
@@ -122,9 +121,8 @@ hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
                             hipStream_t s);
 hipError_t launch_dequant_fat(const void* const q[3], const void* const sc[3],
                               void* const out[3], const int rows[3],
-                              const int K[3], const int out_ld[3], int n,
-                              const int32_t* fat_list, const int32_t* meta,
-                              int grid, hipStream_t s);
+                              const int K[3], int n, const int32_t* fat_list,
+                              const int32_t* meta, int grid, hipStream_t s);
 hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
                                int64_t rows, int K, hipStream_t s);
 hipError_t launch_combine(const void* ypair, int ypair_f16,
