@@ -145,14 +145,18 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         } else {
           const int Rt = R - 256;
           const int rr = min(row0 + (Rt % BT), ne - 1);
-          const uint32_t prow = MODE == 0 ? (uint32_t)a.pair_token[off + rr]
-                                          : (uint32_t)(off + rr);
-          rowoff = prow * (uint32_t)a.a_ld * 2u;
+          if (MODE == 0) {
+            rowoff = (uint32_t)a.pair_token[off + rr] * (uint32_t)a.a_ld * 2u;
+          } else {
+            // the SwiGLU output of full-tile experts is k-block-major too
+            rowoff = (uint32_t)(off + rr) * (uint32_t)kRowB;
+          }
         }
         voff[jj] = rowoff + (uint32_t)c * 16u;
       }
       // bytes from one stage's slice of a row to the next stage's
-      const int s_step = (wave < 2 && tiled) ? N * kRowB : kRowB;
+      const int s_step = wave < 2 ? (tiled ? N * kRowB : kRowB)
+                                  : (MODE == 1 ? a.h_rows * kRowB : kRowB);
       // Refill of ring stage kt. Past the last stage the slice nk-1 is read
       // again (an L2 hit) into a buffer no one reads any more, so every
       // stage issues the same number of loads and every wait below is a
@@ -345,25 +349,42 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
               }
           }
         }
-        // read back 1 KB per instruction: kRowB / 16 lanes per token row
-        constexpr int kLpr = kRowB / 16;
-        constexpr int kRowsPer = 64 / kLpr;
-        const int rl = lane_e / kLpr, jp = lane_e % kLpr;
         const int tok_base = row0 + wt * (BT / 2);
-        const int planes = (MODE == 0 && a.out2) ? 2 : 1;
-        for (int pl = 0; pl < planes; ++pl) {
-          S* dst = reinterpret_cast<S*>(pl ? a.out2 : a.out);
+        if (MODE == 0) {
+          // H of full-tile experts, k-block-major [F / 32][h_rows][32]: per
+          // instruction 16 tokens x one 32-feature block = 1 KB contiguous
+          const int rl = lane_e >> 2, jp = lane_e & 3;
+          const int planes = a.out2 ? 2 : 1;
+          for (int pl = 0; pl < planes; ++pl) {
+            char* dst = reinterpret_cast<char*>(pl ? a.out2 : a.out);
 #pragma unroll 4
-          for (int it = 0; it < 128 / kRowsPer; ++it) {
-            const int tok = it * kRowsPer + rl;
+            for (int it = 0; it < 16; ++it) {
+              const int kbl = it & 1;              // which 32 of the 64 features
+              const int tok = (it >> 1) * 16 + rl;
+              const int sw = ((tok >> 1) & kSwz) << 1;
+              const int j = kbl * 4 + jp;          // 16-byte piece of the row
+              const uint4 v = *reinterpret_cast<const uint4*>(
+                  stg + pl * 16384 + tok * kRowB + (((2 * j) ^ sw) * 8));
+              if (tok_base + tok >= ne) continue;
+              const size_t prow = (size_t)(off + tok_base + tok);
+              const size_t kb = (size_t)((nb * 128 + ww * 64) / 32 + kbl);
+              *reinterpret_cast<uint4*>(dst + ((kb * a.h_rows + prow) * 32) * sizeof(S) + jp * 16) = v;
+            }
+          }
+        } else {
+          // Ypair rows: 1 KB per instruction, 16 lanes per 256-byte row run
+          const int rl = lane_e >> 4, jp = lane_e & 15;
+          S* dst = reinterpret_cast<S*>(a.out);
+#pragma unroll 4
+          for (int it = 0; it < 32; ++it) {
+            const int tok = it * 4 + rl;
             const int sw = ((tok >> 1) & kSwz) << 1;
             const uint4 v = *reinterpret_cast<const uint4*>(
-                stg + pl * 16384 + tok * kRowB + (((2 * jp) ^ sw) * 8));
+                stg + tok * kRowB + (((2 * jp) ^ sw) * 8));
             if (tok_base + tok >= ne) continue;
             const size_t prow = (size_t)(off + tok_base + tok);
-            const int col = MODE == 0 ? nb * 128 + ww * 64 + jp * 8
-                                      : nb * kBW + ww * 128 + jp * 8;
-            if (MODE == 1 && col >= N) continue;
+            const int col = nb * kBW + ww * 128 + jp * 8;
+            if (col >= N) continue;
             *reinterpret_cast<uint4*>(dst + prow * a.out_ld + col) = v;
           }
         }

@@ -166,8 +166,8 @@ struct PhaseScope {
 };
 
 struct FwdLayout {
-  size_t H, H2, Y, full_tiles, sk1, sk4, sk1_tok, sk4_tok, part, fat_slot,
-      fat_list, meta, stg_g, stg_u, stg_d, bytes;
+  size_t H, H2, Ht, Ht2, Y, full_tiles, sk1, sk4, sk1_tok, sk4_tok, part,
+      fat_slot, fat_list, meta, stg_g, stg_u, stg_d, bytes;
   int cap_tiles, cap_sk1, cap_sk4, max_fat, fat_rows;
   bool stream;       // split-K groups on the stream tile
   bool can_full, can_sk1, can_sk4, can_fat;
@@ -224,6 +224,9 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.H = take((size_t)Pmax * L.h_ld * xb + 16);
   L.split_h = xdt == MOE_BF16 && !(o.flags & MOE_OPT_BF16_PLAIN_H);
   L.H2 = take(L.split_h ? (size_t)Pmax * L.h_ld * 2 + 16 : 0);
+  // H of full-tile experts, k-block-major [F / 32][Pmax][32]
+  L.Ht = take(L.can_full ? (size_t)Pmax * F * xb + 16 : 0);
+  L.Ht2 = take(L.can_full && L.split_h ? (size_t)Pmax * F * 2 + 16 : 0);
   L.Y = take((size_t)Pmax * D * (xdt == MOE_F16 ? 2 : 4) + 16);   // Ypair
   L.full_tiles = take((size_t)L.cap_tiles * 8);
   L.sk1 = take((size_t)L.cap_sk1 * 16);
@@ -534,10 +537,20 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     if (L.can_full) {
       PhaseScope ps(rec, stage == 0 ? 2 : 4, s);
       const int nnb = stage == 0 ? F / 128 : (D + 255) / 256;
-      g.list = (const int32_t*)(b + L.full_tiles);
-      g.meta_index = kMetaFullTiles;
+      GemmArgs gf = g;
+      gf.h_rows = (int)Pmax_rows;
+      void* Ht = b + L.Ht;
+      void* Ht2 = L.split_h ? b + L.Ht2 : nullptr;
+      if (stage == 0) {
+        gf.out = Ht; gf.out2 = Ht2;
+      } else {
+        gf.A = Ht; gf.A2 = Ht2;
+        gf.a_bytes = (uint32_t)(Pmax_rows * F * xbytes(x_dtype));
+      }
+      gf.list = (const int32_t*)(b + L.full_tiles);
+      gf.meta_index = kMetaFullTiles;
       const int grid = (int)std::min<int64_t>((int64_t)L.cap_tiles * nnb, full_grid_cap);
-      e = launch_gemm_full(g, x_dtype, grid, s);
+      e = launch_gemm_full(gf, x_dtype, grid, s);
       if (e != hipSuccess) return hip_fail(e, "full tile kernel");
     }
     {

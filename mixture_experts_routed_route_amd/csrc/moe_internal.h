@@ -107,6 +107,9 @@ struct GemmArgs {
   const int32_t* list;      // work list (full tiles or split-K groups)
   const int32_t* meta;      // counts of the work lists
   int meta_index;           // which meta counter holds this list's length
+  int h_rows;               // full tile: rows of the k-block-major H
+                            // ([F / 32][h_rows][32]) it writes (gate/up) or
+                            // reads (down)
   const int32_t* tok;       // stream tile, gate/up: the sk1 groups' x rows
   float* part;              // stream tile: [kStreamMaxRuns, 2, kStreamSlotFloats]
 };
