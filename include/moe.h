@@ -80,11 +80,13 @@ typedef struct {
  *   swiglu_limit      c of h = silu(min(g, c)) * clamp(u, -c, c); <= 0 turns
  *                     the clamp off. Default 7.0.
  *   splitk_max_pairs  S: bf16/f16 experts holding n <= S pairs run the
- *                     split-K tile, the rest the full MFMA tile. An f32
+ *                     split-K (weight-streaming) tile, the rest the full
+ *                     MFMA tile. An f32
  *                     bound compared exactly in f64 (TensorFold PR #1607,
  *                     "Why 3.5, and why a fraction"); 0 sends every expert
  *                     to the full tile, a huge value every expert to
- *                     split-K. Default: the switch point measured on MI355X.
+ *                     split-K. Default 16, the switch point measured on
+ *                     MI355X.
  *   fat_rows          4-bit weights only: experts holding >= fat_rows pairs
  *                     are dequantised once to fp16 and run the full tile;
  *                     the rest run the fused-dequant split-K tile. <= 0 turns
@@ -188,7 +190,9 @@ size_t moe_forward_workspace_bytes(const moe_plan *plan, int32_t D, int32_t F,
  * compute the dispatch buffer in the compute dtype and return the layer
  * output in the residual's fp32, mini-AGI PR #4, minagi/pool.py, the
  * compute-dtype comment) or x's dtype (one rounding of that f32 result).
- * Each kept pair's output is held in f32; the combine weights and sums them. */
+ * Each kept pair's unweighted output is held in fp16 in an fp16 layer (the
+ * precision of its fp16 SwiGLU input) and in f32 otherwise; the combine
+ * multiplies it by the routing weight in f32 and sums in slot order. */
 moe_status moe_forward(const moe_plan *plan, const void *x, int32_t x_dtype,
                        moe_weight w_gate, moe_weight w_up, moe_weight w_down,
                        int32_t D, int32_t F, void *y, int32_t y_dtype,
