@@ -116,8 +116,11 @@ def main():
         return tuple(t.to(dev) for t in w) if isinstance(w, tuple) else w.to(dev)
 
     wg, wu, wd = dv(wl["w_gate"]), dv(wl["w_up"]), dv(wl["w_down"])
+    # an explicit switch point is applied exactly (the sweep of the switch
+    # point compares the two tiles at every size)
+    exact = args.splitk_max_pairs is not None
     opts = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
-                            fat_rows=args.fat_rows)
+                            fat_rows=args.fat_rows, exact_routes=exact)
     if not args.no_phase_events:
         opts.flags |= moe.MOE_OPT_PHASE_EVENTS
 
@@ -180,6 +183,12 @@ def main():
         full_mask = counts < 0
     else:
         full_mask = counts.astype(np.float64) > S
+        if not exact:
+            # an underfilled full route hands experts of <= 256 rows over
+            tiles = int(((counts[full_mask] + 255) // 256).sum())
+            ncu = torch.cuda.get_device_properties(0).multi_processor_count
+            if tiles * (F // 128) < ncu:
+                full_mask &= counts > 256
     sk_mask = (counts > 0) & ~full_mask
     rows_full = int(counts[full_mask].sum())
     wbytes = W.weight_bytes_per_expert(D, F, wl["w_dtype"]) / 3.0   # per matrix

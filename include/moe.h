@@ -86,7 +86,12 @@ typedef struct {
  *                     "Why 3.5, and why a fraction"); 0 sends every expert
  *                     to the full tile, a huge value every expert to
  *                     split-K. Default 16, the switch point measured on
- *                     MI355X.
+ *                     MI355X. Unless MOE_OPT_EXACT_ROUTES is set, a plan
+ *                     whose full-tile experts would not fill one round of
+ *                     the GPU's compute units (their 256-row tiles times
+ *                     F / 128 column blocks < compute units) sends those of
+ *                     them holding <= 256 pairs to split-K as well: the
+ *                     full tile would leave most units idle.
  *   fat_rows          4-bit weights only: experts holding >= fat_rows pairs
  *                     are dequantised once to fp16 and run the full tile;
  *                     the rest run the fused-dequant split-K tile. <= 0 turns
@@ -101,7 +106,8 @@ typedef struct {
  *                     bf16 pair hi + lo (hi = bf16(h), lo = bf16(h - hi),
  *                     about 16 significant bits) and the down projection
  *                     multiplies both, so a layer whose output is mostly
- *                     dropped rows still meets 2e-2 x RMS(ref). */
+ *                     dropped rows still meets 2e-2 x RMS(ref).
+ *                     MOE_OPT_EXACT_ROUTES applies the S rule alone. */
 typedef struct {
     float swiglu_limit;
     float splitk_max_pairs;
@@ -111,6 +117,7 @@ typedef struct {
 
 #define MOE_OPT_PHASE_EVENTS 1
 #define MOE_OPT_BF16_PLAIN_H 2
+#define MOE_OPT_EXACT_ROUTES 4
 
 /* One weight tensor. `scales` is NULL unless dtype is MOE_Q4B32. */
 typedef struct {
@@ -130,8 +137,10 @@ typedef struct {
     int64_t touched;        /* routed experts holding >= 1 kept pair       */
     int64_t max_rows;       /* most kept pairs one routed expert holds     */
     int64_t nonfinite;      /* NaN logits seen (ordered below -inf)        */
-    int64_t thin, full, fat;/* routed experts per forward route, for the
-                               options passed to moe_plan_stats_get        */
+    int64_t thin, full, fat;/* routed experts per forward route by the S
+                               and fat_rows rules of the options passed to
+                               moe_plan_stats_get (without the move of an
+                               underfilled full route to split-K)         */
     double drop_fraction;   /* dropped / pairs (mini-AGI PR #3,
                                tools/bench_hw.py `dropped_share`)          */
 } moe_plan_stats;

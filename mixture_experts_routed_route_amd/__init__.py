@@ -29,6 +29,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, 
 MOE_F32, MOE_BF16, MOE_F16, MOE_Q4B32 = 0, 1, 2, 3
 MOE_OPT_PHASE_EVENTS = 1
 MOE_OPT_BF16_PLAIN_H = 2
+MOE_OPT_EXACT_ROUTES = 4
 MOE_N_PHASES = 7
 PHASES = ("classify", "dequant_once", "gateup_full", "gateup_splitk",
           "down_full", "down_splitk", "combine")
@@ -155,7 +156,9 @@ def moe_options_default() -> Options:
 
 
 def make_options(swiglu_limit=None, splitk_max_pairs=None, fat_rows=None,
-                 flags=None) -> Options:
+                 flags=None, exact_routes=False) -> Options:
+    """Options with the defaults, except what is given. exact_routes sets
+    MOE_OPT_EXACT_ROUTES (the S rule alone decides split-K vs full)."""
     o = moe_options_default()
     if swiglu_limit is not None:
         o.swiglu_limit = float(swiglu_limit)
@@ -165,6 +168,8 @@ def make_options(swiglu_limit=None, splitk_max_pairs=None, fat_rows=None,
         o.fat_rows = int(fat_rows)
     if flags is not None:
         o.flags = int(flags)
+    if exact_routes:
+        o.flags |= MOE_OPT_EXACT_ROUTES
     return o
 
 

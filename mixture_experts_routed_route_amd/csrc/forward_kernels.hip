@@ -70,6 +70,12 @@ __device__ __forceinline__ int block_excl(int v, int* total, int* sh) {
 // One block of 1024 threads. Route per expert from its kept rows n:
 //   mode 0 (f32): split-K; mode 1 (bf16/f16): split-K iff n <= S, else full;
 //   mode 2 (q4): fat iff fat_rows > 0 and n >= fat_rows, else split-K.
+// Mode 1 with full_fill > 0: if the full experts' tiles times the column
+// blocks per tile would not occupy full_fill work-groups (one round of the
+// persistent full tile), the full tile would leave most compute units idle
+// while each busy one walks the whole K; the split-K tile spreads the same
+// weights over every unit instead, so full experts of at most kFullBM rows
+// move to split-K.
 // Full/fat experts are ordered largest first (ties: lower index) and cut into
 // kFullBM-row tiles. Split-K experts are cut into groups of <= 64 rows;
 // groups of at most 16 rows go to the first list, the others to the second;
@@ -82,9 +88,10 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
   __shared__ int order[kPadE];
   __shared__ int sh[16];
   __shared__ int nfull_sh;
+  __shared__ int ntiles_sh;
   const int n = a.n_exp;
   const int n4 = (n + 3) / 4 * 4;
-  if (threadIdx.x == 0) nfull_sh = 0;
+  if (threadIdx.x == 0) { nfull_sh = 0; ntiles_sh = 0; }
   for (int e = threadIdx.x; e < n4; e += blockDim.x) {
     const int c = e < n ? a.counts[e] : 0;
     int r = kRouteNone;
@@ -98,6 +105,21 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
     fkey[e] = r >= kRouteFull ? c : -1;
   }
   __syncthreads();
+  if (a.mode == 1 && a.full_fill > 0) {
+    int t = 0;
+    for (int e = threadIdx.x; e < n; e += blockDim.x)
+      if (rte[e] == kRouteFull) t += (cnt[e] + kFullBM - 1) / kFullBM;
+    if (t) atomicAdd(&ntiles_sh, t);
+    __syncthreads();
+    if ((int64_t)ntiles_sh * a.full_nnb < (int64_t)a.full_fill) {
+      for (int e = threadIdx.x; e < n; e += blockDim.x)
+        if (rte[e] == kRouteFull && cnt[e] <= kFullBM) {
+          rte[e] = kRouteSplitK;
+          fkey[e] = -1;
+        }
+    }
+    __syncthreads();
+  }
   // rank among full/fat experts: more rows first, then the lower index
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     if (rte[e] < kRouteFull) continue;

@@ -212,10 +212,13 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
     L.can_sk4 = L.fat_rows == 0 || L.fat_rows > 17;
   } else {
     const double S = (double)o.splitk_max_pairs;
+    // without MOE_OPT_EXACT_ROUTES an underfilled full route hands experts
+    // of up to kFullBM rows to split-K, in groups of both sizes
+    const bool moves = !(o.flags & MOE_OPT_EXACT_ROUTES) && S < (double)Pmax;
     L.can_fat = false;
     L.can_full = S < (double)Pmax;
-    L.can_sk1 = S >= 1.0;
-    L.can_sk4 = S > 16.0;
+    L.can_sk1 = S >= 1.0 || moves;
+    L.can_sk4 = S > 16.0 || moves;
   }
   const int xb = xbytes(xdt);
   L.h_ld = F + kPadBytes / xb;
@@ -475,6 +478,8 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     ca.n_exp = n_exp;
     ca.mode = wdt == MOE_F32 ? 0 : (wdt == MOE_Q4B32 ? 2 : 1);
     ca.S = (double)o.splitk_max_pairs;
+    ca.full_nnb = F / 128;
+    ca.full_fill = (ca.mode == 1 && !(o.flags & MOE_OPT_EXACT_ROUTES)) ? info.ncu : 0;
     ca.fat_rows = L.fat_rows;
     ca.full_tiles = (int32_t*)(b + L.full_tiles);
     ca.sk1 = (int32_t*)(b + L.sk1);

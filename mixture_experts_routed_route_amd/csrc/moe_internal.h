@@ -64,6 +64,11 @@ struct ClassifyArgs {
   int n_exp;               // E + n_shared
   int mode;                // 0: all split-K (f32), 1: by S (bf16/f16), 2: q4
   double S;                // split-K bound in pairs per expert (f32 value)
+  int full_nnb;            // mode 1: gate/up column blocks per full tile
+  int full_fill;           // mode 1: work-groups that one round of the full
+                           // tile occupies; when its tiles x full_nnb fall
+                           // short of that, experts of <= kFullBM rows move
+                           // to split-K. 0: the S rule alone
   int fat_rows;            // q4: >= fat_rows -> fat; <= 0 off
   int32_t* full_tiles;     // [cap] (expert, row0) pairs as int2
   int32_t* sk1;            // [cap] (expert, row0, nrows, pstart) as int4,

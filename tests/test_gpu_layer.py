@@ -50,7 +50,7 @@ def test_prefill_forced_routes(S):
     """All experts on the full tile (S=0) or all on split-K (S=1e9)."""
     wl = W.config(3)
     say(f"layer prefill_zipf S={S}")
-    opts = moe.make_options(splitk_max_pairs=S)
+    opts = moe.make_options(splitk_max_pairs=S, exact_routes=True)
     p, y = gpu_layer(wl, options=opts)
     check_layer(wl, y, sample_tokens(wl["T"], 96, seed=4))
 
@@ -63,12 +63,30 @@ def test_short_prompt_shared(T):
     check_layer(wl, y, sample_tokens(T, 64, seed=T))
 
 
+@pytest.mark.parametrize("exact", [False, True])
+def test_underfilled_full_route(exact):
+    # the shared expert (250 rows) and a few experts of 17..256 rows: their
+    # full tiles (F / 128 = 2 column blocks each) cannot fill the GPU, so by
+    # default they run as 64-row split-K groups; with exact routes, on the
+    # full tile. Same plan, both within the bar, and equal to each other up
+    # to summation order.
+    bias = torch.zeros(16)
+    bias[:3] = torch.tensor([4.0, 3.0, 2.5])
+    wl = W.make_layer(250, 256, 256, 16, 2, W.BF16, seed=61, n_shared=1,
+                      logit_bias=bias)
+    say(f"layer underfilled full route exact={exact}")
+    p, y = gpu_layer(wl, options=moe.make_options(exact_routes=exact))
+    check_plan(wl, p)
+    check_layer(wl, y)
+
+
 @pytest.mark.parametrize("ppe", [1, 3, 4, 8])
 @pytest.mark.parametrize("S", [0.0, 1e9])
 def test_pairs_per_expert_both_tiles(ppe, S):
     wl = W.config(5, pairs_per_expert=ppe)
     say(f"layer {wl['name']} S={S}")
-    p, y = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=S))
+    p, y = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=S,
+                                                  exact_routes=True))
     check_layer(wl, y, sample_tokens(wl["T"], 24, seed=ppe))
 
 
@@ -124,7 +142,8 @@ def test_stream_tile_row_blocks(S):
     # 64 rows in four token blocks (S > 16), bf16 hi + lo planes included
     wl = W.make_layer(600, 512, 256, 32, 2, W.BF16, seed=51, n_shared=1)
     say(f"layer stream tile S={S}")
-    p, y = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=S))
+    p, y = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=S,
+                                                  exact_routes=True))
     check_layer(wl, y, sample_tokens(wl["T"], 96, seed=3))
 
 
@@ -177,8 +196,10 @@ def test_deterministic_and_routes_agree():
     a = gpu_layer(wl)[1]
     b = gpu_layer(wl)[1]
     assert torch.equal(a, b)                       # bitwise, run to run
-    c = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=0.0))[1]
-    d = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=1e9))[1]
+    c = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=0.0,
+                                               exact_routes=True))[1]
+    d = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=1e9,
+                                               exact_routes=True))[1]
     ref = oracle_layer(wl, sample_tokens(wl["T"], 32, seed=1))
     toks = sample_tokens(wl["T"], 32, seed=1)
     for y in (c, d):
