@@ -54,6 +54,21 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
 }
 
+// Work-item order for a persistent grid of G blocks, in rounds of G items:
+// the blocks of one XCD (hardware block ids b = x mod 8) take one contiguous
+// run of the round's items, so items that share operands (the column blocks
+// of one expert group) run on one XCD and share its L2. A round of R < G
+// items gives XCD x floor(R / 8) or one more. Returns the item of block b in
+// the round starting at rb0, or -1 if b sits this round out.
+__device__ __forceinline__ int xcd_item(int rb0, int b, int G, int n_items) {
+  const int R = min(G, n_items - rb0);
+  if (G & 7) return b < R ? rb0 + b : -1;
+  const int x = b & 7, m = b >> 3;
+  const int q = R >> 3, r = R & 7;
+  if (m >= q + (x < r ? 1 : 0)) return -1;
+  return rb0 + x * q + min(x, r) + m;
+}
+
 // h = silu(min(g, c)) * clamp(u, -c, c); c <= 0: plain silu(g) * u.
 // silu(g) = g / (1 + e^-g) with the hardware's 2^x and reciprocal (about
 // one ulp each): the epilogues evaluate it for every (pair, feature), and a
@@ -91,6 +106,47 @@ __device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
       out[wi][2 * b + 1] = h[1];
     }
   }
+}
+
+// dequant32's 32 values in the order the 4-bit tiles feed the MFMA: out[w]
+// holds K positions 8 w + {0, 2, 4, 6, 1, 3, 5, 7}. The masked nibbles of
+// even and of odd positions each sit in their own byte, and one byte permute
+// with a word of 0x64 exponent bytes builds two fp16 values 0x6400 | v: no
+// per-pair OR as in dequant32. Values are the same fp16_rne(q * s). The A
+// operand of the same MFMA takes the same order (perm_k8).
+__device__ __forceinline__ void dequant32_kperm(uint4 raw, _Float16 s,
+                                                half8 out[4]) {
+  const half2v s2 = {s, s};
+  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+  constexpr uint32_t kExp = 0x64646464u;
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    // v = nibble ^ 8; bytes of lo: v at positions 0, 2, 4, 6; of hi: 1, 3, 5, 7
+    const uint32_t lo = (words[wi] & 0x0F0F0F0Fu) ^ 0x08080808u;
+    const uint32_t hi = ((words[wi] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+    // selector bytes 0..3 pick lo / hi bytes, 4 picks 0x64
+    const uint32_t p[4] = {__builtin_amdgcn_perm(kExp, lo, 0x04010400u),
+                           __builtin_amdgcn_perm(kExp, lo, 0x04030402u),
+                           __builtin_amdgcn_perm(kExp, hi, 0x04010400u),
+                           __builtin_amdgcn_perm(kExp, hi, 0x04030402u)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half2v h = __builtin_bit_cast(half2v, p[j]);
+      h = (h + off) * s2;
+      out[wi][2 * j] = h[0];
+      out[wi][2 * j + 1] = h[1];
+    }
+  }
+}
+
+// Eight 16-bit values a0..a7 reordered as dequant32_kperm orders K:
+// a0 a2 a4 a6 a1 a3 a5 a7.
+__device__ __forceinline__ uint4 perm_k8(uint4 v) {
+  return uint4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u),
+               __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+               __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
+               __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
 }
 
 // Per-pair outputs of the down projection: fp16 when the layer computes in

@@ -17,6 +17,7 @@
 // The combine gathers each token's pair rows, weighted, in fixed order, with
 // no atomics.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -356,8 +357,8 @@ hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
 // f0..f0+15, W_gate f0+16.., W_up f0+16.. for f0 = 32 nb, so g and u of one
 // feature land in matching accumulators of one lane.
 
-// 16-bit activations (bf16/f16), dense or 4-bit weights.
-template <class TT, int WQ, int RB, int MODE, int LO>
+// 16-bit activations and weights (bf16/f16).
+template <class TT, int RB, int MODE, int LO>
 __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
                                               int NNB, float* red) {
   using S = typename TT::S;
@@ -385,29 +386,18 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
     ap2[rb] = LO ? (const char*)a.A2 + (size_t)(off + rr) * a.a_ld * 2 : nullptr;
   }
   const char* bp[4];
-  const uint16_t* bsp[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     int row;
     const void* base;
-    const void* sbase;
     if (MODE == 0) {
       row = nb * 32 + (cb >> 1) * 16 + n;
       base = (cb & 1) ? a.B1 : a.B0;
-      sbase = (cb & 1) ? a.B1s : a.B0s;
     } else {
       row = nb * 64 + cb * 16 + n;
       base = a.B0;
-      sbase = a.B0s;
     }
-    const size_t wrow = (size_t)e * N + row;
-    if (WQ) {
-      bp[cb] = (const char*)base + wrow * (size_t)(K / 2);
-      bsp[cb] = (const uint16_t*)sbase + wrow * (size_t)(K / 32);
-    } else {
-      bp[cb] = (const char*)base + wrow * (size_t)K * 2;
-      bsp[cb] = nullptr;
-    }
+    bp[cb] = (const char*)base + ((size_t)e * N + row) * (size_t)K * 2;
   }
   floatx4 acc[RB][4];
 #pragma unroll
@@ -425,22 +415,10 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
 #pragma unroll
       for (int i = 0; i < 4; ++i) av[rb][i] = as_v8<V8>(ldg16(ap[rb] + (size_t)k0 * 2 + i * 16));
     V8 bv[4][4];
-    if (WQ) {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const uint4 raw = ldg16(bp[cb] + k0 / 2);
-        const uint16_t sb = bsp[cb][k0 / 32];
-        half8 h[4];
-        dequant32(raw, __builtin_bit_cast(_Float16, sb), h);
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bv[cb][i] = __builtin_bit_cast(V8, h[i]);
-      }
-    } else {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bv[cb][i] = as_v8<V8>(ldg16(bp[cb] + (size_t)k0 * 2 + i * 16));
-    }
+      for (int i = 0; i < 4; ++i) bv[cb][i] = as_v8<V8>(ldg16(bp[cb] + (size_t)k0 * 2 + i * 16));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -508,6 +486,158 @@ __device__ __forceinline__ void splitk_body16(const GemmArgs& a, int item,
           for (int cb = 0; cb < 4; ++cb) {
             const int d = nb * 64 + cb * 16 + n;
             store_y1<typename YPairOf<S>::T>(a.out, prow * a.out_ld + d, acc[rb][cb][r]);
+          }
+        }
+      }
+  }
+  __syncthreads();
+}
+
+// fp16 activations, 4-bit weights. As splitk_body16, but a lane reads 32
+// bytes of nibbles per weight row and super-step (256 K values), so the four
+// lanes of a row take one whole 128-byte line at a time: with 16-byte pieces
+// and 128-value super-steps, the two halves of a line came in different
+// super-steps, and rows of power-of-two strides lost the line from L2 in
+// between often enough to read most lines twice. A K not a multiple of 256
+// ends with one 128-value step.
+template <int RB, int KH>
+struct RawQ4 {
+  uint4 av[RB][4 * KH];   // A values k0 .. k0 + 32 KH of the lane's rows
+  uint4 w[4][KH];         // 32 KH nibbles of each column block's row
+  uint32_t sc[4];         // their KH scales (KH = 2: two fp16 in one word)
+};
+
+template <int RB, int MODE>
+__device__ __forceinline__ void splitk_body_q4(const GemmArgs& a, int item,
+                                               int NNB, float* red) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int K = a.K;
+  const int N = a.N;
+  const int g = item / NNB;
+  const int nb = item - g * NNB;
+  const int e = a.list[4 * g];
+  const int row0 = a.list[4 * g + 1];
+  const int nrows = a.list[4 * g + 2];
+  const int off = a.offsets[e];
+  const char* ap[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = row0 + min(rb * 16 + n, nrows - 1);
+    const int arow = MODE == 0 ? a.pair_token[off + rr] : off + rr;
+    ap[rb] = (const char*)a.A + (size_t)arow * a.a_ld * 2;
+  }
+  const uint8_t* bp[4];
+  const uint16_t* bsp[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    int row;
+    const void* base;
+    const void* sbase;
+    if (MODE == 0) {
+      row = nb * 32 + (cb >> 1) * 16 + n;
+      base = (cb & 1) ? a.B1 : a.B0;
+      sbase = (cb & 1) ? a.B1s : a.B0s;
+    } else {
+      row = nb * 64 + cb * 16 + n;
+      base = a.B0;
+      sbase = a.B0s;
+    }
+    const size_t wrow = (size_t)e * N + row;
+    bp[cb] = (const uint8_t*)base + wrow * (size_t)(K / 2);
+    bsp[cb] = (const uint16_t*)sbase + wrow * (size_t)(K / 32);
+  }
+  floatx4 acc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // one super-step of 128 KH values of K from kbase; lane q takes the
+  // 32 KH values from kbase + 32 KH q
+  auto step = [&](auto kh, int kbase) {
+    constexpr int KH = decltype(kh)::value;
+    RawQ4<RB, KH> r;
+    const int k0 = kbase + q * 32 * KH;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4 * KH; ++i) r.av[rb][i] = ldg16(ap[rb] + (size_t)k0 * 2 + i * 16);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+      for (int h = 0; h < KH; ++h) r.w[cb][h] = ldg16(bp[cb] + k0 / 2 + h * 16);
+      if constexpr (KH == 2)
+        r.sc[cb] = *reinterpret_cast<const uint32_t*>(bsp[cb] + k0 / 32);
+      else
+        r.sc[cb] = bsp[cb][k0 / 32];
+    }
+    // every load of the step is issued before the first use: left to
+    // itself, the scheduler sinks loads into the decode to save registers
+    // and then waits on each of them in turn
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int h = 0; h < KH; ++h) {
+        half8 hv[4];
+        dequant32(r.w[cb][h], __builtin_bit_cast(_Float16, (uint16_t)(r.sc[cb] >> (16 * h))), hv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][cb] = mfma16(as_v8<half8>(r.av[rb][4 * h + i]), hv[i], acc[rb][cb]);
+      }
+  };
+  const int nss = K / 256;
+  const int s0 = wave * nss / 4, s1 = (wave + 1) * nss / 4;
+  for (int s = s0; s < s1; ++s) step(std::integral_constant<int, 2>{}, s * 256);
+  if ((K & 255) && wave == 3) step(std::integral_constant<int, 1>{}, nss * 256);
+
+  // fixed-order reduction over the four K quarters: ((w0 + w1) + w2) + w3
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* p = red + ((rb * 4 + cb) * 4 + r) * 64 + lane;
+            *p = (w == 0) ? acc[rb][cb][r] : *p + acc[rb][cb][r];
+          }
+    }
+    __syncthreads();
+  }
+  if (wave == 3) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[rb][cb][r] = red[((rb * 4 + cb) * 4 + r) * 64 + lane] + acc[rb][cb][r];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rb * 16 + q * 4 + r;
+        if (row >= nrows) continue;
+        const size_t prow = (size_t)(off + row0 + row);
+        if (MODE == 0) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int f = nb * 32 + pr * 16 + n;
+            const float h = swiglu(acc[rb][2 * pr][r], acc[rb][2 * pr + 1][r], a.clamp);
+            reinterpret_cast<_Float16*>(a.out)[prow * a.out_ld + f] = (_Float16)h;
+          }
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const int d = nb * 64 + cb * 16 + n;
+            store_y1<_Float16>(a.out, prow * a.out_ld + d, acc[rb][cb][r]);
           }
         }
       }
@@ -635,7 +765,7 @@ __device__ __forceinline__ void splitk_body32(const GemmArgs& a, int item,
   __syncthreads();
 }
 
-template <class TT, int WQ, int RB, int MODE, int LO>
+template <class TT, int RB, int MODE, int LO>
 __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
   __shared__ float red[RB * 4 * 4 * 64];
   const int NNB = MODE == 0 ? a.N / 32 : a.N / 64;
@@ -644,35 +774,55 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
     if constexpr (TT::kBytes == 4)
       splitk_body32<RB, MODE>(a, item, NNB, red);
     else
-      splitk_body16<TT, WQ, RB, MODE, LO>(a, item, NNB, red);
+      splitk_body16<TT, RB, MODE, LO>(a, item, NNB, red);
   }
 }
 
-template <class TT, int WQ, int RB>
+// 4-bit weights, fp16 activations: four blocks per CU (128 registers), so
+// that 16 waves keep their loads in flight. The column blocks of one group
+// run on one XCD: its x rows, read by every column block, stay in that L2
+// while the weights stream past.
+template <int RB, int MODE>
+__global__ __launch_bounds__(256, 4) void gemm_splitk_q4_kernel(GemmArgs a) {
+  __shared__ float red[RB * 4 * 4 * 64];
+  const int NNB = MODE == 0 ? a.N / 32 : a.N / 64;
+  const int n_items = a.meta[a.meta_index] * NNB;
+  for (int rb0 = 0; rb0 < n_items; rb0 += gridDim.x) {
+    const int item = xcd_item(rb0, blockIdx.x, gridDim.x, n_items);
+    if (item >= 0) splitk_body_q4<RB, MODE>(a, item, NNB, red);
+  }
+}
+
+template <class TT, int RB>
 static hipError_t splitk_mode(const GemmArgs& a, int grid, hipStream_t s) {
   if (a.mode == 0)
-    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 0, 0>), dim3(grid), dim3(256), 0, s, a);
-  else if (TT::kBytes == 2 && !WQ && a.A2)
-    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 1, 1>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_splitk_kernel<TT, RB, 0, 0>), dim3(grid), dim3(256), 0, s, a);
+  else if (TT::kBytes == 2 && a.A2)
+    hipLaunchKernelGGL((gemm_splitk_kernel<TT, RB, 1, 1>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_splitk_kernel<TT, WQ, RB, 1, 0>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_splitk_kernel<TT, RB, 1, 0>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <class TT, int WQ>
+template <class TT>
 static hipError_t splitk_rb(const GemmArgs& a, int rb, int grid, hipStream_t s) {
-  return rb == 1 ? splitk_mode<TT, WQ, 1>(a, grid, s) : splitk_mode<TT, WQ, 4>(a, grid, s);
+  return rb == 1 ? splitk_mode<TT, 1>(a, grid, s) : splitk_mode<TT, 4>(a, grid, s);
 }
 
 hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
                               int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (xdt == MOE_F32 && wdt == MOE_F32) return splitk_rb<F32T, 0>(a, rb, grid, s);
-  if (xdt == MOE_BF16 && wdt == MOE_BF16) return splitk_rb<BF16T, 0>(a, rb, grid, s);
-  if (xdt == MOE_F16 && wdt == MOE_F16) return splitk_rb<F16T, 0>(a, rb, grid, s);
+  if (xdt == MOE_F32 && wdt == MOE_F32) return splitk_rb<F32T>(a, rb, grid, s);
+  if (xdt == MOE_BF16 && wdt == MOE_BF16) return splitk_rb<BF16T>(a, rb, grid, s);
+  if (xdt == MOE_F16 && wdt == MOE_F16) return splitk_rb<F16T>(a, rb, grid, s);
   if (xdt == MOE_F16 && wdt == MOE_Q4B32) {
-    // the down stage reads H (fp16) as A in every case
-    return splitk_rb<F16T, 1>(a, rb, grid, s);
+    // groups of <= 16 rows; the down stage reads H (fp16) as A in every case
+    if (rb != 1) return hipErrorInvalidValue;
+    if (a.mode == 0)
+      hipLaunchKernelGGL((gemm_splitk_q4_kernel<1, 0>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_splitk_q4_kernel<1, 1>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
   }
   return hipErrorInvalidValue;
 }

@@ -58,7 +58,10 @@ __global__ __launch_bounds__(256, 2) void gemm_wide_kernel(GemmArgs a) {
   const int n_items = a.meta[a.meta_index] * NNB;
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.A, a.a_bytes);
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  for (int rb0 = 0; rb0 < n_items; rb0 += gridDim.x) {
+    // the column blocks of one group on one XCD (its rows stay in that L2)
+    const int item = xcd_item(rb0, blockIdx.x, gridDim.x, n_items);
+    if (item < 0) continue;
     const int g = item / NNB;
     const int nb = item - g * NNB;
     const int e = a.list[4 * g];
