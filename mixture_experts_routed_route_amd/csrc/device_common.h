@@ -82,71 +82,36 @@ __device__ __forceinline__ float swiglu(float g, float u, float c) {
   return g * __builtin_amdgcn_rcpf(1.f + e) * u;
 }
 
-// 32 consecutive 4-bit values (16 bytes, low nibble first) times their block
-// scale, as 4 x 8 fp16: fp16 bits 0x6400 | v encode 1024 + v exactly, v =
-// nibble ^ 8; subtracting 1032 leaves the signed value q exactly, and one
-// fp16 multiply gives fp16_rne(q * s).
+// 8 consecutive 4-bit values (one 32-bit word, low nibble first) times
+// their block scale, as 8 fp16: fp16 bits 0x6400 | v encode 1024 + v
+// exactly, v = nibble ^ 8; subtracting 1032 leaves the signed value q
+// exactly, and one fp16 multiply gives fp16_rne(q * s).
+__device__ __forceinline__ half8 dequant_word(uint32_t word, _Float16 s) {
+  const half2v s2 = {s, s};
+  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const uint32_t x = word ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu;
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+  half8 out;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    // bytes of the result: [lo_b, 0, hi_b, 0] (selector 12 gives zero)
+    const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
+    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    half2v h = __builtin_bit_cast(half2v, pr);
+    h = (h + off) * s2;
+    out[2 * b] = h[0];
+    out[2 * b + 1] = h[1];
+  }
+  return out;
+}
+
+// 32 consecutive 4-bit values (16 bytes) of one block, as 4 x 8 fp16.
 __device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
-  const half2v s2 = {s, s};
-  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int wi = 0; wi < 4; ++wi) {
-    const uint32_t x = words[wi] ^ 0x88888888u;
-    const uint32_t lo = x & 0x0F0F0F0Fu;
-    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      // bytes of the result: [lo_b, 0, hi_b, 0] (selector 12 gives zero)
-      const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
-      const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
-      half2v h = __builtin_bit_cast(half2v, pr);
-      h = (h + off) * s2;
-      out[wi][2 * b] = h[0];
-      out[wi][2 * b + 1] = h[1];
-    }
-  }
-}
-
-// dequant32's 32 values in the order the 4-bit tiles feed the MFMA: out[w]
-// holds K positions 8 w + {0, 2, 4, 6, 1, 3, 5, 7}. The masked nibbles of
-// even and of odd positions each sit in their own byte, and one byte permute
-// with a word of 0x64 exponent bytes builds two fp16 values 0x6400 | v: no
-// per-pair OR as in dequant32. Values are the same fp16_rne(q * s). The A
-// operand of the same MFMA takes the same order (perm_k8).
-__device__ __forceinline__ void dequant32_kperm(uint4 raw, _Float16 s,
-                                                half8 out[4]) {
-  const half2v s2 = {s, s};
-  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-  constexpr uint32_t kExp = 0x64646464u;
-#pragma unroll
-  for (int wi = 0; wi < 4; ++wi) {
-    // v = nibble ^ 8; bytes of lo: v at positions 0, 2, 4, 6; of hi: 1, 3, 5, 7
-    const uint32_t lo = (words[wi] & 0x0F0F0F0Fu) ^ 0x08080808u;
-    const uint32_t hi = ((words[wi] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
-    // selector bytes 0..3 pick lo / hi bytes, 4 picks 0x64
-    const uint32_t p[4] = {__builtin_amdgcn_perm(kExp, lo, 0x04010400u),
-                           __builtin_amdgcn_perm(kExp, lo, 0x04030402u),
-                           __builtin_amdgcn_perm(kExp, hi, 0x04010400u),
-                           __builtin_amdgcn_perm(kExp, hi, 0x04030402u)};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      half2v h = __builtin_bit_cast(half2v, p[j]);
-      h = (h + off) * s2;
-      out[wi][2 * j] = h[0];
-      out[wi][2 * j + 1] = h[1];
-    }
-  }
-}
-
-// Eight 16-bit values a0..a7 reordered as dequant32_kperm orders K:
-// a0 a2 a4 a6 a1 a3 a5 a7.
-__device__ __forceinline__ uint4 perm_k8(uint4 v) {
-  return uint4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u),
-               __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
-               __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
-               __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
+  out[0] = dequant_word(raw.x, s);
+  out[1] = dequant_word(raw.y, s);
+  out[2] = dequant_word(raw.z, s);
+  out[3] = dequant_word(raw.w, s);
 }
 
 // Per-pair outputs of the down projection: fp16 when the layer computes in

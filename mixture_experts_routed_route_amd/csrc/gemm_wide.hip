@@ -18,6 +18,10 @@
 // f0.., W_gate f0+16.., W_up f0+16.., f0 = 128 nb + 32 w.
 #include "device_common.h"
 
+#ifndef WIDE_OCC
+#define WIDE_OCC 2
+#endif
+
 namespace moe {
 
 namespace {
@@ -43,7 +47,7 @@ template <>
 struct WChunk<0> { uint4 d[4][4]; };
 
 template <class TT, int WQ, int MODE>
-__global__ __launch_bounds__(256, 2) void gemm_wide_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
   using S = typename TT::S;
   using V8 = typename TT::V8;
   __shared__ __attribute__((aligned(1024))) char smem[kNA * kChunkB];
@@ -139,30 +143,31 @@ __global__ __launch_bounds__(256, 2) void gemm_wide_kernel(GemmArgs a) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // per 32-value slice i: the four row blocks' A fragments, then each
+    // column block's slice decoded just before its MFMAs (16 + 16 operand
+    // registers instead of all 64 decoded values at once)
     auto compute = [&](int ch, const WChunk<WQ>& w) {
-      V8 bv[4][4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if constexpr (WQ) {
-          half8 h[4];
-          dequant32(w.q[cb], __builtin_bit_cast(_Float16, (uint16_t)w.s[cb]), h);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) bv[cb][i] = __builtin_bit_cast(V8, h[i]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) bv[cb][i] = __builtin_bit_cast(V8, w.d[cb][i]);
-        }
-      }
       const char* As = smem + (ch % kNA) * kChunkB;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        V8 av[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           const int r = rb * 16 + n;
           const int c = (q * 4 + i) ^ (r & 15);
-          const V8 av = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(As + r * 256 + c * 16));
+          av[rb] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(As + r * 256 + c * 16));
+        }
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma16(av, bv[cb][i], acc[rb][cb]);
+        for (int cb = 0; cb < 4; ++cb) {
+          V8 bv;
+          if constexpr (WQ) {
+            const uint32_t word = i == 0 ? w.q[cb].x : i == 1 ? w.q[cb].y : i == 2 ? w.q[cb].z : w.q[cb].w;
+            bv = __builtin_bit_cast(V8, dequant_word(word, __builtin_bit_cast(_Float16, (uint16_t)w.s[cb])));
+          } else {
+            bv = __builtin_bit_cast(V8, w.d[cb][i]);
+          }
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16(av[rb], bv, acc[rb][cb]);
         }
       }
     };
@@ -250,9 +255,7 @@ hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
       hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 1>), dim3(grid), dim3(256), 0, s, a); \
   } while (0)
   if (xdt == MOE_F16 && wdt == MOE_Q4B32) MOE_WIDE(WF16, 1);
-  else if (xdt == MOE_F16 && wdt == MOE_F16) MOE_WIDE(WF16, 0);
-  else if (xdt == MOE_BF16 && wdt == MOE_BF16) MOE_WIDE(WBF16, 0);
-  else return hipErrorInvalidValue;
+  else return hipErrorInvalidValue;   // 16-bit weights take the stream tile
 #undef MOE_WIDE
   return hipGetLastError();
 }
