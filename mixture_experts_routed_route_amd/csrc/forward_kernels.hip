@@ -247,10 +247,10 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, _Float16 s) {
 // [rows, K] matrix as fp16, k-block-major: [K / 32][rows][32], so that the
 // full tile reads one stage's rows as a single contiguous slab. blockIdx.y
 // picks one of up to three matrices (W_gate, W_up, W_down). A block takes
-// tiles of 64 rows x 4 blocks of 32 values (rows a multiple of 64, K of
-// 128): it reads each row's 64 bytes of nibbles as one run, decodes into LDS
-// in the output order, and writes the tile's four 4 KB runs 1 KB per store
-// instruction.
+// tiles of 64 rows x KB blocks of 32 values (KB = 8 when K is a multiple of
+// 256, so every row's nibbles come as one whole 128-byte line; else 4): it
+// decodes into LDS in the output order and writes the tile's KB 4 KB runs
+// 1 KB per store instruction.
 struct DequantSet {
   const uint8_t* q[3];
   const uint16_t* sc[3];
@@ -258,47 +258,68 @@ struct DequantSet {
   int rows[3], K[3];
 };
 
-__global__ __launch_bounds__(256) void dequant_fat_kernel(
-    DequantSet d, const int32_t* __restrict__ fat_list,
-    const int32_t* __restrict__ meta) {
-  __shared__ __attribute__((aligned(16))) char tile[4 * 64 * 64];   // [kb][row][32 fp16]
-  const int m = blockIdx.y;
+template <int KB>
+__device__ __forceinline__ void dequant_fat_tiles(const DequantSet& d, int m,
+                                                  const int32_t* fat_list,
+                                                  int nfat, char* tile) {
+  constexpr int TPR = 4;                          // threads per row
+  constexpr int BPT = KB / TPR;                   // 32-value blocks per thread
   const uint8_t* __restrict__ q = d.q[m];
   const uint16_t* __restrict__ sc = d.sc[m];
   _Float16* __restrict__ out = d.out[m];
   const int rows = d.rows[m], K = d.K[m];
-  const int nfat = meta[kMetaFat];
   const int kbs = K / 32;                         // 32-value blocks per row
-  const int rt = rows / 64, kt4 = kbs / 4;        // tiles per slot: rt x kt4
-  const int per_slot = rt * kt4;
+  const int rt = rows / 64, ktn = kbs / KB;       // tiles per slot: rt x ktn
+  const int per_slot = rt * ktn;
   const int total = nfat * per_slot;
   const int tid = threadIdx.x;
-  const int r = tid >> 2, qq = tid & 3;           // decode: row, block
+  const int r = tid >> 2, qq = tid & 3;           // decode: row, quarter of the tile's blocks
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int slot = w / per_slot;
     const int rem = w - slot * per_slot;
     const int kq = rem / rt;
-    const int kb0 = kq * 4;
+    const int kb0 = kq * KB;
     const int row0 = (rem - kq * rt) * 64;
     const size_t er = (size_t)fat_list[slot] * rows + row0 + r;
-    const uint4 qa = *reinterpret_cast<const uint4*>(q + er * (size_t)(K / 2) + (kb0 + qq) * 16);
-    const _Float16 sa = __builtin_bit_cast(_Float16, sc[er * (size_t)kbs + kb0 + qq]);
-    half8 ha[4];
-    dequant32(qa, sa, ha);
-    __syncthreads();   // the previous tile's stores have read the LDS tile
-    char* ta = tile + (qq * 64 + r) * 64;
+    uint4 qa[BPT];
+    _Float16 sa[BPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(ta + i * 16) = __builtin_bit_cast(uint4, ha[i]);
+    for (int b = 0; b < BPT; ++b) {
+      const int kb = kb0 + qq * BPT + b;
+      qa[b] = *reinterpret_cast<const uint4*>(q + er * (size_t)(K / 2) + kb * 16);
+      sa[b] = __builtin_bit_cast(_Float16, sc[er * (size_t)kbs + kb]);
+    }
+    __syncthreads();   // the previous tile's stores have read the LDS tile
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      half8 ha[4];
+      dequant32(qa[b], sa[b], ha);
+      char* ta = tile + ((qq * BPT + b) * 64 + r) * 64;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(ta + i * 16) = __builtin_bit_cast(uint4, ha[i]);
+    }
     __syncthreads();
-    // 1024 16-byte pieces; block kb's 64 rows are 4 KB contiguous
+    // KB x 256 16-byte pieces; block kb's 64 rows are 4 KB contiguous
     char* os = reinterpret_cast<char*>(out + (size_t)slot * rows * K);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < KB; ++it) {
       const uint4 v = *reinterpret_cast<const uint4*>(tile + (it * 256 + tid) * 16);
       *reinterpret_cast<uint4*>(os + ((size_t)(kb0 + it) * rows + row0) * 64 + tid * 16) = v;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void dequant_fat_kernel(
+    DequantSet d, const int32_t* __restrict__ fat_list,
+    const int32_t* __restrict__ meta) {
+  __shared__ __attribute__((aligned(16))) char tile[8 * 64 * 64];   // [kb][row][32 fp16]
+  const int m = blockIdx.y;
+  const int nfat = meta[kMetaFat];
+  if (d.K[m] % 256 == 0)
+    dequant_fat_tiles<8>(d, m, fat_list, nfat, tile);
+  else
+    dequant_fat_tiles<4>(d, m, fat_list, nfat, tile);
 }
 
 __global__ __launch_bounds__(256) void dequant_rows_kernel(
