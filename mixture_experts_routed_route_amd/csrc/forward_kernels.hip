@@ -883,14 +883,28 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int t = (int)(idx / per_row);
   const int d = (int)(idx - (size_t)t * per_row) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int p = tok2pair[(size_t)t * k + j];
-    if (p < 0) continue;
-    const float w = topk_w[(size_t)t * k + j];
-    float v[8];
-    load_y8(ypair + (size_t)p * D + d, v);
+  // eight pairs at a time: their indices and weights, then all their rows,
+  // are in flight together; the sum still runs in j order
+  constexpr int kJ = 8;
+  for (int j0 = 0; j0 < k; j0 += kJ) {
+    int p[kJ];
+    float w[kJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i] * w;
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int j = j0 + jj;
+      p[jj] = j < k ? tok2pair[(size_t)t * k + j] : -1;
+      w[jj] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
+    }
+    float v[kJ][8];
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj)
+      if (p[jj] >= 0) load_y8(ypair + (size_t)p[jj] * D + d, v[jj]);
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj)
+      if (p[jj] >= 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[jj][i] * w[jj];
+      }
   }
   if (n_shared) {
     float v[8];
