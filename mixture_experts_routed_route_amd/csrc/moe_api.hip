@@ -45,7 +45,9 @@ inline int xbytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 struct PlanLayout {
   size_t ids, w, slot, tok2pair, hist, total, counts, offsets, pair_token,
       pair_w, stats, bytes;
-  int NC;
+  int NC;     // 64-token permute chunks
+  int NR;     // histogram rows (16 x tpw tokens each)
+  int tpw;    // route tokens per wave
 };
 
 bool desc_ok(const moe_plan_desc* d, std::string* why) {
@@ -77,13 +79,15 @@ PlanLayout plan_layout(const moe_plan_desc& d) {
   const size_t Tk = (size_t)d.T * d.k;
   const size_t P = Tk + (size_t)d.n_shared * d.T;
   L.NC = (d.T + kChunk - 1) / kChunk;
+  L.tpw = route_tpw(d.T);
+  L.NR = (d.T + 16 * L.tpw - 1) / (16 * L.tpw);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   L.ids = take(Tk * 4);
   L.w = take(Tk * 4);
   L.slot = take(Tk * 4);
   L.tok2pair = take(Tk * 4);
-  L.hist = take((size_t)L.NC * (d.E + 1) * 4);
+  L.hist = take((size_t)L.NR * (d.E + 1) * 4);
   L.total = take((size_t)(d.E + 1) * 4);
   L.counts = take((size_t)(d.E + 1) * 4);
   L.offsets = take((size_t)(d.E + 2) * 4);
@@ -325,16 +329,16 @@ moe_status moe_plan_create(const moe_plan_desc* desc, const float* logits,
   hipError_t e;
   if (L.NC > 0) {
     e = launch_route_hist(logits, d.T, d.E, d.k, (int32_t*)(b + L.ids),
-                          (float*)(b + L.w), (int32_t*)(b + L.hist), s);
+                          (float*)(b + L.w), (int32_t*)(b + L.hist), L.tpw, s);
     if (e != hipSuccess) return hip_fail(e, "route kernel");
   }
-  e = launch_scan((int32_t*)(b + L.hist), L.NC, d.T, d.E, d.k, d.n_shared,
+  e = launch_scan((int32_t*)(b + L.hist), L.NR, d.T, d.E, d.k, d.n_shared,
                   limit, (int32_t*)(b + L.total), (int32_t*)(b + L.counts),
                   (int32_t*)(b + L.offsets), (int64_t*)(b + L.stats), s);
   if (e != hipSuccess) return hip_fail(e, "scan kernel");
   if (L.NC > 0) {
     e = launch_permute((const int32_t*)(b + L.ids), (const float*)(b + L.w),
-                       (const int32_t*)(b + L.hist),
+                       (const int32_t*)(b + L.hist), 4 / L.tpw,
                        (const int32_t*)(b + L.offsets), d.T, d.E, d.k,
                        d.n_shared, limit, (int32_t*)(b + L.slot),
                        (int32_t*)(b + L.tok2pair), (int32_t*)(b + L.pair_token),

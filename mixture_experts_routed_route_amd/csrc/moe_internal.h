@@ -15,9 +15,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// Plan chunking: tokens per chunk of the capacity scan (one 64-bit mask per
-// expert and chunk gives the in-chunk stable rank by popcount).
+// Plan chunking: tokens per chunk of the permute (one 64-bit mask per
+// expert and chunk gives the in-chunk stable rank by popcount). The route
+// kernel writes one histogram row per 16 x tpw tokens (16 waves, tpw tokens
+// each): tpw = 4 (one row per chunk) for long prompts, 1 up to
+// kRouteShortT tokens, where a 64-token block would leave most CUs idle.
 constexpr int kChunk = 64;
+constexpr int kRouteShortT = 2048;
+inline int route_tpw(int T) { return T <= kRouteShortT ? 1 : 4; }
 constexpr int kMaxExperts = 1024;
 
 // Token rows per full-tile work item (the classify kernel's tile list).
@@ -46,17 +51,18 @@ enum Meta : int32_t { kMetaFullTiles = 0, kMetaSk1 = 1, kMetaSk4 = 2,
 
 // ---- launchers (plan_kernels.hip) ---------------------------------------
 hipError_t launch_route_hist(const float* logits, int T, int E, int k,
-                             int32_t* ids, float* w, int32_t* hist,
+                             int32_t* ids, float* w, int32_t* hist, int tpw,
                              hipStream_t s);
 hipError_t launch_scan(int32_t* hist, int NC, int T, int E, int k,
                        int n_shared, int64_t limit, int32_t* total,
                        int32_t* counts, int32_t* offsets, int64_t* stats,
                        hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, const float* w,
-                          const int32_t* base, const int32_t* offsets, int T,
-                          int E, int k, int n_shared, int64_t limit,
-                          int32_t* slot, int32_t* tok2pair,
-                          int32_t* pair_token, float* pair_w, hipStream_t s);
+                          const int32_t* base, int rows_per_chunk,
+                          const int32_t* offsets, int T, int E, int k,
+                          int n_shared, int64_t limit, int32_t* slot,
+                          int32_t* tok2pair, int32_t* pair_token,
+                          float* pair_w, hipStream_t s);
 
 // ---- forward (forward_kernels.hip) --------------------------------------
 struct ClassifyArgs {

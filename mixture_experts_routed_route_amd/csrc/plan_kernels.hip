@@ -40,23 +40,23 @@ __device__ __forceinline__ int wave_count(bool pred) {
 // chosen, so equal logits resolve to the lower expert index. A chosen
 // expert's position j is the number of chosen experts ranked above it.
 // Weights: exp(l_j - l_0) / sum_i exp(l_i - l_0) in double, rounded to f32.
-// Block = 16 waves x 4 tokens = one 64-token chunk; the block's histogram
-// row hist[chunk, 0..E-1] counts the chunk's choices per expert, and
-// hist[chunk, E] its NaN logits.
-template <int PER>
+// Block = 16 waves x TPW tokens; the block's histogram row
+// hist[block, 0..E-1] counts its tokens' choices per expert, and
+// hist[block, E] their NaN logits.
+template <int PER, int TPW>
 __global__ __launch_bounds__(1024) void route_hist_kernel(
     const float* __restrict__ logits, int T, int E, int k,
     int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ hist) {
   extern __shared__ int32_t sh_hist[];   // E + 1
-  constexpr int kTokPerWave = kChunk / 16;
+  constexpr int kTokPerWave = TPW;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x;
   for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_hist[e] = 0;
   __syncthreads();
 
-  const int tbase = chunk * kChunk + wave * kTokPerWave;
+  const int tbase = chunk * 16 * TPW + wave * kTokPerWave;
   // every logit this wave needs, loaded up front
   float lv[kTokPerWave][PER];
 #pragma unroll
@@ -172,14 +172,21 @@ __global__ __launch_bounds__(1024) void route_hist_kernel(
 }
 
 hipError_t launch_route_hist(const float* logits, int T, int E, int k,
-                             int32_t* ids, float* w, int32_t* hist,
+                             int32_t* ids, float* w, int32_t* hist, int tpw,
                              hipStream_t s) {
-  const int NC = (T + kChunk - 1) / kChunk;
+  if (tpw != 1 && tpw != 4) return hipErrorInvalidValue;
+  const int NR = (T + 16 * tpw - 1) / (16 * tpw);
   const size_t sh = (size_t)(E + 1) * sizeof(int32_t);
   const int per = (E + 63) / 64;
-#define MOE_ROUTE(P)                                                        \
-  hipLaunchKernelGGL(route_hist_kernel<P>, dim3(NC), dim3(1024), sh, s,    \
-                     logits, T, E, k, ids, w, hist)
+#define MOE_ROUTE(P)                                                             \
+  do {                                                                           \
+    if (tpw == 1)                                                                \
+      hipLaunchKernelGGL((route_hist_kernel<P, 1>), dim3(NR), dim3(1024), sh, s, \
+                         logits, T, E, k, ids, w, hist);                         \
+    else                                                                         \
+      hipLaunchKernelGGL((route_hist_kernel<P, 4>), dim3(NR), dim3(1024), sh, s, \
+                         logits, T, E, k, ids, w, hist);                         \
+  } while (0)
   if (per <= 1) MOE_ROUTE(1);
   else if (per <= 2) MOE_ROUTE(2);
   else if (per <= 4) MOE_ROUTE(4);
@@ -322,10 +329,13 @@ hipError_t launch_scan(int32_t* hist, int NC, int T, int E, int k,
 // One block per 64-token chunk. mask[e] has bit i set when the chunk's token
 // i chose expert e; a pair's rank among the chunk's earlier tokens for the
 // same expert is the popcount of the mask below its bit, so
-// slot = base[chunk, e] + rank counts every earlier token in the prompt.
+// slot = base[chunk's first histogram row, e] + rank counts every earlier
+// token in the prompt (the scanned row holds the counts of all tokens before
+// it; a chunk spans rows_per_chunk rows).
 __global__ __launch_bounds__(256) void permute_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ w,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ base, int rows_per_chunk,
+    const int32_t* __restrict__ offsets,
     int T, int E, int k, int n_shared, int64_t limit,
     int32_t* __restrict__ slot, int32_t* __restrict__ tok2pair,
     int32_t* __restrict__ pair_token, float* __restrict__ pair_w) {
@@ -349,7 +359,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
     const int e = ids[gp];
     const unsigned long long below = (1ull << tl) - 1ull;
     const int rank = __popcll(mask[e] & below);
-    const int sl = base[(size_t)chunk * (E + 1) + e] + rank;
+    const int sl = base[(size_t)chunk * rows_per_chunk * (E + 1) + e] + rank;
     slot[gp] = sl;
     const bool keep = limit < 0 || (int64_t)sl < limit;
     const int pos = keep ? offsets[e] + sl : -1;
@@ -369,15 +379,16 @@ __global__ __launch_bounds__(256) void permute_kernel(
 }
 
 hipError_t launch_permute(const int32_t* ids, const float* w,
-                          const int32_t* base, const int32_t* offsets, int T,
-                          int E, int k, int n_shared, int64_t limit,
-                          int32_t* slot, int32_t* tok2pair,
-                          int32_t* pair_token, float* pair_w, hipStream_t s) {
+                          const int32_t* base, int rows_per_chunk,
+                          const int32_t* offsets, int T, int E, int k,
+                          int n_shared, int64_t limit, int32_t* slot,
+                          int32_t* tok2pair, int32_t* pair_token,
+                          float* pair_w, hipStream_t s) {
   const int NC = (T + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(permute_kernel, dim3(NC), dim3(256),
                      (size_t)E * sizeof(unsigned long long), s, ids, w, base,
-                     offsets, T, E, k, n_shared, limit, slot, tok2pair,
-                     pair_token, pair_w);
+                     rows_per_chunk, offsets, T, E, k, n_shared, limit, slot,
+                     tok2pair, pair_token, pair_w);
   return hipGetLastError();
 }
 
