@@ -11,7 +11,8 @@ steps between two device synchronisations.
 Default workload: the 13,312-token prompt over 256 4-bit experts
 (d_model 4096, expert d_ff 2048, top-8, Zipf(1.1) popularity), the size at
 which the dequant-once FP16 route of Strata PR #4366 was measured.
-``--config N`` selects another named workload (1..5).
+``--config N`` selects another named workload (1..7; 6 and 7 are
+decode-shaped calls of 1..8 tokens, ``--T``).
 
 Prints one JSON line: the metric (routed-expert TFLOP/s, 6 D F flops per
 kept pair), pairs/s, the dominant kernel's roofline (HIP events around its
@@ -199,6 +200,14 @@ def main():
     flops = W.flops_per_pair(D, F) * kept_pairs
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     pairs_s = kept_pairs / (ms_per_step * 1e-3)
+    # the weights of every expert holding a kept pair are read at least once
+    touched = int((counts > 0).sum())
+    wbytes_step = touched * W.weight_bytes_per_expert(D, F, wl["w_dtype"])
+    weight_stream = {"touched_experts": touched,
+                     "bytes_per_step": int(wbytes_step),
+                     "GB_per_s": round(wbytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(wbytes_step / (ms_per_step * 1e-3)
+                                               / 1e9 / PEAK_HBM_GBS, 4)}
 
     # routes per expert (the library's rule, restated for accounting)
     fat_rows = opts.fat_rows if wl["w_dtype"] == "q4b32" else 0
@@ -279,6 +288,7 @@ def main():
                    "capacity_factor": wl["capacity_factor"],
                    "parallelism": "single GPU"},
         "pairs_per_s": round(pairs_s, 1),
+        "weight_stream": weight_stream,
         "kept_pairs": kept_pairs,
         "drop_fraction": st["drop_fraction"],
         "routes": {"full_or_fat_experts": int(full_mask.sum()),

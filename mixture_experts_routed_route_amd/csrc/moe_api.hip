@@ -79,7 +79,7 @@ PlanLayout plan_layout(const moe_plan_desc& d) {
   const size_t Tk = (size_t)d.T * d.k;
   const size_t P = Tk + (size_t)d.n_shared * d.T;
   L.NC = (d.T + kChunk - 1) / kChunk;
-  L.tpw = route_tpw(d.T);
+  L.tpw = route_tpw(d.T, d.E);
   L.NR = (d.T + 16 * L.tpw - 1) / (16 * L.tpw);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -327,6 +327,17 @@ moe_status moe_plan_create(const moe_plan_desc* desc, const float* logits,
   const moe_plan_desc& d = *desc;
   const int64_t limit = capacity_limit(d);
   hipError_t e;
+  if (d.T >= 1 && d.T <= kChunk && (int64_t)d.T * d.k <= kPlanSmallPairs &&
+      d.E <= kPlanSmallE) {
+    // one chunk: route, scan and permute in one block
+    e = launch_plan_small(logits, d.T, d.E, d.k, d.n_shared, limit,
+                          (int32_t*)(b + L.ids), (float*)(b + L.w),
+                          (int32_t*)(b + L.total), (int32_t*)(b + L.counts),
+                          (int32_t*)(b + L.offsets), (int64_t*)(b + L.stats),
+                          (int32_t*)(b + L.slot), (int32_t*)(b + L.tok2pair),
+                          (int32_t*)(b + L.pair_token), (float*)(b + L.pair_w), s);
+    if (e != hipSuccess) return hip_fail(e, "plan kernel");
+  } else {
   if (L.NC > 0) {
     e = launch_route_hist(logits, d.T, d.E, d.k, (int32_t*)(b + L.ids),
                           (float*)(b + L.w), (int32_t*)(b + L.hist), L.tpw, s);
@@ -344,6 +355,7 @@ moe_status moe_plan_create(const moe_plan_desc* desc, const float* logits,
                        (int32_t*)(b + L.tok2pair), (int32_t*)(b + L.pair_token),
                        (float*)(b + L.pair_w), s);
     if (e != hipSuccess) return hip_fail(e, "permute kernel");
+  }
   }
   moe_plan* p = new (std::nothrow) moe_plan;
   if (!p) return fail(MOE_EINVAL, "out of host memory");
@@ -498,7 +510,18 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     e = launch_classify(ca, s);
     if (e != hipSuccess) return hip_fail(e, "classify kernel");
   }
-  if (L.can_fat) {
+  // Routes that this prompt cannot use are not launched: an expert holds at
+  // most T pairs (a token picks k distinct experts; the shared expert takes
+  // every token), so with T <= S no expert leaves the split-K side, with
+  // T < fat_rows none is fat, and with T <= 16 every split-K group is one
+  // group of <= 16 rows (decode-shaped calls).
+  const int64_t row_bound = d.T;
+  const bool run_fat = L.can_fat && row_bound >= L.fat_rows;
+  const bool run_full = L.can_full &&
+      (wdt == MOE_Q4B32 ? run_fat : (double)row_bound > (double)o.splitk_max_pairs);
+  const bool run_sk1 = L.can_sk1;
+  const bool run_sk4 = L.can_sk4 && row_bound > 16;
+  if (run_fat) {
     PhaseScope ps(rec, 1, s);
     const int grid = info.ncu * 8;
     // one launch for the three matrices
@@ -543,7 +566,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       g.B1 = nullptr; g.B1s = nullptr;
       g.S0 = b + L.stg_d; g.S1 = nullptr;
     }
-    if (L.can_full) {
+    if (run_full) {
       PhaseScope ps(rec, stage == 0 ? 2 : 4, s);
       const int nnb = stage == 0 ? F / 128 : (D + 255) / 256;
       GemmArgs gf = g;
@@ -569,7 +592,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
         g.part = (float*)(b + L.part);
       }
       const int stream_grid = std::min(info.ncu, kStreamMaxRuns);
-      if (L.can_sk1) {
+      if (run_sk1) {
         // groups of <= 16 rows
         g.list = (const int32_t*)(b + L.sk1);
         g.meta_index = kMetaSk1;
@@ -582,7 +605,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
         }
         if (e != hipSuccess) return hip_fail(e, "split-K kernel");
       }
-      if (L.can_sk4) {
+      if (run_sk4) {
         // groups of 17..64 rows
         g.list = (const int32_t*)(b + L.sk4);
         g.meta_index = kMetaSk4;

@@ -18,11 +18,18 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // Plan chunking: tokens per chunk of the permute (one 64-bit mask per
 // expert and chunk gives the in-chunk stable rank by popcount). The route
 // kernel writes one histogram row per 16 x tpw tokens (16 waves, tpw tokens
-// each): tpw = 4 (one row per chunk) for long prompts, 1 up to
-// kRouteShortT tokens, where a 64-token block would leave most CUs idle.
+// each): tpw = 4 (one row per chunk) for long prompts over at most 256
+// experts, else 1 (up to kRouteShortT tokens a 64-token block would leave
+// most CUs idle; above 256 experts four tokens' logits do not fit a lane's
+// registers).
 constexpr int kChunk = 64;
 constexpr int kRouteShortT = 2048;
-inline int route_tpw(int T) { return T <= kRouteShortT ? 1 : 4; }
+inline int route_tpw(int T, int E) { return (T <= kRouteShortT || E > 256) ? 1 : 4; }
+// The single-block plan kernel takes prompts of at most kChunk tokens and
+// kPlanSmallPairs (token, choice) pairs, held in LDS, over at most 256
+// experts.
+constexpr int kPlanSmallPairs = 4096;
+constexpr int kPlanSmallE = 256;
 constexpr int kMaxExperts = 1024;
 
 // Token rows per full-tile work item (the classify kernel's tile list).
@@ -63,6 +70,13 @@ hipError_t launch_permute(const int32_t* ids, const float* w,
                           int n_shared, int64_t limit, int32_t* slot,
                           int32_t* tok2pair, int32_t* pair_token,
                           float* pair_w, hipStream_t s);
+
+hipError_t launch_plan_small(const float* logits, int T, int E, int k,
+                             int n_shared, int64_t limit, int32_t* ids,
+                             float* w, int32_t* total, int32_t* counts,
+                             int32_t* offsets, int64_t* stats, int32_t* slot,
+                             int32_t* tok2pair, int32_t* pair_token,
+                             float* pair_w, hipStream_t s);
 
 // ---- forward (forward_kernels.hip) --------------------------------------
 struct ClassifyArgs {

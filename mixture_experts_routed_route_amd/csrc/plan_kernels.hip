@@ -33,13 +33,97 @@ __device__ __forceinline__ int wave_count(bool pred) {
 }
 
 // One wavefront per token; PER = ceil(E / 64) logits per lane (expert
-// lane + 64 p). The k-th largest order key tau is built bit by bit from the
-// top (a candidate stays if at least k keys reach it): 32 steps of
-// compare + ballot + popcount, no data exchange between lanes. Keys above
-// tau are chosen, then keys equal to tau in expert order until k are
-// chosen, so equal logits resolve to the lower expert index. A chosen
-// expert's position j is the number of chosen experts ranked above it.
-// Weights: exp(l_j - l_0) / sum_i exp(l_i - l_0) in double, rounded to f32.
+// lane + 64 p). Selection: k rounds of a wave-wide arg-max over the order
+// keys, ties to the lower expert index, so round j yields the expert of
+// rank j (its position in the token's top-k list) and round 0 the largest
+// logit l_0. Lane j % 64 keeps round j's expert and key in slot j / 64.
+// Weights: exp(l_j - l_0) / sum_i exp(l_i - l_0) in double (the sum in rank
+// order), rounded to f32.
+// The TPW tokens from tbase of one wave: their top-k ids and weights into
+// ids / w, one count per chosen expert into sh_hist (LDS); returns the
+// wave's NaN logits (the same value in every lane).
+template <int PER, int TPW>
+__device__ __forceinline__ int route_wave_tokens(
+    const float* __restrict__ logits, int T, int E, int k, int tbase,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sh_hist) {
+  const int lane = threadIdx.x & 63;
+  int nan_count = 0;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = tbase + i;
+    if (t >= T) break;   // wave-uniform
+    uint32_t key[PER];
+    bool valid[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = lane + 64 * p;
+      valid[p] = e < E;
+      const float l = valid[p] ? logits[(size_t)t * E + e] : 0.f;
+      key[p] = order_key(l);
+      nan_count += (valid[p] && l != l) ? 1 : 0;
+    }
+    bool sel[PER];
+    uint32_t my_key[PER];
+    int my_e[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) { sel[p] = false; my_key[p] = 0u; my_e[p] = 0; }
+    uint32_t top = 0u;
+    for (int jr = 0; jr < k; ++jr) {
+      // candidate: key << 32 | (2^32 - 1 - e); 0 means none
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const uint64_t v = ((uint64_t)key[p] << 32) |
+                           (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * p));
+        if (valid[p] && !sel[p] && v > best) best = v;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)best, off);
+        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        best = o > best ? o : best;
+      }
+      const int ew = (int)(0xFFFFFFFFu - (uint32_t)best);   // wave-uniform
+      const uint32_t kw = (uint32_t)(best >> 32);
+      if (jr == 0) top = kw;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        if (lane + 64 * p == ew) sel[p] = true;
+        if ((jr >> 6) == p && lane == (jr & 63)) { my_key[p] = kw; my_e[p] = ew; }
+      }
+    }
+    const double l0 = (double)key_value(top);
+    double ex[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      ex[p] = (64 * p + lane < k) ? exp((double)key_value(my_key[p]) - l0) : 0.0;
+    // the sum in rank order, the same in every lane
+    double sum = 0.0;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const uint64_t bits = (uint64_t)__double_as_longlong(ex[p]);
+      for (int l = 0; l < 64 && 64 * p + l < k; ++l) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, l);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), l);
+        sum += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int jr = 64 * p + lane;
+      if (jr < k) {
+        ids[(size_t)t * k + jr] = my_e[p];
+        w[(size_t)t * k + jr] = (float)(ex[p] / sum);
+        atomicAdd(&sh_hist[my_e[p]], 1);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) nan_count += __shfl_xor(nan_count, off);
+  return nan_count;
+}
+
 // Block = 16 waves x TPW tokens; the block's histogram row
 // hist[block, 0..E-1] counts its tokens' choices per expert, and
 // hist[block, E] their NaN logits.
@@ -49,122 +133,13 @@ __global__ __launch_bounds__(1024) void route_hist_kernel(
     int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ hist) {
   extern __shared__ int32_t sh_hist[];   // E + 1
-  constexpr int kTokPerWave = TPW;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x;
   for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_hist[e] = 0;
   __syncthreads();
-
-  const int tbase = chunk * 16 * TPW + wave * kTokPerWave;
-  // every logit this wave needs, loaded up front
-  float lv[kTokPerWave][PER];
-#pragma unroll
-  for (int i = 0; i < kTokPerWave; ++i) {
-    const int t = tbase + i;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int e = lane + 64 * p;
-      lv[i][p] = (t < T && e < E) ? logits[(size_t)t * E + e] : 0.f;
-    }
-  }
-  // keys of the wave's tokens (a token past T has no valid expert: it
-  // chooses nothing and writes nothing)
-  uint32_t key[kTokPerWave][PER];
-  bool valid[kTokPerWave][PER];
-  int nan_count = 0;
-#pragma unroll
-  for (int i = 0; i < kTokPerWave; ++i)
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      valid[i][p] = tbase + i < T && lane + 64 * p < E;
-      key[i][p] = order_key(lv[i][p]);
-      nan_count += (valid[i][p] && lv[i][p] != lv[i][p]) ? 1 : 0;
-    }
-  // tau: the k-th largest key of each token, the tokens side by side
-  uint32_t tau[kTokPerWave];
-#pragma unroll
-  for (int i = 0; i < kTokPerWave; ++i) tau[i] = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-#pragma unroll
-    for (int i = 0; i < kTokPerWave; ++i) {
-      const uint32_t test = tau[i] | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int p = 0; p < PER; ++p) cnt += wave_count(valid[i][p] && key[i][p] >= test);
-      if (cnt >= k) tau[i] = test;
-    }
-  }
-  const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-  for (int i = 0; i < kTokPerWave; ++i) {
-    const int t = tbase + i;
-    int above = 0;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) above += wave_count(valid[i][p] && key[i][p] > tau[i]);
-    // ties at tau: the first (k - above) in expert order
-    int ties_before = 0;
-    bool sel[PER];
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const bool eqp = valid[i][p] && key[i][p] == tau[i];
-      const uint64_t eq = __ballot(eqp);
-      const int r = ties_before + __popcll(eq & lanes_below);
-      sel[p] = valid[i][p] && (key[i][p] > tau[i] || (eqp && r < k - above));
-      ties_before += __popcll(eq);
-    }
-    // positions: chosen experts ranked above each chosen one; the largest
-    // chosen key is l_0's
-    int pos[PER];
-#pragma unroll
-    for (int p = 0; p < PER; ++p) pos[p] = 0;
-    uint32_t top = 0u;
-#pragma unroll
-    for (int pp = 0; pp < PER; ++pp) {
-      uint64_t m = __ballot(sel[pp]);
-      while (m) {
-        const int l = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const uint32_t ko = (uint32_t)__builtin_amdgcn_readlane((int)key[i][pp], l);
-        const int eo = l + 64 * pp;
-        top = ko > top ? ko : top;
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-          const int e = lane + 64 * p;
-          pos[p] += (sel[p] && (ko > key[i][p] || (ko == key[i][p] && eo < e))) ? 1 : 0;
-        }
-      }
-    }
-    const double l0 = (double)key_value(top);
-    double ex[PER];
-#pragma unroll
-    for (int p = 0; p < PER; ++p) ex[p] = sel[p] ? exp((double)lv[i][p] - l0) : 0.0;
-    // the sum in expert order, the same in every lane
-    double sum = 0.0;
-#pragma unroll
-    for (int pp = 0; pp < PER; ++pp) {
-      uint64_t m = __ballot(sel[pp]);
-      while (m) {
-        const int l = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const uint64_t bits = (uint64_t)__double_as_longlong(ex[pp]);
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, l);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), l);
-        sum += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      if (sel[p]) {
-        const int e = lane + 64 * p;
-        ids[(size_t)t * k + pos[p]] = e;
-        w[(size_t)t * k + pos[p]] = (float)(ex[p] / sum);
-        atomicAdd(&sh_hist[e], 1);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) nan_count += __shfl_xor(nan_count, off);
+  const int tbase = chunk * 16 * TPW + wave * TPW;
+  const int nan_count = route_wave_tokens<PER, TPW>(logits, T, E, k, tbase, ids, w, sh_hist);
   if (lane == 0 && nan_count) atomicAdd(&sh_hist[E], nan_count);
   __syncthreads();
   for (int e = threadIdx.x; e <= E; e += blockDim.x)
@@ -178,20 +153,15 @@ hipError_t launch_route_hist(const float* logits, int T, int E, int k,
   const int NR = (T + 16 * tpw - 1) / (16 * tpw);
   const size_t sh = (size_t)(E + 1) * sizeof(int32_t);
   const int per = (E + 63) / 64;
-#define MOE_ROUTE(P)                                                             \
-  do {                                                                           \
-    if (tpw == 1)                                                                \
-      hipLaunchKernelGGL((route_hist_kernel<P, 1>), dim3(NR), dim3(1024), sh, s, \
-                         logits, T, E, k, ids, w, hist);                         \
-    else                                                                         \
-      hipLaunchKernelGGL((route_hist_kernel<P, 4>), dim3(NR), dim3(1024), sh, s, \
-                         logits, T, E, k, ids, w, hist);                         \
-  } while (0)
-  if (per <= 1) MOE_ROUTE(1);
-  else if (per <= 2) MOE_ROUTE(2);
-  else if (per <= 4) MOE_ROUTE(4);
-  else if (per <= 8) MOE_ROUTE(8);
-  else MOE_ROUTE(16);
+#define MOE_ROUTE(P, TPW)                                                          \
+  hipLaunchKernelGGL((route_hist_kernel<P, TPW>), dim3(NR), dim3(1024), sh, s,     \
+                     logits, T, E, k, ids, w, hist)
+  if (tpw == 4 && per > 4) return hipErrorInvalidValue;
+  if (per <= 1) { if (tpw == 1) MOE_ROUTE(1, 1); else MOE_ROUTE(1, 4); }
+  else if (per <= 2) { if (tpw == 1) MOE_ROUTE(2, 1); else MOE_ROUTE(2, 4); }
+  else if (per <= 4) { if (tpw == 1) MOE_ROUTE(4, 1); else MOE_ROUTE(4, 4); }
+  else if (per <= 8) MOE_ROUTE(8, 1);
+  else MOE_ROUTE(16, 1);
 #undef MOE_ROUTE
   return hipGetLastError();
 }
@@ -376,6 +346,137 @@ __global__ __launch_bounds__(256) void permute_kernel(
       pair_w[sbase + t0 + tl] = 1.0f;
     }
   }
+}
+
+// The whole plan of a prompt of at most 64 tokens (one permute chunk) in
+// one block: route into LDS, then the counts, offsets and statistics of the
+// scan kernel for a single histogram row (every base is zero), then the
+// permute of that chunk. Same arithmetic and order as the three kernels;
+// one launch instead of three for decode-shaped and short prompts.
+template <int PER>
+__global__ __launch_bounds__(1024) void plan_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int n_shared,
+    int64_t limit, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ total, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int64_t* __restrict__ stats,
+    int32_t* __restrict__ slot, int32_t* __restrict__ tok2pair,
+    int32_t* __restrict__ pair_token, float* __restrict__ pair_w) {
+  __shared__ int32_t sh_hist[kMaxExperts + 1];
+  __shared__ int32_t sh_off[kMaxExperts + 2];
+  __shared__ unsigned long long mask[kMaxExperts];
+  __shared__ int32_t sh_ids[kPlanSmallPairs];
+  __shared__ float sh_w[kPlanSmallPairs];
+  __shared__ int sh_waves[16];
+  __shared__ int red[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_hist[e] = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
+  if (threadIdx.x < 4) red[threadIdx.x] = 0;
+  __syncthreads();
+  // route: 16 waves x 4 tokens
+  const int nan_count = route_wave_tokens<PER, 4>(logits, T, E, k, wave * 4, sh_ids, sh_w, sh_hist);
+  if (lane == 0 && nan_count) atomicAdd(&sh_hist[E], nan_count);
+  __syncthreads();
+  const int np = T * k;
+  for (int p = threadIdx.x; p < np; p += blockDim.x) {
+    ids[p] = sh_ids[p];
+    w[p] = sh_w[p];
+  }
+  // counts, offsets and statistics
+  int kept_local = 0, touched_local = 0, max_local = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int tot = sh_hist[e];
+    total[e] = tot;
+    const int c = (limit < 0 || (int64_t)tot < limit) ? tot : (int)limit;
+    counts[e] = c;
+    kept_local += c;
+    touched_local += c > 0 ? 1 : 0;
+    max_local = max(max_local, c);
+  }
+  if (kept_local) atomicAdd(&red[0], kept_local);
+  if (touched_local) atomicAdd(&red[1], touched_local);
+  if (max_local) atomicMax(&red[2], max_local);
+  if (n_shared && threadIdx.x == 0) counts[E] = T;
+  const int n = E + n_shared;
+  int carry = 0;
+  for (int b = 0; b < n; b += blockDim.x) {
+    const int e = b + threadIdx.x;
+    int c = 0;
+    if (e < E) {
+      const int tot = sh_hist[e];
+      c = (limit < 0 || (int64_t)tot < limit) ? tot : (int)limit;
+    } else if (e < n) {
+      c = T;
+    }
+    int blk_total = 0;
+    const int pre = block_scan_excl(c, &blk_total, sh_waves);
+    if (e < n) {
+      offsets[e] = carry + pre;
+      sh_off[e] = carry + pre;
+    }
+    carry += blk_total;
+  }
+  if (threadIdx.x == 0) {
+    offsets[n] = carry;
+    sh_off[n] = carry;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    stats[0] = (int64_t)T * k - red[0];   // dropped
+    stats[1] = red[0];                    // kept
+    stats[2] = sh_hist[E];                // NaN logits
+    stats[3] = red[1];                    // touched experts
+    stats[4] = red[2];                    // max rows
+    stats[5] = 0;
+    stats[6] = 0;
+    stats[7] = 0;
+  }
+  // permute of the single chunk: slot = rank among earlier tokens
+  for (int p = threadIdx.x; p < np; p += blockDim.x)
+    atomicOr(&mask[sh_ids[p]], 1ull << (p / k));
+  __syncthreads();
+  for (int p = threadIdx.x; p < np; p += blockDim.x) {
+    const int tl = p / k;
+    const int e = sh_ids[p];
+    const unsigned long long below = (1ull << tl) - 1ull;
+    const int sl = __popcll(mask[e] & below);
+    slot[p] = sl;
+    const bool keep = limit < 0 || (int64_t)sl < limit;
+    const int pos = keep ? sh_off[e] + sl : -1;
+    tok2pair[p] = pos;
+    if (keep) {
+      pair_token[pos] = tl;
+      pair_w[pos] = sh_w[p];
+    }
+  }
+  if (n_shared) {
+    const int sbase = sh_off[E];
+    for (int tl = threadIdx.x; tl < T; tl += blockDim.x) {
+      pair_token[sbase + tl] = tl;
+      pair_w[sbase + tl] = 1.0f;
+    }
+  }
+}
+
+hipError_t launch_plan_small(const float* logits, int T, int E, int k,
+                             int n_shared, int64_t limit, int32_t* ids,
+                             float* w, int32_t* total, int32_t* counts,
+                             int32_t* offsets, int64_t* stats, int32_t* slot,
+                             int32_t* tok2pair, int32_t* pair_token,
+                             float* pair_w, hipStream_t s) {
+  if (T < 1 || T > kChunk || (int64_t)T * k > kPlanSmallPairs || E > kPlanSmallE)
+    return hipErrorInvalidValue;
+  const int per = (E + 63) / 64;
+#define MOE_PLAN_SMALL(P)                                                        \
+  hipLaunchKernelGGL((plan_small_kernel<P>), dim3(1), dim3(1024), 0, s, logits, T, \
+                     E, k, n_shared, limit, ids, w, total, counts, offsets,     \
+                     stats, slot, tok2pair, pair_token, pair_w)
+  if (per <= 1) MOE_PLAN_SMALL(1);
+  else if (per <= 2) MOE_PLAN_SMALL(2);
+  else MOE_PLAN_SMALL(4);
+#undef MOE_PLAN_SMALL
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, const float* w,

@@ -63,6 +63,17 @@ def test_short_prompt_shared(T):
     check_layer(wl, y, sample_tokens(T, 64, seed=T))
 
 
+@pytest.mark.parametrize("cfg,T", [(6, 1), (6, 2), (6, 4), (6, 8), (7, 1), (7, 8)])
+def test_decode_shapes(cfg, T):
+    # decode-shaped calls: k distinct experts per token, every touched
+    # expert thin (one 16-row group), the shared expert too for cfg 6
+    wl = W.config(cfg, T=T)
+    say(f"layer {wl['name']}")
+    p, y = gpu_layer(wl)
+    check_plan(wl, p)
+    check_layer(wl, y)
+
+
 @pytest.mark.parametrize("exact", [False, True])
 def test_underfilled_full_route(exact):
     # the shared expert (250 rows) and a few experts of 17..256 rows: their

@@ -40,6 +40,8 @@ CONFIG_NAMES = {
     3: "prefill_zipf",
     4: "long_prompt_q4",
     5: "short_prompt_shared",
+    6: "decode_shared",
+    7: "decode_q4",
 }
 
 
@@ -159,6 +161,8 @@ def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
       bf16; T in {33, 64, 128, 186} with N(0,1) logits, or, given
       ``pairs_per_expert`` p, T = 16p with round-robin logits so every
       routed expert holds exactly p pairs.
+    6 decode on the layer of 5: T in 1..8 (default 1), N(0,1) logits.
+    7 decode on the layer of 4: T in 1..8 (default 1), Zipf(1.1) bias.
     """
     if n == 1:
         return make_layer(64, 128, 256, 8, 2, F32, seed=seed,
@@ -199,6 +203,22 @@ def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
         return make_layer(T5, 2048, 768, 128, 8, BF16, n_shared=1,
                           bf16_logits=True, seed=seed,
                           name=f"{CONFIG_NAMES[5]}_T{T5}",
+                          with_weights=with_weights)
+    if n == 6:
+        # decode-shaped calls on the short-prompt layer: T in 1..8 tokens
+        T6 = 1 if T is None else int(T)
+        return make_layer(T6, 2048, 768, 128, 8, BF16, n_shared=1,
+                          bf16_logits=True, seed=seed,
+                          name=f"{CONFIG_NAMES[6]}_T{T6}",
+                          with_weights=with_weights)
+    if n == 7:
+        # decode-shaped calls on the 4-bit layer: T in 1..8 tokens
+        T7 = 1 if T is None else int(T)
+        g = _gen(seed + 1000)
+        bias = zipf_bias(256, 1.1, g)
+        return make_layer(T7, 4096, 2048, 256, 8, F16, w_dtype=Q4B32,
+                          logit_bias=bias, seed=seed,
+                          name=f"{CONFIG_NAMES[7]}_T{T7}",
                           with_weights=with_weights)
     raise ValueError(f"no workload {n}")
 
