@@ -1,12 +1,16 @@
 // Full MFMA tile of the routed MoE layer on gfx950 (experts holding many
 // rows, and the dequantised-once fp16 copies of 4-bit fat experts).
 //
-// One block = 4 waves computes a 256 (weight rows) x 256 (token rows) tile.
-// K streams through a ring of four 32 KB LDS stages (32 K values each) that
-// buffer_load ... lds fills directly (no register staging): every wave issues
-// eight 1 KB loads per stage, three stages run ahead of the MFMAs, and each
-// lane picks the global 16-byte chunk that lands in the XOR-swizzled LDS slot
-// the MFMA operand reads expect. Waits are explicit counted vmcnt waits plus
+// One block = 8 waves (two per SIMD) computes a 256 (weight rows) x 256
+// (token rows) tile; each wave owns 128 weight rows x 64 token rows (128
+// accumulator registers). K streams through a ring of four 32 KB LDS stages
+// (32 K values each) that buffer_load ... lds fills directly (no register
+// staging): every wave issues four 1 KB loads per stage, three stages run
+// ahead of the MFMAs, and each lane picks the global 16-byte chunk that lands
+// in the XOR-swizzled LDS slot the MFMA operand reads expect. Eight issuing
+// waves keep more of these loads in flight per CU than four (a CU's LDS-DMA
+// stream runs about a third faster), and the second wave on a SIMD issues
+// MFMAs while the first waits. Waits are explicit counted vmcnt waits plus
 // s_barrier, and LDS loads and fragment reads are interleaved with the MFMA
 // stream (sched_group_barrier) so the matrix pipe is not left idle.
 //
@@ -51,17 +55,20 @@ constexpr int kNS = 4;     // LDS stages (kNS - 1 in flight)
 constexpr int kRowB = kBK * 2;
 constexpr int kStage = 512 * kRowB;   // 256 weight + 256 token rows
 constexpr int kGM = 4;     // row tiles per schedule group
-constexpr int kDmaPerWave = 8;        // 1 KB blocks per wave per stage
+constexpr int kWaves = 8;
+constexpr int kDmaPerWave = 32 / kWaves;   // 1 KB blocks per wave per stage
+constexpr int kDmaEarly = kDmaPerWave / 2;  // of them issued before mid-stage
 
 }  // namespace
 
 template <class TT, int MODE, int LO>
-__global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
+__global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   using S = typename TT::S;
   using V8 = typename TT::V8;
   using V4 = typename TT::V4;
   constexpr int BT = LO ? 128 : 256;       // token rows per pass
-  constexpr int TB = BT / 64;              // 32-row token blocks per wave
+  constexpr int TW = BT / 4;               // token rows per wave
+  constexpr int TB = TW / 32;              // 32-row token blocks per wave
   constexpr int NPASS = 256 / BT;          // passes over a 256-row tile
   __shared__ __attribute__((aligned(1024))) char smem[kNS * kStage];
 
@@ -69,7 +76,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
   const int lane = tid & 63;
   // wave index in a scalar register: descriptors and LDS bases stay uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ww = wave >> 1, wt = wave & 1;
+  const int ww = wave >> 2, wt = wave & 3;   // weight half, token quarter
   const int K = a.K, N = a.N;
   const int nk = K / kBK;
   const int NNB = MODE == 0 ? N / 128 : (N + kBW - 1) / kBW;
@@ -111,8 +118,10 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
     const bool tiled = slot >= 0;
     const uint32_t mat_bytes = (uint32_t)N * (uint32_t)K * 2u;
 
+    // waves 0..3 load the stage's 256 weight rows, waves 4..7 its token rows
+    const bool w_wave = wave < kWaves / 2;
     __amdgpu_buffer_rsrc_t r_even, r_odd;   // descriptors of this wave's blocks
-    if (wave < 2) {
+    if (w_wave) {
       const char* b0 = (const char*)(slot >= 0 ? a.S0 : a.B0);
       r_even = make_rsrc(b0 + eix * mat_bytes, mat_bytes);
       if (MODE == 0) {
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         r_odd = r_even;
       }
     } else {
-      r_even = make_rsrc((LO && wave == 3) ? a.A2 : a.A, a.a_bytes);
+      r_even = make_rsrc((LO && wave >= 6) ? a.A2 : a.A, a.a_bytes);   // 6, 7: lo rows
       r_odd = r_even;
     }
 
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;   // stage row
         const int c = (lane & 3) ^ ((R >> 2) & 3);
         uint32_t rowoff;
-        if (wave < 2) {
+        if (w_wave) {
           int row;
           if (MODE == 0)   // 32-row blocks alternate W_gate / W_up
             row = nb * 128 + (R >> 7) * 64 + ((R >> 6) & 1) * 32 + (R & 31);
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         voff[jj] = rowoff + (uint32_t)c * 16u;
       }
       // bytes from one stage's slice of a row to the next stage's
-      const int s_step = wave < 2 ? (tiled ? N * kRowB : kRowB)
+      const int s_step = w_wave ? (tiled ? N * kRowB : kRowB)
                                   : (MODE == 1 ? a.h_rows * kRowB : kRowB);
       // Refill of ring stage kt. Past the last stage the slice nk-1 is read
       // again (an L2 hit) into a buffer no one reads any more, so every
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-          const int r = wt * (BT / 2) + t * 32 + (lane & 31);
+          const int r = wt * TW + t * 32 + (lane & 31);
           f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
           if (LO)
             f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
         } else {
           const int j = idx - 4;
           const int t = LO ? j >> 1 : j;
-          const int r = wt * (BT / 2) + t * 32 + (lane & 31);
+          const int r = wt * TW + t * 32 + (lane & 31);
           if (LO && (j & 1))
             f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
           else
@@ -256,34 +265,41 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
       // leaves it idle: MFMA, LDS read, MFMA, ring refill, ...
       constexpr int kMf = 4 * TB * (LO ? 2 : 1);   // MFMAs per 16-deep step
       constexpr int kRd = 4 + TB * (LO ? 2 : 1);   // fragment reads per step
-      static_assert(kRd == kDmaPerWave, "one refill per fragment read");
+      static_assert(kRd >= kDmaPerWave && kMf >= kRd, "interleave shape");
       for (int kt = 0; kt < nk; ++kt) {
         // LDS writes of the refill and LDS reads keep source order (the
-        // compiler cannot tell them apart), so alternate them here
+        // compiler cannot tell them apart), so alternate them here. Half of
+        // the refill issues here, half after the mid-stage barrier: spread
+        // thin, a refill that waits for a free load slot holds up fewer MFMAs
 #pragma unroll
         for (int q = 0; q < kRd; ++q) {
-          issue_one(kt + kNS - 1, q);
+          if (q < kDmaEarly) issue_one(kt + kNS - 1, q);
           read_piece(kt, 1, q, f1);
         }
         mma(f0);
 #pragma unroll
-        for (int q = 0; q < kMf / 2; ++q) {
+        for (int q = 0; q < kMf; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          if (q < kRd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          if (q < kDmaEarly) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
           if (q < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
         __builtin_amdgcn_sched_barrier(0);
-        // step-1 reads done, stage kt+1 landed for this wave; after the
-        // barrier, for every wave (past the end: unread refill data)
-        wait_vm_lgkm0<(kNS - 2) * kDmaPerWave>();
+        // step-1 reads done, stage kt+1 landed for this wave (stage kt+2 and
+        // the early half of kt+3 may be in flight); after the barrier, for
+        // every wave (past the end: unread refill data)
+        wait_vm_lgkm0<(kNS - 3) * kDmaPerWave + kDmaEarly>();
         __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int q = 0; q < kRd; ++q) read_piece(kt + 1, 0, q, f0);
+        for (int q = 0; q < kRd; ++q) {
+          if (q < kDmaPerWave - kDmaEarly) issue_one(kt + kNS - 1, kDmaEarly + q);
+          read_piece(kt + 1, 0, q, f0);
+        }
         mma(f1);
 #pragma unroll
         for (int q = 0; q < kMf; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          if (q < kDmaPerWave - kDmaEarly)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
           if (q < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -306,13 +322,14 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
       if constexpr (MODE == 0 || sizeof(Y) == 2) {
         // Through LDS: a lane holds 4 consecutive features of one token, so
         // stores straight from the accumulators would write 16 B to each of
-        // 32 rows per instruction. Each wave stages its 128 tokens x (64
-        // features, or 128 outputs) as 2-byte values in its own 32 KB of the
+        // 32 rows per instruction. Each wave stages its 64 tokens x (64
+        // features, or 128 outputs) as 2-byte values in its own 16 KB of the
         // (now idle) ring, token-major with 8-byte chunks XOR-swizzled by
         // token, then stores whole 128 / 256-byte row segments.
         __builtin_amdgcn_s_barrier();   // every wave is done with the ring
-        char* stg = smem + wave * 32768;
+        char* stg = smem + wave * 16384;
         constexpr int kRowB = MODE == 0 ? 128 : 256;     // staged bytes per token
+        static_assert(TW * kRowB * (MODE == 0 ? 2 : 1) <= 16384, "staging fits");
         constexpr int kSwz = MODE == 0 ? 7 : 15;
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
@@ -333,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
                 }
                 const int pc = (p * 8 + rq * 2 + (hi4 >> 2)) ^ sw;
                 *reinterpret_cast<V4*>(stg + tok * kRowB + pc * 8) = hv;
-                if (a.out2) *reinterpret_cast<V4*>(stg + 16384 + tok * kRowB + pc * 8) = lv;
+                if (a.out2) *reinterpret_cast<V4*>(stg + TW * kRowB + tok * kRowB + pc * 8) = lv;
               }
           } else {
 #pragma unroll
@@ -349,7 +366,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
               }
           }
         }
-        const int tok_base = row0 + wt * (BT / 2);
+        const int tok_base = row0 + wt * TW;
         if (MODE == 0) {
           // H of full-tile experts, k-block-major [F / 32][h_rows][32]: per
           // instruction 16 tokens x one 32-feature block = 1 KB contiguous
@@ -358,13 +375,13 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
           for (int pl = 0; pl < planes; ++pl) {
             char* dst = reinterpret_cast<char*>(pl ? a.out2 : a.out);
 #pragma unroll 4
-            for (int it = 0; it < 16; ++it) {
+            for (int it = 0; it < TW / 8; ++it) {
               const int kbl = it & 1;              // which 32 of the 64 features
               const int tok = (it >> 1) * 16 + rl;
               const int sw = ((tok >> 1) & kSwz) << 1;
               const int j = kbl * 4 + jp;          // 16-byte piece of the row
               const uint4 v = *reinterpret_cast<const uint4*>(
-                  stg + pl * 16384 + tok * kRowB + (((2 * j) ^ sw) * 8));
+                  stg + pl * TW * kRowB + tok * kRowB + (((2 * j) ^ sw) * 8));
               if (tok_base + tok >= ne) continue;
               const size_t prow = (size_t)(off + tok_base + tok);
               const size_t kb = (size_t)((nb * 128 + ww * 64) / 32 + kbl);
@@ -376,7 +393,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
           const int rl = lane_e >> 4, jp = lane_e & 15;
           S* dst = reinterpret_cast<S*>(a.out);
 #pragma unroll 4
-          for (int it = 0; it < 32; ++it) {
+          for (int it = 0; it < TW / 4; ++it) {
             const int tok = it * 4 + rl;
             const int sw = ((tok >> 1) & kSwz) << 1;
             const uint4 v = *reinterpret_cast<const uint4*>(
@@ -391,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void gemm_full_kernel(GemmArgs a) {
       } else {
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-          const int trow_ = row0 + wt * (BT / 2) + t * 32 + jt;
+          const int trow_ = row0 + wt * TW + t * 32 + jt;
           if (trow_ >= ne) continue;
           const size_t prow = (size_t)(off + trow_);
 #pragma unroll
@@ -415,16 +432,16 @@ hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
   if (grid <= 0) return hipSuccess;
   if (xdt == MOE_F16) {
     if (a.mode == 0)
-      hipLaunchKernelGGL((gemm_full_kernel<F16T, 0, 0>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 0, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_full_kernel<F16T, 1, 0>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 1, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
   } else if (xdt == MOE_BF16) {
     if (a.mode == 0)
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 0, 0>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 0, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
     else if (a.A2)
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 1>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 1>), dim3(grid), dim3(kWaves * 64), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 0>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 1, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
