@@ -73,11 +73,12 @@ __device__ __forceinline__ int xcd_item(int rb0, int b, int G, int n_items) {
 // silu(g) = g / (1 + e^-g) with the hardware's 2^x and reciprocal (about
 // one ulp each): the epilogues evaluate it for every (pair, feature), and a
 // libm-accurate exp there costs more time than the tile's last stages.
+// The clamps are one v_med3_f32 each (c <= 0 means no clamp: the bound
+// becomes +inf, which the compiler folds once per kernel, not per value).
 __device__ __forceinline__ float swiglu(float g, float u, float c) {
-  if (c > 0.f) {
-    g = fminf(g, c);
-    u = fminf(fmaxf(u, -c), c);
-  }
+  const float cl = c > 0.f ? c : __builtin_inff();
+  g = __builtin_amdgcn_fmed3f(g, -__builtin_inff(), cl);
+  u = __builtin_amdgcn_fmed3f(u, -cl, cl);
   const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896340736f);
   return g * __builtin_amdgcn_rcpf(1.f + e) * u;
 }

@@ -83,9 +83,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   const int n_tiles = a.meta[a.meta_index];
   const int n_items = n_tiles * NNB;
   const int G = gridDim.x;
-  // this lane's rows in its wave's DMA blocks: block b = 8 wave + jj covers
-  // stage rows 16 b .. 16 b + 15; lane writes row 16 b + lane / 4, physical
-  // chunk lane % 4, so it loads logical chunk (lane % 4) ^ ((row >> 2) & 3)
+  // this lane's row within each of its wave's 16-row DMA blocks
   const int dma_r = lane >> 2;
 
   for (int i = blockIdx.x; i < n_items; i += G) {
@@ -138,30 +136,41 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     for (int pass = 0; pass < NPASS; ++pass) {
       const int row0 = tile_row0 + pass * BT;
       if (row0 >= ne) break;   // block-uniform
+      // This lane's row of DMA block jj is stage row 16 (4 wave + jj) + lane / 4;
+      // it loads logical chunk (lane % 4) ^ ((row >> 2) & 3). The branches
+      // are wave-uniform and sit outside the per-block loops, so a token
+      // wave issues its four pair-list loads back to back and waits once.
       uint32_t voff[kDmaPerWave];
+      if (w_wave) {
 #pragma unroll
-      for (int jj = 0; jj < kDmaPerWave; ++jj) {
-        const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;   // stage row
-        const int c = (lane & 3) ^ ((R >> 2) & 3);
-        uint32_t rowoff;
-        if (w_wave) {
+        for (int jj = 0; jj < kDmaPerWave; ++jj) {
+          const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;
           int row;
           if (MODE == 0)   // 32-row blocks alternate W_gate / W_up
             row = nb * 128 + (R >> 7) * 64 + ((R >> 6) & 1) * 32 + (R & 31);
           else
             row = min(nb * kBW + R, N - 1);
-          rowoff = tiled ? (uint32_t)row * (uint32_t)kRowB : (uint32_t)row * (uint32_t)K * 2u;
-        } else {
-          const int Rt = R - 256;
-          const int rr = min(row0 + (Rt % BT), ne - 1);
-          if (MODE == 0) {
-            rowoff = (uint32_t)a.pair_token[off + rr] * (uint32_t)a.a_ld * 2u;
-          } else {
-            // the SwiGLU output of full-tile experts is k-block-major too
-            rowoff = (uint32_t)(off + rr) * (uint32_t)kRowB;
-          }
+          const uint32_t rowoff = tiled ? (uint32_t)row * (uint32_t)kRowB
+                                        : (uint32_t)row * (uint32_t)K * 2u;
+          voff[jj] = rowoff + (uint32_t)((lane & 3) ^ ((R >> 2) & 3)) * 16u;
         }
-        voff[jj] = rowoff + (uint32_t)c * 16u;
+      } else {
+        int prow[kDmaPerWave];
+#pragma unroll
+        for (int jj = 0; jj < kDmaPerWave; ++jj) {
+          const int Rt = 16 * (wave * kDmaPerWave + jj) + dma_r - 256;
+          const int rr = min(row0 + (Rt % BT), ne - 1);
+          // x rows are gathered through the pair list; the SwiGLU output of
+          // full-tile experts is k-block-major, pair rows in order
+          prow[jj] = MODE == 0 ? a.pair_token[off + rr] : off + rr;
+        }
+#pragma unroll
+        for (int jj = 0; jj < kDmaPerWave; ++jj) {
+          const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;
+          const uint32_t rowoff = MODE == 0 ? (uint32_t)prow[jj] * (uint32_t)a.a_ld * 2u
+                                            : (uint32_t)prow[jj] * (uint32_t)kRowB;
+          voff[jj] = rowoff + (uint32_t)((lane & 3) ^ ((R >> 2) & 3)) * 16u;
+        }
       }
       // bytes from one stage's slice of a row to the next stage's
       const int s_step = w_wave ? (tiled ? N * kRowB : kRowB)
