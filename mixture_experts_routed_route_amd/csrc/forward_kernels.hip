@@ -213,6 +213,7 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
     a.meta[kMetaSk4] = c4;
     a.meta[kMetaFat] = cf;
   }
+  if (threadIdx.x >= kMetaQueueGateUp && threadIdx.x < kMetaCount) a.meta[threadIdx.x] = 0;
 }
 
 hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s) {

@@ -24,11 +24,12 @@
 // clamp from Strata PR #4366, "Approach"). Tokens are gathered on load
 // through the plan's pair list; no gathered copy of x is materialised.
 //
-// Work is persistent: block b takes items b, b + G, ... Items are tiles of
-// the classify kernel's largest-first list crossed with output-column
-// blocks; within a round the items of one XCD (blocks b = x mod 8) are a
-// contiguous run of a 4 x 8 (row tiles x column tiles) grouping, so the 32
-// blocks resident on an XCD share their A and B slices in its L2.
+// Work is persistent, one block per CU, items taken from per-XCD queues.
+// Items are tiles of the classify kernel's largest-first list crossed with
+// output-column blocks; within a round the items of one XCD (blocks b = x
+// mod 8) are a contiguous run of a 4 x 8 (row tiles x column tiles)
+// grouping, so the 32 blocks resident on an XCD share their A and B slices
+// in its L2.
 #include "device_common.h"
 
 namespace moe {
@@ -70,7 +71,11 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   constexpr int TW = BT / 4;               // token rows per wave
   constexpr int TB = TW / 32;              // 32-row token blocks per wave
   constexpr int NPASS = 256 / BT;          // passes over a 256-row tile
-  __shared__ __attribute__((aligned(1024))) char smem[kNS * kStage];
+  // the ring, then the block's next work item (one LDS object: with a
+  // second one the compiler guards every fragment read with a wait for all
+  // LDS-DMA loads in flight)
+  __shared__ __attribute__((aligned(1024))) char smem[kNS * kStage + 16];
+  int* const next_item = reinterpret_cast<int*>(smem + kNS * kStage);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,14 +91,46 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   // this lane's row within each of its wave's 16-row DMA blocks
   const int dma_r = lane >> 2;
 
-  for (int i = blockIdx.x; i < n_items; i += G) {
-    // XCD-aware permutation inside a full round, then 4 x 8 grouping
-    int L = i;
-    const int rb0 = (i / G) * G;
-    if ((G & 7) == 0 && rb0 + G <= n_items) {
-      const int w = i - rb0;
-      L = rb0 + (w & 7) * (G >> 3) + (w >> 3);
-    }
+  // Work queues, one per XCD (block b runs on XCD b mod 8): queue x holds,
+  // round by round, the items the XCD-aware order gives XCD x (a round is G
+  // items; within it the G / 8 items of one XCD are a contiguous run of the
+  // 4 x 8 grouping below), and each block takes the next item of its own
+  // queue with an atomic counter. Blocks that run fast take more items; a
+  // block whose queue is empty takes from the other XCDs' queues, so the
+  // launch ends when the work does, not when the slowest block's static
+  // share does. The counter for a block's next item is bumped at the start
+  // of the current one, so its latency is hidden.
+  const bool byx = (G & 7) == 0;
+  const int per = G >> 3;
+  const int xq = byx ? (int)(blockIdx.x & 7) : 0;
+  auto queue_item = [&](int x, int j) -> int {
+    if (!byx) return j < n_items ? j : -1;
+    const int r = j / per;
+    if (r * G >= n_items) return -1;
+    return xcd_item(r * G, (j - r * per) * 8 + x, G, n_items);
+  };
+  auto take = [&](int j_own) -> int {   // thread 0 only
+    int it = queue_item(xq, j_own);
+    if (byx)
+      for (int d = 1; d < 8 && it < 0; ++d) {
+        const int x = (xq + d) & 7;
+        it = queue_item(x, atomicAdd(&a.queue[x], 1));
+      }
+    return it;
+  };
+  if (threadIdx.x == 0) *next_item = take(atomicAdd(&a.queue[xq], 1));
+  wait_vm_lgkm0<63>();
+  __builtin_amdgcn_s_barrier();
+  int L = __builtin_amdgcn_readfirstlane(*next_item);
+
+  // an opaque per-lane zero: with a uniform address the compiler turns the
+  // atomic into a wave-aggregated one whose result it waits for on the spot
+  int zq = 0;
+  asm volatile("" : "+v"(zq));
+  while (L >= 0) {
+    int j_next = 0, jn = 0;
+    if (threadIdx.x == 0) j_next = atomicAdd(a.queue + xq + zq, 1);
+    // 4 x 8 grouping of (row tiles x column blocks)
     const int group = L / (kGM * NNB);
     const int first = group * kGM;
     const int gm = min(kGM, n_tiles - first);
@@ -135,7 +172,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
 
     for (int pass = 0; pass < NPASS; ++pass) {
       const int row0 = tile_row0 + pass * BT;
-      if (row0 >= ne) break;   // block-uniform
+      if (pass > 0 && row0 >= ne) break;   // block-uniform; a tile's first pass has rows
       // This lane's row of DMA block jj is stage row 16 (4 wave + jj) + lane / 4;
       // it loads logical chunk (lane % 4) ^ ((row >> 2) & 3). The branches
       // are wave-uniform and sit outside the per-block loops, so a token
@@ -318,6 +355,10 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       // is issued, so the next pass's refills of the same ring slots are
       // ordered after them whatever order loads complete in
       wait_vmcnt<0>();
+      // the counter bumped at the item's start has returned by now; reading
+      // it here (every wave, in step with the wait above) leaves no load
+      // pending across the item loop for the compiler to wait on later
+      jn = __builtin_amdgcn_readfirstlane(j_next);
       // epilogue: accumulator r of a 32x32 block is weight row
       // 8 (r / 4) + 4 (lane / 32) + r % 4, token column lane % 32
       // lane-derived epilogue values are defined here, after the K loop, so
@@ -433,6 +474,11 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         }
       }
     }
+    // every wave has read next_item before this item's first barrier
+    if (threadIdx.x == 0) *next_item = take(jn);
+    wait_vm_lgkm0<63>();
+    __builtin_amdgcn_s_barrier();
+    L = __builtin_amdgcn_readfirstlane(*next_item);
   }
 }
 

@@ -581,6 +581,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       }
       gf.list = (const int32_t*)(b + L.full_tiles);
       gf.meta_index = kMetaFullTiles;
+      gf.queue = meta + (stage == 0 ? kMetaQueueGateUp : kMetaQueueDown);
       const int grid = (int)std::min<int64_t>((int64_t)L.cap_tiles * nnb, full_grid_cap);
       e = launch_gemm_full(gf, x_dtype, grid, s);
       if (e != hipSuccess) return hip_fail(e, "full tile kernel");

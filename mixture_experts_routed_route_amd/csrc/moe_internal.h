@@ -53,8 +53,11 @@ enum Route : int32_t { kRouteNone = 0, kRouteSplitK = 1, kRouteFull = 2,
                        kRouteFat = 3 };
 
 // Forward meta counters written by the classify kernel.
+// Counters 8..15 and 16..23 are the full tile's work queues (one per XCD)
+// of the gate/up and the down launch; the classify kernel zeroes them.
 enum Meta : int32_t { kMetaFullTiles = 0, kMetaSk1 = 1, kMetaSk4 = 2,
-                      kMetaFat = 3, kMetaCount = 8 };
+                      kMetaFat = 3, kMetaQueueGateUp = 8, kMetaQueueDown = 16,
+                      kMetaCount = 24 };
 
 // ---- launchers (plan_kernels.hip) ---------------------------------------
 hipError_t launch_route_hist(const float* logits, int T, int E, int k,
@@ -132,6 +135,7 @@ struct GemmArgs {
   const int32_t* list;      // work list (full tiles or split-K groups)
   const int32_t* meta;      // counts of the work lists
   int meta_index;           // which meta counter holds this list's length
+  int32_t* queue;           // full tile: 8 zeroed work-queue counters
   int h_rows;               // full tile: rows of the k-block-major H
                             // ([F / 32][h_rows][32]) it writes (gate/up) or
                             // reads (down)
