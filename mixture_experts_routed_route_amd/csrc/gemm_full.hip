@@ -30,6 +30,8 @@
 // mod 8) are a contiguous run of a 4 x 8 (row tiles x column tiles)
 // grouping, so the 32 blocks resident on an XCD share their A and B slices
 // in its L2.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace moe {
@@ -67,10 +69,6 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   using S = typename TT::S;
   using V8 = typename TT::V8;
   using V4 = typename TT::V4;
-  constexpr int BT = LO ? 128 : 256;       // token rows per pass
-  constexpr int TW = BT / 4;               // token rows per wave
-  constexpr int TB = TW / 32;              // 32-row token blocks per wave
-  constexpr int NPASS = 256 / BT;          // passes over a 256-row tile
   // the ring, then the block's next work item (one LDS object: with a
   // second one the compiler guards every fragment read with a wait for all
   // LDS-DMA loads in flight)
@@ -98,8 +96,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   // queue with an atomic counter. Blocks that run fast take more items; a
   // block whose queue is empty takes from the other XCDs' queues, so the
   // launch ends when the work does, not when the slowest block's static
-  // share does. The counter for a block's next item is bumped at the start
-  // of the current one, so its latency is hidden.
+  // share does. The counter for a block's next item is bumped before the
+  // current one's epilogue, whose arithmetic hides its latency.
   const bool byx = (G & 7) == 0;
   const int per = G >> 3;
   const int xq = byx ? (int)(blockIdx.x & 7) : 0;
@@ -124,12 +122,12 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   int L = __builtin_amdgcn_readfirstlane(*next_item);
 
   // an opaque per-lane zero: with a uniform address the compiler turns the
-  // atomic into a wave-aggregated one whose result it waits for on the spot
+  // atomic into a wave-aggregated one (a readfirstlane of the result right
+  // after it, waited for on the spot)
   int zq = 0;
   asm volatile("" : "+v"(zq));
   while (L >= 0) {
     int j_next = 0, jn = 0;
-    if (threadIdx.x == 0) j_next = atomicAdd(a.queue + xq + zq, 1);
     // 4 x 8 grouping of (row tiles x column blocks)
     const int group = L / (kGM * NNB);
     const int first = group * kGM;
@@ -170,9 +168,16 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       r_odd = r_even;
     }
 
-    for (int pass = 0; pass < NPASS; ++pass) {
+    // One pass over BT token rows of the tile: 256, or 128 for a tile of at
+    // most 128 rows (half the MFMA work; waves 6 and 7 load nothing) and for
+    // each of the two passes of a split-H tile (LOP: rows 128..255 of the
+    // stage hold the low plane of the same 128 tokens).
+    auto run = [&](auto bt_c, auto lo_c, int pass) {
+      constexpr int BT = decltype(bt_c)::value;
+      constexpr bool LOP = decltype(lo_c)::value;
+      constexpr int TW = BT / 4;               // token rows per wave
+      constexpr int TB = TW / 32;              // 32-row token blocks per wave
       const int row0 = tile_row0 + pass * BT;
-      if (pass > 0 && row0 >= ne) break;   // block-uniform; a tile's first pass has rows
       // This lane's row of DMA block jj is stage row 16 (4 wave + jj) + lane / 4;
       // it loads logical chunk (lane % 4) ^ ((row >> 2) & 3). The branches
       // are wave-uniform and sit outside the per-block loops, so a token
@@ -217,6 +222,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       // stage issues the same number of loads and every wait below is a
       // constant count.
       auto issue_one = [&](int kt, int jj) {
+        if (!LOP && BT == 128 && wave >= 6) return;   // no rows 384..511
         char* base = smem + (kt % kNS) * kStage + wave * kDmaPerWave * 1024;
         const int soff = min(kt, nk - 1) * s_step;
         const __amdgpu_buffer_rsrc_t rs =
@@ -237,8 +243,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[wi][t][r] = 0.f;
 
-      // operand fragments of one 16-deep K step (hi and, for LO, lo planes)
-      struct Frag { V8 w[4]; V8 t[TB]; V8 tl[LO ? TB : 1]; };
+      // operand fragments of one 16-deep K step (hi and, for LOP, lo planes)
+      struct Frag { V8 w[4]; V8 t[TB]; V8 tl[LOP ? TB : 1]; };
       auto read_frag = [&](int kt, int ks, Frag& f) {
         const char* Ws = smem + (kt % kNS) * kStage;
         const char* Ts = Ws + kBW * kRowB;
@@ -252,12 +258,12 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         for (int t = 0; t < TB; ++t) {
           const int r = wt * TW + t * 32 + (lane & 31);
           f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
-          if (LO)
+          if (LOP)
             f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
         }
       };
       // one fragment read of a step: pieces 0..3 weights, then tokens (hi,
-      // lo interleaved for LO)
+      // lo interleaved for LOP)
       auto read_piece = [&](int kt, int ks, int idx, Frag& f) {
         const char* Ws = smem + (kt % kNS) * kStage;
         const char* Ts = Ws + kBW * kRowB;
@@ -267,9 +273,9 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
           f.w[idx] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ws + swz64(r, ch)));
         } else {
           const int j = idx - 4;
-          const int t = LO ? j >> 1 : j;
+          const int t = LOP ? j >> 1 : j;
           const int r = wt * TW + t * 32 + (lane & 31);
-          if (LO && (j & 1))
+          if (LOP && (j & 1))
             f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
           else
             f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         for (int wi = 0; wi < 4; ++wi)
 #pragma unroll
           for (int t = 0; t < TB; ++t) acc[wi][t] = mfma32(f.w[wi], f.t[t], acc[wi][t]);
-        if (LO) {
+        if (LOP) {
           // low plane of H: (hi + lo) W accumulated in f32
 #pragma unroll
           for (int wi = 0; wi < 4; ++wi)
@@ -309,9 +315,10 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       // MFMAs issue in order behind each other; loads placed between them
       // issue while the matrix pipe is busy instead of in a burst that
       // leaves it idle: MFMA, LDS read, MFMA, ring refill, ...
-      constexpr int kMf = 4 * TB * (LO ? 2 : 1);   // MFMAs per 16-deep step
-      constexpr int kRd = 4 + TB * (LO ? 2 : 1);   // fragment reads per step
-      static_assert(kRd >= kDmaPerWave && kMf >= kRd, "interleave shape");
+      constexpr int kMf = 4 * TB * (LOP ? 2 : 1);  // MFMAs per 16-deep step
+      constexpr int kRd = 4 + TB * (LOP ? 2 : 1);  // fragment reads per step
+      constexpr int kSl = kMf > kRd ? kMf : kRd;   // interleave slots
+      static_assert(kRd >= kDmaPerWave, "one refill per fragment read at most");
       for (int kt = 0; kt < nk; ++kt) {
         // LDS writes of the refill and LDS reads keep source order (the
         // compiler cannot tell them apart), so alternate them here. Half of
@@ -324,8 +331,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         }
         mma(f0);
 #pragma unroll
-        for (int q = 0; q < kMf; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        for (int q = 0; q < kSl; ++q) {
+          if (q < kMf) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
           if (q < kDmaEarly) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
           if (q < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
@@ -342,8 +349,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         }
         mma(f1);
 #pragma unroll
-        for (int q = 0; q < kMf; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        for (int q = 0; q < kSl; ++q) {
+          if (q < kMf) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
           if (q < kDmaPerWave - kDmaEarly)
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
           if (q < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
@@ -355,10 +362,10 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       // is issued, so the next pass's refills of the same ring slots are
       // ordered after them whatever order loads complete in
       wait_vmcnt<0>();
-      // the counter bumped at the item's start has returned by now; reading
-      // it here (every wave, in step with the wait above) leaves no load
-      // pending across the item loop for the compiler to wait on later
-      jn = __builtin_amdgcn_readfirstlane(j_next);
+      // The counter for the block's next item is bumped here and read after
+      // the epilogue's arithmetic, before its stores: the atomic is the only
+      // load in flight then, so the compiler's wait for it costs nothing.
+      if (pass == 0 && threadIdx.x == 0) j_next = atomicAdd(a.queue + xq + zq, 1);
       // epilogue: accumulator r of a 32x32 block is weight row
       // 8 (r / 4) + 4 (lane / 32) + r % 4, token column lane % 32
       // lane-derived epilogue values are defined here, after the K loop, so
@@ -416,6 +423,9 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
               }
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        jn = __builtin_amdgcn_readfirstlane(j_next);
+        __builtin_amdgcn_sched_barrier(0);
         const int tok_base = row0 + wt * TW;
         if (MODE == 0) {
           // H of full-tile experts, k-block-major [F / 32][h_rows][32]: per
@@ -456,6 +466,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
           }
         }
       } else {
+        jn = __builtin_amdgcn_readfirstlane(j_next);
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
           const int trow_ = row0 + wt * TW + t * 32 + jt;
@@ -473,6 +484,14 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
             }
         }
       }
+    };
+    if constexpr (LO) {
+      run(std::integral_constant<int, 128>{}, std::true_type{}, 0);
+      if (tile_row0 + 128 < ne) run(std::integral_constant<int, 128>{}, std::true_type{}, 1);
+    } else if (ne - tile_row0 <= 128) {
+      run(std::integral_constant<int, 128>{}, std::false_type{}, 0);
+    } else {
+      run(std::integral_constant<int, 256>{}, std::false_type{}, 0);
     }
     // every wave has read next_item before this item's first barrier
     if (threadIdx.x == 0) *next_item = take(jn);

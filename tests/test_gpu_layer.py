@@ -91,6 +91,21 @@ def test_underfilled_full_route(exact):
     check_layer(wl, y)
 
 
+@pytest.mark.parametrize("dt", [W.F16, W.BF16])
+def test_full_tile_row_counts(dt):
+    """Every expert on the full tile, with 426, 360, 204, 134, 94, 38, 19, 3
+    and 2 rows: 256-row passes with ragged tails, the 128-row pass of tiles
+    of at most 128 rows (the second tile of the 360-row expert, the small
+    experts) and, for bf16, the split-H down passes; every token checked."""
+    bias = torch.linspace(3.0, -3.0, 16)
+    wl = W.make_layer(640, 256, 256, 16, 2, dt, seed=71, logit_bias=bias)
+    say(f"layer full tile row counts {dt}")
+    p, y = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=0.0,
+                                                  exact_routes=True))
+    check_plan(wl, p)
+    check_layer(wl, y)
+
+
 @pytest.mark.parametrize("ppe", [1, 3, 4, 8])
 @pytest.mark.parametrize("S", [0.0, 1e9])
 def test_pairs_per_expert_both_tiles(ppe, S):
