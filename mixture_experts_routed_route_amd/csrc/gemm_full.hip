@@ -69,11 +69,15 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   using S = typename TT::S;
   using V8 = typename TT::V8;
   using V4 = typename TT::V4;
-  // the ring, then the block's next work item (one LDS object: with a
-  // second one the compiler guards every fragment read with a wait for all
-  // LDS-DMA loads in flight)
-  __shared__ __attribute__((aligned(1024))) char smem[kNS * kStage + 16];
-  int* const next_item = reinterpret_cast<int*>(smem + kNS * kStage);
+  // The ring (128 KB). The block's next work item is passed through its first word (one LDS
+  // object: with a second one the compiler guards every fragment read with
+  // a wait for all LDS-DMA loads in flight). That word is wave 0's epilogue
+  // staging and ring slot 0: thread 0 writes it after wave 0's epilogue and
+  // after every wave's loads have landed (the wait and barrier that end the
+  // K loop), all waves read it after the next barrier, and the next item's
+  // first loads are issued only after the barrier that follows.
+  __shared__ __attribute__((aligned(1024))) char smem[kNS * kStage];
+  int* const next_item = reinterpret_cast<int*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
