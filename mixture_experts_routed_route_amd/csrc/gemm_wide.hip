@@ -4,15 +4,18 @@
 // dozen gathered rows, so re-reading those rows per 64-column block (what the
 // split-K tile does) costs several times the weight bytes. Here one block of
 // 4 waves covers 256 output columns: the expert's rows (<= 64) are staged
-// once per 128-deep K chunk in LDS by direct-to-LDS loads and shared by the
-// four waves, while each wave streams its own 64 weight rows from HBM three
+// once per CK-deep K chunk in LDS by direct-to-LDS loads and shared by the
+// four waves, while each wave streams its own 64 weight rows from HBM
 // chunks ahead and, for 4-bit weights, dequantises them in registers (the
 // fused-dequant tiles the Strata PR #4366 route description leaves to the
-// experts under the fat-row threshold).
+// experts under the fat-row threshold). CK = 256 when K allows: the four
+// lanes of a weight row then read its whole 128-byte line per chunk (with
+// CK = 128 a chunk reads half a line and the other half comes a chunk later,
+// from L2 if it is still there).
 //
 // Lane (n = l % 16, q = l / 16) of v_mfma_f32_16x16x32 holds, for K sub-chunk
-// i of a 128-deep chunk, A/B values at k = 32 q + 8 i .. + 8, matched between
-// operands. A row r of a chunk is 256 bytes in LDS with 16-byte chunk c at
+// i of a chunk, A/B values at k = (CK / 4) q + 8 i .. + 8, matched between
+// operands. A row r of a chunk is 2 CK bytes in LDS with 16-byte chunk c at
 // c ^ (r % 16), so the 16 rows of one operand read hit 16 distinct bank
 // groups. Gate/up column blocks cb = 0..3 of a wave are W_gate f0.., W_up
 // f0.., W_gate f0+16.., W_up f0+16.., f0 = 128 nb + 32 w.
@@ -30,33 +33,43 @@ namespace {
 struct WF16 { using S = _Float16; using V8 = half8; };
 struct WBF16 { using S = __bf16; using V8 = bf16x8; };
 
-constexpr int kChunkK = 128;            // K per LDS chunk
 constexpr int kRowsW = 64;              // token rows per item (4 blocks of 16)
-constexpr int kChunkB = kRowsW * kChunkK * 2;   // 16 KB per LDS chunk
-constexpr int kPD = 3;                  // weight chunks ahead per wave
-constexpr int kNA = 3;                  // LDS chunks of A (two ahead)
+
+// Chunk geometry: CK = 128 keeps three chunks in flight (A two ahead in LDS,
+// weights three ahead in registers), CK = 256 two (same LDS: 64 KB a block).
+template <int CK> struct WGeo {
+  static constexpr int kChunkB = kRowsW * CK * 2;   // LDS bytes per chunk
+  static constexpr int kN = CK == 128 ? 3 : 2;      // chunks in flight (A and W)
+  static constexpr int kSl = CK / 32;               // 32-deep MFMA slices
+  static constexpr int kAi = kChunkB / 1024 / 4;    // A loads per wave per chunk
+  static constexpr int kRowB = CK * 2;              // bytes of an A row
+};
 
 }  // namespace
 
-// Weight operand of one 128-deep chunk for one lane: 4 column blocks.
-template <int WQ>
+// Weight operand of one chunk for one lane: 4 column blocks, CK / 4 values
+// each (4-bit: CK / 128 16-byte pieces and the one or two block scales).
+template <int WQ, int CK>
 struct WChunk;
-template <>
-struct WChunk<1> { uint4 q[4]; uint32_t s[4]; };
-template <>
-struct WChunk<0> { uint4 d[4][4]; };
+template <int CK>
+struct WChunk<1, CK> { uint4 q[4][CK / 128]; uint32_t s[4]; };
+template <int CK>
+struct WChunk<0, CK> { uint4 d[4][CK / 32]; };
 
-template <class TT, int WQ, int MODE>
+template <class TT, int WQ, int MODE, int CK>
 __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
   using S = typename TT::S;
   using V8 = typename TT::V8;
-  __shared__ __attribute__((aligned(1024))) char smem[kNA * kChunkB];
+  using Gm = WGeo<CK>;
+  constexpr int kChunkB = Gm::kChunkB, kN = Gm::kN, kSl = Gm::kSl;
+  constexpr int kAi = Gm::kAi, kRowB = Gm::kRowB;
+  __shared__ __attribute__((aligned(1024))) char smem[kN * kChunkB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, q = lane >> 4;
   const int K = a.K, N = a.N;
-  const int nch = K / kChunkK;
+  const int nch = K / CK;
   const int cols_per_item = MODE == 0 ? 128 : 256;      // features / outputs
   const int NNB = (N + cols_per_item - 1) / cols_per_item;
   const int n_items = a.meta[a.meta_index] * NNB;
@@ -75,21 +88,23 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
 
     // A staging: block of 16 x 1 KB per chunk, 4 per wave; lane writes row
     // 4 b + lane / 16 at physical chunk lane % 16 = logical (lane%16)^(row%16)
-    uint32_t aoff[4];
+    constexpr int kLpr = kRowB / 16;          // lanes per A row in one 1 KB load
+    constexpr int kRpi = 64 / kLpr;           // A rows per 1 KB load
+    uint32_t aoff[kAi];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * (wave * 4 + j) + (lane >> 4);
+    for (int j = 0; j < kAi; ++j) {
+      const int r = kRpi * (wave * kAi + j) + lane / kLpr;
       const int rr = row0 + min(r, nrows - 1);
       const uint32_t prow = MODE == 0 ? (uint32_t)a.pair_token[off + rr]
                                       : (uint32_t)(off + rr);
-      const int c = (lane & 15) ^ (r & 15);
+      const int c = (lane % kLpr) ^ (r & 15);
       aoff[j] = prow * (uint32_t)a.a_ld * 2u + (uint32_t)c * 16u;
     }
     auto issue_a = [&](int ch) {
-      char* base = smem + (ch % kNA) * kChunkB + wave * 4 * 1024;
-      const int soff = min(ch, nch - 1) * kChunkK * 2;
+      char* base = smem + (ch % kN) * kChunkB + wave * kAi * 1024;
+      const int soff = min(ch, nch - 1) * CK * 2;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kAi; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(base + j * 1024),
                                                  16, (int)aoff[j], soff, 0, 0);
     };
@@ -122,17 +137,22 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
         bsp[cb] = nullptr;
       }
     }
-    auto load_w = [&](int ch, WChunk<WQ>& w) {
+    // lane q takes the CK / 4 consecutive K values from k0
+    auto load_w = [&](int ch, WChunk<WQ, CK>& w) {
       const int cc = min(ch, nch - 1);
-      const int k0 = cc * kChunkK + q * 32;
+      const int k0 = cc * CK + q * (CK / 4);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         if constexpr (WQ) {
-          w.q[cb] = ldg16(bp[cb] + k0 / 2);
-          w.s[cb] = (uint32_t)bsp[cb][k0 / 32];
+#pragma unroll
+          for (int h = 0; h < CK / 128; ++h) w.q[cb][h] = ldg16(bp[cb] + k0 / 2 + h * 16);
+          if constexpr (CK == 256)   // two adjacent fp16 scales, 4-byte aligned
+            w.s[cb] = *reinterpret_cast<const uint32_t*>(bsp[cb] + k0 / 32);
+          else
+            w.s[cb] = (uint32_t)bsp[cb][k0 / 32];
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w.d[cb][i] = ldg16(bp[cb] + (size_t)k0 * 2 + i * 16);
+          for (int i = 0; i < kSl; ++i) w.d[cb][i] = ldg16(bp[cb] + (size_t)k0 * 2 + i * 16);
         }
       }
     };
@@ -146,23 +166,26 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
     // per 32-value slice i: the four row blocks' A fragments, then each
     // column block's slice decoded just before its MFMAs (16 + 16 operand
     // registers instead of all 64 decoded values at once)
-    auto compute = [&](int ch, const WChunk<WQ>& w) {
-      const char* As = smem + (ch % kNA) * kChunkB;
+    auto compute = [&](int ch, const WChunk<WQ, CK>& w) {
+      const char* As = smem + (ch % kN) * kChunkB;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kSl; ++i) {
         V8 av[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           const int r = rb * 16 + n;
-          const int c = (q * 4 + i) ^ (r & 15);
-          av[rb] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(As + r * 256 + c * 16));
+          const int c = (q * kSl + i) ^ (r & 15);
+          av[rb] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(As + r * kRowB + c * 16));
         }
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           V8 bv;
           if constexpr (WQ) {
-            const uint32_t word = i == 0 ? w.q[cb].x : i == 1 ? w.q[cb].y : i == 2 ? w.q[cb].z : w.q[cb].w;
-            bv = __builtin_bit_cast(V8, dequant_word(word, __builtin_bit_cast(_Float16, (uint16_t)w.s[cb])));
+            const uint4 wq = w.q[cb][i >> 2];
+            const uint32_t word = (i & 3) == 0 ? wq.x : (i & 3) == 1 ? wq.y : (i & 3) == 2 ? wq.z : wq.w;
+            // the lane's CK / 4 values span CK / 128 blocks of 32
+            const uint16_t sb = (uint16_t)(w.s[cb] >> (16 * (i >> 2)));
+            bv = __builtin_bit_cast(V8, dequant_word(word, __builtin_bit_cast(_Float16, sb)));
           } else {
             bv = __builtin_bit_cast(V8, w.d[cb][i]);
           }
@@ -172,45 +195,43 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
       }
     };
 
-    // Ring: A two chunks ahead in LDS, weights three chunks ahead in
-    // registers. Issue order is W0 A0 W1 A1 W2, then per step s: A(s+2),
-    // compute(s), W(s+3). vmcnt retires in order, so at the top of step s
-    // "A(s) landed" is "at most W(s+1), A(s+1), W(s+2) outstanding", which
-    // also retires W(s) (issued before A(s)). The barrier then publishes
-    // A(s) to all waves and frees the buffer A(s+2) refills (last read by
-    // compute(s-1), before this barrier). Past the end, loads re-read the
-    // last chunk into buffers and slots no one reads.
-    constexpr int kWvm = WQ ? 8 : 16;    // weight loads per chunk per lane
+    // Ring of kN chunks: A kN - 1 chunks ahead in LDS, weights kN ahead in
+    // registers. Issue order is W0 A0 W1 A1 .. W(kN - 1), then per step s:
+    // A(s + kN - 1), compute(s), W(s + kN). vmcnt retires in order, and A(s)
+    // was issued kN - 1 steps before step s, after W(s): at the top of step
+    // s "A(s) landed" is "at most the kN - 1 weight chunks and kN - 2 A
+    // chunks issued since outstanding", which retires W(s) too. The barrier
+    // then publishes A(s) to all waves and frees the buffer A(s + kN - 1)
+    // refills (last read by compute(s - 1), before this barrier). Past the
+    // end, loads re-read the last chunk into buffers and slots no one reads.
+    constexpr int kWvm = WQ ? 4 * (CK / 128) + 4 : 4 * kSl;   // weight loads per chunk per lane
+    constexpr int kWait = (kN - 1) * kWvm + (kN - 2) * kAi;
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    WChunk<WQ> w0, w1, w2;
-    load_w(0, w0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(1, w1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(2, w2);
-    __builtin_amdgcn_sched_barrier(0);
-    auto step = [&](int ch, WChunk<WQ>& w) {
-      wait_vmcnt<2 * kWvm + 4>();
+    WChunk<WQ, CK> wr[kN];
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      load_w(j, wr[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < kN - 1) issue_a(j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    auto step = [&](int ch, WChunk<WQ, CK>& w) {
+      wait_vmcnt<kWait>();
       __builtin_amdgcn_s_barrier();
-      issue_a(ch + 2);
+      issue_a(ch + kN - 1);
       __builtin_amdgcn_sched_barrier(0);
       if (active && ch < nch) compute(ch, w);
       __builtin_amdgcn_sched_barrier(0);
-      load_w(ch + kPD, w);
+      load_w(ch + kN, w);
       __builtin_amdgcn_sched_barrier(0);
     };
     // every path issues the same loads (steps past the end only load), so
     // the compiler's own waits agree with the counted ones
-    const int nsteps = (nch + kPD - 1) / kPD * kPD;
-    for (int ch = 0; ch < nsteps; ch += kPD) {
-      step(ch, w0);
-      step(ch + 1, w1);
-      step(ch + 2, w2);
+    const int nsteps = (nch + kN - 1) / kN * kN;
+    for (int ch = 0; ch < nsteps; ch += kN) {
+#pragma unroll
+      for (int j = 0; j < kN; ++j) step(ch + j, wr[j]);
     }
 
     if (active) {
@@ -247,14 +268,19 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
 hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
                             hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-#define MOE_WIDE(TT, WQ)                                                              \
-  do {                                                                                \
-    if (a.mode == 0)                                                                  \
-      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 0>), dim3(grid), dim3(256), 0, s, a); \
-    else                                                                              \
-      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 1>), dim3(grid), dim3(256), 0, s, a); \
+  // K is a multiple of 128 (the layer's D and F are)
+#define MOE_WIDE(TT, WQ, CK)                                                              \
+  do {                                                                                    \
+    if (a.mode == 0)                                                                      \
+      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 0, CK>), dim3(grid), dim3(256), 0, s, a); \
+    else                                                                                  \
+      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 1, CK>), dim3(grid), dim3(256), 0, s, a); \
   } while (0)
-  if (xdt == MOE_F16 && wdt == MOE_Q4B32) MOE_WIDE(WF16, 1);
+  if (a.K % 128) return hipErrorInvalidValue;
+  if (xdt == MOE_F16 && wdt == MOE_Q4B32) {
+    if (a.K % 256 == 0) MOE_WIDE(WF16, 1, 256);
+    else MOE_WIDE(WF16, 1, 128);
+  }
   else return hipErrorInvalidValue;   // 16-bit weights take the stream tile
 #undef MOE_WIDE
   return hipGetLastError();
