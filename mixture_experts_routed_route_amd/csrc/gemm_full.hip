@@ -111,15 +111,29 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     if (r * G >= n_items) return -1;
     return xcd_item(r * G, (j - r * per) * 8 + x, G, n_items);
   };
+  // items in queue x: its share of the full rounds and of the last one
+  auto queue_size = [&](int x) -> int {
+    const int full = n_items / G, R = n_items - full * G;
+    return full * per + (R >> 3) + (x < (R & 7) ? 1 : 0);
+  };
   auto take = [&](int j_own) -> int {   // thread 0 only
     int it = queue_item(xq, j_own);
-    if (byx)
-      for (int d = 1; d < 8 && it < 0; ++d) {
-        const int x = (xq + d) & 7;
-        it = queue_item(x, atomicAdd(&a.queue[x], 1));
-      }
+    if (it >= 0 || !byx) return it;
+    // own queue empty: read the other counters in one batch and bump only
+    // those with items left (the last blocks of a launch then pay one
+    // round trip, not seven atomics)
+    int seen[8];
+#pragma unroll
+    for (int d = 1; d < 8; ++d)
+      seen[d] = __hip_atomic_load(&a.queue[(xq + d) & 7], __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+    for (int d = 1; d < 8 && it < 0; ++d) {
+      const int x = (xq + d) & 7;
+      if (seen[d] < queue_size(x)) it = queue_item(x, atomicAdd(&a.queue[x], 1));
+    }
     return it;
   };
+  if (n_items == 0) return;
   if (threadIdx.x == 0) *next_item = take(atomicAdd(&a.queue[xq], 1));
   wait_vm_lgkm0<63>();
   __builtin_amdgcn_s_barrier();
