@@ -334,18 +334,37 @@ __global__ __launch_bounds__(256) void gemm_stream_fixup_kernel(GemmArgs a, int 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
     acc[rb][0] = acc[rb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int rn = j; rn <= bl; ++rn) {
-    const int s0 = run_start(U, rn, G);
-    if (s0 == run_start(U, rn + 1, G)) continue;   // empty run
-    const int slot = s0 / nk == item ? 0 : 1;
-    const float* pp = a.part + ((size_t)rn * 2 + slot) * kStreamSlotFloats;
+  // The runs of one item are read UR at a time, all loads before the first
+  // add (a run's partials are a few KB from L2: one round trip for UR runs,
+  // not one each), and added in run order.
+  constexpr int UR = RB == 1 ? 8 : 4;
+  for (int rn0 = j; rn0 <= bl; rn0 += UR) {
+    float v[UR][RB][8];
+    bool live[UR];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int q = 0; q < UR; ++q) {
+      const int rn = rn0 + q;
+      const int s0 = run_start(U, rn, G);
+      // past the item's last run, or an empty run: nothing to add
+      live[q] = rn <= bl && s0 != run_start(U, rn + 1, G);
+      const int slot = s0 / nk == item ? 0 : 1;
+      const float* pp = a.part + ((size_t)(live[q] ? rn : j) * 2 + slot) * kStreamSlotFloats;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        acc[rb][0][r] += pp[(rb * 8 + r) * 256 + tid];
-        acc[rb][1][r] += pp[(rb * 8 + 4 + r) * 256 + tid];
-      }
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) v[q][rb][r] = pp[(rb * 8 + r) * 256 + tid];
+    }
+#pragma unroll
+    for (int q = 0; q < UR; ++q) {
+      if (!live[q]) continue;   // block-uniform
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[rb][0][r] += v[q][rb][r];
+          acc[rb][1][r] += v[q][rb][4 + r];
+        }
+    }
   }
   const int g = item / NNB;
   stream_store<S, MODE, RB>(a, acc, item - g * NNB, a.list[4 * g + 2],
