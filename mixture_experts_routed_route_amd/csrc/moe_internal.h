@@ -21,9 +21,13 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // each): tpw = 4 (one row per chunk) for long prompts over at most 256
 // experts, else 1 (up to kRouteShortT tokens a 64-token block would leave
 // most CUs idle; above 256 experts four tokens' logits do not fit a lane's
-// registers).
+// registers). With tpw = 4, k <= 16 and at most 256 experts a wave ranks its
+// four tokens at once, 16 lanes each; otherwise one after another on all
+// 64 lanes (fewer instructions per token, more per wave).
 constexpr int kChunk = 64;
 constexpr int kRouteShortT = 2048;
+constexpr int kRouteGroupK = 16;
+inline bool route_grouped(int E, int k) { return E <= 256 && k <= kRouteGroupK; }
 inline int route_tpw(int T, int E) { return (T <= kRouteShortT || E > 256) ? 1 : 4; }
 // The single-block plan kernel takes prompts of at most kChunk tokens and
 // kPlanSmallPairs (token, choice) pairs, held in LDS, over at most 256

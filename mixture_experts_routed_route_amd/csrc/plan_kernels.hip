@@ -27,6 +27,36 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float(b);
 }
 
+// One step of a wave-wide max of 64-bit values through DPP (a lane reads
+// another lane's registers in the VALU, no LDS round trip): lanes of the
+// rows in ROWMASK take the larger of their value and the one CTRL routes to
+// them; the others keep theirs.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Max of v over the 64 lanes, returned in every lane (a scalar): lane pairs
+// xor 1 and xor 2 within quads, then the half-row and row mirrors (each lane
+// then holds its 16-lane row's max), then row 0 into row 1 and row 2 into
+// row 3 (row_bcast:15), and row 1 into rows 2 and 3 (row_bcast:31): lane 63
+// holds the max of all four rows.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step<0xB1, 0xF>(v);    // quad_perm [1, 0, 3, 2]
+  v = dpp_max_step<0x4E, 0xF>(v);    // quad_perm [2, 3, 0, 1]
+  v = dpp_max_step<0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);   // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+  v = dpp_max_step<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Number of lanes whose predicate holds, over the wave.
 __device__ __forceinline__ int wave_count(bool pred) {
   return __popcll(__ballot(pred));
@@ -48,6 +78,16 @@ __device__ __forceinline__ int route_wave_tokens(
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sh_hist) {
   const int lane = threadIdx.x & 63;
   int nan_count = 0;
+  // every token's logits are loaded before the first is ranked: one memory
+  // round trip per wave, not one per token
+  float lg[TPW][PER];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = lane + 64 * p;
+      lg[i][p] = (tbase + i < T && e < E) ? logits[(size_t)(tbase + i) * E + e] : 0.f;
+    }
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int t = tbase + i;
@@ -58,7 +98,7 @@ __device__ __forceinline__ int route_wave_tokens(
     for (int p = 0; p < PER; ++p) {
       const int e = lane + 64 * p;
       valid[p] = e < E;
-      const float l = valid[p] ? logits[(size_t)t * E + e] : 0.f;
+      const float l = lg[i][p];
       key[p] = order_key(l);
       nan_count += (valid[p] && l != l) ? 1 : 0;
     }
@@ -77,13 +117,7 @@ __device__ __forceinline__ int route_wave_tokens(
                            (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * p));
         if (valid[p] && !sel[p] && v > best) best = v;
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)best, off);
-        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        best = o > best ? o : best;
-      }
+      best = wave_max_u64(best);
       const int ew = (int)(0xFFFFFFFFu - (uint32_t)best);   // wave-uniform
       const uint32_t kw = (uint32_t)(best >> 32);
       if (jr == 0) top = kw;
@@ -124,6 +158,95 @@ __device__ __forceinline__ int route_wave_tokens(
   return nan_count;
 }
 
+// Max of v over the 16 lanes of each DPP row (lanes 16 g .. 16 g + 15),
+// in every lane of the row.
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+  v = dpp_max_step<0xB1, 0xF>(v);    // quad_perm [1, 0, 3, 2]
+  v = dpp_max_step<0x4E, 0xF>(v);    // quad_perm [2, 3, 0, 1]
+  v = dpp_max_step<0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);   // row_mirror
+  return v;
+}
+
+// The same selection and weights for four tokens at once: token tbase + g
+// takes the 16 lanes of row g (lanes 16 g .. 16 g + 15), P16 = ceil(E / 16)
+// logits per lane (expert lane % 16 + 16 p), so one round of the arg-max is
+// a 16-lane reduction inside a DPP row and the four tokens' rounds share
+// every instruction. Needs E <= 16 P16 <= 256 and k <= 16 (lane 16 g + j
+// keeps round j). Same results as route_wave_tokens.
+template <int P16>
+__device__ __forceinline__ int route_group_tokens(
+    const float* __restrict__ logits, int T, int E, int k, int tbase,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sh_hist) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int t = tbase + (lane >> 4);
+  const bool tv = t < T;   // uniform in the row
+  uint32_t key[P16];
+  bool valid[P16], sel[P16];
+  int nan_count = 0;
+#pragma unroll
+  for (int p = 0; p < P16; ++p) {
+    const int e = l16 + 16 * p;
+    valid[p] = tv && e < E;
+    const float l = valid[p] ? logits[(size_t)t * E + e] : 0.f;
+    key[p] = order_key(l);
+    sel[p] = false;
+    nan_count += wave_count(valid[p] && l != l);
+  }
+  uint32_t my_key = 0u, top = 0u;
+  int my_e = 0;
+  for (int jr = 0; jr < k; ++jr) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int p = 0; p < P16; ++p) {
+      const uint64_t v = ((uint64_t)key[p] << 32) |
+                         (uint64_t)(0xFFFFFFFFu - (uint32_t)(l16 + 16 * p));
+      if (valid[p] && !sel[p] && v > best) best = v;
+    }
+    best = row_max_u64(best);
+    const int ew = (int)(0xFFFFFFFFu - (uint32_t)best);   // uniform in the row
+    const uint32_t kw = (uint32_t)(best >> 32);
+    if (jr == 0) top = kw;
+#pragma unroll
+    for (int p = 0; p < P16; ++p)
+      if (l16 + 16 * p == ew) sel[p] = true;
+    if (l16 == jr) { my_key = kw; my_e = ew; }
+  }
+  const double l0 = (double)key_value(top);
+  const double ex = l16 < k ? exp((double)key_value(my_key) - l0) : 0.0;
+  // the sum in rank order, the same in every lane of the row
+  double sum = 0.0;
+  const int row0 = lane & 48;
+  for (int j = 0; j < k; ++j) sum += __shfl(ex, row0 + j);
+  if (tv && l16 < k) {
+    ids[(size_t)t * k + l16] = my_e;
+    w[(size_t)t * k + l16] = (float)(ex / sum);
+    atomicAdd(&sh_hist[my_e], 1);
+  }
+  return nan_count;
+}
+
+// Histogram rows of 64 tokens from the grouped router: 16 waves x 4 tokens.
+template <int P16>
+__global__ __launch_bounds__(1024) void route_hist_group_kernel(
+    const float* __restrict__ logits, int T, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ hist) {
+  extern __shared__ int32_t sh_hist[];   // E + 1
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x;
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_hist[e] = 0;
+  __syncthreads();
+  const int nan_count = route_group_tokens<P16>(logits, T, E, k, chunk * 64 + wave * 4,
+                                                ids, w, sh_hist);
+  if (lane == 0 && nan_count) atomicAdd(&sh_hist[E], nan_count);
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += blockDim.x)
+    hist[(size_t)chunk * (E + 1) + e] = sh_hist[e];
+}
+
 // Block = 16 waves x TPW tokens; the block's histogram row
 // hist[block, 0..E-1] counts its tokens' choices per expert, and
 // hist[block, E] their NaN logits.
@@ -152,6 +275,19 @@ hipError_t launch_route_hist(const float* logits, int T, int E, int k,
   if (tpw != 1 && tpw != 4) return hipErrorInvalidValue;
   const int NR = (T + 16 * tpw - 1) / (16 * tpw);
   const size_t sh = (size_t)(E + 1) * sizeof(int32_t);
+  if (tpw == 4 && route_grouped(E, k)) {
+    const int p16 = (E + 15) / 16;
+#define MOE_ROUTE_G(P)                                                              \
+    hipLaunchKernelGGL((route_hist_group_kernel<P>), dim3(NR), dim3(1024), sh, s,   \
+                       logits, T, E, k, ids, w, hist)
+    if (p16 <= 1) MOE_ROUTE_G(1);
+    else if (p16 <= 2) MOE_ROUTE_G(2);
+    else if (p16 <= 4) MOE_ROUTE_G(4);
+    else if (p16 <= 8) MOE_ROUTE_G(8);
+    else MOE_ROUTE_G(16);
+#undef MOE_ROUTE_G
+    return hipGetLastError();
+  }
   const int per = (E + 63) / 64;
 #define MOE_ROUTE(P, TPW)                                                          \
   hipLaunchKernelGGL((route_hist_kernel<P, TPW>), dim3(NR), dim3(1024), sh, s,     \
@@ -374,8 +510,18 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
   for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
   if (threadIdx.x < 4) red[threadIdx.x] = 0;
   __syncthreads();
-  // route: 16 waves x 4 tokens
-  const int nan_count = route_wave_tokens<PER, 4>(logits, T, E, k, wave * 4, sh_ids, sh_w, sh_hist);
+  // route: PER > 0: a wave ranks one token at a time on all 64 lanes, one
+  // token per wave up to 16 tokens, else 4 per wave; PER < 0 (more than 16
+  // tokens): four tokens per wave at once, 16 lanes and -PER logits a lane
+  int nan_count;
+  if constexpr (PER > 0) {
+    if (T <= 16)
+      nan_count = route_wave_tokens<PER, 1>(logits, T, E, k, wave, sh_ids, sh_w, sh_hist);
+    else
+      nan_count = route_wave_tokens<PER, 4>(logits, T, E, k, wave * 4, sh_ids, sh_w, sh_hist);
+  } else {
+    nan_count = route_group_tokens<-PER>(logits, T, E, k, wave * 4, sh_ids, sh_w, sh_hist);
+  }
   if (lane == 0 && nan_count) atomicAdd(&sh_hist[E], nan_count);
   __syncthreads();
   const int np = T * k;
@@ -472,7 +618,14 @@ hipError_t launch_plan_small(const float* logits, int T, int E, int k,
   hipLaunchKernelGGL((plan_small_kernel<P>), dim3(1), dim3(1024), 0, s, logits, T, \
                      E, k, n_shared, limit, ids, w, total, counts, offsets,     \
                      stats, slot, tok2pair, pair_token, pair_w)
-  if (per <= 1) MOE_PLAN_SMALL(1);
+  if (T > 16 && route_grouped(E, k)) {
+    const int p16 = (E + 15) / 16;
+    if (p16 <= 1) MOE_PLAN_SMALL(-1);
+    else if (p16 <= 2) MOE_PLAN_SMALL(-2);
+    else if (p16 <= 4) MOE_PLAN_SMALL(-4);
+    else if (p16 <= 8) MOE_PLAN_SMALL(-8);
+    else MOE_PLAN_SMALL(-16);
+  } else if (per <= 1) MOE_PLAN_SMALL(1);
   else if (per <= 2) MOE_PLAN_SMALL(2);
   else MOE_PLAN_SMALL(4);
 #undef MOE_PLAN_SMALL
