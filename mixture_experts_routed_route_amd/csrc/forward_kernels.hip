@@ -186,18 +186,6 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
           dst[1] = row0;
           dst[2] = rows;
           dst[3] = pstart;
-          int32_t* tok = one ? a.sk1_tok : a.sk4_tok;
-          if (tok) {
-            // the group's x rows for the stream tile, clamped to its last
-            tok += (size_t)kStreamTokRows * slot;
-            for (int t0 = 0; t0 < (one ? 16 : kStreamTokRows); t0 += 16) {
-              int tk[16];
-#pragma unroll
-              for (int t = 0; t < 16; ++t) tk[t] = a.pair_token[pstart + min(t0 + t, rows - 1)];
-#pragma unroll
-              for (int t = 0; t < 16; ++t) tok[t0 + t] = tk[t];
-            }
-          }
         }
       }
       a.fat_slot[e] = fat ? pf : -1;
@@ -206,6 +194,23 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
     c1 += t1;
     c4 += t4;
     cf += tf;
+  }
+  if (a.sk1_tok) {
+    // The groups' x rows for the stream tile (a group's rows, clamped to its
+    // last), one row per thread over all groups: one round trip for the
+    // group entries written above, one for the pair list.
+    __syncthreads();   // the group entries are visible to the whole block
+    const int r1 = c1 * 16, r4 = c4 * kStreamTokRows;
+    for (int i = threadIdx.x; i < r1 + r4; i += blockDim.x) {
+      const bool one = i < r1;
+      const int j = one ? i : i - r1;
+      const int slot = one ? j >> 4 : j / kStreamTokRows;
+      const int t = one ? j & 15 : j - slot * kStreamTokRows;
+      const int32_t* g = (one ? a.sk1 : a.sk4) + 4 * slot;
+      const int rows = g[2], pstart = g[3];
+      (one ? a.sk1_tok : a.sk4_tok)[(size_t)kStreamTokRows * slot + t] =
+          a.pair_token[pstart + min(t, rows - 1)];
+    }
   }
   if (threadIdx.x == 0) {
     a.meta[kMetaFullTiles] = n_tiles;
