@@ -12,6 +12,9 @@ listed below; all are pinned by tests in ``tests/test_oracle_*.py``:
 
   route / limit / plan / expert / layer / decode   pinned (brute force,
   closed forms, invariants, numpy library routines).
+  router_logits / router_stats   pinned (a hand-worked product, one-hot rows,
+  closed forms for equal logits and for two experts, a balanced first choice,
+  subset enumeration on tiny inputs).
   The pages' own drop shares and speedups come from trained routers and
   other systems: parity unpinned (no input here reproduces them).
 """
@@ -65,6 +68,8 @@ def lib():
                                 vp]
         L.orc_decode.argtypes = [vp, vp, i32, i64, i64, i64, vp]
         L.orc_decode_f16.argtypes = [vp, i64, vp]
+        L.orc_router_logits.argtypes = [i64, i64, i32, vp, i32, vp, vp]
+        L.orc_router_stats.argtypes = [i64, i32, i32, vp, dbl, vp, vp]
         L.orc_num_threads.restype = i32
         _lib = L
     return _lib
@@ -107,6 +112,35 @@ def route(logits, k: int):
     if rc != 0:
         raise ValueError(f"orc_route failed ({rc})")
     return ids, w
+
+
+def router_logits(x, w_router, dtype: str) -> np.ndarray:
+    """x [T, D] . w_router [E, D]^T in float64 over the stored values."""
+    xa = _np(x)
+    wa = _np(w_router)
+    T, D = xa.shape
+    E = wa.shape[0]
+    out = np.zeros((T, E))
+    rc = lib().orc_router_logits(T, D, E, _p(xa), DT[dtype], _p(wa), _p(out))
+    if rc != 0:
+        raise ValueError(f"orc_router_logits failed ({rc})")
+    return out
+
+
+ROUTER_STATS = ("kept_mass", "want_k", "z_loss", "balance", "aux")
+
+
+def router_stats(logits, k: int, z_weight: float = 1e-3):
+    """({kept_mass, want_k, z_loss, balance, aux} in float64, want per token)."""
+    lg = np.ascontiguousarray(_np(logits), dtype=np.float32)
+    T, E = lg.shape
+    out = np.zeros(5)
+    want = np.zeros(T, np.int32)
+    rc = lib().orc_router_stats(T, E, k, _p(lg), float(z_weight), _p(out),
+                                _p(want))
+    if rc != 0:
+        raise ValueError(f"orc_router_stats failed ({rc})")
+    return dict(zip(ROUTER_STATS, out.tolist())), want
 
 
 def limit(T: int, E: int, k: int, cf: float) -> int:

@@ -17,6 +17,11 @@ pin each other:
   pairs not chosen or dropped, i.e. the single padded rectangle of mini-AGI
   PR #4 (minagi/pool.py, `experts()`), whose maths the grouped path must
   reproduce.
+* ``router_stats`` recomputes the routing statistics of mini-AGI PR #3
+  (minagi/pool.py, `requested(scores)`) with Python floats: the experts a
+  token "wants" by enumerating every subset of experts (the smallest size
+  of a subset holding 0.9 of the mass), the first choices by a counting
+  dictionary, the log-sum-exp with ``math.fsum``.
 """
 
 from __future__ import annotations
@@ -96,3 +101,41 @@ def dense_layer(X, Wg, Wu, Wd, ids, w, keep, c, n_shared=0):
     for s in range(n_shared):
         Y += expert_dense(X, Wg[E + s], Wu[E + s], Wd[E + s], c)
     return Y
+
+
+def router_stats(logits: np.ndarray, k: int, z_weight: float):
+    """(dict of the five statistics, want per token); tiny E only (2^E)."""
+    from itertools import combinations
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    firsts = {}
+    kept = want = zsum = 0.0
+    mean_p = [0.0] * E
+    wants = []
+    for t in range(T):
+        row = [float(v) for v in lg[t]]
+        m = max(row)
+        ex = [math.exp(v - m) for v in row]
+        tot = math.fsum(ex)
+        p = [v / tot for v in ex]
+        lse = m + math.log(tot)
+        zsum += lse * lse
+        order = sorted(range(E), key=lambda e: (-row[e], e))
+        kept += math.fsum(p[e] for e in order[:k])
+        firsts[order[0]] = firsts.get(order[0], 0) + 1
+        for e in range(E):
+            mean_p[e] += p[e] / T
+        need = E
+        for size in range(1, E + 1):
+            if any(math.fsum(p[e] for e in sub) >= 0.9
+                   for sub in combinations(range(E), size)):
+                need = size
+                break
+        wants.append(need)
+        want += need
+    balance = E * math.fsum((firsts.get(e, 0) / T) * mean_p[e]
+                            for e in range(E))
+    z = zsum / T
+    return (dict(kept_mass=kept / T, want_k=want / T, z_loss=z,
+                 balance=balance, aux=balance + z_weight * z),
+            np.array(wants, np.int32))

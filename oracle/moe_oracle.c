@@ -23,6 +23,14 @@
  *   combine  y[t] = sum over kept pairs of weight * expert output; a dropped
  *            pair adds nothing (the weights are filtered by `keep` after they
  *            were normalised, mini-AGI PR #4, minagi/pool.py).
+ *   router   logits = x Wr^T, the linear map from d_model to the experts
+ *            whose output `requested(scores)` ranks, and the statistics that
+ *            function keeps beside the routing: the top-k mass before
+ *            renormalisation, the number of experts the router wants (the
+ *            fewest holding 90 % of the softmax mass), and the auxiliary loss
+ *            (balance term plus z-loss weighted by z_weight) (mini-AGI PR #3,
+ *            minagi/pool.py, `requested(scores)` and the `__init__` signature
+ *            with z_weight=1e-3).
  *
  * Readings where the pages leave a step open (all listed in the design notes):
  *   - top-k by logits (softmax is monotone), ties to the lower expert index,
@@ -32,6 +40,9 @@
  *   - a shared expert (index E) sees every token with weight 1, never drops;
  *   - 4-bit weights: two's-complement nibbles, low nibble = even K index,
  *     one fp16 scale per 32 consecutive K values of an output row, value q*s.
+ *   - router statistics: `want` is counted per token (largest p first, the
+ *     first count whose running sum is >= 0.9) and averaged over tokens; the
+ *     balance term's first choice is rank 0 of the top-k rule above.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC moe_oracle.c -o liboracle.so -lm
  */
@@ -343,6 +354,135 @@ int orc_layer(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
         free(yp);
     }
     return 0;
+}
+
+/* ---- router logits and routing statistics ------------------------------ */
+
+/*
+ * logits[t, e] = sum_d x[t, d] * Wr[e, d], in double over the exactly decoded
+ * inputs (x [T, D] and Wr [E, D] of one dense dtype). The pages route the
+ * output of this map (mini-AGI PR #3, minagi/pool.py, `requested(scores)`).
+ */
+int orc_router_logits(int64_t T, int64_t D, int E, const void *x, int dtype,
+                      const void *wr, double *out)
+{
+    if (T < 0 || D < 1 || E < 1 || dtype < ORC_F32 || dtype > ORC_F16)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                s += dense_value(x, dtype, (size_t)(t * D + d)) *
+                     dense_value(wr, dtype, (size_t)((int64_t)e * D + d));
+            out[t * E + e] = s;
+        }
+    return 0;
+}
+
+static int cmp_desc(const void *a, const void *b)
+{
+    double x = *(const double *)a, y = *(const double *)b;
+    return (x < y) - (x > y);
+}
+
+/*
+ * Statistics of one routing call over the logits it ranked (mini-AGI PR #3,
+ * minagi/pool.py, `requested(scores)`), each token's p = softmax of its E
+ * logits:
+ *   out[0] kept mass: mean over tokens of the mass of p on the k chosen
+ *          experts, taken before the k weights are renormalised;
+ *   out[1] want_k: mean over tokens of the fewest experts whose p, largest
+ *          first, add up to at least 0.9 (want_t[t] per token);
+ *   out[2] z loss: mean over tokens of logsumexp(logits[t])^2;
+ *   out[3] balance: E * sum_e frac_e * mean_t p[t, e], frac_e = share of the
+ *          tokens whose first choice is e;
+ *   out[4] aux = balance + z_weight * z loss.
+ * The chosen experts and the first choice follow orc_route's rank rule.
+ * T == 0 gives zeros. NaN logits: -2.
+ */
+int orc_router_stats(int64_t T, int E, int k, const float *logits,
+                     double z_weight, double *out, int32_t *want_t)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E)
+        return -1;
+    for (int i = 0; i < 5; ++i)
+        out[i] = 0.0;
+    if (T == 0)
+        return 0;
+    int32_t *ids = malloc((size_t)T * k * sizeof *ids);
+    double *w = malloc((size_t)T * k * sizeof *w);
+    double *p = malloc((size_t)T * E * sizeof *p);
+    double *kept = malloc((size_t)T * sizeof *kept);
+    double *z = malloc((size_t)T * sizeof *z);
+    int32_t *need = want_t ? want_t : malloc((size_t)T * sizeof *need);
+    if (!ids || !w || !p || !kept || !z || !need) {
+        free(ids); free(w); free(p); free(kept); free(z);
+        if (!want_t)
+            free(need);
+        return -4;
+    }
+    int rc = orc_route(T, E, k, logits, ids, w);
+    if (rc == 0) {
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const float *l = logits + t * E;
+            double *pt = p + t * E;
+            double m = (double)l[0];
+            for (int e = 1; e < E; ++e)
+                if ((double)l[e] > m)
+                    m = (double)l[e];
+            double s = 0.0;
+            for (int e = 0; e < E; ++e)
+                s += exp((double)l[e] - m);
+            for (int e = 0; e < E; ++e)
+                pt[e] = exp((double)l[e] - m) / s;
+            double lse = m + log(s);
+            z[t] = lse * lse;
+            double km = 0.0;
+            for (int j = 0; j < k; ++j)
+                km += pt[ids[t * k + j]];
+            kept[t] = km;
+            double *sorted = malloc((size_t)E * sizeof *sorted);
+            memcpy(sorted, pt, (size_t)E * sizeof *sorted);
+            qsort(sorted, (size_t)E, sizeof *sorted, cmp_desc);
+            double run = 0.0;
+            int m_need = E;
+            for (int i = 0; i < E; ++i) {
+                run += sorted[i];
+                if (run >= 0.9) {
+                    m_need = i + 1;
+                    break;
+                }
+            }
+            free(sorted);
+            need[t] = m_need;
+        }
+        double sk = 0.0, sw = 0.0, sz = 0.0, bal = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            sk += kept[t];
+            sw += (double)need[t];
+            sz += z[t];
+        }
+        for (int e = 0; e < E; ++e) {
+            double mp = 0.0;
+            int64_t first = 0;
+            for (int64_t t = 0; t < T; ++t) {
+                mp += p[t * E + e];
+                first += ids[t * k] == e;
+            }
+            bal += ((double)first / (double)T) * (mp / (double)T);
+        }
+        out[0] = sk / (double)T;
+        out[1] = sw / (double)T;
+        out[2] = sz / (double)T;
+        out[3] = (double)E * bal;
+        out[4] = out[3] + z_weight * out[2];
+    }
+    free(ids); free(w); free(p); free(kept); free(z);
+    if (!want_t)
+        free(need);
+    return rc;
 }
 
 int orc_num_threads(void)

@@ -370,3 +370,111 @@ def test_q4_layer_matches_dense_bruteforce():
     ref = brute.dense_layer(X, Wg, Wu, Wd, ids, w, pl["keep"].astype(bool),
                             7.0)
     np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------ router and statistics ---
+
+def test_router_logits_hand_worked_product():
+    # every value a small dyadic number, exact in bf16 and in the product
+    x = torch.tensor([[1.0, 2.0], [3.0, -1.0]], dtype=torch.bfloat16)
+    w = torch.tensor([[0.5, 0.25], [-1.0, 2.0], [4.0, 0.0]],
+                     dtype=torch.bfloat16)
+    out = oracle.router_logits(x, w, "bf16")
+    assert out.tolist() == [[1.0, 3.0, 4.0], [1.25, -5.0, 12.0]]
+
+
+def test_router_logits_one_hot_rows_read_columns():
+    D, E = 40, 7
+    w = (torch.randn(E, D, generator=torch.Generator().manual_seed(3))
+         ).to(torch.float16)
+    x = torch.eye(D, dtype=torch.float16)[[0, 5, 39]]
+    out = oracle.router_logits(x, w, "f16")
+    exact = oracle.decode_f16_bits(w.view(torch.int16).numpy().view(np.uint16))
+    np.testing.assert_array_equal(out, exact[:, [0, 5, 39]].T)
+
+
+@pytest.mark.parametrize("E,k", [(16, 4), (256, 8), (5, 5)])
+def test_router_stats_equal_logits(E, k):
+    # p = 1/E everywhere: top-k mass k/E, the 0.9 mass needs ceil(0.9 E)
+    # experts, lse = ln E, and every first choice is expert 0 (lower index),
+    # so the balance term is E * 1 * (1/E) = 1
+    T = 3
+    st, want = oracle.router_stats(np.full((T, E), 0.75, np.float32), k, 0.5)
+    lse = 0.75 + math.log(E)
+    assert st["kept_mass"] == pytest.approx(k / E, rel=1e-14)
+    assert want.tolist() == [math.ceil(0.9 * E)] * T
+    assert st["z_loss"] == pytest.approx(lse * lse, rel=1e-14)
+    assert st["balance"] == pytest.approx(1.0, rel=1e-14)
+    assert st["aux"] == pytest.approx(1.0 + 0.5 * lse * lse, rel=1e-14)
+
+
+@pytest.mark.parametrize("delta", [0.5, 2.0, 2.3, 3.0])
+def test_router_stats_two_experts_closed_form(delta):
+    # logits (delta, 0): p0 = sigmoid(delta); one expert holds 0.9 of the
+    # mass iff p0 >= 0.9 (delta >= ln 9 = 2.197); lse = delta + ln(1 + e^-delta)
+    lg = np.array([[delta, 0.0]] * 4, np.float32)
+    d = float(np.float32(delta))
+    p0 = sigmoid(d)
+    st, want = oracle.router_stats(lg, 1, 1e-3)
+    assert st["kept_mass"] == pytest.approx(p0, rel=1e-14)
+    assert want.tolist() == [1 if p0 >= 0.9 else 2] * 4
+    lse = d + math.log1p(math.exp(-d))
+    assert st["z_loss"] == pytest.approx(lse * lse, rel=1e-14)
+    assert st["balance"] == pytest.approx(2.0 * p0, rel=1e-14)
+
+
+def test_router_stats_balanced_first_choice_gives_one():
+    # first choices spread evenly: frac_e = 1/E, and the mean probabilities
+    # sum to one whatever the logits, so the balance term is exactly 1
+    E, T = 8, 64
+    rng = np.random.default_rng(5)
+    lg = rng.normal(size=(T, E)).astype(np.float32)
+    lg[np.arange(T), np.arange(T) % E] += 20.0
+    st, _ = oracle.router_stats(lg, 2, 0.0)
+    assert st["balance"] == pytest.approx(1.0, rel=1e-13)
+    assert st["aux"] == st["balance"]
+    # all tokens on one expert: frac_0 = 1 and balance = E * mean p_0
+    lg2 = rng.normal(size=(T, E)).astype(np.float32)
+    lg2[:, 0] += 30.0
+    st2, want2 = oracle.router_stats(lg2, 2, 0.0)
+    p = np.exp(lg2.astype(np.float64) - lg2.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    assert st2["balance"] == pytest.approx(E * p[:, 0].mean(), rel=1e-13)
+    assert want2.tolist() == [1] * T
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_router_stats_match_subset_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    T, E, k = 9, 7, 3
+    lg = (rng.normal(size=(T, E)) * rng.uniform(0.3, 3.0)).astype(np.float32)
+    lg[0, 1] = lg[0, 4]          # a tie on the first row
+    st, want = oracle.router_stats(lg, k, 0.01)
+    bst, bwant = brute.router_stats(lg, k, 0.01)
+    assert want.tolist() == bwant.tolist()
+    for key in oracle.ROUTER_STATS:
+        assert st[key] == pytest.approx(bst[key], rel=1e-12), key
+
+
+def test_router_stats_large_logits_stay_finite():
+    # logits near 1000 overflow a naive exp; lse = 1000 + ln(1 + 2 + 4)
+    lg = np.array([[1000.0 + math.log(4.0), 1000.0 + math.log(2.0), 1000.0]],
+                  np.float32)
+    st, want = oracle.router_stats(lg, 1, 1.0)
+    l = lg.astype(np.float64)[0]
+    lse = l[2] + math.log(math.exp(l[0] - l[2]) + math.exp(l[1] - l[2]) + 1.0)
+    assert st["z_loss"] == pytest.approx(lse * lse, rel=1e-14)
+    # the f32 logits hold 1000 + ln 4 to 6e-5: ratios from the stored values
+    a, b = math.exp(l[0] - l[2]), math.exp(l[1] - l[2])
+    assert st["kept_mass"] == pytest.approx(a / (a + b + 1.0), rel=1e-13)
+    assert a / (a + b + 1.0) == pytest.approx(4.0 / 7.0, rel=1e-4)
+    assert want.tolist() == [3]      # about 4/7 + 2/7 = 0.857 < 0.9
+
+
+def test_router_stats_empty_and_nan():
+    st, want = oracle.router_stats(np.zeros((0, 4), np.float32), 2)
+    assert list(st.values()) == [0.0] * 5 and want.size == 0
+    lg = np.zeros((2, 4), np.float32)
+    lg[1, 2] = np.nan
+    with pytest.raises(ValueError):
+        oracle.router_stats(lg, 2)

@@ -223,6 +223,23 @@ def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
     raise ValueError(f"no workload {n}")
 
 
+def make_router(T: int, D: int, E: int, k: int, dtype: str, *, seed: int = 0,
+                capacity_factor: float = 0.0, n_shared: int = 0,
+                spread: float = 0.0) -> dict:
+    """Inputs of the router map: x [T, D] ~ N(0, 1) and its weight [E, D]
+    with rows ~ N(0, s_e^2 / D), so each logit is about N(0, s_e^2). s_e = 1,
+    or with ``spread`` > 0 a seeded log-uniform factor exp(spread * U(-1, 1))
+    per expert, so a few wide experts win most first choices."""
+    g = _gen(seed)
+    x = as_dtype(_normal((T, D), 1.0, g), dtype)
+    scale = torch.ones(E, 1)
+    if spread > 0:
+        scale = torch.exp((torch.rand(E, 1, generator=g) * 2 - 1) * spread)
+    w = as_dtype(_normal((E, D), 1.0 / D ** 0.5, g) * scale, dtype)
+    return dict(T=T, D=D, E=E, k=k, dtype=dtype, x=x, w_router=w,
+                capacity_factor=capacity_factor, n_shared=n_shared)
+
+
 def flops_per_pair(D: int, F: int) -> int:
     """Multiply-adds counted as 2 flops: gate, up and down products."""
     return 6 * D * F
