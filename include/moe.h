@@ -182,6 +182,49 @@ moe_status moe_plan_get_views(const moe_plan *plan, moe_plan_views *out);
 
 void moe_plan_destroy(moe_plan *plan);
 
+/* --- router: logits + statistics + plan in one call ------------------- */
+
+/* Routing statistics of one call, device-resident, written asynchronously
+ * (mini-AGI PR #3, minagi/pool.py, `requested(scores)`; p = softmax of a
+ * token's logits over all E experts):
+ *   kept_mass  mean over tokens of the p mass on the k chosen experts,
+ *              before their weights are renormalised;
+ *   want_k     mean over tokens of the fewest experts whose p, largest
+ *              first, add up to at least 0.9 (counted per token, then
+ *              averaged);
+ *   z_loss     mean over tokens of logsumexp(logits[t])^2;
+ *   balance    E * sum_e frac_e * mean_t p[t, e], frac_e the share of tokens
+ *              whose first choice (rank 0) is e;
+ *   aux        balance + z_weight * z_loss.
+ * Means over T tokens; all zero when T == 0. */
+typedef struct {
+    float kept_mass, want_k, z_loss, balance, aux;
+    float reserved[3];
+} moe_route_stats;
+
+/* Bytes of device workspace moe_route needs (the plan's, then scratch for
+ * the statistics); 0 on invalid desc. */
+size_t moe_route_workspace_bytes(const moe_plan_desc *desc, int32_t D);
+
+/* The router and the plan in one call: logits[T, E] = x[T, D] . w_router[E,
+ * D]^T (x and w_router of one dtype, MOE_F32 / MOE_BF16 / MOE_F16; fp32
+ * accumulation) written to the caller's `logits` (f32, device), then the
+ * plan of moe_plan_create over those logits into `ws` (the handle refers into
+ * it as for moe_plan_create), then, if `stats` (device) or `token_want`
+ * (device int32 [T]) is non-NULL, the routing statistics of those logits and
+ * of the plan's choices. z_weight weighs the z-loss in `aux` (the pages'
+ * default is 1e-3); it must be finite. D must be a multiple of 8 in
+ * 8 .. 2^20; pointers
+ * 16-byte aligned, ws 256-byte aligned. Launches only; no host sync.
+ * Argument errors are found before any launch and leave every output
+ * untouched. The statistics are the same bits from run to run (fixed-order
+ * sums, no float atomics). */
+moe_status moe_route(const moe_plan_desc *desc, const void *x, int32_t x_dtype,
+                     const void *w_router, int32_t D, float z_weight,
+                     float *logits, moe_route_stats *stats,
+                     int32_t *token_want, void *ws, size_t ws_bytes,
+                     void *stream, moe_plan **out);
+
 /* --- forward: experts + combine --------------------------------------- */
 
 void moe_options_default(moe_options *opt);

@@ -10,6 +10,11 @@ fallback. If the library is not built, every call raises.
     plan = moe_plan_create(logits, k=8, capacity_factor=0.0)
     y = moe_forward(plan, x, w_gate, w_up, w_down)
 
+or, with the router map in the same call (logits = x . w_router^T and the
+routing statistics beside the plan):
+
+    plan, logits, stats = moe_route(x, w_router, k=8)
+
 Weights are torch tensors [E (+1 shared), F, D] / [E (+1), D, F] in x's dtype,
 or, for 4-bit block weights, ``(packed uint8 [.., N, K/2], scales fp16
 [.., N, K/32])`` pairs.
@@ -45,7 +50,10 @@ EXPORTED = (
     "moe_plan_get_views", "moe_plan_destroy", "moe_options_default",
     "moe_forward_workspace_bytes", "moe_forward", "moe_dequant_q4",
     "moe_phase_times", "moe_last_error", "moe_version",
+    "moe_route_workspace_bytes", "moe_route",
 )
+
+ROUTE_STATS = ("kept_mass", "want_k", "z_loss", "balance", "aux")
 
 
 class PlanDesc(ctypes.Structure):
@@ -124,6 +132,12 @@ def library(path: str = LIB_PATH):
     L.moe_phase_times.argtypes = [ctypes.POINTER(ctypes.c_double), i32,
                                   ctypes.POINTER(i64), i32]
     L.moe_phase_times.restype = i32
+    L.moe_route_workspace_bytes.argtypes = [ctypes.POINTER(PlanDesc), i32]
+    L.moe_route_workspace_bytes.restype = sz
+    L.moe_route.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, i32,
+                            ctypes.c_float, vp, vp, vp, vp, sz, vp,
+                            ctypes.POINTER(vp)]
+    L.moe_route.restype = i32
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_version.argtypes = []
@@ -219,6 +233,46 @@ def moe_plan_create(logits: torch.Tensor, k: int, capacity_factor: float = 0.0,
     _check(L.moe_plan_create(ctypes.byref(d), logits.data_ptr(), ws.data_ptr(),
                              nbytes, _stream(logits.device), ctypes.byref(h)))
     return Plan(h, ws, logits, d)
+
+
+def moe_route(x: torch.Tensor, w_router: torch.Tensor, k: int,
+              capacity_factor: float = 0.0, n_shared: int = 0,
+              z_weight: float = 1e-3, want_per_token: bool = False,
+              workspace: torch.Tensor | None = None):
+    """logits = x . w_router^T (f32 [T, E]), the plan over them, and the
+    routing statistics as a device f32 tensor [8] (kept_mass, want_k, z_loss,
+    balance, aux, 0, 0, 0). Returns (plan, logits, stats), plus the per-token
+    wanted counts (int32 [T]) when ``want_per_token``."""
+    L = library()
+    if x.dtype not in _TORCH_TO_MOE or x.dim() != 2:
+        raise ValueError("x must be a 2-D float32/bfloat16/float16 tensor")
+    if w_router.dtype != x.dtype or w_router.dim() != 2 \
+            or w_router.shape[1] != x.shape[1] or w_router.device != x.device:
+        raise ValueError("w_router must be [E, D] in x's dtype, on x's device")
+    x, w_router = x.contiguous(), w_router.contiguous()
+    T, D = x.shape
+    E = w_router.shape[0]
+    d = PlanDesc(T, E, int(k), int(n_shared), float(capacity_factor))
+    nbytes = L.moe_route_workspace_bytes(ctypes.byref(d), D)
+    if nbytes == 0:
+        raise MoeError(MOE_EINVAL, moe_last_error())
+    if workspace is not None and workspace.numel() >= nbytes:
+        ws = workspace
+    else:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    logits = torch.empty(T, E, dtype=torch.float32, device=x.device)
+    stats = torch.empty(8, dtype=torch.float32, device=x.device)
+    want = (torch.empty(T, dtype=torch.int32, device=x.device)
+            if want_per_token else None)
+    h = ctypes.c_void_p()
+    _check(L.moe_route(ctypes.byref(d), x.data_ptr(), _TORCH_TO_MOE[x.dtype],
+                       w_router.data_ptr(), D, float(z_weight),
+                       logits.data_ptr(), stats.data_ptr(),
+                       None if want is None else want.data_ptr(),
+                       ws.data_ptr(), nbytes, _stream(x.device),
+                       ctypes.byref(h)))
+    plan = Plan(h, ws, logits, d)
+    return (plan, logits, stats, want) if want_per_token else (plan, logits, stats)
 
 
 def moe_plan_stats_get(plan: Plan, options: Options | None = None) -> dict:
@@ -356,3 +410,4 @@ def moe_phase_times(reset: bool = True) -> tuple:
 # short aliases
 plan = moe_plan_create
 forward = moe_forward
+route = moe_route

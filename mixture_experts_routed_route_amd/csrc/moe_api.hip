@@ -280,6 +280,44 @@ bool weight_ok(const moe_weight& w, int wdt, std::string* why, const char* name)
 
 }  // namespace
 
+// The plan's kernels over `logits` into the workspace at b.
+moe_status launch_plan(const moe_plan_desc& d, const float* logits,
+                       const PlanLayout& L, char* b, int64_t limit,
+                       hipStream_t s) {
+  hipError_t e;
+  if (d.T >= 1 && d.T <= kChunk && (int64_t)d.T * d.k <= kPlanSmallPairs &&
+      d.E <= kPlanSmallE) {
+    // one chunk: route, scan and permute in one block
+    e = launch_plan_small(logits, d.T, d.E, d.k, d.n_shared, limit,
+                          (int32_t*)(b + L.ids), (float*)(b + L.w),
+                          (int32_t*)(b + L.total), (int32_t*)(b + L.counts),
+                          (int32_t*)(b + L.offsets), (int64_t*)(b + L.stats),
+                          (int32_t*)(b + L.slot), (int32_t*)(b + L.tok2pair),
+                          (int32_t*)(b + L.pair_token), (float*)(b + L.pair_w), s);
+    if (e != hipSuccess) return hip_fail(e, "plan kernel");
+  } else {
+    if (L.NC > 0) {
+      e = launch_route_hist(logits, d.T, d.E, d.k, (int32_t*)(b + L.ids),
+                            (float*)(b + L.w), (int32_t*)(b + L.hist), L.tpw, s);
+      if (e != hipSuccess) return hip_fail(e, "route kernel");
+    }
+    e = launch_scan((int32_t*)(b + L.hist), L.NR, d.T, d.E, d.k, d.n_shared,
+                    limit, (int32_t*)(b + L.total), (int32_t*)(b + L.counts),
+                    (int32_t*)(b + L.offsets), (int64_t*)(b + L.stats), s);
+    if (e != hipSuccess) return hip_fail(e, "scan kernel");
+    if (L.NC > 0) {
+      e = launch_permute((const int32_t*)(b + L.ids), (const float*)(b + L.w),
+                         (const int32_t*)(b + L.hist), 4 / L.tpw,
+                         (const int32_t*)(b + L.offsets), d.T, d.E, d.k,
+                         d.n_shared, limit, (int32_t*)(b + L.slot),
+                         (int32_t*)(b + L.tok2pair), (int32_t*)(b + L.pair_token),
+                         (float*)(b + L.pair_w), s);
+      if (e != hipSuccess) return hip_fail(e, "permute kernel");
+    }
+  }
+  return MOE_OK;
+}
+
 struct moe_plan {
   moe_plan_desc desc;
   int64_t limit;
@@ -326,36 +364,71 @@ moe_status moe_plan_create(const moe_plan_desc* desc, const float* logits,
   char* b = static_cast<char*>(ws);
   const moe_plan_desc& d = *desc;
   const int64_t limit = capacity_limit(d);
-  hipError_t e;
-  if (d.T >= 1 && d.T <= kChunk && (int64_t)d.T * d.k <= kPlanSmallPairs &&
-      d.E <= kPlanSmallE) {
-    // one chunk: route, scan and permute in one block
-    e = launch_plan_small(logits, d.T, d.E, d.k, d.n_shared, limit,
-                          (int32_t*)(b + L.ids), (float*)(b + L.w),
-                          (int32_t*)(b + L.total), (int32_t*)(b + L.counts),
-                          (int32_t*)(b + L.offsets), (int64_t*)(b + L.stats),
-                          (int32_t*)(b + L.slot), (int32_t*)(b + L.tok2pair),
-                          (int32_t*)(b + L.pair_token), (float*)(b + L.pair_w), s);
-    if (e != hipSuccess) return hip_fail(e, "plan kernel");
-  } else {
-  if (L.NC > 0) {
-    e = launch_route_hist(logits, d.T, d.E, d.k, (int32_t*)(b + L.ids),
-                          (float*)(b + L.w), (int32_t*)(b + L.hist), L.tpw, s);
-    if (e != hipSuccess) return hip_fail(e, "route kernel");
+  st = launch_plan(d, logits, L, b, limit, s);
+  if (st != MOE_OK) return st;
+  moe_plan* p = new (std::nothrow) moe_plan;
+  if (!p) return fail(MOE_EINVAL, "out of host memory");
+  p->desc = d;
+  p->limit = limit;
+  p->ws = b;
+  p->L = L;
+  *out = p;
+  return MOE_OK;
+}
+
+size_t moe_route_workspace_bytes(const moe_plan_desc* desc, int32_t D) {
+  std::string why;
+  if (!desc_ok(desc, &why)) { fail(MOE_EINVAL, "%s", why.c_str()); return 0; }
+  if (D < 8 || D % 8 || D > kRouterMaxD) {
+    fail(MOE_EINVAL, "D=%d must be a multiple of 8 in 8..%d", D, kRouterMaxD);
+    return 0;
   }
-  e = launch_scan((int32_t*)(b + L.hist), L.NR, d.T, d.E, d.k, d.n_shared,
-                  limit, (int32_t*)(b + L.total), (int32_t*)(b + L.counts),
-                  (int32_t*)(b + L.offsets), (int64_t*)(b + L.stats), s);
-  if (e != hipSuccess) return hip_fail(e, "scan kernel");
-  if (L.NC > 0) {
-    e = launch_permute((const int32_t*)(b + L.ids), (const float*)(b + L.w),
-                       (const int32_t*)(b + L.hist), 4 / L.tpw,
-                       (const int32_t*)(b + L.offsets), d.T, d.E, d.k,
-                       d.n_shared, limit, (int32_t*)(b + L.slot),
-                       (int32_t*)(b + L.tok2pair), (int32_t*)(b + L.pair_token),
-                       (float*)(b + L.pair_w), s);
-    if (e != hipSuccess) return hip_fail(e, "permute kernel");
-  }
+  return plan_layout(*desc).bytes + router_scratch_bytes(desc->T, desc->E);
+}
+
+moe_status moe_route(const moe_plan_desc* desc, const void* x, int32_t x_dtype,
+                     const void* w_router, int32_t D, float z_weight,
+                     float* logits, moe_route_stats* stats,
+                     int32_t* token_want, void* ws, size_t ws_bytes,
+                     void* stream, moe_plan** out) {
+  std::string why;
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!desc_ok(desc, &why)) return fail(MOE_EINVAL, "%s", why.c_str());
+  const moe_plan_desc& d = *desc;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16 && x_dtype != MOE_F16)
+    return fail(MOE_EUNSUPPORTED, "router dtype %d: f32, bf16 or f16 only", x_dtype);
+  if (D < 8 || D % 8 || D > kRouterMaxD)
+    return fail(MOE_EINVAL, "D=%d must be a multiple of 8 in 8..%d", D, kRouterMaxD);
+  if (!std::isfinite(z_weight)) return fail(MOE_EINVAL, "z_weight must be finite");
+  if (d.T > 0 && (!x || !w_router || !logits))
+    return fail(MOE_EINVAL, "x, w_router and logits must be non-NULL");
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits) ||
+      !aligned16(stats) || !aligned16(token_want) ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(MOE_EINVAL, "pointers must be 16-byte and ws 256-byte aligned");
+  const PlanLayout L = plan_layout(d);
+  const size_t need = L.bytes + router_scratch_bytes(d.T, d.E);
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "route workspace %zu bytes < %zu needed",
+                ws_bytes, need);
+  int dev;
+  DevInfo info;
+  moe_status st = device_info(&dev, &info);
+  if (st != MOE_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* b = static_cast<char*>(ws);
+  const int64_t limit = capacity_limit(d);
+  hipError_t e = launch_router_gemm(x, x_dtype, w_router, logits, d.T, D, d.E, s);
+  if (e != hipSuccess) return hip_fail(e, "router kernel");
+  st = launch_plan(d, logits, L, b, limit, s);
+  if (st != MOE_OK) return st;
+  if (stats || token_want) {
+    e = launch_router_stats(logits, (const int32_t*)(b + L.ids), d.T, d.E,
+                            d.k, token_want, b + L.bytes,
+                            reinterpret_cast<float*>(stats), z_weight, s);
+    if (e != hipSuccess) return hip_fail(e, "router statistics kernel");
   }
   moe_plan* p = new (std::nothrow) moe_plan;
   if (!p) return fail(MOE_EINVAL, "out of host memory");

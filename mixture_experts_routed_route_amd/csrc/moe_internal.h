@@ -63,6 +63,14 @@ enum Meta : int32_t { kMetaFullTiles = 0, kMetaSk1 = 1, kMetaSk4 = 2,
                       kMetaFat = 3, kMetaQueueGateUp = 8, kMetaQueueDown = 16,
                       kMetaCount = 24 };
 
+// Router GEMM: prompts of at most kRouterDotT tokens (and fp32 inputs) take
+// the dot-product kernel; longer ones the MFMA tile, 128 x 128 when that
+// gives at least kRouterBigTiles blocks, else 64 x 64.
+constexpr int kRouterDotT = 64;
+constexpr int kRouterBigTiles = 128;
+// d_model bound of the router: a 128-row tile's bytes stay below 2^31.
+constexpr int kRouterMaxD = 1 << 20;
+
 // ---- launchers (plan_kernels.hip) ---------------------------------------
 hipError_t launch_route_hist(const float* logits, int T, int E, int k,
                              int32_t* ids, float* w, int32_t* hist, int tpw,
@@ -165,5 +173,14 @@ hipError_t launch_combine(const void* ypair, int ypair_f16,
                           const int32_t* tok2pair, const float* topk_w,
                           const int32_t* offsets, int T, int D, int k,
                           int n_shared, int E, int ydt, void* y, hipStream_t s);
+
+// ---- router (router.hip) ---------------------------------------------------
+size_t router_scratch_bytes(int T, int E);
+hipError_t launch_router_gemm(const void* x, int xdt, const void* w,
+                              float* logits, int T, int D, int E,
+                              hipStream_t s);
+hipError_t launch_router_stats(const float* logits, const int32_t* ids, int T,
+                               int E, int k, int32_t* want_out, void* scratch,
+                               float* stats, float z_weight, hipStream_t s);
 
 }  // namespace moe

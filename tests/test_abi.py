@@ -130,3 +130,53 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         moe.moe_dequant_q4(torch.zeros(4, 16, dtype=torch.int8),
                            torch.zeros(4, 1, dtype=torch.float16))
+
+
+def _route(lib, d, x=0x1000, xdt=None, w=0x2000, D=128, zw=1e-3,
+           logits=0x3000, stats=0x4000, want=None, ws=0x10000,
+           nbytes=1 << 20, out=True):
+    h = ctypes.c_void_p()
+    return lib.moe_route(ctypes.byref(d), x,
+                         moe.MOE_BF16 if xdt is None else xdt, w, D, zw,
+                         logits, stats, want, ws, nbytes, None,
+                         ctypes.byref(h) if out else None), h
+
+
+def test_route_validation(lib):
+    d = _desc()
+    need = lib.moe_route_workspace_bytes(ctypes.byref(d), 128)
+    assert need > lib.moe_plan_workspace_bytes(ctypes.byref(d)) and need % 256 == 0
+    assert lib.moe_route_workspace_bytes(ctypes.byref(d), 12) == 0      # D % 8
+    assert lib.moe_route_workspace_bytes(ctypes.byref(_desc(k=0)), 128) == 0
+    bad = [dict(xdt=moe.MOE_Q4B32), dict(D=0), dict(D=100), dict(zw=float("nan")),
+           dict(zw=float("inf")), dict(x=None), dict(w=None), dict(logits=None),
+           dict(x=0x1004), dict(logits=0x3008), dict(stats=0x4004),
+           dict(want=0x5002), dict(ws=None), dict(ws=0x10010), dict(out=False)]
+    for kw in bad:
+        st, h = _route(lib, d, nbytes=need, **kw)
+        want = moe.MOE_EUNSUPPORTED if "xdt" in kw else moe.MOE_EINVAL
+        assert st == want, kw
+        assert not h.value
+    st, _ = _route(lib, d, nbytes=need - 1)
+    assert st == moe.MOE_EWORKSPACE
+    st, _ = _route(lib, _desc(E=0), nbytes=need)
+    assert st == moe.MOE_EINVAL
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0,
+                    reason="checks the no-device error path")
+def test_route_no_device_reports_ehip(lib):
+    d = _desc()
+    need = lib.moe_route_workspace_bytes(ctypes.byref(d), 128)
+    st, h = _route(lib, d, nbytes=need)
+    assert st == moe.MOE_EHIP and not h.value
+
+
+def test_python_route_rejects_bad_tensors():
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.moe_route(x, torch.zeros(8, 16, dtype=torch.float16), 2)
+    with pytest.raises(ValueError):
+        moe.moe_route(x, torch.zeros(8, 12, dtype=torch.bfloat16), 2)
+    with pytest.raises(ValueError):
+        moe.moe_route(x.view(-1), torch.zeros(8, 16, dtype=torch.bfloat16), 2)
