@@ -12,7 +12,10 @@ Default workload: the 13,312-token prompt over 256 4-bit experts
 (d_model 4096, expert d_ff 2048, top-8, Zipf(1.1) popularity), the size at
 which the dequant-once FP16 route of Strata PR #4366 was measured.
 ``--config N`` selects another named workload (1..7; 6 and 7 are
-decode-shaped calls of 1..8 tokens, ``--T``).
+decode-shaped calls of 1..8 tokens, ``--T``). ``--router`` times moe_route
+instead (router map x . Wr^T, plan and routing statistics) on the same
+prompt's router: 13,312 tokens (``--T``), d_model 4096, 256 experts, top-8,
+fp16.
 
 Prints one JSON line: the metric (routed-expert TFLOP/s, 6 D F flops per
 kept pair), pairs/s, the dominant kernel's roofline (HIP events around its
@@ -44,7 +47,8 @@ KERNEL_SRC = {"gateup_full": "gemm_full.hip", "down_full": "gemm_full.hip",
               "down_splitk": "forward_kernels.hip",
               "dequant_once": "forward_kernels.hip",
               "combine": "forward_kernels.hip",
-              "classify": "forward_kernels.hip"}
+              "classify": "forward_kernels.hip",
+              "router_gemm": "router.hip"}
 
 
 def parse():
@@ -65,6 +69,8 @@ def parse():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (K more steps, each after "
                          "a 1 GiB write that evicts L2 and the 256 MB MALL)")
+    ap.add_argument("--router", action="store_true",
+                    help="time moe_route (router map + plan + statistics)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one plain elementwise copy of MIB MiB "
                          "(dst = src * 1 in f32: MIB MiB read, MIB MiB "
@@ -111,6 +117,8 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.router:
+        return bench_router(args, dev, torch, moe, W)
     wl = W.config(args.config, capacity_factor=args.capacity_factor, T=args.T,
                   pairs_per_expert=args.pairs_per_expert)
     T, D, F, E, k, ns = (wl[n] for n in ("T", "D", "F", "E", "k", "n_shared"))
@@ -301,6 +309,97 @@ def main():
         "hardware": hardware(torch),
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_router(args, dev, torch, moe, W):
+    """moe_route on the long prompt's router: logits = x . Wr^T (fp16, f32
+    accumulation), the plan over them and the routing statistics."""
+    T = args.T or 13312
+    D, E, k = 4096, 256, 8
+    wl = W.make_router(T, D, E, k, "f16", seed=0, spread=0.5)
+    x, w = wl["x"].to(dev), wl["w_router"].to(dev)
+    flags = 0 if args.no_phase_events else moe.MOE_OPT_PHASE_EVENTS
+    nbytes = moe.moe_route_workspace_bytes_for(T, E, k, D)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    stats = torch.empty(8, dtype=torch.float32, device=dev)
+
+    def step():
+        return moe.moe_route(x, w, k, workspace=ws, flags=flags,
+                             logits=logits, stats=stats)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.moe_phase_times(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flops = 2.0 * T * D * E
+    roofline = None
+    if flags:
+        phase_ms, calls = moe.moe_phase_times(reset=True)
+        per = {n: phase_ms[n] / max(calls, 1)
+               for n in ("router_gemm", "route_plan", "router_stats")}
+        gemm_ms = per["router_gemm"]
+        # x read once, Wr once, logits written once
+        amount = T * D * 2 + E * D * 2 + T * E * 4
+        achieved = amount / (gemm_ms * 1e-3) / 1e9
+        roofline = {"kernel": "router_gemm", "bound": "hbm",
+                    "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": load_traffic("long_prompt_router", "router_gemm"),
+                    "algorithmic_per_launch": amount,
+                    "avg_launch_ms": round(gemm_ms, 4),
+                    "mfma_TFLOPs": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+                    "phase_ms_per_step": {n: round(v, 4) for n, v in per.items()}}
+    st = stats.cpu().numpy().tolist()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_router(wl, args.cpu_seconds)
+    out = {
+        "metric": "router TFLOP/s (2*D*E per token; router map, plan and "
+                  "routing statistics timed together)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded; workloads.make_router)",
+        "config": {"workload": "long_prompt_router", "T": T, "d_model": D,
+                   "experts": E, "top_k": k, "parallelism": "single GPU"},
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "route_stats": dict(zip(moe.ROUTE_STATS, st[:5])),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "hardware": hardware(torch),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_router(wl, target_s):
+    """The oracle's router map and statistics on the first tokens, doubling
+    until about target_s seconds; TFLOP/s of the map (2 D E per token)."""
+    import oracle
+
+    T, D, E, k = wl["T"], wl["D"], wl["E"], wl["k"]
+    n, done, total_t = 16, 0, 0.0
+    while done < T and total_t < target_s:
+        m = min(T, done + n) - done
+        t0 = time.perf_counter()
+        lg = oracle.router_logits(wl["x"][done:done + m], wl["w_router"],
+                                  wl["dtype"])
+        oracle.router_stats(lg.astype("float32"), k)
+        total_t += time.perf_counter() - t0
+        done += m
+        n *= 2
+    return {"value": round(2.0 * D * E * done / total_t / 1e12, 6),
+            "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"router map + statistics of the first {done} of {T} "
+                      f"tokens in {total_t:.1f} s"}
 
 
 def cpu_baseline(wl, target_s):

@@ -218,12 +218,14 @@ size_t moe_route_workspace_bytes(const moe_plan_desc *desc, int32_t D);
  * 16-byte aligned, ws 256-byte aligned. Launches only; no host sync.
  * Argument errors are found before any launch and leave every output
  * untouched. The statistics are the same bits from run to run (fixed-order
- * sums, no float atomics). */
+ * sums, no float atomics). flags: MOE_OPT_PHASE_EVENTS records HIP events
+ * around the router kernel, the plan and the statistics (phases 7, 8, 9 of
+ * moe_phase_times); other bits are ignored. */
 moe_status moe_route(const moe_plan_desc *desc, const void *x, int32_t x_dtype,
                      const void *w_router, int32_t D, float z_weight,
                      float *logits, moe_route_stats *stats,
                      int32_t *token_want, void *ws, size_t ws_bytes,
-                     void *stream, moe_plan **out);
+                     int32_t flags, void *stream, moe_plan **out);
 
 /* --- forward: experts + combine --------------------------------------- */
 
@@ -259,12 +261,14 @@ moe_status moe_forward(const moe_plan *plan, const void *x, int32_t x_dtype,
 moe_status moe_dequant_q4(const void *data, const void *scales, int64_t rows,
                           int64_t K, void *out_f16, void *stream);
 
-/* Milliseconds spent in each forward phase, summed over the moe_forward
- * calls since the last reset that ran with MOE_OPT_PHASE_EVENTS; `calls`
- * receives the count. Phases: 0 classify, 1 dequant-once, 2 gate/up full
- * tile, 3 gate/up split-K, 4 down full tile, 5 down split-K, 6 combine.
- * Synchronises on the recorded events. reset != 0 clears afterwards. */
-#define MOE_N_PHASES 7
+/* Milliseconds spent in each phase, summed over the moe_forward and
+ * moe_route calls since the last reset that ran with MOE_OPT_PHASE_EVENTS;
+ * `calls` receives the number of such calls. Phases: 0 classify,
+ * 1 dequant-once, 2 gate/up full tile, 3 gate/up split-K, 4 down full tile,
+ * 5 down split-K, 6 combine (moe_forward); 7 router kernel, 8 plan,
+ * 9 routing statistics (moe_route). Synchronises on the recorded events.
+ * reset != 0 clears afterwards. */
+#define MOE_N_PHASES 10
 moe_status moe_phase_times(double *ms, int32_t n, int64_t *calls,
                            int32_t reset);
 

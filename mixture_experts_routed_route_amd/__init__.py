@@ -35,9 +35,10 @@ MOE_F32, MOE_BF16, MOE_F16, MOE_Q4B32 = 0, 1, 2, 3
 MOE_OPT_PHASE_EVENTS = 1
 MOE_OPT_BF16_PLAIN_H = 2
 MOE_OPT_EXACT_ROUTES = 4
-MOE_N_PHASES = 7
+MOE_N_PHASES = 10
 PHASES = ("classify", "dequant_once", "gateup_full", "gateup_splitk",
-          "down_full", "down_splitk", "combine")
+          "down_full", "down_splitk", "combine", "router_gemm", "route_plan",
+          "router_stats")
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED",
                 -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
@@ -135,7 +136,7 @@ def library(path: str = LIB_PATH):
     L.moe_route_workspace_bytes.argtypes = [ctypes.POINTER(PlanDesc), i32]
     L.moe_route_workspace_bytes.restype = sz
     L.moe_route.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, i32,
-                            ctypes.c_float, vp, vp, vp, vp, sz, vp,
+                            ctypes.c_float, vp, vp, vp, vp, sz, i32, vp,
                             ctypes.POINTER(vp)]
     L.moe_route.restype = i32
     L.moe_last_error.argtypes = []
@@ -235,10 +236,19 @@ def moe_plan_create(logits: torch.Tensor, k: int, capacity_factor: float = 0.0,
     return Plan(h, ws, logits, d)
 
 
+def moe_route_workspace_bytes_for(T: int, E: int, k: int, D: int,
+                                  capacity_factor: float = 0.0,
+                                  n_shared: int = 0) -> int:
+    d = PlanDesc(T, E, k, n_shared, capacity_factor)
+    return int(library().moe_route_workspace_bytes(ctypes.byref(d), D))
+
+
 def moe_route(x: torch.Tensor, w_router: torch.Tensor, k: int,
               capacity_factor: float = 0.0, n_shared: int = 0,
               z_weight: float = 1e-3, want_per_token: bool = False,
-              workspace: torch.Tensor | None = None):
+              workspace: torch.Tensor | None = None, flags: int = 0,
+              logits: torch.Tensor | None = None,
+              stats: torch.Tensor | None = None):
     """logits = x . w_router^T (f32 [T, E]), the plan over them, and the
     routing statistics as a device f32 tensor [8] (kept_mass, want_k, z_loss,
     balance, aux, 0, 0, 0). Returns (plan, logits, stats), plus the per-token
@@ -260,8 +270,13 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, k: int,
         ws = workspace
     else:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
-    logits = torch.empty(T, E, dtype=torch.float32, device=x.device)
-    stats = torch.empty(8, dtype=torch.float32, device=x.device)
+    if logits is None:
+        logits = torch.empty(T, E, dtype=torch.float32, device=x.device)
+    if logits.shape != (T, E) or logits.dtype != torch.float32 \
+            or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous float32 [T, E] tensor")
+    if stats is None:
+        stats = torch.empty(8, dtype=torch.float32, device=x.device)
     want = (torch.empty(T, dtype=torch.int32, device=x.device)
             if want_per_token else None)
     h = ctypes.c_void_p()
@@ -269,7 +284,7 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, k: int,
                        w_router.data_ptr(), D, float(z_weight),
                        logits.data_ptr(), stats.data_ptr(),
                        None if want is None else want.data_ptr(),
-                       ws.data_ptr(), nbytes, _stream(x.device),
+                       ws.data_ptr(), nbytes, int(flags), _stream(x.device),
                        ctypes.byref(h)))
     plan = Plan(h, ws, logits, d)
     return (plan, logits, stats, want) if want_per_token else (plan, logits, stats)

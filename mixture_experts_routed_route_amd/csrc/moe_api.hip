@@ -390,7 +390,7 @@ moe_status moe_route(const moe_plan_desc* desc, const void* x, int32_t x_dtype,
                      const void* w_router, int32_t D, float z_weight,
                      float* logits, moe_route_stats* stats,
                      int32_t* token_want, void* ws, size_t ws_bytes,
-                     void* stream, moe_plan** out) {
+                     int32_t flags, void* stream, moe_plan** out) {
   std::string why;
   if (!out) return fail(MOE_EINVAL, "out is NULL");
   *out = nullptr;
@@ -420,11 +420,25 @@ moe_status moe_route(const moe_plan_desc* desc, const void* x, int32_t x_dtype,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* b = static_cast<char*>(ws);
   const int64_t limit = capacity_limit(d);
-  hipError_t e = launch_router_gemm(x, x_dtype, w_router, logits, d.T, D, d.E, s);
+  PhaseRecord* rec = nullptr;
+  if (flags & MOE_OPT_PHASE_EVENTS) {
+    rec = acquire_record(&st);
+    if (!rec) return st;
+  }
+  hipError_t e;
+  {
+    PhaseScope ps(rec, 7, s);
+    e = launch_router_gemm(x, x_dtype, w_router, logits, d.T, D, d.E,
+                           (stats || token_want) ? b + L.bytes : nullptr, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "router kernel");
-  st = launch_plan(d, logits, L, b, limit, s);
+  {
+    PhaseScope ps(rec, 8, s);
+    st = launch_plan(d, logits, L, b, limit, s);
+  }
   if (st != MOE_OK) return st;
   if (stats || token_want) {
+    PhaseScope ps(rec, 9, s);
     e = launch_router_stats(logits, (const int32_t*)(b + L.ids), d.T, d.E,
                             d.k, token_want, b + L.bytes,
                             reinterpret_cast<float*>(stats), z_weight, s);

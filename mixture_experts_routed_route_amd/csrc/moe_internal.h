@@ -176,9 +176,11 @@ hipError_t launch_combine(const void* ypair, int ypair_f16,
 
 // ---- router (router.hip) ---------------------------------------------------
 size_t router_scratch_bytes(int T, int E);
+// scratch: the statistics scratch (its accumulators are cleared by the
+// router kernel), or null when no statistics follow
 hipError_t launch_router_gemm(const void* x, int xdt, const void* w,
                               float* logits, int T, int D, int E,
-                              hipStream_t s);
+                              void* scratch, hipStream_t s);
 hipError_t launch_router_stats(const float* logits, const int32_t* ids, int T,
                                int E, int k, int32_t* want_out, void* scratch,
                                float* stats, float z_weight, hipStream_t s);

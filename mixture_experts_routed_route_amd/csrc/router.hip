@@ -20,10 +20,12 @@
 //  * router_dot_kernel: one wave per expert and up to 8 tokens, fp32 FMAs in
 //    a fixed order (fp32 inputs, and prompts too short for a tile).
 //  * router_stats_kernel: per token softmax, log-sum-exp, top-k mass (over the
-//    plan's chosen experts), the wanted count (an exact threshold search in
-//    fp32), and per-block partial sums; router_final_kernel adds the blocks'
-//    partials in a fixed order in double. No float atomics anywhere: every
-//    result is the same bits from run to run.
+//    plan's chosen experts) and the wanted count (an exact threshold search
+//    in fp32); per block, the sums per expert go into cross-block totals as
+//    fixed-point integers (integer atomics: the same total in any order) and
+//    the scalar sums into per-block partials, which router_final_kernel adds
+//    in a fixed order in double. No float atomics anywhere: every result is
+//    the same bits from run to run.
 #include <type_traits>
 
 #include "device_common.h"
@@ -42,7 +44,7 @@ __device__ __forceinline__ int rswz(int r, int c) {
 
 constexpr int kRBK = 32;      // K values per stage
 constexpr int kRNS = 4;       // ring stages
-constexpr int kStatTok = 64;  // tokens per statistics block
+constexpr int kStatTok = 16;  // tokens per statistics block
 
 }  // namespace
 
@@ -54,7 +56,8 @@ constexpr int kStatTok = 64;  // tokens per statistics block
 template <class TT, int BT, int BE>
 __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
     const void* __restrict__ x, const void* __restrict__ w,
-    float* __restrict__ logits, int T, int D, int E) {
+    float* __restrict__ logits, int T, int D, int E,
+    uint32_t* __restrict__ zero, int zero_words) {
   using V8 = typename TT::V8;
   constexpr int kRows = BT + BE;               // LDS rows per stage
   constexpr int kStage = kRows * 64;
@@ -73,6 +76,9 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
   // the expert tiles of one token tile run on one XCD and share its x rows
   const int item = xcd_item(0, blockIdx.x, gridDim.x, n_items);
   if (item < 0) return;   // block-uniform, before any barrier
+  // block 0 clears the statistics accumulators the next kernels add into
+  if (blockIdx.x == 0)
+    for (int i = tid; i < zero_words; i += 256) zero[i] = 0u;
   const int tb = item / n_eb, eb = item - tb * n_eb;
   const int e0 = eb * BE, t0 = tb * BT;
   const int ne = min(BE, E - e0), nt = min(BT, T - t0);
@@ -235,9 +241,13 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 template <class X, int TT>
 __global__ __launch_bounds__(256) void router_dot_kernel(
     const X* __restrict__ x, const X* __restrict__ w,
-    float* __restrict__ logits, int T, int D, int E) {
+    float* __restrict__ logits, int T, int D, int E,
+    uint32_t* __restrict__ zero, int zero_words) {
   constexpr int V = 16 / sizeof(X);
   const int lane = threadIdx.x & 63;
+  // block (0, 0) clears the statistics accumulators the next kernels add into
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < zero_words; i += 256) zero[i] = 0u;
   const int e = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int t0 = blockIdx.x * TT;
   if (e >= E) return;   // wave-uniform; the kernel has no barrier
@@ -349,13 +359,15 @@ __device__ __forceinline__ int grp_sum_i(int v) {
 //   threshold tau (on the bits of p, which order like the values) whose mass
 //   sum(p >= tau) is at least 0.9, found bit by bit; the experts above tau
 //   then count once each and the ones equal to tau as many as the sum needs.
-// Each block takes kStatTok tokens and writes its partial sums: p per expert,
-// first choices per expert, and kept / want / lse^2.
+// Each block takes kStatTok tokens: its sums of p and of first choices per
+// expert are added into the zeroed totals acc_p (fixed point) and acc_c, and
+// its kept / want / lse^2 sums written to part_s.
 template <int G, int PER>
 __global__ __launch_bounds__(256) void router_stats_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ ids, int T,
-    int E, int k, int32_t* __restrict__ want_out, float* __restrict__ part_p,
-    int32_t* __restrict__ part_c, float* __restrict__ part_s) {
+    int E, int k, int32_t* __restrict__ want_out,
+    unsigned long long* __restrict__ acc_p, uint32_t* __restrict__ acc_c,
+    float* __restrict__ part_s) {
   constexpr int kGroups = 64 / G;                 // tokens per wave at once
   constexpr int kPasses = (kStatTok / 4) / kGroups;
   __shared__ float sh_p[4][kMaxExperts];
@@ -460,10 +472,13 @@ __global__ __launch_bounds__(256) void router_stats_kernel(
   }
   if (lane == 0) { sh_s[wave][0] = wk; sh_s[wave][1] = ww; sh_s[wave][2] = wz; }
   __syncthreads();
+  // the block's sums per expert go into the cross-block totals as 2^-40
+  // fixed-point integers: integer adds give the same total in any order
   for (int e = threadIdx.x; e < E; e += 256) {
-    part_p[(size_t)blockIdx.x * E + e] =
-        ((sh_p[0][e] + sh_p[1][e]) + sh_p[2][e]) + sh_p[3][e];
-    part_c[(size_t)blockIdx.x * E + e] = sh_c[e];
+    const float v = ((sh_p[0][e] + sh_p[1][e]) + sh_p[2][e]) + sh_p[3][e];
+    const unsigned long long f = __double2ull_rn((double)v * 1099511627776.0);
+    if (f) atomicAdd(&acc_p[e], f);
+    if (sh_c[e]) atomicAdd(&acc_c[e], (uint32_t)sh_c[e]);
   }
   if (threadIdx.x < 3)
     part_s[blockIdx.x * 4 + threadIdx.x] =
@@ -471,33 +486,29 @@ __global__ __launch_bounds__(256) void router_stats_kernel(
         sh_s[3][threadIdx.x];
 }
 
-// The blocks' partials added in block order in double: out = {kept mass,
-// want_k, z loss, balance, aux, 0, 0, 0}, means over the T tokens (zeros
-// for T == 0).
-__global__ __launch_bounds__(256) void router_final_kernel(
-    const float* __restrict__ part_p, const int32_t* __restrict__ part_c,
-    const float* __restrict__ part_s, int nblk, int T, int E, float z_weight,
-    float* __restrict__ out) {
-  __shared__ double sh[4][256];
+// The totals in double: balance from the per-expert totals, the means from
+// the blocks' partials (each thread's share in block order, then a fixed
+// tree). out = {kept mass, want_k, z loss, balance, aux, 0, 0, 0}, zeros for
+// T == 0.
+__global__ __launch_bounds__(1024) void router_final_kernel(
+    const unsigned long long* __restrict__ acc_p,
+    const uint32_t* __restrict__ acc_c, const float* __restrict__ part_s,
+    int nblk, int T, int E, float z_weight, float* __restrict__ out) {
+  __shared__ double sh[4][1024];
   const int tid = threadIdx.x;
   double bal = 0.0, sk = 0.0, sw = 0.0, sz = 0.0;
-  for (int e = tid; e < E; e += 256) {
-    double ps = 0.0;
-    int64_t c = 0;
-    for (int b = 0; b < nblk; ++b) {
-      ps += (double)part_p[(size_t)b * E + e];
-      c += part_c[(size_t)b * E + e];
+  if (T > 0) {
+    for (int e = tid; e < E; e += 1024)
+      bal += (double)acc_c[e] * ((double)acc_p[e] * 0x1p-40);
+    for (int b = tid; b < nblk; b += 1024) {
+      sk += (double)part_s[b * 4 + 0];
+      sw += (double)part_s[b * 4 + 1];
+      sz += (double)part_s[b * 4 + 2];
     }
-    bal += (double)c * ps;
-  }
-  for (int b = tid; b < nblk; b += 256) {
-    sk += (double)part_s[b * 4 + 0];
-    sw += (double)part_s[b * 4 + 1];
-    sz += (double)part_s[b * 4 + 2];
   }
   sh[0][tid] = bal; sh[1][tid] = sk; sh[2][tid] = sw; sh[3][tid] = sz;
   __syncthreads();
-  for (int h = 128; h >= 1; h >>= 1) {
+  for (int h = 512; h >= 1; h >>= 1) {
     if (tid < h)
 #pragma unroll
       for (int q = 0; q < 4; ++q) sh[q][tid] += sh[q][tid + h];
@@ -521,16 +532,28 @@ __global__ __launch_bounds__(256) void router_final_kernel(
 
 // ---- launchers ------------------------------------------------------------
 
-size_t router_scratch_bytes(int T, int E) {
-  const size_t nblk = (size_t)(T + kStatTok - 1) / kStatTok;
+// Statistics scratch: acc_p [E] u64, acc_c [E] u32 (cleared by the router
+// kernel), part_s [nblk][4] f32.
+struct StatLayout { size_t acc_c, part_s, zero_words, bytes; };
+StatLayout stat_layout(int T, int E) {
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  return al(nblk * E * 4) + al(nblk * E * 4) + al(nblk * 16);
+  const size_t nblk = (size_t)(T + kStatTok - 1) / kStatTok;
+  StatLayout L;
+  L.acc_c = al((size_t)E * 8);
+  L.part_s = L.acc_c + al((size_t)E * 4);
+  L.zero_words = (L.acc_c + (size_t)E * 4) / 4;
+  L.bytes = L.part_s + al(nblk * 16);
+  return L;
 }
+
+size_t router_scratch_bytes(int T, int E) { return stat_layout(T, E).bytes; }
 
 hipError_t launch_router_gemm(const void* x, int xdt, const void* w,
                               float* logits, int T, int D, int E,
-                              hipStream_t s) {
+                              void* scratch, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  uint32_t* zero = static_cast<uint32_t*>(scratch);
+  const int zw = scratch ? (int)stat_layout(T, E).zero_words : 0;
   const bool mfma_ok = xdt != MOE_F32 && D % kRBK == 0 && T > kRouterDotT;
   if (mfma_ok) {
     const int64_t big = (int64_t)((T + 127) / 128) * ((E + 127) / 128);
@@ -538,31 +561,31 @@ hipError_t launch_router_gemm(const void* x, int xdt, const void* w,
       const int grid = (int)big;
       if (xdt == MOE_F16)
         hipLaunchKernelGGL((router_mfma_kernel<RF16, 128, 128>), dim3(grid), dim3(256), 0, s,
-                           x, w, logits, T, D, E);
+                           x, w, logits, T, D, E, zero, zw);
       else
         hipLaunchKernelGGL((router_mfma_kernel<RBF16, 128, 128>), dim3(grid), dim3(256), 0, s,
-                           x, w, logits, T, D, E);
+                           x, w, logits, T, D, E, zero, zw);
     } else {
       const int grid = ((T + 63) / 64) * ((E + 63) / 64);
       if (xdt == MOE_F16)
         hipLaunchKernelGGL((router_mfma_kernel<RF16, 64, 64>), dim3(grid), dim3(256), 0, s,
-                           x, w, logits, T, D, E);
+                           x, w, logits, T, D, E, zero, zw);
       else
         hipLaunchKernelGGL((router_mfma_kernel<RBF16, 64, 64>), dim3(grid), dim3(256), 0, s,
-                           x, w, logits, T, D, E);
+                           x, w, logits, T, D, E, zero, zw);
     }
     return hipGetLastError();
   }
   const dim3 grid((T + 7) / 8, (E + 3) / 4);
   if (xdt == MOE_F32)
     hipLaunchKernelGGL((router_dot_kernel<float, 8>), grid, dim3(256), 0, s,
-                       (const float*)x, (const float*)w, logits, T, D, E);
+                       (const float*)x, (const float*)w, logits, T, D, E, zero, zw);
   else if (xdt == MOE_F16)
     hipLaunchKernelGGL((router_dot_kernel<_Float16, 8>), grid, dim3(256), 0, s,
-                       (const _Float16*)x, (const _Float16*)w, logits, T, D, E);
+                       (const _Float16*)x, (const _Float16*)w, logits, T, D, E, zero, zw);
   else
     hipLaunchKernelGGL((router_dot_kernel<__bf16, 8>), grid, dim3(256), 0, s,
-                       (const __bf16*)x, (const __bf16*)w, logits, T, D, E);
+                       (const __bf16*)x, (const __bf16*)w, logits, T, D, E, zero, zw);
   return hipGetLastError();
 }
 
@@ -570,15 +593,15 @@ hipError_t launch_router_stats(const float* logits, const int32_t* ids, int T,
                                int E, int k, int32_t* want_out, void* scratch,
                                float* stats, float z_weight, hipStream_t s) {
   const int nblk = (T + kStatTok - 1) / kStatTok;
-  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const StatLayout L = stat_layout(T, E);
   char* b = static_cast<char*>(scratch);
-  float* part_p = reinterpret_cast<float*>(b);
-  int32_t* part_c = reinterpret_cast<int32_t*>(b + al((size_t)nblk * E * 4));
-  float* part_s = reinterpret_cast<float*>(b + 2 * al((size_t)nblk * E * 4));
+  unsigned long long* acc_p = reinterpret_cast<unsigned long long*>(b);
+  uint32_t* acc_c = reinterpret_cast<uint32_t*>(b + L.acc_c);
+  float* part_s = reinterpret_cast<float*>(b + L.part_s);
   if (nblk > 0) {
 #define MOE_STATS(G_, PER_)                                                     \
   hipLaunchKernelGGL((router_stats_kernel<G_, PER_>), dim3(nblk), dim3(256), 0, \
-                     s, logits, ids, T, E, k, want_out, part_p, part_c, part_s)
+                     s, logits, ids, T, E, k, want_out, acc_p, acc_c, part_s)
     if (E <= 64) MOE_STATS(16, 4);
     else if (E <= 128) MOE_STATS(16, 8);
     else if (E <= 256) MOE_STATS(16, 16);
@@ -589,8 +612,8 @@ hipError_t launch_router_stats(const float* logits, const int32_t* ids, int T,
     if (e != hipSuccess) return e;
   }
   if (stats) {
-    hipLaunchKernelGGL(router_final_kernel, dim3(1), dim3(256), 0, s, part_p,
-                       part_c, part_s, nblk, T, E, z_weight, stats);
+    hipLaunchKernelGGL(router_final_kernel, dim3(1), dim3(1024), 0, s, acc_p,
+                       acc_c, part_s, nblk, T, E, z_weight, stats);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -138,7 +138,7 @@ def _route(lib, d, x=0x1000, xdt=None, w=0x2000, D=128, zw=1e-3,
     h = ctypes.c_void_p()
     return lib.moe_route(ctypes.byref(d), x,
                          moe.MOE_BF16 if xdt is None else xdt, w, D, zw,
-                         logits, stats, want, ws, nbytes, None,
+                         logits, stats, want, ws, nbytes, 0, None,
                          ctypes.byref(h) if out else None), h
 
 

@@ -162,7 +162,7 @@ def test_route_z_weight_and_no_statistics():
     h = ctypes.c_void_p()
     assert L.moe_route(ctypes.byref(d), x.data_ptr(), moe.MOE_F16, w.data_ptr(),
                        256, ctypes.c_float(0.0), lg.data_ptr(), None, None,
-                       ws.data_ptr(), nb, moe._stream(x.device),
+                       ws.data_ptr(), nb, 0, moe._stream(x.device),
                        ctypes.byref(h)) == moe.MOE_OK
     torch.cuda.synchronize()
     assert torch.equal(lg, l0)
