@@ -43,7 +43,9 @@ __device__ __forceinline__ int rswz(int r, int c) {
 }
 
 constexpr int kRBK = 32;      // K values per stage
-constexpr int kRNS = 4;       // ring stages
+// Ring depth: a stage's loads take about a microsecond to land, so the
+// tile keeps NS - 1 stages (7 x 16 KB or 7 x 8 KB) in flight.
+constexpr int kRNS = 8;
 constexpr int kStatTok = 16;  // tokens per statistics block
 
 }  // namespace
@@ -53,7 +55,7 @@ constexpr int kStatTok = 16;  // tokens per statistics block
 // rows are the MFMA's A operand and the token rows its B operand, so a lane's
 // 32x32 accumulator holds 4 consecutive experts of one token per group of
 // four registers (16-byte stores into the token-major logits).
-template <class TT, int BT, int BE>
+template <class TT, int BT, int BE, int NS>
 __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
     const void* __restrict__ x, const void* __restrict__ w,
     float* __restrict__ logits, int T, int D, int E,
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
   constexpr int kEarly = kDma / 2;             // of them before mid-stage
   constexpr int NI = BE / 64, NJ = BT / 64;    // 32-row blocks per wave
   static_assert(kDma >= 2 && (BE % 64) == 0 && (BT % 64) == 0, "tile shape");
-  __shared__ __attribute__((aligned(1024))) char smem[kRNS * kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
   // refill of ring stage kt; past the last stage the last slice is read again
   // into a slot no one reads, so every wait below counts a constant number
   auto issue_one = [&](int kt, int jj) {
-    char* dst = smem + (kt % kRNS) * kStage + (wave * kDma + jj) * 1024;
+    char* dst = smem + (kt % NS) * kStage + (wave * kDma + jj) * 1024;
     const int soff = min(kt, nk - 1) * 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16,
                                              (int)voff[jj], soff, 0, 0);
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
   struct Frag { V8 a[NI]; V8 b[NJ]; };
   constexpr int kRd = NI + NJ;
   auto read_piece = [&](int kt, int ks, int idx, Frag& f) {
-    const char* S = smem + (kt % kRNS) * kStage;
+    const char* S = smem + (kt % NS) * kStage;
     const int ch = ks * 2 + (lane >> 5);
     if (idx < NI) {
       const int r = we * (BE / 2) + idx * 32 + (lane & 31);
@@ -144,10 +146,10 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
   };
 
 #pragma unroll
-  for (int s = 0; s < kRNS - 1; ++s)
+  for (int s = 0; s < NS - 1; ++s)
 #pragma unroll
     for (int jj = 0; jj < kDma; ++jj) issue_one(s, jj);
-  wait_vmcnt<(kRNS - 2) * kDma>();   // stage 0 landed for this wave
+  wait_vmcnt<(NS - 2) * kDma>();   // stage 0 landed for this wave
   __builtin_amdgcn_s_barrier();
   Frag f0, f1;
 #pragma unroll
@@ -160,11 +162,11 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
     // step 0 multiplies
 #pragma unroll
     for (int q = 0; q < kRd; ++q) {
-      if (q < kEarly) issue_one(kt + kRNS - 1, q);
+      if (q < kEarly) issue_one(kt + NS - 1, q);
       read_piece(kt, 1, q, f1);
     }
 #pragma unroll
-    for (int q = kRd; q < kEarly; ++q) issue_one(kt + kRNS - 1, q);
+    for (int q = kRd; q < kEarly; ++q) issue_one(kt + NS - 1, q);
     mma(f0);
 #pragma unroll
     for (int q = 0; q < kSl; ++q) {
@@ -175,15 +177,15 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
     __builtin_amdgcn_sched_barrier(0);
     // stage kt+1 landed for this wave, then (barrier) for every wave; all
     // reads of stage kt are done before anyone refills its slot
-    wait_vm_lgkm0<(kRNS - 3) * kDma + kEarly>();
+    wait_vm_lgkm0<(NS - 3) * kDma + kEarly>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int q = 0; q < kRd; ++q) {
-      if (q < kDma - kEarly) issue_one(kt + kRNS - 1, kEarly + q);
+      if (q < kDma - kEarly) issue_one(kt + NS - 1, kEarly + q);
       read_piece(kt + 1, 0, q, f0);
     }
 #pragma unroll
-    for (int q = kRd; q < kDma - kEarly; ++q) issue_one(kt + kRNS - 1, kEarly + q);
+    for (int q = kRd; q < kDma - kEarly; ++q) issue_one(kt + NS - 1, kEarly + q);
     mma(f1);
 #pragma unroll
     for (int q = 0; q < kSl; ++q) {
@@ -208,6 +210,173 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int e = e0 + we * (BE / 2) + i * 32 + rq * 8 + hi4;
+        if ((E & 3) == 0) {
+          if (e < E)
+            *reinterpret_cast<float4*>(row + e) =
+                float4{acc[i][j][rq * 4], acc[i][j][rq * 4 + 1],
+                       acc[i][j][rq * 4 + 2], acc[i][j][rq * 4 + 3]};
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (e + q < E) row[e + q] = acc[i][j][rq * 4 + q];
+        }
+      }
+  }
+}
+
+// The 128 x 128 tile on 8 waves with 64-deep stages: each stage holds 256
+// rows of 128 bytes (one whole cache line per row: a stage of 64-byte row
+// slices made every line arrive in two halves, a stage apart). Waves w and
+// w + 4 own the same 64 x 64 outputs; w takes the first two 16-deep steps of
+// every stage and w + 4 the last two, each with its own accumulators, added
+// (first + second) through LDS at the end. Chunk c of LDS row r sits at
+// c ^ ((r >> 1) & 7): the 16 rows one phase of a fragment read touches land
+// on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int rswz128(int r, int c) {
+  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+template <class TT, int NS>
+__global__ __launch_bounds__(512, 1) void router_mfma8_kernel(
+    const void* __restrict__ x, const void* __restrict__ w,
+    float* __restrict__ logits, int T, int D, int E,
+    uint32_t* __restrict__ zero, int zero_words) {
+  using V8 = typename TT::V8;
+  constexpr int BT = 128, BE = 128, BK = 64;
+  constexpr int kStage = (BT + BE) * 128;     // 32 KB
+  constexpr int kDma = kStage / 1024 / 8;     // 4 loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) char smem[NS * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = wave >> 2, wq = wave & 3;
+  const int we = wq >> 1, wt = wq & 1;
+  const int n_eb = (E + BE - 1) / BE;
+  const int n_items = n_eb * ((T + BT - 1) / BT);
+  const int item = xcd_item(0, blockIdx.x, gridDim.x, n_items);
+  if (item < 0) return;   // block-uniform, before any barrier
+  if (blockIdx.x == 0)
+    for (int i = tid; i < zero_words; i += 512) zero[i] = 0u;
+  const int tb = item / n_eb, eb = item - tb * n_eb;
+  const int e0 = eb * BE, t0 = tb * BT;
+  const int ne = min(BE, E - e0), nt = min(BT, T - t0);
+  const int nk = D / BK;
+
+  // waves 0..3 load the expert rows (stage rows 0..127), 4..7 the tokens';
+  // a 1 KB load is 8 rows of 128 bytes, lane L taking row L / 8
+  const bool is_w = wave < 4;
+  const int nrows = is_w ? ne : nt;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+      is_w ? (const char*)w + (size_t)e0 * D * 2 : (const char*)x + (size_t)t0 * D * 2,
+      (uint32_t)nrows * (uint32_t)D * 2u);
+  uint32_t voff[kDma];
+#pragma unroll
+  for (int jj = 0; jj < kDma; ++jj) {
+    const int R = 8 * (wave * kDma + jj) + (lane >> 3);
+    const int r = min(is_w ? R : R - BE, nrows - 1);
+    voff[jj] = (uint32_t)r * (uint32_t)D * 2u +
+               (uint32_t)((lane & 7) ^ ((R >> 1) & 7)) * 16u;
+  }
+  auto issue_one = [&](int kt, int jj) {
+    char* dst = smem + (kt % NS) * kStage + (wave * kDma + jj) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16,
+                                             (int)voff[jj],
+                                             min(kt, nk - 1) * 128, 0, 0);
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  struct Frag { V8 a[2]; V8 b[2]; };
+  // fragments of 16-deep step `step` (0..3) of stage kt
+  auto read = [&](int kt, int step, Frag& f) {
+    const char* S = smem + (kt % NS) * kStage;
+    const int ch = step * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = we * 64 + i * 32 + (lane & 31);
+      f.a[i] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(S + rswz128(r, ch)));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = BE + wt * 64 + j * 32 + (lane & 31);
+      f.b[j] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(S + rswz128(r, ch)));
+    }
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+#pragma unroll
+    for (int jj = 0; jj < kDma; ++jj) issue_one(s, jj);
+  wait_vmcnt<(NS - 2) * kDma>();   // stage 0 landed for this wave
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  read(0, 2 * kq, f0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // second step's reads and the refill three stages ahead, between the
+    // first step's MFMAs
+    read(kt, 2 * kq + 1, f1);
+#pragma unroll
+    for (int jj = 0; jj < kDma; ++jj) issue_one(kt + NS - 1, jj);
+    mma(f0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    // stage kt+1 landed for this wave, then for every wave; every wave's
+    // reads of stage kt were consumed by its MFMAs above, so the slot can be
+    // refilled from the next iteration on
+    wait_vm_lgkm0<(NS - 2) * kDma>();
+    __builtin_amdgcn_s_barrier();
+    read(kt + 1, 2 * kq, f0);
+  }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();   // the ring is free
+  // the second-half waves hand their sums over: [wq][register][lane] floats
+  float* red = reinterpret_cast<float*>(smem) + wq * (64 * 64);
+  if (kq == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (kq == 1) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
+
+  const int hi4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + wt * 64 + j * 32 + (lane & 31);
+    if (t >= T) continue;
+    float* row = logits + (size_t)t * E;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int e = e0 + we * 64 + i * 32 + rq * 8 + hi4;
         if ((E & 3) == 0) {
           if (e < E)
             *reinterpret_cast<float4*>(row + e) =
@@ -557,21 +726,21 @@ hipError_t launch_router_gemm(const void* x, int xdt, const void* w,
   const bool mfma_ok = xdt != MOE_F32 && D % kRBK == 0 && T > kRouterDotT;
   if (mfma_ok) {
     const int64_t big = (int64_t)((T + 127) / 128) * ((E + 127) / 128);
-    if (big >= kRouterBigTiles) {
+    if (big >= kRouterBigTiles && D % 64 == 0) {
       const int grid = (int)big;
       if (xdt == MOE_F16)
-        hipLaunchKernelGGL((router_mfma_kernel<RF16, 128, 128>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((router_mfma8_kernel<RF16, 4>), dim3(grid), dim3(512), 0, s,
                            x, w, logits, T, D, E, zero, zw);
       else
-        hipLaunchKernelGGL((router_mfma_kernel<RBF16, 128, 128>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((router_mfma8_kernel<RBF16, 4>), dim3(grid), dim3(512), 0, s,
                            x, w, logits, T, D, E, zero, zw);
     } else {
       const int grid = ((T + 63) / 64) * ((E + 63) / 64);
       if (xdt == MOE_F16)
-        hipLaunchKernelGGL((router_mfma_kernel<RF16, 64, 64>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((router_mfma_kernel<RF16, 64, 64, kRNS>), dim3(grid), dim3(256), 0, s,
                            x, w, logits, T, D, E, zero, zw);
       else
-        hipLaunchKernelGGL((router_mfma_kernel<RBF16, 64, 64>), dim3(grid), dim3(256), 0, s,
+        hipLaunchKernelGGL((router_mfma_kernel<RBF16, 64, 64, kRNS>), dim3(grid), dim3(256), 0, s,
                            x, w, logits, T, D, E, zero, zw);
     }
     return hipGetLastError();
