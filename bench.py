@@ -156,14 +156,7 @@ def main():
                         out=y, workspace=fwd_ws)
         return pl
 
-    if args.copy_calibration:
-        n = (args.copy_calibration << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args, torch, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -311,6 +304,20 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def copy_calibration(args, torch, dev):
+    """One plain elementwise copy of --copy-calibration MiB (f32, dst = src
+    * 1) for scaling the counters of a profiled run."""
+    if not args.copy_calibration:
+        return
+    n = (args.copy_calibration << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_router(args, dev, torch, moe, W):
     """moe_route on the long prompt's router: logits = x . Wr^T (fp16, f32
     accumulation), the plan over them and the routing statistics."""
@@ -328,6 +335,7 @@ def bench_router(args, dev, torch, moe, W):
         return moe.moe_route(x, w, k, workspace=ws, flags=flags,
                              logits=logits, stats=stats)
 
+    copy_calibration(args, torch, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
