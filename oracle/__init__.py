@@ -32,7 +32,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "moe_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-DT = {"f32": 0, "bf16": 1, "f16": 2, "q4b32": 3}
+DT = {"f32": 0, "bf16": 1, "f16": 2, "q4b32": 3, "q4a32": 4, "q4a64": 5}
 
 _lib = None
 
@@ -224,7 +224,7 @@ def decode(w, e: int, w_dtype: str) -> np.ndarray:
     """Expert e's [N, K] weight matrix decoded exactly to float64."""
     data, scales = _weight(w)
     N = data.shape[1]
-    K = data.shape[2] * (2 if w_dtype == "q4b32" else 1)
+    K = data.shape[2] * (2 if w_dtype.startswith("q4") else 1)
     out = np.zeros((N, K))
     rc = lib().orc_decode(_p(data), _p(scales), DT[w_dtype], e, N, K, _p(out))
     if rc != 0:
@@ -239,13 +239,15 @@ def decode_f16_bits(bits: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant_q4_to_f16_bits(w, e: int) -> np.ndarray:
-    """fp16(q * s) of expert e, rounded to nearest-even: uint16 bits [N, K].
+def dequant_q4_to_f16_bits(w, e: int, w_dtype: str = "q4b32") -> np.ndarray:
+    """fp16 of expert e's 4-bit weights, rounded to nearest-even: uint16 bits
+    [N, K].
 
-    The product q*s is exact in float64 (a 4-bit integer times an fp16), and
-    numpy's float64 -> float16 cast rounds to nearest, ties to even.
+    The value (q*s, or q*s + b for the affine groups) is exact in float64 (a
+    4-bit integer times an fp16, plus an fp16), and numpy's float64 ->
+    float16 cast rounds to nearest, ties to even.
     """
-    exact = decode(w, e, "q4b32")
+    exact = decode(w, e, w_dtype)
     return exact.astype(np.float16).view(np.uint16)
 
 

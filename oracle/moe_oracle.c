@@ -39,7 +39,10 @@
  *   - the clamp: gate clamped above at c, up clamped to [-c, c], c <= 0 off;
  *   - a shared expert (index E) sees every token with weight 1, never drops;
  *   - 4-bit weights: two's-complement nibbles, low nibble = even K index,
- *     one fp16 scale per 32 consecutive K values of an output row, value q*s.
+ *     one fp16 scale per 32 consecutive K values of an output row, value q*s;
+ *     the affine 4-bit groups: unsigned nibbles (low nibble = even K index),
+ *     an fp16 scale and bias per 32 or 64 K values stored as interleaved
+ *     pairs, value q*s + b;
  *   - router statistics: `want` is counted per token (largest p first, the
  *     first count whose running sum is >= 0.9) and averaged over tokens; the
  *     balance term's first choice is rank 0 of the top-k rule above.
@@ -51,7 +54,19 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2, ORC_Q4B32 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2, ORC_Q4B32 = 3, ORC_Q4A32 = 4,
+       ORC_Q4A64 = 5 };
+
+static int is_q4(int dtype)
+{
+    return dtype == ORC_Q4B32 || dtype == ORC_Q4A32 || dtype == ORC_Q4A64;
+}
+
+/* K values that share one scale (and, for the affine formats, one bias). */
+static int q4_group(int dtype)
+{
+    return dtype == ORC_Q4A64 ? 64 : 32;
+}
 
 /* ---- exact decoding of stored values ---------------------------------- */
 
@@ -90,26 +105,37 @@ static double dense_value(const void *base, int dtype, size_t idx)
     }
 }
 
-/* Element (n, kk) of expert e's [N, K] weight matrix, decoded exactly. */
+/* Element (n, kk) of expert e's [N, K] weight matrix, decoded exactly.
+ * Q4B32: two's-complement nibbles, value q * s, one fp16 scale per 32 K
+ * values ([.., N, K/32]). Q4A32 / Q4A64: unsigned nibbles 0..15, value
+ * q * s + b with an fp16 (scale, bias) pair per 32 / 64 K values, the pairs
+ * interleaved ([.., N, K/G, 2]) -- the affine 4-bit groups of the MLX
+ * checkpoints TensorFold PR #1607 serves (its tuner tables: "group 64",
+ * "group 32"). q * s + b is exact in double (a 15-bit product plus an fp16). */
 static double weight_value(const void *data, const void *scales, int dtype,
                            int64_t e, int64_t N, int64_t K, int64_t n, int64_t kk)
 {
-    if (dtype != ORC_Q4B32)
+    if (!is_q4(dtype))
         return dense_value(data, dtype, (size_t)((e * N + n) * K + kk));
     const uint8_t *bytes = (const uint8_t *)data;
     uint8_t byte = bytes[(e * N + n) * (K / 2) + kk / 2];
     int nib = (kk & 1) ? (byte >> 4) : (byte & 15);
-    int q = nib >= 8 ? nib - 16 : nib;           /* two's complement, -8..7 */
     const uint16_t *s = (const uint16_t *)scales;
-    double scale = f16_bits_to_double(s[(e * N + n) * (K / 32) + kk / 32]);
-    return (double)q * scale;
+    if (dtype == ORC_Q4B32) {
+        int q = nib >= 8 ? nib - 16 : nib;       /* two's complement, -8..7 */
+        double scale = f16_bits_to_double(s[(e * N + n) * (K / 32) + kk / 32]);
+        return (double)q * scale;
+    }
+    int64_t G = q4_group(dtype);
+    int64_t at = ((e * N + n) * (K / G) + kk / G) * 2;
+    return (double)nib * f16_bits_to_double(s[at]) + f16_bits_to_double(s[at + 1]);
 }
 
 /* Decode one expert's [N, K] matrix into out (row-major), for the tests. */
 int orc_decode(const void *data, const void *scales, int dtype, int64_t e,
                int64_t N, int64_t K, double *out)
 {
-    if (dtype < ORC_F32 || dtype > ORC_Q4B32 || (dtype == ORC_Q4B32 && K % 32))
+    if (dtype < ORC_F32 || dtype > ORC_Q4A64 || (is_q4(dtype) && K % q4_group(dtype)))
         return -1;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t kk = 0; kk < K; ++kk)
@@ -296,7 +322,7 @@ int orc_expert(int64_t D, int64_t F, int64_t e, const void *xrow, int x_dtype,
                double *yp)
 {
     if (x_dtype < ORC_F32 || x_dtype > ORC_F16 || w_dtype < ORC_F32 ||
-        w_dtype > ORC_Q4B32)
+        w_dtype > ORC_Q4A64)
         return -1;
     double *x = malloc((size_t)D * sizeof *x);
     for (int64_t d = 0; d < D; ++d)
@@ -322,7 +348,8 @@ int orc_layer(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
               const int64_t *tok_list, double *y)
 {
     if (x_dtype < ORC_F32 || x_dtype > ORC_F16 || w_dtype < ORC_F32 ||
-        w_dtype > ORC_Q4B32 || (w_dtype == ORC_Q4B32 && (D % 32 || F % 32)))
+        w_dtype > ORC_Q4A64 ||
+        (is_q4(w_dtype) && (D % q4_group(w_dtype) || F % q4_group(w_dtype))))
         return -1;
     if (!tok_list)
         n_tok = T;

@@ -372,6 +372,65 @@ def test_q4_layer_matches_dense_bruteforce():
     np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("fmt,G", [("q4a32", 32), ("q4a64", 64)])
+def test_q4_affine_decode_ramp_groups_and_rounding(fmt, G):
+    # one row of 128 K values: nibble kk % 16 (low nibble = even index);
+    # group j has scale 2^-j and bias -j - 0.25, so every group boundary
+    # (each G values) changes both, and a swapped nibble or group index
+    # changes the value
+    K = 128
+    packed = np.zeros((1, 1, K // 2), np.uint8)
+    for i in range(K // 2):
+        packed[0, 0, i] = ((2 * i) % 16) | (((2 * i + 1) % 16) << 4)
+    ng = K // G
+    params = np.zeros((1, 1, ng, 2), np.float16)
+    for j in range(ng):
+        params[0, 0, j] = (2.0 ** -j, -j - 0.25)
+    w = (torch.from_numpy(packed), torch.from_numpy(params))
+    got = oracle.decode(w, 0, fmt)[0]
+    want = [(kk % 16) * 2.0 ** -(kk // G) - (kk // G) - 0.25 for kk in range(K)]
+    assert got.tolist() == want
+    # q*s + b rounded once to fp16: with s = 2^-14 * 3 and b = 1, q*s + b
+    # needs more than fp16's 11 bits and rounds to nearest even
+    params2 = np.zeros((1, 1, ng, 2), np.float16)
+    params2[..., 0] = 3 * 2.0 ** -14
+    params2[..., 1] = 1.0
+    w2 = (torch.from_numpy(packed), torch.from_numpy(params2))
+    exact = oracle.decode(w2, 0, fmt)[0]
+    assert exact.tolist() == [(kk % 16) * 3 * 2.0 ** -14 + 1.0 for kk in range(K)]
+    bits = oracle.dequant_q4_to_f16_bits(w2, 0, fmt)[0]
+    ulp = 2.0 ** -10
+    rounded = [math.floor(v / ulp + 0.5) * ulp if (v / ulp) % 1 != 0.5 else
+               (math.floor(v / ulp) + (math.floor(v / ulp) % 2)) * ulp
+               for v in exact.tolist()]
+    assert bits.view(np.float16).astype(np.float64).tolist() == rounded
+
+
+def _numpy_affine_decode(packed, params, G):
+    p = packed.numpy()
+    q = np.stack([p & 15, p >> 4], axis=-1).reshape(*p.shape[:-1], -1)
+    pr = params.numpy().astype(np.float64)
+    s = np.repeat(pr[..., 0], G, axis=-1)
+    b = np.repeat(pr[..., 1], G, axis=-1)
+    return q * s + b
+
+
+@pytest.mark.parametrize("fmt,G", [(W.Q4A32, 32), (W.Q4A64, 64)])
+def test_q4_affine_layer_matches_dense_bruteforce(fmt, G):
+    wl = W.make_layer(8, 128, 192, 3, 2, W.F16, w_dtype=fmt, seed=17)
+    for name in ("w_gate", "w_up", "w_down"):
+        d = _numpy_affine_decode(*wl[name], G)
+        for e in range(3):
+            assert np.array_equal(oracle.decode(wl[name], e, fmt), d[e])
+    ids, w, pl, y = _layer(wl, 0.0)
+    X = wl["x"].to(torch.float64).numpy()
+    Wg, Wu, Wd = (_numpy_affine_decode(*wl[n], G) for n in ("w_gate", "w_up",
+                                                            "w_down"))
+    ref = brute.dense_layer(X, Wg, Wu, Wd, ids, w, pl["keep"].astype(bool),
+                            7.0)
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
+
+
 # ------------------------------------------------ router and statistics ---
 
 def test_router_logits_hand_worked_product():

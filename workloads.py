@@ -31,6 +31,8 @@ from __future__ import annotations
 import torch
 
 F32, BF16, F16, Q4B32 = "f32", "bf16", "f16", "q4b32"
+Q4A32, Q4A64 = "q4a32", "q4a64"
+Q4_FORMATS = (Q4B32, Q4A32, Q4A64)
 
 _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}
 
@@ -109,6 +111,21 @@ def q4_weights(E_total: int, N: int, K: int, g: torch.Generator,
     return packed, scales.to(torch.float16).contiguous()
 
 
+def q4_affine_weights(E_total: int, N: int, K: int, group: int,
+                      g: torch.Generator, scale_lo: float = 0.005,
+                      scale_hi: float = 0.02):
+    """Affine 4-bit weights [E, N, K]: uniform unsigned nibbles and per group
+    of ``group`` K values an fp16 scale ~U(lo, hi) and bias (-7.5 + U(-1, 1))
+    * scale, interleaved as [E, N, K / group, 2] (scale, bias)."""
+    assert K % group == 0
+    packed = _random_bytes(E_total * N * K // 2, g).view(E_total, N, K // 2)
+    ng = K // group
+    scales = torch.empty(E_total, N, ng).uniform_(scale_lo, scale_hi, generator=g)
+    shift = torch.empty(E_total, N, ng).uniform_(-1.0, 1.0, generator=g)
+    params = torch.stack([scales, (shift - 7.5) * scales], dim=-1)
+    return packed, params.to(torch.float16).contiguous()
+
+
 def make_layer(T: int, D: int, F: int, E: int, k: int, dtype: str, *,
                w_dtype: str | None = None, n_shared: int = 0,
                logits: torch.Tensor | None = None, logit_bias=None,
@@ -142,6 +159,11 @@ def make_layer(T: int, D: int, F: int, E: int, k: int, dtype: str, *,
         wg = q4_weights(Et, F, D, g)
         wu = q4_weights(Et, F, D, g)
         wd = q4_weights(Et, D, F, g)
+    elif w_dtype in (Q4A32, Q4A64):
+        grp = 32 if w_dtype == Q4A32 else 64
+        wg = q4_affine_weights(Et, F, D, grp, g)
+        wu = q4_affine_weights(Et, F, D, grp, g)
+        wd = q4_affine_weights(Et, D, F, grp, g)
     else:
         wg, wu, wd = dense_weights(Et, D, F, w_std, w_dtype, g)
     return dict(base, x=x, w_gate=wg, w_up=wu, w_down=wd)
@@ -246,7 +268,8 @@ def flops_per_pair(D: int, F: int) -> int:
 
 
 def weight_bytes_per_expert(D: int, F: int, w_dtype: str) -> float:
-    per = {F32: 4.0, BF16: 2.0, F16: 2.0, Q4B32: 0.5 + 2.0 / 32.0}[w_dtype]
+    per = {F32: 4.0, BF16: 2.0, F16: 2.0, Q4B32: 0.5 + 2.0 / 32.0,
+           Q4A32: 0.5 + 4.0 / 32.0, Q4A64: 0.5 + 4.0 / 64.0}[w_dtype]
     return 3.0 * D * F * per
 
 
