@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (K more steps, each after "
                          "a 1 GiB write that evicts L2 and the 256 MB MALL)")
+    ap.add_argument("--weights", default=None, choices=("q4b32", "q4a32", "q4a64"),
+                    help="4-bit format of workloads 4 and 7 (default q4b32)")
     ap.add_argument("--router", action="store_true",
                     help="time moe_route (router map + plan + statistics)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -120,7 +122,7 @@ def main():
     if args.router:
         return bench_router(args, dev, torch, moe, W)
     wl = W.config(args.config, capacity_factor=args.capacity_factor, T=args.T,
-                  pairs_per_expert=args.pairs_per_expert)
+                  pairs_per_expert=args.pairs_per_expert, w_dtype=args.weights)
     T, D, F, E, k, ns = (wl[n] for n in ("T", "D", "F", "E", "k", "n_shared"))
     logits = wl["logits"].to(dev)
     x = wl["x"].to(dev)
@@ -143,7 +145,8 @@ def main():
     p = moe.moe_plan_create(logits, k, wl["capacity_factor"], ns,
                             workspace=plan_ws)
     wdt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "f16": moe.MOE_F16,
-           "q4b32": moe.MOE_Q4B32}[wl["w_dtype"]]
+           "q4b32": moe.MOE_Q4B32, "q4a32": moe.MOE_Q4A32,
+           "q4a64": moe.MOE_Q4A64}[wl["w_dtype"]]
     xdt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "f16": moe.MOE_F16}[wl["x_dtype"]]
     fwd_ws = torch.empty(moe.moe_forward_workspace_bytes(p, D, F, xdt, wdt, opts),
                          dtype=torch.uint8, device=dev)
@@ -211,11 +214,12 @@ def main():
                                                / 1e9 / PEAK_HBM_GBS, 4)}
 
     # routes per expert (the library's rule, restated for accounting)
-    fat_rows = opts.fat_rows if wl["w_dtype"] == "q4b32" else 0
+    q4 = wl["w_dtype"].startswith("q4")
+    fat_rows = opts.fat_rows if q4 else 0
     if 0 < fat_rows < 17:
         fat_rows = 17
     S = float(opts.splitk_max_pairs)
-    if wl["w_dtype"] == "q4b32":
+    if q4:
         full_mask = (counts >= fat_rows) if fat_rows > 0 else counts < 0
     elif wl["w_dtype"] == "f32":
         full_mask = counts < 0
@@ -243,7 +247,8 @@ def main():
             "down_splitk": ("hbm", wbytes * int(sk_mask.sum())
                             + int(counts[sk_mask].sum()) * (F * xb + D * 4)),
             "dequant_once": ("hbm", int(full_mask.sum()) * 3 * D * F
-                             * (0.5625 + 2.0) if wl["w_dtype"] == "q4b32" else 0),
+                             * (W.weight_bytes_per_expert(1, 1, wl["w_dtype"]) / 3.0 + 2.0)
+                             if q4 else 0),
             "combine": ("hbm", kept_pairs * D * 4 + T * D * 4),
             "classify": ("hbm", 0),
         }

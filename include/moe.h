@@ -63,7 +63,15 @@ typedef enum {
      * complement nibbles (low nibble = even K index), `scales` is fp16
      * [.., N, K/32], one scale per 32 consecutive K values of a row; the
      * value is q * s. Weights only; x must be F16. */
-    MOE_Q4B32 = 3
+    MOE_Q4B32 = 3,
+    /* Affine 4-bit groups (the MLX 4-bit checkpoints of TensorFold PR
+     * #1607, "group 32" / "group 64" in its tuner tables): `data` is uint8
+     * [.., N, K/2] holding unsigned nibbles 0..15 (low nibble = even K
+     * index), `scales` is fp16 [.., N, K/G, 2]: per group of G = 32 / 64
+     * consecutive K values of a row, its scale s then its bias b; the value
+     * is q * s + b. Weights only; x must be F16. */
+    MOE_Q4A32 = 4,
+    MOE_Q4A64 = 5
 } moe_dtype;
 
 /* Plan shape. 1 <= k <= E <= 1024; T >= 0; T*(k+1) < 2^31; n_shared in
@@ -119,7 +127,9 @@ typedef struct {
 #define MOE_OPT_BF16_PLAIN_H 2
 #define MOE_OPT_EXACT_ROUTES 4
 
-/* One weight tensor. `scales` is NULL unless dtype is MOE_Q4B32. */
+/* One weight tensor. `scales` is NULL unless dtype is a 4-bit format; then
+ * it is 4-byte aligned (MOE_Q4B32) or 8-byte aligned (the affine formats):
+ * a lane reads two adjacent block parameters at once. */
 typedef struct {
     int32_t dtype;
     const void *data;
@@ -260,6 +270,15 @@ moe_status moe_forward(const moe_plan *plan, const void *x, int32_t x_dtype,
  * expert's weights decoded to FP16 once). K multiple of 32. Async. */
 moe_status moe_dequant_q4(const void *data, const void *scales, int64_t rows,
                           int64_t K, void *out_f16, void *stream);
+
+/* Dequantise rows of any 4-bit format (MOE_Q4B32, MOE_Q4A32, MOE_Q4A64) to
+ * fp16 once: out[r, c] = fp16_rne(q * s) or fp16_rne(q * s + b) (one
+ * rounding: the affine value is one fp16 fma). K a multiple of the group
+ * (32 or 64); data and out 16-byte aligned, scales 2-byte (Q4B32) or
+ * 4-byte (affine). Async. */
+moe_status moe_dequant_weights(int32_t dtype, const void *data,
+                               const void *scales, int64_t rows, int64_t K,
+                               void *out_f16, void *stream);
 
 /* Milliseconds spent in each phase, summed over the moe_forward and
  * moe_route calls since the last reset that ran with MOE_OPT_PHASE_EVENTS;

@@ -16,8 +16,10 @@ routing statistics beside the plan):
     plan, logits, stats = moe_route(x, w_router, k=8)
 
 Weights are torch tensors [E (+1 shared), F, D] / [E (+1), D, F] in x's dtype,
-or, for 4-bit block weights, ``(packed uint8 [.., N, K/2], scales fp16
-[.., N, K/32])`` pairs.
+or, for 4-bit weights, ``(packed uint8 [.., N, K/2], params fp16)`` pairs:
+params [.., N, K/32] are the block scales of the signed format, params
+[.., N, K/G, 2] the (scale, bias) pairs of the affine format with groups of
+G = 32 or 64 K values (the format follows from the params' shape).
 """
 
 from __future__ import annotations
@@ -32,6 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_F16, MOE_Q4B32 = 0, 1, 2, 3
+MOE_Q4A32, MOE_Q4A64 = 4, 5
 MOE_OPT_PHASE_EVENTS = 1
 MOE_OPT_BF16_PLAIN_H = 2
 MOE_OPT_EXACT_ROUTES = 4
@@ -51,7 +54,7 @@ EXPORTED = (
     "moe_plan_get_views", "moe_plan_destroy", "moe_options_default",
     "moe_forward_workspace_bytes", "moe_forward", "moe_dequant_q4",
     "moe_phase_times", "moe_last_error", "moe_version",
-    "moe_route_workspace_bytes", "moe_route",
+    "moe_route_workspace_bytes", "moe_route", "moe_dequant_weights",
 )
 
 ROUTE_STATS = ("kept_mass", "want_k", "z_loss", "balance", "aux")
@@ -130,6 +133,8 @@ def library(path: str = LIB_PATH):
     L.moe_forward.restype = i32
     L.moe_dequant_q4.argtypes = [vp, vp, i64, i64, vp, vp]
     L.moe_dequant_q4.restype = i32
+    L.moe_dequant_weights.argtypes = [i32, vp, vp, i64, i64, vp, vp]
+    L.moe_dequant_weights.restype = i32
     L.moe_phase_times.argtypes = [ctypes.POINTER(ctypes.c_double), i32,
                                   ctypes.POINTER(i64), i32]
     L.moe_phase_times.restype = i32
@@ -327,15 +332,33 @@ def moe_plan_get_views(plan: Plan) -> dict:
     return out
 
 
+def q4_dtype(data: torch.Tensor, params: torch.Tensor) -> int:
+    """The 4-bit format of a (packed, params) pair, from the params' shape:
+    [.., N, K/32] scales -> MOE_Q4B32; [.., N, K/G, 2] (scale, bias) pairs
+    -> MOE_Q4A32 or MOE_Q4A64 by G."""
+    K = data.shape[-1] * 2
+    if params.dim() == data.dim() and params.shape[-1] * 32 == K:
+        return MOE_Q4B32
+    if params.dim() == data.dim() + 1 and params.shape[-1] == 2:
+        groups = params.shape[-2]
+        if groups * 32 == K:
+            return MOE_Q4A32
+        if groups * 64 == K:
+            return MOE_Q4A64
+    raise ValueError(f"4-bit params of shape {tuple(params.shape)} do not "
+                     f"match packed data of shape {tuple(data.shape)}")
+
+
 def _weight(w, device) -> tuple:
     if isinstance(w, (tuple, list)):
         data, scales = w
         if data.dtype != torch.uint8 or scales.dtype != torch.float16:
-            raise ValueError("4-bit weights are (uint8 data, float16 scales)")
+            raise ValueError("4-bit weights are (uint8 data, float16 params)")
         if data.device != device or scales.device != device:
             raise ValueError("weights must be on the input's device")
         data, scales = data.contiguous(), scales.contiguous()
-        return Weight(MOE_Q4B32, data.data_ptr(), scales.data_ptr()), (data, scales)
+        return (Weight(q4_dtype(data, scales), data.data_ptr(), scales.data_ptr()),
+                (data, scales))
     if w.dtype not in _TORCH_TO_MOE:
         raise ValueError(f"unsupported weight dtype {w.dtype}")
     if w.device != device:
@@ -410,6 +433,23 @@ def moe_dequant_q4(data: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
                       device=data.device)
     _check(library().moe_dequant_q4(data.data_ptr(), scales.data_ptr(), rows,
                                     K, out.data_ptr(), _stream(data.device)))
+    return out
+
+
+def moe_dequant_weights(data: torch.Tensor, params: torch.Tensor) -> torch.Tensor:
+    """fp16 of [.., N, K/2] 4-bit rows in any format (the params' shape
+    picks it): fp16_rne(q * s) or fp16_rne(q * s + b); returns [.., N, K]."""
+    if data.dtype != torch.uint8 or params.dtype != torch.float16:
+        raise ValueError("expects uint8 data and float16 params")
+    data, params = data.contiguous(), params.contiguous()
+    dt = q4_dtype(data, params)
+    K = data.shape[-1] * 2
+    rows = data.numel() // data.shape[-1]
+    out = torch.empty(*data.shape[:-1], K, dtype=torch.float16,
+                      device=data.device)
+    _check(library().moe_dequant_weights(dt, data.data_ptr(), params.data_ptr(),
+                                         rows, K, out.data_ptr(),
+                                         _stream(data.device)))
     return out
 
 

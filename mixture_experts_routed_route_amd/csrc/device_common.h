@@ -115,6 +115,88 @@ __device__ __forceinline__ void dequant32(uint4 raw, _Float16 s, half8 out[4]) {
   out[3] = dequant_word(raw.w, s);
 }
 
+// 4-bit weight formats. FMT 0 (MOE_Q4B32): two's-complement nibbles, one
+// fp16 scale per 32 K values, value q * s. FMT 1 / 2 (MOE_Q4A32 / Q4A64):
+// unsigned nibbles, an fp16 (scale, bias) pair per 32 / 64 K values stored
+// as one 32-bit word (scale in the low half), value q * s + b: the affine
+// 4-bit groups of the MLX checkpoints TensorFold PR #1607 serves.
+template <int FMT> struct Q4F {
+  static constexpr int kGroup = FMT == 2 ? 64 : 32;   // K values per parameter
+  static constexpr int kPB = FMT == 0 ? 2 : 4;         // bytes per parameter
+};
+
+// Parameters of a lane's 32 * KH consecutive K values from k0 (k0 a
+// multiple of 32 * KH) of one weight row whose parameters start at prow.
+struct Q4P { uint32_t w[2]; };
+template <int FMT, int KH>
+__device__ __forceinline__ Q4P load_q4p(const char* prow, int k0) {
+  Q4P p{{0u, 0u}};
+  if constexpr (FMT == 0) {
+    if constexpr (KH == 2)   // two adjacent fp16 scales, 4-byte aligned
+      p.w[0] = *reinterpret_cast<const uint32_t*>(prow + (k0 / 32) * 2);
+    else
+      p.w[0] = *reinterpret_cast<const uint16_t*>(prow + (k0 / 32) * 2);
+  } else if constexpr (FMT == 1) {
+    if constexpr (KH == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(prow + (k0 / 32) * 4);
+      p.w[0] = v.x;
+      p.w[1] = v.y;
+    } else {
+      p.w[0] = *reinterpret_cast<const uint32_t*>(prow + (k0 / 32) * 4);
+    }
+  } else {
+    p.w[0] = *reinterpret_cast<const uint32_t*>(prow + (k0 / 64) * 4);
+  }
+  return p;
+}
+// the parameter of the lane's 32-value block h
+template <int FMT>
+__device__ __forceinline__ uint32_t q4p_block(const Q4P& p, int h) {
+  if constexpr (FMT == 0) return (p.w[0] >> (16 * h)) & 0xFFFFu;
+  else if constexpr (FMT == 1) return p.w[h];
+  else return p.w[0];
+}
+
+// 8 consecutive unsigned 4-bit values (low nibble first) as fp16
+// q * s + b: 0x6400 | q encodes 1024 + q exactly, subtracting 1024 leaves q,
+// and one fp16 fma rounds q * s + b once.
+__device__ __forceinline__ half8 dequant_word_affine(uint32_t word, uint32_t sb) {
+  const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)(sb & 0xFFFFu));
+  const _Float16 bi = __builtin_bit_cast(_Float16, (uint16_t)(sb >> 16));
+  const half2v s2 = {sc, sc};
+  const half2v b2 = {bi, bi};
+  const half2v off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const uint32_t lo = word & 0x0F0F0F0Fu;
+  const uint32_t hi = (word >> 4) & 0x0F0F0F0Fu;
+  half8 out;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
+    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    half2v h = __builtin_bit_cast(half2v, pr) + off;
+    h = __builtin_elementwise_fma(h, s2, b2);
+    out[2 * b] = h[0];
+    out[2 * b + 1] = h[1];
+  }
+  return out;
+}
+
+template <int FMT>
+__device__ __forceinline__ half8 dequant_word_f(uint32_t word, uint32_t param) {
+  if constexpr (FMT == 0)
+    return dequant_word(word, __builtin_bit_cast(_Float16, (uint16_t)param));
+  else
+    return dequant_word_affine(word, param);
+}
+
+template <int FMT>
+__device__ __forceinline__ void dequant32_f(uint4 raw, uint32_t param, half8 out[4]) {
+  out[0] = dequant_word_f<FMT>(raw.x, param);
+  out[1] = dequant_word_f<FMT>(raw.y, param);
+  out[2] = dequant_word_f<FMT>(raw.z, param);
+  out[3] = dequant_word_f<FMT>(raw.w, param);
+}
+
 // Per-pair outputs of the down projection: fp16 when the layer computes in
 // fp16 (no range or precision is lost against its fp16 intermediate), f32
 // otherwise (bf16's 8-bit significand would cost the output its tolerance).

@@ -259,22 +259,23 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, _Float16 s) {
 // 1 KB per store instruction.
 struct DequantSet {
   const uint8_t* q[3];
-  const uint16_t* sc[3];
+  const char* sc[3];      // scales (FMT 0) or (scale, bias) words
   _Float16* out[3];
   int rows[3], K[3];
 };
 
-template <int KB>
+template <int KB, int FMT>
 __device__ __forceinline__ void dequant_fat_tiles(const DequantSet& d, int m,
                                                   const int32_t* fat_list,
                                                   int nfat, char* tile) {
   constexpr int TPR = 4;                          // threads per row
   constexpr int BPT = KB / TPR;                   // 32-value blocks per thread
   const uint8_t* __restrict__ q = d.q[m];
-  const uint16_t* __restrict__ sc = d.sc[m];
+  const char* __restrict__ sc = d.sc[m];
   _Float16* __restrict__ out = d.out[m];
   const int rows = d.rows[m], K = d.K[m];
   const int kbs = K / 32;                         // 32-value blocks per row
+  const int ngr = K / Q4F<FMT>::kGroup;           // parameters per row
   const int rt = rows / 64, ktn = kbs / KB;       // tiles per slot: rt x ktn
   const int per_slot = rt * ktn;
   const int total = nfat * per_slot;
@@ -288,18 +289,22 @@ __device__ __forceinline__ void dequant_fat_tiles(const DequantSet& d, int m,
     const int row0 = (rem - kq * rt) * 64;
     const size_t er = (size_t)fat_list[slot] * rows + row0 + r;
     uint4 qa[BPT];
-    _Float16 sa[BPT];
+    uint32_t pa[BPT];
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
       const int kb = kb0 + qq * BPT + b;
       qa[b] = *reinterpret_cast<const uint4*>(q + er * (size_t)(K / 2) + kb * 16);
-      sa[b] = __builtin_bit_cast(_Float16, sc[er * (size_t)kbs + kb]);
+      if constexpr (FMT == 0)
+        pa[b] = *reinterpret_cast<const uint16_t*>(sc + (er * (size_t)kbs + kb) * 2);
+      else
+        pa[b] = *reinterpret_cast<const uint32_t*>(
+            sc + (er * (size_t)ngr + kb * 32 / Q4F<FMT>::kGroup) * 4);
     }
     __syncthreads();   // the previous tile's stores have read the LDS tile
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
       half8 ha[4];
-      dequant32(qa[b], sa[b], ha);
+      dequant32_f<FMT>(qa[b], pa[b], ha);
       char* ta = tile + ((qq * BPT + b) * 64 + r) * 64;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -316,6 +321,7 @@ __device__ __forceinline__ void dequant_fat_tiles(const DequantSet& d, int m,
   }
 }
 
+template <int FMT>
 __global__ __launch_bounds__(256) void dequant_fat_kernel(
     DequantSet d, const int32_t* __restrict__ fat_list,
     const int32_t* __restrict__ meta) {
@@ -323,53 +329,74 @@ __global__ __launch_bounds__(256) void dequant_fat_kernel(
   const int m = blockIdx.y;
   const int nfat = meta[kMetaFat];
   if (d.K[m] % 256 == 0)
-    dequant_fat_tiles<8>(d, m, fat_list, nfat, tile);
+    dequant_fat_tiles<8, FMT>(d, m, fat_list, nfat, tile);
   else
-    dequant_fat_tiles<4>(d, m, fat_list, nfat, tile);
+    dequant_fat_tiles<4, FMT>(d, m, fat_list, nfat, tile);
 }
 
+template <int FMT>
 __global__ __launch_bounds__(256) void dequant_rows_kernel(
-    const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
+    const uint8_t* __restrict__ q, const char* __restrict__ sc,
     _Float16* __restrict__ out, int64_t rows, int K) {
   const int upr = K / 8;
+  const int ngr = K / Q4F<FMT>::kGroup;
   const size_t total = (size_t)rows * upr;
   for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < total;
        u += (size_t)gridDim.x * blockDim.x) {
     const size_t row = u / upr;
     const int c8 = (int)(u - row * upr);
     const uint32_t word = reinterpret_cast<const uint32_t*>(q + row * (size_t)(K / 2))[c8];
-    const uint16_t sb = sc[row * (size_t)(K / 32) + (c8 >> 2)];
-    reinterpret_cast<uint4*>(out + row * (size_t)K)[c8] =
-        dequant8(word, __builtin_bit_cast(_Float16, sb));
+    if constexpr (FMT == 0) {
+      const uint16_t sb = reinterpret_cast<const uint16_t*>(sc)[row * (size_t)(K / 32) + (c8 >> 2)];
+      reinterpret_cast<uint4*>(out + row * (size_t)K)[c8] =
+          dequant8(word, __builtin_bit_cast(_Float16, sb));
+    } else {
+      const uint32_t p = reinterpret_cast<const uint32_t*>(sc)[
+          row * (size_t)ngr + c8 * 8 / Q4F<FMT>::kGroup];
+      reinterpret_cast<uint4*>(out + row * (size_t)K)[c8] =
+          __builtin_bit_cast(uint4, dequant_word_affine(word, p));
+    }
   }
 }
 
 hipError_t launch_dequant_fat(const void* const q[3], const void* const sc[3],
                               void* const out[3], const int rows[3],
                               const int K[3], int n, const int32_t* fat_list,
-                              const int32_t* meta, int grid, hipStream_t s) {
+                              const int32_t* meta, int grid, int fmt,
+                              hipStream_t s) {
   if (n < 1 || n > 3) return hipErrorInvalidValue;
   DequantSet d{};
   for (int i = 0; i < n; ++i) {
     d.q[i] = (const uint8_t*)q[i];
-    d.sc[i] = (const uint16_t*)sc[i];
+    d.sc[i] = (const char*)sc[i];
     d.out[i] = (_Float16*)out[i];
     d.rows[i] = rows[i];
     d.K[i] = K[i];
   }
-  hipLaunchKernelGGL(dequant_fat_kernel, dim3(grid, n), dim3(256), 0, s, d,
-                     fat_list, meta);
+  if (fmt == 0)
+    hipLaunchKernelGGL(dequant_fat_kernel<0>, dim3(grid, n), dim3(256), 0, s, d, fat_list, meta);
+  else if (fmt == 1)
+    hipLaunchKernelGGL(dequant_fat_kernel<1>, dim3(grid, n), dim3(256), 0, s, d, fat_list, meta);
+  else if (fmt == 2)
+    hipLaunchKernelGGL(dequant_fat_kernel<2>, dim3(grid, n), dim3(256), 0, s, d, fat_list, meta);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
-                               int64_t rows, int K, hipStream_t s) {
+                               int64_t rows, int K, int fmt, hipStream_t s) {
   const size_t units = (size_t)rows * (K / 8);
   const int grid = (int)std::min<size_t>((units + 255) / 256, 65536);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(dequant_rows_kernel, dim3(grid), dim3(256), 0, s,
-                     (const uint8_t*)q, (const uint16_t*)sc, (_Float16*)out,
-                     rows, K);
+#define MOE_DQR(F_)                                                              \
+  hipLaunchKernelGGL(dequant_rows_kernel<F_>, dim3(grid), dim3(256), 0, s,       \
+                     (const uint8_t*)q, (const char*)sc, (_Float16*)out, rows, K)
+  if (fmt == 0) MOE_DQR(0);
+  else if (fmt == 1) MOE_DQR(1);
+  else if (fmt == 2) MOE_DQR(2);
+  else return hipErrorInvalidValue;
+#undef MOE_DQR
   return hipGetLastError();
 }
 
@@ -531,10 +558,10 @@ template <int RB, int KH>
 struct RawQ4 {
   uint4 av[RB][4 * KH];   // A values k0 .. k0 + 32 KH of the lane's rows
   uint4 w[4][KH];         // 32 KH nibbles of each column block's row
-  uint32_t sc[4];         // their KH scales (KH = 2: two fp16 in one word)
+  Q4P p[4];               // their block parameters
 };
 
-template <int RB, int MODE>
+template <int RB, int MODE, int FMT>
 __device__ __forceinline__ void splitk_body_q4(const GemmArgs& a, int item,
                                                int NNB, float* red) {
   const int lane = threadIdx.x & 63;
@@ -556,7 +583,7 @@ __device__ __forceinline__ void splitk_body_q4(const GemmArgs& a, int item,
     ap[rb] = (const char*)a.A + (size_t)arow * a.a_ld * 2;
   }
   const uint8_t* bp[4];
-  const uint16_t* bsp[4];
+  const char* bsp[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     int row;
@@ -573,7 +600,8 @@ __device__ __forceinline__ void splitk_body_q4(const GemmArgs& a, int item,
     }
     const size_t wrow = (size_t)e * N + row;
     bp[cb] = (const uint8_t*)base + wrow * (size_t)(K / 2);
-    bsp[cb] = (const uint16_t*)sbase + wrow * (size_t)(K / 32);
+    bsp[cb] = (const char*)sbase +
+              wrow * (size_t)(K / Q4F<FMT>::kGroup) * Q4F<FMT>::kPB;
   }
   floatx4 acc[RB][4];
 #pragma unroll
@@ -595,10 +623,7 @@ __device__ __forceinline__ void splitk_body_q4(const GemmArgs& a, int item,
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
       for (int h = 0; h < KH; ++h) r.w[cb][h] = ldg16(bp[cb] + k0 / 2 + h * 16);
-      if constexpr (KH == 2)
-        r.sc[cb] = *reinterpret_cast<const uint32_t*>(bsp[cb] + k0 / 32);
-      else
-        r.sc[cb] = bsp[cb][k0 / 32];
+      r.p[cb] = load_q4p<FMT, KH>(bsp[cb], k0);
     }
     // every load of the step is issued before the first use: left to
     // itself, the scheduler sinks loads into the decode to save registers
@@ -609,7 +634,7 @@ __device__ __forceinline__ void splitk_body_q4(const GemmArgs& a, int item,
 #pragma unroll
       for (int h = 0; h < KH; ++h) {
         half8 hv[4];
-        dequant32(r.w[cb][h], __builtin_bit_cast(_Float16, (uint16_t)(r.sc[cb] >> (16 * h))), hv);
+        dequant32_f<FMT>(r.w[cb][h], q4p_block<FMT>(r.p[cb], h), hv);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -809,14 +834,14 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
 // that 16 waves keep their loads in flight. The column blocks of one group
 // run on one XCD: its x rows, read by every column block, stay in that L2
 // while the weights stream past.
-template <int RB, int MODE>
+template <int RB, int MODE, int FMT>
 __global__ __launch_bounds__(256, 4) void gemm_splitk_q4_kernel(GemmArgs a) {
   __shared__ float red[RB * 4 * 4 * 64];
   const int NNB = MODE == 0 ? a.N / 32 : a.N / 64;
   const int n_items = a.meta[a.meta_index] * NNB;
   for (int rb0 = 0; rb0 < n_items; rb0 += gridDim.x) {
     const int item = xcd_item(rb0, blockIdx.x, gridDim.x, n_items);
-    if (item >= 0) splitk_body_q4<RB, MODE>(a, item, NNB, red);
+    if (item >= 0) splitk_body_q4<RB, MODE, FMT>(a, item, NNB, red);
   }
 }
 
@@ -842,13 +867,21 @@ hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
   if (xdt == MOE_F32 && wdt == MOE_F32) return splitk_rb<F32T>(a, rb, grid, s);
   if (xdt == MOE_BF16 && wdt == MOE_BF16) return splitk_rb<BF16T>(a, rb, grid, s);
   if (xdt == MOE_F16 && wdt == MOE_F16) return splitk_rb<F16T>(a, rb, grid, s);
-  if (xdt == MOE_F16 && wdt == MOE_Q4B32) {
+  const int fmt = q4_fmt(wdt);
+  if (xdt == MOE_F16 && fmt >= 0) {
     // groups of <= 16 rows; the down stage reads H (fp16) as A in every case
     if (rb != 1) return hipErrorInvalidValue;
-    if (a.mode == 0)
-      hipLaunchKernelGGL((gemm_splitk_q4_kernel<1, 0>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_splitk_q4_kernel<1, 1>), dim3(grid), dim3(256), 0, s, a);
+#define MOE_SKQ4(F_)                                                                      \
+  do {                                                                                    \
+    if (a.mode == 0)                                                                      \
+      hipLaunchKernelGGL((gemm_splitk_q4_kernel<1, 0, F_>), dim3(grid), dim3(256), 0, s, a); \
+    else                                                                                  \
+      hipLaunchKernelGGL((gemm_splitk_q4_kernel<1, 1, F_>), dim3(grid), dim3(256), 0, s, a); \
+  } while (0)
+    if (fmt == 0) MOE_SKQ4(0);
+    else if (fmt == 1) MOE_SKQ4(1);
+    else MOE_SKQ4(2);
+#undef MOE_SKQ4
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -52,11 +52,13 @@ template <int CK> struct WGeo {
 template <int WQ, int CK>
 struct WChunk;
 template <int CK>
-struct WChunk<1, CK> { uint4 q[4][CK / 128]; uint32_t s[4]; };
+struct WChunk<1, CK> { uint4 q[4][CK / 128]; Q4P s[4]; };
 template <int CK>
 struct WChunk<0, CK> { uint4 d[4][CK / 32]; };
 
-template <class TT, int WQ, int MODE, int CK>
+// FMT: the 4-bit format of the weights (signed with a scale per 32 values,
+// or affine with a (scale, bias) word per 32 / 64 values)
+template <class TT, int WQ, int MODE, int CK, int FMT>
 __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
   using S = typename TT::S;
   using V8 = typename TT::V8;
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
     const int col0 = MODE == 0 ? nb * 128 + wave * 32 : nb * 256 + wave * 64;
     const bool active = col0 < N;       // wave-uniform
     const char* bp[4];
-    const uint16_t* bsp[4];
+    const char* bsp[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       int row;
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
       const size_t wrow = (size_t)e * N + row;
       if (WQ) {
         bp[cb] = (const char*)base + wrow * (size_t)(K / 2);
-        bsp[cb] = (const uint16_t*)sbase + wrow * (size_t)(K / 32);
+        bsp[cb] = (const char*)sbase + wrow * (size_t)(K / Q4F<FMT>::kGroup) * Q4F<FMT>::kPB;
       } else {
         bp[cb] = (const char*)base + wrow * (size_t)K * 2;
         bsp[cb] = nullptr;
@@ -146,10 +148,7 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
         if constexpr (WQ) {
 #pragma unroll
           for (int h = 0; h < CK / 128; ++h) w.q[cb][h] = ldg16(bp[cb] + k0 / 2 + h * 16);
-          if constexpr (CK == 256)   // two adjacent fp16 scales, 4-byte aligned
-            w.s[cb] = *reinterpret_cast<const uint32_t*>(bsp[cb] + k0 / 32);
-          else
-            w.s[cb] = (uint32_t)bsp[cb][k0 / 32];
+          w.s[cb] = load_q4p<FMT, CK / 128>(bsp[cb], k0);
         } else {
 #pragma unroll
           for (int i = 0; i < kSl; ++i) w.d[cb][i] = ldg16(bp[cb] + (size_t)k0 * 2 + i * 16);
@@ -184,8 +183,7 @@ __global__ __launch_bounds__(256, WIDE_OCC) void gemm_wide_kernel(GemmArgs a) {
             const uint4 wq = w.q[cb][i >> 2];
             const uint32_t word = (i & 3) == 0 ? wq.x : (i & 3) == 1 ? wq.y : (i & 3) == 2 ? wq.z : wq.w;
             // the lane's CK / 4 values span CK / 128 blocks of 32
-            const uint16_t sb = (uint16_t)(w.s[cb] >> (16 * (i >> 2)));
-            bv = __builtin_bit_cast(V8, dequant_word(word, __builtin_bit_cast(_Float16, sb)));
+            bv = __builtin_bit_cast(V8, dequant_word_f<FMT>(word, q4p_block<FMT>(w.s[cb], i >> 2)));
           } else {
             bv = __builtin_bit_cast(V8, w.d[cb][i]);
           }
@@ -269,19 +267,25 @@ hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
                             hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   // K is a multiple of 128 (the layer's D and F are)
-#define MOE_WIDE(TT, WQ, CK)                                                              \
+#define MOE_WIDE(TT, WQ, CK, F_)                                                          \
   do {                                                                                    \
     if (a.mode == 0)                                                                      \
-      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 0, CK>), dim3(grid), dim3(256), 0, s, a); \
+      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 0, CK, F_>), dim3(grid), dim3(256), 0, s, a); \
     else                                                                                  \
-      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 1, CK>), dim3(grid), dim3(256), 0, s, a); \
+      hipLaunchKernelGGL((gemm_wide_kernel<TT, WQ, 1, CK, F_>), dim3(grid), dim3(256), 0, s, a); \
+  } while (0)
+#define MOE_WIDE_K(F_)                              \
+  do {                                              \
+    if (a.K % 256 == 0) MOE_WIDE(WF16, 1, 256, F_); \
+    else MOE_WIDE(WF16, 1, 128, F_);                \
   } while (0)
   if (a.K % 128) return hipErrorInvalidValue;
-  if (xdt == MOE_F16 && wdt == MOE_Q4B32) {
-    if (a.K % 256 == 0) MOE_WIDE(WF16, 1, 256);
-    else MOE_WIDE(WF16, 1, 128);
-  }
-  else return hipErrorInvalidValue;   // 16-bit weights take the stream tile
+  const int fmt = q4_fmt(wdt);
+  if (xdt != MOE_F16 || fmt < 0) return hipErrorInvalidValue;   // 16-bit weights take the stream tile
+  if (fmt == 0) MOE_WIDE_K(0);
+  else if (fmt == 1) MOE_WIDE_K(1);
+  else MOE_WIDE_K(2);
+#undef MOE_WIDE_K
 #undef MOE_WIDE
   return hipGetLastError();
 }

@@ -183,7 +183,7 @@ bool dtypes_ok(int xdt, int wdt) {
   return (xdt == MOE_F32 && wdt == MOE_F32) ||
          (xdt == MOE_BF16 && wdt == MOE_BF16) ||
          (xdt == MOE_F16 && wdt == MOE_F16) ||
-         (xdt == MOE_F16 && wdt == MOE_Q4B32);
+         (xdt == MOE_F16 && q4_fmt(wdt) >= 0);
 }
 
 int effective_fat_rows(const moe_options& o) {
@@ -199,7 +199,7 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.cap_tiles = n_exp + (int)(Pmax / kFullBM) + 1;
   L.cap_sk1 = n_exp;
   L.cap_sk4 = n_exp + (int)(Pmax / kSkRows) + 1;
-  L.fat_rows = wdt == MOE_Q4B32 ? effective_fat_rows(o) : 0;
+  L.fat_rows = q4_fmt(wdt) >= 0 ? effective_fat_rows(o) : 0;
   L.max_fat = 0;
   if (L.fat_rows > 0)
     L.max_fat = (int)std::min<int64_t>(n_exp, Pmax / L.fat_rows);
@@ -209,7 +209,7 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
              stream_supported(1, F, D, wdt);
   if (wdt == MOE_F32) {
     L.can_full = false; L.can_sk1 = true; L.can_sk4 = true; L.can_fat = false;
-  } else if (wdt == MOE_Q4B32) {
+  } else if (q4_fmt(wdt) >= 0) {
     L.can_fat = L.max_fat > 0;
     L.can_full = L.can_fat;
     L.can_sk1 = true;
@@ -269,10 +269,13 @@ bool weight_ok(const moe_weight& w, int wdt, std::string* why, const char* name)
   }
   if (!w.data) { snprintf(buf, sizeof buf, "%s data is NULL", name); *why = buf; return false; }
   if (!aligned16(w.data)) { snprintf(buf, sizeof buf, "%s data not 16-byte aligned", name); *why = buf; return false; }
-  if (wdt == MOE_Q4B32) {
-    if (!w.scales) { snprintf(buf, sizeof buf, "%s scales NULL for Q4B32", name); *why = buf; return false; }
-    if ((reinterpret_cast<uintptr_t>(w.scales) & 1u) != 0) {
-      snprintf(buf, sizeof buf, "%s scales not 2-byte aligned", name); *why = buf; return false;
+  if (q4_fmt(wdt) >= 0) {
+    if (!w.scales) { snprintf(buf, sizeof buf, "%s scales NULL for 4-bit weights", name); *why = buf; return false; }
+    // a lane reads two adjacent parameters as one load
+    const uintptr_t al = wdt == MOE_Q4B32 ? 3u : 7u;
+    if ((reinterpret_cast<uintptr_t>(w.scales) & al) != 0) {
+      snprintf(buf, sizeof buf, "%s scales not %d-byte aligned", name, (int)al + 1);
+      *why = buf; return false;
     }
   }
   return true;
@@ -579,7 +582,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     ClassifyArgs ca{};
     ca.counts = (const int32_t*)(pb + p->L.counts);
     ca.n_exp = n_exp;
-    ca.mode = wdt == MOE_F32 ? 0 : (wdt == MOE_Q4B32 ? 2 : 1);
+    ca.mode = wdt == MOE_F32 ? 0 : (q4_fmt(wdt) >= 0 ? 2 : 1);
     ca.S = (double)o.splitk_max_pairs;
     ca.full_nnb = F / 128;
     ca.full_fill = (ca.mode == 1 && !(o.flags & MOE_OPT_EXACT_ROUTES)) ? info.ncu : 0;
@@ -605,7 +608,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   const int64_t row_bound = d.T;
   const bool run_fat = L.can_fat && row_bound >= L.fat_rows;
   const bool run_full = L.can_full &&
-      (wdt == MOE_Q4B32 ? run_fat : (double)row_bound > (double)o.splitk_max_pairs);
+      (q4_fmt(wdt) >= 0 ? run_fat : (double)row_bound > (double)o.splitk_max_pairs);
   const bool run_sk1 = L.can_sk1;
   const bool run_sk4 = L.can_sk4 && row_bound > 16;
   if (run_fat) {
@@ -618,7 +621,8 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     const int rows[3] = {F, F, D};
     const int Ks[3] = {D, D, F};
     e = launch_dequant_fat(q, sc, out, rows, Ks, 3,
-                           (const int32_t*)(b + L.fat_list), meta, grid, s);
+                           (const int32_t*)(b + L.fat_list), meta, grid,
+                           q4_fmt(wdt), s);
     if (e != hipSuccess) return hip_fail(e, "dequant kernel");
   }
 
@@ -732,7 +736,28 @@ moe_status moe_dequant_q4(const void* data, const void* scales, int64_t rows,
   if (!data || !scales || !out_f16) return fail(MOE_EINVAL, "NULL pointer");
   if (!aligned16(data) || !aligned16(out_f16) || (reinterpret_cast<uintptr_t>(scales) & 1u))
     return fail(MOE_EINVAL, "data/out must be 16-byte aligned, scales 2-byte");
-  hipError_t e = launch_dequant_rows(data, scales, out_f16, rows, (int)K,
+  hipError_t e = launch_dequant_rows(data, scales, out_f16, rows, (int)K, 0,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequant kernel");
+  return MOE_OK;
+}
+
+moe_status moe_dequant_weights(int32_t dtype, const void* data,
+                               const void* scales, int64_t rows, int64_t K,
+                               void* out_f16, void* stream) {
+  const int fmt = q4_fmt(dtype);
+  if (fmt < 0) return fail(MOE_EUNSUPPORTED, "dtype %d is not a 4-bit format", dtype);
+  const int G = dtype == MOE_Q4A64 ? 64 : 32;
+  if (rows < 0 || K <= 0 || K % G)
+    return fail(MOE_EINVAL, "rows >= 0 and K a positive multiple of %d", G);
+  if (K > (1 << 30)) return fail(MOE_EUNSUPPORTED, "K too large");
+  if (rows == 0) return MOE_OK;
+  if (!data || !scales || !out_f16) return fail(MOE_EINVAL, "NULL pointer");
+  const uintptr_t al = fmt == 0 ? 1u : 3u;
+  if (!aligned16(data) || !aligned16(out_f16) ||
+      (reinterpret_cast<uintptr_t>(scales) & al))
+    return fail(MOE_EINVAL, "data/out must be 16-byte aligned, scales %d-byte", (int)al + 1);
+  hipError_t e = launch_dequant_rows(data, scales, out_f16, rows, (int)K, fmt,
                                      reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "dequant kernel");
   return MOE_OK;

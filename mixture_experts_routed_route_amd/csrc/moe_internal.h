@@ -52,6 +52,13 @@ constexpr int kStreamMaxRuns = 512;
 constexpr int kStreamSlotFloats = 8192;
 constexpr int kStreamTokRows = 64;
 
+// The format of a 4-bit weight dtype: 0 signed with an fp16 scale per 32
+// K values, 1 / 2 affine with an fp16 (scale, bias) pair per 32 / 64; -1 if
+// the dtype is not a 4-bit one.
+inline int q4_fmt(int wdt) {
+  return wdt == MOE_Q4B32 ? 0 : wdt == MOE_Q4A32 ? 1 : wdt == MOE_Q4A64 ? 2 : -1;
+}
+
 // Forward route tags per expert.
 enum Route : int32_t { kRouteNone = 0, kRouteSplitK = 1, kRouteFull = 2,
                        kRouteFat = 3 };
@@ -163,12 +170,15 @@ hipError_t launch_gemm_stream(const GemmArgs& a, int xdt, int wdt, int rows,
                               int grid, hipStream_t s);
 hipError_t launch_gemm_wide(const GemmArgs& a, int xdt, int wdt, int grid,
                             hipStream_t s);
+// fmt: the 4-bit format (q4_fmt in device_common.h): 0 signed with a scale
+// per 32 values, 1 / 2 affine with a (scale, bias) word per 32 / 64 values
 hipError_t launch_dequant_fat(const void* const q[3], const void* const sc[3],
                               void* const out[3], const int rows[3],
                               const int K[3], int n, const int32_t* fat_list,
-                              const int32_t* meta, int grid, hipStream_t s);
+                              const int32_t* meta, int grid, int fmt,
+                              hipStream_t s);
 hipError_t launch_dequant_rows(const void* q, const void* sc, void* out,
-                               int64_t rows, int K, hipStream_t s);
+                               int64_t rows, int K, int fmt, hipStream_t s);
 hipError_t launch_combine(const void* ypair, int ypair_f16,
                           const int32_t* tok2pair, const float* topk_w,
                           const int32_t* offsets, int T, int D, int k,

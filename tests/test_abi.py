@@ -180,3 +180,12 @@ def test_python_route_rejects_bad_tensors():
         moe.moe_route(x, torch.zeros(8, 12, dtype=torch.bfloat16), 2)
     with pytest.raises(ValueError):
         moe.moe_route(x.view(-1), torch.zeros(8, 16, dtype=torch.bfloat16), 2)
+
+
+def test_affine_params_shape_picks_format():
+    d = torch.zeros(2, 8, 64, dtype=torch.uint8)
+    assert moe.q4_dtype(d, torch.zeros(2, 8, 4, dtype=torch.float16)) == moe.MOE_Q4B32
+    assert moe.q4_dtype(d, torch.zeros(2, 8, 4, 2, dtype=torch.float16)) == moe.MOE_Q4A32
+    assert moe.q4_dtype(d, torch.zeros(2, 8, 2, 2, dtype=torch.float16)) == moe.MOE_Q4A64
+    with pytest.raises(ValueError):
+        moe.q4_dtype(d, torch.zeros(2, 8, 3, 2, dtype=torch.float16))

@@ -170,7 +170,8 @@ def make_layer(T: int, D: int, F: int, E: int, k: int, dtype: str, *,
 
 
 def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
-           pairs_per_expert=None, with_weights: bool = True) -> dict:
+           pairs_per_expert=None, with_weights: bool = True,
+           w_dtype: str | None = None) -> dict:
     """The five named workloads (sizes from the routed-MoE pages).
 
     1 tiny fp32: T=64, D=128, F=256, E=8, top-2, cf 0.
@@ -185,7 +186,15 @@ def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
       routed expert holds exactly p pairs.
     6 decode on the layer of 5: T in 1..8 (default 1), N(0,1) logits.
     7 decode on the layer of 4: T in 1..8 (default 1), Zipf(1.1) bias.
+
+    ``w_dtype`` (4 and 7 only) swaps the 4-bit format: "q4a64" / "q4a32"
+    give affine 4-bit weights (groups of 64 / 32, fp16 scale and bias) of
+    the same shapes; the name gets the format as a suffix.
     """
+    if w_dtype not in (None, Q4B32) and n not in (4, 7):
+        raise ValueError("w_dtype applies to the 4-bit workloads 4 and 7")
+    wq = w_dtype or Q4B32
+    suffix = "" if wq == Q4B32 else "_" + wq
     if n == 1:
         return make_layer(64, 128, 256, 8, 2, F32, seed=seed,
                           capacity_factor=capacity_factor or 0.0,
@@ -207,10 +216,11 @@ def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
     if n == 4:
         g = _gen(seed + 1000)
         bias = zipf_bias(256, 1.1, g)
-        return make_layer(13312, 4096, 2048, 256, 8, F16, w_dtype=Q4B32,
+        return make_layer(13312, 4096, 2048, 256, 8, F16, w_dtype=wq,
                           logit_bias=bias, seed=seed,
                           capacity_factor=capacity_factor or 0.0,
-                          name=CONFIG_NAMES[4], with_weights=with_weights)
+                          name=CONFIG_NAMES[4] + suffix,
+                          with_weights=with_weights)
     if n == 5:
         if pairs_per_expert is not None:
             p = int(pairs_per_expert)
@@ -238,9 +248,9 @@ def config(n: int, *, seed: int = 0, capacity_factor=None, T=None,
         T7 = 1 if T is None else int(T)
         g = _gen(seed + 1000)
         bias = zipf_bias(256, 1.1, g)
-        return make_layer(T7, 4096, 2048, 256, 8, F16, w_dtype=Q4B32,
+        return make_layer(T7, 4096, 2048, 256, 8, F16, w_dtype=wq,
                           logit_bias=bias, seed=seed,
-                          name=f"{CONFIG_NAMES[7]}_T{T7}",
+                          name=f"{CONFIG_NAMES[7]}_T{T7}{suffix}",
                           with_weights=with_weights)
     raise ValueError(f"no workload {n}")
 
