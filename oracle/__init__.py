@@ -12,6 +12,8 @@ listed below; all are pinned by tests in ``tests/test_oracle_*.py``:
 
   route / limit / plan / expert / layer / decode   pinned (brute force,
   closed forms, invariants, numpy library routines).
+  backward / dlogits   pinned (torch float64 autograd of the dense masked
+  layer; central differences of the oracle's own route + layer).
   router_logits / router_stats   pinned (a hand-worked product, one-hot rows,
   closed forms for equal logits and for two experts, a balanced first choice,
   subset enumeration on tiny inputs).
@@ -70,6 +72,10 @@ def lib():
         L.orc_decode_f16.argtypes = [vp, i64, vp]
         L.orc_router_logits.argtypes = [i64, i64, i32, vp, i32, vp, vp]
         L.orc_router_stats.argtypes = [i64, i32, i32, vp, dbl, vp, vp]
+        L.orc_backward.argtypes = [i64, i64, i64, i32, i32, i32, vp, i32, vp,
+                                   vp, vp, vp, vp, vp, i32, dbl, vp, vp, vp,
+                                   vp, i64, vp, vp, i32, vp, vp, vp, vp, vp]
+        L.orc_dlogits.argtypes = [i64, i32, i32, vp, vp, vp, vp]
         L.orc_num_threads.restype = i32
         _lib = L
     return _lib
@@ -218,6 +224,54 @@ def layer(x, w_gate, w_up, w_down, ids, w, keep, *, E: int, n_shared: int,
     if rc != 0:
         raise ValueError(f"orc_layer failed ({rc})")
     return y
+
+
+def backward(x, w_gate, w_up, w_down, ids, w, keep, dy, *, E: int,
+             n_shared: int, x_dtype: str, w_dtype: str, c: float,
+             tokens=None, experts=None, want=("dx", "dw", "dtw")) -> dict:
+    """Gradients of L = sum(dy * y) in float64: dx [tokens or T, D], dw_gate /
+    dw_up [experts or E + n_shared, F, D], dw_down [.., D, F], dtw [T, k]."""
+    xa = _np(x)
+    T, D = xa.shape
+    wg, wgs = _weight(w_gate)
+    wu, wus = _weight(w_up)
+    wd, wds = _weight(w_down)
+    F = wg.shape[1]
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = np.ascontiguousarray(w, np.float64)
+    keep = np.ascontiguousarray(keep, np.uint8)
+    dy = np.ascontiguousarray(_np(dy), np.float64)
+    k = ids.shape[1]
+    tl = None if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    el = None if experts is None else np.ascontiguousarray(experts, np.int32)
+    nt = T if tl is None else tl.shape[0]
+    ne = E + n_shared if el is None else el.shape[0]
+    out = {}
+    dx = np.zeros((nt, D)) if "dx" in want else None
+    dwg = np.zeros((ne, F, D)) if "dw" in want else None
+    dwu = np.zeros((ne, F, D)) if "dw" in want else None
+    dwd = np.zeros((ne, D, F)) if "dw" in want else None
+    dtw = np.zeros((T, k)) if "dtw" in want else None
+    rc = lib().orc_backward(T, D, F, E, k, n_shared, _p(xa), DT[x_dtype],
+                            _p(wg), _p(wgs), _p(wu), _p(wus), _p(wd), _p(wds),
+                            DT[w_dtype], float(c), _p(ids), _p(w), _p(keep),
+                            _p(dy), nt, _p(tl), _p(dx), ne, _p(el), _p(dwg),
+                            _p(dwu), _p(dwd), _p(dtw))
+    if rc != 0:
+        raise ValueError(f"orc_backward failed ({rc})")
+    out.update(dx=dx, dw_gate=dwg, dw_up=dwu, dw_down=dwd, dtw=dtw)
+    return out
+
+
+def dlogits(ids, w, dtw, E: int) -> np.ndarray:
+    """Gradient of the logits [T, E] through the renormalised top-k weights."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = np.ascontiguousarray(w, np.float64)
+    dtw = np.ascontiguousarray(dtw, np.float64)
+    T, k = ids.shape
+    out = np.zeros((T, E))
+    lib().orc_dlogits(T, E, k, _p(ids), _p(w), _p(dtw), _p(out))
+    return out
 
 
 def decode(w, e: int, w_dtype: str) -> np.ndarray:

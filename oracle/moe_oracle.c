@@ -23,6 +23,10 @@
  *   combine  y[t] = sum over kept pairs of weight * expert output; a dropped
  *            pair adds nothing (the weights are filtered by `keep` after they
  *            were normalised, mini-AGI PR #4, minagi/pool.py).
+ *   backward gradients of the layer (x, the three expert weights, the
+ *            routing weights and, through them, the logits): the same
+ *            gradients on every expert slot whatever the dispatch (mini-AGI
+ *            PR #4, tests/test_dispatch.py).
  *   router   logits = x Wr^T, the linear map from d_model to the experts
  *            whose output `requested(scores)` ranks, and the statistics that
  *            function keeps beside the routing: the top-k mass before
@@ -379,6 +383,202 @@ int orc_layer(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
         }
         free(xt);
         free(yp);
+    }
+    return 0;
+}
+
+/* ---- backward ---------------------------------------------------------- */
+
+/*
+ * Gradients of L = sum_t dy[t] . y[t] for one kept pair (token row x, expert
+ * e) whose output is scaled by its weight: dyp = weight * dy[t]. The layer's
+ * forward is y[t] = sum_j keep * w_j * FFN_e(x[t]) (+ the shared expert's
+ * FFN), FFN_e(x) = W_down h, h = silu(min(g, c)) * clamp(u, -c, c),
+ * g = W_gate x, u = W_up x (mini-AGI PR #4, minagi/pool.py, `experts()`;
+ * the clamp of Strata PR #4366, "Approach"). The clamps pass the gradient
+ * where the value is not clamped, boundaries included (g <= c, -c <= u <=
+ * c), like a clamp's subgradient in autograd. Accumulates into dx (D),
+ * dwg / dwu (F x D), dwd (D x F) when they are not NULL.
+ */
+static void pair_backward(int64_t D, int64_t F, int64_t e, const double *x,
+                          const void *wg, const void *wg_s, const void *wu,
+                          const void *wu_s, const void *wd, const void *wd_s,
+                          int w_dtype, double c, const double *dyp, double *dx,
+                          double *dwg, double *dwu, double *dwd)
+{
+    double *g = malloc((size_t)F * sizeof *g);
+    double *u = malloc((size_t)F * sizeof *u);
+    double *h = malloc((size_t)F * sizeof *h);
+    double *yp = malloc((size_t)D * sizeof *yp);
+    expert_ffn(D, F, e, x, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype, c, g, u, h, yp);
+    for (int64_t f = 0; f < F; ++f) {
+        double dh = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            dh += weight_value(wd, wd_s, w_dtype, e, D, F, d, f) * dyp[d];
+        double gc = g[f], uc = u[f], mg = 1.0, mu = 1.0;
+        if (c > 0.0) {
+            if (g[f] > c) { gc = c; mg = 0.0; }
+            if (u[f] < -c) { uc = -c; mu = 0.0; }
+            if (u[f] > c) { uc = c; mu = 0.0; }
+        }
+        double sg = 1.0 / (1.0 + exp(-gc));
+        double dsilu = sg * (1.0 + gc * (1.0 - sg));
+        double dg = dh * uc * dsilu * mg;
+        double du = dh * gc * sg * mu;
+        for (int64_t d = 0; d < D; ++d) {
+            double wgv = weight_value(wg, wg_s, w_dtype, e, F, D, f, d);
+            double wuv = weight_value(wu, wu_s, w_dtype, e, F, D, f, d);
+            if (dx)
+                dx[d] += wgv * dg + wuv * du;
+            if (dwg)
+                dwg[f * D + d] += dg * x[d];
+            if (dwu)
+                dwu[f * D + d] += du * x[d];
+        }
+        if (dwd)
+            for (int64_t d = 0; d < D; ++d)
+                dwd[d * F + f] += dyp[d] * h[f];
+    }
+    free(g); free(u); free(h); free(yp);
+}
+
+/*
+ * Backward of the layer for L = sum_t dy[t] . y[t] (dy [T, D] double):
+ *   dx   [n_tok, D]        for the tokens of tok_list (all T if NULL);
+ *   dwg, dwu [n_exp, F, D] and dwd [n_exp, D, F] for the experts of
+ *        exp_list (all E + n_shared if NULL; index E is the shared one);
+ *   dtw  [T, k]            gradient of each routing weight w_j: dy[t] .
+ *        FFN(x[t]) for a kept pair, 0 for a dropped one (NULL: skipped).
+ * Gradients of the expert weights are the sums over the expert's kept pairs
+ * -- "the same gradients on every slot" is what mini-AGI PR #4's
+ * tests/test_dispatch.py asks of any dispatch. Any pointer may be NULL.
+ */
+int orc_backward(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
+                 const void *x, int x_dtype, const void *wg, const void *wg_s,
+                 const void *wu, const void *wu_s, const void *wd,
+                 const void *wd_s, int w_dtype, double c, const int32_t *ids,
+                 const double *w, const uint8_t *keep, const double *dy,
+                 int64_t n_tok, const int64_t *tok_list, double *dx,
+                 int n_exp, const int32_t *exp_list, double *dwg, double *dwu,
+                 double *dwd, double *dtw)
+{
+    if (x_dtype < ORC_F32 || x_dtype > ORC_F16 || w_dtype < ORC_F32 ||
+        w_dtype > ORC_Q4A64)
+        return -1;
+    if (!tok_list)
+        n_tok = T;
+    if (!exp_list)
+        n_exp = E + n_shared;
+    if (dx) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_tok; ++i) {
+            int64_t t = tok_list ? tok_list[i] : i;
+            double *xt = malloc((size_t)D * sizeof *xt);
+            double *dyp = malloc((size_t)D * sizeof *dyp);
+            double *dxt = dx + i * D;
+            for (int64_t d = 0; d < D; ++d) {
+                xt[d] = dense_value(x, x_dtype, (size_t)(t * D + d));
+                dxt[d] = 0.0;
+            }
+            for (int j = 0; j <= k; ++j) {
+                int64_t e;
+                double wt;
+                if (j < k) {
+                    if (!keep[t * k + j])
+                        continue;
+                    e = ids[t * k + j];
+                    wt = w[t * k + j];
+                } else {
+                    if (!n_shared)
+                        break;
+                    e = E;
+                    wt = 1.0;
+                }
+                for (int64_t d = 0; d < D; ++d)
+                    dyp[d] = wt * dy[t * D + d];
+                pair_backward(D, F, e, xt, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype,
+                              c, dyp, dxt, NULL, NULL, NULL);
+            }
+            free(xt); free(dyp);
+        }
+    }
+    if (dwg || dwu || dwd) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int i = 0; i < n_exp; ++i) {
+            int64_t e = exp_list ? exp_list[i] : i;
+            double *xt = malloc((size_t)D * sizeof *xt);
+            double *dyp = malloc((size_t)D * sizeof *dyp);
+            double *g_ = dwg ? dwg + (size_t)i * F * D : NULL;
+            double *u_ = dwu ? dwu + (size_t)i * F * D : NULL;
+            double *d_ = dwd ? dwd + (size_t)i * D * F : NULL;
+            if (g_) memset(g_, 0, (size_t)F * D * sizeof *g_);
+            if (u_) memset(u_, 0, (size_t)F * D * sizeof *u_);
+            if (d_) memset(d_, 0, (size_t)D * F * sizeof *d_);
+            for (int64_t t = 0; t < T; ++t) {
+                double wt = 0.0;
+                int hit = 0;
+                if (e == E) {
+                    hit = n_shared;
+                    wt = 1.0;
+                } else {
+                    for (int j = 0; j < k; ++j)
+                        if (ids[t * k + j] == e && keep[t * k + j]) {
+                            hit = 1;
+                            wt = w[t * k + j];
+                        }
+                }
+                if (!hit)
+                    continue;
+                for (int64_t d = 0; d < D; ++d) {
+                    xt[d] = dense_value(x, x_dtype, (size_t)(t * D + d));
+                    dyp[d] = wt * dy[t * D + d];
+                }
+                pair_backward(D, F, e, xt, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype,
+                              c, dyp, NULL, g_, u_, d_);
+            }
+            free(xt); free(dyp);
+        }
+    }
+    if (dtw) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t) {
+            double *xt = malloc((size_t)D * sizeof *xt);
+            double *yp = malloc((size_t)D * sizeof *yp);
+            for (int64_t d = 0; d < D; ++d)
+                xt[d] = dense_value(x, x_dtype, (size_t)(t * D + d));
+            for (int j = 0; j < k; ++j) {
+                double s = 0.0;
+                if (keep[t * k + j]) {
+                    expert_ffn(D, F, ids[t * k + j], xt, wg, wg_s, wu, wu_s, wd,
+                               wd_s, w_dtype, c, NULL, NULL, NULL, yp);
+                    for (int64_t d = 0; d < D; ++d)
+                        s += dy[t * D + d] * yp[d];
+                }
+                dtw[t * k + j] = s;
+            }
+            free(xt); free(yp);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Gradient of the logits through the chosen weights w_j = exp(l_j - l_0) /
+ * sum_i exp(l_i - l_0) (softmax renormalised over the k chosen): dl[t, e_j]
+ * = w_j (dtw_j - sum_i w_i dtw_i); experts not chosen get 0 (the top-k
+ * choice is constant under small changes of the logits). out [T, E].
+ */
+int orc_dlogits(int64_t T, int E, int k, const int32_t *ids, const double *w,
+                const double *dtw, double *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int j = 0; j < k; ++j)
+            s += w[t * k + j] * dtw[t * k + j];
+        for (int e = 0; e < E; ++e)
+            out[t * E + e] = 0.0;
+        for (int j = 0; j < k; ++j)
+            out[t * E + ids[t * k + j]] = w[t * k + j] * (dtw[t * k + j] - s);
     }
     return 0;
 }

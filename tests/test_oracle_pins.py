@@ -537,3 +537,113 @@ def test_router_stats_empty_and_nan():
     lg[1, 2] = np.nan
     with pytest.raises(ValueError):
         oracle.router_stats(lg, 2)
+
+
+# ------------------------------------------------------------- backward ---
+
+def _autograd_dense(wl, ids, w, keep, dy, c):
+    """The dense masked layer in torch float64 with autograd: every kept
+    pair's FFN on its token, weighted, plus the shared expert; gradients of
+    sum(dy * y) for x, the three weights and the routing weights."""
+    T, D = wl["x"].shape
+    E, ns = wl["E"], wl["n_shared"]
+    x = wl["x"].to(torch.float64).clone().requires_grad_(True)
+    Wg = torch.from_numpy(np.stack([oracle.decode(wl["w_gate"], e, wl["w_dtype"])
+                                    for e in range(E + ns)])).requires_grad_(True)
+    Wu = torch.from_numpy(np.stack([oracle.decode(wl["w_up"], e, wl["w_dtype"])
+                                    for e in range(E + ns)])).requires_grad_(True)
+    Wd = torch.from_numpy(np.stack([oracle.decode(wl["w_down"], e, wl["w_dtype"])
+                                    for e in range(E + ns)])).requires_grad_(True)
+    wt = torch.from_numpy(np.asarray(w, np.float64)).requires_grad_(True)
+
+    def ffn(e, xr):
+        g = Wg[e] @ xr
+        u = Wu[e] @ xr
+        if c > 0:
+            g = torch.clamp(g, max=c)
+            u = torch.clamp(u, -c, c)
+        return Wd[e] @ (torch.nn.functional.silu(g) * u)
+
+    rows = []
+    for t in range(T):
+        acc = torch.zeros(D, dtype=torch.float64)
+        for j in range(ids.shape[1]):
+            if keep[t, j]:
+                acc = acc + wt[t, j] * ffn(int(ids[t, j]), x[t])
+        if ns:
+            acc = acc + ffn(E, x[t])
+        rows.append(acc)
+    y = torch.stack(rows)
+    (y * torch.from_numpy(dy)).sum().backward()
+    return dict(dx=x.grad.numpy(), dw_gate=Wg.grad.numpy(), dw_up=Wu.grad.numpy(),
+                dw_down=Wd.grad.numpy(), dtw=wt.grad.numpy())
+
+
+@pytest.mark.parametrize("n_shared,cf,c", [(0, 0.0, 7.0), (1, 1.0, 0.6),
+                                           (0, 1.5, 0.0)])
+def test_backward_matches_torch_autograd(n_shared, cf, c):
+    # a tight clamp (0.6) binds on both g and u; cf 1 and 1.5 drop pairs
+    wl = W.make_layer(12, 24, 20, 5, 2, W.BF16, seed=31, w_std=0.4,
+                      n_shared=n_shared)
+    ids, w = oracle.route(wl["logits"], 2)
+    pl = oracle.plan(ids, 5, cf, n_shared)
+    dy = np.random.default_rng(3).normal(size=(12, 24))
+    got = oracle.backward(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids,
+                          w, pl["keep"], dy, E=5, n_shared=n_shared,
+                          x_dtype="bf16", w_dtype="bf16", c=c)
+    ref = _autograd_dense(wl, ids, w, pl["keep"], dy, c)
+    for key in ("dx", "dw_gate", "dw_up", "dw_down", "dtw"):
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-10, atol=1e-12,
+                                   err_msg=key)
+    if cf > 0:
+        assert (pl["keep"] == 0).any()          # drops happened
+        assert np.all(got["dtw"][pl["keep"] == 0] == 0)
+
+
+def test_backward_subsets_match_full():
+    wl = W.make_layer(10, 16, 12, 6, 3, W.F16, seed=32, w_std=0.3, n_shared=1)
+    ids, w = oracle.route(wl["logits"], 3)
+    pl = oracle.plan(ids, 6, 0.0, 1)
+    dy = np.random.default_rng(4).normal(size=(10, 16))
+    kw = dict(E=6, n_shared=1, x_dtype="f16", w_dtype="f16", c=7.0)
+    full = oracle.backward(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids,
+                           w, pl["keep"], dy, **kw)
+    part = oracle.backward(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids,
+                           w, pl["keep"], dy, tokens=[7, 2], experts=[6, 1],
+                           want=("dx", "dw"), **kw)
+    assert np.array_equal(part["dx"], full["dx"][[7, 2]])
+    assert np.array_equal(part["dw_gate"], full["dw_gate"][[6, 1]])
+    assert np.array_equal(part["dw_down"], full["dw_down"][[6, 1]])
+
+
+def test_dlogits_central_differences():
+    # L(logits) = sum(dy * layer(route(logits))) at cf 0; a small change of
+    # the logits keeps the top-k choice, so dL/dl is the chain through the
+    # renormalised weights
+    wl = W.make_layer(4, 16, 12, 6, 3, W.BF16, seed=33, w_std=0.3)
+    dy = np.random.default_rng(5).normal(size=(4, 16))
+    kw = dict(E=6, n_shared=0, x_dtype="bf16", w_dtype="bf16", c=7.0)
+
+    def loss(lg):
+        ids, w = oracle.route(lg, 3)
+        keep = np.ones((4, 3), np.uint8)
+        y = oracle.layer(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids,
+                         w, keep, **kw)
+        return float((y * dy).sum()), ids
+
+    lg0 = wl["logits"].numpy().astype(np.float32)
+    ids, w = oracle.route(lg0, 3)
+    g = oracle.backward(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids,
+                        w, np.ones((4, 3), np.uint8), dy, want=("dtw",), **kw)
+    dl = oracle.dlogits(ids, w, g["dtw"], 6)
+    eps = 2.0 ** -10
+    for t in range(4):
+        for e in range(6):
+            a, b = lg0.copy(), lg0.copy()
+            a[t, e] += eps
+            b[t, e] -= eps
+            la, ia = loss(a)
+            lb, ib = loss(b)
+            assert np.array_equal(ia, ids) and np.array_equal(ib, ids)
+            fd = (la - lb) / (2 * eps)
+            assert fd == pytest.approx(dl[t, e], rel=2e-4, abs=1e-7), (t, e)
