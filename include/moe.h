@@ -263,6 +263,35 @@ moe_status moe_forward(const moe_plan *plan, const void *x, int32_t x_dtype,
                        void *ws, size_t ws_bytes, const moe_options *opt,
                        void *stream);
 
+/* --- backward ----------------------------------------------------------- */
+
+/* Bytes of device workspace moe_backward needs; 0 if unsupported. */
+size_t moe_backward_workspace_bytes(const moe_plan *plan, int32_t D, int32_t F,
+                                    int32_t x_dtype);
+
+/* Gradients of L = sum_t dy[t] . y[t] for the layer moe_forward computes on
+ * the same plan, x and weights (bf16 or f16 layers: x and the three weights
+ * in one 16-bit dtype; 4-bit weights are not trained here): dx [T, D],
+ * dw_gate / dw_up [E + n_shared, F, D], dw_down [E + n_shared, D, F], all
+ * f32 and overwritten; every expert slot gets the sum over its kept pairs
+ * (zeros for an expert with none), the property mini-AGI PR #4's
+ * tests/test_dispatch.py asks of every dispatch. Optional (NULL to skip):
+ * d_topk_w [T, k], the gradient of each routing weight (dy[t] . the pair's
+ * unweighted output; 0 for a dropped pair), and d_logits [T, E], through the
+ * renormalised top-k softmax (w_j (dw_j - sum_i w_i dw_i) on the chosen
+ * experts, 0 elsewhere). The expert outputs are recomputed from x (nothing
+ * is kept from the forward); per-pair intermediates (x rows, w dy, the
+ * SwiGLU output and its gradients) are held in the layer's dtype, products
+ * accumulate in f32. opt: the swiglu_limit of the forward (NULL: defaults).
+ * D and F multiples of 128; pointers 16-byte aligned, ws 256-byte aligned.
+ * Async on `stream`. */
+moe_status moe_backward(const moe_plan *plan, const void *x, int32_t x_dtype,
+                        moe_weight w_gate, moe_weight w_up, moe_weight w_down,
+                        int32_t D, int32_t F, const float *dy, float *dx,
+                        float *dw_gate, float *dw_up, float *dw_down,
+                        float *d_topk_w, float *d_logits, void *ws,
+                        size_t ws_bytes, const moe_options *opt, void *stream);
+
 /* --- standalone pieces ------------------------------------------------- */
 
 /* Dequantise rows of 4-bit block weights to fp16, once: out[r, c] =

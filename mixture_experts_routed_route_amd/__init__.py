@@ -55,6 +55,7 @@ EXPORTED = (
     "moe_forward_workspace_bytes", "moe_forward", "moe_dequant_q4",
     "moe_phase_times", "moe_last_error", "moe_version",
     "moe_route_workspace_bytes", "moe_route", "moe_dequant_weights",
+    "moe_backward_workspace_bytes", "moe_backward",
 )
 
 ROUTE_STATS = ("kept_mass", "want_k", "z_loss", "balance", "aux")
@@ -144,6 +145,12 @@ def library(path: str = LIB_PATH):
                             ctypes.c_float, vp, vp, vp, vp, sz, i32, vp,
                             ctypes.POINTER(vp)]
     L.moe_route.restype = i32
+    L.moe_backward_workspace_bytes.argtypes = [vp, i32, i32, i32]
+    L.moe_backward_workspace_bytes.restype = sz
+    L.moe_backward.argtypes = [vp, vp, i32, Weight, Weight, Weight, i32, i32,
+                               vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                               ctypes.POINTER(Options), vp]
+    L.moe_backward.restype = i32
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_version.argtypes = []
@@ -422,6 +429,52 @@ def moe_forward(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
     return out
 
 
+def moe_backward(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
+                 dy: torch.Tensor, options: Options | None = None,
+                 want_dtw: bool = False, want_dlogits: bool = False,
+                 workspace: torch.Tensor | None = None) -> dict:
+    """Gradients of sum(dy * y) for the layer moe_forward computes with the
+    same plan, x and 16-bit weights: dx [T, D], dw_gate / dw_up [E(+1), F,
+    D], dw_down [E(+1), D, F] (f32), and optionally d_topk_w [T, k] and
+    d_logits [T, E]."""
+    L = library()
+    if x.dtype not in (torch.bfloat16, torch.float16) or x.dim() != 2:
+        raise ValueError("backward takes a 2-D bfloat16/float16 x")
+    x = x.contiguous()
+    T, D = x.shape
+    F = w_gate.shape[1]
+    dy = dy.to(torch.float32).contiguous()
+    if dy.shape != (T, D) or dy.device != x.device:
+        raise ValueError("dy must be [T, D] on x's device")
+    o = options or moe_options_default()
+    wg, keep_g = _weight(w_gate, x.device)
+    wu, keep_u = _weight(w_up, x.device)
+    wd, keep_d = _weight(w_down, x.device)
+    xdt = _TORCH_TO_MOE[x.dtype]
+    nbytes = L.moe_backward_workspace_bytes(plan.handle, D, F, xdt)
+    if nbytes == 0:
+        raise MoeError(MOE_EUNSUPPORTED, moe_last_error())
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    n_exp = plan.E + plan.n_shared
+    f32 = dict(dtype=torch.float32, device=x.device)
+    out = dict(dx=torch.empty(T, D, **f32),
+               dw_gate=torch.empty(n_exp, F, D, **f32),
+               dw_up=torch.empty(n_exp, F, D, **f32),
+               dw_down=torch.empty(n_exp, D, F, **f32))
+    if want_dtw:
+        out["d_topk_w"] = torch.empty(T, plan.k, **f32)
+    if want_dlogits:
+        out["d_logits"] = torch.empty(T, plan.E, **f32)
+    ptr = lambda name: out[name].data_ptr() if name in out else None
+    _check(L.moe_backward(plan.handle, x.data_ptr(), xdt, wg, wu, wd, D, F,
+                          dy.data_ptr(), ptr("dx"), ptr("dw_gate"), ptr("dw_up"),
+                          ptr("dw_down"), ptr("d_topk_w"), ptr("d_logits"),
+                          workspace.data_ptr(), workspace.numel(),
+                          ctypes.byref(o), _stream(x.device)))
+    return out
+
+
 def moe_dequant_q4(data: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
     """fp16_rne(q * s) of [.., N, K/2] 4-bit rows; returns [.., N, K] fp16."""
     if data.dtype != torch.uint8 or scales.dtype != torch.float16:
@@ -466,3 +519,4 @@ def moe_phase_times(reset: bool = True) -> tuple:
 plan = moe_plan_create
 forward = moe_forward
 route = moe_route
+backward = moe_backward

@@ -1,0 +1,444 @@
+// Backward pass of the routed MoE layer on gfx950: gradients of
+// L = sum_t dy[t] . y[t] for x, the three expert weights, the routing
+// weights and (through the renormalised top-k softmax) the logits. Every
+// expert slot gets the sum over its kept pairs, whatever the dispatch -- the
+// property mini-AGI PR #4's tests/test_dispatch.py checks.
+//
+// Per kept pair p = (token t, expert e, weight w) in the plan's expert-sorted
+// order (a pair of the shared expert has w = 1):
+//   X_p  = x[t]                         dYp = w dy[t]        (compute dtype)
+//   [G | U] = X_p [W_gate; W_up]^T      (f32, recomputed)
+//   H    = silu(min(G, c)) clamp(U)     (compute dtype, as the forward)
+//   Yp   = H W_down^T                   dw_j = dy[t] . Yp     (f32)
+//   dH   = dYp W_down                   (f32)
+//   [dG | dU] = SwiGLU backward         (compute dtype)
+//   dXp  = dG W_gate + dU W_up          dx[t] = sum over its pairs (fixed order)
+//   dW_gate[e] = sum_p dG_p x_p^T,  dW_up[e] likewise,  dW_down[e] = sum_p dYp H_p^T
+// The six products run on one grouped MFMA kernel: 64 x 64 output tiles,
+// 32-deep K steps staged through LDS; an operand whose memory is contiguous
+// along K is copied in 16-byte pieces, one contiguous along the output
+// index (the weights read as [K, N], and both operands of the weight
+// gradients, whose K is the pair index) is transposed on its way into LDS.
+#include <type_traits>
+
+#include "device_common.h"
+
+namespace moe {
+
+namespace {
+
+struct BF16B { using S = __bf16; using V8 = bf16x8; };
+struct F16B { using S = _Float16; using V8 = half8; };
+
+constexpr int kBT = 64;   // output tile (rows and columns)
+constexpr int kBK = 32;   // K per LDS step
+
+__device__ __forceinline__ int bswz(int r, int c) {
+  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
+
+}  // namespace
+
+// One operand of a grouped product. Element (i, k) of expert e:
+//   KC (contiguous along K): base[(row0 + i) * ld + k]
+//   IC (contiguous along i): base[(row0 + k) * ld + i]
+// base = p + e * estride (a weight, estride > 0) or p (a per-pair buffer,
+// estride == 0, whose rows start at the expert's first pair: row0 =
+// offsets[e]). With p2, K values from k_split on come from p2 (k - k_split).
+struct BOp {
+  const void* p;
+  const void* p2;
+  int ld;
+  int k_split;
+  int64_t estride;
+};
+
+struct BGemmArgs {
+  BOp a, b;
+  int mode;                 // 0: per pair (rows = the expert's pairs), 1:
+                            // weight gradient (K = the expert's pairs)
+  int M, N, K;              // mode 0: N, K fixed; mode 1: M, N fixed
+  float* c;                 // f32 output
+  int ldc;
+  int64_t c_estride;        // mode 1: output matrix of expert e at e * c_estride
+  const int32_t* offsets;   // [n_exp + 1]
+  const int32_t* tiles;     // mode 0: (expert, first row) per 64-row tile
+  const int32_t* n_tiles;   // mode 0: number of tiles (device)
+  int n_exp;
+};
+
+template <class TT, bool KC>
+__device__ __forceinline__ void load_tile(const BOp& o, int e, int row_base,
+                                          int i0, int ni, int k0, int nk,
+                                          uint4& v, int tid) {
+  // KC: thread -> row i = tid / 4, 8 K values at chunk tid % 4
+  // IC: thread -> k = tid / 8, 8 i values at chunk tid % 8
+  const char* base;
+  int kk = k0;
+  if (o.p2 && k0 >= o.k_split) { base = (const char*)o.p2; kk = k0 - o.k_split; }
+  else base = (const char*)o.p;
+  if (o.estride) base += (size_t)e * o.estride * 2;
+  v = uint4{0u, 0u, 0u, 0u};
+  if constexpr (KC) {
+    const int i = tid >> 2, c = tid & 3;
+    if (i < ni && k0 + c * 8 < nk) {
+      const size_t row = (size_t)(row_base + i0 + i);
+      v = *reinterpret_cast<const uint4*>(base + (row * o.ld + kk + c * 8) * 2);
+    }
+  } else {
+    const int k = tid >> 3, c = tid & 7;
+    if (k0 + k < nk && c * 8 < ni) {
+      const size_t row = (size_t)(row_base + kk + k);
+      v = *reinterpret_cast<const uint4*>(base + (row * o.ld + i0 + c * 8) * 2);
+    }
+  }
+}
+
+template <bool KC>
+__device__ __forceinline__ void store_tile(char* s, const uint4& v, int tid) {
+  if constexpr (KC) {
+    const int i = tid >> 2, c = tid & 3;
+    *reinterpret_cast<uint4*>(s + bswz(i, c)) = v;
+  } else {
+    const int k = tid >> 3, c = tid & 7;
+    uint16_t h[8];
+    __builtin_memcpy(h, &v, 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = c * 8 + j;
+      *reinterpret_cast<uint16_t*>(s + bswz(r, k >> 3) + (k & 7) * 2) = h[j];
+    }
+  }
+}
+
+template <class TT, bool AKC, bool BKC, int MODE>
+__global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs g) {
+  using V8 = typename TT::V8;
+  __shared__ __attribute__((aligned(16))) char sA[2][kBT * 64];
+  __shared__ __attribute__((aligned(16))) char sB[2][kBT * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int e, m0, Me, n0, K, arow, brow;
+  float* cbase;
+  size_t crow0;
+  if constexpr (MODE == 0) {
+    const int nt = g.N / kBT;
+    const int ti = blockIdx.x / nt;
+    if (ti >= *g.n_tiles) return;   // block-uniform, before any barrier
+    n0 = (blockIdx.x - ti * nt) * kBT;
+    e = g.tiles[2 * ti];
+    m0 = g.tiles[2 * ti + 1];
+    const int off = g.offsets[e];
+    Me = min(kBT, g.offsets[e + 1] - off - m0);
+    K = g.K;
+    arow = off;          // A: pair rows of the expert
+    brow = 0;            // B: the expert's weight
+    cbase = g.c;
+    crow0 = (size_t)(off + m0);
+  } else {
+    const int mt = g.M / kBT, nt = g.N / kBT;
+    const int per = mt * nt;
+    e = blockIdx.x / per;
+    const int r = blockIdx.x - e * per;
+    m0 = (r / nt) * kBT;
+    n0 = (r % nt) * kBT;
+    Me = kBT;
+    const int off = g.offsets[e];
+    K = g.offsets[e + 1] - off;
+    arow = off;          // both operands: the expert's pairs along K
+    brow = off;
+    cbase = g.c + (size_t)e * g.c_estride;
+    crow0 = (size_t)m0;
+  }
+  floatx16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int nkt = (K + kBK - 1) / kBK;
+  uint4 va, vb;
+  const int Ne = kBT;   // N is a multiple of the tile in every product
+  if (nkt > 0) {
+    load_tile<TT, AKC>(g.a, e, arow, m0, Me, 0, K, va, tid);
+    load_tile<TT, BKC>(g.b, e, brow, n0, Ne, 0, K, vb, tid);
+    store_tile<AKC>(sA[0], va, tid);
+    store_tile<BKC>(sB[0], vb, tid);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nkt) {
+      load_tile<TT, AKC>(g.a, e, arow, m0, Me, (kt + 1) * kBK, K, va, tid);
+      load_tile<TT, BKC>(g.b, e, brow, n0, Ne, (kt + 1) * kBK, K, vb, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = ks * 2 + (lane >> 5);
+      const V8 fa = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
+          sA[cur] + bswz(wm * 32 + (lane & 31), ch)));
+      const V8 fb = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
+          sB[cur] + bswz(wn * 32 + (lane & 31), ch)));
+      acc = mfma32(fa, fb, acc);
+    }
+    if (kt + 1 < nkt) {
+      store_tile<AKC>(sA[cur ^ 1], va, tid);
+      store_tile<BKC>(sB[cur ^ 1], vb, tid);
+    }
+    __syncthreads();
+  }
+  // accumulator r: A row 8 (r / 4) + 4 (lane / 32) + r % 4, B row lane % 32
+  const int n = n0 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (m < Me) cbase[(crow0 + m) * g.ldc + n] = acc[r];
+  }
+}
+
+// (expert, first row) of every 64-row tile of the per-pair products, in
+// expert order; n_tiles receives the count.
+__global__ __launch_bounds__(1024) void bwd_tiles_kernel(
+    const int32_t* __restrict__ offsets, int n_exp, int32_t* __restrict__ tiles,
+    int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t start[kMaxExperts + 2];
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int e = 0; e < n_exp; ++e) {
+      start[e] = acc;
+      acc += (offsets[e + 1] - offsets[e] + kBT - 1) / kBT;
+    }
+    start[n_exp] = acc;
+    *n_tiles = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n_exp; e += blockDim.x) {
+    const int nt = start[e + 1] - start[e];
+    for (int i = 0; i < nt; ++i) {
+      tiles[2 * (start[e] + i)] = e;
+      tiles[2 * (start[e] + i) + 1] = i * kBT;
+    }
+  }
+}
+
+// X_p = x[pair_token[p]] and dYp = pair_w[p] * dy[t], 8 values a thread.
+template <class S>
+__global__ __launch_bounds__(256) void bwd_gather_kernel(
+    const S* __restrict__ x, const float* __restrict__ dy,
+    const int32_t* __restrict__ pair_token, const float* __restrict__ pair_w,
+    const int32_t* __restrict__ offsets, int n_exp, int D, S* __restrict__ Xp,
+    S* __restrict__ dYp) {
+  const int P = offsets[n_exp];
+  const int upr = D / 8;
+  for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < (size_t)P * upr;
+       u += (size_t)gridDim.x * blockDim.x) {
+    const size_t p = u / upr;
+    const int c = (int)(u - p * upr) * 8;
+    const int t = pair_token[p];
+    const float wv = pair_w[p];
+    *reinterpret_cast<uint4*>(Xp + p * D + c) =
+        *reinterpret_cast<const uint4*>(x + (size_t)t * D + c);
+    S o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = (S)(wv * dy[(size_t)t * D + c + j]);
+    __builtin_memcpy(dYp + p * D + c, o, 16);
+  }
+}
+
+__device__ __forceinline__ float clamp_hi(float v, float c) { return c > 0.f ? fminf(v, c) : v; }
+
+// H = silu(min(G, c)) * clamp(U, -c, c), rounded to the compute dtype
+// (the forward's SwiGLU: hardware 2^x and reciprocal).
+template <class S>
+__global__ __launch_bounds__(256) void bwd_swiglu_kernel(
+    const float* __restrict__ GU, const int32_t* __restrict__ offsets,
+    int n_exp, int F, float c, S* __restrict__ H) {
+  const size_t n = (size_t)offsets[n_exp] * F;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t p = i / F;
+    const int f = (int)(i - p * F);
+    H[i] = (S)swiglu(GU[p * 2 * F + f], GU[p * 2 * F + F + f], c);
+  }
+}
+
+// dG = dH * clamp(U) * silu'(min(G, c)) * [G <= c];
+// dU = dH * silu(min(G, c)) * [-c <= U <= c]; silu'(z) = s (1 + z (1 - s)),
+// s = 1 / (1 + e^-z). Written side by side, [P, 2F], compute dtype.
+template <class S>
+__global__ __launch_bounds__(256) void bwd_swiglu_back_kernel(
+    const float* __restrict__ GU, const float* __restrict__ dH,
+    const int32_t* __restrict__ offsets, int n_exp, int F, float c,
+    S* __restrict__ dGU) {
+  const size_t n = (size_t)offsets[n_exp] * F;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t p = i / F;
+    const int f = (int)(i - p * F);
+    const float g = GU[p * 2 * F + f], u = GU[p * 2 * F + F + f];
+    const float dh = dH[i];
+    float gc = g, uc = u, mg = 1.f, mu = 1.f;
+    if (c > 0.f) {
+      if (g > c) { gc = c; mg = 0.f; }
+      if (u < -c) { uc = -c; mu = 0.f; }
+      if (u > c) { uc = c; mu = 0.f; }
+    }
+    const float s = 1.f / (1.f + expf(-gc));
+    dGU[p * 2 * F + f] = (S)(dh * uc * s * (1.f + gc * (1.f - s)) * mg);
+    dGU[p * 2 * F + F + f] = (S)(dh * gc * s * mu);
+  }
+}
+
+// dtw[t, j] = dy[t] . Yp[tok2pair[t, j]] (0 for a dropped pair); one wave
+// per (t, j), lanes over D in a fixed stride, then a fixed butterfly.
+__global__ __launch_bounds__(256) void bwd_dtw_kernel(
+    const float* __restrict__ dy, const float* __restrict__ Yp,
+    const int32_t* __restrict__ tok2pair, int T, int k, int D,
+    float* __restrict__ dtw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (q >= (int64_t)T * k) return;
+  const int t = (int)(q / k);
+  const int p = tok2pair[q];
+  float s = 0.f;
+  if (p >= 0)
+    for (int d = lane; d < D; d += 64) s = fmaf(dy[(size_t)t * D + d], Yp[(size_t)p * D + d], s);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) dtw[q] = s;
+}
+
+// dx[t] = sum over j of dXp[tok2pair[t, j]] (j ascending, dropped skipped)
+// + the shared pair's row; each output written by one thread.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(
+    const float* __restrict__ dXp, const int32_t* __restrict__ tok2pair,
+    const int32_t* __restrict__ offsets, int T, int k, int D, int n_shared,
+    int E, float* __restrict__ dx) {
+  const size_t n = (size_t)T * D;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t t = i / D;
+    const int d = (int)(i - t * D);
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int p = tok2pair[t * k + j];
+      if (p >= 0) s += dXp[(size_t)p * D + d];
+    }
+    if (n_shared) s += dXp[((size_t)offsets[E] + t) * D + d];
+    dx[i] = s;
+  }
+}
+
+// dl[t, e_j] = w_j (dtw_j - sum_i w_i dtw_i), 0 for experts not chosen.
+__global__ __launch_bounds__(256) void bwd_dlogits_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ w,
+    const float* __restrict__ dtw, int T, int E, int k, float* __restrict__ dl) {
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s += w[(size_t)t * k + j] * dtw[(size_t)t * k + j];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) dl[(size_t)t * E + e] = 0.f;
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += blockDim.x)
+    dl[(size_t)t * E + ids[(size_t)t * k + j]] =
+        w[(size_t)t * k + j] * (dtw[(size_t)t * k + j] - s);
+}
+
+// ---- launcher ---------------------------------------------------------------
+
+size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t tiles = (size_t)((Pmax + kBT - 1) / kBT + n_exp + 1);
+  return al(tiles * 8) + al(16) + al(Pmax * D * 2) * 2 + al(Pmax * 2 * F * 4) +
+         al(Pmax * F * 2) + al(Pmax * D * 4) + al(Pmax * F * 4) +
+         al(Pmax * 2 * F * 2) + al(Pmax * D * 4);
+}
+
+template <class TT>
+static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
+  using S = typename TT::S;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const int64_t Pm = a.Pmax;
+  const int D = a.D, F = a.F, n_exp = a.n_exp;
+  char* b = static_cast<char*>(a.ws);
+  const size_t ntile_cap = (size_t)((Pm + kBT - 1) / kBT + n_exp + 1);
+  int32_t* tiles = reinterpret_cast<int32_t*>(b);        b += al(ntile_cap * 8);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(b);      b += al(16);
+  S* Xp = reinterpret_cast<S*>(b);                       b += al(Pm * D * 2);
+  S* dYp = reinterpret_cast<S*>(b);                      b += al(Pm * D * 2);
+  float* GU = reinterpret_cast<float*>(b);               b += al(Pm * 2 * F * 4);
+  S* H = reinterpret_cast<S*>(b);                        b += al(Pm * F * 2);
+  float* Yp = reinterpret_cast<float*>(b);               b += al(Pm * D * 4);
+  float* dH = reinterpret_cast<float*>(b);               b += al(Pm * F * 4);
+  S* dGU = reinterpret_cast<S*>(b);                      b += al(Pm * 2 * F * 2);
+  float* dXp = reinterpret_cast<float*>(b);
+
+  const int ew_grid = a.ncu * 8;
+  hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
+                     n_exp, tiles, n_tiles);
+  hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
+                     (const S*)a.x, a.dy, a.pair_token, a.pair_w, a.offsets,
+                     n_exp, D, Xp, dYp);
+  const int ub = (int)ntile_cap;
+  auto per_pair = [&](auto akc, auto bkc, const BOp& A, const BOp& B, int N,
+                      int K, float* C, int ldc) {
+    BGemmArgs g{};
+    g.a = A; g.b = B; g.mode = 0; g.N = N; g.K = K; g.c = C; g.ldc = ldc;
+    g.offsets = a.offsets; g.tiles = tiles; g.n_tiles = n_tiles; g.n_exp = n_exp;
+    hipLaunchKernelGGL((bgemm_kernel<TT, decltype(akc)::value, decltype(bkc)::value, 0>),
+                       dim3(ub * (N / kBT)), dim3(256), 0, s, g);
+  };
+  auto weight_grad = [&](const BOp& A, const BOp& B, int M, int N, float* C) {
+    BGemmArgs g{};
+    g.a = A; g.b = B; g.mode = 1; g.M = M; g.N = N; g.c = C; g.ldc = N;
+    g.c_estride = (int64_t)M * N; g.offsets = a.offsets; g.n_exp = n_exp;
+    hipLaunchKernelGGL((bgemm_kernel<TT, false, false, 1>),
+                       dim3(n_exp * (M / kBT) * (N / kBT)), dim3(256), 0, s, g);
+  };
+  using KCt = std::true_type;
+  using ICt = std::false_type;
+  const int64_t wFD = (int64_t)F * D;
+  // [G | U] = X_p [W_gate; W_up]^T
+  per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wg, nullptr, D, 0, wFD},
+           F, D, GU, 2 * F);
+  per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wu, nullptr, D, 0, wFD},
+           F, D, GU + F, 2 * F);
+  hipLaunchKernelGGL((bwd_swiglu_kernel<S>), dim3(ew_grid), dim3(256), 0, s, GU,
+                     a.offsets, n_exp, F, a.clamp, H);
+  // Yp = H W_down^T ; dH = dYp W_down
+  per_pair(KCt{}, KCt{}, BOp{H, nullptr, F, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
+           D, F, Yp, D);
+  per_pair(KCt{}, ICt{}, BOp{dYp, nullptr, D, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
+           F, D, dH, F);
+  hipLaunchKernelGGL((bwd_swiglu_back_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
+                     GU, dH, a.offsets, n_exp, F, a.clamp, dGU);
+  // dXp = [dG | dU] [W_gate; W_up]
+  per_pair(KCt{}, ICt{}, BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{a.wg, a.wu, D, F, wFD},
+           D, 2 * F, dXp, D);
+  // weight gradients (every expert, zero pairs give zeros)
+  weight_grad(BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{Xp, nullptr, D, 0, 0}, F, D, a.dwg);
+  weight_grad(BOp{(const S*)dGU + F, nullptr, 2 * F, 0, 0}, BOp{Xp, nullptr, D, 0, 0},
+              F, D, a.dwu);
+  weight_grad(BOp{dYp, nullptr, D, 0, 0}, BOp{H, nullptr, F, 0, 0}, D, F, a.dwd);
+  if (a.dx)
+    hipLaunchKernelGGL(bwd_dx_kernel, dim3(ew_grid), dim3(256), 0, s, dXp,
+                       a.tok2pair, a.offsets, a.T, a.k, D, a.n_shared, a.E, a.dx);
+  if (a.dtw || a.dlogits) {
+    float* dtw = a.dtw ? a.dtw : a.dtw_scratch;
+    const int64_t q = (int64_t)a.T * a.k;
+    if (q > 0)
+      hipLaunchKernelGGL(bwd_dtw_kernel, dim3((unsigned)((q + 3) / 4)), dim3(256), 0,
+                         s, a.dy, Yp, a.tok2pair, a.T, a.k, D, dtw);
+    if (a.dlogits && a.T > 0)
+      hipLaunchKernelGGL(bwd_dlogits_kernel, dim3(a.T), dim3(256), 0, s, a.ids,
+                         a.topk_w, dtw, a.T, a.E, a.k, a.dlogits);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+  if (a.xdt == MOE_BF16) return run_bwd<BF16B>(a, s);
+  if (a.xdt == MOE_F16) return run_bwd<F16B>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -728,6 +728,76 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   return MOE_OK;
 }
 
+size_t moe_backward_workspace_bytes(const moe_plan* p, int32_t D, int32_t F,
+                                    int32_t x_dtype) {
+  if (!p) { fail(MOE_EINVAL, "plan is NULL"); return 0; }
+  if (x_dtype != MOE_BF16 && x_dtype != MOE_F16) {
+    fail(MOE_EUNSUPPORTED, "backward supports bf16 and f16 layers"); return 0;
+  }
+  if (D <= 0 || F <= 0 || D % 128 || F % 128) {
+    fail(MOE_EINVAL, "D and F must be positive multiples of 128"); return 0;
+  }
+  const moe_plan_desc& d = p->desc;
+  const int64_t Pmax = (int64_t)d.T * d.k + (int64_t)d.n_shared * d.T;
+  return bwd_workspace_bytes(Pmax, d.E + d.n_shared, D, F) +
+         align256((size_t)d.T * d.k * 4);
+}
+
+moe_status moe_backward(const moe_plan* p, const void* x, int32_t x_dtype,
+                        moe_weight w_gate, moe_weight w_up, moe_weight w_down,
+                        int32_t D, int32_t F, const float* dy, float* dx,
+                        float* dw_gate, float* dw_up, float* dw_down,
+                        float* d_topk_w, float* d_logits, void* ws,
+                        size_t ws_bytes, const moe_options* opt, void* stream) {
+  if (!p) return fail(MOE_EINVAL, "plan is NULL");
+  const moe_plan_desc& d = p->desc;
+  const size_t need = moe_backward_workspace_bytes(p, D, F, x_dtype);
+  if (need == 0) return x_dtype != MOE_BF16 && x_dtype != MOE_F16 ? MOE_EUNSUPPORTED : MOE_EINVAL;
+  std::string why;
+  if (w_gate.dtype != x_dtype)
+    return fail(MOE_EUNSUPPORTED, "backward needs weights in x's dtype (16-bit)");
+  if (!weight_ok(w_gate, x_dtype, &why, "w_gate") ||
+      !weight_ok(w_up, x_dtype, &why, "w_up") ||
+      !weight_ok(w_down, x_dtype, &why, "w_down"))
+    return fail(MOE_EINVAL, "%s", why.c_str());
+  if (!dw_gate || !dw_up || !dw_down || (d.T > 0 && (!x || !dy || !dx)))
+    return fail(MOE_EINVAL, "x, dy, dx and the three weight gradients must be non-NULL");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw_gate) ||
+      !aligned16(dw_up) || !aligned16(dw_down) || !aligned16(d_topk_w) ||
+      !aligned16(d_logits) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(MOE_EINVAL, "pointers must be 16-byte and ws 256-byte aligned");
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "backward workspace %zu bytes < %zu needed", ws_bytes, need);
+  const moe_options o = opt ? *opt : defaults();
+  int dev;
+  DevInfo info;
+  moe_status st = device_info(&dev, &info);
+  if (st != MOE_OK) return st;
+  const char* pb = p->ws;
+  BwdArgs a{};
+  a.xdt = x_dtype; a.T = d.T; a.D = D; a.F = F; a.E = d.E; a.k = d.k;
+  a.n_shared = d.n_shared; a.n_exp = d.E + d.n_shared;
+  a.Pmax = (int64_t)d.T * d.k + (int64_t)d.n_shared * d.T;
+  a.ncu = info.ncu;
+  a.x = x; a.dy = dy; a.wg = w_gate.data; a.wu = w_up.data; a.wd = w_down.data;
+  a.clamp = o.swiglu_limit;
+  a.offsets = (const int32_t*)(pb + p->L.offsets);
+  a.pair_token = (const int32_t*)(pb + p->L.pair_token);
+  a.pair_w = (const float*)(pb + p->L.pair_w);
+  a.tok2pair = (const int32_t*)(pb + p->L.tok2pair);
+  a.ids = (const int32_t*)(pb + p->L.ids);
+  a.topk_w = (const float*)(pb + p->L.w);
+  a.dx = dx; a.dwg = dw_gate; a.dwu = dw_up; a.dwd = dw_down;
+  a.dtw = d_topk_w; a.dlogits = d_logits;
+  char* b = static_cast<char*>(ws);
+  a.ws = b;
+  a.dtw_scratch = reinterpret_cast<float*>(b + bwd_workspace_bytes(a.Pmax, a.n_exp, D, F));
+  hipError_t e = launch_backward(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward kernels");
+  return MOE_OK;
+}
+
 moe_status moe_dequant_q4(const void* data, const void* scales, int64_t rows,
                           int64_t K, void* out_f16, void* stream) {
   if (rows < 0 || K <= 0 || K % 32) return fail(MOE_EINVAL, "rows >= 0 and K a positive multiple of 32");

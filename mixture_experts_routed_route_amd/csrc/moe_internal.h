@@ -184,6 +184,26 @@ hipError_t launch_combine(const void* ypair, int ypair_f16,
                           const int32_t* offsets, int T, int D, int k,
                           int n_shared, int E, int ydt, void* y, hipStream_t s);
 
+// ---- backward (backward.hip) --------------------------------------------
+struct BwdArgs {
+  int xdt;                      // MOE_BF16 or MOE_F16 (x and the weights)
+  int T, D, F, E, k, n_shared, n_exp;
+  int64_t Pmax;                 // most pairs the plan can hold
+  int ncu;
+  const void* x;                // [T, D]
+  const float* dy;              // [T, D]
+  const void* wg; const void* wu; const void* wd;
+  float clamp;
+  const int32_t* offsets; const int32_t* pair_token; const float* pair_w;
+  const int32_t* tok2pair; const int32_t* ids; const float* topk_w;
+  float* dx; float* dwg; float* dwu; float* dwd;   // outputs (f32)
+  float* dtw; float* dlogits;   // optional outputs
+  float* dtw_scratch;           // [T, k] when dlogits is wanted without dtw
+  void* ws;                     // bwd_workspace_bytes
+};
+size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+
 // ---- router (router.hip) ---------------------------------------------------
 size_t router_scratch_bytes(int T, int E);
 // scratch: the statistics scratch (its accumulators are cleared by the

@@ -189,3 +189,12 @@ def test_affine_params_shape_picks_format():
     assert moe.q4_dtype(d, torch.zeros(2, 8, 2, 2, dtype=torch.float16)) == moe.MOE_Q4A64
     with pytest.raises(ValueError):
         moe.q4_dtype(d, torch.zeros(2, 8, 3, 2, dtype=torch.float16))
+
+
+def test_backward_validation(lib):
+    assert lib.moe_backward_workspace_bytes(None, 128, 128, moe.MOE_BF16) == 0
+    w = moe.Weight(moe.MOE_BF16, 0x1000, None)
+    st = lib.moe_backward(None, 0x1000, moe.MOE_BF16, w, w, w, 128, 128, 0x2000,
+                          0x3000, 0x4000, 0x5000, 0x6000, None, None, 0x10000,
+                          1 << 20, None, None)
+    assert st == moe.MOE_EINVAL
