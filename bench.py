@@ -48,7 +48,9 @@ KERNEL_SRC = {"gateup_full": "gemm_full.hip", "down_full": "gemm_full.hip",
               "dequant_once": "forward_kernels.hip",
               "combine": "forward_kernels.hip",
               "classify": "forward_kernels.hip",
-              "router_gemm": "router.hip"}
+              "router_gemm": "router.hip",
+              "bwd_weights": "backward.hip", "bwd_data": "backward.hip",
+              "bwd_recompute": "backward.hip"}
 
 
 def parse():
@@ -71,6 +73,9 @@ def parse():
                          "a 1 GiB write that evicts L2 and the 256 MB MALL)")
     ap.add_argument("--weights", default=None, choices=("q4b32", "q4a32", "q4a64"),
                     help="4-bit format of workloads 4 and 7 (default q4b32)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_backward on the workload's plan (16-bit "
+                         "workloads; default the prefill one)")
     ap.add_argument("--router", action="store_true",
                     help="time moe_route (router map + plan + statistics)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -121,6 +126,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.router:
         return bench_router(args, dev, torch, moe, W)
+    if args.backward:
+        return bench_backward(args, dev, torch, moe, W)
     wl = W.config(args.config, capacity_factor=args.capacity_factor, T=args.T,
                   pairs_per_expert=args.pairs_per_expert, w_dtype=args.weights)
     T, D, F, E, k, ns = (wl[n] for n in ("T", "D", "F", "E", "k", "n_shared"))
@@ -391,6 +398,121 @@ def bench_router(args, dev, torch, moe, W):
         "hardware": hardware(torch),
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_backward(args, dev, torch, moe, W):
+    """moe_backward on a 16-bit workload's plan (default: the prefill layer,
+    4096 tokens, d_model 2048, d_ff 768, 128 experts, top-8, bf16): dx, the
+    three weight gradients, the routing-weight and logit gradients of
+    sum(dy * y) for a seeded dy ~ N(0, 1). Flops per kept pair: 18 D F
+    (the recomputed gate/up and down products, dH, dX, and the three weight
+    gradients, 2 D F each, gate/up and dX twice)."""
+    import numpy as np
+
+    cfg = args.config if args.config != 4 else 3
+    wl = W.config(cfg, capacity_factor=args.capacity_factor, T=args.T,
+                  pairs_per_expert=args.pairs_per_expert)
+    if wl["w_dtype"] not in ("bf16", "f16"):
+        raise SystemExit("--backward needs a bf16 or f16 workload (2, 3, 5, 6)")
+    T, D, F, E, k, ns = (wl[n] for n in ("T", "D", "F", "E", "k", "n_shared"))
+    x = wl["x"].to(dev)
+    wg, wu, wd = (wl[n].to(dev) for n in ("w_gate", "w_up", "w_down"))
+    dy = torch.randn(T, D, generator=torch.Generator().manual_seed(1)).to(dev)
+    plan = moe.moe_plan_create(wl["logits"].to(dev), k, wl["capacity_factor"], ns)
+    opts = moe.make_options()
+    if not args.no_phase_events:
+        opts.flags |= moe.MOE_OPT_PHASE_EVENTS
+    ws = None
+
+    def step():
+        return moe.moe_backward(plan, x, wg, wu, wd, dy, options=opts,
+                                want_dtw=True, want_dlogits=True, workspace=ws)
+
+    out = step()
+    torch.cuda.synchronize()
+    ws = torch.empty(moe.library().moe_backward_workspace_bytes(
+        plan.handle, D, F, moe._TORCH_TO_MOE[x.dtype]), dtype=torch.uint8, device=dev)
+    copy_calibration(args, torch, dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.moe_phase_times(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    counts = moe.moe_plan_get_views(plan)["counts"].cpu().numpy().astype(np.int64)
+    P = int(counts.sum())
+    flops = 18.0 * D * F * P
+    roofline = None
+    if not args.no_phase_events:
+        phase_ms, calls = moe.moe_phase_times(reset=True)
+        per = {n: phase_ms[n] / max(calls, 1)
+               for n in ("bwd_recompute", "bwd_data", "bwd_weights", "bwd_routing")}
+        amount = {"bwd_recompute": 6.0 * D * F * P, "bwd_data": 6.0 * D * F * P,
+                  "bwd_weights": 6.0 * D * F * P}
+        dom = max(amount, key=lambda n: per[n])
+        achieved = amount[dom] / (per[dom] * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[wl["x_dtype"]]
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": load_traffic(wl["name"], dom),
+                    "algorithmic_per_launch": amount[dom],
+                    "avg_launch_ms": round(per[dom], 4),
+                    "phase_ms_per_step": {n: round(v, 4) for n, v in per.items()}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_backward(wl, dy.cpu(), args.cpu_seconds)
+    line = {
+        "metric": "backward TFLOP/s per MoE layer (18*D*F per kept pair)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl["x_dtype"],
+        "data": "synthetic (seeded; workloads.py)",
+        "config": {"workload": wl["name"] + "_backward", "T": T, "d_model": D,
+                   "d_ff": F, "experts": E, "top_k": k, "shared": ns,
+                   "parallelism": "single GPU"},
+        "kept_pairs": P,
+        "pairs_per_s": round(P / (ms * 1e-3), 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "hardware": hardware(torch),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_backward(wl, dy, target_s):
+    """The oracle's dx path (each kept pair: g, u, h, the pair output, dH
+    and dx, 12 D F flops) on the first tokens, doubling until about
+    target_s seconds."""
+    import numpy as np
+
+    import oracle
+
+    ids, w = oracle.route(wl["logits"], wl["k"])
+    pl = oracle.plan(ids, wl["E"], wl["capacity_factor"], wl["n_shared"])
+    n, done, total_t, pairs = 4, 0, 0.0, 0
+    T = wl["T"]
+    dyn = dy.numpy().astype(np.float64)
+    while done < T and total_t < target_s:
+        toks = np.arange(done, min(T, done + n))
+        t0 = time.perf_counter()
+        oracle.backward(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], ids, w,
+                        pl["keep"], dyn, E=wl["E"], n_shared=wl["n_shared"],
+                        x_dtype=wl["x_dtype"], w_dtype=wl["w_dtype"],
+                        c=wl["swiglu_limit"], tokens=toks, want=("dx",))
+        total_t += time.perf_counter() - t0
+        pairs += int(pl["keep"][toks].sum()) + wl["n_shared"] * len(toks)
+        done += len(toks)
+        n *= 2
+    return {"value": round(12.0 * wl["D"] * wl["F"] * pairs / total_t / 1e12, 6),
+            "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"dx of the first {done} tokens ({pairs} kept pairs) in "
+                      f"{total_t:.1f} s; the oracle's dx path, 12 D F flops a pair"}
 
 
 def cpu_baseline_router(wl, target_s):

@@ -282,7 +282,8 @@ size_t moe_backward_workspace_bytes(const moe_plan *plan, int32_t D, int32_t F,
  * experts, 0 elsewhere). The expert outputs are recomputed from x (nothing
  * is kept from the forward); per-pair intermediates (x rows, w dy, the
  * SwiGLU output and its gradients) are held in the layer's dtype, products
- * accumulate in f32. opt: the swiglu_limit of the forward (NULL: defaults).
+ * accumulate in f32. opt: the swiglu_limit of the forward (NULL: defaults);
+ * MOE_OPT_PHASE_EVENTS times its four phases (moe_phase_times 10..13).
  * D and F multiples of 128; pointers 16-byte aligned, ws 256-byte aligned.
  * Async on `stream`. */
 moe_status moe_backward(const moe_plan *plan, const void *x, int32_t x_dtype,
@@ -314,9 +315,10 @@ moe_status moe_dequant_weights(int32_t dtype, const void *data,
  * `calls` receives the number of such calls. Phases: 0 classify,
  * 1 dequant-once, 2 gate/up full tile, 3 gate/up split-K, 4 down full tile,
  * 5 down split-K, 6 combine (moe_forward); 7 router kernel, 8 plan,
- * 9 routing statistics (moe_route). Synchronises on the recorded events.
- * reset != 0 clears afterwards. */
-#define MOE_N_PHASES 10
+ * 9 routing statistics (moe_route); 10 recompute, 11 data gradients,
+ * 12 weight gradients, 13 routing-weight gradients (moe_backward).
+ * Synchronises on the recorded events. reset != 0 clears afterwards. */
+#define MOE_N_PHASES 14
 moe_status moe_phase_times(double *ms, int32_t n, int64_t *calls,
                            int32_t reset);
 

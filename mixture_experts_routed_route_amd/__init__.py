@@ -38,10 +38,11 @@ MOE_Q4A32, MOE_Q4A64 = 4, 5
 MOE_OPT_PHASE_EVENTS = 1
 MOE_OPT_BF16_PLAIN_H = 2
 MOE_OPT_EXACT_ROUTES = 4
-MOE_N_PHASES = 10
+MOE_N_PHASES = 14
 PHASES = ("classify", "dequant_once", "gateup_full", "gateup_splitk",
           "down_full", "down_splitk", "combine", "router_gemm", "route_plan",
-          "router_stats")
+          "router_stats", "bwd_recompute", "bwd_data", "bwd_weights",
+          "bwd_routing")
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED",
                 -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}

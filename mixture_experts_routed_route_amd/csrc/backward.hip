@@ -353,8 +353,10 @@ size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
          al(Pmax * 2 * F * 2) + al(Pmax * D * 4);
 }
 
+// stage 0: gather, recompute [G | U], H and Yp; 1: dH, dG / dU, dXp, dx;
+// 2: the weight gradients; 3: the routing-weight and logit gradients
 template <class TT>
-static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
+static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   using S = typename TT::S;
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const int64_t Pm = a.Pmax;
@@ -373,11 +375,6 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   float* dXp = reinterpret_cast<float*>(b);
 
   const int ew_grid = a.ncu * 8;
-  hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
-                     n_exp, tiles, n_tiles);
-  hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
-                     (const S*)a.x, a.dy, a.pair_token, a.pair_w, a.offsets,
-                     n_exp, D, Xp, dYp);
   const int ub = (int)ntile_cap;
   auto per_pair = [&](auto akc, auto bkc, const BOp& A, const BOp& B, int N,
                       int K, float* C, int ldc) {
@@ -397,32 +394,41 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   using KCt = std::true_type;
   using ICt = std::false_type;
   const int64_t wFD = (int64_t)F * D;
-  // [G | U] = X_p [W_gate; W_up]^T
-  per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wg, nullptr, D, 0, wFD},
-           F, D, GU, 2 * F);
-  per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wu, nullptr, D, 0, wFD},
-           F, D, GU + F, 2 * F);
-  hipLaunchKernelGGL((bwd_swiglu_kernel<S>), dim3(ew_grid), dim3(256), 0, s, GU,
-                     a.offsets, n_exp, F, a.clamp, H);
-  // Yp = H W_down^T ; dH = dYp W_down
-  per_pair(KCt{}, KCt{}, BOp{H, nullptr, F, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
-           D, F, Yp, D);
-  per_pair(KCt{}, ICt{}, BOp{dYp, nullptr, D, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
-           F, D, dH, F);
-  hipLaunchKernelGGL((bwd_swiglu_back_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
-                     GU, dH, a.offsets, n_exp, F, a.clamp, dGU);
-  // dXp = [dG | dU] [W_gate; W_up]
-  per_pair(KCt{}, ICt{}, BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{a.wg, a.wu, D, F, wFD},
-           D, 2 * F, dXp, D);
-  // weight gradients (every expert, zero pairs give zeros)
-  weight_grad(BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{Xp, nullptr, D, 0, 0}, F, D, a.dwg);
-  weight_grad(BOp{(const S*)dGU + F, nullptr, 2 * F, 0, 0}, BOp{Xp, nullptr, D, 0, 0},
-              F, D, a.dwu);
-  weight_grad(BOp{dYp, nullptr, D, 0, 0}, BOp{H, nullptr, F, 0, 0}, D, F, a.dwd);
-  if (a.dx)
-    hipLaunchKernelGGL(bwd_dx_kernel, dim3(ew_grid), dim3(256), 0, s, dXp,
-                       a.tok2pair, a.offsets, a.T, a.k, D, a.n_shared, a.E, a.dx);
-  if (a.dtw || a.dlogits) {
+  if (stage == 0) {
+    hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
+                       n_exp, tiles, n_tiles);
+    hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
+                       (const S*)a.x, a.dy, a.pair_token, a.pair_w, a.offsets,
+                       n_exp, D, Xp, dYp);
+    // [G | U] = X_p [W_gate; W_up]^T
+    per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wg, nullptr, D, 0, wFD},
+             F, D, GU, 2 * F);
+    per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wu, nullptr, D, 0, wFD},
+             F, D, GU + F, 2 * F);
+    hipLaunchKernelGGL((bwd_swiglu_kernel<S>), dim3(ew_grid), dim3(256), 0, s, GU,
+                       a.offsets, n_exp, F, a.clamp, H);
+    // Yp = H W_down^T (for the routing-weight gradients)
+    per_pair(KCt{}, KCt{}, BOp{H, nullptr, F, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
+             D, F, Yp, D);
+  } else if (stage == 1) {
+    // dH = dYp W_down
+    per_pair(KCt{}, ICt{}, BOp{dYp, nullptr, D, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
+             F, D, dH, F);
+    hipLaunchKernelGGL((bwd_swiglu_back_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
+                       GU, dH, a.offsets, n_exp, F, a.clamp, dGU);
+    // dXp = [dG | dU] [W_gate; W_up]
+    per_pair(KCt{}, ICt{}, BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{a.wg, a.wu, D, F, wFD},
+             D, 2 * F, dXp, D);
+    if (a.dx)
+      hipLaunchKernelGGL(bwd_dx_kernel, dim3(ew_grid), dim3(256), 0, s, dXp,
+                         a.tok2pair, a.offsets, a.T, a.k, D, a.n_shared, a.E, a.dx);
+  } else if (stage == 2) {
+    // weight gradients (every expert, zero pairs give zeros)
+    weight_grad(BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{Xp, nullptr, D, 0, 0}, F, D, a.dwg);
+    weight_grad(BOp{(const S*)dGU + F, nullptr, 2 * F, 0, 0}, BOp{Xp, nullptr, D, 0, 0},
+                F, D, a.dwu);
+    weight_grad(BOp{dYp, nullptr, D, 0, 0}, BOp{H, nullptr, F, 0, 0}, D, F, a.dwd);
+  } else if (a.dtw || a.dlogits) {
     float* dtw = a.dtw ? a.dtw : a.dtw_scratch;
     const int64_t q = (int64_t)a.T * a.k;
     if (q > 0)
@@ -435,9 +441,9 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
-  if (a.xdt == MOE_BF16) return run_bwd<BF16B>(a, s);
-  if (a.xdt == MOE_F16) return run_bwd<F16B>(a, s);
+hipError_t launch_backward(const BwdArgs& a, int stage, hipStream_t s) {
+  if (a.xdt == MOE_BF16) return run_bwd<BF16B>(a, stage, s);
+  if (a.xdt == MOE_F16) return run_bwd<F16B>(a, stage, s);
   return hipErrorInvalidValue;
 }
 

@@ -793,8 +793,20 @@ moe_status moe_backward(const moe_plan* p, const void* x, int32_t x_dtype,
   char* b = static_cast<char*>(ws);
   a.ws = b;
   a.dtw_scratch = reinterpret_cast<float*>(b + bwd_workspace_bytes(a.Pmax, a.n_exp, D, F));
-  hipError_t e = launch_backward(a, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "backward kernels");
+  PhaseRecord* rec = nullptr;
+  if (o.flags & MOE_OPT_PHASE_EVENTS) {
+    rec = acquire_record(&st);
+    if (!rec) return st;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int stage = 0; stage < 4; ++stage) {
+    hipError_t e;
+    {
+      PhaseScope ps(rec, 10 + stage, s);
+      e = launch_backward(a, stage, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "backward kernels");
+  }
   return MOE_OK;
 }
 
