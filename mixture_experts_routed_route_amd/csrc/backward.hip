@@ -14,11 +14,14 @@
 //   [dG | dU] = SwiGLU backward         (compute dtype)
 //   dXp  = dG W_gate + dU W_up          dx[t] = sum over its pairs (fixed order)
 //   dW_gate[e] = sum_p dG_p x_p^T,  dW_up[e] likewise,  dW_down[e] = sum_p dYp H_p^T
-// The six products run on one grouped MFMA kernel: 64 x 64 output tiles,
-// 32-deep K steps staged through LDS; an operand whose memory is contiguous
-// along K is copied in 16-byte pieces, one contiguous along the output
-// index (the weights read as [K, N], and both operands of the weight
-// gradients, whose K is the pair index) is transposed on its way into LDS.
+// The six products run on grouped MFMA kernels staged through LDS: an
+// operand whose memory is contiguous along K is copied in 16-byte pieces,
+// one contiguous along the output index (the weights read as [K, N], and
+// both operands of the weight gradients, whose K is the pair index) is
+// transposed on its way into LDS. Products of two K-contiguous operands take
+// 64 x 128 tiles and 64-deep steps of 128-byte LDS rows; the others 64 x 64
+// tiles and 32-deep steps of 64-byte rows, whose transposing stores collide
+// on fewer banks.
 #include <type_traits>
 
 #include "device_common.h"
@@ -30,12 +33,8 @@ namespace {
 struct BF16B { using S = __bf16; using V8 = bf16x8; };
 struct F16B { using S = _Float16; using V8 = half8; };
 
-constexpr int kBT = 64;   // output tile (rows and columns)
-constexpr int kBK = 32;   // K per LDS step
-
-__device__ __forceinline__ int bswz(int r, int c) {
-  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
-}
+constexpr int kBT = 64;   // rows of a per-pair tile
+constexpr int kPN = 128;  // columns of a per-pair tile
 
 }  // namespace
 
@@ -64,11 +63,197 @@ struct BGemmArgs {
   const int32_t* offsets;   // [n_exp + 1]
   const int32_t* tiles;     // mode 0: (expert, first row) per 64-row tile
   const int32_t* n_tiles;   // mode 0: number of tiles (device)
+  const int32_t* koff;      // mode 1 on pair-transposed operands: expert e's
+                            // K columns start at koff[e] (a multiple of 8)
+                            // and run to koff[e + 1] (zero padded)
   int n_exp;
 };
 
-template <class TT, bool KC>
+// A BR x 64 operand tile (BR rows of the product, 64 K values) in LDS as
+// BR rows of 128 bytes; chunk c of row r sits at c ^ ((r >> 1) & 7), so the
+// 16 rows one phase of a fragment read touches hit 16 distinct bank groups.
+__device__ __forceinline__ int bswz(int r, int c) {
+  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// Loads of one tile into registers: KC: 8 chunks of 8 K values per row,
+// thread t takes row t / 8 + 32 q, chunk t % 8; IC: BR / 8 chunks of 8 row
+// values per K row, thread t takes K row t / (BR / 8) + (2048 / BR) q, chunk
+// t % (BR / 8). Elements past the operand's rows or K read as zero.
+template <bool KC, int BR>
+struct TileRegs { uint4 v[BR * 8 / 256]; };
+
+template <bool KC, int BR>
 __device__ __forceinline__ void load_tile(const BOp& o, int e, int row_base,
+                                          int i0, int ni, int k0, int nk,
+                                          TileRegs<KC, BR>& t, int tid,
+                                          int kcol = 0) {
+  constexpr int NQ = BR * 8 / 256;
+  const char* base;
+  int kk = k0;
+  if (o.p2 && k0 >= o.k_split) { base = (const char*)o.p2; kk = k0 - o.k_split; }
+  else base = (const char*)o.p;
+  if (o.estride) base += (size_t)e * o.estride * 2;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    t.v[q] = uint4{0u, 0u, 0u, 0u};
+    if constexpr (KC) {
+      const int i = (tid >> 3) + 32 * q, c = tid & 7;
+      if (i < ni && k0 + c * 8 < nk) {
+        const size_t row = (size_t)(row_base + i0 + i);
+        t.v[q] = *reinterpret_cast<const uint4*>(base + (row * o.ld + kcol + kk + c * 8) * 2);
+      }
+    } else {
+      constexpr int CPR = BR / 8;                 // chunks per K row
+      const int k = tid / CPR + (256 / CPR) * q, c = tid % CPR;
+      if (k0 + k < nk && c * 8 < ni) {
+        const size_t row = (size_t)(row_base + kk + k);
+        t.v[q] = *reinterpret_cast<const uint4*>(base + (row * o.ld + i0 + c * 8) * 2);
+      }
+    }
+  }
+}
+
+template <bool KC, int BR>
+__device__ __forceinline__ void store_tile(char* s, const TileRegs<KC, BR>& t, int tid) {
+  constexpr int NQ = BR * 8 / 256;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if constexpr (KC) {
+      const int i = (tid >> 3) + 32 * q, c = tid & 7;
+      *reinterpret_cast<uint4*>(s + bswz(i, c)) = t.v[q];
+    } else {
+      constexpr int CPR = BR / 8;
+      const int k = tid / CPR + (256 / CPR) * q, c = tid % CPR;
+      uint16_t h[8];
+      __builtin_memcpy(h, &t.v[q], 16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint16_t*>(s + bswz(c * 8 + j, k >> 3) + (k & 7) * 2) = h[j];
+    }
+  }
+}
+
+// C tile BM x BN per block of 4 waves (2 x 2, each (BM / 2) x (BN / 2) in
+// 32 x 32 blocks), K in 64-deep steps: the next step's global loads are in
+// registers while the current one multiplies out of LDS.
+template <class TT, bool AKC, bool BKC, int MODE, int BM, int BN>
+__global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs g) {
+  using V8 = typename TT::V8;
+  constexpr int NI = BM / 64, NJ = BN / 64;
+  __shared__ __attribute__((aligned(16))) char sA[2][BM * 128];
+  __shared__ __attribute__((aligned(16))) char sB[2][BN * 128];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int e, m0, Me, n0, K, arow, brow, kcol = 0;
+  float* cbase;
+  size_t crow0;
+  if constexpr (MODE == 0) {
+    const int nt = g.N / BN;
+    const int ti = blockIdx.x / nt;
+    if (ti >= *g.n_tiles) return;   // block-uniform, before any barrier
+    n0 = (blockIdx.x - ti * nt) * BN;
+    e = g.tiles[2 * ti];
+    m0 = g.tiles[2 * ti + 1];
+    const int off = g.offsets[e];
+    Me = min(BM, g.offsets[e + 1] - off - m0);
+    K = g.K;
+    arow = off;          // A: pair rows of the expert
+    brow = 0;            // B: the expert's weight
+    cbase = g.c;
+    crow0 = (size_t)(off + m0);
+  } else {
+    const int mt = g.M / BM, nt = g.N / BN;
+    const int per = mt * nt;
+    e = blockIdx.x / per;
+    const int r = blockIdx.x - e * per;
+    m0 = (r / nt) * BM;
+    n0 = (r % nt) * BN;
+    Me = BM;
+    // both operands transposed per pair ([features, pairs]): rows are the
+    // features, the expert's pairs the K columns koff[e] .. koff[e + 1]
+    kcol = g.koff[e];
+    K = g.koff[e + 1] - kcol;
+    arow = 0;
+    brow = 0;
+    cbase = g.c + (size_t)e * g.c_estride;
+    crow0 = (size_t)m0;
+  }
+  floatx16 acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int nkt = (K + 63) / 64;
+  TileRegs<AKC, BM> ra;
+  TileRegs<BKC, BN> rb;
+  if (nkt > 0) {
+    load_tile<AKC, BM>(g.a, e, arow, m0, Me, 0, K, ra, tid, kcol);
+    load_tile<BKC, BN>(g.b, e, brow, n0, BN, 0, K, rb, tid, kcol);
+    store_tile<AKC, BM>(sA[0], ra, tid);
+    store_tile<BKC, BN>(sB[0], rb, tid);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nkt) {
+      load_tile<AKC, BM>(g.a, e, arow, m0, Me, (kt + 1) * 64, K, ra, tid, kcol);
+      load_tile<BKC, BN>(g.b, e, brow, n0, BN, (kt + 1) * 64, K, rb, tid, kcol);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = ks * 2 + (lane >> 5);
+      V8 fa[NI], fb[NJ];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        fa[i] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
+            sA[cur] + bswz(wm * (BM / 2) + i * 32 + (lane & 31), ch)));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        fb[j] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
+            sB[cur] + bswz(wn * (BN / 2) + j * 32 + (lane & 31), ch)));
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < nkt) {
+      store_tile<AKC, BM>(sA[cur ^ 1], ra, tid);
+      store_tile<BKC, BN>(sB[cur ^ 1], rb, tid);
+    }
+    __syncthreads();
+  }
+  // accumulator r of block (i, j): A row 8 (r / 4) + 4 (lane / 32) + r % 4,
+  // B row lane % 32
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < Me) cbase[(crow0 + m) * g.ldc + n] = acc[i][j][r];
+      }
+  }
+}
+
+// The 64 x 64, 32-deep variant: rows of 64 bytes in LDS (chunk c of row r
+// at c ^ ((r >> 2) & 3)). Its transposing stores collide less than those of
+// the 128-byte rows above, so the products with an operand contiguous along
+// the output index run on it.
+constexpr int kT32 = 64;
+constexpr int kBK32 = 32;
+__device__ __forceinline__ int bswz32(int r, int c) {
+  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
+
+template <class TT, bool KC>
+__device__ __forceinline__ void load_tile32(const BOp& o, int e, int row_base,
                                           int i0, int ni, int k0, int nk,
                                           uint4& v, int tid) {
   // KC: thread -> row i = tid / 4, 8 K values at chunk tid % 4
@@ -95,10 +280,10 @@ __device__ __forceinline__ void load_tile(const BOp& o, int e, int row_base,
 }
 
 template <bool KC>
-__device__ __forceinline__ void store_tile(char* s, const uint4& v, int tid) {
+__device__ __forceinline__ void store_tile32(char* s, const uint4& v, int tid) {
   if constexpr (KC) {
     const int i = tid >> 2, c = tid & 3;
-    *reinterpret_cast<uint4*>(s + bswz(i, c)) = v;
+    *reinterpret_cast<uint4*>(s + bswz32(i, c)) = v;
   } else {
     const int k = tid >> 3, c = tid & 7;
     uint16_t h[8];
@@ -106,16 +291,16 @@ __device__ __forceinline__ void store_tile(char* s, const uint4& v, int tid) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = c * 8 + j;
-      *reinterpret_cast<uint16_t*>(s + bswz(r, k >> 3) + (k & 7) * 2) = h[j];
+      *reinterpret_cast<uint16_t*>(s + bswz32(r, k >> 3) + (k & 7) * 2) = h[j];
     }
   }
 }
 
 template <class TT, bool AKC, bool BKC, int MODE>
-__global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs g) {
+__global__ __launch_bounds__(256) void bgemm32_kernel(BGemmArgs g) {
   using V8 = typename TT::V8;
-  __shared__ __attribute__((aligned(16))) char sA[2][kBT * 64];
-  __shared__ __attribute__((aligned(16))) char sB[2][kBT * 64];
+  __shared__ __attribute__((aligned(16))) char sA[2][kT32 * 64];
+  __shared__ __attribute__((aligned(16))) char sB[2][kT32 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -124,27 +309,27 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs g) {
   float* cbase;
   size_t crow0;
   if constexpr (MODE == 0) {
-    const int nt = g.N / kBT;
+    const int nt = g.N / kT32;
     const int ti = blockIdx.x / nt;
     if (ti >= *g.n_tiles) return;   // block-uniform, before any barrier
-    n0 = (blockIdx.x - ti * nt) * kBT;
+    n0 = (blockIdx.x - ti * nt) * kT32;
     e = g.tiles[2 * ti];
     m0 = g.tiles[2 * ti + 1];
     const int off = g.offsets[e];
-    Me = min(kBT, g.offsets[e + 1] - off - m0);
+    Me = min(kT32, g.offsets[e + 1] - off - m0);
     K = g.K;
     arow = off;          // A: pair rows of the expert
     brow = 0;            // B: the expert's weight
     cbase = g.c;
     crow0 = (size_t)(off + m0);
   } else {
-    const int mt = g.M / kBT, nt = g.N / kBT;
+    const int mt = g.M / kT32, nt = g.N / kT32;
     const int per = mt * nt;
     e = blockIdx.x / per;
     const int r = blockIdx.x - e * per;
-    m0 = (r / nt) * kBT;
-    n0 = (r % nt) * kBT;
-    Me = kBT;
+    m0 = (r / nt) * kT32;
+    n0 = (r % nt) * kT32;
+    Me = kT32;
     const int off = g.offsets[e];
     K = g.offsets[e + 1] - off;
     arow = off;          // both operands: the expert's pairs along K
@@ -155,34 +340,34 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs g) {
   floatx16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int nkt = (K + kBK - 1) / kBK;
+  const int nkt = (K + kBK32 - 1) / kBK32;
   uint4 va, vb;
-  const int Ne = kBT;   // N is a multiple of the tile in every product
+  const int Ne = kT32;   // N is a multiple of the tile in every product
   if (nkt > 0) {
-    load_tile<TT, AKC>(g.a, e, arow, m0, Me, 0, K, va, tid);
-    load_tile<TT, BKC>(g.b, e, brow, n0, Ne, 0, K, vb, tid);
-    store_tile<AKC>(sA[0], va, tid);
-    store_tile<BKC>(sB[0], vb, tid);
+    load_tile32<TT, AKC>(g.a, e, arow, m0, Me, 0, K, va, tid);
+    load_tile32<TT, BKC>(g.b, e, brow, n0, Ne, 0, K, vb, tid);
+    store_tile32<AKC>(sA[0], va, tid);
+    store_tile32<BKC>(sB[0], vb, tid);
   }
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nkt) {
-      load_tile<TT, AKC>(g.a, e, arow, m0, Me, (kt + 1) * kBK, K, va, tid);
-      load_tile<TT, BKC>(g.b, e, brow, n0, Ne, (kt + 1) * kBK, K, vb, tid);
+      load_tile32<TT, AKC>(g.a, e, arow, m0, Me, (kt + 1) * kBK32, K, va, tid);
+      load_tile32<TT, BKC>(g.b, e, brow, n0, Ne, (kt + 1) * kBK32, K, vb, tid);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int ch = ks * 2 + (lane >> 5);
       const V8 fa = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
-          sA[cur] + bswz(wm * 32 + (lane & 31), ch)));
+          sA[cur] + bswz32(wm * 32 + (lane & 31), ch)));
       const V8 fb = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
-          sB[cur] + bswz(wn * 32 + (lane & 31), ch)));
+          sB[cur] + bswz32(wn * 32 + (lane & 31), ch)));
       acc = mfma32(fa, fb, acc);
     }
     if (kt + 1 < nkt) {
-      store_tile<AKC>(sA[cur ^ 1], va, tid);
-      store_tile<BKC>(sB[cur ^ 1], vb, tid);
+      store_tile32<AKC>(sA[cur ^ 1], va, tid);
+      store_tile32<BKC>(sB[cur ^ 1], vb, tid);
     }
     __syncthreads();
   }
@@ -197,17 +382,24 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs g) {
 
 // (expert, first row) of every 64-row tile of the per-pair products, in
 // expert order; n_tiles receives the count.
+// Also the padded column offsets of the pair-transposed buffers: expert e's
+// pairs at columns koff[e] .. koff[e] + n_e, koff[e + 1] = koff[e] + n_e
+// rounded up to 8.
 __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
     const int32_t* __restrict__ offsets, int n_exp, int32_t* __restrict__ tiles,
-    int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ n_tiles, int32_t* __restrict__ koff) {
   __shared__ int32_t start[kMaxExperts + 2];
   if (threadIdx.x == 0) {
-    int acc = 0;
+    int acc = 0, col = 0;
     for (int e = 0; e < n_exp; ++e) {
       start[e] = acc;
-      acc += (offsets[e + 1] - offsets[e] + kBT - 1) / kBT;
+      koff[e] = col;
+      const int ne = offsets[e + 1] - offsets[e];
+      acc += (ne + kBT - 1) / kBT;
+      col += (ne + 7) & ~7;
     }
     start[n_exp] = acc;
+    koff[n_exp] = col;
     *n_tiles = acc;
   }
   __syncthreads();
@@ -217,6 +409,52 @@ __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
       tiles[2 * (start[e] + i)] = e;
       tiles[2 * (start[e] + i) + 1] = i * kBT;
     }
+  }
+}
+
+// out[c, koff[e] + i] = in[offsets[e] + i, c] for the pairs of a 64-row
+// tile (a tile holds one expert's pairs) and a 64-column block, with zeros
+// in the padding columns after an expert's last pair. Staged through LDS
+// (65-element rows: the column reads of the write-out avoid bank clashes).
+template <class S>
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(
+    const S* __restrict__ in, int C, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
+    const int32_t* __restrict__ koff, int ld_out, S* __restrict__ out) {
+  __shared__ S t[64][65];
+  const int nc = C / 64;
+  const int ti = blockIdx.x / nc;
+  if (ti >= *n_tiles) return;
+  const int c0 = (blockIdx.x - ti * nc) * 64;
+  const int e = tiles[2 * ti], m0 = tiles[2 * ti + 1];
+  const int off = offsets[e];
+  const int ne = offsets[e + 1] - off;
+  const int Me = min(64, ne - m0);
+  const int tid = threadIdx.x;
+  for (int q = tid; q < 64 * 8; q += 256) {
+    const int r = q >> 3, ch = q & 7;
+    S v[8];
+    if (r < Me) {
+      const uint4 u = *reinterpret_cast<const uint4*>(in + (size_t)(off + m0 + r) * C + c0 + ch * 8);
+      __builtin_memcpy(v, &u, 16);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (S)0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[r][ch * 8 + j] = v[j];
+  }
+  __syncthreads();
+  const int cols = min(64, ((ne + 7) & ~7) - m0);   // valid + padding
+  for (int q = tid; q < 64 * 8; q += 256) {
+    const int c = q >> 3, ch = q & 7;
+    if (ch * 8 >= cols) continue;
+    S v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = t[ch * 8 + j][c];
+    uint4 u;
+    __builtin_memcpy(&u, v, 16);
+    *reinterpret_cast<uint4*>(out + (size_t)(c0 + c) * ld_out + koff[e] + m0 + ch * 8) = u;
   }
 }
 
@@ -345,12 +583,20 @@ __global__ __launch_bounds__(256) void bwd_dlogits_kernel(
 
 // ---- launcher ---------------------------------------------------------------
 
+// pair columns of the transposed buffers: every expert padded to 8, the row
+// length a multiple of 64 (16-byte aligned rows)
+static int64_t bwd_pcols(int64_t Pmax, int n_exp) {
+  return (Pmax + 8 * (int64_t)n_exp + 63) & ~(int64_t)63;
+}
+
 size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t tiles = (size_t)((Pmax + kBT - 1) / kBT + n_exp + 1);
-  return al(tiles * 8) + al(16) + al(Pmax * D * 2) * 2 + al(Pmax * 2 * F * 4) +
-         al(Pmax * F * 2) + al(Pmax * D * 4) + al(Pmax * F * 4) +
-         al(Pmax * 2 * F * 2) + al(Pmax * D * 4);
+  const size_t Pp = (size_t)bwd_pcols(Pmax, n_exp);
+  return al(tiles * 8) + al(16) + al((n_exp + 1) * 4) + al(Pmax * D * 2) * 2 +
+         al(Pmax * 2 * F * 4) + al(Pmax * F * 2) + al(Pmax * D * 4) +
+         al(Pmax * F * 4) + al(Pmax * 2 * F * 2) + al(Pmax * D * 4) +
+         al(Pp * D * 2) * 2 + al(Pp * 2 * F * 2) + al(Pp * F * 2);
 }
 
 // stage 0: gather, recompute [G | U], H and Yp; 1: dH, dG / dU, dXp, dx;
@@ -365,6 +611,7 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const size_t ntile_cap = (size_t)((Pm + kBT - 1) / kBT + n_exp + 1);
   int32_t* tiles = reinterpret_cast<int32_t*>(b);        b += al(ntile_cap * 8);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(b);      b += al(16);
+  int32_t* koff = reinterpret_cast<int32_t*>(b);         b += al((n_exp + 1) * 4);
   S* Xp = reinterpret_cast<S*>(b);                       b += al(Pm * D * 2);
   S* dYp = reinterpret_cast<S*>(b);                      b += al(Pm * D * 2);
   float* GU = reinterpret_cast<float*>(b);               b += al(Pm * 2 * F * 4);
@@ -372,7 +619,12 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   float* Yp = reinterpret_cast<float*>(b);               b += al(Pm * D * 4);
   float* dH = reinterpret_cast<float*>(b);               b += al(Pm * F * 4);
   S* dGU = reinterpret_cast<S*>(b);                      b += al(Pm * 2 * F * 2);
-  float* dXp = reinterpret_cast<float*>(b);
+  float* dXp = reinterpret_cast<float*>(b);              b += al(Pm * D * 4);
+  const int64_t Pp = bwd_pcols(Pm, n_exp);
+  S* Xt = reinterpret_cast<S*>(b);                       b += al(Pp * D * 2);
+  S* dYt = reinterpret_cast<S*>(b);                      b += al(Pp * D * 2);
+  S* dGUt = reinterpret_cast<S*>(b);                     b += al(Pp * 2 * F * 2);
+  S* Ht = reinterpret_cast<S*>(b);
 
   const int ew_grid = a.ncu * 8;
   const int ub = (int)ntile_cap;
@@ -381,22 +633,33 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
     BGemmArgs g{};
     g.a = A; g.b = B; g.mode = 0; g.N = N; g.K = K; g.c = C; g.ldc = ldc;
     g.offsets = a.offsets; g.tiles = tiles; g.n_tiles = n_tiles; g.n_exp = n_exp;
-    hipLaunchKernelGGL((bgemm_kernel<TT, decltype(akc)::value, decltype(bkc)::value, 0>),
-                       dim3(ub * (N / kBT)), dim3(256), 0, s, g);
+    if constexpr (decltype(bkc)::value)
+      hipLaunchKernelGGL((bgemm_kernel<TT, decltype(akc)::value, true, 0, kBT, kPN>),
+                         dim3(ub * (N / kPN)), dim3(256), 0, s, g);
+    else
+      hipLaunchKernelGGL((bgemm32_kernel<TT, decltype(akc)::value, false, 0>),
+                         dim3(ub * (N / kT32)), dim3(256), 0, s, g);
   };
+  // weight gradients on the pair-transposed copies: both operands
+  // contiguous along the pair index
   auto weight_grad = [&](const BOp& A, const BOp& B, int M, int N, float* C) {
     BGemmArgs g{};
     g.a = A; g.b = B; g.mode = 1; g.M = M; g.N = N; g.c = C; g.ldc = N;
-    g.c_estride = (int64_t)M * N; g.offsets = a.offsets; g.n_exp = n_exp;
-    hipLaunchKernelGGL((bgemm_kernel<TT, false, false, 1>),
-                       dim3(n_exp * (M / kBT) * (N / kBT)), dim3(256), 0, s, g);
+    g.c_estride = (int64_t)M * N; g.offsets = a.offsets; g.koff = koff;
+    g.n_exp = n_exp;
+    hipLaunchKernelGGL((bgemm_kernel<TT, true, true, 1, 128, 128>),
+                       dim3(n_exp * (M / 128) * (N / 128)), dim3(256), 0, s, g);
+  };
+  auto transpose = [&](const S* in, int C, S* outp) {
+    hipLaunchKernelGGL((bwd_transpose_kernel<S>), dim3(ub * (C / 64)), dim3(256), 0, s,
+                       in, C, a.offsets, tiles, n_tiles, koff, (int)Pp, outp);
   };
   using KCt = std::true_type;
   using ICt = std::false_type;
   const int64_t wFD = (int64_t)F * D;
   if (stage == 0) {
     hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
-                       n_exp, tiles, n_tiles);
+                       n_exp, tiles, n_tiles, koff);
     hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
                        (const S*)a.x, a.dy, a.pair_token, a.pair_w, a.offsets,
                        n_exp, D, Xp, dYp);
@@ -424,10 +687,16 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
                          a.tok2pair, a.offsets, a.T, a.k, D, a.n_shared, a.E, a.dx);
   } else if (stage == 2) {
     // weight gradients (every expert, zero pairs give zeros)
-    weight_grad(BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{Xp, nullptr, D, 0, 0}, F, D, a.dwg);
-    weight_grad(BOp{(const S*)dGU + F, nullptr, 2 * F, 0, 0}, BOp{Xp, nullptr, D, 0, 0},
-                F, D, a.dwu);
-    weight_grad(BOp{dYp, nullptr, D, 0, 0}, BOp{H, nullptr, F, 0, 0}, D, F, a.dwd);
+    transpose(Xp, D, Xt);
+    transpose(dYp, D, dYt);
+    transpose(dGU, 2 * F, dGUt);
+    transpose(H, F, Ht);
+    weight_grad(BOp{dGUt, nullptr, (int)Pp, 0, 0}, BOp{Xt, nullptr, (int)Pp, 0, 0},
+                F, D, a.dwg);
+    weight_grad(BOp{dGUt + (size_t)F * Pp, nullptr, (int)Pp, 0, 0},
+                BOp{Xt, nullptr, (int)Pp, 0, 0}, F, D, a.dwu);
+    weight_grad(BOp{dYt, nullptr, (int)Pp, 0, 0}, BOp{Ht, nullptr, (int)Pp, 0, 0},
+                D, F, a.dwd);
   } else if (a.dtw || a.dlogits) {
     float* dtw = a.dtw ? a.dtw : a.dtw_scratch;
     const int64_t q = (int64_t)a.T * a.k;
