@@ -451,15 +451,27 @@ def bench_backward(args, dev, torch, moe, W):
         phase_ms, calls = moe.moe_phase_times(reset=True)
         per = {n: phase_ms[n] / max(calls, 1)
                for n in ("bwd_recompute", "bwd_data", "bwd_weights", "bwd_routing")}
-        amount = {"bwd_recompute": 6.0 * D * F * P, "bwd_data": 6.0 * D * F * P,
-                  "bwd_weights": 6.0 * D * F * P}
+        # recompute and data gradients: 6 D F flops a pair each (matrix
+        # cores); weight gradients: writing the f32 gradients of every
+        # expert (3 E' D F x 4 B) plus reading the per-pair operands once
+        # outweighs their 6 D F flops a pair at the HBM / MFMA ridge
+        n_exp = E + ns
+        amount = {"bwd_recompute": ("mfma", 6.0 * D * F * P),
+                  "bwd_data": ("mfma", 6.0 * D * F * P),
+                  "bwd_weights": ("hbm", 3.0 * n_exp * D * F * 4
+                                  + P * (2.0 * D + 3.0 * F) * W.dtype_bytes(wl["x_dtype"]))}
         dom = max(amount, key=lambda n: per[n])
-        achieved = amount[dom] / (per[dom] * 1e-3) / 1e12
-        peak = PEAK_TFLOPS[wl["x_dtype"]]
-        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        bound, amt = amount[dom]
+        if bound == "mfma":
+            achieved = amt / (per[dom] * 1e-3) / 1e12
+            peak, u = PEAK_TFLOPS[wl["x_dtype"]], "TFLOP/s"
+        else:
+            achieved = amt / (per[dom] * 1e-3) / 1e9
+            peak, u = PEAK_HBM_GBS, "GB/s"
+        roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2),
+                    "peak": peak, "unit": u, "frac": round(achieved / peak, 4),
                     "traffic": load_traffic(wl["name"], dom),
-                    "algorithmic_per_launch": amount[dom],
+                    "algorithmic_per_launch": amt,
                     "avg_launch_ms": round(per[dom], 4),
                     "phase_ms_per_step": {n: round(v, 4) for n, v in per.items()}}
     cpu = None

@@ -242,6 +242,171 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs g) {
   }
 }
 
+// Products of two K-contiguous operands on 128 x 128 tiles, operands
+// streamed HBM -> LDS by buffer_load ... lds through a ring of four 32 KB
+// stages (64 K values, one whole 128-byte line per row), so that several
+// stages' loads are in flight: waves 0..3 load the A rows, 4..7 the B rows;
+// waves w and w + 4 own the same 64 x 64 outputs and take the first and
+// second half of each stage's K, their sums added through LDS at the end.
+// MODE 0: A = 128 pair rows of an expert (the 128-row tile list), B = rows
+// of its weight, K fixed. MODE 1: both operands pair-transposed, rows are
+// features, K = the expert's columns koff[e] .. koff[e + 1] (a multiple of
+// 64, zero padded).
+__device__ __forceinline__ int dswz(int r, int c) {
+  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+template <class TT, int MODE, int NS>
+__global__ __launch_bounds__(512, NS == 2 ? 2 : 1) void bgemm_dma_kernel(BGemmArgs g) {
+  using V8 = typename TT::V8;
+  constexpr int kStage = 256 * 128;           // 128 A + 128 B rows
+  constexpr int kDma = kStage / 1024 / 8;     // 4 loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) char smem[NS * kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = wave >> 2, wq = wave & 3;
+  const int wm = wq >> 1, wn = wq & 1;
+  int e, m0, Me, n0, nk, kcol;
+  const char* abase;
+  const char* bbase;
+  uint32_t a_rows, b_rows;      // rows each descriptor may touch
+  float* cbase;
+  size_t crow0;
+  if constexpr (MODE == 0) {
+    const int nt = g.N / 128;
+    const int ti = blockIdx.x / nt;
+    if (ti >= *g.n_tiles) return;   // block-uniform, before any barrier
+    n0 = (blockIdx.x - ti * nt) * 128;
+    e = g.tiles[2 * ti];
+    m0 = g.tiles[2 * ti + 1];
+    const int off = g.offsets[e];
+    Me = min(128, g.offsets[e + 1] - off - m0);
+    nk = g.K / 64;
+    kcol = 0;
+    abase = (const char*)g.a.p + (size_t)(off + m0) * g.a.ld * 2;
+    a_rows = (uint32_t)Me;
+    bbase = (const char*)g.b.p + ((size_t)e * g.b.estride + (size_t)n0 * g.b.ld) * 2;
+    b_rows = 128;
+    cbase = g.c;
+    crow0 = (size_t)(off + m0);
+  } else {
+    const int mt = g.M / 128, nt = g.N / 128;
+    const int per = mt * nt;
+    e = blockIdx.x / per;
+    const int r = blockIdx.x - e * per;
+    m0 = (r / nt) * 128;
+    n0 = (r % nt) * 128;
+    Me = 128;
+    kcol = g.koff[e];
+    nk = (g.koff[e + 1] - kcol) / 64;
+    abase = (const char*)g.a.p + ((size_t)m0 * g.a.ld + kcol) * 2;
+    a_rows = 128;
+    bbase = (const char*)g.b.p + ((size_t)n0 * g.b.ld + kcol) * 2;
+    b_rows = 128;
+    cbase = g.c + (size_t)e * g.c_estride;
+    crow0 = (size_t)m0;
+  }
+  if (nk == 0) {   // an expert without pairs: zero gradients (block-uniform)
+    for (int i = tid; i < 128 * 128; i += 512)
+      cbase[(crow0 + (i >> 7)) * g.ldc + n0 + (i & 127)] = 0.f;
+    return;
+  }
+  const bool is_a = wave < 4;
+  const int ld = is_a ? g.a.ld : g.b.ld;
+  const int nrows = (int)(is_a ? a_rows : b_rows);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+      is_a ? abase : bbase, (uint32_t)((size_t)(nrows - 1) * ld * 2 + (size_t)nk * 128));
+  uint32_t voff[kDma];
+#pragma unroll
+  for (int jj = 0; jj < kDma; ++jj) {
+    const int R = 8 * (wave * kDma + jj) + (lane >> 3);   // stage row 0..255
+    const int r = min(is_a ? R : R - 128, nrows - 1);
+    voff[jj] = (uint32_t)r * (uint32_t)ld * 2u + (uint32_t)((lane & 7) ^ ((R >> 1) & 7)) * 16u;
+  }
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int jj = 0; jj < kDma; ++jj) {
+      char* dst = smem + (kt % NS) * kStage + (wave * kDma + jj) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, (int)voff[jj],
+                                               min(kt, nk - 1) * 128, 0, 0);
+    }
+  };
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  struct Frag { V8 a[2]; V8 b[2]; };
+  auto read = [&](int kt, int step, Frag& f) {
+    const char* S = smem + (kt % NS) * kStage;
+    const int ch = step * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      f.a[i] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
+          S + dswz(wm * 64 + i * 32 + (lane & 31), ch)));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      f.b[j] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
+          S + dswz(128 + wn * 64 + j * 32 + (lane & 31), ch)));
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+  };
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) issue(st);
+  wait_vmcnt<(NS - 2) * kDma>();
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  read(0, 2 * kq, f0);
+  for (int kt = 0; kt < nk; ++kt) {
+    read(kt, 2 * kq + 1, f1);
+    issue(kt + NS - 1);
+    mma(f0);
+    mma(f1);
+    // stage kt+1 landed for this wave, then for every wave; the reads of
+    // stage kt were consumed above, so its slot may be refilled next
+    wait_vm_lgkm0<(NS - 2) * kDma>();
+    __builtin_amdgcn_s_barrier();
+    read(kt + 1, 2 * kq, f0);
+  }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();   // the ring is free
+  float* red = reinterpret_cast<float*>(smem) + wq * (64 * 64);
+  if (kq == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (kq == 1) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < Me) cbase[(crow0 + m) * g.ldc + n] = acc[i][j][r];
+      }
+  }
+}
+
 // The 64 x 64, 32-deep variant: rows of 64 bytes in LDS (chunk c of row r
 // at c ^ ((r >> 2) & 3)). Its transposing stores collide less than those of
 // the 128-byte rows above, so the products with an operand contiguous along
@@ -382,25 +547,31 @@ __global__ __launch_bounds__(256) void bgemm32_kernel(BGemmArgs g) {
 
 // (expert, first row) of every 64-row tile of the per-pair products, in
 // expert order; n_tiles receives the count.
-// Also the padded column offsets of the pair-transposed buffers: expert e's
-// pairs at columns koff[e] .. koff[e] + n_e, koff[e + 1] = koff[e] + n_e
-// rounded up to 8.
+// Also the 128-row tiles, and the padded column offsets of the
+// pair-transposed buffers: expert e's pairs at columns koff[e] .. koff[e] +
+// n_e, koff[e + 1] = koff[e] + n_e rounded up to 64 (zeros in between).
 __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
     const int32_t* __restrict__ offsets, int n_exp, int32_t* __restrict__ tiles,
-    int32_t* __restrict__ n_tiles, int32_t* __restrict__ koff) {
+    int32_t* __restrict__ n_tiles, int32_t* __restrict__ tiles128,
+    int32_t* __restrict__ n_tiles128, int32_t* __restrict__ koff) {
   __shared__ int32_t start[kMaxExperts + 2];
+  __shared__ int32_t start2[kMaxExperts + 2];
   if (threadIdx.x == 0) {
-    int acc = 0, col = 0;
+    int acc = 0, acc2 = 0, col = 0;
     for (int e = 0; e < n_exp; ++e) {
       start[e] = acc;
+      start2[e] = acc2;
       koff[e] = col;
       const int ne = offsets[e + 1] - offsets[e];
       acc += (ne + kBT - 1) / kBT;
-      col += (ne + 7) & ~7;
+      acc2 += (ne + 127) / 128;
+      col += (ne + 63) & ~63;
     }
     start[n_exp] = acc;
+    start2[n_exp] = acc2;
     koff[n_exp] = col;
     *n_tiles = acc;
+    *n_tiles128 = acc2;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < n_exp; e += blockDim.x) {
@@ -408,6 +579,11 @@ __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
     for (int i = 0; i < nt; ++i) {
       tiles[2 * (start[e] + i)] = e;
       tiles[2 * (start[e] + i) + 1] = i * kBT;
+    }
+    const int nt2 = start2[e + 1] - start2[e];
+    for (int i = 0; i < nt2; ++i) {
+      tiles128[2 * (start2[e] + i)] = e;
+      tiles128[2 * (start2[e] + i) + 1] = i * 128;
     }
   }
 }
@@ -445,10 +621,9 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
     for (int j = 0; j < 8; ++j) t[r][ch * 8 + j] = v[j];
   }
   __syncthreads();
-  const int cols = min(64, ((ne + 7) & ~7) - m0);   // valid + padding
+  // all 64 columns: past the expert's last pair they are its zero padding
   for (int q = tid; q < 64 * 8; q += 256) {
     const int c = q >> 3, ch = q & 7;
-    if (ch * 8 >= cols) continue;
     S v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = t[ch * 8 + j][c];
@@ -583,17 +758,16 @@ __global__ __launch_bounds__(256) void bwd_dlogits_kernel(
 
 // ---- launcher ---------------------------------------------------------------
 
-// pair columns of the transposed buffers: every expert padded to 8, the row
-// length a multiple of 64 (16-byte aligned rows)
+// pair columns of the transposed buffers: every expert padded to 64
 static int64_t bwd_pcols(int64_t Pmax, int n_exp) {
-  return (Pmax + 8 * (int64_t)n_exp + 63) & ~(int64_t)63;
+  return (Pmax + 64 * (int64_t)n_exp + 63) & ~(int64_t)63;
 }
 
 size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t tiles = (size_t)((Pmax + kBT - 1) / kBT + n_exp + 1);
   const size_t Pp = (size_t)bwd_pcols(Pmax, n_exp);
-  return al(tiles * 8) + al(16) + al((n_exp + 1) * 4) + al(Pmax * D * 2) * 2 +
+  return al(tiles * 8) * 2 + al(16) * 2 + al((n_exp + 1) * 4) + al(Pmax * D * 2) * 2 +
          al(Pmax * 2 * F * 4) + al(Pmax * F * 2) + al(Pmax * D * 4) +
          al(Pmax * F * 4) + al(Pmax * 2 * F * 2) + al(Pmax * D * 4) +
          al(Pp * D * 2) * 2 + al(Pp * 2 * F * 2) + al(Pp * F * 2);
@@ -611,6 +785,8 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const size_t ntile_cap = (size_t)((Pm + kBT - 1) / kBT + n_exp + 1);
   int32_t* tiles = reinterpret_cast<int32_t*>(b);        b += al(ntile_cap * 8);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(b);      b += al(16);
+  int32_t* tiles128 = reinterpret_cast<int32_t*>(b);     b += al(ntile_cap * 8);
+  int32_t* n_tiles128 = reinterpret_cast<int32_t*>(b);   b += al(16);
   int32_t* koff = reinterpret_cast<int32_t*>(b);         b += al((n_exp + 1) * 4);
   S* Xp = reinterpret_cast<S*>(b);                       b += al(Pm * D * 2);
   S* dYp = reinterpret_cast<S*>(b);                      b += al(Pm * D * 2);
@@ -628,15 +804,18 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
 
   const int ew_grid = a.ncu * 8;
   const int ub = (int)ntile_cap;
+  const int ub128 = (int)((Pm + 127) / 128 + n_exp + 1);
   auto per_pair = [&](auto akc, auto bkc, const BOp& A, const BOp& B, int N,
                       int K, float* C, int ldc) {
     BGemmArgs g{};
     g.a = A; g.b = B; g.mode = 0; g.N = N; g.K = K; g.c = C; g.ldc = ldc;
     g.offsets = a.offsets; g.tiles = tiles; g.n_tiles = n_tiles; g.n_exp = n_exp;
-    if constexpr (decltype(bkc)::value)
-      hipLaunchKernelGGL((bgemm_kernel<TT, decltype(akc)::value, true, 0, kBT, kPN>),
-                         dim3(ub * (N / kPN)), dim3(256), 0, s, g);
-    else
+    if constexpr (decltype(bkc)::value) {
+      g.tiles = tiles128;
+      g.n_tiles = n_tiles128;
+      hipLaunchKernelGGL((bgemm_dma_kernel<TT, 0, 4>), dim3(ub128 * (N / 128)), dim3(512),
+                         0, s, g);
+    } else
       hipLaunchKernelGGL((bgemm32_kernel<TT, decltype(akc)::value, false, 0>),
                          dim3(ub * (N / kT32)), dim3(256), 0, s, g);
   };
@@ -647,8 +826,8 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
     g.a = A; g.b = B; g.mode = 1; g.M = M; g.N = N; g.c = C; g.ldc = N;
     g.c_estride = (int64_t)M * N; g.offsets = a.offsets; g.koff = koff;
     g.n_exp = n_exp;
-    hipLaunchKernelGGL((bgemm_kernel<TT, true, true, 1, 128, 128>),
-                       dim3(n_exp * (M / 128) * (N / 128)), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((bgemm_dma_kernel<TT, 1, 2>),
+                       dim3(n_exp * (M / 128) * (N / 128)), dim3(512), 0, s, g);
   };
   auto transpose = [&](const S* in, int C, S* outp) {
     hipLaunchKernelGGL((bwd_transpose_kernel<S>), dim3(ub * (C / 64)), dim3(256), 0, s,
@@ -659,7 +838,7 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const int64_t wFD = (int64_t)F * D;
   if (stage == 0) {
     hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
-                       n_exp, tiles, n_tiles, koff);
+                       n_exp, tiles, n_tiles, tiles128, n_tiles128, koff);
     hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
                        (const S*)a.x, a.dy, a.pair_token, a.pair_w, a.offsets,
                        n_exp, D, Xp, dYp);
