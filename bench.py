@@ -276,7 +276,8 @@ def main():
                     "traffic": traffic,
                     "algorithmic_per_launch": amount,
                     "avg_launch_ms": round(per[dom], 4),
-                    "phase_ms_per_step": {n: round(v, 4) for n, v in per.items()}}
+                    "phase_ms_per_step": {n: round(v, 4) for n, v in per.items()
+                                          if v > 0}}
 
     cpu = None
     if not args.no_cpu_baseline:
