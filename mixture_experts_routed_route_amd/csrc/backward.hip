@@ -14,14 +14,12 @@
 //   [dG | dU] = SwiGLU backward         (compute dtype)
 //   dXp  = dG W_gate + dU W_up          dx[t] = sum over its pairs (fixed order)
 //   dW_gate[e] = sum_p dG_p x_p^T,  dW_up[e] likewise,  dW_down[e] = sum_p dYp H_p^T
-// The six products run on grouped MFMA kernels staged through LDS: an
-// operand whose memory is contiguous along K is copied in 16-byte pieces,
-// one contiguous along the output index (the weights read as [K, N], and
-// both operands of the weight gradients, whose K is the pair index) is
-// transposed on its way into LDS. Products of two K-contiguous operands take
-// 64 x 128 tiles and 64-deep steps of 128-byte LDS rows; the others 64 x 64
-// tiles and 32-deep steps of 64-byte rows, whose transposing stores collide
-// on fewer banks.
+// The six products run on grouped MFMA kernels over 128 x 128 tiles whose
+// operands stream HBM -> LDS by buffer_load ... lds through a ring of
+// 64-deep stages: the weight gradients, whose K is the pair index, on
+// pair-transposed copies of their operands; dH and dX, which read their
+// weights as [K, N], with those rows kept in LDS as in memory and each K
+// fragment assembled from 2-byte reads.
 #include <type_traits>
 
 #include "device_common.h"
@@ -33,8 +31,7 @@ namespace {
 struct BF16B { using S = __bf16; using V8 = bf16x8; };
 struct F16B { using S = _Float16; using V8 = half8; };
 
-constexpr int kBT = 64;   // rows of a per-pair tile
-constexpr int kPN = 128;  // columns of a per-pair tile
+constexpr int kBT = 64;   // rows of a tile of the transposes
 
 }  // namespace
 
@@ -61,186 +58,13 @@ struct BGemmArgs {
   int ldc;
   int64_t c_estride;        // mode 1: output matrix of expert e at e * c_estride
   const int32_t* offsets;   // [n_exp + 1]
-  const int32_t* tiles;     // mode 0: (expert, first row) per 64-row tile
+  const int32_t* tiles;     // mode 0: (expert, first row) per 128-row tile
   const int32_t* n_tiles;   // mode 0: number of tiles (device)
   const int32_t* koff;      // mode 1 on pair-transposed operands: expert e's
                             // K columns start at koff[e] (a multiple of 8)
                             // and run to koff[e + 1] (zero padded)
   int n_exp;
 };
-
-// A BR x 64 operand tile (BR rows of the product, 64 K values) in LDS as
-// BR rows of 128 bytes; chunk c of row r sits at c ^ ((r >> 1) & 7), so the
-// 16 rows one phase of a fragment read touches hit 16 distinct bank groups.
-__device__ __forceinline__ int bswz(int r, int c) {
-  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
-}
-
-// Loads of one tile into registers: KC: 8 chunks of 8 K values per row,
-// thread t takes row t / 8 + 32 q, chunk t % 8; IC: BR / 8 chunks of 8 row
-// values per K row, thread t takes K row t / (BR / 8) + (2048 / BR) q, chunk
-// t % (BR / 8). Elements past the operand's rows or K read as zero.
-template <bool KC, int BR>
-struct TileRegs { uint4 v[BR * 8 / 256]; };
-
-template <bool KC, int BR>
-__device__ __forceinline__ void load_tile(const BOp& o, int e, int row_base,
-                                          int i0, int ni, int k0, int nk,
-                                          TileRegs<KC, BR>& t, int tid,
-                                          int kcol = 0) {
-  constexpr int NQ = BR * 8 / 256;
-  const char* base;
-  int kk = k0;
-  if (o.p2 && k0 >= o.k_split) { base = (const char*)o.p2; kk = k0 - o.k_split; }
-  else base = (const char*)o.p;
-  if (o.estride) base += (size_t)e * o.estride * 2;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    t.v[q] = uint4{0u, 0u, 0u, 0u};
-    if constexpr (KC) {
-      const int i = (tid >> 3) + 32 * q, c = tid & 7;
-      if (i < ni && k0 + c * 8 < nk) {
-        const size_t row = (size_t)(row_base + i0 + i);
-        t.v[q] = *reinterpret_cast<const uint4*>(base + (row * o.ld + kcol + kk + c * 8) * 2);
-      }
-    } else {
-      constexpr int CPR = BR / 8;                 // chunks per K row
-      const int k = tid / CPR + (256 / CPR) * q, c = tid % CPR;
-      if (k0 + k < nk && c * 8 < ni) {
-        const size_t row = (size_t)(row_base + kk + k);
-        t.v[q] = *reinterpret_cast<const uint4*>(base + (row * o.ld + i0 + c * 8) * 2);
-      }
-    }
-  }
-}
-
-template <bool KC, int BR>
-__device__ __forceinline__ void store_tile(char* s, const TileRegs<KC, BR>& t, int tid) {
-  constexpr int NQ = BR * 8 / 256;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    if constexpr (KC) {
-      const int i = (tid >> 3) + 32 * q, c = tid & 7;
-      *reinterpret_cast<uint4*>(s + bswz(i, c)) = t.v[q];
-    } else {
-      constexpr int CPR = BR / 8;
-      const int k = tid / CPR + (256 / CPR) * q, c = tid % CPR;
-      uint16_t h[8];
-      __builtin_memcpy(h, &t.v[q], 16);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint16_t*>(s + bswz(c * 8 + j, k >> 3) + (k & 7) * 2) = h[j];
-    }
-  }
-}
-
-// C tile BM x BN per block of 4 waves (2 x 2, each (BM / 2) x (BN / 2) in
-// 32 x 32 blocks), K in 64-deep steps: the next step's global loads are in
-// registers while the current one multiplies out of LDS.
-template <class TT, bool AKC, bool BKC, int MODE, int BM, int BN>
-__global__ __launch_bounds__(256) void bgemm_kernel(BGemmArgs g) {
-  using V8 = typename TT::V8;
-  constexpr int NI = BM / 64, NJ = BN / 64;
-  __shared__ __attribute__((aligned(16))) char sA[2][BM * 128];
-  __shared__ __attribute__((aligned(16))) char sB[2][BN * 128];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  int e, m0, Me, n0, K, arow, brow, kcol = 0;
-  float* cbase;
-  size_t crow0;
-  if constexpr (MODE == 0) {
-    const int nt = g.N / BN;
-    const int ti = blockIdx.x / nt;
-    if (ti >= *g.n_tiles) return;   // block-uniform, before any barrier
-    n0 = (blockIdx.x - ti * nt) * BN;
-    e = g.tiles[2 * ti];
-    m0 = g.tiles[2 * ti + 1];
-    const int off = g.offsets[e];
-    Me = min(BM, g.offsets[e + 1] - off - m0);
-    K = g.K;
-    arow = off;          // A: pair rows of the expert
-    brow = 0;            // B: the expert's weight
-    cbase = g.c;
-    crow0 = (size_t)(off + m0);
-  } else {
-    const int mt = g.M / BM, nt = g.N / BN;
-    const int per = mt * nt;
-    e = blockIdx.x / per;
-    const int r = blockIdx.x - e * per;
-    m0 = (r / nt) * BM;
-    n0 = (r % nt) * BN;
-    Me = BM;
-    // both operands transposed per pair ([features, pairs]): rows are the
-    // features, the expert's pairs the K columns koff[e] .. koff[e + 1]
-    kcol = g.koff[e];
-    K = g.koff[e + 1] - kcol;
-    arow = 0;
-    brow = 0;
-    cbase = g.c + (size_t)e * g.c_estride;
-    crow0 = (size_t)m0;
-  }
-  floatx16 acc[NI][NJ];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int nkt = (K + 63) / 64;
-  TileRegs<AKC, BM> ra;
-  TileRegs<BKC, BN> rb;
-  if (nkt > 0) {
-    load_tile<AKC, BM>(g.a, e, arow, m0, Me, 0, K, ra, tid, kcol);
-    load_tile<BKC, BN>(g.b, e, brow, n0, BN, 0, K, rb, tid, kcol);
-    store_tile<AKC, BM>(sA[0], ra, tid);
-    store_tile<BKC, BN>(sB[0], rb, tid);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nkt) {
-      load_tile<AKC, BM>(g.a, e, arow, m0, Me, (kt + 1) * 64, K, ra, tid, kcol);
-      load_tile<BKC, BN>(g.b, e, brow, n0, BN, (kt + 1) * 64, K, rb, tid, kcol);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
-      V8 fa[NI], fb[NJ];
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        fa[i] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
-            sA[cur] + bswz(wm * (BM / 2) + i * 32 + (lane & 31), ch)));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        fb[j] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
-            sB[cur] + bswz(wn * (BN / 2) + j * 32 + (lane & 31), ch)));
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
-    }
-    if (kt + 1 < nkt) {
-      store_tile<AKC, BM>(sA[cur ^ 1], ra, tid);
-      store_tile<BKC, BN>(sB[cur ^ 1], rb, tid);
-    }
-    __syncthreads();
-  }
-  // accumulator r of block (i, j): A row 8 (r / 4) + 4 (lane / 32) + r % 4,
-  // B row lane % 32
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < Me) cbase[(crow0 + m) * g.ldc + n] = acc[i][j][r];
-      }
-  }
-}
 
 // Products of two K-contiguous operands on 128 x 128 tiles, operands
 // streamed HBM -> LDS by buffer_load ... lds through a ring of four 32 KB
@@ -407,141 +231,167 @@ __global__ __launch_bounds__(512, NS == 2 ? 2 : 1) void bgemm_dma_kernel(BGemmAr
   }
 }
 
-// The 64 x 64, 32-deep variant: rows of 64 bytes in LDS (chunk c of row r
-// at c ^ ((r >> 2) & 3)). Its transposing stores collide less than those of
-// the 128-byte rows above, so the products with an operand contiguous along
-// the output index run on it.
-constexpr int kT32 = 64;
-constexpr int kBK32 = 32;
-__device__ __forceinline__ int bswz32(int r, int c) {
-  return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+// Per-pair products whose weight is read as [K, N] (dH = dYp W_down, and
+// dX = [dG | dU] [W_gate; W_up], whose K runs through both weights): the
+// same 128 x 128 tiles and ring as above, but a stage's 64 weight rows land
+// in LDS as they are in memory (64 rows of 128 N values, 256 bytes; the
+// 16-byte chunk c of row k at c ^ 4 for k / 8 odd, so that the two halves of
+// a wave, reading rows k and k + 8, hit different banks), and each lane
+// assembles its 8-deep K fragment from eight 2-byte reads.
+__device__ __forceinline__ int icoff(int k, int n) {
+  return k * 256 + ((((n >> 3) ^ (((k >> 3) & 1) << 2))) << 4) + (n & 7) * 2;
 }
 
-template <class TT, bool KC>
-__device__ __forceinline__ void load_tile32(const BOp& o, int e, int row_base,
-                                          int i0, int ni, int k0, int nk,
-                                          uint4& v, int tid) {
-  // KC: thread -> row i = tid / 4, 8 K values at chunk tid % 4
-  // IC: thread -> k = tid / 8, 8 i values at chunk tid % 8
-  const char* base;
-  int kk = k0;
-  if (o.p2 && k0 >= o.k_split) { base = (const char*)o.p2; kk = k0 - o.k_split; }
-  else base = (const char*)o.p;
-  if (o.estride) base += (size_t)e * o.estride * 2;
-  v = uint4{0u, 0u, 0u, 0u};
-  if constexpr (KC) {
-    const int i = tid >> 2, c = tid & 3;
-    if (i < ni && k0 + c * 8 < nk) {
-      const size_t row = (size_t)(row_base + i0 + i);
-      v = *reinterpret_cast<const uint4*>(base + (row * o.ld + kk + c * 8) * 2);
-    }
-  } else {
-    const int k = tid >> 3, c = tid & 7;
-    if (k0 + k < nk && c * 8 < ni) {
-      const size_t row = (size_t)(row_base + kk + k);
-      v = *reinterpret_cast<const uint4*>(base + (row * o.ld + i0 + c * 8) * 2);
-    }
-  }
-}
-
-template <bool KC>
-__device__ __forceinline__ void store_tile32(char* s, const uint4& v, int tid) {
-  if constexpr (KC) {
-    const int i = tid >> 2, c = tid & 3;
-    *reinterpret_cast<uint4*>(s + bswz32(i, c)) = v;
-  } else {
-    const int k = tid >> 3, c = tid & 7;
-    uint16_t h[8];
-    __builtin_memcpy(h, &v, 16);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = c * 8 + j;
-      *reinterpret_cast<uint16_t*>(s + bswz32(r, k >> 3) + (k & 7) * 2) = h[j];
-    }
-  }
-}
-
-template <class TT, bool AKC, bool BKC, int MODE>
-__global__ __launch_bounds__(256) void bgemm32_kernel(BGemmArgs g) {
+template <class TT, int NS>
+__global__ __launch_bounds__(512, 1) void bgemm_dma_ic_kernel(BGemmArgs g) {
   using V8 = typename TT::V8;
-  __shared__ __attribute__((aligned(16))) char sA[2][kT32 * 64];
-  __shared__ __attribute__((aligned(16))) char sB[2][kT32 * 64];
+  constexpr int kA = 128 * 128;               // A: 128 pair rows x 128 B
+  constexpr int kB = 64 * 256;                // B: 64 K rows x 256 B
+  constexpr int kStage = kA + kB;             // 32 KB
+  constexpr int kDma = kStage / 1024 / 8;     // 4 loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) char smem[NS * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  int e, m0, Me, n0, K, arow, brow;
-  float* cbase;
-  size_t crow0;
-  if constexpr (MODE == 0) {
-    const int nt = g.N / kT32;
-    const int ti = blockIdx.x / nt;
-    if (ti >= *g.n_tiles) return;   // block-uniform, before any barrier
-    n0 = (blockIdx.x - ti * nt) * kT32;
-    e = g.tiles[2 * ti];
-    m0 = g.tiles[2 * ti + 1];
-    const int off = g.offsets[e];
-    Me = min(kT32, g.offsets[e + 1] - off - m0);
-    K = g.K;
-    arow = off;          // A: pair rows of the expert
-    brow = 0;            // B: the expert's weight
-    cbase = g.c;
-    crow0 = (size_t)(off + m0);
-  } else {
-    const int mt = g.M / kT32, nt = g.N / kT32;
-    const int per = mt * nt;
-    e = blockIdx.x / per;
-    const int r = blockIdx.x - e * per;
-    m0 = (r / nt) * kT32;
-    n0 = (r % nt) * kT32;
-    Me = kT32;
-    const int off = g.offsets[e];
-    K = g.offsets[e + 1] - off;
-    arow = off;          // both operands: the expert's pairs along K
-    brow = off;
-    cbase = g.c + (size_t)e * g.c_estride;
-    crow0 = (size_t)m0;
-  }
-  floatx16 acc;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = wave >> 2, wq = wave & 3;
+  const int wm = wq >> 1, wn = wq & 1;
+  const int nt = g.N / 128;
+  const int ti = blockIdx.x / nt;
+  if (ti >= *g.n_tiles) return;   // block-uniform, before any barrier
+  const int n0 = (blockIdx.x - ti * nt) * 128;
+  const int e = g.tiles[2 * ti];
+  const int m0 = g.tiles[2 * ti + 1];
+  const int off = g.offsets[e];
+  const int Me = min(128, g.offsets[e + 1] - off - m0);
+  const int nk = g.K / 64;
+  const size_t crow0 = (size_t)(off + m0);
+  // waves 0..3: A rows (8 rows of 128 B per 1 KB load); 4..7: B K-rows
+  // (4 rows of 256 B per 1 KB load)
+  const bool is_a = wave < 4;
+  __amdgpu_buffer_rsrc_t rs, rs2;
+  uint32_t voff[kDma];
+  if (is_a) {
+    const char* abase = (const char*)g.a.p + (size_t)(off + m0) * g.a.ld * 2;
+    rs = make_rsrc(abase, (uint32_t)((size_t)(Me - 1) * g.a.ld * 2 + (size_t)nk * 128));
+    rs2 = rs;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int nkt = (K + kBK32 - 1) / kBK32;
-  uint4 va, vb;
-  const int Ne = kT32;   // N is a multiple of the tile in every product
-  if (nkt > 0) {
-    load_tile32<TT, AKC>(g.a, e, arow, m0, Me, 0, K, va, tid);
-    load_tile32<TT, BKC>(g.b, e, brow, n0, Ne, 0, K, vb, tid);
-    store_tile32<AKC>(sA[0], va, tid);
-    store_tile32<BKC>(sB[0], vb, tid);
+    for (int jj = 0; jj < kDma; ++jj) {
+      const int R = 8 * (wave * kDma + jj) + (lane >> 3);
+      const int r = min(R, Me - 1);
+      voff[jj] = (uint32_t)r * (uint32_t)g.a.ld * 2u +
+                 (uint32_t)((lane & 7) ^ ((R >> 1) & 7)) * 16u;
+    }
+  } else {
+    // the weight rows of this expert: [K rows][ld] with the N columns n0..;
+    // with p2, K values from k_split on come from the second matrix
+    const char* b1 = (const char*)g.b.p + ((size_t)e * g.b.estride + n0) * 2;
+    const char* b2 = g.b.p2 ? (const char*)g.b.p2 + ((size_t)e * g.b.estride + n0) * 2 : b1;
+    const int k1 = g.b.p2 ? g.b.k_split : g.K;
+    rs = make_rsrc(b1, (uint32_t)((size_t)(k1 - 1) * g.b.ld * 2 + 256));
+    rs2 = make_rsrc(b2, (uint32_t)((size_t)(g.K - k1 > 0 ? g.K - k1 - 1 : 0) * g.b.ld * 2 + 256));
+#pragma unroll
+    for (int jj = 0; jj < kDma; ++jj) {
+      const int kr = 4 * ((wave - 4) * kDma + jj) + (lane >> 4);   // K row 0..63
+      const int p = lane & 15;                                      // LDS chunk
+      const int c = p ^ (((kr >> 3) & 1) << 2);                     // its N chunk
+      voff[jj] = (uint32_t)kr * (uint32_t)g.b.ld * 2u + (uint32_t)c * 16u;
+    }
+  }
+  const int ksplit = g.b.p2 ? g.b.k_split : g.K;
+  auto issue = [&](int kt) {
+    const int kc = min(kt, nk - 1);
+#pragma unroll
+    for (int jj = 0; jj < kDma; ++jj) {
+      char* dst = smem + (kt % NS) * kStage + (wave * kDma + jj) * 1024;
+      if (is_a) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, (int)voff[jj],
+                                                 kc * 128, 0, 0);
+      } else {
+        const int k0 = kc * 64;
+        const bool second = k0 >= ksplit;
+        const int krow = second ? k0 - ksplit : k0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rs2 : rs, (lds_ptr_t)dst, 16,
+                                                 (int)voff[jj], krow * g.b.ld * 2, 0, 0);
+      }
+    }
+  };
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  struct Frag { V8 a[2]; V8 b[2]; };
+  auto read = [&](int kt, int step, Frag& f) {
+    const char* S = smem + (kt % NS) * kStage;
+    const int ch = step * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      f.a[i] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
+          S + dswz(wm * 64 + i * 32 + (lane & 31), ch)));
+    const char* B = S + kA;
+    const int kb = step * 16 + 8 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wn * 64 + j * 32 + (lane & 31);
+      uint16_t h[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        h[q] = *reinterpret_cast<const uint16_t*>(B + icoff(kb + q, n));
+      f.b[j] = __builtin_bit_cast(V8, h);
+    }
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+  };
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) issue(st);
+  wait_vmcnt<(NS - 2) * kDma>();
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  read(0, 2 * kq, f0);
+  for (int kt = 0; kt < nk; ++kt) {
+    read(kt, 2 * kq + 1, f1);
+    issue(kt + NS - 1);
+    mma(f0);
+    mma(f1);
+    wait_vm_lgkm0<(NS - 2) * kDma>();
+    __builtin_amdgcn_s_barrier();
+    read(kt + 1, 2 * kq, f0);
+  }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();   // the ring is free
+  float* red = reinterpret_cast<float*>(smem) + wq * (64 * 64);
+  if (kq == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
   }
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nkt) {
-      load_tile32<TT, AKC>(g.a, e, arow, m0, Me, (kt + 1) * kBK32, K, va, tid);
-      load_tile32<TT, BKC>(g.b, e, brow, n0, Ne, (kt + 1) * kBK32, K, vb, tid);
-    }
+  if (kq == 1) return;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
-      const V8 fa = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
-          sA[cur] + bswz32(wm * 32 + (lane & 31), ch)));
-      const V8 fb = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(
-          sB[cur] + bswz32(wn * 32 + (lane & 31), ch)));
-      acc = mfma32(fa, fb, acc);
-    }
-    if (kt + 1 < nkt) {
-      store_tile32<AKC>(sA[cur ^ 1], va, tid);
-      store_tile32<BKC>(sB[cur ^ 1], vb, tid);
-    }
-    __syncthreads();
-  }
-  // accumulator r: A row 8 (r / 4) + 4 (lane / 32) + r % 4, B row lane % 32
-  const int n = n0 + wn * 32 + (lane & 31);
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (m < Me) cbase[(crow0 + m) * g.ldc + n] = acc[r];
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < Me) g.c[(crow0 + m) * g.ldc + n] = acc[i][j][r];
+      }
   }
 }
 
@@ -815,9 +665,12 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
       g.n_tiles = n_tiles128;
       hipLaunchKernelGGL((bgemm_dma_kernel<TT, 0, 4>), dim3(ub128 * (N / 128)), dim3(512),
                          0, s, g);
-    } else
-      hipLaunchKernelGGL((bgemm32_kernel<TT, decltype(akc)::value, false, 0>),
-                         dim3(ub * (N / kT32)), dim3(256), 0, s, g);
+    } else {
+      g.tiles = tiles128;
+      g.n_tiles = n_tiles128;
+      hipLaunchKernelGGL((bgemm_dma_ic_kernel<TT, 4>), dim3(ub128 * (N / 128)), dim3(512),
+                         0, s, g);
+    }
   };
   // weight gradients on the pair-transposed copies: both operands
   // contiguous along the pair index
