@@ -500,9 +500,10 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
     const float wv = pair_w[p];
     *reinterpret_cast<uint4*>(Xp + p * D + c) =
         *reinterpret_cast<const uint4*>(x + (size_t)t * D + c);
-    S o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = (S)(wv * dy[(size_t)t * D + c + j]);
+    const float4 d0 = *reinterpret_cast<const float4*>(dy + (size_t)t * D + c);
+    const float4 d1 = *reinterpret_cast<const float4*>(dy + (size_t)t * D + c + 4);
+    S o[8] = {(S)(wv * d0.x), (S)(wv * d0.y), (S)(wv * d0.z), (S)(wv * d0.w),
+              (S)(wv * d1.x), (S)(wv * d1.y), (S)(wv * d1.z), (S)(wv * d1.w)};
     __builtin_memcpy(dYp + p * D + c, o, 16);
   }
 }
@@ -510,49 +511,69 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
 __device__ __forceinline__ float clamp_hi(float v, float c) { return c > 0.f ? fminf(v, c) : v; }
 
 // H = silu(min(G, c)) * clamp(U, -c, c), rounded to the compute dtype
-// (the forward's SwiGLU: hardware 2^x and reciprocal).
+// (the forward's SwiGLU: hardware 2^x and reciprocal); 4 features a thread.
 template <class S>
 __global__ __launch_bounds__(256) void bwd_swiglu_kernel(
     const float* __restrict__ GU, const int32_t* __restrict__ offsets,
     int n_exp, int F, float c, S* __restrict__ H) {
-  const size_t n = (size_t)offsets[n_exp] * F;
+  const size_t n = (size_t)offsets[n_exp] * (F / 4);
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
-    const size_t p = i / F;
-    const int f = (int)(i - p * F);
-    H[i] = (S)swiglu(GU[p * 2 * F + f], GU[p * 2 * F + F + f], c);
+    const size_t p = i / (F / 4);
+    const int f = (int)(i - p * (F / 4)) * 4;
+    const float4 g = *reinterpret_cast<const float4*>(GU + p * 2 * F + f);
+    const float4 u = *reinterpret_cast<const float4*>(GU + p * 2 * F + F + f);
+    S o[4] = {(S)swiglu(g.x, u.x, c), (S)swiglu(g.y, u.y, c), (S)swiglu(g.z, u.z, c),
+              (S)swiglu(g.w, u.w, c)};
+    __builtin_memcpy(H + p * F + f, o, 8);
   }
 }
 
 // dG = dH * clamp(U) * silu'(min(G, c)) * [G <= c];
 // dU = dH * silu(min(G, c)) * [-c <= U <= c]; silu'(z) = s (1 + z (1 - s)),
-// s = 1 / (1 + e^-z). Written side by side, [P, 2F], compute dtype.
+// s = 1 / (1 + e^-z). Written side by side, [P, 2F], compute dtype; 4
+// features a thread.
+__device__ __forceinline__ void swiglu_back1(float g, float u, float dh, float c,
+                                             float& dg, float& du) {
+  float gc = g, uc = u, mg = 1.f, mu = 1.f;
+  if (c > 0.f) {
+    if (g > c) { gc = c; mg = 0.f; }
+    if (u < -c) { uc = -c; mu = 0.f; }
+    if (u > c) { uc = c; mu = 0.f; }
+  }
+  const float s = 1.f / (1.f + expf(-gc));
+  dg = dh * uc * s * (1.f + gc * (1.f - s)) * mg;
+  du = dh * gc * s * mu;
+}
+
 template <class S>
 __global__ __launch_bounds__(256) void bwd_swiglu_back_kernel(
     const float* __restrict__ GU, const float* __restrict__ dH,
     const int32_t* __restrict__ offsets, int n_exp, int F, float c,
     S* __restrict__ dGU) {
-  const size_t n = (size_t)offsets[n_exp] * F;
+  const size_t n = (size_t)offsets[n_exp] * (F / 4);
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
-    const size_t p = i / F;
-    const int f = (int)(i - p * F);
-    const float g = GU[p * 2 * F + f], u = GU[p * 2 * F + F + f];
-    const float dh = dH[i];
-    float gc = g, uc = u, mg = 1.f, mu = 1.f;
-    if (c > 0.f) {
-      if (g > c) { gc = c; mg = 0.f; }
-      if (u < -c) { uc = -c; mu = 0.f; }
-      if (u > c) { uc = c; mu = 0.f; }
-    }
-    const float s = 1.f / (1.f + expf(-gc));
-    dGU[p * 2 * F + f] = (S)(dh * uc * s * (1.f + gc * (1.f - s)) * mg);
-    dGU[p * 2 * F + F + f] = (S)(dh * gc * s * mu);
+    const size_t p = i / (F / 4);
+    const int f = (int)(i - p * (F / 4)) * 4;
+    const float4 g = *reinterpret_cast<const float4*>(GU + p * 2 * F + f);
+    const float4 u = *reinterpret_cast<const float4*>(GU + p * 2 * F + F + f);
+    const float4 d = *reinterpret_cast<const float4*>(dH + p * F + f);
+    float dg[4], du[4];
+    swiglu_back1(g.x, u.x, d.x, c, dg[0], du[0]);
+    swiglu_back1(g.y, u.y, d.y, c, dg[1], du[1]);
+    swiglu_back1(g.z, u.z, d.z, c, dg[2], du[2]);
+    swiglu_back1(g.w, u.w, d.w, c, dg[3], du[3]);
+    S og[4] = {(S)dg[0], (S)dg[1], (S)dg[2], (S)dg[3]};
+    S ou[4] = {(S)du[0], (S)du[1], (S)du[2], (S)du[3]};
+    __builtin_memcpy(dGU + p * 2 * F + f, og, 8);
+    __builtin_memcpy(dGU + p * 2 * F + F + f, ou, 8);
   }
 }
 
 // dtw[t, j] = dy[t] . Yp[tok2pair[t, j]] (0 for a dropped pair); one wave
-// per (t, j), lanes over D in a fixed stride, then a fixed butterfly.
+// per (t, j), lanes over D four values at a time in a fixed stride, then a
+// fixed butterfly.
 __global__ __launch_bounds__(256) void bwd_dtw_kernel(
     const float* __restrict__ dy, const float* __restrict__ Yp,
     const int32_t* __restrict__ tok2pair, int T, int k, int D,
@@ -564,30 +585,43 @@ __global__ __launch_bounds__(256) void bwd_dtw_kernel(
   const int p = tok2pair[q];
   float s = 0.f;
   if (p >= 0)
-    for (int d = lane; d < D; d += 64) s = fmaf(dy[(size_t)t * D + d], Yp[(size_t)p * D + d], s);
+    for (int d = lane * 4; d < D; d += 256) {
+      const float4 a = *reinterpret_cast<const float4*>(dy + (size_t)t * D + d);
+      const float4 b = *reinterpret_cast<const float4*>(Yp + (size_t)p * D + d);
+      s = fmaf(a.x, b.x, s);
+      s = fmaf(a.y, b.y, s);
+      s = fmaf(a.z, b.z, s);
+      s = fmaf(a.w, b.w, s);
+    }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) dtw[q] = s;
 }
 
 // dx[t] = sum over j of dXp[tok2pair[t, j]] (j ascending, dropped skipped)
-// + the shared pair's row; each output written by one thread.
+// + the shared pair's row; each output written by one thread, 4 at a time.
 __global__ __launch_bounds__(256) void bwd_dx_kernel(
     const float* __restrict__ dXp, const int32_t* __restrict__ tok2pair,
     const int32_t* __restrict__ offsets, int T, int k, int D, int n_shared,
     int E, float* __restrict__ dx) {
-  const size_t n = (size_t)T * D;
+  const size_t n = (size_t)T * (D / 4);
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
-    const size_t t = i / D;
-    const int d = (int)(i - t * D);
-    float s = 0.f;
+    const size_t t = i / (D / 4);
+    const int d = (int)(i - t * (D / 4)) * 4;
+    float4 s = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int p = tok2pair[t * k + j];
-      if (p >= 0) s += dXp[(size_t)p * D + d];
+      if (p >= 0) {
+        const float4 v = *reinterpret_cast<const float4*>(dXp + (size_t)p * D + d);
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      }
     }
-    if (n_shared) s += dXp[((size_t)offsets[E] + t) * D + d];
-    dx[i] = s;
+    if (n_shared) {
+      const float4 v = *reinterpret_cast<const float4*>(dXp + ((size_t)offsets[E] + t) * D + d);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    *reinterpret_cast<float4*>(dx + t * D + d) = s;
   }
 }
 
