@@ -80,12 +80,64 @@ __device__ __forceinline__ int dswz(int r, int c) {
   return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
 }
 
+// The 128 x 128 f32 C tile of an 8-wave block (waves w and w + 4 hold the
+// two k-halves of the same 64 x 64 quarter) through LDS: [128][128] f32,
+// 16-byte chunks XOR 8 on rows with bit 2 set (the two row halves of an
+// MFMA store land on other banks). The k-half kq = 1 stores its sums, kq = 0
+// adds its own in place, then all eight waves write whole rows with 16-byte
+// stores; rows at or past Me are not written. ct must hold 64 KB and be free.
+__device__ __forceinline__ void store_c_tile(float* ct, const floatx16 (&acc)[2][2],
+                                             int tid, int kq, int wm, int wn, int Me,
+                                             float* c, int ldc) {
+  const int lane = tid & 63;
+  auto cix = [](int m, int n) {
+    return m * 128 + (((n >> 2) ^ (((m >> 2) & 1) << 3)) << 2) + (n & 3);
+  };
+  if (kq == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          ct[cix(m, n)] = acc[i][j][r];
+        }
+      }
+  }
+  __syncthreads();
+  if (kq == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          ct[cix(m, n)] += acc[i][j][r];
+        }
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int q = tid + 512 * it;
+    const int m = q >> 5, ch = q & 31;
+    if (m < Me)
+      *reinterpret_cast<float4*>(c + (size_t)m * ldc + ch * 4) =
+          *reinterpret_cast<const float4*>(ct + cix(m, ch * 4));
+  }
+}
+
 template <class TT, int MODE, int NS>
 __global__ __launch_bounds__(512, NS == 2 ? 2 : 1) void bgemm_dma_kernel(BGemmArgs g) {
   using V8 = typename TT::V8;
   constexpr int kStage = 256 * 128;           // 128 A + 128 B rows
   constexpr int kDma = kStage / 1024 / 8;     // 4 loads per wave per stage
   __shared__ __attribute__((aligned(1024))) char smem[NS * kStage];
+  static_assert(NS * kStage >= 128 * 128 * 4, "the C tile is staged in the ring");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -201,34 +253,8 @@ __global__ __launch_bounds__(512, NS == 2 ? 2 : 1) void bgemm_dma_kernel(BGemmAr
   }
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();   // the ring is free
-  float* red = reinterpret_cast<float*>(smem) + wq * (64 * 64);
-  if (kq == 1) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
-  }
-  __syncthreads();
-  if (kq == 1) return;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < Me) cbase[(crow0 + m) * g.ldc + n] = acc[i][j][r];
-      }
-  }
+  store_c_tile(reinterpret_cast<float*>(smem), acc, tid, kq, wm, wn, Me,
+               cbase + crow0 * g.ldc + n0, g.ldc);
 }
 
 // Per-pair products whose weight is read as [K, N] (dH = dYp W_down, and
@@ -365,34 +391,8 @@ __global__ __launch_bounds__(512, 1) void bgemm_dma_ic_kernel(BGemmArgs g) {
   }
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();   // the ring is free
-  float* red = reinterpret_cast<float*>(smem) + wq * (64 * 64);
-  if (kq == 1) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
-  }
-  __syncthreads();
-  if (kq == 1) return;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < Me) g.c[(crow0 + m) * g.ldc + n] = acc[i][j][r];
-      }
-  }
+  store_c_tile(reinterpret_cast<float*>(smem), acc, tid, kq, wm, wn, Me,
+               g.c + crow0 * g.ldc + n0, g.ldc);
 }
 
 // (expert, first row) of every 64-row tile of the per-pair products, in
