@@ -62,6 +62,7 @@ struct BGemmArgs {
   const int32_t* n_tiles;   // mode 0: number of tiles (device)
   const int32_t* koff;      // mode 1 on pair-transposed operands: expert e's
                             // K columns start at koff[e] (a multiple of 8)
+  const int32_t* eord;      // mode 1: the experts, most K columns first
                             // and run to koff[e + 1] (zero padded)
   int n_exp;
 };
@@ -169,8 +170,11 @@ __global__ __launch_bounds__(512, NS == 2 ? 2 : 1) void bgemm_dma_kernel(BGemmAr
   } else {
     const int mt = g.M / 128, nt = g.N / 128;
     const int per = mt * nt;
-    e = blockIdx.x / per;
-    const int r = blockIdx.x - e * per;
+    // longest processing time first: the experts with the most pairs take
+    // the first blocks, so their long tiles do not run alone at the end
+    const int ei = blockIdx.x / per;
+    const int r = blockIdx.x - ei * per;
+    e = g.eord[ei];
     m0 = (r / nt) * 128;
     n0 = (r % nt) * 128;
     Me = 128;
@@ -403,9 +407,11 @@ __global__ __launch_bounds__(512, 1) void bgemm_dma_ic_kernel(BGemmArgs g) {
 __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
     const int32_t* __restrict__ offsets, int n_exp, int32_t* __restrict__ tiles,
     int32_t* __restrict__ n_tiles, int32_t* __restrict__ tiles128,
-    int32_t* __restrict__ n_tiles128, int32_t* __restrict__ koff) {
+    int32_t* __restrict__ n_tiles128, int32_t* __restrict__ koff,
+    int32_t* __restrict__ eord) {
   __shared__ int32_t start[kMaxExperts + 2];
   __shared__ int32_t start2[kMaxExperts + 2];
+  __shared__ int32_t kcol[kMaxExperts + 2];
   if (threadIdx.x == 0) {
     int acc = 0, acc2 = 0, col = 0;
     for (int e = 0; e < n_exp; ++e) {
@@ -415,7 +421,8 @@ __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
       const int ne = offsets[e + 1] - offsets[e];
       acc += (ne + kBT - 1) / kBT;
       acc2 += (ne + 127) / 128;
-      col += (ne + 63) & ~63;
+      kcol[e] = (ne + 63) & ~63;
+      col += kcol[e];
     }
     start[n_exp] = acc;
     start2[n_exp] = acc2;
@@ -424,6 +431,13 @@ __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
     *n_tiles128 = acc2;
   }
   __syncthreads();
+  // eord: the experts by K columns, descending, ties by index (a permutation)
+  for (int e = threadIdx.x; e < n_exp; e += blockDim.x) {
+    const int ke = kcol[e];
+    int rank = 0;
+    for (int f = 0; f < n_exp; ++f) rank += kcol[f] > ke || (kcol[f] == ke && f < e);
+    eord[rank] = e;
+  }
   for (int e = threadIdx.x; e < n_exp; e += blockDim.x) {
     const int nt = start[e + 1] - start[e];
     for (int i = 0; i < nt; ++i) {
@@ -651,7 +665,7 @@ size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t tiles = (size_t)((Pmax + kBT - 1) / kBT + n_exp + 1);
   const size_t Pp = (size_t)bwd_pcols(Pmax, n_exp);
-  return al(tiles * 8) * 2 + al(16) * 2 + al((n_exp + 1) * 4) + al(Pmax * D * 2) * 2 +
+  return al(tiles * 8) * 2 + al(16) * 2 + al((n_exp + 1) * 4) + al(n_exp * 4) + al(Pmax * D * 2) * 2 +
          al(Pmax * 2 * F * 4) + al(Pmax * F * 2) + al(Pmax * D * 4) +
          al(Pmax * F * 4) + al(Pmax * 2 * F * 2) + al(Pmax * D * 4) +
          al(Pp * D * 2) * 2 + al(Pp * 2 * F * 2) + al(Pp * F * 2);
@@ -672,6 +686,7 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   int32_t* tiles128 = reinterpret_cast<int32_t*>(b);     b += al(ntile_cap * 8);
   int32_t* n_tiles128 = reinterpret_cast<int32_t*>(b);   b += al(16);
   int32_t* koff = reinterpret_cast<int32_t*>(b);         b += al((n_exp + 1) * 4);
+  int32_t* eord = reinterpret_cast<int32_t*>(b);         b += al(n_exp * 4);
   S* Xp = reinterpret_cast<S*>(b);                       b += al(Pm * D * 2);
   S* dYp = reinterpret_cast<S*>(b);                      b += al(Pm * D * 2);
   float* GU = reinterpret_cast<float*>(b);               b += al(Pm * 2 * F * 4);
@@ -711,7 +726,7 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   auto weight_grad = [&](const BOp& A, const BOp& B, int M, int N, float* C) {
     BGemmArgs g{};
     g.a = A; g.b = B; g.mode = 1; g.M = M; g.N = N; g.c = C; g.ldc = N;
-    g.c_estride = (int64_t)M * N; g.offsets = a.offsets; g.koff = koff;
+    g.c_estride = (int64_t)M * N; g.offsets = a.offsets; g.koff = koff; g.eord = eord;
     g.n_exp = n_exp;
     hipLaunchKernelGGL((bgemm_dma_kernel<TT, 1, 2>),
                        dim3(n_exp * (M / 128) * (N / 128)), dim3(512), 0, s, g);
@@ -725,7 +740,7 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const int64_t wFD = (int64_t)F * D;
   if (stage == 0) {
     hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
-                       n_exp, tiles, n_tiles, tiles128, n_tiles128, koff);
+                       n_exp, tiles, n_tiles, tiles128, n_tiles128, koff, eord);
     hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
                        (const S*)a.x, a.dy, a.pair_token, a.pair_w, a.offsets,
                        n_exp, D, Xp, dYp);
