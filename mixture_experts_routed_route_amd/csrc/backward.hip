@@ -6,20 +6,22 @@
 //
 // Per kept pair p = (token t, expert e, weight w) in the plan's expert-sorted
 // order (a pair of the shared expert has w = 1):
-//   X_p  = x[t]                         dYp = w dy[t]        (compute dtype)
+//   X_p  = x[t]        dYu = dy[t], dYp = w dy[t]              (compute dtype)
 //   [G | U] = X_p [W_gate; W_up]^T      (f32, recomputed)
 //   H    = silu(min(G, c)) clamp(U)     (compute dtype, as the forward)
-//   Yp   = H W_down^T                   dw_j = dy[t] . Yp     (f32)
-//   dH   = dYp W_down                   (f32)
+//   dH'  = dYu W_down,  dH = w dH'      (f32)
+//   dw_j = dH' . H  (= dy[t] . H W_down^T, the expert's output, regrouped:
+//                    no product for the per-pair outputs is needed)
 //   [dG | dU] = SwiGLU backward         (compute dtype)
 //   dXp  = dG W_gate + dU W_up          dx[t] = sum over its pairs (fixed order)
 //   dW_gate[e] = sum_p dG_p x_p^T,  dW_up[e] likewise,  dW_down[e] = sum_p dYp H_p^T
-// The six products run on grouped MFMA kernels over 128 x 128 tiles whose
+// The five products run on grouped MFMA kernels over 128 x 128 tiles whose
 // operands stream HBM -> LDS by buffer_load ... lds through a ring of
 // 64-deep stages: the weight gradients, whose K is the pair index, on
 // pair-transposed copies of their operands; dH and dX, which read their
 // weights as [K, N], with those rows kept in LDS as in memory and each K
 // fragment assembled from 2-byte reads.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -497,13 +499,14 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
   }
 }
 
-// X_p = x[pair_token[p]] and dYp = pair_w[p] * dy[t], 8 values a thread.
+// X_p = x[pair_token[p]], dYu = dy[t] and dYp = pair_w[p] * dy[t], 8 values
+// a thread.
 template <class S>
 __global__ __launch_bounds__(256) void bwd_gather_kernel(
     const S* __restrict__ x, const float* __restrict__ dy,
     const int32_t* __restrict__ pair_token, const float* __restrict__ pair_w,
     const int32_t* __restrict__ offsets, int n_exp, int D, S* __restrict__ Xp,
-    S* __restrict__ dYp) {
+    S* __restrict__ dYu, S* __restrict__ dYp) {
   const int P = offsets[n_exp];
   const int upr = D / 8;
   for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < (size_t)P * upr;
@@ -519,6 +522,8 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
     S o[8] = {(S)(wv * d0.x), (S)(wv * d0.y), (S)(wv * d0.z), (S)(wv * d0.w),
               (S)(wv * d1.x), (S)(wv * d1.y), (S)(wv * d1.z), (S)(wv * d1.w)};
     __builtin_memcpy(dYp + p * D + c, o, 16);
+    S ou[8] = {(S)d0.x, (S)d0.y, (S)d0.z, (S)d0.w, (S)d1.x, (S)d1.y, (S)d1.z, (S)d1.w};
+    __builtin_memcpy(dYu + p * D + c, ou, 16);
   }
 }
 
@@ -560,56 +565,54 @@ __device__ __forceinline__ void swiglu_back1(float g, float u, float dh, float c
   du = dh * gc * s * mu;
 }
 
+// dH = pair_w[p] dH'_p; dG, dU from dH as above; and dtw_p = dH'_p . H_p,
+// H_p = SwiGLU(G, U) rounded to the compute dtype as the forward rounds it.
+// One wave per pair: lanes over F four values at a time in a fixed stride,
+// then a fixed butterfly for dtw_p.
 template <class S>
 __global__ __launch_bounds__(256) void bwd_swiglu_back_kernel(
-    const float* __restrict__ GU, const float* __restrict__ dH,
-    const int32_t* __restrict__ offsets, int n_exp, int F, float c,
-    S* __restrict__ dGU) {
-  const size_t n = (size_t)offsets[n_exp] * (F / 4);
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const size_t p = i / (F / 4);
-    const int f = (int)(i - p * (F / 4)) * 4;
-    const float4 g = *reinterpret_cast<const float4*>(GU + p * 2 * F + f);
-    const float4 u = *reinterpret_cast<const float4*>(GU + p * 2 * F + F + f);
-    const float4 d = *reinterpret_cast<const float4*>(dH + p * F + f);
-    float dg[4], du[4];
-    swiglu_back1(g.x, u.x, d.x, c, dg[0], du[0]);
-    swiglu_back1(g.y, u.y, d.y, c, dg[1], du[1]);
-    swiglu_back1(g.z, u.z, d.z, c, dg[2], du[2]);
-    swiglu_back1(g.w, u.w, d.w, c, dg[3], du[3]);
-    S og[4] = {(S)dg[0], (S)dg[1], (S)dg[2], (S)dg[3]};
-    S ou[4] = {(S)du[0], (S)du[1], (S)du[2], (S)du[3]};
-    __builtin_memcpy(dGU + p * 2 * F + f, og, 8);
-    __builtin_memcpy(dGU + p * 2 * F + F + f, ou, 8);
+    const float* __restrict__ GU, const float* __restrict__ dHu,
+    const float* __restrict__ pair_w, const int32_t* __restrict__ offsets,
+    int n_exp, int F, float c, S* __restrict__ dGU, float* __restrict__ dtwp) {
+  const int lane = threadIdx.x & 63;
+  const int P = offsets[n_exp];
+  for (int p = blockIdx.x * 4 + (threadIdx.x >> 6); p < P; p += gridDim.x * 4) {
+    const float w = pair_w[p];
+    const float* gr = GU + (size_t)p * 2 * F;
+    float acc = 0.f;
+    for (int f = lane * 4; f < F; f += 256) {
+      const float4 g = *reinterpret_cast<const float4*>(gr + f);
+      const float4 u = *reinterpret_cast<const float4*>(gr + F + f);
+      const float4 d = *reinterpret_cast<const float4*>(dHu + (size_t)p * F + f);
+      const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+      const float dv[4] = {d.x, d.y, d.z, d.w};
+      S og[4], ou[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(dv[q], (float)(S)swiglu(gv[q], uv[q], c), acc);
+        float dg, du;
+        swiglu_back1(gv[q], uv[q], w * dv[q], c, dg, du);
+        og[q] = (S)dg;
+        ou[q] = (S)du;
+      }
+      __builtin_memcpy(dGU + (size_t)p * 2 * F + f, og, 8);
+      __builtin_memcpy(dGU + (size_t)p * 2 * F + F + f, ou, 8);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) dtwp[p] = acc;
   }
 }
 
-// dtw[t, j] = dy[t] . Yp[tok2pair[t, j]] (0 for a dropped pair); one wave
-// per (t, j), lanes over D four values at a time in a fixed stride, then a
-// fixed butterfly.
+// dtw[t, j] = dtw_p of the token's j-th pair (0 for a dropped pair).
 __global__ __launch_bounds__(256) void bwd_dtw_kernel(
-    const float* __restrict__ dy, const float* __restrict__ Yp,
-    const int32_t* __restrict__ tok2pair, int T, int k, int D,
+    const float* __restrict__ dtwp, const int32_t* __restrict__ tok2pair, int64_t n,
     float* __restrict__ dtw) {
-  const int lane = threadIdx.x & 63;
-  const int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (q >= (int64_t)T * k) return;
-  const int t = (int)(q / k);
-  const int p = tok2pair[q];
-  float s = 0.f;
-  if (p >= 0)
-    for (int d = lane * 4; d < D; d += 256) {
-      const float4 a = *reinterpret_cast<const float4*>(dy + (size_t)t * D + d);
-      const float4 b = *reinterpret_cast<const float4*>(Yp + (size_t)p * D + d);
-      s = fmaf(a.x, b.x, s);
-      s = fmaf(a.y, b.y, s);
-      s = fmaf(a.z, b.z, s);
-      s = fmaf(a.w, b.w, s);
-    }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) dtw[q] = s;
+  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int p = tok2pair[q];
+    dtw[q] = p >= 0 ? dtwp[p] : 0.f;
+  }
 }
 
 // dx[t] = sum over j of dXp[tok2pair[t, j]] (j ascending, dropped skipped)
@@ -666,12 +669,12 @@ size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
   const size_t tiles = (size_t)((Pmax + kBT - 1) / kBT + n_exp + 1);
   const size_t Pp = (size_t)bwd_pcols(Pmax, n_exp);
   return al(tiles * 8) * 2 + al(16) * 2 + al((n_exp + 1) * 4) + al(n_exp * 4) + al(Pmax * D * 2) * 2 +
-         al(Pmax * 2 * F * 4) + al(Pmax * F * 2) + al(Pmax * D * 4) +
+         al(Pmax * 2 * F * 4) + al(Pmax * F * 2) + al(Pmax * D * 2) + al(Pmax * 4) +
          al(Pmax * F * 4) + al(Pmax * 2 * F * 2) + al(Pmax * D * 4) +
          al(Pp * D * 2) * 2 + al(Pp * 2 * F * 2) + al(Pp * F * 2);
 }
 
-// stage 0: gather, recompute [G | U], H and Yp; 1: dH, dG / dU, dXp, dx;
+// stage 0: gather, recompute [G | U] and H; 1: dH', dG / dU and dtw_p, dXp, dx;
 // 2: the weight gradients; 3: the routing-weight and logit gradients
 template <class TT>
 static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
@@ -691,7 +694,8 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   S* dYp = reinterpret_cast<S*>(b);                      b += al(Pm * D * 2);
   float* GU = reinterpret_cast<float*>(b);               b += al(Pm * 2 * F * 4);
   S* H = reinterpret_cast<S*>(b);                        b += al(Pm * F * 2);
-  float* Yp = reinterpret_cast<float*>(b);               b += al(Pm * D * 4);
+  S* dYu = reinterpret_cast<S*>(b);                      b += al(Pm * D * 2);
+  float* dtwp = reinterpret_cast<float*>(b);             b += al(Pm * 4);
   float* dH = reinterpret_cast<float*>(b);               b += al(Pm * F * 4);
   S* dGU = reinterpret_cast<S*>(b);                      b += al(Pm * 2 * F * 2);
   float* dXp = reinterpret_cast<float*>(b);              b += al(Pm * D * 4);
@@ -743,7 +747,7 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
                        n_exp, tiles, n_tiles, tiles128, n_tiles128, koff, eord);
     hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
                        (const S*)a.x, a.dy, a.pair_token, a.pair_w, a.offsets,
-                       n_exp, D, Xp, dYp);
+                       n_exp, D, Xp, dYu, dYp);
     // [G | U] = X_p [W_gate; W_up]^T
     per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wg, nullptr, D, 0, wFD},
              F, D, GU, 2 * F);
@@ -751,15 +755,12 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
              F, D, GU + F, 2 * F);
     hipLaunchKernelGGL((bwd_swiglu_kernel<S>), dim3(ew_grid), dim3(256), 0, s, GU,
                        a.offsets, n_exp, F, a.clamp, H);
-    // Yp = H W_down^T (for the routing-weight gradients)
-    per_pair(KCt{}, KCt{}, BOp{H, nullptr, F, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
-             D, F, Yp, D);
   } else if (stage == 1) {
-    // dH = dYp W_down
-    per_pair(KCt{}, ICt{}, BOp{dYp, nullptr, D, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
+    // dH' = dYu W_down (unscaled; the SwiGLU backward applies pair_w)
+    per_pair(KCt{}, ICt{}, BOp{dYu, nullptr, D, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
              F, D, dH, F);
     hipLaunchKernelGGL((bwd_swiglu_back_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
-                       GU, dH, a.offsets, n_exp, F, a.clamp, dGU);
+                       GU, dH, a.pair_w, a.offsets, n_exp, F, a.clamp, dGU, dtwp);
     // dXp = [dG | dU] [W_gate; W_up]
     per_pair(KCt{}, ICt{}, BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{a.wg, a.wu, D, F, wFD},
              D, 2 * F, dXp, D);
@@ -782,8 +783,8 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
     float* dtw = a.dtw ? a.dtw : a.dtw_scratch;
     const int64_t q = (int64_t)a.T * a.k;
     if (q > 0)
-      hipLaunchKernelGGL(bwd_dtw_kernel, dim3((unsigned)((q + 3) / 4)), dim3(256), 0,
-                         s, a.dy, Yp, a.tok2pair, a.T, a.k, D, dtw);
+      hipLaunchKernelGGL(bwd_dtw_kernel, dim3((unsigned)std::min<int64_t>((q + 255) / 256, ew_grid)),
+                         dim3(256), 0, s, dtwp, a.tok2pair, q, dtw);
     if (a.dlogits && a.T > 0)
       hipLaunchKernelGGL(bwd_dlogits_kernel, dim3(a.T), dim3(256), 0, s, a.ids,
                          a.topk_w, dtw, a.T, a.E, a.k, a.dlogits);

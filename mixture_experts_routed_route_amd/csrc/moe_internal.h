@@ -202,9 +202,9 @@ struct BwdArgs {
   void* ws;                     // bwd_workspace_bytes
 };
 size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F);
-// stage 0: recompute (gather, [G | U], H, Yp); 1: data gradients (dH,
-// dG / dU, dXp, dx); 2: weight gradients; 3: routing-weight and logit
-// gradients
+// stage 0: recompute (gather, [G | U], H); 1: data gradients (dH', dG / dU
+// with the per-pair routing-weight dots, dXp, dx); 2: weight gradients; 3:
+// routing-weight and logit gradients
 hipError_t launch_backward(const BwdArgs& a, int stage, hipStream_t s);
 
 // ---- router (router.hip) ---------------------------------------------------
