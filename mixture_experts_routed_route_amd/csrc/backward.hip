@@ -6,7 +6,8 @@
 //
 // Per kept pair p = (token t, expert e, weight w) in the plan's expert-sorted
 // order (a pair of the shared expert has w = 1):
-//   X_p  = x[t]        dYu = dy[t], dYp = w dy[t]              (compute dtype)
+//   X_p  = x[t]        dYu = dy[t], dYp = w dy[t]   (compute dtype; dYp only
+//                                                     as its transposed copy)
 //   [G | U] = X_p [W_gate; W_up]^T      (f32, recomputed)
 //   H    = silu(min(G, c)) clamp(U)     (compute dtype, as the forward)
 //   dH'  = dYu W_down,  dH = w dH'      (f32)
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(512, NS == 2 ? 2 : 1) void bgemm_dma_kernel(BGemmAr
                cbase + crow0 * g.ldc + n0, g.ldc);
 }
 
-// Per-pair products whose weight is read as [K, N] (dH = dYp W_down, and
+// Per-pair products whose weight is read as [K, N] (dH' = dYu W_down, and
 // dX = [dG | dU] [W_gate; W_up], whose K runs through both weights): the
 // same 128 x 128 tiles and ring as above, but a stage's 64 weight rows land
 // in LDS as they are in memory (64 rows of 128 N values, 256 bytes; the
@@ -462,7 +463,8 @@ template <class S>
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(
     const S* __restrict__ in, int C, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    const int32_t* __restrict__ koff, int ld_out, S* __restrict__ out) {
+    const int32_t* __restrict__ koff, int ld_out, const float* __restrict__ rw,
+    S* __restrict__ out) {
   __shared__ S t[64][65];
   const int nc = C / 64;
   const int ti = blockIdx.x / nc;
@@ -479,6 +481,11 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
     if (r < Me) {
       const uint4 u = *reinterpret_cast<const uint4*>(in + (size_t)(off + m0 + r) * C + c0 + ch * 8);
       __builtin_memcpy(v, &u, 16);
+      if (rw) {
+        const float w = rw[off + m0 + r];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (S)(w * (float)v[j]);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = (S)0.f;
@@ -499,14 +506,12 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
   }
 }
 
-// X_p = x[pair_token[p]], dYu = dy[t] and dYp = pair_w[p] * dy[t], 8 values
-// a thread.
+// X_p = x[pair_token[p]] and dYu = dy[t], 8 values a thread.
 template <class S>
 __global__ __launch_bounds__(256) void bwd_gather_kernel(
     const S* __restrict__ x, const float* __restrict__ dy,
-    const int32_t* __restrict__ pair_token, const float* __restrict__ pair_w,
-    const int32_t* __restrict__ offsets, int n_exp, int D, S* __restrict__ Xp,
-    S* __restrict__ dYu, S* __restrict__ dYp) {
+    const int32_t* __restrict__ pair_token, const int32_t* __restrict__ offsets,
+    int n_exp, int D, S* __restrict__ Xp, S* __restrict__ dYu) {
   const int P = offsets[n_exp];
   const int upr = D / 8;
   for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < (size_t)P * upr;
@@ -514,39 +519,16 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
     const size_t p = u / upr;
     const int c = (int)(u - p * upr) * 8;
     const int t = pair_token[p];
-    const float wv = pair_w[p];
     *reinterpret_cast<uint4*>(Xp + p * D + c) =
         *reinterpret_cast<const uint4*>(x + (size_t)t * D + c);
     const float4 d0 = *reinterpret_cast<const float4*>(dy + (size_t)t * D + c);
     const float4 d1 = *reinterpret_cast<const float4*>(dy + (size_t)t * D + c + 4);
-    S o[8] = {(S)(wv * d0.x), (S)(wv * d0.y), (S)(wv * d0.z), (S)(wv * d0.w),
-              (S)(wv * d1.x), (S)(wv * d1.y), (S)(wv * d1.z), (S)(wv * d1.w)};
-    __builtin_memcpy(dYp + p * D + c, o, 16);
     S ou[8] = {(S)d0.x, (S)d0.y, (S)d0.z, (S)d0.w, (S)d1.x, (S)d1.y, (S)d1.z, (S)d1.w};
     __builtin_memcpy(dYu + p * D + c, ou, 16);
   }
 }
 
 __device__ __forceinline__ float clamp_hi(float v, float c) { return c > 0.f ? fminf(v, c) : v; }
-
-// H = silu(min(G, c)) * clamp(U, -c, c), rounded to the compute dtype
-// (the forward's SwiGLU: hardware 2^x and reciprocal); 4 features a thread.
-template <class S>
-__global__ __launch_bounds__(256) void bwd_swiglu_kernel(
-    const float* __restrict__ GU, const int32_t* __restrict__ offsets,
-    int n_exp, int F, float c, S* __restrict__ H) {
-  const size_t n = (size_t)offsets[n_exp] * (F / 4);
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const size_t p = i / (F / 4);
-    const int f = (int)(i - p * (F / 4)) * 4;
-    const float4 g = *reinterpret_cast<const float4*>(GU + p * 2 * F + f);
-    const float4 u = *reinterpret_cast<const float4*>(GU + p * 2 * F + F + f);
-    S o[4] = {(S)swiglu(g.x, u.x, c), (S)swiglu(g.y, u.y, c), (S)swiglu(g.z, u.z, c),
-              (S)swiglu(g.w, u.w, c)};
-    __builtin_memcpy(H + p * F + f, o, 8);
-  }
-}
 
 // dG = dH * clamp(U) * silu'(min(G, c)) * [G <= c];
 // dU = dH * silu(min(G, c)) * [-c <= U <= c]; silu'(z) = s (1 + z (1 - s)),
@@ -565,15 +547,17 @@ __device__ __forceinline__ void swiglu_back1(float g, float u, float dh, float c
   du = dh * gc * s * mu;
 }
 
-// dH = pair_w[p] dH'_p; dG, dU from dH as above; and dtw_p = dH'_p . H_p,
-// H_p = SwiGLU(G, U) rounded to the compute dtype as the forward rounds it.
+// dH = pair_w[p] dH'_p; dG, dU from dH as above; H_p = SwiGLU(G, U) rounded
+// to the compute dtype as the forward rounds it (silu with the hardware's
+// 2^x and reciprocal); and dtw_p = dH'_p . H_p.
 // One wave per pair: lanes over F four values at a time in a fixed stride,
 // then a fixed butterfly for dtw_p.
 template <class S>
 __global__ __launch_bounds__(256) void bwd_swiglu_back_kernel(
     const float* __restrict__ GU, const float* __restrict__ dHu,
     const float* __restrict__ pair_w, const int32_t* __restrict__ offsets,
-    int n_exp, int F, float c, S* __restrict__ dGU, float* __restrict__ dtwp) {
+    int n_exp, int F, float c, S* __restrict__ dGU, S* __restrict__ H,
+    float* __restrict__ dtwp) {
   const int lane = threadIdx.x & 63;
   const int P = offsets[n_exp];
   for (int p = blockIdx.x * 4 + (threadIdx.x >> 6); p < P; p += gridDim.x * 4) {
@@ -586,10 +570,11 @@ __global__ __launch_bounds__(256) void bwd_swiglu_back_kernel(
       const float4 d = *reinterpret_cast<const float4*>(dHu + (size_t)p * F + f);
       const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
       const float dv[4] = {d.x, d.y, d.z, d.w};
-      S og[4], ou[4];
+      S og[4], ou[4], oh[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc = fmaf(dv[q], (float)(S)swiglu(gv[q], uv[q], c), acc);
+        oh[q] = (S)swiglu(gv[q], uv[q], c);
+        acc = fmaf(dv[q], (float)oh[q], acc);
         float dg, du;
         swiglu_back1(gv[q], uv[q], w * dv[q], c, dg, du);
         og[q] = (S)dg;
@@ -597,6 +582,7 @@ __global__ __launch_bounds__(256) void bwd_swiglu_back_kernel(
       }
       __builtin_memcpy(dGU + (size_t)p * 2 * F + f, og, 8);
       __builtin_memcpy(dGU + (size_t)p * 2 * F + F + f, ou, 8);
+      __builtin_memcpy(H + (size_t)p * F + f, oh, 8);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
@@ -668,7 +654,7 @@ size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t tiles = (size_t)((Pmax + kBT - 1) / kBT + n_exp + 1);
   const size_t Pp = (size_t)bwd_pcols(Pmax, n_exp);
-  return al(tiles * 8) * 2 + al(16) * 2 + al((n_exp + 1) * 4) + al(n_exp * 4) + al(Pmax * D * 2) * 2 +
+  return al(tiles * 8) * 2 + al(16) * 2 + al((n_exp + 1) * 4) + al(n_exp * 4) + al(Pmax * D * 2) +
          al(Pmax * 2 * F * 4) + al(Pmax * F * 2) + al(Pmax * D * 2) + al(Pmax * 4) +
          al(Pmax * F * 4) + al(Pmax * 2 * F * 2) + al(Pmax * D * 4) +
          al(Pp * D * 2) * 2 + al(Pp * 2 * F * 2) + al(Pp * F * 2);
@@ -691,7 +677,6 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   int32_t* koff = reinterpret_cast<int32_t*>(b);         b += al((n_exp + 1) * 4);
   int32_t* eord = reinterpret_cast<int32_t*>(b);         b += al(n_exp * 4);
   S* Xp = reinterpret_cast<S*>(b);                       b += al(Pm * D * 2);
-  S* dYp = reinterpret_cast<S*>(b);                      b += al(Pm * D * 2);
   float* GU = reinterpret_cast<float*>(b);               b += al(Pm * 2 * F * 4);
   S* H = reinterpret_cast<S*>(b);                        b += al(Pm * F * 2);
   S* dYu = reinterpret_cast<S*>(b);                      b += al(Pm * D * 2);
@@ -735,9 +720,9 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
     hipLaunchKernelGGL((bgemm_dma_kernel<TT, 1, 2>),
                        dim3(n_exp * (M / 128) * (N / 128)), dim3(512), 0, s, g);
   };
-  auto transpose = [&](const S* in, int C, S* outp) {
+  auto transpose = [&](const S* in, int C, S* outp, const float* rw) {
     hipLaunchKernelGGL((bwd_transpose_kernel<S>), dim3(ub * (C / 64)), dim3(256), 0, s,
-                       in, C, a.offsets, tiles, n_tiles, koff, (int)Pp, outp);
+                       in, C, a.offsets, tiles, n_tiles, koff, (int)Pp, rw, outp);
   };
   using KCt = std::true_type;
   using ICt = std::false_type;
@@ -746,21 +731,19 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
     hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
                        n_exp, tiles, n_tiles, tiles128, n_tiles128, koff, eord);
     hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
-                       (const S*)a.x, a.dy, a.pair_token, a.pair_w, a.offsets,
-                       n_exp, D, Xp, dYu, dYp);
+                       (const S*)a.x, a.dy, a.pair_token, a.offsets,
+                       n_exp, D, Xp, dYu);
     // [G | U] = X_p [W_gate; W_up]^T
     per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wg, nullptr, D, 0, wFD},
              F, D, GU, 2 * F);
     per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wu, nullptr, D, 0, wFD},
              F, D, GU + F, 2 * F);
-    hipLaunchKernelGGL((bwd_swiglu_kernel<S>), dim3(ew_grid), dim3(256), 0, s, GU,
-                       a.offsets, n_exp, F, a.clamp, H);
   } else if (stage == 1) {
     // dH' = dYu W_down (unscaled; the SwiGLU backward applies pair_w)
     per_pair(KCt{}, ICt{}, BOp{dYu, nullptr, D, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
              F, D, dH, F);
     hipLaunchKernelGGL((bwd_swiglu_back_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
-                       GU, dH, a.pair_w, a.offsets, n_exp, F, a.clamp, dGU, dtwp);
+                       GU, dH, a.pair_w, a.offsets, n_exp, F, a.clamp, dGU, H, dtwp);
     // dXp = [dG | dU] [W_gate; W_up]
     per_pair(KCt{}, ICt{}, BOp{dGU, nullptr, 2 * F, 0, 0}, BOp{a.wg, a.wu, D, F, wFD},
              D, 2 * F, dXp, D);
@@ -769,10 +752,10 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
                          a.tok2pair, a.offsets, a.T, a.k, D, a.n_shared, a.E, a.dx);
   } else if (stage == 2) {
     // weight gradients (every expert, zero pairs give zeros)
-    transpose(Xp, D, Xt);
-    transpose(dYp, D, dYt);
-    transpose(dGU, 2 * F, dGUt);
-    transpose(H, F, Ht);
+    transpose(Xp, D, Xt, nullptr);
+    transpose(dYu, D, dYt, a.pair_w);   // dYp = pair_w dy[t], transposed
+    transpose(dGU, 2 * F, dGUt, nullptr);
+    transpose(H, F, Ht, nullptr);
     weight_grad(BOp{dGUt, nullptr, (int)Pp, 0, 0}, BOp{Xt, nullptr, (int)Pp, 0, 0},
                 F, D, a.dwg);
     weight_grad(BOp{dGUt + (size_t)F * Pp, nullptr, (int)Pp, 0, 0},
