@@ -405,9 +405,10 @@ def bench_backward(args, dev, torch, moe, W):
     """moe_backward on a 16-bit workload's plan (default: the prefill layer,
     4096 tokens, d_model 2048, d_ff 768, 128 experts, top-8, bf16): dx, the
     three weight gradients, the routing-weight and logit gradients of
-    sum(dy * y) for a seeded dy ~ N(0, 1). Flops per kept pair: 18 D F
-    (the recomputed gate/up and down products, dH, dX, and the three weight
-    gradients, 2 D F each, gate/up and dX twice)."""
+    sum(dy * y) for a seeded dy ~ N(0, 1). Flops per kept pair: 16 D F, the
+    products the backward runs (the recomputed gate/up products, dH, dX over
+    both weights and the three weight gradients, 2 D F each, gate/up and dX
+    twice); the routing-weight gradients are dots, not a product."""
     import numpy as np
 
     cfg = args.config if args.config != 4 else 3
@@ -446,7 +447,7 @@ def bench_backward(args, dev, torch, moe, W):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     counts = moe.moe_plan_get_views(plan)["counts"].cpu().numpy().astype(np.int64)
     P = int(counts.sum())
-    flops = 18.0 * D * F * P
+    flops = 16.0 * D * F * P
     roofline = None
     if not args.no_phase_events:
         phase_ms, calls = moe.moe_phase_times(reset=True)
@@ -479,7 +480,7 @@ def bench_backward(args, dev, torch, moe, W):
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_backward(wl, dy.cpu(), args.cpu_seconds)
     line = {
-        "metric": "backward TFLOP/s per MoE layer (18*D*F per kept pair)",
+        "metric": "backward TFLOP/s per MoE layer (16*D*F per kept pair)",
         "value": round(flops / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
