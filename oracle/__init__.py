@@ -10,7 +10,7 @@ into ``liboracle.so`` next to it. ``brute.py`` holds independent numpy
 restatements for tiny inputs that pin it. Parity status of every function is
 listed below; all are pinned by tests in ``tests/test_oracle_*.py``:
 
-  route / limit / plan / expert / layer / decode   pinned (brute force,
+  route / limit / plan / expert / pairs / layer / decode   pinned (brute force,
   closed forms, invariants, numpy library routines).
   backward / dlogits   pinned (torch float64 autograd of the dense masked
   layer; central differences of the oracle's own route + layer).
@@ -68,6 +68,8 @@ def lib():
         L.orc_layer.argtypes = [i64, i64, i64, i32, i32, i32, vp, i32, vp, vp,
                                 vp, vp, vp, vp, i32, dbl, vp, vp, vp, i64, vp,
                                 vp]
+        L.orc_pairs.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32, vp,
+                                vp, vp, vp, vp, vp, i32, dbl, vp]
         L.orc_decode.argtypes = [vp, vp, i32, i64, i64, i64, vp]
         L.orc_decode_f16.argtypes = [vp, i64, vp]
         L.orc_router_logits.argtypes = [i64, i64, i32, vp, i32, vp, vp]
@@ -199,6 +201,30 @@ def expert(x_row, e: int, w_gate, w_up, w_down, x_dtype: str, w_dtype: str,
     if rc != 0:
         raise ValueError(f"orc_expert failed ({rc})")
     return g, u, h, yp
+
+
+def pairs(x, w_gate, w_up, w_down, tokens, experts, *, x_dtype: str,
+          w_dtype: str, c: float) -> np.ndarray:
+    """Unweighted expert outputs yp [n, D] (float64) of the (tokens[i],
+    experts[i]) pairs: FFN_e(x[t]) before the routing weight."""
+    xa = _np(x)
+    T, D = xa.shape
+    wg, wgs = _weight(w_gate)
+    wu, wus = _weight(w_up)
+    wd, wds = _weight(w_down)
+    F = wg.shape[1]
+    n_exp = wg.shape[0]
+    tl = np.ascontiguousarray(tokens, np.int64)
+    el = np.ascontiguousarray(experts, np.int32)
+    if tl.shape != el.shape or tl.ndim != 1:
+        raise ValueError("tokens and experts must be 1-D and of one length")
+    yp = np.zeros((tl.shape[0], D))
+    rc = lib().orc_pairs(tl.shape[0], T, D, F, n_exp, _p(tl), _p(el), _p(xa),
+                         DT[x_dtype], _p(wg), _p(wgs), _p(wu), _p(wus), _p(wd),
+                         _p(wds), DT[w_dtype], float(c), _p(yp))
+    if rc != 0:
+        raise ValueError(f"orc_pairs failed ({rc})")
+    return yp
 
 
 def layer(x, w_gate, w_up, w_down, ids, w, keep, *, E: int, n_shared: int,

@@ -26,7 +26,7 @@
  *   backward gradients of the layer (x, the three expert weights, the
  *            routing weights and, through them, the logits): the same
  *            gradients on every expert slot whatever the dispatch (mini-AGI
- *            PR #4, tests/test_dispatch.py).
+ *            PR #3, tests/test_dispatch.py).
  *   router   logits = x Wr^T, the linear map from d_model to the experts
  *            whose output `requested(scores)` ranks, and the statistics that
  *            function keeps beside the routing: the top-k mass before
@@ -337,6 +337,38 @@ int orc_expert(int64_t D, int64_t F, int64_t e, const void *xrow, int x_dtype,
     return 0;
 }
 
+/*
+ * The unweighted expert output of n (token, expert) pairs, yp[i] =
+ * FFN_{experts[i]}(x[tokens[i]]): the rows the combine weighs and sums
+ * (mini-AGI PR #4, minagi/pool.py, `experts()` then the weighted gather
+ * back to tokens). One pair per OpenMP iteration.
+ */
+int orc_pairs(int64_t n, int64_t T, int64_t D, int64_t F, int n_exp,
+              const int64_t *tokens, const int32_t *experts, const void *x,
+              int x_dtype, const void *wg, const void *wg_s, const void *wu,
+              const void *wu_s, const void *wd, const void *wd_s,
+              int w_dtype, double c, double *yp)
+{
+    if (x_dtype < ORC_F32 || x_dtype > ORC_F16 || w_dtype < ORC_F32 ||
+        w_dtype > ORC_Q4A64 ||
+        (is_q4(w_dtype) && (D % q4_group(w_dtype) || F % q4_group(w_dtype))))
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= T || experts[i] < 0 ||
+            experts[i] >= n_exp)
+            return -2;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        double *xt = malloc((size_t)D * sizeof *xt);
+        for (int64_t d = 0; d < D; ++d)
+            xt[d] = dense_value(x, x_dtype, (size_t)(tokens[i] * D + d));
+        expert_ffn(D, F, experts[i], xt, wg, wg_s, wu, wu_s, wd, wd_s,
+                   w_dtype, c, NULL, NULL, NULL, yp + i * D);
+        free(xt);
+    }
+    return 0;
+}
+
 /* ---- the layer --------------------------------------------------------- */
 
 /*
@@ -450,8 +482,9 @@ static void pair_backward(int64_t D, int64_t F, int64_t e, const double *x,
  *   dtw  [T, k]            gradient of each routing weight w_j: dy[t] .
  *        FFN(x[t]) for a kept pair, 0 for a dropped one (NULL: skipped).
  * Gradients of the expert weights are the sums over the expert's kept pairs
- * -- "the same gradients on every slot" is what mini-AGI PR #4's
- * tests/test_dispatch.py asks of any dispatch. Any pointer may be NULL.
+ * -- mini-AGI PR #3's tests/test_dispatch.py asks any dispatch to give each
+ * expert slot the gradient running every expert gives. Any pointer may be
+ * NULL.
  */
 int orc_backward(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
                  const void *x, int x_dtype, const void *wg, const void *wg_s,

@@ -372,6 +372,46 @@ def test_q4_layer_matches_dense_bruteforce():
     np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("dt,wdt", [(W.BF16, W.BF16), (W.F16, W.Q4B32),
+                                    (W.F16, W.Q4A64)])
+def test_pair_outputs_match_dense_experts(dt, wdt):
+    # oracle.pairs on an arbitrary pair list (repeated tokens, every expert,
+    # the shared slot, out of order) against numpy matmuls of independently
+    # decoded weights, one expert at a time
+    wl = W.make_layer(9, 128, 128, 4, 2, dt, w_dtype=wdt, seed=18, w_std=0.2,
+                      n_shared=1)
+    toks = np.array([8, 0, 3, 3, 5, 1, 8, 2])
+    exps = np.array([4, 2, 0, 1, 3, 4, 0, 2])
+    got = oracle.pairs(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], toks,
+                       exps, x_dtype=dt, w_dtype=wdt, c=7.0)
+    if wdt == W.Q4B32:
+        Wg, Wu, Wd = (_numpy_q4_decode(*wl[n]) for n in ("w_gate", "w_up",
+                                                         "w_down"))
+    elif wdt == W.Q4A64:
+        Wg, Wu, Wd = (_numpy_affine_decode(*wl[n], 64)
+                      for n in ("w_gate", "w_up", "w_down"))
+    else:
+        Wg, Wu, Wd = (_f64(wl[n]) for n in ("w_gate", "w_up", "w_down"))
+    X = _f64(wl["x"])
+    for i, (t, e) in enumerate(zip(toks, exps)):
+        ref = brute.expert_dense(X[t:t + 1], Wg[e], Wu[e], Wd[e], 7.0)[0]
+        np.testing.assert_allclose(got[i], ref, rtol=1e-11, atol=1e-13)
+    # the layer is the weighted sum of the kept pairs' outputs
+    ids, w, pl, y = _layer(wl, 0.0)
+    T, k = ids.shape
+    tt = np.repeat(np.arange(T), k)
+    yp = oracle.pairs(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], tt,
+                      ids.reshape(-1), x_dtype=dt, w_dtype=wdt, c=7.0)
+    sh = oracle.pairs(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"],
+                      np.arange(T), np.full(T, 4), x_dtype=dt, w_dtype=wdt,
+                      c=7.0)
+    mix = (yp.reshape(T, k, -1) * w[:, :, None]).sum(1) + sh
+    np.testing.assert_allclose(y, mix, rtol=1e-11, atol=1e-13)
+    with pytest.raises(ValueError):
+        oracle.pairs(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"], [9],
+                     [0], x_dtype=dt, w_dtype=wdt, c=7.0)
+
+
 @pytest.mark.parametrize("fmt,G", [("q4a32", 32), ("q4a64", 64)])
 def test_q4_affine_decode_ramp_groups_and_rounding(fmt, G):
     # one row of 128 K values: nibble kk % 16 (low nibble = even index);
