@@ -285,15 +285,18 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /*
  * g = Wg[e] x, u = Wu[e] x, h = silu(min(g, c)) * clamp(u, -c, c) (no clamp
- * when c <= 0), yp = Wd[e] h. Any of g, u, h may be NULL.
+ * when c <= 0), yp = Wd[e] h. Any of g, u, h, yp may be NULL. par != 0
+ * spreads the independent rows over OpenMP threads (for a caller outside a
+ * parallel region); each value is computed the same way either way.
  */
 static void expert_ffn(int64_t D, int64_t F, int64_t e, const double *x,
                        const void *wg, const void *wg_s, const void *wu,
                        const void *wu_s, const void *wd, const void *wd_s,
                        int w_dtype, double c, double *g, double *u, double *h,
-                       double *yp)
+                       double *yp, int par)
 {
     double *hh = malloc((size_t)F * sizeof *hh);
+#pragma omp parallel for schedule(static) if (par)
     for (int64_t f = 0; f < F; ++f) {
         double gs = 0.0, us = 0.0;
         for (int64_t d = 0; d < D; ++d) {
@@ -310,7 +313,8 @@ static void expert_ffn(int64_t D, int64_t F, int64_t e, const double *x,
         if (u) u[f] = us;
         if (h) h[f] = hh[f];
     }
-    for (int64_t d = 0; d < D; ++d) {
+#pragma omp parallel for schedule(static) if (par && yp)
+    for (int64_t d = 0; d < (yp ? D : 0); ++d) {
         double s = 0.0;
         for (int64_t f = 0; f < F; ++f)
             s += weight_value(wd, wd_s, w_dtype, e, D, F, d, f) * hh[f];
@@ -332,7 +336,7 @@ int orc_expert(int64_t D, int64_t F, int64_t e, const void *xrow, int x_dtype,
     for (int64_t d = 0; d < D; ++d)
         x[d] = dense_value(xrow, x_dtype, (size_t)d);
     expert_ffn(D, F, e, x, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype, c, g, u, h,
-               yp);
+               yp, 0);
     free(x);
     return 0;
 }
@@ -363,7 +367,7 @@ int orc_pairs(int64_t n, int64_t T, int64_t D, int64_t F, int n_exp,
         for (int64_t d = 0; d < D; ++d)
             xt[d] = dense_value(x, x_dtype, (size_t)(tokens[i] * D + d));
         expert_ffn(D, F, experts[i], xt, wg, wg_s, wu, wu_s, wd, wd_s,
-                   w_dtype, c, NULL, NULL, NULL, yp + i * D);
+                   w_dtype, c, NULL, NULL, NULL, yp + i * D, 0);
         free(xt);
     }
     return 0;
@@ -403,13 +407,13 @@ int orc_layer(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
             if (!keep[t * k + j])
                 continue;
             expert_ffn(D, F, ids[t * k + j], xt, wg, wg_s, wu, wu_s, wd, wd_s,
-                       w_dtype, c, NULL, NULL, NULL, yp);
+                       w_dtype, c, NULL, NULL, NULL, yp, 0);
             for (int64_t d = 0; d < D; ++d)
                 yt[d] += w[t * k + j] * yp[d];
         }
         if (n_shared) {
             expert_ffn(D, F, E, xt, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype, c,
-                       NULL, NULL, NULL, yp);
+                       NULL, NULL, NULL, yp, 0);
             for (int64_t d = 0; d < D; ++d)
                 yt[d] += yp[d];
         }
@@ -430,19 +434,22 @@ int orc_layer(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
  * the clamp of Strata PR #4366, "Approach"). The clamps pass the gradient
  * where the value is not clamped, boundaries included (g <= c, -c <= u <=
  * c), like a clamp's subgradient in autograd. Accumulates into dx (D),
- * dwg / dwu (F x D), dwd (D x F) when they are not NULL.
+ * dwg / dwu (F x D), dwd (D x F) when they are not NULL. par != 0 (only
+ * with dx NULL: its sum runs over f) spreads the rows f over OpenMP
+ * threads, each row computed the same way.
  */
 static void pair_backward(int64_t D, int64_t F, int64_t e, const double *x,
                           const void *wg, const void *wg_s, const void *wu,
                           const void *wu_s, const void *wd, const void *wd_s,
                           int w_dtype, double c, const double *dyp, double *dx,
-                          double *dwg, double *dwu, double *dwd)
+                          double *dwg, double *dwu, double *dwd, int par)
 {
     double *g = malloc((size_t)F * sizeof *g);
     double *u = malloc((size_t)F * sizeof *u);
     double *h = malloc((size_t)F * sizeof *h);
-    double *yp = malloc((size_t)D * sizeof *yp);
-    expert_ffn(D, F, e, x, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype, c, g, u, h, yp);
+    expert_ffn(D, F, e, x, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype, c, g, u, h,
+               NULL, par);
+#pragma omp parallel for schedule(static) if (par && !dx)
     for (int64_t f = 0; f < F; ++f) {
         double dh = 0.0;
         for (int64_t d = 0; d < D; ++d)
@@ -471,7 +478,7 @@ static void pair_backward(int64_t D, int64_t F, int64_t e, const double *x,
             for (int64_t d = 0; d < D; ++d)
                 dwd[d * F + f] += dyp[d] * h[f];
     }
-    free(g); free(u); free(h); free(yp);
+    free(g); free(u); free(h);
 }
 
 /*
@@ -530,13 +537,15 @@ int orc_backward(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
                 for (int64_t d = 0; d < D; ++d)
                     dyp[d] = wt * dy[t * D + d];
                 pair_backward(D, F, e, xt, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype,
-                              c, dyp, dxt, NULL, NULL, NULL);
+                              c, dyp, dxt, NULL, NULL, NULL, 0);
             }
             free(xt); free(dyp);
         }
     }
     if (dwg || dwu || dwd) {
-#pragma omp parallel for schedule(dynamic, 1)
+        /* one expert, one kept pair at a time, in token order; the rows f of
+         * a pair's gradient are spread over the threads (an expert may hold
+         * most of the pairs) */
         for (int i = 0; i < n_exp; ++i) {
             int64_t e = exp_list ? exp_list[i] : i;
             double *xt = malloc((size_t)D * sizeof *xt);
@@ -567,7 +576,7 @@ int orc_backward(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
                     dyp[d] = wt * dy[t * D + d];
                 }
                 pair_backward(D, F, e, xt, wg, wg_s, wu, wu_s, wd, wd_s, w_dtype,
-                              c, dyp, NULL, g_, u_, d_);
+                              c, dyp, NULL, g_, u_, d_, 1);
             }
             free(xt); free(dyp);
         }
@@ -583,7 +592,7 @@ int orc_backward(int64_t T, int64_t D, int64_t F, int E, int k, int n_shared,
                 double s = 0.0;
                 if (keep[t * k + j]) {
                     expert_ffn(D, F, ids[t * k + j], xt, wg, wg_s, wu, wu_s, wd,
-                               wd_s, w_dtype, c, NULL, NULL, NULL, yp);
+                               wd_s, w_dtype, c, NULL, NULL, NULL, yp, 0);
                     for (int64_t d = 0; d < D; ++d)
                         s += dy[t * D + d] * yp[d];
                 }
