@@ -43,8 +43,10 @@ CSRC = os.path.join(ROOT, "mixture_experts_routed_route_amd", "csrc")
 # source file of each phase's kernel: a committed counter summary applies to
 # the phase only while this file (and the shared header) is unchanged
 KERNEL_SRC = {"gateup_full": "gemm_full.hip", "down_full": "gemm_full.hip",
-              "gateup_splitk": "forward_kernels.hip",
-              "down_splitk": "forward_kernels.hip",
+              "gateup_thin16": "forward_kernels.hip",
+              "down_thin16": "forward_kernels.hip",
+              "gateup_thin64": "gemm_wide.hip",
+              "down_thin64": "gemm_wide.hip",
               "dequant_once": "forward_kernels.hip",
               "combine": "forward_kernels.hip",
               "classify": "forward_kernels.hip",
@@ -211,23 +213,20 @@ def main():
     flops = W.flops_per_pair(D, F) * kept_pairs
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     pairs_s = kept_pairs / (ms_per_step * 1e-3)
-    # the weights of every expert holding a kept pair are read at least once
     touched = int((counts > 0).sum())
-    wbytes_step = touched * W.weight_bytes_per_expert(D, F, wl["w_dtype"])
-    weight_stream = {"touched_experts": touched,
-                     "bytes_per_step": int(wbytes_step),
-                     "GB_per_s": round(wbytes_step / (ms_per_step * 1e-3) / 1e9, 1),
-                     "frac_of_hbm_peak": round(wbytes_step / (ms_per_step * 1e-3)
-                                               / 1e9 / PEAK_HBM_GBS, 4)}
 
     # routes per expert (the library's rule, restated for accounting)
     q4 = wl["w_dtype"].startswith("q4")
     fat_rows = opts.fat_rows if q4 else 0
     if 0 < fat_rows < 17:
         fat_rows = 17
+    if q4 and T < fat_rows:
+        fat_rows_eff = 0
+    else:
+        fat_rows_eff = fat_rows
     S = float(opts.splitk_max_pairs)
     if q4:
-        full_mask = (counts >= fat_rows) if fat_rows > 0 else counts < 0
+        full_mask = (counts >= fat_rows_eff) if fat_rows_eff > 0 else counts < 0
     elif wl["w_dtype"] == "f32":
         full_mask = counts < 0
     else:
@@ -240,45 +239,26 @@ def main():
                 full_mask &= counts > 256
     sk_mask = (counts > 0) & ~full_mask
     rows_full = int(counts[full_mask].sum())
-    wbytes = W.weight_bytes_per_expert(D, F, wl["w_dtype"]) / 3.0   # per matrix
-    xb = W.dtype_bytes(wl["x_dtype"])
+    phase_units = route_units(counts, full_mask, sk_mask, D, F, wl, T, kept_pairs)
 
     roofline = None
+    routes = None
     if phase_ms:
         per = {name: v / max(calls, 1) for name, v in phase_ms.items()}
-        unit = {
-            "gateup_full": ("mfma", 4.0 * D * F * rows_full),
-            "down_full": ("mfma", 2.0 * D * F * rows_full),
-            "gateup_splitk": ("hbm", 2 * wbytes * int(sk_mask.sum())
-                              + int(counts[sk_mask].sum()) * D * xb),
-            "down_splitk": ("hbm", wbytes * int(sk_mask.sum())
-                            + int(counts[sk_mask].sum()) * (F * xb + D * 4)),
-            "dequant_once": ("hbm", int(full_mask.sum()) * 3 * D * F
-                             * (W.weight_bytes_per_expert(1, 1, wl["w_dtype"]) / 3.0 + 2.0)
-                             if q4 else 0),
-            "combine": ("hbm", kept_pairs * D * 4 + T * D * 4),
-            "classify": ("hbm", 0),
-        }
+        routes = {}
+        for name, (bound, amount, extra) in phase_units.items():
+            ms = per.get(name, 0.0)
+            if ms <= 0 or amount <= 0:
+                continue
+            routes[name] = roofline_entry(bound, amount, ms, wl["x_dtype"], extra)
         dom = max((n for n in per if per[n] > 0), key=lambda n: per[n])
-        bound, amount = unit[dom]
-        sec = per[dom] * 1e-3
-        if bound == "mfma":
-            achieved = amount / sec / 1e12
-            peak = PEAK_TFLOPS[wl["x_dtype"]]
-            u = "TFLOP/s"
-        else:
-            achieved = amount / sec / 1e9
-            peak = PEAK_HBM_GBS
-            u = "GB/s"
-        traffic = load_traffic(wl["name"], dom)
-        roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2),
-                    "peak": peak, "unit": u, "frac": round(achieved / peak, 4),
-                    "traffic": traffic,
-                    "algorithmic_per_launch": amount,
-                    "avg_launch_ms": round(per[dom], 4),
-                    "phase_ms_per_step": {n: round(v, 4) for n, v in per.items()
-                                          if v > 0}}
-
+        if dom in routes:
+            roofline = dict(kernel=dom, **routes[dom])
+            roofline["traffic"] = load_traffic(wl["name"], dom)
+            roofline["algorithmic_per_launch"] = phase_units[dom][1]
+            roofline["avg_launch_ms"] = round(per[dom], 4)
+            roofline["phase_ms_per_step"] = {n: round(v, 4) for n, v in per.items()
+                                             if v > 0}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
@@ -302,19 +282,81 @@ def main():
                    "capacity_factor": wl["capacity_factor"],
                    "parallelism": "single GPU"},
         "pairs_per_s": round(pairs_s, 1),
-        "weight_stream": weight_stream,
         "kept_pairs": kept_pairs,
         "drop_fraction": st["drop_fraction"],
-        "routes": {"full_or_fat_experts": int(full_mask.sum()),
-                   "splitk_experts": int(sk_mask.sum()),
-                   "rows_full": rows_full,
-                   "splitk_max_pairs": S, "fat_rows": fat_rows},
+        "route_counts": {"touched_experts": touched,
+                         "full_or_fat_experts": int(full_mask.sum()),
+                         "splitk_experts": int(sk_mask.sum()),
+                         "rows_full": rows_full,
+                         "splitk_max_pairs": S, "fat_rows": fat_rows},
         "roofline": roofline,
+        "routes": routes,
         "cold": cold,
         "cpu_baseline": cpu,
         "hardware": hardware(torch),
     }
     print(json.dumps(out), flush=True)
+
+
+def route_units(counts, full_mask, sk_mask, D, F, wl, T, kept_pairs):
+    """Algorithmic work of each forward phase, per step: (bound, amount,
+    details). Full tile: 4 D F (gate/up) and 2 D F (down) flops per pair of
+    a full-route expert. Thin groups (an expert's split-K rows cut into
+    groups of <= 64; a group of <= 16 rows runs in the 16-row launch, the
+    others in the 64-row one): per group its expert's weights of the stage
+    once, its activation rows in and its output rows out. Dequant-once: each
+    fat matrix read packed and written as fp16 once. Combine: each kept
+    pair's output row read once, y written once."""
+    import numpy as np
+
+    import workloads as W
+    bw = W.weight_bytes_per_expert(1, 1, wl["w_dtype"]) / 3.0   # B per weight
+    xb = W.dtype_bytes(wl["x_dtype"])
+    yb = 2 if wl["x_dtype"] == "f16" else 4          # per-pair output rows
+    rows_full = int(counts[full_mask].sum())
+    g16 = g64 = r16 = r64 = 0
+    for c in counts[sk_mask]:
+        c = int(c)
+        ng = (c + 63) // 64
+        last = c - 64 * (ng - 1)
+        g64 += ng - 1 + (1 if last > 16 else 0)
+        r64 += 64 * (ng - 1) + (last if last > 16 else 0)
+        if last <= 16:
+            g16 += 1
+            r16 += last
+    gu_w, d_w = 2.0 * D * F * bw, 1.0 * D * F * bw
+    units = {
+        "gateup_full": ("mfma", 4.0 * D * F * rows_full, {"rows": rows_full}),
+        "down_full": ("mfma", 2.0 * D * F * rows_full, {"rows": rows_full}),
+        "gateup_thin16": ("hbm", g16 * gu_w + r16 * (D + F) * xb,
+                          {"groups": g16, "rows": r16}),
+        "gateup_thin64": ("hbm", g64 * gu_w + r64 * (D + F) * xb,
+                          {"groups": g64, "rows": r64}),
+        "down_thin16": ("hbm", g16 * d_w + r16 * (F * xb + D * yb),
+                        {"groups": g16, "rows": r16}),
+        "down_thin64": ("hbm", g64 * d_w + r64 * (F * xb + D * yb),
+                        {"groups": g64, "rows": r64}),
+        "combine": ("hbm", kept_pairs * D * yb + T * D * 4, {"pairs": kept_pairs}),
+    }
+    if wl["w_dtype"].startswith("q4"):
+        n_fat = int(full_mask.sum())
+        units["dequant_once"] = ("hbm", n_fat * 3.0 * D * F * (bw + 2.0),
+                                 {"experts": n_fat})
+    return units
+
+
+def roofline_entry(bound, amount, ms, x_dtype, extra=None):
+    sec = ms * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = amount / sec / 1e12, PEAK_TFLOPS[x_dtype], "TFLOP/s"
+    else:
+        achieved, peak, unit = amount / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    out = {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+           "unit": unit, "frac": round(achieved / peak, 4), "ms": round(ms, 4),
+           "amount": amount}
+    if extra:
+        out.update(extra)
+    return out
 
 
 def copy_calibration(args, torch, dev):
@@ -453,12 +495,13 @@ def bench_backward(args, dev, torch, moe, W):
         phase_ms, calls = moe.moe_phase_times(reset=True)
         per = {n: phase_ms[n] / max(calls, 1)
                for n in ("bwd_recompute", "bwd_data", "bwd_weights", "bwd_routing")}
-        # recompute and data gradients: 6 D F flops a pair each (matrix
-        # cores); weight gradients: writing the f32 gradients of every
+        # recompute: the gate and up products, 4 D F flops a pair; data
+        # gradients: dH' and dX over both weights, 6 D F (matrix cores);
+        # weight gradients: writing the f32 gradients of every
         # expert (3 E' D F x 4 B) plus reading the per-pair operands once
         # outweighs their 6 D F flops a pair at the HBM / MFMA ridge
         n_exp = E + ns
-        amount = {"bwd_recompute": ("mfma", 6.0 * D * F * P),
+        amount = {"bwd_recompute": ("mfma", 4.0 * D * F * P),
                   "bwd_data": ("mfma", 6.0 * D * F * P),
                   "bwd_weights": ("hbm", 3.0 * n_exp * D * F * 4
                                   + P * (2.0 * D + 3.0 * F) * W.dtype_bytes(wl["x_dtype"]))}

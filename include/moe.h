@@ -35,7 +35,8 @@
  *     K-contiguous: W_gate, W_up are [E + n_shared, F, D], W_down is
  *     [E + n_shared, D, F], as the pages use them through W.transpose(1, 2).
  *   - Supported dtype pairs (x, W): (F32, F32), (BF16, BF16), (F16, F16),
- *     (F16, Q4B32). Anything else is MOE_EUNSUPPORTED, never a fallback.
+ *     (F16, Q4B32), (F16, Q4A32), (F16, Q4A64). Anything else is
+ *     MOE_EUNSUPPORTED, never a fallback.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -108,13 +109,17 @@ typedef struct {
  *                     #4366, maintainer's review). Default 64.
  *   flags             MOE_OPT_PHASE_EVENTS records HIP events around each
  *                     forward phase on `stream` (see moe_phase_times).
- *                     MOE_OPT_BF16_PLAIN_H keeps the SwiGLU output of bf16
- *                     layers as one bf16 value (the pages' compute-dtype
- *                     buffer). By default a bf16 layer carries it as a
- *                     bf16 pair hi + lo (hi = bf16(h), lo = bf16(h - hi),
- *                     about 16 significant bits) and the down projection
- *                     multiplies both, so a layer whose output is mostly
- *                     dropped rows still meets 2e-2 x RMS(ref).
+ *                     The SwiGLU output H of a bf16 layer is one bf16 value
+ *                     (the pages' compute-dtype buffer) when the plan is
+ *                     uncapped, and a bf16 pair hi + lo (hi = bf16(h),
+ *                     lo = bf16(h - hi), about 16 significant bits, the down
+ *                     projection multiplying both) when it is capped: a
+ *                     capped plan's dropped pairs can leave most rows of y
+ *                     at zero, which shrinks RMS(y) against the rounding
+ *                     error of the others, and the pair keeps such a layer
+ *                     within 2e-2 x RMS(ref). MOE_OPT_BF16_SPLIT_H forces
+ *                     the pair, MOE_OPT_BF16_PLAIN_H the one value (with
+ *                     both set, the pair).
  *                     MOE_OPT_EXACT_ROUTES applies the S rule alone. */
 typedef struct {
     float swiglu_limit;
@@ -126,6 +131,7 @@ typedef struct {
 #define MOE_OPT_PHASE_EVENTS 1
 #define MOE_OPT_BF16_PLAIN_H 2
 #define MOE_OPT_EXACT_ROUTES 4
+#define MOE_OPT_BF16_SPLIT_H 8
 
 /* One weight tensor. `scales` is NULL unless dtype is a 4-bit format; then
  * it is 4-byte aligned (MOE_Q4B32) or 8-byte aligned (the affine formats):
@@ -263,6 +269,46 @@ moe_status moe_forward(const moe_plan *plan, const void *x, int32_t x_dtype,
                        void *ws, size_t ws_bytes, const moe_options *opt,
                        void *stream);
 
+/* Device buffers of moe_forward inside its workspace `ws`, for inspection
+ * after a call with the same plan, sizes, dtypes and options (tests and
+ * debugging); the pointers stay valid while `ws` does. P is the most pairs
+ * the plan can hold, T * k + n_shared * T; a pair's row is its index in the
+ * plan's expert-sorted pair list (offsets[e] + its slot).
+ *   h, h_lo      [P, h_ld] SwiGLU output of the pairs of experts on the
+ *                split-K (thin) routes, x's dtype; h_lo is the bf16 low
+ *                plane (NULL unless the layer carries one);
+ *   ht, ht_lo    [F / 32][P][32] SwiGLU output of the pairs of experts on the
+ *                full tile (NULL when the layout has no full route);
+ *   ypair        [P, D] each kept pair's unweighted expert output, fp16
+ *                (ypair_dtype MOE_F16) in an fp16 layer, else f32;
+ *   fat_slot     [E + n_shared] slot of each fat 4-bit expert's fp16 copies,
+ *                -1 for the others (NULL without a fat route);
+ *   fat_copy     the fp16 copies the dequantise-once step writes of the fat
+ *                experts' W_gate, W_up and W_down (Strata PR #4366,
+ *                "Approach": an expert's weights decoded to FP16 once): slot
+ *                s of matrix m ([N, K] = [F, D], [F, D], [D, F]) starts
+ *                s * N * K values after fat_copy[m] and is laid out
+ *                [K / 32][N][32] (NULL without a fat route); fat_slots is
+ *                the number of slots the workspace holds.
+ * Returns MOE_EINVAL on a NULL plan, ws or out, or sizes the workspace query
+ * refuses. */
+typedef struct {
+    const void *h, *h_lo;
+    int64_t h_ld;
+    const void *ht, *ht_lo;
+    int64_t pairs_max;
+    const void *ypair;
+    int32_t ypair_dtype;
+    const int32_t *fat_slot;
+    const void *fat_copy[3];
+    int64_t fat_slots;
+} moe_forward_views;
+
+moe_status moe_forward_get_views(const moe_plan *plan, int32_t D, int32_t F,
+                                 int32_t x_dtype, int32_t w_dtype,
+                                 const moe_options *opt, const void *ws,
+                                 moe_forward_views *out);
+
 /* --- backward ----------------------------------------------------------- */
 
 /* Bytes of device workspace moe_backward needs; 0 if unsupported. */
@@ -274,7 +320,7 @@ size_t moe_backward_workspace_bytes(const moe_plan *plan, int32_t D, int32_t F,
  * in one 16-bit dtype; 4-bit weights are not trained here): dx [T, D],
  * dw_gate / dw_up [E + n_shared, F, D], dw_down [E + n_shared, D, F], all
  * f32 and overwritten; every expert slot gets the sum over its kept pairs
- * (zeros for an expert with none), the property mini-AGI PR #4's
+ * (zeros for an expert with none), the property mini-AGI PR #3's
  * tests/test_dispatch.py asks of every dispatch. Optional (NULL to skip):
  * d_topk_w [T, k], the gradient of each routing weight (dy[t] . the pair's
  * unweighted output; 0 for a dropped pair), and d_logits [T, E], through the
@@ -313,12 +359,14 @@ moe_status moe_dequant_weights(int32_t dtype, const void *data,
 /* Milliseconds spent in each phase, summed over the moe_forward and
  * moe_route calls since the last reset that ran with MOE_OPT_PHASE_EVENTS;
  * `calls` receives the number of such calls. Phases: 0 classify,
- * 1 dequant-once, 2 gate/up full tile, 3 gate/up split-K, 4 down full tile,
- * 5 down split-K, 6 combine (moe_forward); 7 router kernel, 8 plan,
- * 9 routing statistics (moe_route); 10 recompute, 11 data gradients,
- * 12 weight gradients, 13 routing-weight gradients (moe_backward).
- * Synchronises on the recorded events. reset != 0 clears afterwards. */
-#define MOE_N_PHASES 14
+ * 1 dequant-once, 2 gate/up full tile, 3 gate/up split-K groups of <= 16
+ * rows, 4 down full tile, 5 down split-K groups of <= 16 rows, 6 combine,
+ * 14 gate/up split-K groups of 17..64 rows, 15 down groups of 17..64 rows
+ * (moe_forward); 7 router kernel, 8 plan, 9 routing statistics
+ * (moe_route); 10 recompute, 11 data gradients, 12 weight gradients,
+ * 13 routing-weight gradients (moe_backward). Synchronises on the recorded
+ * events. reset != 0 clears afterwards. */
+#define MOE_N_PHASES 16
 moe_status moe_phase_times(double *ms, int32_t n, int64_t *calls,
                            int32_t reset);
 

@@ -38,11 +38,12 @@ MOE_Q4A32, MOE_Q4A64 = 4, 5
 MOE_OPT_PHASE_EVENTS = 1
 MOE_OPT_BF16_PLAIN_H = 2
 MOE_OPT_EXACT_ROUTES = 4
-MOE_N_PHASES = 14
-PHASES = ("classify", "dequant_once", "gateup_full", "gateup_splitk",
-          "down_full", "down_splitk", "combine", "router_gemm", "route_plan",
+MOE_OPT_BF16_SPLIT_H = 8
+MOE_N_PHASES = 16
+PHASES = ("classify", "dequant_once", "gateup_full", "gateup_thin16",
+          "down_full", "down_thin16", "combine", "router_gemm", "route_plan",
           "router_stats", "bwd_recompute", "bwd_data", "bwd_weights",
-          "bwd_routing")
+          "bwd_routing", "gateup_thin64", "down_thin64")
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED",
                 -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
@@ -56,7 +57,7 @@ EXPORTED = (
     "moe_forward_workspace_bytes", "moe_forward", "moe_dequant_q4",
     "moe_phase_times", "moe_last_error", "moe_version",
     "moe_route_workspace_bytes", "moe_route", "moe_dequant_weights",
-    "moe_backward_workspace_bytes", "moe_backward",
+    "moe_backward_workspace_bytes", "moe_backward", "moe_forward_get_views",
 )
 
 ROUTE_STATS = ("kept_mass", "want_k", "z_loss", "balance", "aux")
@@ -90,6 +91,16 @@ class PlanViews(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_id", "topk_w", "slot", "tok2pair", "counts", "offsets",
         "pair_token", "pair_w", "stats")]
+
+
+class ForwardViews(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("h_lo", ctypes.c_void_p),
+                ("h_ld", ctypes.c_int64), ("ht", ctypes.c_void_p),
+                ("ht_lo", ctypes.c_void_p), ("pairs_max", ctypes.c_int64),
+                ("ypair", ctypes.c_void_p), ("ypair_dtype", ctypes.c_int32),
+                ("fat_slot", ctypes.c_void_p),
+                ("fat_copy", ctypes.c_void_p * 3),
+                ("fat_slots", ctypes.c_int64)]
 
 
 class MoeError(RuntimeError):
@@ -133,6 +144,10 @@ def library(path: str = LIB_PATH):
     L.moe_forward.argtypes = [vp, vp, i32, Weight, Weight, Weight, i32, i32,
                               vp, i32, vp, sz, ctypes.POINTER(Options), vp]
     L.moe_forward.restype = i32
+    L.moe_forward_get_views.argtypes = [vp, i32, i32, i32, i32,
+                                        ctypes.POINTER(Options), vp,
+                                        ctypes.POINTER(ForwardViews)]
+    L.moe_forward_get_views.restype = i32
     L.moe_dequant_q4.argtypes = [vp, vp, i64, i64, vp, vp]
     L.moe_dequant_q4.restype = i32
     L.moe_dequant_weights.argtypes = [i32, vp, vp, i64, i64, vp, vp]
@@ -382,6 +397,36 @@ def _dims(w_gate):
     return w_gate.shape[1], w_gate.shape[2]
 
 
+def _check_weight_shapes(plan, w_gate, w_up, w_down, D: int, F: int):
+    """W_gate, W_up [n, F, D] and W_down [n, D, F] (4-bit: packed [.., K/2]
+    with matching params) with n >= E + n_shared experts, one format: a
+    mismatched tensor would otherwise be read out of bounds on the device."""
+    n_need = plan.E + plan.n_shared
+    want = {"w_gate": (F, D), "w_up": (F, D), "w_down": (D, F)}
+    fmt = None
+    for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        N, K = want[name]
+        if isinstance(w, (tuple, list)):
+            data, params = w
+            if data.dim() != 3 or tuple(data.shape[1:]) != (N, K // 2):
+                raise ValueError(f"{name} packed data must be [n, {N}, {K // 2}], "
+                                 f"got {tuple(data.shape)}")
+            if tuple(params.shape[:2]) != tuple(data.shape[:2]):
+                raise ValueError(f"{name} params {tuple(params.shape)} do not "
+                                 f"match its data {tuple(data.shape)}")
+            f = q4_dtype(data, params)
+        else:
+            if w.dim() != 3 or tuple(w.shape[1:]) != (N, K):
+                raise ValueError(f"{name} must be [n, {N}, {K}], got {tuple(w.shape)}")
+            data, f = w, w.dtype
+        if data.shape[0] < n_need:
+            raise ValueError(f"{name} holds {data.shape[0]} experts, the plan "
+                             f"needs {n_need} (E + n_shared)")
+        if fmt is not None and f != fmt:
+            raise ValueError("w_gate, w_up and w_down must share one format")
+        fmt = f
+
+
 def moe_forward_workspace_bytes(plan: Plan, D: int, F: int, x_dtype: int,
                                 w_dtype: int, options: Options | None = None) -> int:
     o = options or moe_options_default()
@@ -406,6 +451,7 @@ def moe_forward(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
     F, Dw = _dims(w_gate)
     if Dw != D:
         raise ValueError(f"weights have d_model {Dw}, x has {D}")
+    _check_weight_shapes(plan, w_gate, w_up, w_down, D, F)
     o = options or moe_options_default()
     wg, keep_g = _weight(w_gate, x.device)
     wu, keep_u = _weight(w_up, x.device)
@@ -430,6 +476,55 @@ def moe_forward(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
     return out
 
 
+def moe_forward_get_views(plan: Plan, workspace: torch.Tensor, D: int, F: int,
+                          x_dtype: torch.dtype, w_dtype: int,
+                          options: Options | None = None) -> dict:
+    """torch views of a forward workspace after a moe_forward call with the
+    same plan, sizes, dtypes and options: ``ypair`` [P, D] (unweighted
+    per-pair outputs, rows in the plan's pair order), ``h`` [P, h_ld] (thin
+    routes' SwiGLU output), ``ht`` [F/32, P, 32] (full tile's), and for 4-bit
+    fat routes ``fat_slot`` [E + n_shared] and ``fat_copy`` (three uint16
+    views [n_slots, K/32, N, 32] of the fp16 copies of W_gate, W_up,
+    W_down)."""
+    v = ForwardViews()
+    o = options or moe_options_default()
+    xdt = _TORCH_TO_MOE[x_dtype]
+    _check(library().moe_forward_get_views(plan.handle, D, F, xdt, int(w_dtype),
+                                           ctypes.byref(o),
+                                           workspace.data_ptr(),
+                                           ctypes.byref(v)))
+    base = workspace.data_ptr()
+    P = int(v.pairs_max)
+    n_exp = plan.E + plan.n_shared
+
+    def view(ptr, n, dtype):
+        off = ptr - base
+        size = torch.tensor([], dtype=dtype).element_size()
+        return workspace[off:off + n * size].view(dtype)
+
+    yd = torch.float16 if v.ypair_dtype == MOE_F16 else torch.float32
+    out = {"ypair": view(v.ypair, P * D, yd).view(P, D),
+           "h": view(v.h, P * int(v.h_ld), x_dtype).view(P, int(v.h_ld))}
+    if v.h_lo:
+        out["h_lo"] = view(v.h_lo, P * int(v.h_ld), x_dtype).view(P, int(v.h_ld))
+    if v.ht:
+        out["ht"] = view(v.ht, P * F, x_dtype).view(F // 32, P, 32)
+    if v.ht_lo:
+        out["ht_lo"] = view(v.ht_lo, P * F, x_dtype).view(F // 32, P, 32)
+    if v.fat_slot:
+        out["fat_slot"] = view(v.fat_slot, n_exp, torch.int32)
+    if v.fat_copy[0]:
+        dims = ((F, D), (F, D), (D, F))
+        n_slots = int(v.fat_slots)
+        copies = []
+        for m in range(3):
+            N, K = dims[m]
+            copies.append(view(v.fat_copy[m], n_slots * N * K, torch.int16)
+                          .view(n_slots, K // 32, N, 32))
+        out["fat_copy"] = copies
+    return out
+
+
 def moe_backward(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
                  dy: torch.Tensor, options: Options | None = None,
                  want_dtw: bool = False, want_dlogits: bool = False,
@@ -443,7 +538,12 @@ def moe_backward(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
         raise ValueError("backward takes a 2-D bfloat16/float16 x")
     x = x.contiguous()
     T, D = x.shape
+    if T != plan.T:
+        raise ValueError(f"x has {T} tokens, the plan {plan.T}")
+    if isinstance(w_gate, (tuple, list)):
+        raise ValueError("backward takes 16-bit weights (4-bit ones are frozen)")
     F = w_gate.shape[1]
+    _check_weight_shapes(plan, w_gate, w_up, w_down, D, F)
     dy = dy.to(torch.float32).contiguous()
     if dy.shape != (T, D) or dy.device != x.device:
         raise ValueError("dy must be [T, D] on x's device")

@@ -2,7 +2,7 @@
 // L = sum_t dy[t] . y[t] for x, the three expert weights, the routing
 // weights and (through the renormalised top-k softmax) the logits. Every
 // expert slot gets the sum over its kept pairs, whatever the dispatch -- the
-// property mini-AGI PR #4's tests/test_dispatch.py checks.
+// property mini-AGI PR #3's tests/test_dispatch.py checks.
 //
 // Per kept pair p = (token t, expert e, weight w) in the plan's expert-sorted
 // order (a pair of the shared expert has w = 1):
@@ -547,9 +547,12 @@ __device__ __forceinline__ void swiglu_back1(float g, float u, float dh, float c
   du = dh * gc * s * mu;
 }
 
-// dH = pair_w[p] dH'_p; dG, dU from dH as above; H_p = SwiGLU(G, U) rounded
-// to the compute dtype as the forward rounds it (silu with the hardware's
-// 2^x and reciprocal); and dtw_p = dH'_p . H_p.
+// dH = pair_w[p] dH'_p; dG, dU from dH as above; H_p = SwiGLU(G, U) (silu
+// with the hardware's 2^x and reciprocal), stored rounded once to the
+// compute dtype for the dW_down product -- the plain one-value H of the
+// forward; a bf16 forward that also carries H's low plane keeps about 16
+// bits, so its dW_down differs from this one by that one rounding -- and
+// dtw_p = dH'_p . H_p taken on the unrounded f32 H.
 // One wave per pair: lanes over F four values at a time in a fixed stride,
 // then a fixed butterfly for dtw_p.
 template <class S>
@@ -573,8 +576,9 @@ __global__ __launch_bounds__(256) void bwd_swiglu_back_kernel(
       S og[4], ou[4], oh[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        oh[q] = (S)swiglu(gv[q], uv[q], c);
-        acc = fmaf(dv[q], (float)oh[q], acc);
+        const float hq = swiglu(gv[q], uv[q], c);
+        oh[q] = (S)hq;
+        acc = fmaf(dv[q], hq, acc);
         float dg, du;
         swiglu_back1(gv[q], uv[q], w * dv[q], c, dg, du);
         og[q] = (S)dg;

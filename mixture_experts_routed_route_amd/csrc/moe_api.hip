@@ -200,8 +200,11 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.cap_sk1 = n_exp;
   L.cap_sk4 = n_exp + (int)(Pmax / kSkRows) + 1;
   L.fat_rows = q4_fmt(wdt) >= 0 ? effective_fat_rows(o) : 0;
+  // an expert holds at most T pairs (k distinct experts per token; the
+  // shared one takes each token once), so a prompt of fewer than fat_rows
+  // tokens has no fat expert
   L.max_fat = 0;
-  if (L.fat_rows > 0)
+  if (L.fat_rows > 0 && d.T >= L.fat_rows)
     L.max_fat = (int)std::min<int64_t>(n_exp, Pmax / L.fat_rows);
   // the stream tile takes the split-K groups of a bf16/f16/q4 layer whose
   // sizes it tiles
@@ -229,7 +232,12 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
   L.H = take((size_t)Pmax * L.h_ld * xb + 16);
-  L.split_h = xdt == MOE_BF16 && !(o.flags & MOE_OPT_BF16_PLAIN_H);
+  // bf16 H: the low plane by default only for capped plans (their dropped
+  // pairs leave rows of y at zero, which lowers RMS(y) against the rounding
+  // error of the rows that are not); an explicit flag decides otherwise
+  L.split_h = xdt == MOE_BF16 &&
+              ((o.flags & MOE_OPT_BF16_SPLIT_H) ||
+               (!(o.flags & MOE_OPT_BF16_PLAIN_H) && d.capacity_factor > 0.f));
   L.H2 = take(L.split_h ? (size_t)Pmax * L.h_ld * 2 + 16 : 0);
   // H of full-tile experts, k-block-major [F / 32][Pmax][32]
   L.Ht = take(L.can_full ? (size_t)Pmax * F * xb + 16 : 0);
@@ -678,7 +686,6 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       if (e != hipSuccess) return hip_fail(e, "full tile kernel");
     }
     {
-      PhaseScope ps(rec, stage == 0 ? 3 : 5, s);
       const int nnb = stage == 0 ? F / 32 : D / 64;
       if (L.stream) {
         g.part = (float*)(b + L.part);
@@ -686,6 +693,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       const int stream_grid = std::min(info.ncu, kStreamMaxRuns);
       if (run_sk1) {
         // groups of <= 16 rows
+        PhaseScope ps(rec, stage == 0 ? 3 : 5, s);
         g.list = (const int32_t*)(b + L.sk1);
         g.meta_index = kMetaSk1;
         if (L.stream) {
@@ -699,6 +707,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       }
       if (run_sk4) {
         // groups of 17..64 rows
+        PhaseScope ps(rec, stage == 0 ? 14 : 15, s);
         g.list = (const int32_t*)(b + L.sk4);
         g.meta_index = kMetaSk4;
         if (x_dtype == MOE_F32) {
@@ -725,6 +734,33 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
                        d.n_shared, d.E, y_dtype, y, s);
     if (e != hipSuccess) return hip_fail(e, "combine kernel");
   }
+  return MOE_OK;
+}
+
+moe_status moe_forward_get_views(const moe_plan* p, int32_t D, int32_t F,
+                                 int32_t x_dtype, int32_t w_dtype,
+                                 const moe_options* opt, const void* ws,
+                                 moe_forward_views* v) {
+  if (!p || !ws || !v) return fail(MOE_EINVAL, "NULL plan, workspace or views");
+  if (D <= 0 || F <= 0 || D % 128 || F % 128 || !dtypes_ok(x_dtype, w_dtype))
+    return fail(MOE_EINVAL, "bad sizes or dtypes for the forward views");
+  const moe_options o = opt ? *opt : defaults();
+  const FwdLayout L = fwd_layout(p->desc, D, F, x_dtype, w_dtype, o);
+  const char* b = static_cast<const char*>(ws);
+  const bool fat = L.max_fat > 0;
+  v->h = b + L.H;
+  v->h_lo = L.split_h ? b + L.H2 : nullptr;
+  v->h_ld = L.h_ld;
+  v->ht = L.can_full ? b + L.Ht : nullptr;
+  v->ht_lo = L.can_full && L.split_h ? b + L.Ht2 : nullptr;
+  v->pairs_max = (int64_t)p->desc.T * p->desc.k + (int64_t)p->desc.n_shared * p->desc.T;
+  v->ypair = b + L.Y;
+  v->ypair_dtype = x_dtype == MOE_F16 ? MOE_F16 : MOE_F32;
+  v->fat_slot = L.can_fat ? reinterpret_cast<const int32_t*>(b + L.fat_slot) : nullptr;
+  v->fat_copy[0] = fat ? b + L.stg_g : nullptr;
+  v->fat_copy[1] = fat ? b + L.stg_u : nullptr;
+  v->fat_copy[2] = fat ? b + L.stg_d : nullptr;
+  v->fat_slots = L.max_fat;
   return MOE_OK;
 }
 

@@ -109,3 +109,78 @@ def check_layer(wl, y, tokens=None, ref=None):
     tol = TOL[wl["x_dtype"]]
     assert err <= tol * rms + 1e-30, f"max err {err:.3e} > {tol} x RMS {rms:.3e}"
     return err, rms
+
+
+WDT = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "f16": moe.MOE_F16,
+       "q4b32": moe.MOE_Q4B32, "q4a32": moe.MOE_Q4A32, "q4a64": moe.MOE_Q4A64}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def gpu_layer_views(wl, options=None, dev="cuda"):
+    """The layer through the C ABI with an explicit forward workspace, and
+    torch views of that workspace after the call (per-pair outputs, SwiGLU
+    buffers, the dequantised fp16 copies of fat experts)."""
+    p = gpu_plan(wl, dev)
+    x = wl["x"].to(dev)
+    wg, wu, wd = (to_dev(wl[n], dev) for n in ("w_gate", "w_up", "w_down"))
+    o = options or moe.moe_options_default()
+    D, F = wl["D"], wl["F"]
+    xdt = TORCH_DT[wl["x_dtype"]]
+    wdt = WDT[wl["w_dtype"]]
+    nbytes = moe.moe_forward_workspace_bytes(p, D, F, WDT[wl["x_dtype"]], wdt, o)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    y = moe.moe_forward(p, x, wg, wu, wd, options=o, workspace=ws)
+    torch.cuda.synchronize()
+    views = moe.moe_forward_get_views(p, ws, D, F, xdt, wdt, o)
+    return p, y, views
+
+
+def check_fat_copies(wl, p, views, fat_rows, max_experts=None):
+    """The fp16 copies the forward's dequantise-once step wrote, bit for bit
+    against fp16_rne of the oracle's exact value (q * s, or q * s + b), for
+    every fat expert (or the first, a middle and the last max_experts of
+    them); the fat set is exactly the experts holding >= fat_rows pairs and
+    the slots number them in expert order."""
+    counts = plan_arrays(p)["counts"]
+    fs = views["fat_slot"].cpu().numpy()
+    fat = np.where(fs >= 0)[0]
+    want_fat = np.where(counts >= fat_rows)[0] if fat_rows > 0 else fat[:0]
+    assert np.array_equal(fat, want_fat), "fat experts differ"
+    assert np.array_equal(fs[fat], np.arange(len(fat))), "fat slots"
+    sel = fat
+    if max_experts is not None and len(fat) > max_experts:
+        idx = np.unique(np.linspace(0, len(fat) - 1, max_experts).astype(int))
+        sel = fat[idx]
+    D, F = wl["D"], wl["F"]
+    dims = {"w_gate": (F, D), "w_up": (F, D), "w_down": (D, F)}
+    for m, name in enumerate(("w_gate", "w_up", "w_down")):
+        N, K = dims[name]
+        for e in sel:
+            got = views["fat_copy"][m][int(fs[e])].cpu().numpy().view(np.uint16)
+            got = got.transpose(1, 0, 2).reshape(N, K)
+            want = oracle.dequant_q4_to_f16_bits(wl[name], int(e), wl["w_dtype"])
+            assert np.array_equal(got, want), f"{name} of expert {e}"
+    return sel
+
+
+def check_pairs(wl, p, views, experts, tol=None):
+    """Every kept pair of the given experts: its unweighted expert output
+    (the row the combine weighs) against the oracle's, max|err| <= TOL *
+    RMS(ref) over the checked pairs."""
+    a = plan_arrays(p)
+    off, pt = a["offsets"], a["pair_token"]
+    rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in experts])
+    exps = np.concatenate([np.full(off[e + 1] - off[e], e) for e in experts])
+    assert rows.size > 0
+    ref = oracle.pairs(wl["x"], wl["w_gate"], wl["w_up"], wl["w_down"],
+                       pt[rows], exps, x_dtype=wl["x_dtype"],
+                       w_dtype=wl["w_dtype"], c=wl["swiglu_limit"])
+    got = views["ypair"][torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    assert np.all(np.isfinite(got)), "non-finite pair output"
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(got - ref)))
+    t = TOL[wl["x_dtype"]] if tol is None else tol
+    say(f"  {rows.size} pairs of {len(experts)} experts: max err / RMS = "
+        f"{err / (rms + 1e-300):.2e}")
+    assert err <= t * rms + 1e-30, f"pairs: max err {err:.3e} > {t} x RMS {rms:.3e}"
+    return rows.size

@@ -198,3 +198,51 @@ def test_backward_validation(lib):
                           0x3000, 0x4000, 0x5000, 0x6000, None, None, 0x10000,
                           1 << 20, None, None)
     assert st == moe.MOE_EINVAL
+
+
+class _FakePlan:
+    """Just the shape of a plan: the binding's checks run before any call."""
+    def __init__(self, T, E, k, n_shared=0):
+        self.T, self.E, self.k, self.n_shared = T, E, k, n_shared
+        self.handle = None
+
+
+@pytest.mark.parametrize("case", ["gate_experts", "up_shape", "down_shape",
+                                  "shared_missing", "mixed_dtype", "q4_data",
+                                  "q4_params", "q4_mixed_format"])
+def test_python_weight_shapes_rejected_before_launch(case):
+    T, D, F, E = 4, 128, 256, 8
+    bf = dict(dtype=torch.bfloat16)
+    x = torch.zeros(T, D, **bf)
+    wg, wu, wd = (torch.zeros(E, F, D, **bf), torch.zeros(E, F, D, **bf),
+                  torch.zeros(E, D, F, **bf))
+    plan = _FakePlan(T, E, 2)
+    if case == "gate_experts":
+        wg = torch.zeros(E - 1, F, D, **bf)
+    elif case == "up_shape":
+        wu = torch.zeros(E, F, D + 128, **bf)
+    elif case == "down_shape":
+        wd = torch.zeros(E, F, D, **bf)
+    elif case == "shared_missing":
+        plan = _FakePlan(T, E, 2, n_shared=1)
+    elif case == "mixed_dtype":
+        wu = torch.zeros(E, F, D, dtype=torch.float16)
+    else:
+        x = torch.zeros(T, D, dtype=torch.float16)
+        def q4(N, K, G=None):
+            d = torch.zeros(E, N, K // 2, dtype=torch.uint8)
+            p = (torch.zeros(E, N, K // 32, dtype=torch.float16) if G is None
+                 else torch.zeros(E, N, K // G, 2, dtype=torch.float16))
+            return d, p
+        wg, wu, wd = q4(F, D), q4(F, D), q4(D, F)
+        if case == "q4_data":
+            wd = (torch.zeros(E, D, F, dtype=torch.uint8), wd[1])
+        elif case == "q4_params":
+            wu = (wu[0], torch.zeros(E, F - 1, D // 32, dtype=torch.float16))
+        else:
+            wd = q4(D, F, 64)
+    with pytest.raises(ValueError):
+        moe.moe_forward(plan, x, wg, wu, wd)
+    if case in ("gate_experts", "up_shape", "down_shape", "shared_missing"):
+        with pytest.raises(ValueError):
+            moe.moe_backward(plan, x, wg, wu, wd, torch.zeros(T, D))

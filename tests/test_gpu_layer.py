@@ -10,8 +10,9 @@ import torch
 import mixture_experts_routed_route_amd as moe
 import oracle
 import workloads as W
-from helpers import (check_layer, check_plan, gpu_layer, gpu_plan,
-                     oracle_layer, sample_tokens, say, to_dev)
+from helpers import (check_fat_copies, check_layer, check_pairs, check_plan,
+                     gpu_layer, gpu_layer_views, gpu_plan, oracle_layer,
+                     plan_arrays, sample_tokens, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +54,34 @@ def test_prefill_forced_routes(S):
     opts = moe.make_options(splitk_max_pairs=S, exact_routes=True)
     p, y = gpu_layer(wl, options=opts)
     check_layer(wl, y, sample_tokens(wl["T"], 96, seed=4))
+
+
+@pytest.mark.parametrize("flag", ["plain", "split"])
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_bf16_h_one_value_or_pair(cfg, flag):
+    """The prefill and short-prompt layers with H forced to one bf16 value
+    (the default for their uncapped plans) or to the hi + lo pair: both
+    within the bar, every route (cfg 5 adds the shared expert)."""
+    wl = W.config(cfg)
+    f = moe.MOE_OPT_BF16_PLAIN_H if flag == "plain" else moe.MOE_OPT_BF16_SPLIT_H
+    say(f"layer {wl['name']} bf16 H {flag}")
+    p, y, views = gpu_layer_views(wl, options=moe.make_options(flags=f))
+    assert ("h_lo" in views) == (flag == "split")
+    counts = plan_arrays(p)["counts"]
+    live = np.where(counts > 0)[0]
+    check_pairs(wl, p, views, live[np.linspace(0, len(live) - 1, 6).astype(int)])
+    check_layer(wl, y, sample_tokens(wl["T"], 96, seed=5))
+
+
+@pytest.mark.parametrize("cf", [0.0, 1.25])
+def test_bf16_h_default_follows_capacity(cf):
+    """Without a flag, a bf16 layer carries H's low plane exactly when its
+    plan is capped."""
+    wl = W.make_layer(200, 256, 256, 16, 2, W.BF16, seed=29,
+                      capacity_factor=cf, logit_bias=torch.linspace(2, -2, 16))
+    p, y, views = gpu_layer_views(wl)
+    assert ("h_lo" in views) == (cf > 0)
+    check_layer(wl, y)
 
 
 @pytest.mark.parametrize("T", [33, 64, 128, 186])
@@ -117,22 +146,39 @@ def test_pairs_per_expert_both_tiles(ppe, S):
 
 
 def test_long_prompt_q4():
+    """The 13,312-token 4-bit workload: the plan in full; the dequantised
+    fp16 copies of three fat experts (first, middle, last slot) bit-exact as
+    the forward's own dequant-once step wrote them; the per-pair output of
+    every pair on a thin expert (split-K groups of <= 16 rows and the wide
+    tile's 17..63) against the oracle; the layer output on sampled tokens."""
     wl = W.config(4)
     say("layer long_prompt_q4 (13312 tokens, 4-bit experts)")
-    p, y = gpu_layer(wl)
+    p, y, views = gpu_layer_views(wl)
     st = moe.moe_plan_stats_get(p)
     assert st["fat"] > 0 and st["touched"] > st["fat"]   # both routes used
     check_plan(wl, p)
+    check_fat_copies(wl, p, views, 64, max_experts=3)
+    counts = plan_arrays(p)["counts"]
+    thin = np.where((counts > 0) & (counts < 64))[0]
+    assert (counts[thin] <= 16).any() and (counts[thin] > 16).any()
+    assert check_pairs(wl, p, views, thin) >= 1000
     check_layer(wl, y, sample_tokens(wl["T"], 40, seed=7))
 
 
 @pytest.mark.parametrize("fat_rows", [0, 17, 64, 100000])
 def test_q4_routes_small(fat_rows):
-    """4-bit experts on the fat (dequant-once) and fused-dequant routes."""
+    """4-bit experts on the fat (dequant-once) and fused-dequant routes:
+    every fat expert's fp16 copies bit-exact (gate/up K = 256, down K = 384:
+    both decode tile depths), every pair's output, the layer."""
     wl = W.make_layer(520, 256, 384, 6, 2, W.F16, w_dtype=W.Q4B32, seed=21,
                       logit_bias=torch.tensor([3.0, 2.0, 1.0, 0.0, -2.0, -4.0]))
     say(f"layer q4 small fat_rows={fat_rows}")
-    p, y = gpu_layer(wl, options=moe.make_options(fat_rows=fat_rows))
+    p, y, views = gpu_layer_views(wl, options=moe.make_options(fat_rows=fat_rows))
+    counts = plan_arrays(p)["counts"]
+    eff = 0 if fat_rows <= 0 else max(fat_rows, 17)
+    if 0 < eff <= counts.max():
+        assert len(check_fat_copies(wl, p, views, eff)) > 0
+    check_pairs(wl, p, views, np.where(counts > 0)[0])
     check_layer(wl, y, sample_tokens(wl["T"], 64, seed=fat_rows % 97))
 
 
