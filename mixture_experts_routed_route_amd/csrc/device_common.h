@@ -83,6 +83,23 @@ __device__ __forceinline__ float swiglu(float g, float u, float c) {
   return g * __builtin_amdgcn_rcpf(1.f + e) * u;
 }
 
+// The 8 nibbles of a word (low nibble first) as 4 pairs of fp16 bit
+// patterns 0x6400 | v (the fp16 value 1024 + v, exactly): byte-interleave
+// the low and high nibbles into [v0 v1 v2 v3], [v4 v5 v6 v7], then spread
+// each byte to the low byte of a 16-bit half whose high byte v_perm takes
+// from a register of 0x64 bytes (two selects a pair, no OR).
+__device__ __forceinline__ void unpack_nibbles(uint32_t x, uint32_t out[4]) {
+  const uint32_t lo = x & 0x0F0F0F0Fu;          // v0 v2 v4 v6
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;   // v1 v3 v5 v7
+  const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // v0 v1 v2 v3
+  const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // v4 v5 v6 v7
+  const uint32_t c = 0x64646464u;
+  out[0] = __builtin_amdgcn_perm(c, p0, 0x04010400u);   // [v0, 0x64, v1, 0x64]
+  out[1] = __builtin_amdgcn_perm(c, p0, 0x04030402u);
+  out[2] = __builtin_amdgcn_perm(c, p1, 0x04010400u);
+  out[3] = __builtin_amdgcn_perm(c, p1, 0x04030402u);
+}
+
 // 8 consecutive 4-bit values (one 32-bit word, low nibble first) times
 // their block scale, as 8 fp16: fp16 bits 0x6400 | v encode 1024 + v
 // exactly, v = nibble ^ 8; subtracting 1032 leaves the signed value q
@@ -90,16 +107,12 @@ __device__ __forceinline__ float swiglu(float g, float u, float c) {
 __device__ __forceinline__ half8 dequant_word(uint32_t word, _Float16 s) {
   const half2v s2 = {s, s};
   const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const uint32_t x = word ^ 0x88888888u;
-  const uint32_t lo = x & 0x0F0F0F0Fu;
-  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+  uint32_t pr[4];
+  unpack_nibbles(word ^ 0x88888888u, pr);
   half8 out;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    // bytes of the result: [lo_b, 0, hi_b, 0] (selector 12 gives zero)
-    const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
-    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
-    half2v h = __builtin_bit_cast(half2v, pr);
+    half2v h = __builtin_bit_cast(half2v, pr[b]);
     h = (h + off) * s2;
     out[2 * b] = h[0];
     out[2 * b + 1] = h[1];
@@ -166,14 +179,12 @@ __device__ __forceinline__ half8 dequant_word_affine(uint32_t word, uint32_t sb)
   const half2v s2 = {sc, sc};
   const half2v b2 = {bi, bi};
   const half2v off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const uint32_t lo = word & 0x0F0F0F0Fu;
-  const uint32_t hi = (word >> 4) & 0x0F0F0F0Fu;
+  uint32_t pr[4];
+  unpack_nibbles(word, pr);
   half8 out;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
-    const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
-    half2v h = __builtin_bit_cast(half2v, pr) + off;
+    half2v h = __builtin_bit_cast(half2v, pr[b]) + off;
     h = __builtin_elementwise_fma(h, s2, b2);
     out[2 * b] = h[0];
     out[2 * b + 1] = h[1];

@@ -227,27 +227,6 @@ hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s) {
 }
 
 // ---- dequantise once --------------------------------------------------------
-//
-// One unit = 8 consecutive values of a row: 4 bytes of nibbles in, 16 bytes
-// of fp16 out, so a wave's loads cover 256 contiguous bytes and its stores
-// 1 KB. The four lanes of a 32-value block share its scale.
-
-__device__ __forceinline__ uint4 dequant8(uint32_t word, _Float16 s) {
-  const half2v s2 = {s, s};
-  const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const uint32_t x = word ^ 0x88888888u;
-  const uint32_t lo = x & 0x0F0F0F0Fu;
-  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
-  uint32_t o[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const uint32_t sel = 0x0C000C00u | ((4u + b) << 16) | (uint32_t)b;
-    half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u);
-    h = (h + off) * s2;
-    o[b] = __builtin_bit_cast(uint32_t, h);
-  }
-  return uint4{o[0], o[1], o[2], o[3]};
-}
 
 // Fat experts: slot s of a staging buffer holds expert fat_list[s]'s
 // [rows, K] matrix as fp16, k-block-major: [K / 32][rows][32], so that the
@@ -334,6 +313,9 @@ __global__ __launch_bounds__(256) void dequant_fat_kernel(
     dequant_fat_tiles<4, FMT>(d, m, fat_list, nfat, tile);
 }
 
+// One unit = 8 consecutive values of a row: 4 bytes of nibbles in, 16 bytes
+// of fp16 out, so a wave's loads cover 256 contiguous bytes and its stores
+// 1 KB. The four lanes of a 32-value block share its scale.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_rows_kernel(
     const uint8_t* __restrict__ q, const char* __restrict__ sc,
@@ -349,7 +331,7 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(
     if constexpr (FMT == 0) {
       const uint16_t sb = reinterpret_cast<const uint16_t*>(sc)[row * (size_t)(K / 32) + (c8 >> 2)];
       reinterpret_cast<uint4*>(out + row * (size_t)K)[c8] =
-          dequant8(word, __builtin_bit_cast(_Float16, sb));
+          __builtin_bit_cast(uint4, dequant_word(word, __builtin_bit_cast(_Float16, sb)));
     } else {
       const uint32_t p = reinterpret_cast<const uint32_t*>(sc)[
           row * (size_t)ngr + c8 * 8 / Q4F<FMT>::kGroup];

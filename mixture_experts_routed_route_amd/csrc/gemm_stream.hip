@@ -31,7 +31,9 @@
 //    classify kernel fills.
 //  * 4-bit experts do not come here: their thin groups are bound by the
 //    decode arithmetic, not the stream, and take the register-streaming
-//    split-K and wide tiles, which keep more waves per CU.
+//    split-K and wide tiles, which keep more waves per CU (a variant of
+//    this tile that decodes the weights after they land in LDS, with two
+//    or four workgroups per CU, ran 14-30 % slower than those).
 #include "device_common.h"
 
 namespace moe {
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs a) {
       if (whole) {
         stream_store<S, MODE, RB>(a, acc, c_nb, c_nrows, c_pstart, wave, lane);
       } else {
-        float* pp = a.part + ((size_t)b * 2 + (item == first_item ? 0 : 1)) * kStreamSlotFloats;
+        float* pp = a.part + ((size_t)b * 2 + (item == first_item ? 0 : 1)) * (kStreamSlotFloats1 * RB);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(256) void gemm_stream_fixup_kernel(GemmArgs a, int 
       // past the item's last run, or an empty run: nothing to add
       live[q] = rn <= bl && s0 != run_start(U, rn + 1, G);
       const int slot = s0 / nk == item ? 0 : 1;
-      const float* pp = a.part + ((size_t)(live[q] ? rn : j) * 2 + slot) * kStreamSlotFloats;
+      const float* pp = a.part + ((size_t)(live[q] ? rn : j) * 2 + slot) * (kStreamSlotFloats1 * RB);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -404,7 +406,7 @@ static hipError_t stream_rb(const GemmArgs& a, int rows, int grid, hipStream_t s
 hipError_t launch_gemm_stream(const GemmArgs& a, int xdt, int wdt, int rows,
                               int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (grid > kStreamMaxRuns || rows < 1 || rows > kStreamTokRows)
+  if (rows < 1 || rows > kStreamTokRows || grid > stream_max_runs(rows <= 16 ? 1 : 4))
     return hipErrorInvalidValue;
   if (xdt == MOE_BF16 && wdt == MOE_BF16) return stream_rb<SBF16>(a, rows, grid, s);
   if (xdt == MOE_F16 && wdt == MOE_F16) return stream_rb<SF16>(a, rows, grid, s);

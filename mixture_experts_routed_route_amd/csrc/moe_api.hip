@@ -29,6 +29,20 @@ moe_status fail(moe_status st, const char* fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+moe_status moe::set_error(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+namespace {
+
 moe_status hip_fail(hipError_t e, const char* where) {
   return fail(MOE_EHIP, "%s: %s (%s)", where, hipGetErrorName(e),
               hipGetErrorString(e));
@@ -248,7 +262,7 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.sk4 = take((size_t)L.cap_sk4 * 16);
   L.sk1_tok = take(L.stream ? (size_t)L.cap_sk1 * kStreamTokRows * 4 : 0);
   L.sk4_tok = take(L.stream ? (size_t)L.cap_sk4 * kStreamTokRows * 4 : 0);
-  L.part = take(L.stream ? (size_t)kStreamMaxRuns * 2 * kStreamSlotFloats * 4 : 0);
+  L.part = take(L.stream ? (size_t)kStreamPartFloats * 4 : 0);
   L.fat_slot = take((size_t)n_exp * 4);
   L.fat_list = take((size_t)n_exp * 4);
   L.meta = take(kMetaCount * 4);
@@ -690,7 +704,8 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       if (L.stream) {
         g.part = (float*)(b + L.part);
       }
-      const int stream_grid = std::min(info.ncu, kStreamMaxRuns);
+      const int stream_grid1 = std::min(info.ncu, stream_max_runs(1));
+      const int stream_grid4 = std::min(info.ncu, stream_max_runs(4));
       if (run_sk1) {
         // groups of <= 16 rows
         PhaseScope ps(rec, stage == 0 ? 3 : 5, s);
@@ -698,7 +713,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
         g.meta_index = kMetaSk1;
         if (L.stream) {
           g.tok = (const int32_t*)(b + L.sk1_tok);
-          e = launch_gemm_stream(g, x_dtype, wdt, 16, stream_grid, s);
+          e = launch_gemm_stream(g, x_dtype, wdt, 16, stream_grid1, s);
         } else {
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk1 * nnb, sk_rb1_grid_cap);
           e = launch_gemm_splitk(g, x_dtype, wdt, 1, grid, s);
@@ -715,7 +730,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
           e = launch_gemm_splitk(g, x_dtype, wdt, 4, grid, s);
         } else if (L.stream) {
           g.tok = (const int32_t*)(b + L.sk4_tok);
-          e = launch_gemm_stream(g, x_dtype, wdt, kStreamTokRows, stream_grid, s);
+          e = launch_gemm_stream(g, x_dtype, wdt, kStreamTokRows, stream_grid4, s);
         } else {
           // wide fused-dequant tile, 256 columns per item
           const int wnb = stage == 0 ? (F + 127) / 128 : (D + 255) / 256;

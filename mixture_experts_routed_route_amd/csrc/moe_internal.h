@@ -44,13 +44,16 @@ constexpr int kPadBytes = 256;
 // Split-K tile: output columns per item and rows per row block.
 constexpr int kSkNB = 64;
 constexpr int kSkRows = 64;   // rows per split-K group (4 blocks of 16)
-// Stream tile: most runs (workgroups) per launch; each run owns two fp32
-// partial-sum slots of 256 threads x 32 values in the workspace. Its groups
-// hold at most kStreamTokRows pairs (the classify kernel's token table has
-// that many entries per group).
-constexpr int kStreamMaxRuns = 512;
-constexpr int kStreamSlotFloats = 8192;
+// Stream tile: each run (workgroup) of a launch owns two fp32 partial-sum
+// slots of 256 threads x 8 RB values (RB = 16-row token blocks of its
+// groups) in a workspace buffer of kStreamPartFloats, so a launch takes at
+// most kStreamPartFloats / (2 x 2048 RB) runs. Its groups hold at most
+// kStreamTokRows pairs (the classify kernel's token table has that many
+// entries per group).
+constexpr int kStreamSlotFloats1 = 2048;          // per 16-row block
+constexpr int kStreamPartFloats = 2 * 2048 * 2048;
 constexpr int kStreamTokRows = 64;
+inline int stream_max_runs(int rb) { return kStreamPartFloats / (2 * kStreamSlotFloats1 * rb); }
 
 // The format of a 4-bit weight dtype: 0 signed with an fp16 scale per 32
 // K values, 1 / 2 affine with an fp16 (scale, bias) pair per 32 / 64; -1 if
@@ -77,6 +80,9 @@ constexpr int kRouterDotT = 64;
 constexpr int kRouterBigTiles = 128;
 // d_model bound of the router: a 128-row tile's bytes stay below 2^31.
 constexpr int kRouterMaxD = 1 << 20;
+
+// Sets this thread's last-error message (moe_last_error) and returns st.
+moe_status set_error(moe_status st, const char* fmt, ...);
 
 // ---- launchers (plan_kernels.hip) ---------------------------------------
 hipError_t launch_route_hist(const float* logits, int T, int E, int k,
@@ -159,7 +165,7 @@ struct GemmArgs {
                             // ([F / 32][h_rows][32]) it writes (gate/up) or
                             // reads (down)
   const int32_t* tok;       // stream tile, gate/up: the sk1 groups' x rows
-  float* part;              // stream tile: [kStreamMaxRuns, 2, kStreamSlotFloats]
+  float* part;              // stream tile: [runs, 2, 2048 RB] floats
 };
 hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
                             hipStream_t s);
