@@ -58,7 +58,9 @@ EXPORTED = (
     "moe_phase_times", "moe_last_error", "moe_version",
     "moe_route_workspace_bytes", "moe_route", "moe_dequant_weights",
     "moe_backward_workspace_bytes", "moe_backward", "moe_forward_get_views",
+    "moe_forward_noalloc",
 )
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 ROUTE_STATS = ("kept_mass", "want_k", "z_loss", "balance", "aux")
 
@@ -144,6 +146,9 @@ def library(path: str = LIB_PATH):
     L.moe_forward.argtypes = [vp, vp, i32, Weight, Weight, Weight, i32, i32,
                               vp, i32, vp, sz, ctypes.POINTER(Options), vp]
     L.moe_forward.restype = i32
+    L.moe_forward_noalloc.argtypes = [vp, vp, i32, Weight, Weight, Weight, i32,
+                                      i32, vp, i32, ctypes.POINTER(Options), vp]
+    L.moe_forward_noalloc.restype = i32
     L.moe_forward_get_views.argtypes = [vp, i32, i32, i32, i32,
                                         ctypes.POINTER(Options), vp,
                                         ctypes.POINTER(ForwardViews)]
@@ -473,6 +478,40 @@ def moe_forward(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
                          workspace.data_ptr(),
                          workspace.numel(), ctypes.byref(o),
                          _stream(x.device)))
+    return out
+
+
+def moe_forward_noalloc(plan: Plan, x: torch.Tensor, w_gate, w_up, w_down,
+                        options: Options | None = None,
+                        out: torch.Tensor | None = None,
+                        y_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """moe_forward with the library's own per-GPU scratch as its workspace
+    (no device allocation inside the call; pass ``out`` to allocate nothing
+    here either). Calls that overlap on one GPU race on that scratch."""
+    L = library()
+    if x.dtype not in _TORCH_TO_MOE or x.dim() != 2:
+        raise ValueError("x must be a 2-D float32/bfloat16/float16 tensor")
+    x = x.contiguous()
+    T, D = x.shape
+    if T != plan.T:
+        raise ValueError(f"x has {T} tokens, the plan {plan.T}")
+    F, Dw = _dims(w_gate)
+    if Dw != D:
+        raise ValueError(f"weights have d_model {Dw}, x has {D}")
+    _check_weight_shapes(plan, w_gate, w_up, w_down, D, F)
+    o = options or moe_options_default()
+    wg, keep_g = _weight(w_gate, x.device)
+    wu, keep_u = _weight(w_up, x.device)
+    wd, keep_d = _weight(w_down, x.device)
+    if out is None:
+        out = torch.empty(T, D, dtype=y_dtype, device=x.device)
+    if out.dtype not in (torch.float32, x.dtype) or out.shape != (T, D) \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, D] f32 or x-dtype tensor")
+    _check(L.moe_forward_noalloc(plan.handle, x.data_ptr(), _TORCH_TO_MOE[x.dtype],
+                                 wg, wu, wd, D, F, out.data_ptr(),
+                                 _TORCH_TO_MOE[out.dtype], ctypes.byref(o),
+                                 _stream(x.device)))
     return out
 
 
