@@ -147,7 +147,10 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs a) {
   const int NNB = MODE == 0 ? N / 64 : N / 128;
   const int U = a.meta[a.meta_index] * NNB * nk;   // below 2^31 (host check)
   const int G = gridDim.x, b = blockIdx.x;
-  const int u0 = run_start(U, b, G), u1 = run_start(U, b + 1, G);
+  // a.part null: the launch has a workgroup for every item there can be,
+  // and workgroup b takes item b whole (no partial sums, no fix-up)
+  const int u0 = a.part ? run_start(U, b, G) : min(U, b * nk);
+  const int u1 = a.part ? run_start(U, b + 1, G) : min(U, (b + 1) * nk);
   if (u0 >= u1) return;   // whole block
   const int first_item = u0 / nk;
 
@@ -381,15 +384,19 @@ bool stream_supported(int mode, int K, int N, int wdt) {
 
 template <class TT, int RB>
 static hipError_t stream_launch(const GemmArgs& a, int grid, hipStream_t s) {
+  // without partial-sum slots every workgroup takes one whole item: no
+  // fix-up pass
   if (a.mode == 0) {
     hipLaunchKernelGGL((gemm_stream_kernel<TT, RB, 0, 0>), dim3(grid), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((gemm_stream_fixup_kernel<TT, RB, 0>), dim3(grid), dim3(256), 0, s, a, grid);
+    if (a.part)
+      hipLaunchKernelGGL((gemm_stream_fixup_kernel<TT, RB, 0>), dim3(grid), dim3(256), 0, s, a, grid);
   } else {
     if (a.A2)
       hipLaunchKernelGGL((gemm_stream_kernel<TT, RB, 1, 1>), dim3(grid), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((gemm_stream_kernel<TT, RB, 1, 0>), dim3(grid), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((gemm_stream_fixup_kernel<TT, RB, 1>), dim3(grid), dim3(256), 0, s, a, grid);
+    if (a.part)
+      hipLaunchKernelGGL((gemm_stream_fixup_kernel<TT, RB, 1>), dim3(grid), dim3(256), 0, s, a, grid);
   }
   return hipGetLastError();
 }
@@ -406,7 +413,8 @@ static hipError_t stream_rb(const GemmArgs& a, int rows, int grid, hipStream_t s
 hipError_t launch_gemm_stream(const GemmArgs& a, int xdt, int wdt, int rows,
                               int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (rows < 1 || rows > kStreamTokRows || grid > stream_max_runs(rows <= 16 ? 1 : 4))
+  if (rows < 1 || rows > kStreamTokRows ||
+      (a.part && grid > stream_max_runs(rows <= 16 ? 1 : 4)))
     return hipErrorInvalidValue;
   if (xdt == MOE_BF16 && wdt == MOE_BF16) return stream_rb<SBF16>(a, rows, grid, s);
   if (xdt == MOE_F16 && wdt == MOE_F16) return stream_rb<SF16>(a, rows, grid, s);

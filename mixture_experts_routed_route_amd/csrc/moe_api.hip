@@ -58,11 +58,21 @@ inline int xbytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
 struct PlanLayout {
   size_t ids, w, slot, tok2pair, hist, total, counts, offsets, pair_token,
-      pair_w, stats, bytes;
+      pair_w, stats, dlist, dtok, dmeta, bytes;
   int NC;     // 64-token permute chunks
   int NR;     // histogram rows (16 x tpw tokens each)
   int tpw;    // route tokens per wave
+  bool small; // one-block plan kernel
+  bool decode;// ... which also writes the decode-shaped thin-group list
 };
+
+// The one-block plan kernel takes prompts of at most kChunk tokens over at
+// most kPlanSmallE experts; for at most kDecodeT tokens it also writes the
+// thin-group list (every expert then holds at most kDecodeT pairs).
+inline bool plan_is_small(const moe_plan_desc& d) {
+  return d.T >= 1 && d.T <= kChunk && (int64_t)d.T * d.k <= kPlanSmallPairs &&
+         d.E <= kPlanSmallE;
+}
 
 bool desc_ok(const moe_plan_desc* d, std::string* why) {
   char buf[256];
@@ -108,6 +118,12 @@ PlanLayout plan_layout(const moe_plan_desc& d) {
   L.pair_token = take(P * 4 + 4);
   L.pair_w = take(P * 4 + 4);
   L.stats = take(8 * 8);
+  L.small = plan_is_small(d);
+  L.decode = L.small && d.T <= kDecodeT;
+  const size_t ng = L.decode ? (size_t)(d.E + d.n_shared) : 0;
+  L.dlist = take(ng * 16);
+  L.dtok = take(ng * kStreamTokRows * 4);
+  L.dmeta = take(L.decode ? kMetaCount * 4 : 0);
   L.bytes = o;
   return L;
 }
@@ -310,15 +326,17 @@ moe_status launch_plan(const moe_plan_desc& d, const float* logits,
                        const PlanLayout& L, char* b, int64_t limit,
                        hipStream_t s) {
   hipError_t e;
-  if (d.T >= 1 && d.T <= kChunk && (int64_t)d.T * d.k <= kPlanSmallPairs &&
-      d.E <= kPlanSmallE) {
+  if (L.small) {
     // one chunk: route, scan and permute in one block
+    const DecodeGroups dg{(int32_t*)(b + L.dlist), (int32_t*)(b + L.dtok),
+                          (int32_t*)(b + L.dmeta)};
     e = launch_plan_small(logits, d.T, d.E, d.k, d.n_shared, limit,
                           (int32_t*)(b + L.ids), (float*)(b + L.w),
                           (int32_t*)(b + L.total), (int32_t*)(b + L.counts),
                           (int32_t*)(b + L.offsets), (int64_t*)(b + L.stats),
                           (int32_t*)(b + L.slot), (int32_t*)(b + L.tok2pair),
-                          (int32_t*)(b + L.pair_token), (float*)(b + L.pair_w), s);
+                          (int32_t*)(b + L.pair_token), (float*)(b + L.pair_w),
+                          L.decode ? &dg : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "plan kernel");
   } else {
     if (L.NC > 0) {
@@ -598,8 +616,17 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   const int n_exp = d.E + d.n_shared;
   int32_t* meta = (int32_t*)(b + L.meta);
   hipError_t e;
+  // A decode-shaped plan holds at most kDecodeT pairs an expert, so every
+  // expert is one thin group unless the S rule sends experts of that size
+  // to the full tile; then the plan's own group list stands in for the
+  // classify kernel's.
+  const bool decode = p->L.decode &&
+      (wdt == MOE_F32 || q4_fmt(wdt) >= 0 ||
+       (double)o.splitk_max_pairs >= (double)d.T);
 
-  {
+  if (decode) {
+    meta = (int32_t*)(pb + p->L.dmeta);
+  } else {
     PhaseScope ps(rec, 0, s);
     ClassifyArgs ca{};
     ca.counts = (const int32_t*)(pb + p->L.counts);
@@ -628,11 +655,15 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   // T < fat_rows none is fat, and with T <= 16 every split-K group is one
   // group of <= 16 rows (decode-shaped calls).
   const int64_t row_bound = d.T;
-  const bool run_fat = L.can_fat && row_bound >= L.fat_rows;
-  const bool run_full = L.can_full &&
+  const bool run_fat = !decode && L.can_fat && row_bound >= L.fat_rows;
+  const bool run_full = !decode && L.can_full &&
       (q4_fmt(wdt) >= 0 ? run_fat : (double)row_bound > (double)o.splitk_max_pairs);
-  const bool run_sk1 = L.can_sk1;
-  const bool run_sk4 = L.can_sk4 && row_bound > 16;
+  const bool run_sk1 = L.can_sk1 || decode;
+  const bool run_sk4 = !decode && L.can_sk4 && row_bound > 16;
+  const int32_t* sk1_list = decode ? (const int32_t*)(pb + p->L.dlist)
+                                   : (const int32_t*)(b + L.sk1);
+  const int32_t* sk1_tok = decode ? (const int32_t*)(pb + p->L.dtok)
+                                  : (const int32_t*)(b + L.sk1_tok);
   if (run_fat) {
     PhaseScope ps(rec, 1, s);
     const int grid = info.ncu * 8;
@@ -709,11 +740,23 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       if (run_sk1) {
         // groups of <= 16 rows
         PhaseScope ps(rec, stage == 0 ? 3 : 5, s);
-        g.list = (const int32_t*)(b + L.sk1);
+        g.list = sk1_list;
         g.meta_index = kMetaSk1;
         if (L.stream) {
-          g.tok = (const int32_t*)(b + L.sk1_tok);
-          e = launch_gemm_stream(g, x_dtype, wdt, 16, stream_grid1, s);
+          g.tok = sk1_tok;
+          // a decode-shaped call has at most T k + n_shared groups: when
+          // their items fit one workgroup each on the GPU, the launch takes
+          // them whole (no partial sums, no fix-up)
+          const int64_t max_items =
+              (int64_t)std::min<int64_t>(n_exp, (int64_t)d.T * d.k + d.n_shared) *
+              (stage == 0 ? F / 64 : D / 128);
+          GemmArgs gs = g;
+          int grid = stream_grid1;
+          if (decode && max_items <= info.ncu) {
+            gs.part = nullptr;
+            grid = (int)max_items;
+          }
+          e = launch_gemm_stream(gs, x_dtype, wdt, 16, grid, s);
         } else {
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk1 * nnb, sk_rb1_grid_cap);
           e = launch_gemm_splitk(g, x_dtype, wdt, 1, grid, s);

@@ -99,12 +99,24 @@ hipError_t launch_permute(const int32_t* ids, const float* w,
                           int32_t* tok2pair, int32_t* pair_token,
                           float* pair_w, hipStream_t s);
 
+// A decode-shaped plan (at most kDecodeT tokens: every expert holds at most
+// that many pairs, one thin group each) also carries the thin-group list
+// the classify kernel would build: (expert, 0, rows, first pair) per touched
+// expert in expert order, each group's x rows (kStreamTokRows entries,
+// clamped to its last row) and the group count at dmeta[kMetaSk1].
+constexpr int kDecodeT = 16;
+struct DecodeGroups {
+  int32_t* list;   // [E + n_shared, 4]
+  int32_t* tok;    // [E + n_shared, kStreamTokRows]
+  int32_t* meta;   // [kMetaCount]
+};
 hipError_t launch_plan_small(const float* logits, int T, int E, int k,
                              int n_shared, int64_t limit, int32_t* ids,
                              float* w, int32_t* total, int32_t* counts,
                              int32_t* offsets, int64_t* stats, int32_t* slot,
                              int32_t* tok2pair, int32_t* pair_token,
-                             float* pair_w, hipStream_t s);
+                             float* pair_w, const DecodeGroups* dg,
+                             hipStream_t s);
 
 // ---- forward (forward_kernels.hip) --------------------------------------
 struct ClassifyArgs {

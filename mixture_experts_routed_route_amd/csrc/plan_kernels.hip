@@ -496,8 +496,11 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
     int32_t* __restrict__ total, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int64_t* __restrict__ stats,
     int32_t* __restrict__ slot, int32_t* __restrict__ tok2pair,
-    int32_t* __restrict__ pair_token, float* __restrict__ pair_w) {
+    int32_t* __restrict__ pair_token, float* __restrict__ pair_w,
+    DecodeGroups dg) {
   __shared__ int32_t sh_hist[kMaxExperts + 1];
+  __shared__ int32_t sh_grp[kMaxExperts + 2];   // decode: expert of group g
+  __shared__ int32_t sh_pt[kPlanSmallPairs + kDecodeT];   // decode: pair tokens
   __shared__ int32_t sh_off[kMaxExperts + 2];
   __shared__ unsigned long long mask[kMaxExperts];
   __shared__ int32_t sh_ids[kPlanSmallPairs];
@@ -545,7 +548,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
   if (max_local) atomicMax(&red[2], max_local);
   if (n_shared && threadIdx.x == 0) counts[E] = T;
   const int n = E + n_shared;
-  int carry = 0;
+  int carry = 0, gcarry = 0;
   for (int b = 0; b < n; b += blockDim.x) {
     const int e = b + threadIdx.x;
     int c = 0;
@@ -562,10 +565,31 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
       sh_off[e] = carry + pre;
     }
     carry += blk_total;
+    if (dg.list) {
+      // decode groups: one per touched expert, numbered in expert order
+      int g_total = 0;
+      const int gpre = block_scan_excl(c > 0 ? 1 : 0, &g_total, sh_waves);
+      if (e < n) {
+        const int g = gcarry + gpre;
+        if (c > 0) {
+          sh_grp[g] = e;
+          dg.list[4 * g] = e;
+          dg.list[4 * g + 1] = 0;
+          dg.list[4 * g + 2] = c;
+          dg.list[4 * g + 3] = carry - blk_total + pre;
+        }
+      }
+      gcarry += g_total;
+    }
   }
+  const int dg_groups = gcarry;
   if (threadIdx.x == 0) {
     offsets[n] = carry;
     sh_off[n] = carry;
+    if (dg.list) {
+      for (int i = 0; i < kMetaCount; ++i) dg.meta[i] = 0;
+      dg.meta[kMetaSk1] = gcarry;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -594,6 +618,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
     if (keep) {
       pair_token[pos] = tl;
       pair_w[pos] = sh_w[p];
+      if (dg.list) sh_pt[pos] = tl;
     }
   }
   if (n_shared) {
@@ -601,6 +626,19 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
     for (int tl = threadIdx.x; tl < T; tl += blockDim.x) {
       pair_token[sbase + tl] = tl;
       pair_w[sbase + tl] = 1.0f;
+      if (dg.list) sh_pt[sbase + tl] = tl;
+    }
+  }
+  if (dg.list) {
+    // each group's x rows, kStreamTokRows entries, rows past the group's
+    // last clamped to it; 64 threads a group, contiguous stores
+    __syncthreads();
+    const int ng = dg_groups;
+    for (int i = threadIdx.x; i < ng * kStreamTokRows; i += blockDim.x) {
+      const int g = i / kStreamTokRows, r = i - g * kStreamTokRows;
+      const int e = sh_grp[g];
+      const int c = sh_off[e + 1] - sh_off[e];
+      dg.tok[i] = sh_pt[sh_off[e] + min(r, c - 1)];
     }
   }
 }
@@ -610,14 +648,20 @@ hipError_t launch_plan_small(const float* logits, int T, int E, int k,
                              float* w, int32_t* total, int32_t* counts,
                              int32_t* offsets, int64_t* stats, int32_t* slot,
                              int32_t* tok2pair, int32_t* pair_token,
-                             float* pair_w, hipStream_t s) {
+                             float* pair_w, const DecodeGroups* dgp,
+                             hipStream_t s) {
   if (T < 1 || T > kChunk || (int64_t)T * k > kPlanSmallPairs || E > kPlanSmallE)
     return hipErrorInvalidValue;
+  DecodeGroups dg{nullptr, nullptr, nullptr};
+  if (dgp) {
+    if (T > kDecodeT) return hipErrorInvalidValue;
+    dg = *dgp;
+  }
   const int per = (E + 63) / 64;
 #define MOE_PLAN_SMALL(P)                                                        \
   hipLaunchKernelGGL((plan_small_kernel<P>), dim3(1), dim3(1024), 0, s, logits, T, \
                      E, k, n_shared, limit, ids, w, total, counts, offsets,     \
-                     stats, slot, tok2pair, pair_token, pair_w)
+                     stats, slot, tok2pair, pair_token, pair_w, dg)
   if (T > 16 && route_grouped(E, k)) {
     const int p16 = (E + 15) / 16;
     if (p16 <= 1) MOE_PLAN_SMALL(-1);

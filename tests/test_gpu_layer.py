@@ -103,6 +103,26 @@ def test_decode_shapes(cfg, T):
     check_layer(wl, y)
 
 
+@pytest.mark.parametrize("T", [1, 5, 16])
+@pytest.mark.parametrize("dt", [W.F32, W.F16])
+def test_decode_groups_from_plan(dt, T):
+    """Prompts of at most 16 tokens take the plan kernel's thin-group list
+    instead of the classify kernel's (every expert holds at most T pairs);
+    with a capacity cap some pairs drop, with S below T the classify kernel
+    still decides (then experts may go to the full tile): all within the
+    bar, plan bit-exact."""
+    wl = W.make_layer(T, 256, 256, 16, 4, dt, seed=80 + T, capacity_factor=1.0,
+                      n_shared=1, logit_bias=torch.linspace(1.5, -1.5, 16))
+    say(f"layer decode groups {dt} T={T}")
+    p, y = gpu_layer(wl)
+    check_plan(wl, p)
+    check_layer(wl, y)
+    if dt != W.F32:
+        p2, y2 = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=0.5,
+                                                        exact_routes=True))
+        check_layer(wl, y2)
+
+
 @pytest.mark.parametrize("exact", [False, True])
 def test_underfilled_full_route(exact):
     # the shared expert (250 rows) and a few experts of 17..256 rows: their
