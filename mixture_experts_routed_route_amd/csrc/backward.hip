@@ -407,13 +407,18 @@ __global__ __launch_bounds__(512, 1) void bgemm_dma_ic_kernel(BGemmArgs g) {
 // Also the 128-row tiles, and the padded column offsets of the
 // pair-transposed buffers: expert e's pairs at columns koff[e] .. koff[e] +
 // n_e, koff[e + 1] = koff[e] + n_e rounded up to 64 (zeros in between).
+// Also the 256-row tiles of the full tile's recompute of [G | U], heaviest
+// experts first, with its count at q256[0] and its eight work-queue
+// counters q256[8..15] zeroed.
 __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
     const int32_t* __restrict__ offsets, int n_exp, int32_t* __restrict__ tiles,
     int32_t* __restrict__ n_tiles, int32_t* __restrict__ tiles128,
     int32_t* __restrict__ n_tiles128, int32_t* __restrict__ koff,
-    int32_t* __restrict__ eord) {
+    int32_t* __restrict__ eord, int32_t* __restrict__ tiles256,
+    int32_t* __restrict__ q256) {
   __shared__ int32_t start[kMaxExperts + 2];
   __shared__ int32_t start2[kMaxExperts + 2];
+  __shared__ int32_t start3[kMaxExperts + 2];   // by rank in eord
   __shared__ int32_t kcol[kMaxExperts + 2];
   if (threadIdx.x == 0) {
     int acc = 0, acc2 = 0, col = 0;
@@ -435,11 +440,34 @@ __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
   }
   __syncthreads();
   // eord: the experts by K columns, descending, ties by index (a permutation)
+  __shared__ int32_t sh_eord[kMaxExperts + 2];
   for (int e = threadIdx.x; e < n_exp; e += blockDim.x) {
     const int ke = kcol[e];
     int rank = 0;
     for (int f = 0; f < n_exp; ++f) rank += kcol[f] > ke || (kcol[f] == ke && f < e);
     eord[rank] = e;
+    sh_eord[rank] = e;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc3 = 0;
+    for (int r = 0; r < n_exp; ++r) {
+      const int e = sh_eord[r];
+      start3[r] = acc3;
+      acc3 += (offsets[e + 1] - offsets[e] + 255) / 256;
+    }
+    start3[n_exp] = acc3;
+    q256[0] = acc3;
+  }
+  if (threadIdx.x >= 8 && threadIdx.x < 16) q256[threadIdx.x] = 0;
+  __syncthreads();
+  for (int r = threadIdx.x; r < n_exp; r += blockDim.x) {
+    const int e = sh_eord[r];
+    const int nt = start3[r + 1] - start3[r];
+    for (int i = 0; i < nt; ++i) {
+      tiles256[2 * (start3[r] + i)] = e;
+      tiles256[2 * (start3[r] + i) + 1] = i * 256;
+    }
   }
   for (int e = threadIdx.x; e < n_exp; e += blockDim.x) {
     const int nt = start[e + 1] - start[e];
@@ -661,7 +689,8 @@ size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
   return al(tiles * 8) * 2 + al(16) * 2 + al((n_exp + 1) * 4) + al(n_exp * 4) + al(Pmax * D * 2) +
          al(Pmax * 2 * F * 4) + al(Pmax * F * 2) + al(Pmax * D * 2) + al(Pmax * 4) +
          al(Pmax * F * 4) + al(Pmax * 2 * F * 2) + al(Pmax * D * 4) +
-         al(Pp * D * 2) * 2 + al(Pp * 2 * F * 2) + al(Pp * F * 2);
+         al(Pp * D * 2) * 2 + al(Pp * 2 * F * 2) + al(Pp * F * 2) +
+         al(tiles * 8) + al(64);
 }
 
 // stage 0: gather, recompute [G | U] and H; 1: dH', dG / dU and dtw_p, dXp, dx;
@@ -692,7 +721,9 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   S* Xt = reinterpret_cast<S*>(b);                       b += al(Pp * D * 2);
   S* dYt = reinterpret_cast<S*>(b);                      b += al(Pp * D * 2);
   S* dGUt = reinterpret_cast<S*>(b);                     b += al(Pp * 2 * F * 2);
-  S* Ht = reinterpret_cast<S*>(b);
+  S* Ht = reinterpret_cast<S*>(b);                       b += al(Pp * F * 2);
+  int32_t* tiles256 = reinterpret_cast<int32_t*>(b);     b += al(ntile_cap * 8);
+  int32_t* q256 = reinterpret_cast<int32_t*>(b);
 
   const int ew_grid = a.ncu * 8;
   const int ub = (int)ntile_cap;
@@ -733,15 +764,24 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const int64_t wFD = (int64_t)F * D;
   if (stage == 0) {
     hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
-                       n_exp, tiles, n_tiles, tiles128, n_tiles128, koff, eord);
+                       n_exp, tiles, n_tiles, tiles128, n_tiles128, koff, eord,
+                       tiles256, q256);
     hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
                        (const S*)a.x, a.dy, a.pair_token, a.offsets,
                        n_exp, D, Xp, dYu);
-    // [G | U] = X_p [W_gate; W_up]^T
-    per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wg, nullptr, D, 0, wFD},
-             F, D, GU, 2 * F);
-    per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wu, nullptr, D, 0, wFD},
-             F, D, GU + F, 2 * F);
+    // [G | U] = X_p [W_gate; W_up]^T on the forward's full tile (x rows
+    // gathered through the pair list, raw f32 outputs)
+    GemmArgs gf{};
+    gf.mode = 2; gf.K = D; gf.N = F;
+    gf.A = a.x; gf.a_bytes = (uint32_t)((size_t)a.T * D * 2); gf.a_ld = D;
+    gf.out = GU; gf.out_ld = 2 * F;
+    gf.pair_token = a.pair_token; gf.offsets = a.offsets; gf.pair_w = a.pair_w;
+    gf.B0 = a.wg; gf.B1 = a.wu; gf.fat_slot = nullptr;
+    gf.list = tiles256; gf.meta = q256; gf.meta_index = 0; gf.queue = q256 + 8;
+    gf.clamp = a.clamp;
+    const int full_grid = (int)std::min<int64_t>((int64_t)ntile_cap * (F / 128), a.ncu);
+    hipError_t e = launch_gemm_full(gf, a.xdt, full_grid, s);
+    if (e != hipSuccess) return e;
   } else if (stage == 1) {
     // dH' = dYu W_down (unscaled; the SwiGLU backward applies pair_w)
     per_pair(KCt{}, ICt{}, BOp{dYu, nullptr, D, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},

@@ -24,6 +24,9 @@
 // clamp from Strata PR #4366, "Approach"). Tokens are gathered on load
 // through the plan's pair list; no gathered copy of x is materialised.
 //
+// MODE 2 (the backward's recompute) loads as MODE 0 and writes the raw f32
+// G and U of every pair instead of the SwiGLU output.
+//
 // Work is persistent, one block per CU, items taken from per-XCD queues.
 // Items are tiles of the classify kernel's largest-first list crossed with
 // output-column blocks; within a round the items of one XCD (blocks b = x
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   const int ww = wave >> 2, wt = wave & 3;   // weight half, token quarter
   const int K = a.K, N = a.N;
   const int nk = K / kBK;
-  const int NNB = MODE == 0 ? N / 128 : (N + kBW - 1) / kBW;
+  const int NNB = MODE != 1 ? N / 128 : (N + kBW - 1) / kBW;
   const int n_tiles = a.meta[a.meta_index];
   const int n_items = n_tiles * NNB;
   const int G = gridDim.x;
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     if (w_wave) {
       const char* b0 = (const char*)(slot >= 0 ? a.S0 : a.B0);
       r_even = make_rsrc(b0 + eix * mat_bytes, mat_bytes);
-      if (MODE == 0) {
+      if (MODE != 1) {
         const char* b1 = (const char*)(slot >= 0 ? a.S1 : a.B1);
         r_odd = make_rsrc(b1 + eix * mat_bytes, mat_bytes);
       } else {
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         for (int jj = 0; jj < kDmaPerWave; ++jj) {
           const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;
           int row;
-          if (MODE == 0)   // 32-row blocks alternate W_gate / W_up
+          if (MODE != 1)   // 32-row blocks alternate W_gate / W_up
             row = nb * 128 + (R >> 7) * 64 + ((R >> 6) & 1) * 32 + (R & 31);
           else
             row = min(nb * kBW + R, N - 1);
@@ -222,12 +225,12 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
           const int rr = min(row0 + (Rt % BT), ne - 1);
           // x rows are gathered through the pair list; the SwiGLU output of
           // full-tile experts is k-block-major, pair rows in order
-          prow[jj] = MODE == 0 ? a.pair_token[off + rr] : off + rr;
+          prow[jj] = MODE != 1 ? a.pair_token[off + rr] : off + rr;
         }
 #pragma unroll
         for (int jj = 0; jj < kDmaPerWave; ++jj) {
           const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;
-          const uint32_t rowoff = MODE == 0 ? (uint32_t)prow[jj] * (uint32_t)a.a_ld * 2u
+          const uint32_t rowoff = MODE != 1 ? (uint32_t)prow[jj] * (uint32_t)a.a_ld * 2u
                                             : (uint32_t)prow[jj] * (uint32_t)kRowB;
           voff[jj] = rowoff + (uint32_t)((lane & 3) ^ ((R >> 2) & 3)) * 16u;
         }
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         char* base = smem + (kt % kNS) * kStage + wave * kDmaPerWave * 1024;
         const int soff = min(kt, nk - 1) * s_step;
         const __amdgpu_buffer_rsrc_t rs =
-            (MODE == 0 && ((jj >> 1) & 1)) ? r_odd : r_even;
+            (MODE != 1 && ((jj >> 1) & 1)) ? r_odd : r_even;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (lds_ptr_t)(base + jj * 1024), 16, (int)voff[jj], soff, 0, 0);
       };
@@ -394,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       const int jt = lane_e & 31;
       const int hi4 = (lane_e >> 5) * 4;
       using Y = typename YPairOf<S>::T;
-      if constexpr (MODE == 0 || sizeof(Y) == 2) {
+      if constexpr (MODE == 0 || (MODE == 1 && sizeof(Y) == 2)) {
         // Through LDS: a lane holds 4 consecutive features of one token, so
         // stores straight from the accumulators would write 16 B to each of
         // 32 rows per instruction. Each wave stages its 64 tokens x (64
@@ -494,11 +497,20 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
           for (int wi = 0; wi < 4; ++wi)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-              const int d = nb * kBW + ww * 128 + wi * 32 + rq * 8 + hi4;
-              if (d >= N) continue;
-              store_y4<Y>(a.out, prow * a.out_ld + d, acc[wi][t][rq * 4 + 0],
-                          acc[wi][t][rq * 4 + 1], acc[wi][t][rq * 4 + 2],
-                          acc[wi][t][rq * 4 + 3]);
+              if constexpr (MODE == 2) {
+                // raw G (even 32-row blocks) and U (odd) of feature f, f32:
+                // [G | U] rows of 2 N values
+                const int f = nb * 128 + ww * 64 + (wi >> 1) * 32 + rq * 8 + hi4;
+                store_y4<float>(a.out, prow * a.out_ld + f + ((wi & 1) ? N : 0),
+                                acc[wi][t][rq * 4 + 0], acc[wi][t][rq * 4 + 1],
+                                acc[wi][t][rq * 4 + 2], acc[wi][t][rq * 4 + 3]);
+              } else {
+                const int d = nb * kBW + ww * 128 + wi * 32 + rq * 8 + hi4;
+                if (d >= N) continue;
+                store_y4<Y>(a.out, prow * a.out_ld + d, acc[wi][t][rq * 4 + 0],
+                            acc[wi][t][rq * 4 + 1], acc[wi][t][rq * 4 + 2],
+                            acc[wi][t][rq * 4 + 3]);
+              }
             }
         }
       }
@@ -522,6 +534,15 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
 hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
                             hipStream_t s) {
   if (grid <= 0) return hipSuccess;
+  if (a.mode == 2) {
+    if (xdt == MOE_F16)
+      hipLaunchKernelGGL((gemm_full_kernel<F16T, 2, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+    else if (xdt == MOE_BF16)
+      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 2, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (xdt == MOE_F16) {
     if (a.mode == 0)
       hipLaunchKernelGGL((gemm_full_kernel<F16T, 0, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);

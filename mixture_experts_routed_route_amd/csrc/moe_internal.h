@@ -147,7 +147,8 @@ hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s);
 
 // Operand set of one GEMM stage (gate/up or down).
 struct GemmArgs {
-  int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down
+  int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down,
+                            // 2: gate/up raw f32 [G | U] (full tile only)
   int K, N;                 // K: reduction; N: output width (F or D)
   const void* A;            // gate/up: x [T, D]; down: H [P, F]
   const void* A2;           // down, bf16 split H: the low plane; else null
