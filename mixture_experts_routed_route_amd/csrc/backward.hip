@@ -402,83 +402,130 @@ __global__ __launch_bounds__(512, 1) void bgemm_dma_ic_kernel(BGemmArgs g) {
                g.c + crow0 * g.ldc + n0, g.ldc);
 }
 
-// (expert, first row) of every 64-row tile of the per-pair products, in
-// expert order; n_tiles receives the count.
-// Also the 128-row tiles, and the padded column offsets of the
-// pair-transposed buffers: expert e's pairs at columns koff[e] .. koff[e] +
-// n_e, koff[e + 1] = koff[e] + n_e rounded up to 64 (zeros in between).
-// Also the 256-row tiles of the full tile's recompute of [G | U], heaviest
-// experts first, with its count at q256[0] and its eight work-queue
-// counters q256[8..15] zeroed.
+// Exclusive prefix sums of v[0, n) in place, by a block of 1024 threads;
+// returns the total to every thread. wsum: 17 ints of shared memory.
+__device__ int block_scan_excl(int32_t* v, int n, int32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int C = (n + 1023) / 1024;   // items per thread, consecutive
+  int loc = 0;
+  for (int i = 0; i < C; ++i) {
+    const int e = tid * C + i;
+    if (e < n) loc += v[e];
+  }
+  int incl = loc;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int t = wsum[i];
+      wsum[i] = acc;
+      acc += t;
+    }
+    wsum[16] = acc;
+  }
+  __syncthreads();
+  int run = wsum[w] + incl - loc;
+  for (int i = 0; i < C; ++i) {
+    const int e = tid * C + i;
+    if (e < n) {
+      const int t = v[e];
+      v[e] = run;
+      run += t;
+    }
+  }
+  const int total = wsum[16];
+  __syncthreads();
+  return total;
+}
+
+// The work lists of the backward's products, one block of 1024 threads:
+//  - (expert, first row) of every 64-row tile (the transposes) and every
+//    128-row tile (dH', dX), in expert order, with their counts;
+//  - the padded column offsets of the pair-transposed buffers: expert e's
+//    pairs at columns koff[e] .. koff[e] + n_e, koff[e + 1] = koff[e] + n_e
+//    rounded up to 64 (zeros in between);
+//  - eord, the experts by padded column count, most first (ties by index);
+//  - the full tile's lists, in eord order: the 256-row pair tiles of the
+//    recompute of [G | U] (q[0] of them), and the 256-row tiles of the two
+//    weight-gradient products over every expert, m_gu = 2F rows of
+//    [dG | dU]^T (q[1] of them) and m_dn = D rows of (w dy)^T (q[2]); their
+//    work-queue counters q[8..15], q[16..23], q[24..31] are zeroed.
 __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
-    const int32_t* __restrict__ offsets, int n_exp, int32_t* __restrict__ tiles,
-    int32_t* __restrict__ n_tiles, int32_t* __restrict__ tiles128,
-    int32_t* __restrict__ n_tiles128, int32_t* __restrict__ koff,
-    int32_t* __restrict__ eord, int32_t* __restrict__ tiles256,
-    int32_t* __restrict__ q256) {
-  __shared__ int32_t start[kMaxExperts + 2];
-  __shared__ int32_t start2[kMaxExperts + 2];
-  __shared__ int32_t start3[kMaxExperts + 2];   // by rank in eord
-  __shared__ int32_t kcol[kMaxExperts + 2];
-  if (threadIdx.x == 0) {
-    int acc = 0, acc2 = 0, col = 0;
-    for (int e = 0; e < n_exp; ++e) {
-      start[e] = acc;
-      start2[e] = acc2;
-      koff[e] = col;
-      const int ne = offsets[e + 1] - offsets[e];
-      acc += (ne + kBT - 1) / kBT;
-      acc2 += (ne + 127) / 128;
-      kcol[e] = (ne + 63) & ~63;
-      col += kcol[e];
-    }
-    start[n_exp] = acc;
-    start2[n_exp] = acc2;
-    koff[n_exp] = col;
-    *n_tiles = acc;
-    *n_tiles128 = acc2;
+    const int32_t* __restrict__ offsets, int n_exp, int m_gu, int m_dn,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    int32_t* __restrict__ tiles128, int32_t* __restrict__ n_tiles128,
+    int32_t* __restrict__ koff, int32_t* __restrict__ eord,
+    int32_t* __restrict__ tiles256, int32_t* __restrict__ wl_gu,
+    int32_t* __restrict__ wl_dn, int32_t* __restrict__ q) {
+  __shared__ int32_t cnt[kMaxExperts + 2];
+  __shared__ int32_t s1[kMaxExperts + 2], s2[kMaxExperts + 2];
+  __shared__ int32_t s3[kMaxExperts + 2], s4[kMaxExperts + 2];
+  __shared__ int32_t ord[kMaxExperts + 2];
+  __shared__ int32_t wsum[17];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n_exp; e += blockDim.x) {
+    const int ne = offsets[e + 1] - offsets[e];
+    cnt[e] = ne;
+    s1[e] = (ne + kBT - 1) / kBT;
+    s2[e] = (ne + 127) / 128;
+    s3[e] = (ne + 63) & ~63;
   }
   __syncthreads();
-  // eord: the experts by K columns, descending, ties by index (a permutation)
-  __shared__ int32_t sh_eord[kMaxExperts + 2];
-  for (int e = threadIdx.x; e < n_exp; e += blockDim.x) {
-    const int ke = kcol[e];
+  const int n1 = block_scan_excl(s1, n_exp, wsum);
+  const int n2 = block_scan_excl(s2, n_exp, wsum);
+  const int ncol = block_scan_excl(s3, n_exp, wsum);
+  for (int e = tid; e < n_exp; e += blockDim.x) {
+    koff[e] = s3[e];
+    const int kc = (cnt[e] + 63) & ~63;
     int rank = 0;
-    for (int f = 0; f < n_exp; ++f) rank += kcol[f] > ke || (kcol[f] == ke && f < e);
+    for (int f = 0; f < n_exp; ++f) {
+      const int kf = (cnt[f] + 63) & ~63;
+      rank += kf > kc || (kf == kc && f < e);
+    }
     eord[rank] = e;
-    sh_eord[rank] = e;
+    ord[rank] = e;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc3 = 0;
-    for (int r = 0; r < n_exp; ++r) {
-      const int e = sh_eord[r];
-      start3[r] = acc3;
-      acc3 += (offsets[e + 1] - offsets[e] + 255) / 256;
-    }
-    start3[n_exp] = acc3;
-    q256[0] = acc3;
-  }
-  if (threadIdx.x >= 8 && threadIdx.x < 16) q256[threadIdx.x] = 0;
+  for (int r = tid; r < n_exp; r += blockDim.x) s4[r] = (cnt[ord[r]] + 255) / 256;
   __syncthreads();
-  for (int r = threadIdx.x; r < n_exp; r += blockDim.x) {
-    const int e = sh_eord[r];
-    const int nt = start3[r + 1] - start3[r];
-    for (int i = 0; i < nt; ++i) {
-      tiles256[2 * (start3[r] + i)] = e;
-      tiles256[2 * (start3[r] + i) + 1] = i * 256;
+  const int n4 = block_scan_excl(s4, n_exp, wsum);
+  if (tid == 0) {
+    koff[n_exp] = ncol;
+    *n_tiles = n1;
+    *n_tiles128 = n2;
+  }
+  const int tg = (m_gu + 255) / 256, td = (m_dn + 255) / 256;
+  if (tid < 32) q[tid] = tid == 0 ? n4 : tid == 1 ? n_exp * tg : tid == 2 ? n_exp * td : 0;
+  for (int e = tid; e < n_exp; e += blockDim.x) {
+    const int ne = cnt[e];
+    for (int i = 0; i * kBT < ne; ++i) {
+      tiles[2 * (s1[e] + i)] = e;
+      tiles[2 * (s1[e] + i) + 1] = i * kBT;
+    }
+    for (int i = 0; i * 128 < ne; ++i) {
+      tiles128[2 * (s2[e] + i)] = e;
+      tiles128[2 * (s2[e] + i) + 1] = i * 128;
     }
   }
-  for (int e = threadIdx.x; e < n_exp; e += blockDim.x) {
-    const int nt = start[e + 1] - start[e];
-    for (int i = 0; i < nt; ++i) {
-      tiles[2 * (start[e] + i)] = e;
-      tiles[2 * (start[e] + i) + 1] = i * kBT;
+  for (int r = tid; r < n_exp; r += blockDim.x) {
+    const int e = ord[r];
+    for (int i = 0; i * 256 < cnt[e]; ++i) {
+      tiles256[2 * (s4[r] + i)] = e;
+      tiles256[2 * (s4[r] + i) + 1] = i * 256;
     }
-    const int nt2 = start2[e + 1] - start2[e];
-    for (int i = 0; i < nt2; ++i) {
-      tiles128[2 * (start2[e] + i)] = e;
-      tiles128[2 * (start2[e] + i) + 1] = i * 128;
+    for (int i = 0; i < tg; ++i) {
+      wl_gu[2 * (r * tg + i)] = e;
+      wl_gu[2 * (r * tg + i) + 1] = i * 256;
+    }
+    for (int i = 0; i < td; ++i) {
+      wl_dn[2 * (r * td + i)] = e;
+      wl_dn[2 * (r * td + i) + 1] = i * 256;
     }
   }
 }
@@ -690,7 +737,9 @@ size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
          al(Pmax * 2 * F * 4) + al(Pmax * F * 2) + al(Pmax * D * 2) + al(Pmax * 4) +
          al(Pmax * F * 4) + al(Pmax * 2 * F * 2) + al(Pmax * D * 4) +
          al(Pp * D * 2) * 2 + al(Pp * 2 * F * 2) + al(Pp * F * 2) +
-         al(tiles * 8) + al(64);
+         al(tiles * 8) + al(128) +
+         al((size_t)n_exp * ((2 * F + 255) / 256) * 8) +
+         al((size_t)n_exp * ((D + 255) / 256) * 8);
 }
 
 // stage 0: gather, recompute [G | U] and H; 1: dH', dG / dU and dtw_p, dXp, dx;
@@ -723,7 +772,13 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   S* dGUt = reinterpret_cast<S*>(b);                     b += al(Pp * 2 * F * 2);
   S* Ht = reinterpret_cast<S*>(b);                       b += al(Pp * F * 2);
   int32_t* tiles256 = reinterpret_cast<int32_t*>(b);     b += al(ntile_cap * 8);
-  int32_t* q256 = reinterpret_cast<int32_t*>(b);
+  int32_t* q = reinterpret_cast<int32_t*>(b);            b += al(128);
+  int32_t* wl_gu = reinterpret_cast<int32_t*>(b);
+  b += al((size_t)n_exp * ((2 * F + 255) / 256) * 8);
+  int32_t* wl_dn = reinterpret_cast<int32_t*>(b);
+  // the full tile addresses its operands with 32-bit buffer offsets
+  const bool full_ok = (size_t)a.T * D * 2 < ((size_t)1 << 31) &&
+                       (size_t)std::max(2 * F, D) * (size_t)Pp * 2 < ((size_t)1 << 32);
 
   const int ew_grid = a.ncu * 8;
   const int ub = (int)ntile_cap;
@@ -764,24 +819,31 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const int64_t wFD = (int64_t)F * D;
   if (stage == 0) {
     hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
-                       n_exp, tiles, n_tiles, tiles128, n_tiles128, koff, eord,
-                       tiles256, q256);
+                       n_exp, 2 * F, D, tiles, n_tiles, tiles128, n_tiles128, koff,
+                       eord, tiles256, wl_gu, wl_dn, q);
     hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
                        (const S*)a.x, a.dy, a.pair_token, a.offsets,
                        n_exp, D, Xp, dYu);
     // [G | U] = X_p [W_gate; W_up]^T on the forward's full tile (x rows
     // gathered through the pair list, raw f32 outputs)
-    GemmArgs gf{};
-    gf.mode = 2; gf.K = D; gf.N = F;
-    gf.A = a.x; gf.a_bytes = (uint32_t)((size_t)a.T * D * 2); gf.a_ld = D;
-    gf.out = GU; gf.out_ld = 2 * F;
-    gf.pair_token = a.pair_token; gf.offsets = a.offsets; gf.pair_w = a.pair_w;
-    gf.B0 = a.wg; gf.B1 = a.wu; gf.fat_slot = nullptr;
-    gf.list = tiles256; gf.meta = q256; gf.meta_index = 0; gf.queue = q256 + 8;
-    gf.clamp = a.clamp;
-    const int full_grid = (int)std::min<int64_t>((int64_t)ntile_cap * (F / 128), a.ncu);
-    hipError_t e = launch_gemm_full(gf, a.xdt, full_grid, s);
-    if (e != hipSuccess) return e;
+    if (full_ok) {
+      GemmArgs gf{};
+      gf.mode = 2; gf.K = D; gf.N = F;
+      gf.A = a.x; gf.a_bytes = (uint32_t)((size_t)a.T * D * 2); gf.a_ld = D;
+      gf.out = GU; gf.out_ld = 2 * F;
+      gf.pair_token = a.pair_token; gf.offsets = a.offsets; gf.pair_w = a.pair_w;
+      gf.B0 = a.wg; gf.B1 = a.wu; gf.fat_slot = nullptr;
+      gf.list = tiles256; gf.meta = q; gf.meta_index = 0; gf.queue = q + 8;
+      gf.clamp = a.clamp;
+      const int grid = (int)std::min<int64_t>((int64_t)ntile_cap * (F / 128), a.ncu);
+      const hipError_t e = launch_gemm_full(gf, a.xdt, grid, s);
+      if (e != hipSuccess) return e;
+    } else {
+      per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wg, nullptr, D, 0, wFD},
+               F, D, GU, 2 * F);
+      per_pair(KCt{}, KCt{}, BOp{Xp, nullptr, D, 0, 0}, BOp{a.wu, nullptr, D, 0, wFD},
+               F, D, GU + F, 2 * F);
+    }
   } else if (stage == 1) {
     // dH' = dYu W_down (unscaled; the SwiGLU backward applies pair_w)
     per_pair(KCt{}, ICt{}, BOp{dYu, nullptr, D, 0, 0}, BOp{a.wd, nullptr, F, 0, wFD},
@@ -800,12 +862,34 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
     transpose(dYu, D, dYt, a.pair_w);   // dYp = pair_w dy[t], transposed
     transpose(dGU, 2 * F, dGUt, nullptr);
     transpose(H, F, Ht, nullptr);
-    weight_grad(BOp{dGUt, nullptr, (int)Pp, 0, 0}, BOp{Xt, nullptr, (int)Pp, 0, 0},
-                F, D, a.dwg);
-    weight_grad(BOp{dGUt + (size_t)F * Pp, nullptr, (int)Pp, 0, 0},
-                BOp{Xt, nullptr, (int)Pp, 0, 0}, F, D, a.dwu);
-    weight_grad(BOp{dYt, nullptr, (int)Pp, 0, 0}, BOp{Ht, nullptr, (int)Pp, 0, 0},
-                D, F, a.dwd);
+    if (full_ok) {
+      // on the full tile: 256 x 256 tiles of every expert's gradient, K =
+      // its padded pair columns, heaviest experts first
+      auto wgrad_full = [&](const S* A, int M, const S* B, int N, float* out,
+                            float* out2, int row_split, const int32_t* list,
+                            int mi, int32_t* queue) {
+        GemmArgs g{};
+        g.mode = 3; g.K = kBT; g.N = N; g.M = M; g.row_split = row_split;
+        g.A = A; g.a_bytes = (uint32_t)((size_t)M * Pp * 2); g.a_ld = (int)Pp;
+        g.B0 = B; g.b_bytes = (uint32_t)((size_t)N * Pp * 2); g.b_ld = (int)Pp;
+        // expert e's gradient: row_split rows of N at e row_split N
+        g.koff = koff; g.out = out; g.out2 = out2; g.out_estride = (int64_t)row_split * N;
+        g.list = list; g.meta = q; g.meta_index = mi; g.queue = queue;
+        const int64_t items = (int64_t)n_exp * ((M + 255) / 256) * ((N + 255) / 256);
+        return launch_gemm_full(g, a.xdt, (int)std::min<int64_t>(items, a.ncu), s);
+      };
+      hipError_t e = wgrad_full(dGUt, 2 * F, Xt, D, a.dwg, a.dwu, F, wl_gu, 1, q + 16);
+      if (e != hipSuccess) return e;
+      e = wgrad_full(dYt, D, Ht, F, a.dwd, a.dwd, D, wl_dn, 2, q + 24);
+      if (e != hipSuccess) return e;
+    } else {
+      weight_grad(BOp{dGUt, nullptr, (int)Pp, 0, 0}, BOp{Xt, nullptr, (int)Pp, 0, 0},
+                  F, D, a.dwg);
+      weight_grad(BOp{dGUt + (size_t)F * Pp, nullptr, (int)Pp, 0, 0},
+                  BOp{Xt, nullptr, (int)Pp, 0, 0}, F, D, a.dwu);
+      weight_grad(BOp{dYt, nullptr, (int)Pp, 0, 0}, BOp{Ht, nullptr, (int)Pp, 0, 0},
+                  D, F, a.dwd);
+    }
   } else if (a.dtw || a.dlogits) {
     float* dtw = a.dtw ? a.dtw : a.dtw_scratch;
     const int64_t q = (int64_t)a.T * a.k;

@@ -25,7 +25,11 @@
 // through the plan's pair list; no gathered copy of x is materialised.
 //
 // MODE 2 (the backward's recompute) loads as MODE 0 and writes the raw f32
-// G and U of every pair instead of the SwiGLU output.
+// G and U of every pair instead of the SwiGLU output. MODE 3 (the
+// backward's weight gradients) multiplies two pair-transposed operands,
+// both contiguous along the pair index: the tile's rows come from A, its
+// columns from B0, K is the item's expert's (padded) pair count, and the f32
+// result goes to the expert's gradient matrix.
 //
 // Work is persistent, one block per CU, items taken from per-XCD queues.
 // Items are tiles of the classify kernel's largest-first list crossed with
@@ -88,8 +92,9 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ww = wave >> 2, wt = wave & 3;   // weight half, token quarter
   const int K = a.K, N = a.N;
-  const int nk = K / kBK;
-  const int NNB = MODE != 1 ? N / 128 : (N + kBW - 1) / kBW;
+  const int nk0 = K / kBK;
+  constexpr bool kGU = MODE == 0 || MODE == 2;   // W_gate / W_up rows interleaved
+  const int NNB = kGU ? N / 128 : (N + kBW - 1) / kBW;
   const int n_tiles = a.meta[a.meta_index];
   const int n_items = n_tiles * NNB;
   const int G = gridDim.x;
@@ -162,8 +167,14 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     typedef const __attribute__((address_space(4))) int32_t* sconst_i32;
     const int e = ((sconst_i32)a.list)[2 * ti_];
     const int tile_row0 = ((sconst_i32)a.list)[2 * ti_ + 1];
-    const int off = ((sconst_i32)a.offsets)[e];
-    const int ne = ((sconst_i32)a.offsets)[e + 1] - off;
+    // MODE 3: the tile's rows are rows of A, not pairs; K is the expert's
+    // pair columns (none: the item writes zeros, its loads read in-bounds
+    // columns of the next expert, or the buffer's zero tail, and go unused)
+    const int off = MODE == 3 ? 0 : ((sconst_i32)a.offsets)[e];
+    const int ne = MODE == 3 ? a.M : ((sconst_i32)a.offsets)[e + 1] - off;
+    const int kc0 = MODE == 3 ? ((sconst_i32)a.koff)[e] : 0;
+    const int nk = MODE == 3 ? (((sconst_i32)a.koff)[e + 1] - kc0) / kBK : nk0;
+    const int nkl = max(nk, 1);
     const int slot = a.fat_slot ? ((sconst_i32)a.fat_slot)[e] : -1;
     const size_t eix = slot >= 0 ? (size_t)slot : (size_t)e;
     // caller weights are [N, K] rows of K; the fp16 fat copies are
@@ -175,10 +186,13 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     // waves 0..3 load the stage's 256 weight rows, waves 4..7 its token rows
     const bool w_wave = wave < kWaves / 2;
     __amdgpu_buffer_rsrc_t r_even, r_odd;   // descriptors of this wave's blocks
-    if (w_wave) {
+    if (MODE == 3 && w_wave) {
+      r_even = make_rsrc(a.B0, a.b_bytes);
+      r_odd = r_even;
+    } else if (w_wave) {
       const char* b0 = (const char*)(slot >= 0 ? a.S0 : a.B0);
       r_even = make_rsrc(b0 + eix * mat_bytes, mat_bytes);
-      if (MODE != 1) {
+      if (kGU) {
         const char* b1 = (const char*)(slot >= 0 ? a.S1 : a.B1);
         r_odd = make_rsrc(b1 + eix * mat_bytes, mat_bytes);
       } else {
@@ -209,12 +223,14 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         for (int jj = 0; jj < kDmaPerWave; ++jj) {
           const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;
           int row;
-          if (MODE != 1)   // 32-row blocks alternate W_gate / W_up
+          if (kGU)   // 32-row blocks alternate W_gate / W_up
             row = nb * 128 + (R >> 7) * 64 + ((R >> 6) & 1) * 32 + (R & 31);
           else
             row = min(nb * kBW + R, N - 1);
-          const uint32_t rowoff = tiled ? (uint32_t)row * (uint32_t)kRowB
-                                        : (uint32_t)row * (uint32_t)K * 2u;
+          const uint32_t rowoff =
+              MODE == 3 ? ((uint32_t)row * (uint32_t)a.b_ld + (uint32_t)kc0) * 2u
+              : tiled   ? (uint32_t)row * (uint32_t)kRowB
+                        : (uint32_t)row * (uint32_t)K * 2u;
           voff[jj] = rowoff + (uint32_t)((lane & 3) ^ ((R >> 2) & 3)) * 16u;
         }
       } else {
@@ -225,13 +241,15 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
           const int rr = min(row0 + (Rt % BT), ne - 1);
           // x rows are gathered through the pair list; the SwiGLU output of
           // full-tile experts is k-block-major, pair rows in order
-          prow[jj] = MODE != 1 ? a.pair_token[off + rr] : off + rr;
+          prow[jj] = kGU ? a.pair_token[off + rr] : off + rr;
         }
 #pragma unroll
         for (int jj = 0; jj < kDmaPerWave; ++jj) {
           const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;
-          const uint32_t rowoff = MODE != 1 ? (uint32_t)prow[jj] * (uint32_t)a.a_ld * 2u
-                                            : (uint32_t)prow[jj] * (uint32_t)kRowB;
+          const uint32_t rowoff =
+              MODE == 3 ? ((uint32_t)prow[jj] * (uint32_t)a.a_ld + (uint32_t)kc0) * 2u
+              : kGU     ? (uint32_t)prow[jj] * (uint32_t)a.a_ld * 2u
+                        : (uint32_t)prow[jj] * (uint32_t)kRowB;
           voff[jj] = rowoff + (uint32_t)((lane & 3) ^ ((R >> 2) & 3)) * 16u;
         }
       }
@@ -245,9 +263,9 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       auto issue_one = [&](int kt, int jj) {
         if (!LOP && BT == 128 && wave >= 6) return;   // no rows 384..511
         char* base = smem + (kt % kNS) * kStage + wave * kDmaPerWave * 1024;
-        const int soff = min(kt, nk - 1) * s_step;
+        const int soff = min(kt, nkl - 1) * s_step;
         const __amdgpu_buffer_rsrc_t rs =
-            (MODE != 1 && ((jj >> 1) & 1)) ? r_odd : r_even;
+            (kGU && ((jj >> 1) & 1)) ? r_odd : r_even;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (lds_ptr_t)(base + jj * 1024), 16, (int)voff[jj], soff, 0, 0);
       };
@@ -397,7 +415,47 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       const int jt = lane_e & 31;
       const int hi4 = (lane_e >> 5) * 4;
       using Y = typename YPairOf<S>::T;
-      if constexpr (MODE == 0 || (MODE == 1 && sizeof(Y) == 2)) {
+      if constexpr (MODE == 3) {
+        // f32 gradient rows through LDS: each 32-row block of the wave's
+        // rows (32 x 128 outputs, 16 KB) is staged row-major in the wave's
+        // 16 KB of the idle ring, 16-byte chunk c of row r at c ^ (r & 7)
+        // (the 8 rows a write phase touches hit 8 different bank groups),
+        // then written as whole 512-byte row segments, two rows a store
+        __builtin_amdgcn_s_barrier();   // every wave is done with the ring
+        char* stg = smem + wave * 16384;
+        const int col0 = nb * kBW + ww * 128;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+#pragma unroll
+          for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int c = wi * 8 + rq * 2 + (hi4 >> 2);
+              *reinterpret_cast<float4*>(stg + jt * 512 + ((c ^ (jt & 7)) << 4)) =
+                  float4{acc[wi][t][rq * 4 + 0], acc[wi][t][rq * 4 + 1],
+                         acc[wi][t][rq * 4 + 2], acc[wi][t][rq * 4 + 3]};
+            }
+          if (t == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            jn = __builtin_amdgcn_readfirstlane(j_next);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          const int c = lane_e & 31;
+          const int d = col0 + c * 4;
+#pragma unroll 4
+          for (int it = 0; it < 16; ++it) {
+            const int r = it * 2 + (lane_e >> 5);
+            const float4 v =
+                *reinterpret_cast<const float4*>(stg + r * 512 + ((c ^ (r & 7)) << 4));
+            const int trow_ = row0 + wt * TW + t * 32 + r;
+            if (trow_ >= ne || d >= N) continue;
+            const bool lo = trow_ < a.row_split;
+            float* dst = reinterpret_cast<float*>(lo ? a.out : a.out2) +
+                         (size_t)e * a.out_estride;
+            *reinterpret_cast<float4*>(dst + (size_t)(lo ? trow_ : trow_ - a.row_split) * N + d) = v;
+          }
+        }
+      } else if constexpr (MODE == 0 || (MODE == 1 && sizeof(Y) == 2)) {
         // Through LDS: a lane holds 4 consecutive features of one token, so
         // stores straight from the accumulators would write 16 B to each of
         // 32 rows per instruction. Each wave stages its 64 tokens x (64
@@ -534,13 +592,20 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
 hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
                             hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (a.mode == 2) {
-    if (xdt == MOE_F16)
-      hipLaunchKernelGGL((gemm_full_kernel<F16T, 2, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
-    else if (xdt == MOE_BF16)
-      hipLaunchKernelGGL((gemm_full_kernel<BF16T, 2, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
-    else
+  if (a.mode == 2 || a.mode == 3) {
+    if (xdt == MOE_F16) {
+      if (a.mode == 2)
+        hipLaunchKernelGGL((gemm_full_kernel<F16T, 2, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_full_kernel<F16T, 3, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+    } else if (xdt == MOE_BF16) {
+      if (a.mode == 2)
+        hipLaunchKernelGGL((gemm_full_kernel<BF16T, 2, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_full_kernel<BF16T, 3, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+    } else {
       return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   if (xdt == MOE_F16) {
