@@ -24,12 +24,22 @@
 // clamp from Strata PR #4366, "Approach"). Tokens are gathered on load
 // through the plan's pair list; no gathered copy of x is materialised.
 //
-// MODE 2 (the backward's recompute) loads as MODE 0 and writes the raw f32
-// G and U of every pair instead of the SwiGLU output. MODE 3 (the
-// backward's weight gradients) multiplies two pair-transposed operands,
-// both contiguous along the pair index: the tile's rows come from A, its
-// columns from B0, K is the item's expert's (padded) pair count, and the f32
-// result goes to the expert's gradient matrix.
+// The backward's products run on the same tile:
+//  MODE 2 (recompute) loads as MODE 0 and writes the raw f32 G and U of
+//    every pair instead of the SwiGLU output;
+//  MODE 3 (weight gradients): C_e = A_e^T B_e over the expert's pairs, A and
+//    B0 per-pair rows ([P, M], [P, N]): K is the pair index, the tile's rows
+//    are columns of A, its columns are columns of B0;
+//  MODE 4 (dH' = dY W_down) and MODE 5 (dX = [dG | dU] [W_gate; W_up]):
+//    per-pair rows of A times weights read as [K, N] (N contiguous; MODE 5's
+//    K runs over W_gate, then W_up).
+// An operand whose K index is its row index (both of MODE 3's, the weights
+// of MODES 4 and 5) is staged K-row-major, [32 K rows][256] of 512 bytes,
+// 16-byte chunk c of K row k at c ^ 2 (k & 3), and its MFMA fragments are
+// read with the transposing LDS read (ds_read_b64_tr_b16): lane i of a
+// 16-lane group names 4 values of K row i / 4, lane l receives column l of
+// the group's 4 rows. The f32 outputs of MODES 3 to 5 are staged through LDS
+// and stored as whole rows.
 //
 // Work is persistent, one block per CU, items taken from per-XCD queues.
 // Items are tiles of the classify kernel's largest-first list crossed with
@@ -46,6 +56,9 @@ namespace moe {
 namespace {
 
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) const char* lds_cptr_t;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 struct F16T { using S = _Float16; using V8 = half8; using V4 = half4v; };
@@ -94,6 +107,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   const int K = a.K, N = a.N;
   const int nk0 = K / kBK;
   constexpr bool kGU = MODE == 0 || MODE == 2;   // W_gate / W_up rows interleaved
+  constexpr bool kWIC = MODE >= 3;   // weight side staged K-row-major
+  constexpr bool kTIC = MODE == 3;   // token side staged K-row-major
   const int NNB = kGU ? N / 128 : (N + kBW - 1) / kBW;
   const int n_tiles = a.meta[a.meta_index];
   const int n_items = n_tiles * NNB;
@@ -167,13 +182,14 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     typedef const __attribute__((address_space(4))) int32_t* sconst_i32;
     const int e = ((sconst_i32)a.list)[2 * ti_];
     const int tile_row0 = ((sconst_i32)a.list)[2 * ti_ + 1];
-    // MODE 3: the tile's rows are rows of A, not pairs; K is the expert's
-    // pair columns (none: the item writes zeros, its loads read in-bounds
-    // columns of the next expert, or the buffer's zero tail, and go unused)
-    const int off = MODE == 3 ? 0 : ((sconst_i32)a.offsets)[e];
-    const int ne = MODE == 3 ? a.M : ((sconst_i32)a.offsets)[e + 1] - off;
-    const int kc0 = MODE == 3 ? ((sconst_i32)a.koff)[e] : 0;
-    const int nk = MODE == 3 ? (((sconst_i32)a.koff)[e + 1] - kc0) / kBK : nk0;
+    // MODE 3: the tile's rows are columns of A, not pairs, and K is the
+    // expert's pairs pb .. pb + np (a ragged last stage reads zeros; no
+    // pairs: the item writes zeros, its loads read zeros and go unused)
+    const int pb = ((sconst_i32)a.offsets)[e];
+    const int np = ((sconst_i32)a.offsets)[e + 1] - pb;
+    const int off = MODE == 3 ? 0 : pb;
+    const int ne = MODE == 3 ? a.M : np;
+    const int nk = MODE == 3 ? (np + kBK - 1) / kBK : nk0;
     const int nkl = max(nk, 1);
     const int slot = a.fat_slot ? ((sconst_i32)a.fat_slot)[e] : -1;
     const size_t eix = slot >= 0 ? (size_t)slot : (size_t)e;
@@ -189,6 +205,11 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     if (MODE == 3 && w_wave) {
       r_even = make_rsrc(a.B0, a.b_bytes);
       r_odd = r_even;
+    } else if (kWIC && w_wave) {
+      // MODE 4: W_down [K = D][N = F]; MODE 5: W_gate, W_up [F][N = D]
+      const uint32_t wb = (uint32_t)(MODE == 5 ? K / 2 : K) * (uint32_t)N * 2u;
+      r_even = make_rsrc((const char*)a.B0 + (size_t)e * wb, wb);
+      r_odd = MODE == 5 ? make_rsrc((const char*)a.B1 + (size_t)e * wb, wb) : r_even;
     } else if (w_wave) {
       const char* b0 = (const char*)(slot >= 0 ? a.S0 : a.B0);
       r_even = make_rsrc(b0 + eix * mat_bytes, mat_bytes);
@@ -218,7 +239,24 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       // are wave-uniform and sit outside the per-block loops, so a token
       // wave issues its four pair-list loads back to back and waits once.
       uint32_t voff[kDmaPerWave];
-      if (w_wave) {
+      // K-row-major operands: DMA block jj of this wave (its side's block
+      // b = 4 (wave % 4) + jj) holds K rows 2b and 2b + 1; the lane loads
+      // chunk (lane % 32) ^ 2 (k & 3) of K row k = 2b + lane / 32
+      auto ic_row = [&](int jj) { return 2 * ((wave & 3) * kDmaPerWave + jj) + (lane >> 5); };
+      auto ic_col = [&](int jj) { return (((lane & 31) ^ (2 * (ic_row(jj) & 3))) * 8); };
+      if (kWIC && w_wave) {
+#pragma unroll
+        for (int jj = 0; jj < kDmaPerWave; ++jj) {
+          const int col = nb * kBW + ic_col(jj);
+          const int kr = (MODE == 3 ? pb : 0) + ic_row(jj);
+          voff[jj] = ((uint32_t)kr * (uint32_t)(MODE == 3 ? a.b_ld : N) + (uint32_t)col) * 2u;
+        }
+      } else if (kTIC) {
+#pragma unroll
+        for (int jj = 0; jj < kDmaPerWave; ++jj)
+          voff[jj] = ((uint32_t)(pb + ic_row(jj)) * (uint32_t)a.a_ld +
+                      (uint32_t)(row0 + ic_col(jj))) * 2u;
+      } else if (w_wave) {
 #pragma unroll
         for (int jj = 0; jj < kDmaPerWave; ++jj) {
           const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;
@@ -227,10 +265,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
             row = nb * 128 + (R >> 7) * 64 + ((R >> 6) & 1) * 32 + (R & 31);
           else
             row = min(nb * kBW + R, N - 1);
-          const uint32_t rowoff =
-              MODE == 3 ? ((uint32_t)row * (uint32_t)a.b_ld + (uint32_t)kc0) * 2u
-              : tiled   ? (uint32_t)row * (uint32_t)kRowB
-                        : (uint32_t)row * (uint32_t)K * 2u;
+          const uint32_t rowoff = tiled ? (uint32_t)row * (uint32_t)kRowB
+                                        : (uint32_t)row * (uint32_t)K * 2u;
           voff[jj] = rowoff + (uint32_t)((lane & 3) ^ ((R >> 2) & 3)) * 16u;
         }
       } else {
@@ -246,28 +282,38 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
 #pragma unroll
         for (int jj = 0; jj < kDmaPerWave; ++jj) {
           const int R = 16 * (wave * kDmaPerWave + jj) + dma_r;
-          const uint32_t rowoff =
-              MODE == 3 ? ((uint32_t)prow[jj] * (uint32_t)a.a_ld + (uint32_t)kc0) * 2u
-              : kGU     ? (uint32_t)prow[jj] * (uint32_t)a.a_ld * 2u
-                        : (uint32_t)prow[jj] * (uint32_t)kRowB;
+          // MODE 1: the k-block-major H; else rows of a_ld values
+          const uint32_t rowoff = MODE == 1 ? (uint32_t)prow[jj] * (uint32_t)kRowB
+                                            : (uint32_t)prow[jj] * (uint32_t)a.a_ld * 2u;
           voff[jj] = rowoff + (uint32_t)((lane & 3) ^ ((R >> 2) & 3)) * 16u;
         }
       }
-      // bytes from one stage's slice of a row to the next stage's
-      const int s_step = w_wave ? (tiled ? N * kRowB : kRowB)
-                                  : (MODE == 1 ? a.h_rows * kRowB : kRowB);
+      // bytes from one stage's slice of a row to the next stage's (K-row-
+      // major operands: 32 rows further)
+      const int s_step = (kWIC && w_wave) ? kBK * (MODE == 3 ? a.b_ld : N) * 2
+                       : (kTIC && !w_wave) ? kBK * a.a_ld * 2
+                       : w_wave ? (tiled ? N * kRowB : kRowB)
+                                : (MODE == 1 ? a.h_rows * kRowB : kRowB);
       // Refill of ring stage kt. Past the last stage the slice nk-1 is read
       // again (an L2 hit) into a buffer no one reads any more, so every
       // stage issues the same number of loads and every wait below is a
       // constant count.
       auto issue_one = [&](int kt, int jj) {
-        if (!LOP && BT == 128 && wave >= 6) return;   // no rows 384..511
+        if (!kTIC && !LOP && BT == 128 && wave >= 6) return;   // no rows 384..511
         char* base = smem + (kt % kNS) * kStage + wave * kDmaPerWave * 1024;
-        const int soff = min(kt, nkl - 1) * s_step;
-        const __amdgpu_buffer_rsrc_t rs =
-            (kGU && ((jj >> 1) & 1)) ? r_odd : r_even;
+        const int kc = min(kt, nkl - 1);
+        int soff = kc * s_step;
+        __amdgpu_buffer_rsrc_t rs = (kGU && ((jj >> 1) & 1)) ? r_odd : r_even;
+        if (MODE == 5 && w_wave && kc * kBK >= (K >> 1)) {   // W_up's K rows
+          rs = r_odd;
+          soff = (kc * kBK - (K >> 1)) * N * 2;
+        }
+        uint32_t vo = voff[jj];
+        // K rows past the expert's last pair read as zeros (an offset past
+        // the descriptor's range loads 0)
+        if (MODE == 3 && kc * kBK + ic_row(jj) >= np) vo = 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_ptr_t)(base + jj * 1024), 16, (int)voff[jj], soff, 0, 0);
+            rs, (lds_ptr_t)(base + jj * 1024), 16, (int)vo, soff, 0, 0);
       };
       auto issue = [&](int kt) {
 #pragma unroll
@@ -284,19 +330,76 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
 
       // operand fragments of one 16-deep K step (hi and, for LOP, lo planes)
       struct Frag { V8 w[4]; V8 t[TB]; V8 tl[LOP ? TB : 1]; };
+      // the NF fragments of 32 columns c0 + 32 j (j < NF) of a K-row-major
+      // operand, K step ks: per fragment two transposing reads (K rows +0..3
+      // and +4..7 of the lane group's 8). In one asm block that waits for
+      // them: the compiler would put a wait for every LDS-DMA load in flight
+      // before each such read it issues itself.
+      auto rd_ic = [&](const char* base, int c0, int ks, V8* out, auto nf_c) {
+        constexpr int NF = decltype(nf_c)::value;
+        const int g = lane >> 4, i = lane & 15;
+        const int kr = ks * 16 + (g >> 1) * 8 + (i >> 2);
+        uint32_t ad[NF];
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const int col = c0 + 32 * j + (g & 1) * 16 + (i & 3) * 4;
+          const int boff = ((((col >> 3) ^ (2 * (kr & 3))) << 4) | ((col & 7) * 2));
+          ad[j] = (uint32_t)(uintptr_t)(lds_cptr_t)(base + kr * 512 + boff);
+        }
+        v4i16_t r[2 * NF];
+        if constexpr (NF == 4) {
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
+              "ds_read_b64_tr_b16 %2, %9\n\tds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
+              "ds_read_b64_tr_b16 %4, %10\n\tds_read_b64_tr_b16 %5, %10 offset:2048\n\t"
+              "ds_read_b64_tr_b16 %6, %11\n\tds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]),
+                "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+              : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+              : "memory");
+        } else if constexpr (NF == 2) {
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+              "ds_read_b64_tr_b16 %2, %5\n\tds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+              : "v"(ad[0]), "v"(ad[1])
+              : "memory");
+        } else {
+          static_assert(NF == 1, "1, 2 or 4 fragments");
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(r[0]), "=&v"(r[1])
+              : "v"(ad[0])
+              : "memory");
+        }
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const v8i16_t v = {r[2 * j][0], r[2 * j][1], r[2 * j][2], r[2 * j][3],
+                             r[2 * j + 1][0], r[2 * j + 1][1], r[2 * j + 1][2],
+                             r[2 * j + 1][3]};
+          out[j] = __builtin_bit_cast(V8, v);
+        }
+      };
       auto read_frag = [&](int kt, int ks, Frag& f) {
         const char* Ws = smem + (kt % kNS) * kStage;
         const char* Ts = Ws + kBW * kRowB;
         const int ch = ks * 2 + (lane >> 5);
+        if constexpr (kWIC) rd_ic(Ws, ww * 128, ks, f.w, std::integral_constant<int, 4>{});
+        if constexpr (kTIC) rd_ic(Ts, wt * TW, ks, f.t, std::integral_constant<int, TB>{});
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
           const int r = ww * 128 + wi * 32 + (lane & 31);
-          f.w[wi] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ws + swz64(r, ch)));
+          if constexpr (!kWIC)
+            f.w[wi] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ws + swz64(r, ch)));
         }
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
           const int r = wt * TW + t * 32 + (lane & 31);
-          f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
+          if constexpr (!kTIC)
+            f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
           if (LOP)
             f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
         }
@@ -309,14 +412,20 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         const int ch = ks * 2 + (lane >> 5);
         if (idx < 4) {
           const int r = ww * 128 + idx * 32 + (lane & 31);
-          f.w[idx] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ws + swz64(r, ch)));
+          if constexpr (kWIC) {   // all four in the first piece
+            if (idx == 0) rd_ic(Ws, ww * 128, ks, f.w, std::integral_constant<int, 4>{});
+          } else {
+            f.w[idx] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ws + swz64(r, ch)));
+          }
         } else {
           const int j = idx - 4;
           const int t = LOP ? j >> 1 : j;
           const int r = wt * TW + t * 32 + (lane & 31);
           if (LOP && (j & 1))
             f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
-          else
+          else if constexpr (kTIC) {   // all TB in the first token piece
+            if (j == 0) rd_ic(Ts, wt * TW, ks, f.t, std::integral_constant<int, TB>{});
+          } else
             f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
         }
       };
@@ -415,8 +524,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       const int jt = lane_e & 31;
       const int hi4 = (lane_e >> 5) * 4;
       using Y = typename YPairOf<S>::T;
-      if constexpr (MODE == 3) {
-        // f32 gradient rows through LDS: each 32-row block of the wave's
+      if constexpr (MODE >= 3) {
+        // f32 rows through LDS: each 32-row block of the wave's
         // rows (32 x 128 outputs, 16 KB) is staged row-major in the wave's
         // 16 KB of the idle ring, 16-byte chunk c of row r at c ^ (r & 7)
         // (the 8 rows a write phase touches hit 8 different bank groups),
@@ -449,10 +558,15 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
                 *reinterpret_cast<const float4*>(stg + r * 512 + ((c ^ (r & 7)) << 4));
             const int trow_ = row0 + wt * TW + t * 32 + r;
             if (trow_ >= ne || d >= N) continue;
-            const bool lo = trow_ < a.row_split;
-            float* dst = reinterpret_cast<float*>(lo ? a.out : a.out2) +
-                         (size_t)e * a.out_estride;
-            *reinterpret_cast<float4*>(dst + (size_t)(lo ? trow_ : trow_ - a.row_split) * N + d) = v;
+            if constexpr (MODE == 3) {   // expert e's gradient, split in two
+              const bool lo = trow_ < a.row_split;
+              float* dst = reinterpret_cast<float*>(lo ? a.out : a.out2) +
+                           (size_t)e * a.out_estride;
+              *reinterpret_cast<float4*>(dst + (size_t)(lo ? trow_ : trow_ - a.row_split) * N + d) = v;
+            } else {                     // per-pair rows
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
+                                         (size_t)(off + trow_) * a.out_ld + d) = v;
+            }
           }
         }
       } else if constexpr (MODE == 0 || (MODE == 1 && sizeof(Y) == 2)) {
@@ -592,17 +706,24 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
 hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
                             hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (a.mode == 2 || a.mode == 3) {
+  if (a.mode >= 2) {   // the backward's products
+    const dim3 g(grid), b(kWaves * 64);
     if (xdt == MOE_F16) {
-      if (a.mode == 2)
-        hipLaunchKernelGGL((gemm_full_kernel<F16T, 2, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
-      else
-        hipLaunchKernelGGL((gemm_full_kernel<F16T, 3, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+      switch (a.mode) {
+        case 2: hipLaunchKernelGGL((gemm_full_kernel<F16T, 2, 0>), g, b, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((gemm_full_kernel<F16T, 3, 0>), g, b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemm_full_kernel<F16T, 4, 0>), g, b, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((gemm_full_kernel<F16T, 5, 0>), g, b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+      }
     } else if (xdt == MOE_BF16) {
-      if (a.mode == 2)
-        hipLaunchKernelGGL((gemm_full_kernel<BF16T, 2, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
-      else
-        hipLaunchKernelGGL((gemm_full_kernel<BF16T, 3, 0>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+      switch (a.mode) {
+        case 2: hipLaunchKernelGGL((gemm_full_kernel<BF16T, 2, 0>), g, b, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((gemm_full_kernel<BF16T, 3, 0>), g, b, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemm_full_kernel<BF16T, 4, 0>), g, b, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((gemm_full_kernel<BF16T, 5, 0>), g, b, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+      }
     } else {
       return hipErrorInvalidValue;
     }

@@ -863,6 +863,16 @@ moe_status moe_backward(const moe_plan* p, const void* x, int32_t x_dtype,
   if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
   if (ws_bytes < need)
     return fail(MOE_EWORKSPACE, "backward workspace %zu bytes < %zu needed", ws_bytes, need);
+  {
+    // the products address x and the per-pair 16-bit operands with 31-bit
+    // buffer offsets
+    const size_t Pmax = (size_t)d.T * d.k + (size_t)d.n_shared * d.T;
+    const size_t lim31 = ((size_t)1 << 31) - 1;
+    if ((size_t)d.T * D * 2 > lim31 || Pmax * std::max(2 * F, D) * 2 > lim31 ||
+        (size_t)D * F * 2 > lim31)
+      return fail(MOE_EUNSUPPORTED, "x, each per-pair operand (pairs x max(2F, D) "
+                  "16-bit values) and each weight matrix must stay below 2 GiB");
+  }
   const moe_options o = opt ? *opt : defaults();
   int dev;
   DevInfo info;

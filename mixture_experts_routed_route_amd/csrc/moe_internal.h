@@ -147,9 +147,12 @@ hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s);
 
 // Operand set of one GEMM stage (gate/up or down).
 struct GemmArgs {
-  int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down,
-                            // 2: gate/up raw f32 [G | U] (full tile only),
-                            // 3: weight gradient (full tile only, below)
+  int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down; the
+                            // full tile's backward modes: 2 gate/up raw f32
+                            // [G | U], 3 weight gradient (below), 4 dH' (A
+                            // per-pair rows, B0 = W_down as [K, N]), 5 dX (A
+                            // per-pair rows, B0 / B1 = W_gate / W_up as the
+                            // two halves of K)
   int K, N;                 // K: reduction; N: output width (F or D)
   const void* A;            // gate/up: x [T, D]; down: H [P, F]
   const void* A2;           // down, bf16 split H: the low plane; else null
@@ -180,13 +183,12 @@ struct GemmArgs {
                             // reads (down)
   const int32_t* tok;       // stream tile, gate/up: the sk1 groups' x rows
   float* part;              // stream tile: [runs, 2, 2048 RB] floats
-  // Mode 3, per expert e over its pair columns koff[e] .. koff[e + 1] (a
-  // multiple of 32, zero padded) of the pair-transposed A [M, a_ld] and
-  // B0 [N, b_ld]: the f32 C_e = A_e B_e^T, rows below row_split to
-  // out + e out_estride, the rest to out2 + e out_estride (rows of N).
-  // The work list holds (expert, first row) per 256-row tile.
-  const int32_t* koff;
-  uint32_t b_bytes;         // bytes of B0: below 2^32
+  // Mode 3, per expert e over its pairs (the plan's offsets) of the per-pair
+  // A [P, M] (a_ld = M) and B0 [P, N] (b_ld = N): the f32 C_e = A_e^T B_e,
+  // rows below row_split to out + e out_estride, the rest to out2 + e
+  // out_estride (rows of N). The work list holds (expert, first row) per
+  // 256-row tile.
+  uint32_t b_bytes;         // bytes of B0: below 2^31
   int b_ld;
   int M, row_split;
   int64_t out_estride;
