@@ -51,8 +51,8 @@ KERNEL_SRC = {"gateup_full": "gemm_full.hip", "down_full": "gemm_full.hip",
               "combine": "forward_kernels.hip",
               "classify": "forward_kernels.hip",
               "router_gemm": "router.hip",
-              "bwd_weights": "backward.hip", "bwd_data": "backward.hip",
-              "bwd_recompute": "backward.hip"}
+              "bwd_weights": "gemm_full.hip", "bwd_data": "gemm_full.hip",
+              "bwd_recompute": "gemm_full.hip"}
 
 
 def parse():

@@ -326,12 +326,14 @@ size_t moe_backward_workspace_bytes(const moe_plan *plan, int32_t D, int32_t F,
  * unweighted output; 0 for a dropped pair), and d_logits [T, E], through the
  * renormalised top-k softmax (w_j (dw_j - sum_i w_i dw_i) on the chosen
  * experts, 0 elsewhere). The expert outputs are recomputed from x (nothing
- * is kept from the forward); per-pair intermediates (x rows, w dy, the
- * SwiGLU output and its gradients) are held in the layer's dtype, products
- * accumulate in f32. opt: the swiglu_limit of the forward (NULL: defaults);
- * MOE_OPT_PHASE_EVENTS times its four phases (moe_phase_times 10..13).
- * D and F multiples of 128; pointers 16-byte aligned, ws 256-byte aligned.
- * Async on `stream`. */
+ * is kept from the forward); per-pair intermediates (x rows, dy rows, w
+ * times the SwiGLU output, the SwiGLU gradients) are held in the layer's
+ * dtype, products accumulate in f32. opt: the swiglu_limit of the forward
+ * (NULL: defaults); MOE_OPT_PHASE_EVENTS times its four phases
+ * (moe_phase_times 10..13). D and F multiples of 128; pointers 16-byte
+ * aligned, ws 256-byte aligned. MOE_EUNSUPPORTED when x, a per-pair operand
+ * (T k + n_shared T pairs x max(2F, D) 16-bit values) or a weight matrix
+ * reaches 2 GiB. Async on `stream`. */
 moe_status moe_backward(const moe_plan *plan, const void *x, int32_t x_dtype,
                         moe_weight w_gate, moe_weight w_up, moe_weight w_down,
                         int32_t D, int32_t F, const float *dy, float *dx,
