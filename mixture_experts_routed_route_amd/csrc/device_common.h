@@ -88,9 +88,12 @@ __device__ __forceinline__ float swiglu(float g, float u, float c) {
 // the low and high nibbles into [v0 v1 v2 v3], [v4 v5 v6 v7], then spread
 // each byte to the low byte of a 16-bit half whose high byte v_perm takes
 // from a register of 0x64 bytes (two selects a pair, no OR).
-__device__ __forceinline__ void unpack_nibbles(uint32_t x, uint32_t out[4]) {
-  const uint32_t lo = x & 0x0F0F0F0Fu;          // v0 v2 v4 v6
-  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;   // v1 v3 v5 v7
+// flip: XORed into every isolated nibble (8 turns a two's-complement nibble
+// q into q + 8; the mask and the flip make one three-input logic op).
+__device__ __forceinline__ void unpack_nibbles(uint32_t x, uint32_t out[4],
+                                               uint32_t flip = 0u) {
+  const uint32_t lo = (x & 0x0F0F0F0Fu) ^ flip;          // v0 v2 v4 v6
+  const uint32_t hi = ((x >> 4) & 0x0F0F0F0Fu) ^ flip;   // v1 v3 v5 v7
   const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // v0 v1 v2 v3
   const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // v4 v5 v6 v7
   const uint32_t c = 0x64646464u;
@@ -102,13 +105,13 @@ __device__ __forceinline__ void unpack_nibbles(uint32_t x, uint32_t out[4]) {
 
 // 8 consecutive 4-bit values (one 32-bit word, low nibble first) times
 // their block scale, as 8 fp16: fp16 bits 0x6400 | v encode 1024 + v
-// exactly, v = nibble ^ 8; subtracting 1032 leaves the signed value q
-// exactly, and one fp16 multiply gives fp16_rne(q * s).
+// exactly, v = nibble ^ 8 = q + 8; subtracting 1032 leaves the signed value
+// q exactly, and one fp16 multiply gives fp16_rne(q * s).
 __device__ __forceinline__ half8 dequant_word(uint32_t word, _Float16 s) {
   const half2v s2 = {s, s};
   const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   uint32_t pr[4];
-  unpack_nibbles(word ^ 0x88888888u, pr);
+  unpack_nibbles(word, pr, 0x08080808u);
   half8 out;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
