@@ -260,25 +260,41 @@ __device__ __forceinline__ void dequant_fat_tiles(const DequantSet& d, int m,
   const int total = nfat * per_slot;
   const int tid = threadIdx.x;
   const int r = tid >> 2, qq = tid & 3;           // decode: row, quarter of the tile's blocks
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+  // a tile's nibbles and parameters, loaded one tile ahead: the next tile's
+  // loads are in flight while this one is decoded and stored
+  uint4 qa[BPT], qn[BPT];
+  uint32_t pa[BPT], pn[BPT];
+  auto load = [&](int w, uint4* qv, uint32_t* pv) {
     const int slot = w / per_slot;
     const int rem = w - slot * per_slot;
     const int kq = rem / rt;
     const int kb0 = kq * KB;
     const int row0 = (rem - kq * rt) * 64;
     const size_t er = (size_t)fat_list[slot] * rows + row0 + r;
-    uint4 qa[BPT];
-    uint32_t pa[BPT];
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
       const int kb = kb0 + qq * BPT + b;
-      qa[b] = *reinterpret_cast<const uint4*>(q + er * (size_t)(K / 2) + kb * 16);
+      qv[b] = *reinterpret_cast<const uint4*>(q + er * (size_t)(K / 2) + kb * 16);
       if constexpr (FMT == 0)
-        pa[b] = *reinterpret_cast<const uint16_t*>(sc + (er * (size_t)kbs + kb) * 2);
+        pv[b] = *reinterpret_cast<const uint16_t*>(sc + (er * (size_t)kbs + kb) * 2);
       else
-        pa[b] = *reinterpret_cast<const uint32_t*>(
+        pv[b] = *reinterpret_cast<const uint32_t*>(
             sc + (er * (size_t)ngr + kb * 32 / Q4F<FMT>::kGroup) * 4);
     }
+  };
+  if (blockIdx.x < total) load(blockIdx.x, qn, pn);
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int slot = w / per_slot;
+    const int rem = w - slot * per_slot;
+    const int kq = rem / rt;
+    const int kb0 = kq * KB;
+    const int row0 = (rem - kq * rt) * 64;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      qa[b] = qn[b];
+      pa[b] = pn[b];
+    }
+    if (w + (int)gridDim.x < total) load(w + gridDim.x, qn, pn);
     __syncthreads();   // the previous tile's stores have read the LDS tile
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
