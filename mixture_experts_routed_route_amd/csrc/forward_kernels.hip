@@ -303,14 +303,20 @@ __device__ __forceinline__ void dequant_fat_tiles(const DequantSet& d, int m,
       char* ta = tile + ((qq * BPT + b) * 64 + r) * 64;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(ta + i * 16) = __builtin_bit_cast(uint4, ha[i]);
+        *reinterpret_cast<uint4*>(ta + ((i ^ qq) * 16)) = __builtin_bit_cast(uint4, ha[i]);
     }
     __syncthreads();
-    // KB x 256 16-byte pieces; block kb's 64 rows are 4 KB contiguous
+    // KB x 256 16-byte pieces; block kb's 64 rows are 4 KB contiguous. In
+    // LDS, 16-byte piece c of a row of block kb sits at c ^ (kb / BPT): the
+    // four threads of a row decode blocks BPT apart, and their stores of
+    // the same piece would otherwise hit one bank group; the reads take
+    // whole rows.
     char* os = reinterpret_cast<char*>(out + (size_t)slot * rows * K);
 #pragma unroll
     for (int it = 0; it < KB; ++it) {
-      const uint4 v = *reinterpret_cast<const uint4*>(tile + (it * 256 + tid) * 16);
+      const int rr = tid >> 2, pc = tid & 3;
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          tile + ((it * 64 + rr) * 4 + (pc ^ ((it / BPT) & 3))) * 16);
       *reinterpret_cast<uint4*>(os + ((size_t)(kb0 + it) * rows + row0) * 64 + tid * 16) = v;
     }
   }
