@@ -38,7 +38,8 @@
 // 16-byte chunk c of K row k at c ^ 2 (k & 3), and its MFMA fragments are
 // read with the transposing LDS read (ds_read_b64_tr_b16): lane i of a
 // 16-lane group names 4 values of K row i / 4, lane l receives column l of
-// the group's 4 rows. The f32 outputs of MODES 3 to 5 are staged through LDS
+// the group's 4 rows. The f32 outputs of MODES 3 to 5, and MODE 1's f32
+// per-pair outputs (16-bit layers other than fp16), are staged through LDS
 // and stored as whole rows.
 //
 // Work is persistent, one block per CU, items taken from per-XCD queues.
@@ -524,7 +525,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       const int jt = lane_e & 31;
       const int hi4 = (lane_e >> 5) * 4;
       using Y = typename YPairOf<S>::T;
-      if constexpr (MODE >= 3) {
+      if constexpr (MODE >= 3 || (MODE == 1 && sizeof(Y) == 4)) {
         // f32 rows through LDS: each 32-row block of the wave's
         // rows (32 x 128 outputs, 16 KB) is staged row-major in the wave's
         // 16 KB of the idle ring, 16-byte chunk c of row r at c ^ (r & 7)
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
               float* dst = reinterpret_cast<float*>(lo ? a.out : a.out2) +
                            (size_t)e * a.out_estride;
               *reinterpret_cast<float4*>(dst + (size_t)(lo ? trow_ : trow_ - a.row_split) * N + d) = v;
-            } else {                     // per-pair rows
+            } else {                     // per-pair rows (MODE 1: Ypair)
               *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
                                          (size_t)(off + trow_) * a.out_ld + d) = v;
             }

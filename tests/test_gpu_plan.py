@@ -46,6 +46,26 @@ def test_plan_exact_pairs_per_expert(ppe):
     assert np.all(g["counts"][:128] == ppe)
 
 
+@pytest.mark.parametrize("T", [65, 128, 200, 256])
+@pytest.mark.parametrize("E,k,cf", [(64, 8, 1.0), (256, 8, 0.0), (256, 2, 1.25),
+                                    (16, 1, 2.0)])
+def test_plan_prompts_of_65_to_256_tokens(T, E, k, cf):
+    """Prompts just past the one-block plan's 64 tokens: the chunked plan's
+    slot ranks cross chunk boundaries, and with a capacity limit they
+    decide the drops (ranks counted on the histogram rows of earlier
+    chunks)."""
+    rng = np.random.default_rng(T * 7 + E + k)
+    logits = (rng.standard_normal((T, E)) +
+              1.5 * rng.standard_normal(E)).astype(np.float32)
+    wl = dict(name=f"small{T}", T=T, E=E, k=k, n_shared=int(cf == 0.0),
+              capacity_factor=cf, logits=torch.from_numpy(logits))
+    say(f"plan T={T} E={E} k={k} cf={cf}")
+    p = gpu_plan(wl)
+    g, ref, st = check_plan(wl, p)
+    if cf > 0:
+        assert st["limit"] > 0
+
+
 def _tie_heavy(T, E, rng):
     vals = np.array([-2.0, -0.0, 0.0, 0.5, 0.5, 1.0, 3.0], np.float32)
     return vals[rng.integers(0, len(vals), size=(T, E))]
