@@ -157,6 +157,31 @@ def test_backward_uneven_slots():
         close(g["d_topk_w"], ref["dtw"], "d_topk_w", dt)
 
 
+@pytest.mark.parametrize("dt", [W.BF16, W.F16])
+def test_backward_ragged_tiles(dt):
+    """d_model 384 and d_ff 640 (multiples of 128, not of 256): the last
+    256-wide block of every product's output is half outside it, and the
+    weight gradients' 256-row tiles of D rows end half empty; one expert
+    holds more than 256 pairs (two pair tiles, nine 32-pair stages), a
+    shared expert every token, and a capacity limit drops pairs."""
+    bias = torch.tensor([3.0, 0.5, 0.0, 0.0, -0.5, -1.0, -1.0, -9.0])
+    wl = W.make_layer(300, 384, 640, 8, 2, dt, seed=67, w_std=0.08,
+                      logit_bias=bias, n_shared=1, capacity_factor=3.5)
+    dy = torch.randn(300, 384, generator=torch.Generator().manual_seed(13))
+    say(f"backward ragged tiles {dt} D=384 F=640")
+    p, g = run_backward(wl, dy)
+    ref, pl = oracle_grads(wl, p, dy, 7.0)
+    counts = plan_arrays(p)["counts"]
+    assert counts[:8].max() > 256 and (pl["keep"] == 0).any()
+    slots = np.arange(9)
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        close(g[key], ref[key], key, dt)
+        close_slots(g[key], ref[key], slots, counts, key, dt)
+    close_rows(g["dx"], ref["dx"], "dx", dt)
+    close(g["d_topk_w"], ref["dtw"], "d_topk_w", dt)
+    close(g["d_logits"], ref["dlogits"], "d_logits", dt)
+
+
 def test_backward_empty_experts_get_zero_gradients():
     # 16 experts, 8 tokens top-1 with logits that favour the first four:
     # most slots hold no pair and must read zero
