@@ -51,7 +51,7 @@ KERNEL_SRC = {"gateup_full": "gemm_full.hip", "down_full": "gemm_full.hip",
               "combine": "forward_kernels.hip",
               "classify": "forward_kernels.hip",
               "router_gemm": "router.hip",
-              "bwd_weights": "gemm_full.hip", "bwd_data": "gemm_full.hip",
+              "bwd_weights": "gemm_wgrad.hip", "bwd_data": "gemm_full.hip",
               "bwd_recompute": "gemm_full.hip"}
 
 

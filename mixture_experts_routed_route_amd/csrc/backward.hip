@@ -16,14 +16,14 @@
 //   dXp  = dG W_gate + dU W_up          dx[t] = sum over its pairs (fixed order)
 //   dW_gate[e] = sum_p dG_p x_p^T,  dW_up[e] likewise,
 //   dW_down[e] = sum_p dYu_p (w H_p)^T   (w H_p rounded to the compute dtype)
-// The five products run on the forward's full tile (gemm_full.hip): 256 x 256
-// tiles of 8 waves on 32x32x16 MFMAs, operands streamed HBM -> LDS by
-// buffer_load ... lds through a four-stage ring, persistent blocks fed from
-// per-XCD work queues, the heaviest experts first. [G | U] gathers x's rows
-// through the pair list as the forward does; dH' and dX read the weights as
-// [K, N] and the weight gradients read both per-pair operands with K (the
-// pair index) as the row index, those operands staged K-row-major and read
-// with the transposing LDS read; every f32 output row is stored whole.
+// The three per-pair products run on the forward's full tile (gemm_full.hip):
+// 256 x 256 tiles of 8 waves on 32x32x16 MFMAs, operands streamed HBM -> LDS
+// by buffer_load ... lds through a four-stage ring, persistent blocks fed
+// from per-XCD work queues, the heaviest experts first. [G | U] gathers x's
+// rows through the pair list as the forward does; dH' and dX read the
+// weights as [K, N], staged K-row-major and read with the transposing LDS
+// read; every f32 output row is stored whole. The weight gradients, whose
+// reduction runs over the pairs, have their own kernel (gemm_wgrad.hip).
 #include <algorithm>
 
 #include "device_common.h"
@@ -35,9 +35,9 @@ namespace {
 struct BF16B { using S = __bf16; };
 struct F16B { using S = _Float16; };
 
-// ints of the work-queue block: list lengths at 0..2, five launches' eight
+// ints of the work-queue block: the tile count at 0, three launches' eight
 // counters from 8 on
-constexpr int kBwdQueueInts = 48;
+constexpr int kBwdQueueInts = 32;
 
 }  // namespace
 
@@ -83,18 +83,16 @@ __device__ int block_scan_excl(int32_t* v, int n, int32_t* wsum) {
   return total;
 }
 
-// The full tile's work lists, one block of 1024 threads, the experts taken
-// by pair count, most first (ties by index):
+// The work lists, one block of 1024 threads, the experts taken by pair
+// count, most first (ties by index):
+//  - eord, that order (the weight gradients' expert order);
 //  - q[0] 256-row tiles (expert, first pair row) of the per-pair products
-//    ([G | U], dH', dX);
-//  - q[1] (expert, first row) of every 256-row tile of the dW_gate / dW_up
-//    product over m_gu = 2F rows, q[2] of the dW_down product over m_dn = D
-//    rows, for every expert (an expert without pairs gets zeros);
+//    ([G | U], dH', dX) in the list tiles256;
 //  - the work-queue counters, q[8 + 8 i .. 15 + 8 i] of launch i, zeroed.
 __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
-    const int32_t* __restrict__ offsets, int n_exp, int m_gu, int m_dn,
-    int32_t* __restrict__ tiles256, int32_t* __restrict__ wl_gu,
-    int32_t* __restrict__ wl_dn, int32_t* __restrict__ q) {
+    const int32_t* __restrict__ offsets, int n_exp,
+    int32_t* __restrict__ tiles256, int32_t* __restrict__ q,
+    int32_t* __restrict__ eord) {
   __shared__ int32_t cnt[kMaxExperts + 2];
   __shared__ int32_t s4[kMaxExperts + 2];
   __shared__ int32_t ord[kMaxExperts + 2];
@@ -107,27 +105,18 @@ __global__ __launch_bounds__(1024) void bwd_tiles_kernel(
     int rank = 0;
     for (int f = 0; f < n_exp; ++f) rank += cnt[f] > c || (cnt[f] == c && f < e);
     ord[rank] = e;
+    eord[rank] = e;
   }
   __syncthreads();
   for (int r = tid; r < n_exp; r += blockDim.x) s4[r] = (cnt[ord[r]] + 255) / 256;
   __syncthreads();
   const int n4 = block_scan_excl(s4, n_exp, wsum);
-  const int tg = (m_gu + 255) / 256, td = (m_dn + 255) / 256;
-  if (tid < kBwdQueueInts)
-    q[tid] = tid == 0 ? n4 : tid == 1 ? n_exp * tg : tid == 2 ? n_exp * td : 0;
+  if (tid < kBwdQueueInts) q[tid] = tid == 0 ? n4 : 0;
   for (int r = tid; r < n_exp; r += blockDim.x) {
     const int e = ord[r];
     for (int i = 0; i * 256 < cnt[e]; ++i) {
       tiles256[2 * (s4[r] + i)] = e;
       tiles256[2 * (s4[r] + i) + 1] = i * 256;
-    }
-    for (int i = 0; i < tg; ++i) {
-      wl_gu[2 * (r * tg + i)] = e;
-      wl_gu[2 * (r * tg + i) + 1] = i * 256;
-    }
-    for (int i = 0; i < td; ++i) {
-      wl_dn[2 * (r * td + i)] = e;
-      wl_dn[2 * (r * td + i) + 1] = i * 256;
     }
   }
 }
@@ -278,16 +267,15 @@ __global__ __launch_bounds__(256) void bwd_dlogits_kernel(
 namespace {
 // byte size of each workspace region, in order
 struct BwdLayout {
-  size_t tiles256, wl_gu, wl_dn, q, Xp, GU, Hw, dYu, dtwp, dH, dGU, dXp;
+  size_t tiles256, q, eord, Xp, GU, Hw, dYu, dtwp, dH, dGU, dXp;
 };
 BwdLayout bwd_layout(int64_t Pmax, int n_exp, int D, int F) {
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t P = (size_t)Pmax;
   BwdLayout L;
   L.tiles256 = al(((P + 255) / 256 + n_exp + 1) * 8);
-  L.wl_gu = al((size_t)n_exp * ((2 * F + 255) / 256) * 8);
-  L.wl_dn = al((size_t)n_exp * ((D + 255) / 256) * 8);
   L.q = al(kBwdQueueInts * 4);
+  L.eord = al((size_t)n_exp * 4);
   L.Xp = al(P * D * 2);
   L.GU = al(P * 2 * F * 4);
   L.Hw = al(P * F * 2);
@@ -302,7 +290,7 @@ BwdLayout bwd_layout(int64_t Pmax, int n_exp, int D, int F) {
 
 size_t bwd_workspace_bytes(int64_t Pmax, int n_exp, int D, int F) {
   const BwdLayout L = bwd_layout(Pmax, n_exp, D, F);
-  return L.tiles256 + L.wl_gu + L.wl_dn + L.q + L.Xp + L.GU + L.Hw + L.dYu +
+  return L.tiles256 + L.q + L.eord + L.Xp + L.GU + L.Hw + L.dYu +
          L.dtwp + L.dH + L.dGU + L.dXp;
 }
 
@@ -316,9 +304,8 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const BwdLayout L = bwd_layout(Pm, n_exp, D, F);
   char* b = static_cast<char*>(a.ws);
   int32_t* tiles256 = reinterpret_cast<int32_t*>(b);  b += L.tiles256;
-  int32_t* wl_gu = reinterpret_cast<int32_t*>(b);     b += L.wl_gu;
-  int32_t* wl_dn = reinterpret_cast<int32_t*>(b);     b += L.wl_dn;
   int32_t* q = reinterpret_cast<int32_t*>(b);         b += L.q;
+  int32_t* eord = reinterpret_cast<int32_t*>(b);      b += L.eord;
   S* Xp = reinterpret_cast<S*>(b);                    b += L.Xp;
   float* GU = reinterpret_cast<float*>(b);            b += L.GU;
   S* Hw = reinterpret_cast<S*>(b);                    b += L.Hw;
@@ -344,24 +331,10 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
     const int64_t nnb = mode == 2 ? N / 128 : (N + 255) / 256;
     return launch_gemm_full(g, a.xdt, (int)std::min<int64_t>(tile_cap * nnb, a.ncu), s);
   };
-  // a weight gradient: expert e's C_e = A_e^T B_e over its pairs, rows
-  // below row_split to out[e], the rest to out2[e]
-  auto wgrad = [&](const S* A, int M, const S* B, int N, float* out, float* out2,
-                   int row_split, const int32_t* list, int mi, int qi) {
-    GemmArgs g{};
-    g.mode = 3; g.K = 0; g.N = N; g.M = M; g.row_split = row_split;
-    g.A = A; g.a_bytes = (uint32_t)((size_t)Pm * M * 2); g.a_ld = M;
-    g.B0 = B; g.b_bytes = (uint32_t)((size_t)Pm * N * 2); g.b_ld = N;
-    g.offsets = a.offsets; g.fat_slot = nullptr;
-    g.out = out; g.out2 = out2; g.out_estride = (int64_t)row_split * N;
-    g.list = list; g.meta = q; g.meta_index = mi; g.queue = q + 8 + 8 * qi;
-    const int64_t items = (int64_t)n_exp * ((M + 255) / 256) * ((N + 255) / 256);
-    return launch_gemm_full(g, a.xdt, (int)std::min<int64_t>(items, a.ncu), s);
-  };
   hipError_t e = hipSuccess;
   if (stage == 0) {
     hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets,
-                       n_exp, 2 * F, D, tiles256, wl_gu, wl_dn, q);
+                       n_exp, tiles256, q, eord);
     hipLaunchKernelGGL((bwd_gather_kernel<S>), dim3(ew_grid), dim3(256), 0, s,
                        (const S*)a.x, a.dy, a.pair_token, a.offsets,
                        n_exp, D, Xp, dYu);
@@ -380,10 +353,21 @@ static hipError_t run_bwd(const BwdArgs& a, int stage, hipStream_t s) {
       hipLaunchKernelGGL(bwd_dx_kernel, dim3(ew_grid), dim3(256), 0, s, dXp,
                          a.tok2pair, a.offsets, a.T, a.k, D, a.n_shared, a.E, a.dx);
   } else if (stage == 2) {
-    // weight gradients of every expert (no pairs: zeros)
-    e = wgrad(dGU, 2 * F, Xp, D, a.dwg, a.dwu, F, wl_gu, 1, 3);
+    // weight gradients of every expert (no pairs: zeros), two 128 x 256
+    // tiles a CU
+    auto wgrad2 = [&](const S* A, int M, const S* B, int N, float* out,
+                      float* out2, int row_split) {
+      WgradArgs w{};
+      w.A = A; w.a_bytes = (uint32_t)((size_t)Pm * M * 2); w.a_ld = M; w.M = M;
+      w.B = B; w.b_bytes = (uint32_t)((size_t)Pm * N * 2); w.b_ld = N; w.N = N;
+      w.offsets = a.offsets; w.eord = eord; w.n_exp = n_exp;
+      w.out = out; w.out2 = out2; w.row_split = row_split;
+      w.out_estride = (int64_t)row_split * N;
+      return launch_wgrad(w, a.xdt, s);
+    };
+    e = wgrad2(dGU, 2 * F, Xp, D, a.dwg, a.dwu, F);
     if (e != hipSuccess) return e;
-    e = wgrad(dYu, D, Hw, F, a.dwd, a.dwd, D, wl_dn, 2, 4);
+    e = wgrad2(dYu, D, Hw, F, a.dwd, a.dwd, D);
   } else if (a.dtw || a.dlogits) {
     float* dtw = a.dtw ? a.dtw : a.dtw_scratch;
     const int64_t nq = (int64_t)a.T * a.k;

@@ -27,20 +27,18 @@
 // The backward's products run on the same tile:
 //  MODE 2 (recompute) loads as MODE 0 and writes the raw f32 G and U of
 //    every pair instead of the SwiGLU output;
-//  MODE 3 (weight gradients): C_e = A_e^T B_e over the expert's pairs, A and
-//    B0 per-pair rows ([P, M], [P, N]): K is the pair index, the tile's rows
-//    are columns of A, its columns are columns of B0;
 //  MODE 4 (dH' = dY W_down) and MODE 5 (dX = [dG | dU] [W_gate; W_up]):
 //    per-pair rows of A times weights read as [K, N] (N contiguous; MODE 5's
 //    K runs over W_gate, then W_up).
-// An operand whose K index is its row index (both of MODE 3's, the weights
-// of MODES 4 and 5) is staged K-row-major, [32 K rows][256] of 512 bytes,
+// Their weights, read with the K index as the row index, are staged
+// K-row-major, [32 K rows][256] of 512 bytes,
 // 16-byte chunk c of K row k at c ^ 2 (k & 3), and its MFMA fragments are
 // read with the transposing LDS read (ds_read_b64_tr_b16): lane i of a
 // 16-lane group names 4 values of K row i / 4, lane l receives column l of
-// the group's 4 rows. The f32 outputs of MODES 3 to 5, and MODE 1's f32
+// the group's 4 rows. The f32 outputs of MODES 4 and 5, and MODE 1's f32
 // per-pair outputs (16-bit layers other than fp16), are staged through LDS
-// and stored as whole rows.
+// and stored as whole rows. (The backward's weight gradients run on their
+// own kernel, gemm_wgrad.hip.)
 //
 // Work is persistent, one block per CU, items taken from per-XCD queues.
 // Items are tiles of the classify kernel's largest-first list crossed with
@@ -106,10 +104,9 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ww = wave >> 2, wt = wave & 3;   // weight half, token quarter
   const int K = a.K, N = a.N;
-  const int nk0 = K / kBK;
+  const int nk = K / kBK;
   constexpr bool kGU = MODE == 0 || MODE == 2;   // W_gate / W_up rows interleaved
-  constexpr bool kWIC = MODE >= 3;   // weight side staged K-row-major
-  constexpr bool kTIC = MODE == 3;   // token side staged K-row-major
+  constexpr bool kWIC = MODE >= 4;   // weight side staged K-row-major
   const int NNB = kGU ? N / 128 : (N + kBW - 1) / kBW;
   const int n_tiles = a.meta[a.meta_index];
   const int n_items = n_tiles * NNB;
@@ -183,15 +180,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     typedef const __attribute__((address_space(4))) int32_t* sconst_i32;
     const int e = ((sconst_i32)a.list)[2 * ti_];
     const int tile_row0 = ((sconst_i32)a.list)[2 * ti_ + 1];
-    // MODE 3: the tile's rows are columns of A, not pairs, and K is the
-    // expert's pairs pb .. pb + np (a ragged last stage reads zeros; no
-    // pairs: the item writes zeros, its loads read zeros and go unused)
-    const int pb = ((sconst_i32)a.offsets)[e];
-    const int np = ((sconst_i32)a.offsets)[e + 1] - pb;
-    const int off = MODE == 3 ? 0 : pb;
-    const int ne = MODE == 3 ? a.M : np;
-    const int nk = MODE == 3 ? (np + kBK - 1) / kBK : nk0;
-    const int nkl = max(nk, 1);
+    const int off = ((sconst_i32)a.offsets)[e];
+    const int ne = ((sconst_i32)a.offsets)[e + 1] - off;
     const int slot = a.fat_slot ? ((sconst_i32)a.fat_slot)[e] : -1;
     const size_t eix = slot >= 0 ? (size_t)slot : (size_t)e;
     // caller weights are [N, K] rows of K; the fp16 fat copies are
@@ -203,10 +193,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
     // waves 0..3 load the stage's 256 weight rows, waves 4..7 its token rows
     const bool w_wave = wave < kWaves / 2;
     __amdgpu_buffer_rsrc_t r_even, r_odd;   // descriptors of this wave's blocks
-    if (MODE == 3 && w_wave) {
-      r_even = make_rsrc(a.B0, a.b_bytes);
-      r_odd = r_even;
-    } else if (kWIC && w_wave) {
+    if (kWIC && w_wave) {
       // MODE 4: W_down [K = D][N = F]; MODE 5: W_gate, W_up [F][N = D]
       const uint32_t wb = (uint32_t)(MODE == 5 ? K / 2 : K) * (uint32_t)N * 2u;
       r_even = make_rsrc((const char*)a.B0 + (size_t)e * wb, wb);
@@ -240,23 +227,17 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       // are wave-uniform and sit outside the per-block loops, so a token
       // wave issues its four pair-list loads back to back and waits once.
       uint32_t voff[kDmaPerWave];
-      // K-row-major operands: DMA block jj of this wave (its side's block
-      // b = 4 (wave % 4) + jj) holds K rows 2b and 2b + 1; the lane loads
-      // chunk (lane % 32) ^ 2 (k & 3) of K row k = 2b + lane / 32
+      // K-row-major weights: DMA block jj of weight wave w holds K rows 2b
+      // and 2b + 1, b = 4 w + jj; the lane loads chunk (lane % 32) ^ 2 (k & 3)
+      // of K row k = 2b + lane / 32
       auto ic_row = [&](int jj) { return 2 * ((wave & 3) * kDmaPerWave + jj) + (lane >> 5); };
       auto ic_col = [&](int jj) { return (((lane & 31) ^ (2 * (ic_row(jj) & 3))) * 8); };
       if (kWIC && w_wave) {
 #pragma unroll
         for (int jj = 0; jj < kDmaPerWave; ++jj) {
           const int col = nb * kBW + ic_col(jj);
-          const int kr = (MODE == 3 ? pb : 0) + ic_row(jj);
-          voff[jj] = ((uint32_t)kr * (uint32_t)(MODE == 3 ? a.b_ld : N) + (uint32_t)col) * 2u;
+          voff[jj] = ((uint32_t)ic_row(jj) * (uint32_t)N + (uint32_t)col) * 2u;
         }
-      } else if (kTIC) {
-#pragma unroll
-        for (int jj = 0; jj < kDmaPerWave; ++jj)
-          voff[jj] = ((uint32_t)(pb + ic_row(jj)) * (uint32_t)a.a_ld +
-                      (uint32_t)(row0 + ic_col(jj))) * 2u;
       } else if (w_wave) {
 #pragma unroll
         for (int jj = 0; jj < kDmaPerWave; ++jj) {
@@ -291,8 +272,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       }
       // bytes from one stage's slice of a row to the next stage's (K-row-
       // major operands: 32 rows further)
-      const int s_step = (kWIC && w_wave) ? kBK * (MODE == 3 ? a.b_ld : N) * 2
-                       : (kTIC && !w_wave) ? kBK * a.a_ld * 2
+      const int s_step = (kWIC && w_wave) ? kBK * N * 2
                        : w_wave ? (tiled ? N * kRowB : kRowB)
                                 : (MODE == 1 ? a.h_rows * kRowB : kRowB);
       // Refill of ring stage kt. Past the last stage the slice nk-1 is read
@@ -300,21 +280,17 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       // stage issues the same number of loads and every wait below is a
       // constant count.
       auto issue_one = [&](int kt, int jj) {
-        if (!kTIC && !LOP && BT == 128 && wave >= 6) return;   // no rows 384..511
+        if (!LOP && BT == 128 && wave >= 6) return;   // no rows 384..511
         char* base = smem + (kt % kNS) * kStage + wave * kDmaPerWave * 1024;
-        const int kc = min(kt, nkl - 1);
+        const int kc = min(kt, nk - 1);
         int soff = kc * s_step;
         __amdgpu_buffer_rsrc_t rs = (kGU && ((jj >> 1) & 1)) ? r_odd : r_even;
         if (MODE == 5 && w_wave && kc * kBK >= (K >> 1)) {   // W_up's K rows
           rs = r_odd;
           soff = (kc * kBK - (K >> 1)) * N * 2;
         }
-        uint32_t vo = voff[jj];
-        // K rows past the expert's last pair read as zeros (an offset past
-        // the descriptor's range loads 0)
-        if (MODE == 3 && kc * kBK + ic_row(jj) >= np) vo = 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_ptr_t)(base + jj * 1024), 16, (int)vo, soff, 0, 0);
+            rs, (lds_ptr_t)(base + jj * 1024), 16, (int)voff[jj], soff, 0, 0);
       };
       auto issue = [&](int kt) {
 #pragma unroll
@@ -389,7 +365,6 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
         const char* Ts = Ws + kBW * kRowB;
         const int ch = ks * 2 + (lane >> 5);
         if constexpr (kWIC) rd_ic(Ws, ww * 128, ks, f.w, std::integral_constant<int, 4>{});
-        if constexpr (kTIC) rd_ic(Ts, wt * TW, ks, f.t, std::integral_constant<int, TB>{});
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
           const int r = ww * 128 + wi * 32 + (lane & 31);
@@ -399,8 +374,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
           const int r = wt * TW + t * 32 + (lane & 31);
-          if constexpr (!kTIC)
-            f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
+          f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
           if (LOP)
             f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
         }
@@ -424,9 +398,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
           const int r = wt * TW + t * 32 + (lane & 31);
           if (LOP && (j & 1))
             f.tl[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r + BT, ch)));
-          else if constexpr (kTIC) {   // all TB in the first token piece
-            if (j == 0) rd_ic(Ts, wt * TW, ks, f.t, std::integral_constant<int, TB>{});
-          } else
+          else
             f.t[t] = __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(Ts + swz64(r, ch)));
         }
       };
@@ -525,7 +497,7 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
       const int jt = lane_e & 31;
       const int hi4 = (lane_e >> 5) * 4;
       using Y = typename YPairOf<S>::T;
-      if constexpr (MODE >= 3 || (MODE == 1 && sizeof(Y) == 4)) {
+      if constexpr (MODE >= 4 || (MODE == 1 && sizeof(Y) == 4)) {
         // f32 rows through LDS: each 32-row block of the wave's
         // rows (32 x 128 outputs, 16 KB) is staged row-major in the wave's
         // 16 KB of the idle ring, 16-byte chunk c of row r at c ^ (r & 7)
@@ -559,15 +531,8 @@ __global__ __launch_bounds__(512, 1) void gemm_full_kernel(GemmArgs a) {
                 *reinterpret_cast<const float4*>(stg + r * 512 + ((c ^ (r & 7)) << 4));
             const int trow_ = row0 + wt * TW + t * 32 + r;
             if (trow_ >= ne || d >= N) continue;
-            if constexpr (MODE == 3) {   // expert e's gradient, split in two
-              const bool lo = trow_ < a.row_split;
-              float* dst = reinterpret_cast<float*>(lo ? a.out : a.out2) +
-                           (size_t)e * a.out_estride;
-              *reinterpret_cast<float4*>(dst + (size_t)(lo ? trow_ : trow_ - a.row_split) * N + d) = v;
-            } else {                     // per-pair rows (MODE 1: Ypair)
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
-                                         (size_t)(off + trow_) * a.out_ld + d) = v;
-            }
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
+                                       (size_t)(off + trow_) * a.out_ld + d) = v;
           }
         }
       } else if constexpr (MODE == 0 || (MODE == 1 && sizeof(Y) == 2)) {
@@ -712,7 +677,6 @@ hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
     if (xdt == MOE_F16) {
       switch (a.mode) {
         case 2: hipLaunchKernelGGL((gemm_full_kernel<F16T, 2, 0>), g, b, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((gemm_full_kernel<F16T, 3, 0>), g, b, 0, s, a); break;
         case 4: hipLaunchKernelGGL((gemm_full_kernel<F16T, 4, 0>), g, b, 0, s, a); break;
         case 5: hipLaunchKernelGGL((gemm_full_kernel<F16T, 5, 0>), g, b, 0, s, a); break;
         default: return hipErrorInvalidValue;
@@ -720,7 +684,6 @@ hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
     } else if (xdt == MOE_BF16) {
       switch (a.mode) {
         case 2: hipLaunchKernelGGL((gemm_full_kernel<BF16T, 2, 0>), g, b, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((gemm_full_kernel<BF16T, 3, 0>), g, b, 0, s, a); break;
         case 4: hipLaunchKernelGGL((gemm_full_kernel<BF16T, 4, 0>), g, b, 0, s, a); break;
         case 5: hipLaunchKernelGGL((gemm_full_kernel<BF16T, 5, 0>), g, b, 0, s, a); break;
         default: return hipErrorInvalidValue;

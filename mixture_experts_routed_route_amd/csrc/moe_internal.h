@@ -149,10 +149,9 @@ hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s);
 struct GemmArgs {
   int mode;                 // 0: gate/up (+ clamped SwiGLU), 1: down; the
                             // full tile's backward modes: 2 gate/up raw f32
-                            // [G | U], 3 weight gradient (below), 4 dH' (A
-                            // per-pair rows, B0 = W_down as [K, N]), 5 dX (A
-                            // per-pair rows, B0 / B1 = W_gate / W_up as the
-                            // two halves of K)
+                            // [G | U], 4 dH' (A per-pair rows, B0 = W_down
+                            // as [K, N]), 5 dX (A per-pair rows, B0 / B1 =
+                            // W_gate / W_up as the two halves of K)
   int K, N;                 // K: reduction; N: output width (F or D)
   const void* A;            // gate/up: x [T, D]; down: H [P, F]
   const void* A2;           // down, bf16 split H: the low plane; else null
@@ -183,18 +182,25 @@ struct GemmArgs {
                             // reads (down)
   const int32_t* tok;       // stream tile, gate/up: the sk1 groups' x rows
   float* part;              // stream tile: [runs, 2, 2048 RB] floats
-  // Mode 3, per expert e over its pairs (the plan's offsets) of the per-pair
-  // A [P, M] (a_ld = M) and B0 [P, N] (b_ld = N): the f32 C_e = A_e^T B_e,
-  // rows below row_split to out + e out_estride, the rest to out2 + e
-  // out_estride (rows of N). The work list holds (expert, first row) per
-  // 256-row tile.
-  uint32_t b_bytes;         // bytes of B0: below 2^31
-  int b_ld;
-  int M, row_split;
-  int64_t out_estride;
 };
 hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
                             hipStream_t s);
+
+// Weight gradients (gemm_wgrad.hip): for every expert e (heaviest first in
+// eord), C_e = A_e^T B_e over its kept pairs offsets[e] .. offsets[e + 1] of
+// the per-pair A [P, M] (a_ld = M) and B [P, N] (b_ld = N), f32; rows below
+// row_split to out + e out_estride, the rest to out2 + e out_estride (rows
+// of N values); zeros for an expert without pairs.
+struct WgradArgs {
+  const void* A; uint32_t a_bytes; int a_ld; int M;   // bytes below 2^31
+  const void* B; uint32_t b_bytes; int b_ld; int N;
+  const int32_t* offsets;
+  const int32_t* eord;
+  int n_exp;
+  float* out; float* out2; int row_split;
+  int64_t out_estride;
+};
+hipError_t launch_wgrad(const WgradArgs& a, int xdt, hipStream_t s);
 hipError_t launch_gemm_splitk(const GemmArgs& a, int xdt, int wdt, int rb,
                               int grid, hipStream_t s);
 bool stream_supported(int mode, int K, int N, int wdt);

@@ -155,6 +155,20 @@ def test_full_tile_row_counts(dt):
     check_layer(wl, y)
 
 
+@pytest.mark.parametrize("dt", [W.F16, W.BF16])
+def test_full_tile_ragged_widths(dt):
+    """d_model 384 and d_ff 640 on the full tile: the last 256-wide block
+    of the down projection's outputs (and, for bf16, of the f32 rows it
+    writes through LDS) is half outside d_model; every token checked."""
+    bias = torch.linspace(2.0, -2.0, 8)
+    wl = W.make_layer(400, 384, 640, 8, 2, dt, seed=73, logit_bias=bias)
+    say(f"layer full tile D=384 F=640 {dt}")
+    p, y = gpu_layer(wl, options=moe.make_options(splitk_max_pairs=0.0,
+                                                  exact_routes=True))
+    check_plan(wl, p)
+    check_layer(wl, y)
+
+
 @pytest.mark.parametrize("ppe", [1, 3, 4, 8])
 @pytest.mark.parametrize("S", [0.0, 1e9])
 def test_pairs_per_expert_both_tiles(ppe, S):
