@@ -218,7 +218,8 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
     a.meta[kMetaSk4] = c4;
     a.meta[kMetaFat] = cf;
   }
-  if (threadIdx.x >= kMetaQueueGateUp && threadIdx.x < kMetaCount) a.meta[threadIdx.x] = 0;
+  for (int i = kMetaQueueGateUp + threadIdx.x; i < kMetaCount; i += blockDim.x)
+    a.meta[i] = 0;
 }
 
 hipError_t launch_classify(const ClassifyArgs& a, hipStream_t s) {

@@ -10,9 +10,18 @@
 //    weight rows: 64 gate + 64 up features, or 128 down rows). The units of
 //    one launch are cut into equal contiguous runs, one per workgroup, so
 //    every CU streams the same number of bytes whatever the item count.
-//    An item cut by a run boundary leaves fp32 partial sums in the
-//    workspace; a fix-up kernel adds them in run order (deterministic) and
-//    runs the epilogue.
+//    An item cut by run boundaries leaves fp32 partial sums in the
+//    workspace, one per run; per wave, each run then counts its arrival on
+//    the item's counter, and the wave that arrives last adds the partials
+//    in run order (deterministic: the same sums whoever arrives last) and
+//    runs the epilogue, then zeroes the counter for the next launch. The
+//    runs of one item may sit on different XCDs, whose L2s are not coherent
+//    with each other: the partials are written and read with agent-scope
+//    accesses (sc1: through to the coherent side of the L2s), and each wave
+//    waits for its partial stores to complete before it counts. An
+//    agent-scope release / acquire fence pair would do the same by writing
+//    back and invalidating the whole L2 at every arrival, which cost more
+//    than the separate fix-up launch it replaces.
 //  * Each workgroup keeps an LDS ring of stages filled by direct-to-LDS
 //    buffer loads (no register staging). A stage holds 128 weight rows of
 //    256 contiguous bytes (128 bf16/fp16 values) and the group's 16 * RB
@@ -41,6 +50,10 @@ namespace moe {
 namespace {
 
 typedef const __attribute__((address_space(4))) int32_t* sconst_i32;
+
+// Fewest units a run takes (the short prompts ran 2-8 % faster with 2 than
+// with 4 or 8: their 17..64-row launches hold a few hundred units)
+constexpr int kStreamMinUnits = 2;
 
 constexpr int kLdsBytes = 163840;
 
@@ -121,9 +134,69 @@ __device__ __forceinline__ void stream_store(const GemmArgs& a,
 __device__ __forceinline__ int run_start(int U, int b, int G) {
   return (int)((int64_t)U * b / G);
 }
+// Partial sums cross XCDs: agent-scope stores and loads (sc1), which the
+// L2s do not keep to themselves.
+__device__ __forceinline__ void part_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float part_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// the two partial-sum slots of run b: 0 for an item the run starts in, 1
+// for the item it ends in (when that is another one)
+__device__ __forceinline__ float* part_slot(const GemmArgs& a, int b, int slot, int RB) {
+  return a.part + ((size_t)b * 2 + slot) * (size_t)(kStreamSlotFloats1 * RB);
+}
 // the run holding unit u: largest b with run_start(b) <= u
 __device__ __forceinline__ int run_of(int U, int u, int G) {
   return (int)(((int64_t)(u + 1) * G - 1) / U);
+}
+
+// The partial sums of item's runs j0 .. bl (this wave's share), added in
+// run order, then the epilogue. Runs are read UR at a time, all loads
+// before the first add (one round trip for UR runs, not one each).
+template <class S, int MODE, int RB>
+__device__ __forceinline__ void fixup_item(const GemmArgs& a, int U, int G,
+                                           int item, int j0, int bl, int nb,
+                                           int nrows, int pstart, int wave,
+                                           int lane) {
+  const int nk = a.K / 128;
+  const int tid = wave * 64 + lane;
+  floatx4 acc[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    acc[rb][0] = acc[rb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  constexpr int UR = RB == 1 ? 8 : 4;
+  for (int rn0 = j0; rn0 <= bl; rn0 += UR) {
+    float v[UR][RB][8];
+    bool live[UR];
+#pragma unroll
+    for (int q = 0; q < UR; ++q) {
+      const int rn = min(rn0 + q, bl);
+      const int s0 = run_start(U, rn, G);
+      // past bl, or a run without units (a launch of more runs than units)
+      live[q] = rn0 + q <= bl && s0 != run_start(U, rn + 1, G);
+      // the run starts inside the item (slot 0) or before it (slot 1)
+      const int slot = s0 / nk == item ? 0 : 1;
+      const float* pp = part_slot(a, rn, slot, RB);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) v[q][rb][r] = part_load(pp + (rb * 8 + r) * 256 + tid);
+    }
+#pragma unroll
+    for (int q = 0; q < UR; ++q) {
+      if (!live[q]) continue;   // wave-uniform
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[rb][0][r] += v[q][rb][r];
+          acc[rb][1][r] += v[q][rb][4 + r];
+        }
+    }
+  }
+  stream_store<S, MODE, RB>(a, acc, nb, nrows, pstart, wave, lane);
 }
 
 }  // namespace
@@ -146,7 +219,12 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs a) {
   const int nk = K / Gm::BK;
   const int NNB = MODE == 0 ? N / 64 : N / 128;
   const int U = a.meta[a.meta_index] * NNB * nk;   // below 2^31 (host check)
-  const int G = gridDim.x, b = blockIdx.x;
+  // runs of at least kStreamMinUnits units (fewer runs than workgroups when
+  // the launch holds little work: every cut item's last run reads one
+  // partial per run of the item)
+  const int G = a.part ? min((int)gridDim.x, max(1, U / kStreamMinUnits)) : (int)gridDim.x;
+  const int b = blockIdx.x;
+  if (b >= G) return;   // whole block
   // a.part null: the launch has a workgroup for every item there can be,
   // and workgroup b takes item b whole (no partial sums, no fix-up)
   const int u0 = a.part ? run_start(U, b, G) : min(U, b * nk);
@@ -276,6 +354,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs a) {
   for (int p = 0; p < NS - 1; ++p) issue(min(u0 + p, u1 - 1), p);
 
   int cmp_item = -1, c_nb = 0, c_nrows = 0, c_pstart = 0;
+  int pend[2] = {-1, -1};   // cut items this run left partials of (slot 0, 1)
   for (int u = u0; u < u1; ++u) {
     const int j = u - u0;
     wait_vmcnt<(NS - 2) * nI>();    // unit u landed (this wave's share)
@@ -298,14 +377,15 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs a) {
       if (whole) {
         stream_store<S, MODE, RB>(a, acc, c_nb, c_nrows, c_pstart, wave, lane);
       } else {
-        float* pp = a.part + ((size_t)b * 2 + (item == first_item ? 0 : 1)) * (kStreamSlotFloats1 * RB);
+        float* pp = part_slot(a, b, item == first_item ? 0 : 1, RB);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            pp[(rb * 8 + r) * 256 + tid] = acc[rb][0][r];
-            pp[(rb * 8 + 4 + r) * 256 + tid] = acc[rb][1][r];
+            part_store(pp + (rb * 8 + r) * 256 + tid, acc[rb][0][r]);
+            part_store(pp + (rb * 8 + 4 + r) * 256 + tid, acc[rb][1][r]);
           }
+        pend[item == first_item ? 0 : 1] = item;
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -314,66 +394,34 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt<0>();   // no direct-to-LDS write outlives the workgroup
-}
 
-// Items cut by run boundaries: the partial sums of their runs, added in run
-// order, then the same epilogue. Block j looks at the boundary after run j
-// and handles the item only if j is the item's first run.
-template <class TT, int RB, int MODE>
-__global__ __launch_bounds__(256) void gemm_stream_fixup_kernel(GemmArgs a, int G) {
-  using S = typename TT::S;
-  using Gm = Geo<RB, 0>;
-  const int nk = a.K / Gm::BK;
-  const int NNB = MODE == 0 ? a.N / 64 : a.N / 128;
-  const int U = a.meta[a.meta_index] * NNB * nk;
-  const int j = blockIdx.x;
-  if (j + 1 >= G || U == 0) return;
-  const int v = run_start(U, j + 1, G);
-  if (v >= U || v % nk == 0) return;
-  const int item = v / nk;
-  const int fu = item * nk;
-  if (run_of(U, fu, G) != j) return;
-  const int bl = run_of(U, fu + nk - 1, G);
-  const int tid = threadIdx.x;
-  floatx4 acc[RB][2];
+  // Arrivals on the cut items, after the run (a fence drains every load in
+  // flight, so none sits inside the stream). Runs j0 .. bl hold an item's
+  // nk units, j0 the one holding its first unit: a cut item is the last
+  // item of that run, so no two cut items share it. The counter of (j0,
+  // wave) adds up the units each run did; the run whose units complete nk
+  // arrives last.
+  if (pend[0] >= 0 || pend[1] >= 0) {
+    // the wait above also saw this wave's partial stores complete
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-    acc[rb][0] = acc[rb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // The runs of one item are read UR at a time, all loads before the first
-  // add (a run's partials are a few KB from L2: one round trip for UR runs,
-  // not one each), and added in run order.
-  constexpr int UR = RB == 1 ? 8 : 4;
-  for (int rn0 = j; rn0 <= bl; rn0 += UR) {
-    float v[UR][RB][8];
-    bool live[UR];
-#pragma unroll
-    for (int q = 0; q < UR; ++q) {
-      const int rn = rn0 + q;
-      const int s0 = run_start(U, rn, G);
-      // past the item's last run, or an empty run: nothing to add
-      live[q] = rn <= bl && s0 != run_start(U, rn + 1, G);
-      const int slot = s0 / nk == item ? 0 : 1;
-      const float* pp = a.part + ((size_t)(live[q] ? rn : j) * 2 + slot) * (kStreamSlotFloats1 * RB);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) v[q][rb][r] = pp[(rb * 8 + r) * 256 + tid];
-    }
-#pragma unroll
-    for (int q = 0; q < UR; ++q) {
-      if (!live[q]) continue;   // block-uniform
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[rb][0][r] += v[q][rb][r];
-          acc[rb][1][r] += v[q][rb][4 + r];
-        }
+    for (int i = 0; i < 2; ++i) {
+      const int item = pend[i];
+      if (item < 0) continue;
+      const int fu = item * nk;
+      const int j0 = run_of(U, fu, G), bl = run_of(U, fu + nk - 1, G);
+      const int mine = min(u1, fu + nk) - max(u0, fu);
+      int32_t* cnt = a.fix + 4 * j0 + wave;
+      int old = 0;
+      if (lane == 0) old = atomicAdd(cnt, mine);
+      old = __builtin_amdgcn_readfirstlane(old);
+      if (old + mine != nk) continue;   // wave-uniform
+      const sconst_i32 Lc = (sconst_i32)a.list;
+      const int g = item / NNB;
+      fixup_item<S, MODE, RB>(a, U, G, item, j0, bl, item - g * NNB,
+                              Lc[4 * g + 2], Lc[4 * g + 3], wave, lane);
+      if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  const int g = item / NNB;
-  stream_store<S, MODE, RB>(a, acc, item - g * NNB, a.list[4 * g + 2],
-                            a.list[4 * g + 3], tid >> 6, tid & 63);
 }
 
 bool stream_supported(int mode, int K, int N, int wdt) {
@@ -384,20 +432,12 @@ bool stream_supported(int mode, int K, int N, int wdt) {
 
 template <class TT, int RB>
 static hipError_t stream_launch(const GemmArgs& a, int grid, hipStream_t s) {
-  // without partial-sum slots every workgroup takes one whole item: no
-  // fix-up pass
-  if (a.mode == 0) {
+  if (a.mode == 0)
     hipLaunchKernelGGL((gemm_stream_kernel<TT, RB, 0, 0>), dim3(grid), dim3(256), 0, s, a);
-    if (a.part)
-      hipLaunchKernelGGL((gemm_stream_fixup_kernel<TT, RB, 0>), dim3(grid), dim3(256), 0, s, a, grid);
-  } else {
-    if (a.A2)
-      hipLaunchKernelGGL((gemm_stream_kernel<TT, RB, 1, 1>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_stream_kernel<TT, RB, 1, 0>), dim3(grid), dim3(256), 0, s, a);
-    if (a.part)
-      hipLaunchKernelGGL((gemm_stream_fixup_kernel<TT, RB, 1>), dim3(grid), dim3(256), 0, s, a, grid);
-  }
+  else if (a.A2)
+    hipLaunchKernelGGL((gemm_stream_kernel<TT, RB, 1, 1>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_stream_kernel<TT, RB, 1, 0>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -414,7 +454,8 @@ hipError_t launch_gemm_stream(const GemmArgs& a, int xdt, int wdt, int rows,
                               int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (rows < 1 || rows > kStreamTokRows ||
-      (a.part && grid > stream_max_runs(rows <= 16 ? 1 : 4)))
+      (a.part && (grid > stream_max_runs(rows <= 16 ? 1 : 4) ||
+                  grid > kStreamMaxRuns || !a.fix)))
     return hipErrorInvalidValue;
   if (xdt == MOE_BF16 && wdt == MOE_BF16) return stream_rb<SBF16>(a, rows, grid, s);
   if (xdt == MOE_F16 && wdt == MOE_F16) return stream_rb<SF16>(a, rows, grid, s);

@@ -734,6 +734,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       const int nnb = stage == 0 ? F / 32 : D / 64;
       if (L.stream) {
         g.part = (float*)(b + L.part);
+        g.fix = meta + kMetaFix;
       }
       const int stream_grid1 = std::min(info.ncu, stream_max_runs(1));
       const int stream_grid4 = std::min(info.ncu, stream_max_runs(4));

@@ -53,7 +53,13 @@ constexpr int kSkRows = 64;   // rows per split-K group (4 blocks of 16)
 constexpr int kStreamSlotFloats1 = 2048;          // per 16-row block
 constexpr int kStreamPartFloats = 2 * 2048 * 2048;
 constexpr int kStreamTokRows = 64;
-inline int stream_max_runs(int rb) { return kStreamPartFloats / (2 * kStreamSlotFloats1 * rb); }
+// At most this many runs a launch: the arrival counters of the items cut by
+// run boundaries are kept per (run, wave).
+constexpr int kStreamMaxRuns = 512;
+inline int stream_max_runs(int rb) {
+  const int by_part = kStreamPartFloats / (2 * kStreamSlotFloats1 * rb);
+  return by_part < kStreamMaxRuns ? by_part : kStreamMaxRuns;
+}
 
 // The format of a 4-bit weight dtype: 0 signed with an fp16 scale per 32
 // K values, 1 / 2 affine with an fp16 (scale, bias) pair per 32 / 64; -1 if
@@ -66,12 +72,14 @@ inline int q4_fmt(int wdt) {
 enum Route : int32_t { kRouteNone = 0, kRouteSplitK = 1, kRouteFull = 2,
                        kRouteFat = 3 };
 
-// Forward meta counters written by the classify kernel.
-// Counters 8..15 and 16..23 are the full tile's work queues (one per XCD)
-// of the gate/up and the down launch; the classify kernel zeroes them.
+// Forward meta counters written by the classify kernel (or, for a
+// decode-shaped plan, by the plan kernel). Counters 8..15 and 16..23 are the
+// full tile's work queues (one per XCD) of the gate/up and the down launch;
+// from 32 on, the stream tile's arrival counters, 4 per run; the classify
+// (plan) kernel zeroes them all, and the stream tile leaves its own at zero.
 enum Meta : int32_t { kMetaFullTiles = 0, kMetaSk1 = 1, kMetaSk4 = 2,
                       kMetaFat = 3, kMetaQueueGateUp = 8, kMetaQueueDown = 16,
-                      kMetaCount = 24 };
+                      kMetaFix = 32, kMetaCount = kMetaFix + 4 * kStreamMaxRuns };
 
 // Router GEMM: prompts of at most kRouterDotT tokens (and fp32 inputs) take
 // the dot-product kernel; longer ones the MFMA tile, 128 x 128 when that
@@ -182,6 +190,9 @@ struct GemmArgs {
                             // reads (down)
   const int32_t* tok;       // stream tile, gate/up: the sk1 groups' x rows
   float* part;              // stream tile: [runs, 2, 2048 RB] floats
+  int32_t* fix;             // stream tile: [runs, 4] arrival counters of the
+                            // items cut by run boundaries (zero on entry,
+                            // left at zero)
 };
 hipError_t launch_gemm_full(const GemmArgs& a, int xdt, int grid,
                             hipStream_t s);

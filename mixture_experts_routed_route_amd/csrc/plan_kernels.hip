@@ -586,11 +586,11 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
   if (threadIdx.x == 0) {
     offsets[n] = carry;
     sh_off[n] = carry;
-    if (dg.list) {
-      for (int i = 0; i < kMetaCount; ++i) dg.meta[i] = 0;
-      dg.meta[kMetaSk1] = gcarry;
-    }
+    if (dg.list) dg.meta[kMetaSk1] = gcarry;
   }
+  if (dg.list)
+    for (int i = threadIdx.x; i < kMetaCount; i += blockDim.x)
+      if (i != kMetaSk1) dg.meta[i] = 0;
   __syncthreads();
   if (threadIdx.x == 0) {
     stats[0] = (int64_t)T * k - red[0];   // dropped
