@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (K more steps, each after "
                          "a 1 GiB write that evicts L2 and the 256 MB MALL)")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="MOE_OPT_ONE_STREAM: every launch on the caller's "
+                         "stream (no second stream for the thin groups)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph pass (plan + forward captured once "
                          "into a HIP graph, K replays timed)")
@@ -146,8 +149,10 @@ def main():
     # an explicit switch point is applied exactly (the sweep of the switch
     # point compares the two tiles at every size)
     exact = args.splitk_max_pairs is not None
+    one = moe.MOE_OPT_ONE_STREAM if args.one_stream else 0
     opts = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
                             fat_rows=args.fat_rows, exact_routes=exact)
+    opts.flags |= one
     if not args.no_phase_events:
         opts.flags |= moe.MOE_OPT_PHASE_EVENTS
 
@@ -186,6 +191,21 @@ def main():
     phase_ms, calls = ((None, 0) if args.no_phase_events
                        else moe.moe_phase_times(reset=True))
 
+    # Per-phase times with every launch on one stream (outside the timed
+    # region): in the timed steps the thin groups' launches run on the
+    # library's second stream beside the full tiles, so their event spans
+    # there include waiting for compute units; each phase's roofline
+    # fraction comes from this pass, where phases run one after another.
+    solo_ms, solo_calls = None, 0
+    if phase_ms and not args.one_stream:
+        o_solo = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
+                                  fat_rows=args.fat_rows, exact_routes=exact)
+        o_solo.flags |= moe.MOE_OPT_ONE_STREAM | moe.MOE_OPT_PHASE_EVENTS
+        for _ in range(min(args.steps, 10)):
+            step(o_solo)
+        torch.cuda.synchronize()
+        solo_ms, solo_calls = moe.moe_phase_times(reset=True)
+
     # Cold-cache pass (outside the timed region above): each step follows
     # a 1 GiB write, so x, the weights and the plan start in HBM, not in L2
     # or the MALL; HIP events on the stream the library runs on time each
@@ -194,6 +214,7 @@ def main():
     if not args.no_cold:
         o_cold = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
                                   fat_rows=args.fat_rows, exact_routes=exact)
+        o_cold.flags |= one
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         evs = [(torch.cuda.Event(enable_timing=True),
                 torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -217,6 +238,7 @@ def main():
     if not args.no_graph:
         o_g = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
                                fat_rows=args.fat_rows, exact_routes=exact)
+        o_g.flags |= one
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(side):
@@ -278,20 +300,34 @@ def main():
     routes = None
     if phase_ms:
         per = {name: v / max(calls, 1) for name, v in phase_ms.items()}
+        solo = ({name: v / max(solo_calls, 1) for name, v in solo_ms.items()}
+                if solo_ms else per)
         routes = {}
         for name, (bound, amount, extra) in phase_units.items():
-            ms = per.get(name, 0.0)
+            ms = solo.get(name, 0.0)
             if ms <= 0 or amount <= 0:
                 continue
             routes[name] = roofline_entry(bound, amount, ms, wl["x_dtype"], extra)
-        dom = max((n for n in per if per[n] > 0), key=lambda n: per[n])
-        if dom in routes:
-            roofline = dict(kernel=dom, **routes[dom])
+        # the dominant kernel, timed in the steps themselves; the thin
+        # phases of a layer with full-tile experts ran on the second stream
+        # there, their spans stretched by the full tiles beside them
+        thin = {"gateup_thin16", "down_thin16", "gateup_thin64", "down_thin64"}
+        main = [n for n in per if per[n] > 0 and n not in thin]
+        if not any(n in ("gateup_full", "down_full") for n in main):
+            main = [n for n in per if per[n] > 0]
+        dom = max(main, key=lambda n: per[n])
+        if dom in phase_units and phase_units[dom][1] > 0:
+            bound, amount, extra = phase_units[dom]
+            roofline = dict(kernel=dom, **roofline_entry(bound, amount, per[dom],
+                                                         wl["x_dtype"], extra))
             roofline["traffic"] = load_traffic(wl["name"], dom)
-            roofline["algorithmic_per_launch"] = phase_units[dom][1]
+            roofline["algorithmic_per_launch"] = amount
             roofline["avg_launch_ms"] = round(per[dom], 4)
             roofline["phase_ms_per_step"] = {n: round(v, 4) for n, v in per.items()
                                              if v > 0}
+            if solo_ms:
+                roofline["phase_ms_per_step_one_stream"] = {
+                    n: round(v, 4) for n, v in solo.items() if v > 0}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
@@ -324,6 +360,9 @@ def main():
                          "splitk_max_pairs": S, "fat_rows": fat_rows},
         "roofline": roofline,
         "routes": routes,
+        "routes_timing": (None if routes is None else
+                          "each phase alone, every launch on one stream (a "
+                          "pass of its own)" if solo_ms else "the timed steps"),
         "cold": cold,
         "graph": graph,
         "cpu_baseline": cpu,

@@ -120,7 +120,16 @@ typedef struct {
  *                     within 2e-2 x RMS(ref). MOE_OPT_BF16_SPLIT_H forces
  *                     the pair, MOE_OPT_BF16_PLAIN_H the one value (with
  *                     both set, the pair).
- *                     MOE_OPT_EXACT_ROUTES applies the S rule alone. */
+ *                     MOE_OPT_EXACT_ROUTES applies the S rule alone.
+ *                     By default a prompt with experts on both sides runs
+ *                     its thin-group launches on a second stream of the
+ *                     same device, owned by the library (default priority),
+ *                     forked from `stream` after the route classification
+ *                     and joined back before the combine, so they overlap
+ *                     the fat experts' dequantisation and full tiles; the
+ *                     call still orders after earlier work on `stream` and
+ *                     before later work on it. MOE_OPT_ONE_STREAM keeps
+ *                     every launch on `stream`. */
 typedef struct {
     float swiglu_limit;
     float splitk_max_pairs;
@@ -132,6 +141,7 @@ typedef struct {
 #define MOE_OPT_BF16_PLAIN_H 2
 #define MOE_OPT_EXACT_ROUTES 4
 #define MOE_OPT_BF16_SPLIT_H 8
+#define MOE_OPT_ONE_STREAM 16
 
 /* One weight tensor. `scales` is NULL unless dtype is a 4-bit format; then
  * it is 4-byte aligned (MOE_Q4B32) or 8-byte aligned (the affine formats):

@@ -39,6 +39,7 @@ MOE_OPT_PHASE_EVENTS = 1
 MOE_OPT_BF16_PLAIN_H = 2
 MOE_OPT_EXACT_ROUTES = 4
 MOE_OPT_BF16_SPLIT_H = 8
+MOE_OPT_ONE_STREAM = 16
 MOE_N_PHASES = 16
 PHASES = ("classify", "dequant_once", "gateup_full", "gateup_thin16",
           "down_full", "down_thin16", "combine", "router_gemm", "route_plan",

@@ -156,6 +156,43 @@ moe_status device_info(int* dev, DevInfo* info) {
   return MOE_OK;
 }
 
+// ---- the forward's second stream ------------------------------------------
+//
+// Per device: a non-blocking stream at the default priority and the two
+// events that fork it from the caller's stream and join it back. The mutex
+// is held from the fork to the join of one call, so calls from several
+// host threads do not interleave their records of the events.
+constexpr double kForkMinWork = 2147483648.0;   // T k D F, 2^31
+
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+std::mutex g_side_mu;
+std::vector<SideStream*> g_side;   // never freed: lives as long as the process
+
+SideStream* side_stream(int dev, moe_status* st) {
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if ((int)g_side.size() <= dev) g_side.resize(dev + 1, nullptr);
+  if (!g_side[dev]) {
+    SideStream* ss = new SideStream;
+    hipError_t e = hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss->join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      *st = hip_fail(e, "second stream");
+      if (ss->join) hipEventDestroy(ss->join);
+      if (ss->fork) hipEventDestroy(ss->fork);
+      if (ss->s) hipStreamDestroy(ss->s);
+      delete ss;
+      return nullptr;
+    }
+    g_side[dev] = ss;
+  }
+  return g_side[dev];
+}
+
 // ---- phase events ---------------------------------------------------------
 
 struct PhaseRecord {
@@ -660,6 +697,29 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       (q4_fmt(wdt) >= 0 ? run_fat : (double)row_bound > (double)o.splitk_max_pairs);
   const bool run_sk1 = L.can_sk1 || decode;
   const bool run_sk4 = !decode && L.can_sk4 && row_bound > 16;
+  // Thin groups beside fat / full ones: their launches (weight-stream or
+  // decode bound) run on the second stream, overlapping the dequantisation
+  // and the full tiles, whose buffers they do not touch (they write H and
+  // Ypair rows of their own pairs only). The fork and the join cost about
+  // 20 us of dependency latency, so small layers stay on one stream: at
+  // most T k D F = 2^31 multiply-adds a product (the skewed 2048-token
+  // layer, 2^31, lost 23 us; the 4096-token prefill layer, 2^35.6, gained
+  // 24 us).
+  const bool fork = !(o.flags & MOE_OPT_ONE_STREAM) && (run_fat || run_full) &&
+                    (run_sk1 || run_sk4) &&
+                    (double)d.T * d.k * D * F > kForkMinWork;
+  SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  hipStream_t ts = s;   // the thin launches' stream
+  if (fork) {
+    side = side_stream(dev, &st);
+    if (!side) return st;
+    side_lock = std::unique_lock<std::mutex>(side->mu);
+    e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "fork of the second stream");
+    ts = side->s;
+  }
   const int32_t* sk1_list = decode ? (const int32_t*)(pb + p->L.dlist)
                                    : (const int32_t*)(b + L.sk1);
   const int32_t* sk1_tok = decode ? (const int32_t*)(pb + p->L.dtok)
@@ -740,7 +800,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       const int stream_grid4 = std::min(info.ncu, stream_max_runs(4));
       if (run_sk1) {
         // groups of <= 16 rows
-        PhaseScope ps(rec, stage == 0 ? 3 : 5, s);
+        PhaseScope ps(rec, stage == 0 ? 3 : 5, ts);
         g.list = sk1_list;
         g.meta_index = kMetaSk1;
         if (L.stream) {
@@ -757,35 +817,40 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
             gs.part = nullptr;
             grid = (int)max_items;
           }
-          e = launch_gemm_stream(gs, x_dtype, wdt, 16, grid, s);
+          e = launch_gemm_stream(gs, x_dtype, wdt, 16, grid, ts);
         } else {
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk1 * nnb, sk_rb1_grid_cap);
-          e = launch_gemm_splitk(g, x_dtype, wdt, 1, grid, s);
+          e = launch_gemm_splitk(g, x_dtype, wdt, 1, grid, ts);
         }
         if (e != hipSuccess) return hip_fail(e, "split-K kernel");
       }
       if (run_sk4) {
         // groups of 17..64 rows
-        PhaseScope ps(rec, stage == 0 ? 14 : 15, s);
+        PhaseScope ps(rec, stage == 0 ? 14 : 15, ts);
         g.list = (const int32_t*)(b + L.sk4);
         g.meta_index = kMetaSk4;
         if (x_dtype == MOE_F32) {
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * nnb, sk_rb4_grid_cap);
-          e = launch_gemm_splitk(g, x_dtype, wdt, 4, grid, s);
+          e = launch_gemm_splitk(g, x_dtype, wdt, 4, grid, ts);
         } else if (L.stream) {
           g.tok = (const int32_t*)(b + L.sk4_tok);
-          e = launch_gemm_stream(g, x_dtype, wdt, kStreamTokRows, stream_grid4, s);
+          e = launch_gemm_stream(g, x_dtype, wdt, kStreamTokRows, stream_grid4, ts);
         } else {
           // wide fused-dequant tile, 256 columns per item
           const int wnb = stage == 0 ? (F + 127) / 128 : (D + 255) / 256;
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * wnb, info.ncu * 2);
-          e = launch_gemm_wide(g, x_dtype, wdt, grid, s);
+          e = launch_gemm_wide(g, x_dtype, wdt, grid, ts);
         }
         if (e != hipSuccess) return hip_fail(e, "split-K kernel");
       }
     }
   }
   {
+    if (fork) {
+      e = hipEventRecord(side->join, ts);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+      if (e != hipSuccess) return hip_fail(e, "join of the second stream");
+    }
     PhaseScope ps(rec, 6, s);
     e = launch_combine(Y, x_dtype == MOE_F16, (const int32_t*)(pb + p->L.tok2pair),
                        (const float*)(pb + p->L.w),

@@ -318,6 +318,25 @@ def test_deterministic_and_routes_agree():
         assert torch.equal(va[key], vb[key])
 
 
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_second_stream_matches_one_stream(cfg):
+    """The thin groups' launches on the library's second stream (forked
+    after the classification, joined before the combine) give the same
+    bits as every launch on the caller's stream: the same kernels on
+    disjoint rows, with the join ordering the combine after both."""
+    wl = W.config(cfg)
+    say(f"second stream vs one stream {wl['name']}")
+    p = gpu_plan(wl)
+    x = wl["x"].cuda()
+    w = [to_dev(wl[n]) for n in ("w_gate", "w_up", "w_down")]
+    two = moe.moe_forward(p, x, *w)
+    one = moe.moe_forward(p, x, *w, options=moe.make_options(flags=moe.MOE_OPT_ONE_STREAM))
+    two_again = moe.moe_forward(p, x, *w)
+    torch.cuda.synchronize()
+    assert torch.equal(two, one)
+    assert torch.equal(two, two_again)
+
+
 def test_swiglu_clamp_binds_and_matches():
     """Large weights so |g| > 7 often: the clamp decides the output."""
     wl = W.make_layer(96, 128, 256, 4, 2, W.F32, seed=27, w_std=0.9)
