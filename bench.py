@@ -308,15 +308,18 @@ def main():
             if ms <= 0 or amount <= 0:
                 continue
             routes[name] = roofline_entry(bound, amount, ms, wl["x_dtype"], extra)
-        # the dominant kernel, timed in the steps themselves; the thin
-        # phases of a layer with full-tile experts ran on the second stream
+        # the dominant kernel, timed in the steps themselves; where the
+        # library forked its second stream (its rule, restated: thin groups
+        # beside full-tile ones, T k D F above 2^31) the thin phases ran
         # there, their spans stretched by the full tiles beside them
         thin = {"gateup_thin16", "down_thin16", "gateup_thin64", "down_thin64"}
-        main = [n for n in per if per[n] > 0 and n not in thin]
-        if not any(n in ("gateup_full", "down_full") for n in main):
-            main = [n for n in per if per[n] > 0]
-        dom = max(main, key=lambda n: per[n])
-        if dom in phase_units and phase_units[dom][1] > 0:
+        forked = (not args.one_stream and T * k * D * F > 2 ** 31
+                  and any(per.get(n, 0) > 0 for n in ("gateup_full", "down_full"))
+                  and any(per.get(n, 0) > 0 for n in thin))
+        cand = [n for n in per if per[n] > 0 and n in phase_units
+                and not (forked and n in thin)]
+        dom = max(cand, key=lambda n: per[n]) if cand else None
+        if dom is not None and phase_units[dom][1] > 0:
             bound, amount, extra = phase_units[dom]
             roofline = dict(kernel=dom, **roofline_entry(bound, amount, per[dom],
                                                          wl["x_dtype"], extra))
