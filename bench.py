@@ -310,14 +310,14 @@ def main():
             routes[name] = roofline_entry(bound, amount, ms, wl["x_dtype"], extra)
         # the dominant kernel, timed in the steps themselves; where the
         # library forked its second stream (its rule, restated: thin groups
-        # beside full-tile ones, T k D F above 2^31) the thin phases ran
+        # beside full-tile ones, T k D F above 2^33) the thin phases ran
         # there, their spans stretched by the full tiles beside them
         thin = {"gateup_thin16", "down_thin16", "gateup_thin64", "down_thin64"}
-        forked = (not args.one_stream and T * k * D * F > 2 ** 31
+        forked = (not args.one_stream and T * k * D * F > 2 ** 33
                   and any(per.get(n, 0) > 0 for n in ("gateup_full", "down_full"))
                   and any(per.get(n, 0) > 0 for n in thin))
         cand = [n for n in per if per[n] > 0 and n in phase_units
-                and not (forked and n in thin)]
+                and phase_units[n][1] > 0 and not (forked and n in thin)]
         dom = max(cand, key=lambda n: per[n]) if cand else None
         if dom is not None and phase_units[dom][1] > 0:
             bound, amount, extra = phase_units[dom]

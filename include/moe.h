@@ -121,15 +121,16 @@ typedef struct {
  *                     the pair, MOE_OPT_BF16_PLAIN_H the one value (with
  *                     both set, the pair).
  *                     MOE_OPT_EXACT_ROUTES applies the S rule alone.
- *                     By default a prompt with experts on both sides runs
- *                     its thin-group launches on a second stream of the
- *                     same device, owned by the library (default priority),
- *                     forked from `stream` after the route classification
- *                     and joined back before the combine, so they overlap
- *                     the fat experts' dequantisation and full tiles; the
- *                     call still orders after earlier work on `stream` and
- *                     before later work on it. MOE_OPT_ONE_STREAM keeps
- *                     every launch on `stream`. */
+ *                     By default a prompt with experts on both sides and
+ *                     T k D F above 2^33 runs its thin-group launches on a
+ *                     second stream of the same device, owned by the
+ *                     library (default priority), forked from `stream`
+ *                     after the route classification and joined back
+ *                     before the combine, so they overlap the fat experts'
+ *                     dequantisation and full tiles; the call still orders
+ *                     after earlier work on `stream` and before later work
+ *                     on it. MOE_OPT_ONE_STREAM keeps every launch on
+ *                     `stream`. */
 typedef struct {
     float swiglu_limit;
     float splitk_max_pairs;

@@ -162,7 +162,7 @@ moe_status device_info(int* dev, DevInfo* info) {
 // events that fork it from the caller's stream and join it back. The mutex
 // is held from the fork to the join of one call, so calls from several
 // host threads do not interleave their records of the events.
-constexpr double kForkMinWork = 2147483648.0;   // T k D F, 2^31
+constexpr double kForkMinWork = 8589934592.0;   // T k D F, 2^33
 
 struct SideStream {
   hipStream_t s = nullptr;
@@ -702,9 +702,10 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   // and the full tiles, whose buffers they do not touch (they write H and
   // Ypair rows of their own pairs only). The fork and the join cost about
   // 20 us of dependency latency, so small layers stay on one stream: at
-  // most T k D F = 2^31 multiply-adds a product (the skewed 2048-token
+  // most T k D F = 2^33 multiply-adds a product (the skewed 2048-token
   // layer, 2^31, lost 23 us; the 4096-token prefill layer, 2^35.6, gained
-  // 24 us).
+  // 24 us; a short prompt whose full route the classify kernel empties
+  // pays the fork for nothing).
   const bool fork = !(o.flags & MOE_OPT_ONE_STREAM) && (run_fat || run_full) &&
                     (run_sk1 || run_sk4) &&
                     (double)d.T * d.k * D * F > kForkMinWork;
