@@ -21,7 +21,9 @@ extern "C" {
  * (loaded with the library, held until the process ends); the caller still
  * passes the plan, x, the weights and y, and everything else follows
  * moe_forward. It allocates no device memory and calls no allocating
- * routine: MOE_OPT_PHASE_EVENTS is ignored (recording would create events).
+ * routine: MOE_OPT_PHASE_EVENTS is ignored (recording would create events)
+ * and every launch stays on `stream`, as with MOE_OPT_ONE_STREAM (the
+ * second stream of moe_forward is created on its first use).
  * A call whose moe_forward_workspace_bytes exceeds the scratch returns
  * MOE_EWORKSPACE before any launch (decode-shaped calls and short prompts
  * fit: the 128-token prompt over 128 experts of d_model 2048 / d_ff 768

@@ -45,7 +45,8 @@ extern "C" moe_status moe_forward_noalloc(const moe_plan* plan, const void* x,
   moe_options o;
   if (opt) o = *opt;
   else moe_options_default(&o);
-  o.flags &= ~MOE_OPT_PHASE_EVENTS;
+  o.flags &= ~MOE_OPT_PHASE_EVENTS;   // recording would create events
+  o.flags |= MOE_OPT_ONE_STREAM;      // the second stream is created on first use
   // the size query validates the plan, sizes and dtypes and names the cause
   const size_t need = moe_forward_workspace_bytes(plan, D, F, x_dtype,
                                                   w_gate.dtype, &o);
