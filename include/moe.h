@@ -129,8 +129,10 @@ typedef struct {
  *                     before the combine, so they overlap the fat experts'
  *                     dequantisation and full tiles; the call still orders
  *                     after earlier work on `stream` and before later work
- *                     on it. MOE_OPT_ONE_STREAM keeps every launch on
- *                     `stream`. */
+ *                     on it; the first such call on a device creates the
+ *                     stream and two events (under graph capture, make it
+ *                     before capturing). MOE_OPT_ONE_STREAM keeps every
+ *                     launch on `stream`. */
 typedef struct {
     float swiglu_limit;
     float splitk_max_pairs;
