@@ -277,6 +277,22 @@ def test_thin_tiles_few_groups(dt, T):
     check_layer(wl, y)
 
 
+@pytest.mark.parametrize("T,E,k", [(20, 16, 2), (40, 4, 2)])
+def test_stream_tile_cut_items_many_runs(T, E, k):
+    """Prompts just past the decode shape on few experts with d_model 2048:
+    a stream launch holds a few hundred to a few thousand units (16 a
+    128-row item), cut into runs of at least two, so an item spans 2 to 8
+    runs and the run that arrives last adds that many partial sums inside
+    the launch (the shared expert's 20 rows at T = 20: one group of 17..64
+    rows, 12 items over 96 runs of two units); groups of <= 16 rows (one
+    16-row block) and of 17..64 rows (four); the same bits run to run."""
+    wl = W.make_layer(T, 2048, 768, E, k, W.BF16, seed=60 + T, n_shared=1)
+    say(f"stream tile, items over many runs, T={T} E={E}")
+    p, y = gpu_layer(wl)
+    check_layer(wl, y)
+    assert torch.equal(y, gpu_layer(wl)[1])
+
+
 def test_edge_empty_prompt():
     wl = W.make_layer(0, 128, 128, 4, 2, W.BF16, seed=25)
     p, y = gpu_layer(wl)
