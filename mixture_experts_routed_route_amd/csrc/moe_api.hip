@@ -712,6 +712,20 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   SideStream* side = nullptr;
   std::unique_lock<std::mutex> side_lock;
   hipStream_t ts = s;   // the thin launches' stream
+  // joins the second stream back into `stream` on every way out, errors
+  // included, so nothing the call launched outlives it on `stream`'s order
+  struct Join {
+    SideStream* side = nullptr;
+    hipStream_t s = nullptr;
+    hipError_t run() {
+      if (!side) return hipSuccess;
+      hipError_t e = hipEventRecord(side->join, side->s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+      side = nullptr;
+      return e;
+    }
+    ~Join() { run(); }
+  } join;
   if (fork) {
     side = side_stream(dev, &st);
     if (!side) return st;
@@ -720,6 +734,8 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
     if (e != hipSuccess) return hip_fail(e, "fork of the second stream");
     ts = side->s;
+    join.side = side;
+    join.s = s;
   }
   const int32_t* sk1_list = decode ? (const int32_t*)(pb + p->L.dlist)
                                    : (const int32_t*)(b + L.sk1);
@@ -847,11 +863,8 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     }
   }
   {
-    if (fork) {
-      e = hipEventRecord(side->join, ts);
-      if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
-      if (e != hipSuccess) return hip_fail(e, "join of the second stream");
-    }
+    e = join.run();
+    if (e != hipSuccess) return hip_fail(e, "join of the second stream");
     PhaseScope ps(rec, 6, s);
     e = launch_combine(Y, x_dtype == MOE_F16, (const int32_t*)(pb + p->L.tok2pair),
                        (const float*)(pb + p->L.w),
