@@ -150,12 +150,14 @@ def main():
     # point compares the two tiles at every size)
     exact = args.splitk_max_pairs is not None
     one = moe.MOE_OPT_ONE_STREAM if args.one_stream else 0
-    opts = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
-                            fat_rows=args.fat_rows, exact_routes=exact)
-    opts.flags |= one
-    if not args.no_phase_events:
-        opts.flags |= moe.MOE_OPT_PHASE_EVENTS
 
+    def options(flags=0):
+        o = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
+                             fat_rows=args.fat_rows, exact_routes=exact)
+        o.flags |= one | flags
+        return o
+
+    opts = options()
     plan_ws = torch.empty(moe.moe_plan_workspace_bytes(T, E, k,
                                                        wl["capacity_factor"], ns),
                           dtype=torch.uint8, device=dev)
@@ -169,105 +171,21 @@ def main():
                          dtype=torch.uint8, device=dev)
     y = torch.empty(T, D, dtype=torch.float32, device=dev)
 
-    def step(o=None):
+    def step(o):
         pl = moe.moe_plan_create(logits, k, wl["capacity_factor"], ns,
                                  workspace=plan_ws)
-        moe.moe_forward(pl, x, wg, wu, wd, options=opts if o is None else o,
-                        out=y, workspace=fwd_ws)
+        moe.moe_forward(pl, x, wg, wu, wd, options=o, out=y, workspace=fwd_ws)
         return pl
 
     copy_calibration(args, torch, dev)
     for _ in range(args.warmup):
-        step()
+        pl = step(opts)
     torch.cuda.synchronize()
-    moe.moe_phase_times(reset=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        pl = step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    phase_ms, calls = ((None, 0) if args.no_phase_events
-                       else moe.moe_phase_times(reset=True))
-
-    # Per-phase times with every launch on one stream (outside the timed
-    # region): in the timed steps the thin groups' launches run on the
-    # library's second stream beside the full tiles, so their event spans
-    # there include waiting for compute units; each phase's roofline
-    # fraction comes from this pass, where phases run one after another.
-    solo_ms, solo_calls = None, 0
-    if phase_ms and not args.one_stream:
-        o_solo = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
-                                  fat_rows=args.fat_rows, exact_routes=exact)
-        o_solo.flags |= moe.MOE_OPT_ONE_STREAM | moe.MOE_OPT_PHASE_EVENTS
-        for _ in range(min(args.steps, 10)):
-            step(o_solo)
-        torch.cuda.synchronize()
-        solo_ms, solo_calls = moe.moe_phase_times(reset=True)
-
-    # Cold-cache pass (outside the timed region above): each step follows
-    # a 1 GiB write, so x, the weights and the plan start in HBM, not in L2
-    # or the MALL; HIP events on the stream the library runs on time each
-    # step alone.
-    cold = None
-    if not args.no_cold:
-        o_cold = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
-                                  fat_rows=args.fat_rows, exact_routes=exact)
-        o_cold.flags |= one
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        evs = [(torch.cuda.Event(enable_timing=True),
-                torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for i, (ea, eb) in enumerate(evs):
-            flush.fill_(i & 255)
-            ea.record()
-            step(o_cold)
-            eb.record()
-        torch.cuda.synchronize()
-        ts = sorted(ea.elapsed_time(eb) for ea, eb in evs)
-        cold = {"median_ms": round(ts[len(ts) // 2], 4), "min_ms": round(ts[0], 4),
-                "steps": len(ts),
-                "method": "1 GiB written before each step; HIP events per step"}
-        del flush
-
-    # Graph pass (outside the timed region above): one step captured into a
-    # HIP graph and replayed, so the host's per-call work (argument checks,
-    # launches) is paid once; what remains is the kernels and the gaps
-    # between them. Short prompts and decode calls are launch-bound.
-    graph = None
-    if not args.no_graph:
-        o_g = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,
-                               fat_rows=args.fat_rows, exact_routes=exact)
-        o_g.flags |= one
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(side):
-            step(o_g)
-        torch.cuda.current_stream(dev).wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(o_g)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
-        torch.cuda.synchronize()
-        gms = (time.perf_counter() - t0) * 1e3 / args.steps
-        graph = {"ms_per_step": round(gms, 4), "replays": args.steps,
-                 "method": "plan + forward captured once (torch.cuda.CUDAGraph "
-                           "on the library's stream), replays timed back to back"}
-        del g
 
     # routing facts of this workload (one host read, outside the timing)
     st = moe.moe_plan_stats_get(pl, opts)
     counts = moe.moe_plan_get_views(pl)["counts"].cpu().numpy().astype(np.int64)
     kept_pairs = int(counts.sum())                       # shared included
-    flops = W.flops_per_pair(D, F) * kept_pairs
-    tflops = flops / (ms_per_step * 1e-3) / 1e12
-    pairs_s = kept_pairs / (ms_per_step * 1e-3)
     touched = int((counts > 0).sum())
 
     # routes per expert (the library's rule, restated for accounting)
@@ -296,41 +214,121 @@ def main():
     rows_full = int(counts[full_mask].sum())
     phase_units = route_units(counts, full_mask, sk_mask, D, F, wl, T, kept_pairs)
 
-    roofline = None
+    # Per-phase times with every launch on one stream (a pass of its own,
+    # 10 steps, outside the timed region): in the timed steps the thin
+    # groups' launches run on the library's second stream beside the full
+    # tiles, and their event spans there include waiting for compute units;
+    # each phase's roofline fraction comes from this pass, where the phases
+    # run one after another.
+    solo = None
     routes = None
-    if phase_ms:
-        per = {name: v / max(calls, 1) for name, v in phase_ms.items()}
-        solo = ({name: v / max(solo_calls, 1) for name, v in solo_ms.items()}
-                if solo_ms else per)
+    dom = None
+    if not args.no_phase_events:
+        o_solo = options(moe.MOE_OPT_ONE_STREAM | moe.MOE_OPT_PHASE_EVENTS)
+        moe.moe_phase_times(reset=True)
+        for _ in range(min(args.steps, 10)):
+            step(o_solo)
+        torch.cuda.synchronize()
+        solo_ms, solo_calls = moe.moe_phase_times(reset=True)
+        solo = {name: v / max(solo_calls, 1) for name, v in solo_ms.items()}
         routes = {}
         for name, (bound, amount, extra) in phase_units.items():
             ms = solo.get(name, 0.0)
             if ms <= 0 or amount <= 0:
                 continue
             routes[name] = roofline_entry(bound, amount, ms, wl["x_dtype"], extra)
-        # the dominant kernel, timed in the steps themselves; where the
-        # library forked its second stream (its rule, restated: thin groups
-        # beside full-tile ones, T k D F above 2^33) the thin phases ran
+        # the dominant kernel, timed in the steps themselves below; where the
+        # library forks its second stream (its rule, restated: thin groups
+        # beside full-tile ones, T k D F above 2^33) the thin phases run
         # there, their spans stretched by the full tiles beside them
         thin = {"gateup_thin16", "down_thin16", "gateup_thin64", "down_thin64"}
         forked = (not args.one_stream and T * k * D * F > 2 ** 33
-                  and any(per.get(n, 0) > 0 for n in ("gateup_full", "down_full"))
-                  and any(per.get(n, 0) > 0 for n in thin))
-        cand = [n for n in per if per[n] > 0 and n in phase_units
+                  and any(solo.get(n, 0) > 0 for n in ("gateup_full", "down_full"))
+                  and any(solo.get(n, 0) > 0 for n in thin))
+        cand = [n for n in solo if solo[n] > 0 and n in phase_units
                 and phase_units[n][1] > 0 and not (forked and n in thin)]
-        dom = max(cand, key=lambda n: per[n]) if cand else None
-        if dom is not None and phase_units[dom][1] > 0:
-            bound, amount, extra = phase_units[dom]
-            roofline = dict(kernel=dom, **roofline_entry(bound, amount, per[dom],
-                                                         wl["x_dtype"], extra))
-            roofline["traffic"] = load_traffic(wl["name"], dom)
-            roofline["algorithmic_per_launch"] = amount
-            roofline["avg_launch_ms"] = round(per[dom], 4)
-            roofline["phase_ms_per_step"] = {n: round(v, 4) for n, v in per.items()
-                                             if v > 0}
-            if solo_ms:
-                roofline["phase_ms_per_step_one_stream"] = {
-                    n: round(v, 4) for n, v in solo.items() if v > 0}
+        dom = max(cand, key=lambda n: solo[n]) if cand else None
+
+    # The timed steps: HIP events only around the dominant phase (each
+    # recorded pair makes the GPU drain the work before it, a few
+    # microseconds a phase), on the stream that phase runs on.
+    o_timed = (options(moe.MOE_OPT_PHASE_EVENTS |
+                       moe.MOE_OPT_PHASE_ONLY(moe.PHASES.index(dom)))
+               if dom is not None else opts)
+    moe.moe_phase_times(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pl = step(o_timed)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    timed_ms, timed_calls = moe.moe_phase_times(reset=True)
+    flops = W.flops_per_pair(D, F) * kept_pairs
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    pairs_s = kept_pairs / (ms_per_step * 1e-3)
+
+    roofline = None
+    if dom is not None:
+        dom_ms = timed_ms[dom] / max(timed_calls, 1)
+        bound, amount, extra = phase_units[dom]
+        roofline = dict(kernel=dom, **roofline_entry(bound, amount, dom_ms,
+                                                     wl["x_dtype"], extra))
+        roofline["traffic"] = load_traffic(wl["name"], dom)
+        roofline["algorithmic_per_launch"] = amount
+        roofline["avg_launch_ms"] = round(dom_ms, 4)
+        roofline["phase_ms_per_step_one_stream"] = {
+            n: round(v, 4) for n, v in solo.items() if v > 0}
+
+    # Cold-cache pass (outside the timed region above): each step follows
+    # a 1 GiB write, so x, the weights and the plan start in HBM, not in L2
+    # or the MALL; HIP events on the stream the library runs on time each
+    # step alone.
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i, (ea, eb) in enumerate(evs):
+            flush.fill_(i & 255)
+            ea.record()
+            step(opts)
+            eb.record()
+        torch.cuda.synchronize()
+        ts = sorted(ea.elapsed_time(eb) for ea, eb in evs)
+        cold = {"median_ms": round(ts[len(ts) // 2], 4), "min_ms": round(ts[0], 4),
+                "steps": len(ts),
+                "method": "1 GiB written before each step; HIP events per step"}
+        del flush
+
+    # Graph pass (outside the timed region above): one step captured into a
+    # HIP graph and replayed, so the host's per-call work (argument checks,
+    # launches) is paid once; what remains is the kernels and the gaps
+    # between them. Short prompts and decode calls are launch-bound.
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step(opts)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(opts)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph = {"ms_per_step": round(gms, 4), "replays": args.steps,
+                 "method": "plan + forward captured once (torch.cuda.CUDAGraph "
+                           "on the library's stream), replays timed back to back"}
+        del g
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
@@ -365,7 +363,7 @@ def main():
         "routes": routes,
         "routes_timing": (None if routes is None else
                           "each phase alone, every launch on one stream (a "
-                          "pass of its own)" if solo_ms else "the timed steps"),
+                          "pass of its own)"),
         "cold": cold,
         "graph": graph,
         "cpu_baseline": cpu,

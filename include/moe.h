@@ -108,7 +108,11 @@ typedef struct {
  *                     tiles owning experts of 16 rows or fewer (Strata PR
  *                     #4366, maintainer's review). Default 64.
  *   flags             MOE_OPT_PHASE_EVENTS records HIP events around each
- *                     forward phase on `stream` (see moe_phase_times).
+ *                     forward phase on the stream it runs on (see
+ *                     moe_phase_times); with any of the bits
+ *                     MOE_OPT_PHASE_ONLY(p) also set, only those phases
+ *                     (each pair of events makes the GPU drain the work
+ *                     before it: a few microseconds a phase).
  *                     The SwiGLU output H of a bf16 layer is one bf16 value
  *                     (the pages' compute-dtype buffer) when the plan is
  *                     uncapped, and a bf16 pair hi + lo (hi = bf16(h),
@@ -145,6 +149,8 @@ typedef struct {
 #define MOE_OPT_EXACT_ROUTES 4
 #define MOE_OPT_BF16_SPLIT_H 8
 #define MOE_OPT_ONE_STREAM 16
+#define MOE_OPT_PHASE_SHIFT 16
+#define MOE_OPT_PHASE_ONLY(p) ((int32_t)(1u << (MOE_OPT_PHASE_SHIFT + (p))))
 
 /* One weight tensor. `scales` is NULL unless dtype is a 4-bit format; then
  * it is 4-byte aligned (MOE_Q4B32) or 8-byte aligned (the affine formats):
@@ -249,7 +255,8 @@ size_t moe_route_workspace_bytes(const moe_plan_desc *desc, int32_t D);
  * untouched. The statistics are the same bits from run to run (fixed-order
  * sums, no float atomics). flags: MOE_OPT_PHASE_EVENTS records HIP events
  * around the router kernel, the plan and the statistics (phases 7, 8, 9 of
- * moe_phase_times); other bits are ignored. */
+ * moe_phase_times; MOE_OPT_PHASE_ONLY bits select among them); other bits
+ * are ignored. */
 moe_status moe_route(const moe_plan_desc *desc, const void *x, int32_t x_dtype,
                      const void *w_router, int32_t D, float z_weight,
                      float *logits, moe_route_stats *stats,
@@ -343,7 +350,7 @@ size_t moe_backward_workspace_bytes(const moe_plan *plan, int32_t D, int32_t F,
  * times the SwiGLU output, the SwiGLU gradients) are held in the layer's
  * dtype, products accumulate in f32. opt: the swiglu_limit of the forward
  * (NULL: defaults); MOE_OPT_PHASE_EVENTS times its four phases
- * (moe_phase_times 10..13). D and F multiples of 128; pointers 16-byte
+ * (moe_phase_times 10..13; MOE_OPT_PHASE_ONLY bits select among them). D and F multiples of 128; pointers 16-byte
  * aligned, ws 256-byte aligned. MOE_EUNSUPPORTED when x, a per-pair operand
  * (T k + n_shared T pairs x max(2F, D) 16-bit values) or a weight matrix
  * reaches 2 GiB. Async on `stream`. */

@@ -40,6 +40,14 @@ MOE_OPT_BF16_PLAIN_H = 2
 MOE_OPT_EXACT_ROUTES = 4
 MOE_OPT_BF16_SPLIT_H = 8
 MOE_OPT_ONE_STREAM = 16
+MOE_OPT_PHASE_SHIFT = 16
+
+
+def MOE_OPT_PHASE_ONLY(p: int) -> int:
+    """Option bit: with MOE_OPT_PHASE_EVENTS, record phase p (see PHASES);
+    any such bit set limits the recording to the phases selected."""
+    v = 1 << (MOE_OPT_PHASE_SHIFT + p)
+    return v - (1 << 32) if v >= (1 << 31) else v   # the int32 flags field
 MOE_N_PHASES = 16
 PHASES = ("classify", "dequant_once", "gateup_full", "gateup_thin16",
           "down_full", "down_thin16", "combine", "router_gemm", "route_plan",

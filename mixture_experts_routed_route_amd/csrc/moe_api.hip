@@ -198,12 +198,14 @@ SideStream* side_stream(int dev, moe_status* st) {
 struct PhaseRecord {
   hipEvent_t ev[2 * MOE_N_PHASES];
   bool used[MOE_N_PHASES];
+  uint32_t mask;   // the phases this call records
 };
 std::mutex g_ev_mu;
 std::vector<PhaseRecord> g_records;
 size_t g_records_used = 0;
 
-PhaseRecord* acquire_record(moe_status* st) {
+// flags: the call's option flags; bits 16 + p select phase p (none: all)
+PhaseRecord* acquire_record(int32_t flags, moe_status* st) {
   std::lock_guard<std::mutex> lock(g_ev_mu);
   if (g_records_used == g_records.size()) {
     PhaseRecord r{};
@@ -218,6 +220,8 @@ PhaseRecord* acquire_record(moe_status* st) {
   }
   PhaseRecord* r = &g_records[g_records_used++];
   for (int i = 0; i < MOE_N_PHASES; ++i) r->used[i] = false;
+  const uint32_t sel = (uint32_t)flags >> MOE_OPT_PHASE_SHIFT;
+  r->mask = sel ? sel : 0xFFFFu;
   return r;
 }
 
@@ -225,7 +229,8 @@ struct PhaseScope {
   PhaseRecord* rec;
   int phase;
   hipStream_t s;
-  PhaseScope(PhaseRecord* r, int p, hipStream_t st) : rec(r), phase(p), s(st) {
+  PhaseScope(PhaseRecord* r, int p, hipStream_t st)
+      : rec(r && ((r->mask >> p) & 1u) ? r : nullptr), phase(p), s(st) {
     if (rec) hipEventRecord(rec->ev[2 * phase], s);
   }
   ~PhaseScope() {
@@ -502,7 +507,7 @@ moe_status moe_route(const moe_plan_desc* desc, const void* x, int32_t x_dtype,
   const int64_t limit = capacity_limit(d);
   PhaseRecord* rec = nullptr;
   if (flags & MOE_OPT_PHASE_EVENTS) {
-    rec = acquire_record(&st);
+    rec = acquire_record(flags, &st);
     if (!rec) return st;
   }
   hipError_t e;
@@ -644,7 +649,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
   if (st != MOE_OK) return st;
   PhaseRecord* rec = nullptr;
   if (o.flags & MOE_OPT_PHASE_EVENTS) {
-    rec = acquire_record(&st);
+    rec = acquire_record(o.flags, &st);
     if (!rec) return st;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -979,7 +984,7 @@ moe_status moe_backward(const moe_plan* p, const void* x, int32_t x_dtype,
   a.dtw_scratch = reinterpret_cast<float*>(b + bwd_workspace_bytes(a.Pmax, a.n_exp, D, F));
   PhaseRecord* rec = nullptr;
   if (o.flags & MOE_OPT_PHASE_EVENTS) {
-    rec = acquire_record(&st);
+    rec = acquire_record(o.flags, &st);
     if (!rec) return st;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
