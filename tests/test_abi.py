@@ -250,3 +250,26 @@ def test_python_weight_shapes_rejected_before_launch(case):
     if case in ("gate_experts", "up_shape", "down_shape", "shared_missing"):
         with pytest.raises(ValueError):
             moe.moe_backward(plan, x, wg, wu, wd, torch.zeros(T, D))
+
+
+def test_binding_constants_match_the_header():
+    """The binding's option flags, phase count and status codes are the
+    header's #defines (read from include/moe.h), and MOE_OPT_PHASE_ONLY(p)
+    is the header's macro for every phase, as a signed 32-bit flags value."""
+    import os
+    import re
+
+    import mixture_experts_routed_route_amd as moe
+
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")).read()
+    defs = dict(re.findall(r"#define\s+(MOE_\w+)\s+\(?(-?\d+)\)?\s*$", hdr, re.M))
+    for name in ("MOE_OPT_PHASE_EVENTS", "MOE_OPT_BF16_PLAIN_H", "MOE_OPT_EXACT_ROUTES",
+                 "MOE_OPT_BF16_SPLIT_H", "MOE_OPT_ONE_STREAM", "MOE_OPT_PHASE_SHIFT",
+                 "MOE_N_PHASES"):
+        assert name in defs, name
+        assert getattr(moe, name) == int(defs[name]), name
+    assert len(moe.PHASES) == moe.MOE_N_PHASES
+    for p in range(moe.MOE_N_PHASES):
+        v = (1 << (int(defs["MOE_OPT_PHASE_SHIFT"]) + p)) & 0xFFFFFFFF
+        v = v - (1 << 32) if v >= (1 << 31) else v
+        assert moe.MOE_OPT_PHASE_ONLY(p) == v

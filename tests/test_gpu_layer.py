@@ -353,6 +353,32 @@ def test_second_stream_matches_one_stream(cfg):
     assert torch.equal(two, two_again)
 
 
+def test_phase_events_only_selected():
+    """MOE_OPT_PHASE_ONLY bits limit the recorded phases to those selected
+    (here the gate/up full tile); with none set every phase that ran is
+    timed. The output is the same bits either way."""
+    wl = W.config(3)
+    say("phase events, selected and all")
+    p = gpu_plan(wl)
+    x = wl["x"].cuda()
+    w = [to_dev(wl[n]) for n in ("w_gate", "w_up", "w_down")]
+    moe.moe_phase_times(reset=True)
+    one = moe.make_options(flags=moe.MOE_OPT_PHASE_EVENTS |
+                           moe.MOE_OPT_PHASE_ONLY(moe.PHASES.index("gateup_full")))
+    y1 = moe.moe_forward(p, x, *w, options=one)
+    ms, calls = moe.moe_phase_times(reset=True)
+    assert calls == 1
+    assert ms["gateup_full"] > 0
+    assert all(v == 0 for n, v in ms.items() if n != "gateup_full")
+    y2 = moe.moe_forward(p, x, *w, options=moe.make_options(flags=moe.MOE_OPT_PHASE_EVENTS))
+    ms2, calls2 = moe.moe_phase_times(reset=True)
+    assert calls2 == 1
+    for n in ("classify", "gateup_full", "down_full", "gateup_thin16", "combine"):
+        assert ms2[n] > 0, n
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
 def test_swiglu_clamp_binds_and_matches():
     """Large weights so |g| > 7 often: the clamp decides the output."""
     wl = W.make_layer(96, 128, 256, 4, 2, W.F32, seed=27, w_std=0.9)
