@@ -76,6 +76,10 @@ def parse():
     ap.add_argument("--one-stream", action="store_true",
                     help="MOE_OPT_ONE_STREAM: every launch on the caller's "
                          "stream (no second stream for the thin groups)")
+    ap.add_argument("--tiled-decode", action="store_true",
+                    help="MOE_OPT_TILED_DECODE: a one-token call on a 16-bit "
+                         "layer runs the split-K tile and the combine "
+                         "instead of the matrix-vector kernels")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph pass (plan + forward captured once "
                          "into a HIP graph, K replays timed)")
@@ -150,6 +154,8 @@ def main():
     # point compares the two tiles at every size)
     exact = args.splitk_max_pairs is not None
     one = moe.MOE_OPT_ONE_STREAM if args.one_stream else 0
+    if args.tiled_decode:
+        one |= moe.MOE_OPT_TILED_DECODE
 
     def options(flags=0):
         o = moe.make_options(splitk_max_pairs=args.splitk_max_pairs,

@@ -136,7 +136,17 @@ typedef struct {
  *                     on it; the first such call on a device creates the
  *                     stream and two events (under graph capture, make it
  *                     before capturing). MOE_OPT_ONE_STREAM keeps every
- *                     launch on `stream`. */
+ *                     launch on `stream`.
+ *                     A one-token call (T = 1) on a bf16 / fp16 layer runs
+ *                     two matrix-vector launches instead of the split-K
+ *                     tile and the combine: one token's experts are
+ *                     distinct, each holds one pair (mini-AGI PR #3,
+ *                     minagi/pool.py, the one-row case), so the call is
+ *                     the chosen experts' weight stream, spread over every
+ *                     compute unit; the second launch also sums the pairs
+ *                     into y in the combine's order and precision (phases
+ *                     3 and 5 of moe_phase_times; 6 is not used).
+ *                     MOE_OPT_TILED_DECODE keeps such calls on the tile. */
 typedef struct {
     float swiglu_limit;
     float splitk_max_pairs;
@@ -149,6 +159,7 @@ typedef struct {
 #define MOE_OPT_EXACT_ROUTES 4
 #define MOE_OPT_BF16_SPLIT_H 8
 #define MOE_OPT_ONE_STREAM 16
+#define MOE_OPT_TILED_DECODE 32
 #define MOE_OPT_PHASE_SHIFT 16
 #define MOE_OPT_PHASE_ONLY(p) ((int32_t)(1u << (MOE_OPT_PHASE_SHIFT + (p))))
 

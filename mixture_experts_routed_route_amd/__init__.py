@@ -40,6 +40,7 @@ MOE_OPT_BF16_PLAIN_H = 2
 MOE_OPT_EXACT_ROUTES = 4
 MOE_OPT_BF16_SPLIT_H = 8
 MOE_OPT_ONE_STREAM = 16
+MOE_OPT_TILED_DECODE = 32
 MOE_OPT_PHASE_SHIFT = 16
 
 

@@ -666,6 +666,37 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       (wdt == MOE_F32 || q4_fmt(wdt) >= 0 ||
        (double)o.splitk_max_pairs >= (double)d.T);
 
+  // One token on a 16-bit layer: each of its experts holds one pair, so
+  // every product is a matrix-vector product; two launches read the chosen
+  // experts' weights across all compute units, the second also summing the
+  // pairs into y (no combine launch).
+  if (decode && d.T == 1 && L.stream && x_dtype == wdt &&
+      !(o.flags & MOE_OPT_TILED_DECODE) && gemv_supported(D, F, d.k, d.n_shared)) {
+    GemvArgs ga{};
+    ga.x = x;
+    ga.wg = w_gate.data; ga.wu = w_up.data; ga.wd = w_down.data;
+    ga.ids = (const int32_t*)(pb + p->L.ids);
+    ga.tok2pair = (const int32_t*)(pb + p->L.tok2pair);
+    ga.w = (const float*)(pb + p->L.w);
+    ga.offsets = (const int32_t*)(pb + p->L.offsets);
+    ga.h = b + L.H;
+    ga.h2 = L.split_h ? b + L.H2 : nullptr;
+    ga.h_ld = L.h_ld;
+    ga.ypair = b + L.Y;
+    ga.y = y;
+    ga.D = D; ga.F = F; ga.k = d.k; ga.E = d.E; ga.n_shared = d.n_shared;
+    ga.clamp = o.swiglu_limit;
+    {
+      PhaseScope ps(rec, 3, s);
+      e = launch_gemv_gateup(ga, x_dtype, s);
+      if (e != hipSuccess) return hip_fail(e, "one-token gate/up kernel");
+    }
+    PhaseScope ps(rec, 5, s);
+    e = launch_gemv_down(ga, x_dtype, y_dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "one-token down kernel");
+    return MOE_OK;
+  }
+
   if (decode) {
     meta = (int32_t*)(pb + p->L.dmeta);
   } else {

@@ -233,6 +233,31 @@ hipError_t launch_combine(const void* ypair, int ypair_f16,
                           const int32_t* offsets, int T, int D, int k,
                           int n_shared, int E, int ydt, void* y, hipStream_t s);
 
+// One-token calls on bf16 / fp16 layers (gemv_decode.hip): gate/up and
+// SwiGLU, then down with the combine, one matrix-vector product per weight
+// row of the token's experts.
+struct GemvArgs {
+  const void* x;            // [D] the token's row (x's dtype)
+  const void* wg;           // W_gate [E + n_shared, F, D]
+  const void* wu;           // W_up   [E + n_shared, F, D]
+  const void* wd;           // W_down [E + n_shared, D, F]
+  const int32_t* ids;       // [k] the token's experts (plan)
+  const int32_t* tok2pair;  // [k] their pair rows, -1 if dropped (plan)
+  const float* w;           // [k] routing weights (plan)
+  const int32_t* offsets;   // [E + n_shared + 1] (plan): the shared row
+  void* h;                  // H [P, h_ld], x's dtype
+  void* h2;                 // bf16 low plane of H, or null
+  int h_ld;
+  void* ypair;              // [P, D] unweighted expert outputs (fp16 in an
+                            // fp16 layer, else f32)
+  void* y;                  // [D] the output, y's dtype
+  int D, F, k, E, n_shared;
+  float clamp;
+};
+bool gemv_supported(int D, int F, int k, int n_shared);
+hipError_t launch_gemv_gateup(const GemvArgs& a, int xdt, hipStream_t s);
+hipError_t launch_gemv_down(const GemvArgs& a, int xdt, int ydt, hipStream_t s);
+
 // ---- backward (backward.hip) --------------------------------------------
 struct BwdArgs {
   int xdt;                      // MOE_BF16 or MOE_F16 (x and the weights)

@@ -264,7 +264,8 @@ def test_binding_constants_match_the_header():
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")).read()
     defs = dict(re.findall(r"#define\s+(MOE_\w+)\s+\(?(-?\d+)\)?\s*$", hdr, re.M))
     for name in ("MOE_OPT_PHASE_EVENTS", "MOE_OPT_BF16_PLAIN_H", "MOE_OPT_EXACT_ROUTES",
-                 "MOE_OPT_BF16_SPLIT_H", "MOE_OPT_ONE_STREAM", "MOE_OPT_PHASE_SHIFT",
+                 "MOE_OPT_BF16_SPLIT_H", "MOE_OPT_ONE_STREAM", "MOE_OPT_TILED_DECODE",
+                 "MOE_OPT_PHASE_SHIFT",
                  "MOE_N_PHASES"):
         assert name in defs, name
         assert getattr(moe, name) == int(defs[name]), name
