@@ -195,12 +195,14 @@ __global__ __launch_bounds__(1024) void classify_kernel(ClassifyArgs a) {
     c4 += t4;
     cf += tf;
   }
-  if (a.sk1_tok) {
-    // The groups' x rows for the stream tile (a group's rows, clamped to its
-    // last), one row per thread over all groups: one round trip for the
-    // group entries written above, one for the pair list.
+  if (a.sk1_tok || a.sk4_tok) {
+    // The groups' x rows for the stream tile, and for the wide 4-bit tile
+    // (sk4 only), a group's rows clamped to its last, one row per thread
+    // over all groups: one round trip for the group entries written above,
+    // one for the pair list.
     __syncthreads();   // the group entries are visible to the whole block
-    const int r1 = c1 * 16, r4 = c4 * kStreamTokRows;
+    const int r1 = a.sk1_tok ? c1 * 16 : 0;
+    const int r4 = a.sk4_tok ? c4 * kStreamTokRows : 0;
     for (int i = threadIdx.x; i < r1 + r4; i += blockDim.x) {
       const bool one = i < r1;
       const int j = one ? i : i - r1;

@@ -318,8 +318,11 @@ FwdLayout fwd_layout(const moe_plan_desc& d, int D, int F, int xdt, int wdt,
   L.full_tiles = take((size_t)L.cap_tiles * 8);
   L.sk1 = take((size_t)L.cap_sk1 * 16);
   L.sk4 = take((size_t)L.cap_sk4 * 16);
+  // the groups' x rows: read by the stream tile and (17..64-row groups)
+  // by the wide 4-bit tile
   L.sk1_tok = take(L.stream ? (size_t)L.cap_sk1 * kStreamTokRows * 4 : 0);
-  L.sk4_tok = take(L.stream ? (size_t)L.cap_sk4 * kStreamTokRows * 4 : 0);
+  L.sk4_tok = take(L.stream || q4_fmt(wdt) >= 0
+                       ? (size_t)L.cap_sk4 * kStreamTokRows * 4 : 0);
   L.part = take(L.stream ? (size_t)kStreamPartFloats * 4 : 0);
   L.fat_slot = take((size_t)n_exp * 4);
   L.fat_list = take((size_t)n_exp * 4);
@@ -715,7 +718,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
     ca.offsets = (const int32_t*)(pb + p->L.offsets);
     ca.pair_token = (const int32_t*)(pb + p->L.pair_token);
     ca.sk1_tok = L.stream ? (int32_t*)(b + L.sk1_tok) : nullptr;
-    ca.sk4_tok = L.stream ? (int32_t*)(b + L.sk4_tok) : nullptr;
+    ca.sk4_tok = L.stream || ca.mode == 2 ? (int32_t*)(b + L.sk4_tok) : nullptr;
     ca.fat_slot = (int32_t*)(b + L.fat_slot);
     ca.fat_list = (int32_t*)(b + L.fat_list);
     ca.meta = meta;
@@ -890,6 +893,7 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
           e = launch_gemm_stream(g, x_dtype, wdt, kStreamTokRows, stream_grid4, ts);
         } else {
           // wide fused-dequant tile, 256 columns per item
+          g.tok = (const int32_t*)(b + L.sk4_tok);
           const int wnb = stage == 0 ? (F + 127) / 128 : (D + 255) / 256;
           const int grid = (int)std::min<int64_t>((int64_t)L.cap_sk4 * wnb, info.ncu * 2);
           e = launch_gemm_wide(g, x_dtype, wdt, grid, ts);

@@ -146,7 +146,8 @@ struct ClassifyArgs {
   const int32_t* pair_token;   // [P]
   int32_t* sk1_tok;        // [cap, kStreamTokRows]: x rows of each sk1
                            // group, clamped to its last row; or null
-  int32_t* sk4_tok;        // the same for sk4; or null
+  int32_t* sk4_tok;        // the same for sk4 (stream tile, wide 4-bit
+                           // tile); or null
   int32_t* fat_slot;       // [n_exp]
   int32_t* fat_list;       // [n_exp]
   int32_t* meta;           // [kMetaCount]
@@ -188,7 +189,9 @@ struct GemmArgs {
   int h_rows;               // full tile: rows of the k-block-major H
                             // ([F / 32][h_rows][32]) it writes (gate/up) or
                             // reads (down)
-  const int32_t* tok;       // stream tile, gate/up: the sk1 groups' x rows
+  const int32_t* tok;       // gate/up of the stream tile and the wide 4-bit
+                            // tile: the listed groups' x rows
+                            // (kStreamTokRows a group)
   float* part;              // stream tile: [runs, 2, 2048 RB] floats
   int32_t* fix;             // stream tile: [runs, 4] arrival counters of the
                             // items cut by run boundaries (zero on entry,
