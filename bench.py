@@ -77,8 +77,8 @@ def parse():
                     help="MOE_OPT_ONE_STREAM: every launch on the caller's "
                          "stream (no second stream for the thin groups)")
     ap.add_argument("--tiled-decode", action="store_true",
-                    help="MOE_OPT_TILED_DECODE: a one-token call on a 16-bit "
-                         "layer runs the split-K tile and the combine "
+                    help="MOE_OPT_TILED_DECODE: a one-token call runs the "
+                         "split-K tile and the combine "
                          "instead of the matrix-vector kernels")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph pass (plan + forward captured once "

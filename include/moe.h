@@ -137,8 +137,10 @@ typedef struct {
  *                     stream and two events (under graph capture, make it
  *                     before capturing). MOE_OPT_ONE_STREAM keeps every
  *                     launch on `stream`.
- *                     A one-token call (T = 1) on a bf16 / fp16 layer runs
- *                     two matrix-vector launches instead of the split-K
+ *                     A one-token call (T = 1) on a bf16 / fp16 layer, or
+ *                     on a 4-bit layer with fp16 x (weights decoded in
+ *                     registers as the thin tiles decode them), runs two
+ *                     matrix-vector launches instead of the split-K
  *                     tile and the combine: one token's experts are
  *                     distinct, each holds one pair (mini-AGI PR #3,
  *                     minagi/pool.py, the one-row case), so the call is

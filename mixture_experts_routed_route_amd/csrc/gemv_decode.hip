@@ -1,4 +1,5 @@
-// One-token calls (T = 1) on bf16 / fp16 layers, on gfx950.
+// One-token calls (T = 1) on bf16 / fp16 layers and on 4-bit layers with
+// fp16 activations, on gfx950.
 //
 // A single token's k choices are k distinct experts, each holding exactly
 // one of its pairs, and only those experts' weights need to be read
@@ -233,6 +234,182 @@ hipError_t down_launch(const GemvArgs& a, int ydt, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+// ---- 4-bit weights, fp16 activations -----------------------------------
+//
+// A 16-byte piece of a 4-bit weight row holds 32 consecutive K values: one
+// parameter block of the signed and affine-32 formats, half a group of the
+// affine-64 one. A lane decodes its pieces in registers to the values the
+// thin tiles use (fp16_rne(q s), or q s + b rounded once: Strata PR #4366,
+// "Approach", decodes a 4-bit expert's weights to FP16; the affine groups
+// are TensorFold PR #1607's) and takes the dot products with the matching
+// 32 values of the activation row two at a time, f32 accumulation
+// (v_dot2_f32_f16). Same workgroup shapes as the 16-bit kernels.
+
+constexpr int kGvSlotsQ = 2;    // pieces a lane holds per row at once, gate/up
+constexpr int kGvSlotsQD = 1;   // the same, down
+
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// sum over the 32 values of one piece: decoded weights times x (4 x 16 B)
+template <int FMT>
+__device__ __forceinline__ float dot_piece_q4(uint4 wq, uint32_t prm,
+                                              const uint4 (&xv)[4], float acc) {
+  const uint32_t words[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half8 w8 = dequant_word_f<FMT>(words[i], prm);
+    const half8 x8 = __builtin_bit_cast(half8, xv[i]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc = __builtin_amdgcn_fdot2(h2v{w8[2 * t], w8[2 * t + 1]},
+                                   h2v{x8[2 * t], x8[2 * t + 1]}, acc, false);
+  }
+  return acc;
+}
+
+// the parameter word of piece ci (32 K values from 32 ci) of a row whose
+// parameters start at prow
+template <int FMT>
+__device__ __forceinline__ uint32_t piece_param(const char* prow, int ci) {
+  return q4p_block<FMT>(load_q4p<FMT, 1>(prow, ci * 32), 0);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void gemv_gateup_q4_kernel(GemvArgs a) {
+  using Q = Q4F<FMT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nfb = a.F / kGvFB;
+  const int j = blockIdx.x / nfb;
+  const int f0 = (blockIdx.x - j * nfb) * kGvFB + wave * 4;
+  int e, p;
+  pair_of(a, j, e, p);
+  if (p < 0) return;   // a dropped pair: no row
+  const _Float16* x = (const _Float16*)a.x;
+  const char* rows[8];
+  const char* prms[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const size_t wrow = (size_t)e * a.F + f0 + (r & 3);
+    const char* base = (const char*)(r < 4 ? a.wg : a.wu);
+    const char* pbase = (const char*)(r < 4 ? a.wgs : a.wus);
+    rows[r] = base + wrow * (size_t)(a.D / 2);
+    prms[r] = pbase + wrow * (size_t)(a.D / Q::kGroup) * Q::kPB;
+  }
+  const int np = a.D / 32;   // pieces a row
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < np; c0 += 64 * kGvSlotsQ) {
+    uint4 wv[8][kGvSlotsQ], xv[kGvSlotsQ][4];
+    uint32_t pv[8][kGvSlotsQ];
+#pragma unroll
+    for (int c = 0; c < kGvSlotsQ; ++c) {
+      const int ci = c0 + c * 64 + lane;
+      const bool ok = ci < np;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        wv[r][c] = ok ? ldg16(rows[r] + (size_t)ci * 16) : uint4{0u, 0u, 0u, 0u};
+        pv[r][c] = ok ? piece_param<FMT>(prms[r], ci) : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[c][i] = ok ? ldg16(x + (size_t)ci * 32 + 8 * i) : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int c = 0; c < kGvSlotsQ; ++c)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r] = dot_piece_q4<FMT>(wv[r][c], pv[r][c], xv[c], acc[r]);
+  }
+  // lane l: row 4 b5 + 2 b4 + b3; gate rows 0..3 on lanes with b5 = 0, the
+  // up row of the same feature on lane l ^ 32
+  const float v = wave_sum8(acc, lane);
+  const float u = __shfl_xor(v, 32);
+  if ((lane & 39) == 0) {   // lanes 0, 8, 16, 24: features f0 .. f0 + 3
+    const int f = f0 + ((lane >> 3) & 3);
+    ((_Float16*)a.h)[(size_t)p * a.h_ld + f] = (_Float16)swiglu(v, u, a.clamp);
+  }
+}
+
+// blockDim.x = 64 min(J, 16): wave w takes pairs w, w + waves, ...; the
+// pair outputs are fp16 (the fp16 layer's pair buffer) and summed as the
+// 16-bit down kernel sums them
+template <int FMT, class O>
+__global__ __launch_bounds__(1024) void gemv_down_q4_kernel(GemvArgs a) {
+  using Q = Q4F<FMT>;
+  extern __shared__ float ys[];   // [J][kGvDB]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int d0 = blockIdx.x * kGvDB;
+  const int J = a.k + a.n_shared;
+  const int np = a.F / 32;
+  const _Float16* H = (const _Float16*)a.h;
+  for (int j = wave; j < J; j += nw) {
+    int e, p;
+    pair_of(a, j, e, p);
+    if (p < 0) continue;   // wave-uniform: a dropped pair
+    const size_t wrow0 = (size_t)e * a.D + d0;
+    const char* w0 = (const char*)a.wd + wrow0 * (size_t)(a.F / 2);
+    const char* p0 = (const char*)a.wds + wrow0 * (size_t)(a.F / Q::kGroup) * Q::kPB;
+    const _Float16* hp = H + (size_t)p * a.h_ld;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < np; c0 += 64 * kGvSlotsQD) {
+      uint4 wv[8][kGvSlotsQD], hv[kGvSlotsQD][4];
+      uint32_t pv[8][kGvSlotsQD];
+#pragma unroll
+      for (int c = 0; c < kGvSlotsQD; ++c) {
+        const int ci = c0 + c * 64 + lane;
+        const bool ok = ci < np;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          wv[r][c] = ok ? ldg16(w0 + (size_t)r * (a.F / 2) + (size_t)ci * 16)
+                        : uint4{0u, 0u, 0u, 0u};
+          pv[r][c] = ok ? piece_param<FMT>(p0 + (size_t)r * (a.F / Q::kGroup) * Q::kPB, ci)
+                        : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          hv[c][i] = ok ? ldg16(hp + (size_t)ci * 32 + 8 * i) : uint4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int c = 0; c < kGvSlotsQD; ++c)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] = dot_piece_q4<FMT>(wv[r][c], pv[r][c], hv[c], acc[r]);
+    }
+    const float v = wave_sum8(acc, lane);
+    if ((lane & 7) == 0) {   // lane 8 r holds column d0 + r
+      const int r = lane >> 3;
+      const _Float16 yv = (_Float16)v;
+      ((_Float16*)a.ypair)[(size_t)p * a.D + d0 + r] = yv;
+      ys[j * kGvDB + r] = (float)yv;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kGvDB) {
+    const int c = threadIdx.x;
+    float acc = 0.f;
+    for (int j = 0; j < a.k; ++j)
+      if (a.tok2pair[j] >= 0) acc += ys[j * kGvDB + c] * a.w[j];
+    if (a.n_shared) acc += ys[a.k * kGvDB + c];
+    ((O*)a.y)[d0 + c] = (O)acc;
+  }
+}
+
+template <int FMT>
+hipError_t down_q4_launch(const GemvArgs& a, int ydt, hipStream_t s) {
+  const int grid = a.D / kGvDB;
+  const int J = a.k + a.n_shared;
+  const int threads = 64 * (J < 16 ? J : 16);
+  const size_t lds = (size_t)J * kGvDB * 4;
+  if (ydt == MOE_F32)
+    hipLaunchKernelGGL((gemv_down_q4_kernel<FMT, float>), dim3(grid), dim3(threads), lds, s, a);
+  else if (ydt == MOE_BF16)
+    hipLaunchKernelGGL((gemv_down_q4_kernel<FMT, __bf16>), dim3(grid), dim3(threads), lds, s, a);
+  else
+    hipLaunchKernelGGL((gemv_down_q4_kernel<FMT, _Float16>), dim3(grid), dim3(threads), lds, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemv_supported(int D, int F, int k, int n_shared) {
@@ -240,9 +417,28 @@ bool gemv_supported(int D, int F, int k, int n_shared) {
          F % 8 == 0 && (size_t)(k + n_shared) * kGvDB * 4 <= 65536;
 }
 
+// 4-bit weights: K values in whole pieces of 32 (whole groups of 64 for
+// the affine-64 format) along both products
+bool gemv_q4_supported(int D, int F, int k, int n_shared, int fmt) {
+  const int grp = fmt == 2 ? 64 : 32;
+  return fmt >= 0 && fmt <= 2 && gemv_supported(D, F, k, n_shared) &&
+         D % grp == 0 && F % grp == 0;
+}
+
 hipError_t launch_gemv_gateup(const GemvArgs& a, int xdt, hipStream_t s) {
-  if (!gemv_supported(a.D, a.F, a.k, a.n_shared)) return hipErrorInvalidValue;
   const int grid = (a.k + a.n_shared) * (a.F / kGvFB);
+  if (a.fmt >= 0) {
+    if (xdt != MOE_F16 || !gemv_q4_supported(a.D, a.F, a.k, a.n_shared, a.fmt))
+      return hipErrorInvalidValue;
+    if (a.fmt == 0)
+      hipLaunchKernelGGL((gemv_gateup_q4_kernel<0>), dim3(grid), dim3(256), 0, s, a);
+    else if (a.fmt == 1)
+      hipLaunchKernelGGL((gemv_gateup_q4_kernel<1>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemv_gateup_q4_kernel<2>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if (!gemv_supported(a.D, a.F, a.k, a.n_shared)) return hipErrorInvalidValue;
   if (xdt == MOE_BF16)
     hipLaunchKernelGGL((gemv_gateup_kernel<__bf16>), dim3(grid), dim3(256), 0, s, a);
   else if (xdt == MOE_F16)
@@ -253,6 +449,13 @@ hipError_t launch_gemv_gateup(const GemvArgs& a, int xdt, hipStream_t s) {
 }
 
 hipError_t launch_gemv_down(const GemvArgs& a, int xdt, int ydt, hipStream_t s) {
+  if (a.fmt >= 0) {
+    if (xdt != MOE_F16 || a.h2 || !gemv_q4_supported(a.D, a.F, a.k, a.n_shared, a.fmt))
+      return hipErrorInvalidValue;
+    if (a.fmt == 0) return down_q4_launch<0>(a, ydt, s);
+    if (a.fmt == 1) return down_q4_launch<1>(a, ydt, s);
+    return down_q4_launch<2>(a, ydt, s);
+  }
   if (!gemv_supported(a.D, a.F, a.k, a.n_shared)) return hipErrorInvalidValue;
   // the pair buffer's type is the tiles': fp16 in an fp16 layer, else f32
   if (xdt == MOE_BF16)

@@ -669,15 +669,21 @@ moe_status moe_forward(const moe_plan* p, const void* x, int32_t x_dtype,
       (wdt == MOE_F32 || q4_fmt(wdt) >= 0 ||
        (double)o.splitk_max_pairs >= (double)d.T);
 
-  // One token on a 16-bit layer: each of its experts holds one pair, so
-  // every product is a matrix-vector product; two launches read the chosen
-  // experts' weights across all compute units, the second also summing the
-  // pairs into y (no combine launch).
-  if (decode && d.T == 1 && L.stream && x_dtype == wdt &&
-      !(o.flags & MOE_OPT_TILED_DECODE) && gemv_supported(D, F, d.k, d.n_shared)) {
+  // One token on a 16-bit layer, or on a 4-bit layer with fp16 x: each of
+  // its experts holds one pair, so every product is a matrix-vector
+  // product; two launches read the chosen experts' weights across all
+  // compute units, the second also summing the pairs into y (no combine
+  // launch).
+  const int fmt = q4_fmt(wdt);
+  const bool gemv16 = L.stream && x_dtype == wdt && gemv_supported(D, F, d.k, d.n_shared);
+  const bool gemv4 = fmt >= 0 && x_dtype == MOE_F16 &&
+                     gemv_q4_supported(D, F, d.k, d.n_shared, fmt);
+  if (decode && d.T == 1 && (gemv16 || gemv4) && !(o.flags & MOE_OPT_TILED_DECODE)) {
     GemvArgs ga{};
     ga.x = x;
     ga.wg = w_gate.data; ga.wu = w_up.data; ga.wd = w_down.data;
+    ga.wgs = w_gate.scales; ga.wus = w_up.scales; ga.wds = w_down.scales;
+    ga.fmt = fmt;
     ga.ids = (const int32_t*)(pb + p->L.ids);
     ga.tok2pair = (const int32_t*)(pb + p->L.tok2pair);
     ga.w = (const float*)(pb + p->L.w);

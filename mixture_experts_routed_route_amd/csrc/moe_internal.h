@@ -244,6 +244,10 @@ struct GemvArgs {
   const void* wg;           // W_gate [E + n_shared, F, D]
   const void* wu;           // W_up   [E + n_shared, F, D]
   const void* wd;           // W_down [E + n_shared, D, F]
+  const void* wgs;          // 4-bit weights: the parameters of W_gate,
+  const void* wus;          // W_up and W_down ([.., N, K / group] fp16
+  const void* wds;          // scales or (scale, bias) words); else null
+  int fmt;                  // 4-bit format (q4_fmt), or -1
   const int32_t* ids;       // [k] the token's experts (plan)
   const int32_t* tok2pair;  // [k] their pair rows, -1 if dropped (plan)
   const float* w;           // [k] routing weights (plan)
@@ -258,6 +262,7 @@ struct GemvArgs {
   float clamp;
 };
 bool gemv_supported(int D, int F, int k, int n_shared);
+bool gemv_q4_supported(int D, int F, int k, int n_shared, int fmt);
 hipError_t launch_gemv_gateup(const GemvArgs& a, int xdt, hipStream_t s);
 hipError_t launch_gemv_down(const GemvArgs& a, int xdt, int ydt, hipStream_t s);
 

@@ -1,5 +1,5 @@
-"""One-token calls (T = 1) on bf16 / fp16 layers take the two matrix-vector
-kernels (gate/up + SwiGLU, then down with the combine) instead of the
+"""One-token calls (T = 1) on bf16 / fp16 layers, and on 4-bit layers with
+fp16 x, take the two matrix-vector kernels (gate/up + SwiGLU, then down with the combine) instead of the
 split-K tile and the combine kernel. Checked against the oracle: the output,
 every pair's unweighted expert output (the pair buffer the combine would
 read), and the same call kept on the tile (MOE_OPT_TILED_DECODE), both
@@ -7,7 +7,10 @@ within the bar; y in x's dtype is the f32 output rounded once. Shapes: the
 short-prompt layer's (D 2048, F 768, top-8 + a shared expert), a capped
 plan (the bf16 hi + lo SwiGLU pair) with a binding clamp, k = E, a long F
 (the down kernel's K in several passes) and a long D (gate/up in several
-passes), an odd number of pairs for the down kernel's groups of four."""
+passes), an odd number of pairs for the down kernel's groups of four; for
+the three 4-bit formats the long-prompt layer's sizes (D 4096, F 2048,
+top-8), a capped plan with a shared expert, and long rows for either
+product (the pieces of a row in several passes)."""
 
 import numpy as np
 import pytest
@@ -15,7 +18,8 @@ import torch
 
 import mixture_experts_routed_route_amd as moe
 import workloads as W
-from helpers import check_layer, check_pairs, gpu_layer, gpu_layer_views, plan_arrays, say
+from helpers import (check_layer, check_pairs, gpu_layer, gpu_layer_views, plan_arrays,
+                     say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,3 +79,44 @@ def test_one_token_phases_and_repeat():
         check_layer(wl2, y2)
         _, y3 = gpu_layer(wl2, plan=p2)
         assert torch.equal(y2, y3)
+
+
+Q4_CASES = [
+    # w_dtype, D, F, E, k, n_shared, cf, clamp
+    (W.Q4B32, 4096, 2048, 16, 8, 0, 0.0, 7.0),
+    (W.Q4A32, 4096, 2048, 16, 8, 0, 0.0, 7.0),
+    (W.Q4A64, 4096, 2048, 16, 8, 0, 0.0, 7.0),
+    (W.Q4B32, 256, 384, 16, 4, 1, 1.0, 0.5),
+    (W.Q4A64, 640, 128, 8, 8, 1, 2.0, 0.0),
+    (W.Q4B32, 128, 4096, 32, 2, 0, 0.0, 7.0),
+    (W.Q4A32, 8192, 256, 8, 3, 1, 0.0, 7.0),
+]
+
+
+@pytest.mark.parametrize("case", Q4_CASES, ids=lambda c: f"{c[0]}-D{c[1]}-F{c[2]}-k{c[4]}")
+def test_one_token_q4_against_oracle_and_tile(case):
+    wdt, D, F, E, k, ns, cf, c = case
+    wl = W.make_layer(1, D, F, E, k, W.F16, w_dtype=wdt, seed=D + F + k,
+                      n_shared=ns, capacity_factor=cf, swiglu_limit=c)
+    say(f"one token 4-bit {case}")
+    opts = moe.make_options(swiglu_limit=c)
+    moe.moe_phase_times(reset=True)
+    ph = moe.make_options(swiglu_limit=c, flags=moe.MOE_OPT_PHASE_EVENTS)
+    p, y, views = gpu_layer_views(wl, options=ph)
+    ms, calls = moe.moe_phase_times(reset=True)
+    assert calls == 1 and ms["combine"] == 0   # the down kernel summed y
+    check_layer(wl, y)
+    counts = plan_arrays(p)["counts"]
+    experts = np.nonzero(counts)[0]
+    assert len(experts) == k + ns
+    check_pairs(wl, p, views, experts)
+    tiled = moe.make_options(swiglu_limit=c, flags=moe.MOE_OPT_TILED_DECODE)
+    _, y_t = gpu_layer(wl, options=tiled, plan=p)
+    check_layer(wl, y_t)
+    x = wl["x"].cuda()
+    wg, wu, wd = (to_dev(wl[n]) for n in ("w_gate", "w_up", "w_down"))
+    yx = moe.moe_forward(p, x, wg, wu, wd, options=opts, y_dtype=x.dtype)
+    y2 = moe.moe_forward(p, x, wg, wu, wd, options=opts)
+    torch.cuda.synchronize()
+    assert torch.equal(yx, y.to(x.dtype))
+    assert torch.equal(y2, y)
