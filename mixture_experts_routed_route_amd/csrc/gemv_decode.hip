@@ -246,7 +246,7 @@ hipError_t down_launch(const GemvArgs& a, int ydt, hipStream_t s) {
 // 32 values of the activation row two at a time, f32 accumulation
 // (v_dot2_f32_f16). Same workgroup shapes as the 16-bit kernels.
 
-constexpr int kGvSlotsQ = 2;    // pieces a lane holds per row at once, gate/up
+constexpr int kGvSlotsQ = 1;    // pieces a lane holds per row at once, gate/up
 constexpr int kGvSlotsQD = 1;   // the same, down
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
